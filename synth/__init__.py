@@ -1,0 +1,16 @@
+"""Seeded synthetic workloads for the cache-aware streaming Conformer chunk step.
+
+This package only draws numbers: the five workload configurations, seeded weights,
+inputs and injected stream states. It holds none of the encoder's arithmetic, so the
+oracle under ``oracle/`` and the HIP path can both consume it without sharing any
+computation.
+"""
+from .configs import C1, C2, C3, C4, C5, CONFIGS, EncConfig, get_config  # noqa: F401
+from .gen import (  # noqa: F401
+    bf16_round,
+    make_weights,
+    make_inputs,
+    make_state,
+    make_token_head,
+    weight_names,
+)

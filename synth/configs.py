@@ -1,0 +1,70 @@
+"""The five synthetic workloads (sizes, precisions, stream counts, step counts).
+
+Model sizes follow the Parakeet-EOU-120M model card ("Config" table: 17 encoder layers,
+hidden 512, attention context 70) and the fluidaudio-web streaming spec ("Why this is
+provably correct": chunk 2, left 70; "State": 14-frame mel tail, 8-column conv cache;
+"Status", Nemotron variant: right context 3 with a provisional tail).
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class EncConfig:
+    name: str
+    seed: int               # master seed of this workload
+    n_layers: int = 17
+    d_model: int = 512
+    n_heads: int = 8
+    d_ff: int = 2048
+    dw_kernel: int = 9      # depthwise kernel; the conv cache holds dw_kernel-1 columns
+    att_left: int = 70      # Lc: left attention context, also the K/V cache depth
+    att_chunk: int = 2      # frames per attention chunk (push granularity)
+    att_right: int = 0      # right context (lookahead variant only)
+    n_emit: int = 2         # frames emitted per stream per push
+    n_lookahead: int = 0    # provisional frames recomputed every pass (lookahead variant)
+    joint_dim: int = 640    # 0 = no joint projection
+    frontend: bool = False  # 3 causal stride-2 convs over log-mel
+    mel_bins: int = 128
+    mel_per_chunk: int = 16
+    mel_tail: int = 14
+    dtype: str = "f32"      # "f32" or "bf16"
+    streams: int = 1
+    chunks: int = 100       # pushes per stream in the workload
+    staggered: bool = False  # streams start from injected random states
+    token_classes: int = 1026  # check-only token head: 1024 vocab + blank + EOU
+
+    @property
+    def head_dim(self) -> int:
+        return self.d_model // self.n_heads
+
+    @property
+    def n_compute(self) -> int:
+        """Frames run through the layers per stream per push."""
+        return self.n_emit + self.n_lookahead
+
+    @property
+    def conv_cache(self) -> int:
+        return self.dw_kernel - 1
+
+    def replace(self, **kw) -> "EncConfig":
+        return dataclasses.replace(self, **kw)
+
+
+C1 = EncConfig(name="C1_tiny_f32", seed=0, n_layers=2, d_model=64, n_heads=4, d_ff=256,
+               joint_dim=0, dtype="f32", streams=1, chunks=100)
+C2 = EncConfig(name="C2_eou_f32_1stream", seed=1, dtype="f32", streams=1, chunks=1000)
+C3 = EncConfig(name="C3_eou_bf16_256streams", seed=2, dtype="bf16", streams=256, chunks=200,
+               staggered=True)
+C4 = EncConfig(name="C4_eou_bf16_1024streams_frontend", seed=3, dtype="bf16", streams=1024,
+               chunks=100, staggered=True, frontend=True)
+C5 = EncConfig(name="C5_lookahead_bf16_512streams", seed=4, dtype="bf16", streams=512, chunks=300,
+               staggered=True, att_right=3, n_emit=2, n_lookahead=8)
+
+CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
+
+
+def get_config(key: str) -> EncConfig:
+    return CONFIGS[key]
