@@ -1,0 +1,17 @@
+"""Cache-aware streaming Conformer chunk step for MI355X (gfx950).
+
+The work runs in ``libcac.so`` (HIP kernels behind the C ABI of ``include/cac.h``);
+``binding`` is its thin ctypes wrapper.
+"""
+from .binding import (  # noqa: F401
+    CAC_BF16,
+    CAC_F32,
+    CAC_FLAG_DRY_RUN,
+    CAC_FLAG_POISON,
+    CacError,
+    StreamingEncoder,
+    load,
+    make_config,
+    pack_params,
+    param_order,
+)

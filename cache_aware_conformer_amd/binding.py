@@ -1,0 +1,280 @@
+"""ctypes binding of libcac.so (include/cac.h). Argument marshalling only: every step of the
+chunk step runs in the library's HIP kernels; torch provides device memory and the stream.
+
+The library must have been built (``__graft_entry__.build()`` or
+``python cache_aware_conformer_amd/build.py``); loading fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcac.so")
+
+CAC_OK, CAC_EINVAL, CAC_ESTATE, CAC_ENOMEM, CAC_EHIP, CAC_ENODEV = 0, -1, -2, -3, -4, -5
+CAC_F32, CAC_BF16 = 0, 1
+CAC_FLAG_DRY_RUN, CAC_FLAG_POISON = 1, 2
+ERROR_NAMES = {CAC_EINVAL: "CAC_EINVAL", CAC_ESTATE: "CAC_ESTATE", CAC_ENOMEM: "CAC_ENOMEM",
+               CAC_EHIP: "CAC_EHIP", CAC_ENODEV: "CAC_ENODEV"}
+
+# every function the header declares, with (restype, argtypes)
+_i32, _sz, _vp, _ip, _fp = C.c_int32, C.c_size_t, C.c_void_p, C.POINTER(C.c_int32), C.POINTER(C.c_float)
+
+
+class cac_config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "n_layers", "d_model", "n_heads", "d_ff", "dw_kernel", "att_left", "att_chunk", "att_right",
+        "n_emit", "n_lookahead", "joint_dim", "frontend", "mel_bins", "mel_per_chunk", "mel_tail",
+        "dtype", "max_streams", "max_push_frames", "flags")]
+
+
+_CFGP = C.POINTER(cac_config)
+SIGNATURES = {
+    "cac_param_count": (_sz, [_CFGP]),
+    "cac_workspace_bytes": (_sz, [_CFGP]),
+    "cac_state_floats": (_sz, [_CFGP]),
+    "cac_create_streams": (_i32, [_CFGP, _fp, _sz, _vp, _sz, _vp, C.POINTER(_vp)]),
+    "cac_push_chunk": (_i32, [_vp, _i32, _ip, _i32, _vp, _vp, _ip]),
+    "cac_reset_stream": (_i32, [_vp, _i32, _ip]),
+    "cac_flush": (_i32, [_vp, _i32, _ip, _vp, _ip]),
+    "cac_export_state": (_i32, [_vp, _i32, _ip, _ip, _ip, _vp]),
+    "cac_import_state": (_i32, [_vp, _i32, _ip, _ip, _ip, _vp]),
+    "cac_stream_info": (_i32, [_vp, _i32, _ip, _ip, _ip]),
+    "cac_set_stream": (_i32, [_vp, _vp]),
+    "cac_synchronize": (_i32, [_vp]),
+    "cac_destroy": (_i32, [_vp]),
+    "cac_last_error": (C.c_char_p, [_vp]),
+    "cac_test_gemm": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+}
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load libcac.so once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype, f.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+class CacError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def param_order(cfg):
+    """(name, shape) of the parameters in the order cac_create_streams reads them (the
+    order the header documents)."""
+    D, F, H, K, P = cfg.d_model, cfg.d_ff, cfg.n_heads, cfg.dw_kernel, cfg.joint_dim
+    hd = D // H
+    out = []
+    for l in range(cfg.n_layers):
+        p = f"l{l}."
+        ff = lambda pre: [(pre + "ln_g", (D,)), (pre + "ln_b", (D,)), (pre + "w1", (D, F)), (pre + "b1", (F,)),  # noqa: E731
+                          (pre + "w2", (F, D)), (pre + "b2", (D,))]
+        out += ff(p + "ff1.")
+        out += [(p + "att.ln_g", (D,)), (p + "att.ln_b", (D,))]
+        for m in "qkv":
+            out += [(p + f"att.w{m}", (D, D)), (p + f"att.b{m}", (D,))]
+        out += [(p + "att.wo", (D, D)), (p + "att.bo", (D,)), (p + "att.pos_u", (H, hd)),
+                (p + "att.pos_v", (H, hd)), (p + "att.wpos", (D, D))]
+        out += [(p + "conv.ln_g", (D,)), (p + "conv.ln_b", (D,)), (p + "conv.pw1", (D, 2 * D)),
+                (p + "conv.pw1_b", (2 * D,)), (p + "conv.dw", (D, K)), (p + "conv.dw_b", (D,)),
+                (p + "conv.pw2", (D, D)), (p + "conv.pw2_b", (D,))]
+        out += ff(p + "ff2.")
+        out += [(p + "out.ln_g", (D,)), (p + "out.ln_b", (D,))]
+    if P:
+        out += [("joint.w", (D, P)), ("joint.b", (P,))]
+    if cfg.frontend:
+        B = cfg.mel_bins
+        out += [("fe.c1.w", (D, B, 3)), ("fe.c1.b", (D,)), ("fe.c2.w", (D, D, 3)), ("fe.c2.b", (D,)),
+                ("fe.c3.w", (D, D, 3)), ("fe.c3.b", (D,))]
+    return out
+
+
+def make_config(cfg, max_streams=None, max_push_frames=8, flags=0) -> cac_config:
+    """cac_config from any object with the workload attribute names (dtype 'f32'/'bf16')."""
+    c = cac_config()
+    for name in ("n_layers", "d_model", "n_heads", "d_ff", "dw_kernel", "att_left", "att_chunk",
+                 "att_right", "n_emit", "n_lookahead", "joint_dim", "mel_bins", "mel_per_chunk", "mel_tail"):
+        setattr(c, name, int(getattr(cfg, name)))
+    c.frontend = int(bool(cfg.frontend))
+    c.dtype = CAC_BF16 if str(cfg.dtype) in ("bf16", "bfloat16", str(CAC_BF16)) else CAC_F32
+    c.max_streams = int(max_streams if max_streams is not None else cfg.streams)
+    c.max_push_frames = int(max_push_frames)
+    c.flags = int(flags)
+    return c
+
+
+def pack_params(cfg, params: dict) -> np.ndarray:
+    order = param_order(cfg)
+    flat = np.empty(sum(int(np.prod(s)) for _, s in order), dtype=np.float32)
+    o = 0
+    for name, shape in order:
+        a = np.asarray(params[name], dtype=np.float32)
+        if a.shape != tuple(shape):
+            raise ValueError(f"{name}: expected shape {shape}, got {a.shape}")
+        n = a.size
+        flat[o:o + n] = a.reshape(-1)
+        o += n
+    return flat
+
+
+def _ids(ids) -> tuple:
+    arr = np.ascontiguousarray(np.asarray(ids, dtype=np.int32).reshape(-1))
+    return arr, arr.ctypes.data_as(_ip)
+
+
+@dataclass
+class StreamInfo:
+    pos: int
+    pending: int
+    flushed: bool
+
+
+class StreamingEncoder:
+    """One library context: repacked weights and the state of ``max_streams`` streams in one
+    device workspace (a torch uint8 tensor), work enqueued on the current torch stream."""
+
+    def __init__(self, cfg, params: dict, max_streams=None, max_push_frames=8, flags=0, device="cuda:0"):
+        self.lib = load()
+        self.cfg = cfg
+        self.c = make_config(cfg, max_streams, max_push_frames, flags)
+        self.dry = bool(flags & CAC_FLAG_DRY_RUN)
+        self.P = cfg.joint_dim or cfg.d_model
+        n = self.lib.cac_param_count(C.byref(self.c))
+        if n == 0:
+            self.lib.cac_create_streams(C.byref(self.c), None, 0, None, 0, None, C.byref(C.c_void_p()))
+            raise CacError(CAC_EINVAL, self.lib.cac_last_error(None).decode())
+        flat = pack_params(cfg, params)
+        assert flat.size == n, (flat.size, n)
+        self.ws_bytes = self.lib.cac_workspace_bytes(C.byref(self.c))
+        self.sfloats = self.lib.cac_state_floats(C.byref(self.c))
+        ctx = C.c_void_p()
+        if self.dry:
+            ws_ptr, stream = None, None
+            self.ws = None
+        else:
+            import torch
+            self.torch = torch
+            self.device = torch.device(device)
+            self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+            base = self.ws.data_ptr()
+            ws_ptr = (base + 255) // 256 * 256
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        rc = self.lib.cac_create_streams(C.byref(self.c), flat.ctypes.data_as(_fp), n, ws_ptr,
+                                         self.ws_bytes, stream, C.byref(ctx))
+        if rc != CAC_OK:
+            raise CacError(rc, self.lib.cac_last_error(None).decode())
+        self.ctx = ctx
+
+    # -- helpers -----------------------------------------------------------------------
+    def _check(self, rc):
+        if rc < 0:
+            raise CacError(rc, self.lib.cac_last_error(self.ctx).decode())
+        return rc
+
+    def out_frames(self):
+        return self.cfg.n_lookahead if self.cfg.n_lookahead else None
+
+    # -- calls -------------------------------------------------------------------------
+    def push_chunk(self, stream_ids, x, out=None, n_frames=None):
+        """x: device tensor [n, n_frames, D] (or [n, 16, mel_bins]) in the compute dtype.
+        Returns (out [n, n_frames_out, P] float32, emitted per stream as np.int32)."""
+        ids, idp = _ids(stream_ids)
+        n = ids.size
+        if n_frames is None:
+            if self.cfg.n_lookahead:
+                n_frames = self.cfg.n_emit
+            elif self.cfg.frontend:
+                n_frames = 2
+            else:
+                n_frames = x.shape[1]
+        if out is None and not self.dry:
+            out = self.torch.empty((n, n_frames, self.P), dtype=self.torch.float32, device=self.device)
+        emitted = np.zeros(n, dtype=np.int32)
+        xp = None if x is None else (x.data_ptr() if hasattr(x, "data_ptr") else int(x))
+        op = None if out is None else (out.data_ptr() if hasattr(out, "data_ptr") else int(out))
+        self._check(self.lib.cac_push_chunk(self.ctx, n, idp, int(n_frames), xp, op, emitted.ctypes.data_as(_ip)))
+        return out, emitted
+
+    def reset_stream(self, stream_ids):
+        ids, idp = _ids(stream_ids)
+        return self._check(self.lib.cac_reset_stream(self.ctx, ids.size, idp))
+
+    def flush(self, stream_ids, out=None):
+        ids, idp = _ids(stream_ids)
+        n = ids.size
+        if out is None and not self.dry and self.cfg.n_lookahead:
+            out = self.torch.empty((n, self.cfg.n_lookahead, self.P), dtype=self.torch.float32, device=self.device)
+        frames = np.zeros(n, dtype=np.int32)
+        op = None if out is None else out.data_ptr()
+        self._check(self.lib.cac_flush(self.ctx, n, idp, op, frames.ctypes.data_as(_ip)))
+        return out, frames
+
+    def export_state(self, stream_ids):
+        ids, idp = _ids(stream_ids)
+        n = ids.size
+        blob = self.torch.empty((n, self.sfloats), dtype=self.torch.float32, device=self.device)
+        pos = np.zeros(n, dtype=np.int32)
+        pend = np.zeros(n, dtype=np.int32)
+        self._check(self.lib.cac_export_state(self.ctx, n, idp, pos.ctypes.data_as(_ip),
+                                              pend.ctypes.data_as(_ip), blob.data_ptr()))
+        return pos, pend, blob
+
+    def import_state(self, stream_ids, pos, pending, blob):
+        ids, idp = _ids(stream_ids)
+        pos = np.ascontiguousarray(np.asarray(pos, dtype=np.int32))
+        pend = np.ascontiguousarray(np.asarray(pending if pending is not None else np.zeros_like(pos), dtype=np.int32))
+        bp = blob.data_ptr() if blob is not None else None
+        return self._check(self.lib.cac_import_state(self.ctx, ids.size, idp, pos.ctypes.data_as(_ip),
+                                                     pend.ctypes.data_as(_ip), bp))
+
+    def stream_info(self, stream_id) -> StreamInfo:
+        p, q, f = C.c_int32(), C.c_int32(), C.c_int32()
+        self._check(self.lib.cac_stream_info(self.ctx, int(stream_id), C.byref(p), C.byref(q), C.byref(f)))
+        return StreamInfo(p.value, q.value, bool(f.value))
+
+    def set_stream(self, stream):
+        return self._check(self.lib.cac_set_stream(self.ctx, stream))
+
+    def synchronize(self):
+        return self._check(self.lib.cac_synchronize(self.ctx))
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            self.lib.cac_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def test_gemm(dtype: int, path: int, A, W, bias=None, out=None, stream=None):
+    """C = A W^T + bias through the library's dense kernels (test-only export)."""
+    import torch
+    lib = load()
+    M, K = A.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    s = stream if stream is not None else torch.cuda.current_stream(A.device).cuda_stream
+    rc = lib.cac_test_gemm(dtype, path, M, N, K, A.data_ptr(), W.data_ptr(),
+                           None if bias is None else bias.data_ptr(), out.data_ptr(), s)
+    if rc != CAC_OK:
+        raise CacError(rc, "cac_test_gemm failed")
+    return out

@@ -1,0 +1,779 @@
+// C ABI of the chunk-step library (include/cac.h): validation, workspace layout, weight
+// repacking, host-side stream bookkeeping and the per-push launch sequence.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/cac.h"
+#include "common.h"
+
+void kernels_init();
+
+namespace {
+
+thread_local std::string g_create_error;
+
+// ------------------------------------------------------------------------------- dimensions
+struct Dims {
+  int L, D, H, hd, F, K, Kc, Lc, c, right, ne, nla, nc, P, fe, bins, mpc, tail, dt, S, npush, flags;
+  bool lookahead;
+  int nfmax;          // frames per stream a call runs through the layers
+  int R, Rc, Rx;      // ring depths: K/V, depthwise input, pending inputs
+  int rel_lo, nrel;   // relative offsets covered by the position table
+  size_t esz;         // bytes per compute-dtype element
+};
+
+bool make_dims(const cac_config* c, Dims& d, std::string& why) {
+  if (!c) { why = "config is NULL"; return false; }
+  d.L = c->n_layers; d.D = c->d_model; d.H = c->n_heads; d.F = c->d_ff; d.K = c->dw_kernel;
+  d.Lc = c->att_left; d.c = c->att_chunk; d.right = c->att_right; d.ne = c->n_emit;
+  d.nla = c->n_lookahead; d.P = c->joint_dim; d.fe = c->frontend; d.bins = c->mel_bins;
+  d.mpc = c->mel_per_chunk; d.tail = c->mel_tail; d.dt = c->dtype; d.S = c->max_streams;
+  d.npush = c->max_push_frames; d.flags = c->flags;
+  auto bad = [&](const char* m) { why = m; return false; };
+  if (d.L < 1 || d.L > 64) return bad("n_layers must be in [1, 64]");
+  if (d.D < 64 || d.D > 4096 || d.D % 64) return bad("d_model must be a multiple of 64 in [64, 4096]");
+  if (d.H < 1 || d.D % d.H) return bad("n_heads must divide d_model");
+  d.hd = d.D / d.H;
+  if (d.hd != 16 && d.hd != 32 && d.hd != 64) return bad("head_dim must be 16, 32 or 64");
+  if (d.F < 64 || d.F > 4096 || d.F % 64) return bad("d_ff must be a multiple of 64 in [64, 4096]");
+  if (d.K < 1 || d.K > 17) return bad("dw_kernel must be in [1, 17]");
+  d.Kc = d.K - 1;
+  if (d.Lc < 0 || d.Lc > 512) return bad("att_left must be in [0, 512]");
+  if (d.c < 1 || d.c > 16) return bad("att_chunk must be in [1, 16]");
+  if (d.nla < 0 || d.ne < 1) return bad("n_emit must be >= 1 and n_lookahead >= 0");
+  d.lookahead = d.nla > 0;
+  if (!d.lookahead && d.right != 0) return bad("att_right needs the lookahead variant (n_lookahead > 0)");
+  if (d.right < 0 || d.right > 64) return bad("att_right must be in [0, 64]");
+  d.nc = d.ne + d.nla;
+  if (d.nc > 16) return bad("n_emit + n_lookahead must be <= 16");
+  if (d.P < 0 || d.P > 8192) return bad("joint_dim must be in [0, 8192]");
+  if (d.dt != CAC_F32 && d.dt != CAC_BF16) return bad("dtype must be CAC_F32 or CAC_BF16");
+  if (d.S < 1 || d.S > (1 << 20)) return bad("max_streams must be in [1, 2^20]");
+  if (d.fe) {
+    if (d.lookahead) return bad("the front end is supported with the exact variant only");
+    if (d.mpc != 16 || d.tail != 14) return bad("the front end needs mel_per_chunk 16 and mel_tail 14");
+    if (d.bins < 32 || d.bins > 1024 || d.bins % 32) return bad("mel_bins must be a multiple of 32 in [32, 1024]");
+  } else {
+    d.bins = 0; d.tail = 0; d.mpc = 0;
+  }
+  if (d.lookahead) {
+    d.nfmax = d.nc;
+  } else {
+    if (d.npush < d.c || d.npush > 16 || d.npush % d.c) return bad("max_push_frames must be a multiple of att_chunk in [att_chunk, 16]");
+    if (d.fe && d.npush < 2) return bad("the front end pushes 2 frames per chunk");
+    d.nfmax = d.npush;
+  }
+  d.R = d.Lc + d.nfmax;
+  d.Rc = d.Kc + d.nfmax;
+  d.Rx = d.lookahead ? d.nc : 0;
+  if (d.lookahead) { d.rel_lo = -d.right; d.nrel = d.Lc + d.right + 1; }
+  else { d.rel_lo = -(d.c - 1); d.nrel = d.Lc + 2 * d.c - 1; }
+  d.esz = d.dt == CAC_BF16 ? 2 : 4;
+  if (attention_shmem(d.nfmax, d.Lc + d.nfmax, d.nrel, d.hd) > 160 * 1024) return bad("attention tile exceeds LDS: reduce att_left or frames per call");
+  return true;
+}
+
+// ------------------------------------------------------------------------------- layout
+struct Bump {
+  size_t off = 0;
+  size_t take(size_t bytes) { off = (off + 255) & ~(size_t)255; size_t o = off; off += bytes; return o; }
+};
+
+struct LayerOff {
+  size_t ln[10];  // ff1 g,b  att g,b  conv g,b  ff2 g,b  out g,b
+  size_t b_ff1_1, b_ff1_2, b_qkv, b_o, b_pw1, b_dw, b_pw2, b_ff2_1, b_ff2_2, pos_u, pos_v, dw_w, wpos;
+  size_t w_ff1_1, w_ff1_2, w_qkv, w_o, w_pw1, w_pw2, w_ff2_1, w_ff2_2;
+  size_t size;
+};
+
+struct Layout {
+  LayerOff lo;
+  size_t layers, wj, bj, fe_w[3], fe_b[3], weights_end;
+  size_t posproj, kring, vring, cring, tail, x0, pos, pend;
+  size_t ids, cids, cidx, sids, spos, spend;
+  size_t x, y, q, h, o, e, win, fe1, fe2;
+  size_t total;
+};
+
+Layout make_layout(const Dims& d) {
+  Layout t{};
+  const size_t D = d.D, F = d.F, f4 = 4, e = d.esz;
+  Bump b;
+  LayerOff& lo = t.lo;
+  for (int i = 0; i < 10; ++i) lo.ln[i] = b.take(D * f4);
+  lo.b_ff1_1 = b.take(F * f4); lo.b_ff1_2 = b.take(D * f4); lo.b_qkv = b.take(3 * D * f4);
+  lo.b_o = b.take(D * f4); lo.b_pw1 = b.take(2 * D * f4); lo.b_dw = b.take(D * f4);
+  lo.b_pw2 = b.take(D * f4); lo.b_ff2_1 = b.take(F * f4); lo.b_ff2_2 = b.take(D * f4);
+  lo.pos_u = b.take(D * f4); lo.pos_v = b.take(D * f4); lo.dw_w = b.take((size_t)d.K * D * f4);
+  lo.wpos = b.take(D * D * f4);
+  lo.w_ff1_1 = b.take(F * D * e); lo.w_ff1_2 = b.take(D * F * e); lo.w_qkv = b.take(3 * D * D * e);
+  lo.w_o = b.take(D * D * e); lo.w_pw1 = b.take(2 * D * D * e); lo.w_pw2 = b.take(D * D * e);
+  lo.w_ff2_1 = b.take(F * D * e); lo.w_ff2_2 = b.take(D * F * e);
+  lo.size = (b.take(0) + 255) & ~(size_t)255;
+
+  Bump w;
+  t.layers = w.take(lo.size * d.L);
+  if (d.P) { t.wj = w.take((size_t)d.P * D * e); t.bj = w.take((size_t)d.P * f4); }
+  if (d.fe) {
+    const size_t kin[3] = {(size_t)3 * d.bins, 3 * D, 3 * D};
+    for (int i = 0; i < 3; ++i) { t.fe_w[i] = w.take(D * kin[i] * e); t.fe_b[i] = w.take(D * f4); }
+  }
+  t.weights_end = w.take(0);
+  const size_t S = d.S, L = d.L, M = S * d.nfmax;
+  t.posproj = w.take(L * d.H * d.nrel * d.hd * f4);
+  t.kring = w.take(L * S * d.H * d.R * d.hd * e);
+  t.vring = w.take(L * S * d.H * d.R * d.hd * e);
+  t.cring = w.take(L * S * d.Rc * D * e);
+  t.tail = w.take(S * d.tail * d.bins * e);
+  t.x0 = w.take(S * d.Rx * D * e);
+  t.pos = w.take(S * 4); t.pend = w.take(S * 4);
+  t.ids = w.take(S * 4); t.cids = w.take(S * 4); t.cidx = w.take(S * 4);
+  t.sids = w.take(S * 4); t.spos = w.take(S * 4); t.spend = w.take(S * 4);
+  t.x = w.take(M * D * f4); t.y = w.take(M * D * e); t.q = w.take(M * D * f4);
+  t.h = w.take(M * F * e); t.o = w.take(M * D * e); t.e = w.take(M * D * e);
+  if (d.fe) {
+    t.win = w.take(S * (d.tail + d.mpc) * d.bins * e);
+    t.fe1 = w.take(S * 11 * D * e);
+    t.fe2 = w.take(S * 5 * D * e);
+  }
+  t.total = w.take(0);
+  return t;
+}
+
+size_t param_count(const Dims& d) {
+  const size_t D = d.D, F = d.F, H = d.H, hd = d.hd;
+  size_t per = 0;
+  per += 2 * D + D * F + F + F * D + D;                        // ff1
+  per += 2 * D + 4 * (D * D + D) + 2 * H * hd + D * D;         // att
+  per += 2 * D + D * 2 * D + 2 * D + D * d.K + D + D * D + D;  // conv
+  per += 2 * D + D * F + F + F * D + D;                        // ff2
+  per += 2 * D;                                                // out
+  size_t n = per * d.L;
+  if (d.P) n += D * d.P + d.P;
+  if (d.fe) n += D * d.bins * 3 + D + 2 * (D * D * 3 + D);
+  return n;
+}
+
+size_t state_floats(const Dims& d) {
+  return 2 * (size_t)d.L * d.Lc * d.D + (size_t)d.L * d.Kc * d.D + (size_t)d.tail * d.bins + (size_t)d.nla * d.D;
+}
+
+// ------------------------------------------------------------------------------- host packing
+uint16_t to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+struct Packer {
+  std::vector<uint8_t>& buf;
+  int dt;
+  void f32(size_t off, const float* src, size_t n) { memcpy(buf.data() + off, src, n * 4); }
+  void op(size_t off, size_t idx, float v) {
+    if (dt == CAC_BF16) ((uint16_t*)(buf.data() + off))[idx] = to_bf16(v);
+    else ((float*)(buf.data() + off))[idx] = v;
+  }
+  // in [K][N] row-major -> out [N][K]
+  void transpose(size_t off, const float* in, size_t K, size_t N, size_t row0 = 0) {
+    for (size_t k = 0; k < K; ++k)
+      for (size_t n = 0; n < N; ++n) op(off, (row0 + n) * K + k, in[k * N + n]);
+  }
+};
+
+int glu_a_col_host(int c) { return (c >> 5) * 64 + (c & 31); }
+
+}  // namespace
+
+// ------------------------------------------------------------------------------- context
+struct cac_ctx {
+  Dims d;
+  Layout lay;
+  char* ws = nullptr;
+  hipStream_t stream = nullptr;
+  bool dry = false;
+  std::vector<int32_t> hpos, hpend;
+  std::vector<uint8_t> flushed;
+  std::vector<int32_t> dev_ids, dev_cids, dev_cidx;  // contents last uploaded
+  std::vector<int32_t> stamp;
+  int32_t stamp_gen = 0;
+  std::string err;
+
+  template <class T> T* P(size_t off) const { return (T*)(ws + off); }
+  int fail(int code, const std::string& m) { err = m; return code; }
+};
+
+namespace {
+
+int check_ids(cac_ctx* c, int32_t n, const int32_t* ids, bool need_open) {
+  if (n < 1 || n > c->d.S) return c->fail(CAC_EINVAL, "stream count out of range");
+  if (!ids) return c->fail(CAC_EINVAL, "stream id list is NULL");
+  if (++c->stamp_gen == INT32_MAX) { std::fill(c->stamp.begin(), c->stamp.end(), 0); c->stamp_gen = 1; }
+  for (int i = 0; i < n; ++i) {
+    const int id = ids[i];
+    if (id < 0 || id >= c->d.S) return c->fail(CAC_EINVAL, "stream id " + std::to_string(id) + " out of range");
+    if (c->stamp[id] == c->stamp_gen) return c->fail(CAC_EINVAL, "stream id " + std::to_string(id) + " appears twice");
+    c->stamp[id] = c->stamp_gen;
+    if (need_open && c->flushed[id]) return c->fail(CAC_ESTATE, "stream " + std::to_string(id) + " was flushed; reset it first");
+  }
+  return CAC_OK;
+}
+
+hipError_t upload(cac_ctx* c, std::vector<int32_t>& cache, size_t off, const int32_t* src, int n) {
+  if ((int)cache.size() == n && memcmp(cache.data(), src, n * 4) == 0) return hipSuccess;
+  cache.assign(src, src + n);
+  return hipMemcpyAsync(c->ws + off, cache.data(), (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+}
+
+// ------------------------------------------------------------------------------- layer pass
+// The launch sequence of the Conformer blocks for the rows of one call (cv.n_streams streams x
+// cv.nf frames, row m = stream m / nf, frame m % nf), starting from float32 rows in x.
+struct Pass {
+  cac_ctx* c;
+  Launcher& L;
+  CallView cv;
+  int M;
+
+  EpiArgs epi0() const {
+    EpiArgs e{};
+    e.cv = cv;
+    e.D = c->d.D; e.H = c->d.H; e.hd = c->d.hd; e.R = c->d.R; e.Rc = c->d.Rc;
+    return e;
+  }
+  // dense product whose A operand is LayerNorm(x) (float32 residual rows)
+  void gemm_ln(const float* g_ln, const float* b_ln, const void* W, int N, int K, const EpiArgs& e) {
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K; g.W = W; g.epi = e;
+    g.A = c->P<float>(c->lay.x); g.amap = RowMap{INT_MAX, 0, K};
+    g.a_f32 = 1; g.ln_g = g_ln; g.ln_b = b_ln; g.a_scratch = c->P<void>(c->lay.y);
+    launch_gemm(L, g, c->d.dt, 0);
+  }
+  void gemm_plain(const void* A, int lda, const void* W, int N, int K, const EpiArgs& e) {
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K; g.A = A; g.W = W; g.epi = e;
+    g.amap = RowMap{INT_MAX, 0, lda};
+    launch_gemm(L, g, c->d.dt, 0);
+  }
+  void ff(char* lb, int ln_idx, size_t b1, size_t b2, size_t w1, size_t w2) {
+    const Dims& d = c->d;
+    const LayerOff& lo = c->lay.lo;
+    EpiArgs up = epi0();
+    up.kind = EPI_SILU; up.bias = (const float*)(lb + b1); up.out = c->P<void>(c->lay.h); up.ldo = d.F;
+    gemm_ln((const float*)(lb + lo.ln[ln_idx]), (const float*)(lb + lo.ln[ln_idx + 1]), lb + w1, d.F, d.D, up);
+    EpiArgs dn = epi0();
+    dn.kind = EPI_RESID; dn.bias = (const float*)(lb + b2); dn.out = c->P<void>(c->lay.x); dn.ldo = d.D; dn.alpha = 0.5f;
+    gemm_plain(c->P<void>(c->lay.h), d.F, lb + w2, d.D, d.F, dn);
+  }
+
+  void layers() {
+    const Dims& d = c->d;
+    const LayerOff& lo = c->lay.lo;
+    for (int l = 0; l < d.L; ++l) {
+      char* lb = c->ws + c->lay.layers + (size_t)l * lo.size;
+      const size_t kvl = (size_t)d.S * d.H * d.R * d.hd * d.esz;
+      char* kr = c->ws + c->lay.kring + l * kvl;
+      char* vr = c->ws + c->lay.vring + l * kvl;
+      char* cr = c->ws + c->lay.cring + (size_t)l * d.S * d.Rc * d.D * d.esz;
+      // FF1 (macaron half step)
+      ff(lb, 0, lo.b_ff1_1, lo.b_ff1_2, lo.w_ff1_1, lo.w_ff1_2);
+      // MHSA: q to a buffer, k and v straight into the ring slots of their positions
+      EpiArgs qkv = epi0();
+      qkv.kind = EPI_QKV; qkv.bias = (const float*)(lb + lo.b_qkv); qkv.qbuf = c->P<float>(c->lay.q);
+      qkv.kring = kr; qkv.vring = vr;
+      gemm_ln((const float*)(lb + lo.ln[2]), (const float*)(lb + lo.ln[3]), lb + lo.w_qkv, 3 * d.D, d.D, qkv);
+      AttnArgs at{};
+      at.cv = cv; at.q = c->P<float>(c->lay.q); at.kring = kr; at.vring = vr;
+      at.posproj = c->P<float>(c->lay.posproj) + (size_t)l * d.H * d.nrel * d.hd;
+      at.pos_u = (const float*)(lb + lo.pos_u); at.pos_v = (const float*)(lb + lo.pos_v);
+      at.o = c->P<void>(c->lay.o);
+      at.D = d.D; at.H = d.H; at.R = d.R; at.Lc = d.Lc; at.chunk = d.c; at.right = d.right;
+      at.lookahead = d.lookahead; at.rel_lo = d.rel_lo; at.nrel = d.nrel;
+      at.scale = 1.0f / sqrtf((float)d.hd);
+      launch_attention(L, at, d.dt, d.hd);
+      EpiArgs wo = epi0();
+      wo.kind = EPI_RESID; wo.bias = (const float*)(lb + lo.b_o); wo.out = c->P<void>(c->lay.x); wo.ldo = d.D; wo.alpha = 1.0f;
+      gemm_plain(c->P<void>(c->lay.o), d.D, lb + lo.w_o, d.D, d.D, wo);
+      // conv module: LN -> pw1 -> GLU into the ring; depthwise + SiLU; pw2 + residual
+      EpiArgs glu = epi0();
+      glu.kind = EPI_GLU; glu.bias = (const float*)(lb + lo.b_pw1); glu.cring = cr;
+      gemm_ln((const float*)(lb + lo.ln[4]), (const float*)(lb + lo.ln[5]), lb + lo.w_pw1, 2 * d.D, d.D, glu);
+      DwArgs dw{cv, cr, (const float*)(lb + lo.dw_w), (const float*)(lb + lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
+      launch_dwconv(L, dw, d.dt);
+      EpiArgs pw2 = epi0();
+      pw2.kind = EPI_RESID; pw2.bias = (const float*)(lb + lo.b_pw2); pw2.out = c->P<void>(c->lay.x); pw2.ldo = d.D; pw2.alpha = 1.0f;
+      gemm_plain(c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, d.D, pw2);
+      // FF2 (macaron half step), then the block's own LayerNorm in place
+      ff(lb, 6, lo.b_ff2_1, lo.b_ff2_2, lo.w_ff2_1, lo.w_ff2_2);
+      LnArgs lo_out{c->P<float>(c->lay.x), c->P<void>(c->lay.x), (const float*)(lb + lo.ln[8]),
+                    (const float*)(lb + lo.ln[9]), M, d.D, 1};
+      launch_ln(L, lo_out, d.dt);
+    }
+  }
+
+  // encoder-side joint projection of the rows picked by amap into d_out (rows remapped by omap)
+  void joint(float* d_out, int rows, RowMap amap, const int32_t* omap, int ogroup, int ostride) {
+    const Dims& d = c->d;
+    if (d.P == 0) {
+      CopyRowsArgs cp{c->P<float>(c->lay.x), amap, d_out, omap, ogroup, ostride, rows, d.D};
+      launch_copy_rows(L, cp);
+      return;
+    }
+    EpiArgs e = epi0();
+    e.kind = EPI_F32; e.out = d_out; e.ldo = d.P; e.bias = c->P<float>(c->lay.bj);
+    e.omap = omap; e.ogroup = ogroup; e.ostride = ostride;
+    GemmArgs g{};
+    g.M = rows; g.N = d.P; g.K = d.D; g.A = c->P<float>(c->lay.x); g.amap = amap;
+    g.W = c->P<void>(c->lay.wj); g.epi = e; g.a_f32 = 1; g.a_scratch = c->P<void>(c->lay.y);
+    launch_gemm(L, g, d.dt, 0);
+  }
+};
+
+StateArgs state_args(cac_ctx* c, int n) {
+  const Dims& d = c->d;
+  const Layout& lay = c->lay;
+  StateArgs sa{};
+  sa.ids = c->P<int32_t>(lay.sids); sa.hpos = c->P<int32_t>(lay.spos); sa.hpend = c->P<int32_t>(lay.spend);
+  sa.pos = c->P<int32_t>(lay.pos); sa.pend = c->P<int32_t>(lay.pend);
+  sa.kring = c->ws + lay.kring; sa.vring = c->ws + lay.vring; sa.cring = c->ws + lay.cring;
+  sa.tail = c->ws + lay.tail; sa.x0 = c->ws + lay.x0;
+  sa.n = n; sa.S = d.S; sa.L = d.L; sa.D = d.D; sa.H = d.H; sa.hd = d.hd; sa.R = d.R; sa.Rc = d.Rc;
+  sa.Lc = d.Lc; sa.Kc = d.Kc; sa.tail_rows = d.tail; sa.bins = d.bins; sa.nla = d.nla; sa.Rx = d.Rx;
+  sa.state_floats = (long)state_floats(d);
+  sa.dtype = d.dt; sa.poison = (d.flags & CAC_FLAG_POISON) ? 1 : 0;
+  return sa;
+}
+
+int finish(cac_ctx* c, Launcher& L, int ok_value) {
+  if (L.err != hipSuccess) return c->fail(CAC_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(L.err));
+  return ok_value;
+}
+
+}  // namespace
+
+// =============================================================================== C ABI
+extern "C" {
+
+size_t cac_param_count(const cac_config* cfg) {
+  Dims d;
+  std::string why;
+  return make_dims(cfg, d, why) ? param_count(d) : 0;
+}
+
+size_t cac_workspace_bytes(const cac_config* cfg) {
+  Dims d;
+  std::string why;
+  return make_dims(cfg, d, why) ? make_layout(d).total : 0;
+}
+
+size_t cac_state_floats(const cac_config* cfg) {
+  Dims d;
+  std::string why;
+  return make_dims(cfg, d, why) ? state_floats(d) : 0;
+}
+
+const char* cac_last_error(const cac_ctx* ctx) {
+  return ctx ? ctx->err.c_str() : g_create_error.c_str();
+}
+
+int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t n_params,
+                           void* d_workspace, size_t ws_bytes, void* hip_stream, cac_ctx** out) {
+  g_create_error.clear();
+  if (!out) { g_create_error = "out is NULL"; return CAC_EINVAL; }
+  *out = nullptr;
+  Dims d;
+  if (!make_dims(cfg, d, g_create_error)) return CAC_EINVAL;
+  const size_t np = param_count(d);
+  if (!h_params) { g_create_error = "parameter array is NULL"; return CAC_EINVAL; }
+  if (n_params != np) {
+    g_create_error = "expected " + std::to_string(np) + " parameters, got " + std::to_string(n_params);
+    return CAC_EINVAL;
+  }
+  const bool dry = (d.flags & CAC_FLAG_DRY_RUN) != 0;
+  Layout lay = make_layout(d);
+  if (!dry) {
+    if (!d_workspace) { g_create_error = "workspace is NULL"; return CAC_EINVAL; }
+    if (((uintptr_t)d_workspace) & 255) { g_create_error = "workspace must be 256-byte aligned"; return CAC_EINVAL; }
+    if (ws_bytes < lay.total) {
+      g_create_error = "workspace too small: need " + std::to_string(lay.total) + " bytes";
+      return CAC_ENOMEM;
+    }
+  }
+  cac_ctx* c = new cac_ctx();
+  c->d = d; c->lay = lay; c->ws = (char*)d_workspace; c->stream = (hipStream_t)hip_stream; c->dry = dry;
+  c->hpos.assign(d.S, 0); c->hpend.assign(d.S, 0); c->flushed.assign(d.S, 0); c->stamp.assign(d.S, 0);
+  if (dry) { *out = c; return CAC_OK; }
+
+  kernels_init();
+  // repack the parameters on the host, then one copy into the workspace
+  std::vector<uint8_t> wbuf(lay.weights_end, 0);
+  Packer pk{wbuf, d.dt};
+  const float* p = h_params;
+  const size_t D = d.D, F = d.F;
+  auto take = [&](size_t n) { const float* r = p; p += n; return r; };
+  for (int l = 0; l < d.L; ++l) {
+    const size_t base = lay.layers + (size_t)l * lay.lo.size;
+    const LayerOff& lo = lay.lo;
+    auto ffp = [&](int lnidx, size_t b1, size_t b2, size_t w1, size_t w2) {
+      pk.f32(base + lo.ln[lnidx], take(D), D); pk.f32(base + lo.ln[lnidx + 1], take(D), D);
+      pk.transpose(base + w1, take(D * F), D, F); pk.f32(base + b1, take(F), F);
+      pk.transpose(base + w2, take(F * D), F, D); pk.f32(base + b2, take(D), D);
+    };
+    ffp(0, lo.b_ff1_1, lo.b_ff1_2, lo.w_ff1_1, lo.w_ff1_2);
+    pk.f32(base + lo.ln[2], take(D), D); pk.f32(base + lo.ln[3], take(D), D);
+    for (int m = 0; m < 3; ++m) {  // wq, wk, wv stacked as rows of [3D][D]
+      pk.transpose(base + lo.w_qkv, take(D * D), D, D, (size_t)m * D);
+      pk.f32(base + lo.b_qkv + (size_t)m * D * 4, take(D), D);
+    }
+    pk.transpose(base + lo.w_o, take(D * D), D, D); pk.f32(base + lo.b_o, take(D), D);
+    pk.f32(base + lo.pos_u, take(D), D); pk.f32(base + lo.pos_v, take(D), D);
+    pk.f32(base + lo.wpos, take(D * D), D * D);
+    pk.f32(base + lo.ln[4], take(D), D); pk.f32(base + lo.ln[5], take(D), D);
+    {  // pw1 [D][2D] -> GLU-packed rows: value channel c at glu_a_col(c), its gate 32 rows later
+      const float* w = take(D * 2 * D);
+      for (size_t ch = 0; ch < D; ++ch) {
+        const size_t ra = glu_a_col_host((int)ch), rb = ra + 32;
+        for (size_t k = 0; k < D; ++k) {
+          pk.op(base + lo.w_pw1, ra * D + k, w[k * 2 * D + ch]);
+          pk.op(base + lo.w_pw1, rb * D + k, w[k * 2 * D + D + ch]);
+        }
+      }
+      pk.f32(base + lo.b_pw1, take(2 * D), 2 * D);
+    }
+    {  // dw [D][K] -> taps [K][D]
+      const float* w = take(D * d.K);
+      float* dst = (float*)(wbuf.data() + base + lo.dw_w);
+      for (size_t ch = 0; ch < D; ++ch)
+        for (int k = 0; k < d.K; ++k) dst[(size_t)k * D + ch] = w[ch * d.K + k];
+      pk.f32(base + lo.b_dw, take(D), D);
+    }
+    pk.transpose(base + lo.w_pw2, take(D * D), D, D); pk.f32(base + lo.b_pw2, take(D), D);
+    ffp(6, lo.b_ff2_1, lo.b_ff2_2, lo.w_ff2_1, lo.w_ff2_2);
+    pk.f32(base + lo.ln[8], take(D), D); pk.f32(base + lo.ln[9], take(D), D);
+  }
+  if (d.P) {
+    pk.transpose(lay.wj, take(D * d.P), D, d.P);
+    pk.f32(lay.bj, take(d.P), d.P);
+  }
+  if (d.fe) {  // conv [out][in][tap] -> [out][tap * in + c_in] (matches a window of 3 rows)
+    const size_t cin[3] = {(size_t)d.bins, D, D};
+    for (int i = 0; i < 3; ++i) {
+      const float* w = take(D * cin[i] * 3);
+      for (size_t o = 0; o < D; ++o)
+        for (size_t ci = 0; ci < cin[i]; ++ci)
+          for (int t = 0; t < 3; ++t) pk.op(lay.fe_w[i], o * 3 * cin[i] + t * cin[i] + ci, w[(o * cin[i] + ci) * 3 + t]);
+      pk.f32(lay.fe_b[i], take(D), D);
+    }
+  }
+  hipError_t e = hipMemcpyAsync(c->ws, wbuf.data(), wbuf.size(), hipMemcpyHostToDevice, c->stream);
+  Launcher L;
+  L.stream = c->stream;
+  if (e == hipSuccess) {
+    // the position tables read the float32 Wpos copy of every layer (strided by layer block)
+    for (int l = 0; l < d.L && L.err == hipSuccess; ++l) {
+      PosProjArgs pa{c->P<float>(lay.layers + (size_t)l * lay.lo.size + lay.lo.wpos),
+                     c->P<float>(lay.posproj) + (size_t)l * d.H * d.nrel * d.hd, 1, d.D, d.H, d.hd, d.rel_lo, d.nrel};
+      launch_posproj(L, pa);
+    }
+    e = L.err;
+  }
+  std::vector<int32_t> all(d.S);
+  for (int i = 0; i < d.S; ++i) all[i] = i;
+  if (e == hipSuccess) {
+    e = hipMemcpyAsync(c->ws + lay.sids, all.data(), (size_t)d.S * 4, hipMemcpyHostToDevice, c->stream);
+    if (e == hipSuccess) {
+      StateArgs sa = state_args(c, d.S);
+      launch_state(L, sa, 0);
+      e = L.err;
+    }
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  }
+  if (e != hipSuccess) {
+    g_create_error = std::string("HIP error during create: ") + hipGetErrorString(e);
+    delete c;
+    return CAC_EHIP;
+  }
+  *out = c;
+  return CAC_OK;
+}
+
+
+int32_t cac_push_chunk(cac_ctx* c, int32_t n, const int32_t* ids, int32_t n_frames, const void* d_input,
+                       float* d_out, int32_t* h_emitted) {
+  if (!c) return CAC_EINVAL;
+  const Dims& d = c->d;
+  int rc = check_ids(c, n, ids, true);
+  if (rc) return rc;
+  if (d.lookahead) {
+    if (n_frames != d.ne) return c->fail(CAC_EINVAL, "the lookahead variant takes n_emit frames per push");
+  } else if (d.fe) {
+    if (n_frames != 2) return c->fail(CAC_EINVAL, "with the front end a push is one 16-frame mel chunk (2 frames)");
+  } else if (n_frames < d.c || n_frames > d.npush || n_frames % d.c) {
+    return c->fail(CAC_EINVAL, "n_frames must be a multiple of att_chunk in [att_chunk, max_push_frames]");
+  }
+  if (!d_input || !d_out) return c->fail(CAC_EINVAL, "input or output pointer is NULL");
+
+  // host bookkeeping decides who runs a pass (lookahead: streams whose pending frames reach
+  // n_emit + n_lookahead after this push)
+  std::vector<int32_t> cids, cidx;
+  if (d.lookahead) {
+    for (int i = 0; i < n; ++i)
+      if (c->hpend[ids[i]] + d.ne >= d.nc) { cids.push_back(ids[i]); cidx.push_back(i); }
+  }
+  const int emitted = d.lookahead ? (cids.empty() ? 0 : d.ne) : n_frames;
+  auto commit = [&]() {
+    for (int i = 0; i < n; ++i) {
+      const int id = ids[i];
+      if (d.lookahead) c->hpend[id] += d.ne;
+      else c->hpos[id] += n_frames;
+      if (h_emitted) h_emitted[i] = 0;
+    }
+    if (d.lookahead) {
+      for (size_t j = 0; j < cids.size(); ++j) {
+        c->hpos[cids[j]] += d.ne;
+        c->hpend[cids[j]] -= d.ne;
+        if (h_emitted) h_emitted[cidx[j]] = d.ne;
+      }
+    } else if (h_emitted) {
+      for (int i = 0; i < n; ++i) h_emitted[i] = n_frames;
+    }
+  };
+  if (c->dry) { commit(); return c->fail(CAC_ENODEV, "dry-run context: no device work"); }
+
+  Launcher L;
+  L.stream = c->stream;
+  L.err = upload(c, c->dev_ids, c->lay.ids, ids, n);
+  const int32_t* dids = c->P<int32_t>(c->lay.ids);
+  int32_t* dpos = c->P<int32_t>(c->lay.pos);
+  int32_t* dpend = c->P<int32_t>(c->lay.pend);
+  if (!d.lookahead) {
+    CallView cv{dids, dpos, n_frames, n};
+    const int M = n * n_frames;
+    if (d.fe) {
+      FeWindowArgs fw{cv, d_input, c->ws + c->lay.tail, c->ws + c->lay.win, d.bins, d.tail, d.mpc};
+      launch_fe_window(L, fw, d.dt);
+      const int wrows = d.tail + d.mpc;
+      struct { int rows, neg; size_t in, out; int K; RowMap m; } st3[3] = {
+          {11, 6, c->lay.win, c->lay.fe1, 3 * d.bins, RowMap{11, wrows * d.bins, 2 * d.bins}},
+          {5, 2, c->lay.fe1, c->lay.fe2, 3 * d.D, RowMap{5, 11 * d.D, 2 * d.D}},
+          {2, 0, c->lay.fe2, c->lay.x, 3 * d.D, RowMap{2, 5 * d.D, 2 * d.D}}};
+      for (int i = 0; i < 3; ++i) {
+        EpiArgs e{};
+        e.cv = cv; e.bias = c->P<float>(c->lay.fe_b[i]);
+        if (i < 2) { e.kind = EPI_RELU_FE; e.out = c->ws + st3[i].out; e.ldo = d.D; e.fe_rows_per_stream = st3[i].rows; e.fe_neg_rows = st3[i].neg; }
+        else { e.kind = EPI_F32; e.out = c->ws + c->lay.x; e.ldo = d.D; }
+        GemmArgs g{};
+        g.M = n * st3[i].rows; g.N = d.D; g.K = st3[i].K; g.A = c->ws + st3[i].in; g.amap = st3[i].m;
+        g.W = c->ws + c->lay.fe_w[i]; g.epi = e;
+        launch_gemm(L, g, d.dt, 0);
+      }
+    } else {
+      InputArgs ia{d_input, c->P<float>(c->lay.x), M, d.D};
+      launch_input(L, ia, d.dt);
+    }
+    Pass ps{c, L, cv, M};
+    ps.layers();
+    ps.joint(d_out, M, RowMap{INT_MAX, 0, d.D}, nullptr, 1, 0);
+    AdvanceArgs ad{dids, dpos, dpend, n, n_frames, 0};
+    launch_advance(L, ad);
+  } else {
+    CallView pv{dids, dpos, d.ne, n};
+    LaStoreArgs ls{pv, dpend, d_input, c->ws + c->lay.x0, d.D, d.Rx};
+    launch_la_store(L, ls, d.dt);
+    AdvanceArgs a1{dids, dpos, dpend, n, 0, d.ne};
+    launch_advance(L, a1);
+    const int nC = (int)cids.size();
+    if (nC > 0) {
+      if (L.err == hipSuccess) L.err = upload(c, c->dev_cids, c->lay.cids, cids.data(), nC);
+      if (L.err == hipSuccess) L.err = upload(c, c->dev_cidx, c->lay.cidx, cidx.data(), nC);
+      const int32_t* dcids = c->P<int32_t>(c->lay.cids);
+      CallView cv{dcids, dpos, d.nc, nC};
+      LaGatherArgs lg{cv, c->ws + c->lay.x0, c->P<float>(c->lay.x), d.D, d.Rx};
+      launch_la_gather(L, lg, d.dt);
+      Pass ps{c, L, cv, nC * d.nc};
+      ps.layers();
+      ps.joint(d_out, nC * d.ne, RowMap{d.ne, d.nc * d.D, d.D}, c->P<int32_t>(c->lay.cidx), d.ne, d.ne);
+      AdvanceArgs a2{dcids, dpos, dpend, nC, d.ne, -d.ne};
+      launch_advance(L, a2);
+    }
+  }
+  rc = finish(c, L, emitted);
+  if (rc >= 0) commit();
+  return rc;
+}
+
+int32_t cac_reset_stream(cac_ctx* c, int32_t n, const int32_t* ids) {
+  if (!c) return CAC_EINVAL;
+  int rc = check_ids(c, n, ids, false);
+  if (rc) return rc;
+  if (!c->dry) {
+    Launcher L;
+    L.stream = c->stream;
+    L.err = hipMemcpyAsync(c->ws + c->lay.sids, ids, (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+    StateArgs sa = state_args(c, n);
+    launch_state(L, sa, 0);
+    rc = finish(c, L, n);
+    if (rc < 0) return rc;
+  }
+  for (int i = 0; i < n; ++i) { c->hpos[ids[i]] = 0; c->hpend[ids[i]] = 0; c->flushed[ids[i]] = 0; }
+  return c->dry ? c->fail(CAC_ENODEV, "dry-run context: no device work") : n;
+}
+
+int32_t cac_flush(cac_ctx* c, int32_t n, const int32_t* ids, float* d_out, int32_t* h_frames_out) {
+  if (!c) return CAC_EINVAL;
+  const Dims& d = c->d;
+  int rc = check_ids(c, n, ids, true);
+  if (rc) return rc;
+  int maxm = 0;
+  if (d.lookahead)
+    for (int i = 0; i < n; ++i) maxm = std::max(maxm, c->hpend[ids[i]]);
+  if (maxm > 0 && !d_out) return c->fail(CAC_EINVAL, "output pointer is NULL");
+  auto commit = [&]() {
+    for (int i = 0; i < n; ++i) {
+      const int id = ids[i];
+      if (h_frames_out) h_frames_out[i] = d.lookahead ? c->hpend[id] : 0;
+      if (d.lookahead) { c->hpos[id] += c->hpend[id]; c->hpend[id] = 0; }
+      c->flushed[id] = 1;
+    }
+  };
+  if (c->dry || maxm == 0) {
+    commit();
+    return c->dry ? c->fail(CAC_ENODEV, "dry-run context: no device work") : 0;
+  }
+  Launcher L;
+  L.stream = c->stream;
+  // one final pass per distinct pending count; pending frames see keys up to their own end
+  for (int m = 1; m <= d.nla && L.err == hipSuccess; ++m) {
+    std::vector<int32_t> cids, cidx;
+    for (int i = 0; i < n; ++i)
+      if (c->hpend[ids[i]] == m) { cids.push_back(ids[i]); cidx.push_back(i); }
+    if (cids.empty()) continue;
+    const int nC = (int)cids.size();
+    L.err = upload(c, c->dev_cids, c->lay.cids, cids.data(), nC);
+    if (L.err == hipSuccess) L.err = upload(c, c->dev_cidx, c->lay.cidx, cidx.data(), nC);
+    const int32_t* dcids = c->P<int32_t>(c->lay.cids);
+    int32_t* dpos = c->P<int32_t>(c->lay.pos);
+    CallView cv{dcids, dpos, m, nC};
+    LaGatherArgs lg{cv, c->ws + c->lay.x0, c->P<float>(c->lay.x), d.D, d.Rx};
+    launch_la_gather(L, lg, d.dt);
+    Pass ps{c, L, cv, nC * m};
+    ps.layers();
+    ps.joint(d_out, nC * m, RowMap{INT_MAX, 0, d.D}, c->P<int32_t>(c->lay.cidx), m, d.nla);
+    AdvanceArgs ad{dcids, dpos, c->P<int32_t>(c->lay.pend), nC, m, -m};
+    launch_advance(L, ad);
+    // the cached id lists must not be reused by a later push with stale contents
+  }
+  rc = finish(c, L, maxm);
+  if (rc >= 0) commit();
+  return rc;
+}
+
+int32_t cac_export_state(cac_ctx* c, int32_t n, const int32_t* ids, int32_t* h_pos, int32_t* h_pending, float* d_state) {
+  if (!c) return CAC_EINVAL;
+  int rc = check_ids(c, n, ids, false);
+  if (rc) return rc;
+  if (!h_pos || !d_state) return c->fail(CAC_EINVAL, "position or state pointer is NULL");
+  if (c->d.lookahead && !h_pending) return c->fail(CAC_EINVAL, "pending pointer is NULL");
+  std::vector<int32_t> pos(n), pend(n);
+  for (int i = 0; i < n; ++i) { pos[i] = c->hpos[ids[i]]; pend[i] = c->hpend[ids[i]]; }
+  if (c->dry) return c->fail(CAC_ENODEV, "dry-run context: no device work");
+  Launcher L;
+  L.stream = c->stream;
+  L.err = hipMemcpyAsync(c->ws + c->lay.sids, ids, (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  if (L.err == hipSuccess) L.err = hipMemcpyAsync(c->ws + c->lay.spos, pos.data(), (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  if (L.err == hipSuccess) L.err = hipMemcpyAsync(c->ws + c->lay.spend, pend.data(), (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  StateArgs sa = state_args(c, n);
+  sa.blob = d_state;
+  launch_state(L, sa, 2);
+  if (L.err == hipSuccess) L.err = hipStreamSynchronize(c->stream);
+  rc = finish(c, L, n);
+  if (rc < 0) return rc;
+  for (int i = 0; i < n; ++i) { h_pos[i] = pos[i]; if (h_pending) h_pending[i] = pend[i]; }
+  return n;
+}
+
+int32_t cac_import_state(cac_ctx* c, int32_t n, const int32_t* ids, const int32_t* h_pos, const int32_t* h_pending, const float* d_state) {
+  if (!c) return CAC_EINVAL;
+  const Dims& d = c->d;
+  int rc = check_ids(c, n, ids, false);
+  if (rc) return rc;
+  if (!h_pos || !d_state) return c->fail(CAC_EINVAL, "position or state pointer is NULL");
+  std::vector<int32_t> pend(n, 0);
+  for (int i = 0; i < n; ++i) {
+    if (h_pos[i] < 0) return c->fail(CAC_ESTATE, "negative stream position");
+    if (!d.lookahead && h_pos[i] % d.c) return c->fail(CAC_ESTATE, "stream position off the attention chunk grid");
+    if (d.lookahead) {
+      if (!h_pending) return c->fail(CAC_EINVAL, "pending pointer is NULL");
+      if (h_pending[i] < 0 || h_pending[i] > d.nla) return c->fail(CAC_ESTATE, "pending count out of [0, n_lookahead]");
+      pend[i] = h_pending[i];
+    }
+  }
+  if (c->dry) return c->fail(CAC_ENODEV, "dry-run context: no device work");
+  Launcher L;
+  L.stream = c->stream;
+  L.err = hipMemcpyAsync(c->ws + c->lay.sids, ids, (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  if (L.err == hipSuccess) L.err = hipMemcpyAsync(c->ws + c->lay.spos, h_pos, (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  if (L.err == hipSuccess) L.err = hipMemcpyAsync(c->ws + c->lay.spend, pend.data(), (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  StateArgs sa = state_args(c, n);
+  sa.blob = const_cast<float*>(d_state);
+  launch_state(L, sa, 0);
+  launch_state(L, sa, 1);
+  if (L.err == hipSuccess) L.err = hipStreamSynchronize(c->stream);
+  rc = finish(c, L, n);
+  if (rc < 0) return rc;
+  for (int i = 0; i < n; ++i) { c->hpos[ids[i]] = h_pos[i]; c->hpend[ids[i]] = pend[i]; c->flushed[ids[i]] = 0; }
+  return n;
+}
+
+int32_t cac_stream_info(const cac_ctx* c, int32_t id, int32_t* pos, int32_t* pending, int32_t* flushed) {
+  if (!c || id < 0 || id >= c->d.S) return CAC_EINVAL;
+  if (pos) *pos = c->hpos[id];
+  if (pending) *pending = c->hpend[id];
+  if (flushed) *flushed = c->flushed[id];
+  return CAC_OK;
+}
+
+int32_t cac_set_stream(cac_ctx* c, void* s) {
+  if (!c) return CAC_EINVAL;
+  c->stream = (hipStream_t)s;
+  return CAC_OK;
+}
+
+int32_t cac_synchronize(cac_ctx* c) {
+  if (!c) return CAC_EINVAL;
+  if (c->dry) return CAC_OK;
+  hipError_t e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("device error: ") + hipGetErrorString(e));
+  return CAC_OK;
+}
+
+int32_t cac_destroy(cac_ctx* c) {
+  delete c;
+  return CAC_OK;
+}
+
+int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t K, const void* d_A, const void* d_W,
+                      const float* d_bias, float* d_C, void* hip_stream) {
+  if (dtype != CAC_F32 && dtype != CAC_BF16) return CAC_EINVAL;
+  if (M < 1 || N < 1 || K < 1 || !d_A || !d_W || !d_C) return CAC_EINVAL;
+  if (path < 0 || path > 2 || (path == 2 && dtype != CAC_BF16)) return CAC_EINVAL;
+  if (dtype == CAC_BF16 && path != 1 && K % 32) return CAC_EINVAL;  // MFMA tiles step K by 32
+  if ((size_t)8 * K * 4 > 160 * 1024 && path != 2) return CAC_EINVAL;
+  kernels_init();
+  Launcher L;
+  L.stream = (hipStream_t)hip_stream;
+  EpiArgs e{};
+  e.kind = EPI_F32; e.bias = d_bias; e.out = d_C; e.ldo = N;
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K; g.A = d_A; g.W = d_W; g.amap = RowMap{INT_MAX, 0, K}; g.epi = e;
+  launch_gemm(L, g, dtype, path);
+  return L.err == hipSuccess ? CAC_OK : CAC_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+// Shared device/host definitions of the chunk-step library: element types, kernel argument
+// structs (every kernel takes exactly one POD struct, so a launch sequence can be recorded as
+// HIP graph kernel nodes and re-pointed later), and the launch wrappers kernels.hip exports.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t bf16_t;  // bfloat16 storage
+
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+
+// ------------------------------------------------------------------------ element helpers
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);  // keep NaN a NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                         // nearest, ties to even
+  return (bf16_t)(u >> 16);
+}
+template <typename T> __device__ __forceinline__ float ld(const T* p);
+template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+template <typename T> __device__ __forceinline__ void st(T* p, float v);
+template <> __device__ __forceinline__ void st<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st<bf16_t>(bf16_t* p, float v) { *p = f2bf(v); }
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// ------------------------------------------------------------------------ row addressing
+// Row m of a logical [M][K] operand lives at base + (m / group) * group_stride +
+// (m % group) * row_stride elements. Plain row-major: group = M (or any value > M),
+// row_stride = lda. Used for strided im2col views and for picking emitted rows.
+struct RowMap {
+  int group, group_stride, row_stride;
+  __host__ __device__ __forceinline__ long off(int m) const {
+    return (long)(m / group) * group_stride + (long)(m % group) * row_stride;
+  }
+};
+
+// ------------------------------------------------------------------------ per-call view
+// What a kernel needs to know about the streams of the current call: row m of the call's
+// activations belongs to call slot s = m / nf (stream id ids[s]) and is that stream's frame
+// m % nf, at absolute position pos[ids[s]] + m % nf.
+struct CallView {
+  const int32_t* ids;  // [n_streams] stream ids of this call (device)
+  const int32_t* pos;  // [max_streams] stream positions (device)
+  int nf;              // frames per stream in this call
+  int n_streams;
+};
+
+// ------------------------------------------------------------------------ epilogues
+enum EpiKind {
+  EPI_STORE = 0,   // out_t[m][n] = acc + b                       (compute dtype)
+  EPI_SILU = 1,    // out_t[m][n] = silu(acc + b)                 (compute dtype)
+  EPI_RELU_FE = 2, // out_t[m][n] = relu(acc + b), 0 for rows before the stream start
+  EPI_RESID = 3,   // x[m][n] += alpha * (acc + b)                (float32 residual)
+  EPI_F32 = 4,     // out_f[row_out(m)][n] = acc + b              (float32)
+  EPI_QKV = 5,     // q -> qbuf (f32); k, v -> ring slots of the row's position
+  EPI_GLU = 6,     // a*sigmoid(b) of GLU-packed column pairs -> conv ring slot
+};
+
+struct EpiArgs {
+  int kind;
+  const float* bias;  // [N] (may be null)
+  void* out;          // EPI_STORE/SILU/RELU_FE: compute dtype; EPI_RESID/F32: float
+  int ldo;
+  float alpha;
+  // EPI_F32 output row remap (lookahead emits a subset of rows): row_out = omap[m / ogroup] *
+  // ostride + m % ogroup when omap != null
+  const int32_t* omap;
+  int ogroup, ostride;
+  // EPI_RELU_FE: rows (s, j) with j < fe_neg_rows are zeroed for streams at position 0
+  int fe_rows_per_stream, fe_neg_rows;
+  // EPI_QKV / EPI_GLU
+  CallView cv;
+  float* qbuf;          // [M][D] float32
+  void* kring;          // [S][H][R][hd] of this layer (compute dtype)
+  void* vring;
+  void* cring;          // [S][Rc][D] of this layer (compute dtype)
+  int D, H, hd, R, Rc;
+};
+
+// ------------------------------------------------------------------------ kernel args
+struct GemmArgs {
+  int M, N, K;           // C[M][N] = A[M][K] . W[N][K]^T ; for EPI_GLU N counts packed columns
+  const void* A;         // compute dtype, or float32 when a_f32
+  RowMap amap;
+  const void* W;         // [N][K] compute dtype
+  int a_f32;             // A is float32: LayerNorm'ed (ln_g != null) and/or rounded to the
+  const float* ln_g;     // compute dtype before the product; the MFMA path first writes that
+  const float* ln_b;     // operand to a_scratch ([M][K], compute dtype)
+  void* a_scratch;
+  int upb;               // small-M kernel: output units (columns, or GLU channels) per block
+  EpiArgs epi;
+};
+
+struct LnArgs {
+  const float* x;  // [M][D]
+  void* y;         // [M][D] (compute dtype, or float32 when in place)
+  const float* g;
+  const float* b;
+  int M, D;
+  int out_f32;     // 1: y is float32
+};
+
+struct AttnArgs {
+  CallView cv;
+  const float* q;       // [M][D] float32 (q rows of the call)
+  const void* kring;    // layer base [S][H][R][hd]
+  const void* vring;
+  const float* posproj; // layer base [H][nrel][hd]
+  const float* pos_u;   // [H][hd]
+  const float* pos_v;
+  void* o;              // [M][D] compute dtype
+  int D, H, R, Lc, chunk, right, lookahead, rel_lo, nrel;
+  float scale;
+};
+
+struct DwArgs {
+  CallView cv;
+  const void* cring;   // layer base [S][Rc][D]
+  const float* w;      // [K][D] taps
+  const float* b;      // [D]
+  void* e;             // [M][D] compute dtype
+  int D, K, Rc;
+};
+
+struct InputArgs {      // x[m][c] = in[m][c] (float32 residual from compute dtype input)
+  const void* in;
+  float* x;
+  int M, D;
+};
+
+struct FeWindowArgs {   // win[s] = [tail(14) || mel_new(16)]; tail = last 14 of win
+  CallView cv;
+  const void* mel;      // [n][mel_per_chunk][bins]
+  void* tail;           // [S][mel_tail][bins]
+  void* win;            // [n][mel_tail + mel_per_chunk][bins]
+  int bins, mel_tail, mel_new;
+};
+
+struct CopyRowsArgs {    // out[row_out(m)][c] = x[amap(m) + c], row_out as in EPI_F32
+  const float* x;
+  RowMap amap;
+  float* out;
+  const int32_t* omap;
+  int ogroup, ostride, M, D;
+};
+
+struct CvtArgs {         // y[m][k] = bf16(x[amap(m) + k])
+  const float* x;
+  RowMap amap;
+  void* y;
+  int M, K;
+};
+
+struct AdvanceArgs {    // pos[ids[s]] += adv, pend[ids[s]] += dpend
+  const int32_t* ids;
+  int32_t* pos;
+  int32_t* pend;
+  int n, adv, dpend;
+};
+
+struct PosProjArgs {    // table[l][h][r][d] = sum_e PE(rel_lo + r, e) Wpos_l[e][h*hd + d]
+  const float* wpos;    // [L][D][D]
+  float* table;         // [L][H][nrel][hd]
+  int L, D, H, hd, rel_lo, nrel;
+};
+
+struct StateArgs {      // reset / import / export of whole streams
+  const int32_t* ids;   // [n]
+  const int32_t* hpos;  // [n] positions (import) ; out for export via pos array
+  const int32_t* hpend; // [n]
+  int32_t* pos;         // [S]
+  int32_t* pend;        // [S]
+  void* kring; void* vring; void* cring; void* tail; void* x0;  // whole state regions
+  float* blob;          // [n][state_floats]
+  int n, S, L, D, H, hd, R, Rc, Lc, Kc, tail_rows, bins, nla, Rx;
+  long state_floats;
+  int dtype, poison;
+};
+
+struct LaStoreArgs {    // lookahead: append new frames to each stream's pending ring
+  CallView cv;          // call streams; nf = frames per push
+  const int32_t* pend;
+  const void* in;       // [n][nf][D]
+  void* x0;             // [S][Rx][D]
+  int D, Rx;
+};
+struct LaGatherArgs {   // lookahead: x rows of a pass from the pending ring
+  CallView cv;          // compute streams; nf = frames per pass
+  const void* x0;
+  float* x;
+  int D, Rx;
+};
+
+// ------------------------------------------------------------------------ launcher
+// Kernels are launched through a Launcher: either straight onto a stream, or appended to a
+// HIP graph as a chain of kernel nodes (node handles are kept so pointer arguments can be
+// re-pointed before each replay).
+struct Launcher {
+  hipStream_t stream = nullptr;
+  hipGraph_t graph = nullptr;        // non-null: record instead of launch
+  hipGraphNode_t last = nullptr;
+  hipGraphNode_t last_node = nullptr;  // node of the most recent launch (record mode)
+  hipError_t err = hipSuccess;
+  void launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* args);
+};
+
+// ------------------------------------------------------------------------ wrappers
+void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path);
+void launch_ln(Launcher& L, const LnArgs& a, int dtype);
+void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd);
+void launch_dwconv(Launcher& L, const DwArgs& a, int dtype);
+void launch_input(Launcher& L, const InputArgs& a, int dtype);
+void launch_copy_rows(Launcher& L, const CopyRowsArgs& a);
+void kernels_init();
+void launch_fe_window(Launcher& L, const FeWindowArgs& a, int dtype);
+void launch_advance(Launcher& L, const AdvanceArgs& a);
+void launch_posproj(Launcher& L, const PosProjArgs& a);
+void launch_state(Launcher& L, const StateArgs& a, int op);  // 0 reset, 1 import, 2 export
+void launch_la_store(Launcher& L, const LaStoreArgs& a, int dtype);
+void launch_la_gather(Launcher& L, const LaGatherArgs& a, int dtype);
+size_t attention_shmem(int nf, int nk_max, int nrel, int hd);

@@ -1,0 +1,183 @@
+/* cac.h — C ABI of the cache-aware streaming Conformer chunk step on MI355X (gfx950).
+ *
+ * What one push computes (per stream, per chunk of n subsampled frames), following
+ * "True streaming encode — implementation spec" (fluidaudio-web STREAMING.md), "Per-chunk flow"
+ * steps 2-4, with the state of its "State" section:
+ *   [optional front end: 3 causal stride-2 k=3 convs over [melTail || 16 new mel frames]]
+ *   for each of n_layers Conformer blocks:
+ *     x += 1/2 FF1(x); x += MHSA_relpos(LN(x)) against the layer's K/V cache (<= att_left rows)
+ *     under the chunked-causal mask on absolute positions; x += ConvModule(x) with the layer's
+ *     depthwise cache (dw_kernel-1 columns of GLU output); x += 1/2 FF2(x); x = LN_out(x)
+ *   z = x Wj + bj  (the encoder-side joint projection, computed once per frame: "Fast
+ *                   Accuracy-Preserving RNNT Beam Search on Apple Silicon", "Delete Repeated
+ *                   Projection Work First")
+ * The lookahead variant (same spec, "Status", Nemotron bullet) computes n_emit + n_lookahead
+ * frames per pass with right context att_right, emits n_emit and caches only those.
+ *
+ * Conventions
+ *   - Every function returns int32: >= 0 on success (a count where stated), < 0 an error code.
+ *   - "d_" pointers are device memory (hipMalloc'd by the caller), "h_" pointers host memory.
+ *   - All device work is enqueued on the HIP stream given at create time (or by
+ *     cac_set_stream); no call synchronises the host except where stated. Outputs are valid
+ *     once that stream has been synchronised.
+ *   - The library never allocates device memory: the caller provides one workspace of
+ *     cac_workspace_bytes() bytes that holds the repacked weights, every stream's state and
+ *     all activations. The library keeps a pointer to it until cac_destroy.
+ *   - Arguments are validated on the host before any device work; on error nothing is
+ *     enqueued and the context is unchanged. cac_last_error() then describes the failure.
+ *   - One context is used by one host thread at a time; there is no internal locking.
+ */
+#ifndef CAC_H
+#define CAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* error codes */
+#define CAC_OK 0
+#define CAC_EINVAL (-1)  /* bad config or argument: null pointer, id out of range, duplicate id
+                            in one call, n not a multiple of att_chunk, too many frames */
+#define CAC_ESTATE (-2)  /* stream state forbids the call: push to a flushed stream (reset it
+                            first), state import that does not fit the config */
+#define CAC_ENOMEM (-3)  /* workspace smaller than cac_workspace_bytes() */
+#define CAC_EHIP (-4)    /* a HIP runtime call or a kernel launch failed */
+#define CAC_ENODEV (-5)  /* the context was created with CAC_FLAG_DRY_RUN: no device work */
+
+/* compute dtype of GEMM operands and caches (residual stream, LayerNorm, softmax, GLU and the
+   depthwise conv always run in fp32) */
+#define CAC_F32 0
+#define CAC_BF16 1
+
+/* config flags */
+#define CAC_FLAG_DRY_RUN 1 /* host-only context: validation and stream bookkeeping, no device
+                              calls (workspace may be NULL); pushes return CAC_ENODEV after
+                              validating and updating host bookkeeping */
+#define CAC_FLAG_POISON 2  /* reset fills cache slots with NaN instead of 0: a read of any slot
+                              that does not hold a valid row shows up as NaN in the outputs */
+
+typedef struct cac_ctx cac_ctx;
+
+typedef struct {
+  int32_t n_layers;      /* Conformer blocks (17; the model card's "Config" table) */
+  int32_t d_model;       /* D (512), a multiple of 64 */
+  int32_t n_heads;       /* H (8); head_dim = D/H must be 16, 32 or 64 */
+  int32_t d_ff;          /* F (2048), a multiple of 64 */
+  int32_t dw_kernel;     /* depthwise kernel width (9); cache of dw_kernel-1 columns, <= 16 */
+  int32_t att_left;      /* Lc: left attention context = K/V cache rows (70) */
+  int32_t att_chunk;     /* c: attention chunk in frames (2); pushes are multiples of c */
+  int32_t att_right;     /* right context of the lookahead variant (3), else 0 */
+  int32_t n_emit;        /* frames emitted per pass (lookahead variant), else frames per push */
+  int32_t n_lookahead;   /* provisional frames recomputed every pass (8), 0 = exact streaming */
+  int32_t joint_dim;     /* P (640); 0 = no joint projection, outputs are the hidden rows */
+  int32_t frontend;      /* 1 = inputs are log-mel chunks run through the conv front end */
+  int32_t mel_bins;      /* 128 */
+  int32_t mel_per_chunk; /* 16 mel frames -> 2 subsampled frames */
+  int32_t mel_tail;      /* 14 */
+  int32_t dtype;         /* CAC_F32 or CAC_BF16 */
+  int32_t max_streams;   /* stream ids are 0 .. max_streams-1 */
+  int32_t max_push_frames; /* most frames one push may carry (exact variant), <= 16 */
+  int32_t flags;         /* CAC_FLAG_* */
+} cac_config;
+
+/* Number of float parameters cac_create_streams expects, in this order (all float32, host):
+ *   for each layer l = 0 .. n_layers-1:
+ *     ff1: ln_g[D] ln_b[D] w1[D][F] b1[F] w2[F][D] b2[D]
+ *     att: ln_g[D] ln_b[D] wq[D][D] bq[D] wk[D][D] bk[D] wv[D][D] bv[D] wo[D][D] bo[D]
+ *          pos_u[H][hd] pos_v[H][hd] wpos[D][D]
+ *     conv: ln_g[D] ln_b[D] pw1[D][2D] pw1_b[2D] dw[D][dw_kernel] dw_b[D] pw2[D][D] pw2_b[D]
+ *     ff2: ln_g[D] ln_b[D] w1[D][F] b1[F] w2[F][D] b2[D]
+ *     out: ln_g[D] ln_b[D]
+ *   if joint_dim: joint w[D][P] b[P]
+ *   if frontend: c1 w[D][mel_bins][3] b[D]; c2 w[D][D][3] b[D]; c3 w[D][D][3] b[D]
+ * Matrices are [in][out] row-major (y = x W + b); conv weights are [out][in][tap].
+ * Returns 0 for an invalid config. */
+size_t cac_param_count(const cac_config* cfg);
+
+/* Bytes of device workspace a context needs (weights + state of max_streams streams +
+ * activations for max_streams * frames-per-pass rows). Returns 0 for an invalid config. */
+size_t cac_workspace_bytes(const cac_config* cfg);
+
+/* Floats per stream in the canonical state blob of cac_export_state / cac_import_state:
+ *   K[n_layers][att_left][D], V[n_layers][att_left][D]   row r = position pos-att_left+r
+ *   conv[n_layers][dw_kernel-1][D]                       column j = position pos-(K-1)+j
+ *   mel_tail[mel_tail][mel_bins]                         (frontend only)
+ *   x0[n_lookahead][D]  pending layer-0 inputs, row j = position pos+j (lookahead only)
+ * Rows of positions before 0 are ignored on import and written as 0 on export. */
+size_t cac_state_floats(const cac_config* cfg);
+
+/* Validate cfg, repack the float32 host parameters (h_params, cac_param_count floats) into the
+ * workspace in the compute layout (bf16 rounding to nearest even for CAC_BF16), compute each
+ * layer's projected position table (streaming spec step 3: "posProj rows precomputed per
+ * layer"), reset every stream to position 0, and return the context in *out. hip_stream is a
+ * hipStream_t (NULL = default stream). Synchronises hip_stream before returning. The caller may
+ * free h_params afterwards; d_workspace must stay allocated until cac_destroy. */
+int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t n_params,
+                           void* d_workspace, size_t ws_bytes, void* hip_stream, cac_ctx** out);
+
+/* Push one chunk for n_streams streams (ids in h_stream_ids, distinct, in [0, max_streams)).
+ *   exact variant: d_input is [n_streams][n_frames][D] (or [n_streams][mel_per_chunk][mel_bins]
+ *     log-mel with the front end, n_frames = mel_per_chunk/8), in the compute dtype (float32 or
+ *     bf16); n_frames a multiple of att_chunk, <= max_push_frames (front end: exactly 2).
+ *     d_out receives [n_streams][n_frames][P] float32 (P = joint_dim, or D without joint).
+ *   lookahead variant: n_frames must equal n_emit; the frames join each stream's pending
+ *     inputs; streams with n_emit + n_lookahead pending run one pass and emit n_emit frames
+ *     into d_out rows [i][0 .. n_emit) ; streams still warming up emit nothing.
+ * h_emitted (optional, n_streams int32) receives each stream's emitted frame count.
+ * Returns the largest per-stream emitted count. Asynchronous (see Conventions). */
+int32_t cac_push_chunk(cac_ctx* ctx, int32_t n_streams, const int32_t* h_stream_ids,
+                       int32_t n_frames, const void* d_input, float* d_out, int32_t* h_emitted);
+
+/* Return streams to the fresh state (streaming spec, "Engine + mic wiring": reset zeroes the
+ * caches, mel tail and position). Returns n. */
+int32_t cac_reset_stream(cac_ctx* ctx, int32_t n, const int32_t* h_stream_ids);
+
+/* End streams (streaming spec, "Status": padBottom at flush only). The lookahead variant runs a
+ * final pass over each stream's pending frames and writes all of them to d_out
+ * ([n][n_lookahead][P], first h_frames_out[i] rows of stream i); the exact variant has nothing
+ * left to emit. Flushed streams reject pushes until reset. Returns the largest frame count. */
+int32_t cac_flush(cac_ctx* ctx, int32_t n, const int32_t* h_stream_ids, float* d_out,
+                  int32_t* h_frames_out);
+
+/* Copy the state of n streams into / from the canonical float32 layout (cac_state_floats per
+ * stream, d_state is [n][cac_state_floats] device memory). h_pos: stream positions (frames
+ * emitted); h_pending: pending layer-0 inputs of the lookahead variant (ignored otherwise,
+ * may be NULL then). Import requires 0 <= pending <= n_lookahead. */
+int32_t cac_export_state(cac_ctx* ctx, int32_t n, const int32_t* h_stream_ids, int32_t* h_pos,
+                         int32_t* h_pending, float* d_state);
+int32_t cac_import_state(cac_ctx* ctx, int32_t n, const int32_t* h_stream_ids,
+                         const int32_t* h_pos, const int32_t* h_pending, const float* d_state);
+
+/* Host view of a stream: position, pending frames, flushed flag (no device access). */
+int32_t cac_stream_info(const cac_ctx* ctx, int32_t stream_id, int32_t* pos, int32_t* pending,
+                        int32_t* flushed);
+
+/* Change the HIP stream later calls enqueue on. */
+int32_t cac_set_stream(cac_ctx* ctx, void* hip_stream);
+
+/* Synchronise the context's stream and report any asynchronous device error (CAC_EHIP). */
+int32_t cac_synchronize(cac_ctx* ctx);
+
+/* Free the host context (the workspace stays the caller's). Accepts NULL. */
+int32_t cac_destroy(cac_ctx* ctx);
+
+/* Description of the last error on ctx; with ctx == NULL, of the last failed
+ * cac_create_streams on this thread. Never NULL. */
+const char* cac_last_error(const cac_ctx* ctx);
+
+/* Test-only: C[M][N] (float32) = A[M][K] W[N][K]^T + bias through the library's dense kernels
+ * (dtype selects bf16 or float32 operands for A and W; bias may be NULL). path: 0 = the
+ * library's own choice, 1 = the small-M kernel, 2 = the MFMA tile kernel (bf16 only).
+ * Enqueued on hip_stream. */
+int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t K,
+                      const void* d_A, const void* d_W, const float* d_bias, float* d_C,
+                      void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CAC_H */

@@ -24,11 +24,12 @@ from .configs import EncConfig
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
-    a = np.ascontiguousarray(x, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+    """Round finite float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    a = np.array(x, dtype=np.float32, copy=True, order="C")
+    u = a.view(np.uint32)
+    u += np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    u &= np.uint32(0xFFFF0000)
+    return a
 
 
 def _rng(cfg: EncConfig, name: str) -> np.random.Generator:
@@ -37,6 +38,12 @@ def _rng(cfg: EncConfig, name: str) -> np.random.Generator:
 
 def _draw(cfg: EncConfig, name: str, shape, std: float, mean: float = 0.0) -> np.ndarray:
     x = (mean + std * _rng(cfg, name).standard_normal(shape)).astype(np.float32)
+    return bf16_round(x) if cfg.dtype == "bf16" else x
+
+
+def _draw_unit(cfg: EncConfig, name: str, shape) -> np.ndarray:
+    """N(0,1) drawn directly in float32 (inputs and injected states, the bulk of the data)."""
+    x = _rng(cfg, name).standard_normal(shape, dtype=np.float32)
     return bf16_round(x) if cfg.dtype == "bf16" else x
 
 
@@ -108,9 +115,9 @@ def make_inputs(cfg: EncConfig, stream: int, chunks: int | None = None) -> np.nd
     [chunks, mel_per_chunk, mel_bins] log-mel frames when the front end is on."""
     n = cfg.chunks
     if cfg.frontend:
-        x = _draw(cfg, f"input.s{stream}", (n, cfg.mel_per_chunk, cfg.mel_bins), 1.0)
+        x = _draw_unit(cfg, f"input.s{stream}", (n, cfg.mel_per_chunk, cfg.mel_bins))
     else:
-        x = _draw(cfg, f"input.s{stream}", (n, cfg.n_emit, cfg.d_model), 1.0)
+        x = _draw_unit(cfg, f"input.s{stream}", (n, cfg.n_emit, cfg.d_model))
     return x if chunks is None else x[:chunks]
 
 
@@ -136,19 +143,19 @@ def make_state(cfg: EncConfig, stream: int) -> dict:
     fill = c * int(g.integers(0, Lc // c + 1))
     pos = fill if fill < Lc else Lc + c * int(g.integers(0, 5001))
     fill = min(pos, Lc)
-    k = _draw(cfg, f"state.s{stream}.k", (L, Lc, D), 1.0)
-    v = _draw(cfg, f"state.s{stream}.v", (L, Lc, D), 1.0)
+    k = _draw_unit(cfg, f"state.s{stream}.k", (L, Lc, D))
+    v = _draw_unit(cfg, f"state.s{stream}.v", (L, Lc, D))
     k[:, : Lc - fill] = 0.0
     v[:, : Lc - fill] = 0.0
-    conv = _draw(cfg, f"state.s{stream}.conv", (L, Kc, D), 1.0)
+    conv = _draw_unit(cfg, f"state.s{stream}.conv", (L, Kc, D))
     nneg = max(0, Kc - pos)
     conv[:, :nneg] = 0.0
     st = {"pos": pos, "fill": fill, "k": k, "v": v, "conv": conv, "mel_tail": None, "x0_tail": None}
     if cfg.frontend:
-        mt = _draw(cfg, f"state.s{stream}.mel", (cfg.mel_tail, cfg.mel_bins), 1.0)
+        mt = _draw_unit(cfg, f"state.s{stream}.mel", (cfg.mel_tail, cfg.mel_bins))
         if pos == 0:
             mt[:] = 0.0
         st["mel_tail"] = mt
     if cfg.n_lookahead:
-        st["x0_tail"] = _draw(cfg, f"state.s{stream}.x0", (cfg.n_lookahead, D), 1.0)
+        st["x0_tail"] = _draw_unit(cfg, f"state.s{stream}.x0", (cfg.n_lookahead, D))
     return st

@@ -1,0 +1,168 @@
+"""Host-side tests of the C ABI: the library loads and exports every declared symbol, the
+parameter/state layouts agree with the binding, and argument validation and stream
+bookkeeping behave as the header states. No device work: dry-run contexts only."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import cache_aware_conformer_amd as cac
+from cache_aware_conformer_amd.binding import CAC_EINVAL, CAC_ENODEV, CAC_ENOMEM, CAC_ESTATE, CacError, cac_config
+from synth import C1, C2, C3, C4, C5, make_weights, weight_names
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cac.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cac_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = cac.load()
+    names = header_functions()
+    assert len(names) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", cac.binding.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (cac_[a-z_]+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert set(names) == set(cac.binding.SIGNATURES)
+
+
+@pytest.mark.parametrize("cfg", [C1, C2, C3, C4, C5], ids=lambda c: c.name)
+def test_param_and_state_layouts(cfg):
+    lib = cac.load()
+    c = cac.make_config(cfg)
+    n = lib.cac_param_count(C.byref(c))
+    assert n == sum(int(np.prod(s)) for _, s in cac.param_order(cfg))
+    # the generator and the binding name the same tensors in the same order
+    assert [nm for nm, _ in cac.param_order(cfg)] == [nm for nm, *_ in weight_names(cfg)]
+    L, Lc, D = cfg.n_layers, cfg.att_left, cfg.d_model
+    expect = 2 * L * Lc * D + L * (cfg.dw_kernel - 1) * D
+    expect += cfg.mel_tail * cfg.mel_bins if cfg.frontend else 0
+    expect += cfg.n_lookahead * D
+    assert lib.cac_state_floats(C.byref(c)) == expect
+    assert lib.cac_workspace_bytes(C.byref(c)) > 0
+
+
+@pytest.mark.parametrize("field,value", [("d_model", 100), ("n_heads", 3), ("d_ff", 100), ("dtype", 7),
+                                         ("max_streams", 0), ("att_chunk", 0), ("max_push_frames", 3),
+                                         ("att_right", 2), ("dw_kernel", 0), ("n_layers", 0)])
+def test_bad_config_rejected(field, value):
+    lib = cac.load()
+    c = cac.make_config(C1)
+    setattr(c, field, value)
+    assert lib.cac_param_count(C.byref(c)) == 0
+    assert lib.cac_workspace_bytes(C.byref(c)) == 0
+    ctx = C.c_void_p()
+    rc = lib.cac_create_streams(C.byref(c), None, 0, None, 0, None, C.byref(ctx))
+    assert rc == CAC_EINVAL and not ctx.value
+    assert lib.cac_last_error(None)
+
+
+def test_create_rejects_small_workspace_and_wrong_param_count():
+    lib = cac.load()
+    c = cac.make_config(C1)
+    flat = cac.pack_params(C1, make_weights(C1))
+    ctx = C.c_void_p()
+    fp = flat.ctypes.data_as(C.POINTER(C.c_float))
+    need = lib.cac_workspace_bytes(C.byref(c))
+    # fake (never touched) aligned address: the size check comes before any device call
+    assert lib.cac_create_streams(C.byref(c), fp, flat.size, C.c_void_p(1 << 20), need - 1, None, C.byref(ctx)) == CAC_ENOMEM
+    assert b"too small" in lib.cac_last_error(None)
+    assert lib.cac_create_streams(C.byref(c), fp, flat.size - 1, C.c_void_p(1 << 20), need, None, C.byref(ctx)) == CAC_EINVAL
+    assert lib.cac_create_streams(C.byref(c), fp, flat.size, C.c_void_p((1 << 20) + 4), need, None, C.byref(ctx)) == CAC_EINVAL
+
+
+def dry(cfg, streams=4):
+    return cac.StreamingEncoder(cfg, make_weights(cfg), max_streams=streams, flags=cac.CAC_FLAG_DRY_RUN)
+
+
+def push(enc, ids, n_frames):
+    ids_a = np.asarray(ids, dtype=np.int32)
+    em = np.zeros(len(ids_a), dtype=np.int32)
+    rc = enc.lib.cac_push_chunk(enc.ctx, len(ids_a), ids_a.ctypes.data_as(C.POINTER(C.c_int32)), n_frames,
+                                C.c_void_p(16), C.c_void_p(16), em.ctypes.data_as(C.POINTER(C.c_int32)))
+    return rc, em
+
+
+def test_push_validation_and_positions():
+    enc = dry(C1)
+    assert push(enc, [0, 1], 2)[0] == CAC_ENODEV          # validated, bookkept, no device
+    assert enc.stream_info(0).pos == 2 and enc.stream_info(2).pos == 0
+    assert push(enc, [0], 3)[0] == CAC_EINVAL             # off the chunk grid
+    assert push(enc, [0], 10)[0] == CAC_EINVAL            # beyond max_push_frames
+    assert push(enc, [4], 2)[0] == CAC_EINVAL             # unknown id
+    assert push(enc, [-1], 2)[0] == CAC_EINVAL
+    assert push(enc, [1, 1], 2)[0] == CAC_EINVAL          # duplicate id
+    assert b"twice" in enc.lib.cac_last_error(enc.ctx)
+    assert enc.stream_info(1).pos == 2                     # failed calls change nothing
+    assert push(enc, [3, 0], 4)[0] == CAC_ENODEV
+    assert enc.stream_info(0).pos == 6 and enc.stream_info(3).pos == 4
+    rc = enc.lib.cac_push_chunk(enc.ctx, 1, np.zeros(1, np.int32).ctypes.data_as(C.POINTER(C.c_int32)), 2, None, None, None)
+    assert rc == CAC_EINVAL
+
+
+def test_flush_then_push_needs_reset():
+    enc = dry(C1)
+    push(enc, [2], 2)
+    with pytest.raises(CacError) as e:
+        enc.flush([2])
+    assert e.value.code == CAC_ENODEV
+    assert enc.stream_info(2).flushed
+    assert push(enc, [2], 2)[0] == CAC_ESTATE
+    assert push(enc, [1, 2], 2)[0] == CAC_ESTATE
+    assert enc.stream_info(1).pos == 0
+    with pytest.raises(CacError):
+        enc.reset_stream([2])
+    info = enc.stream_info(2)
+    assert info.pos == 0 and not info.flushed
+    assert push(enc, [2], 2)[0] == CAC_ENODEV
+
+
+def test_lookahead_bookkeeping():
+    """Streams warm up until n_emit + n_lookahead frames are pending, then emit n_emit per
+    push; a flush emits what is pending."""
+    cfg = C5.replace(n_layers=1, streams=3)
+    enc = dry(cfg, streams=3)
+    seen = []
+    for k in range(6):
+        rc, em = push(enc, [0, 1] if k < 3 else [0, 1, 2], 2)
+        assert rc == CAC_ENODEV
+        seen.append(em.tolist())
+    assert [s[0] for s in seen] == [0, 0, 0, 0, 2, 2]
+    assert seen[5][2] == 0
+    assert push(enc, [0], 4)[0] == CAC_EINVAL   # the lookahead variant takes n_emit frames
+    i0, i2 = enc.stream_info(0), enc.stream_info(2)
+    assert (i0.pos, i0.pending) == (4, 8) and (i2.pos, i2.pending) == (0, 6)
+    frames = np.zeros(2, np.int32)
+    ids = np.array([0, 2], np.int32)
+    rc = enc.lib.cac_flush(enc.ctx, 2, ids.ctypes.data_as(C.POINTER(C.c_int32)), C.c_void_p(16),
+                           frames.ctypes.data_as(C.POINTER(C.c_int32)))
+    assert rc == CAC_ENODEV and frames.tolist() == [8, 6]
+    assert enc.stream_info(0).pos == 12 and enc.stream_info(2).pos == 6
+
+
+def test_frontend_push_is_one_mel_chunk():
+    enc = dry(C4.replace(n_layers=1, streams=2), streams=2)
+    assert push(enc, [0], 4)[0] == CAC_EINVAL
+    assert push(enc, [0], 2)[0] == CAC_ENODEV
+
+
+def test_import_validation():
+    enc = dry(C5.replace(n_layers=1, streams=2), streams=2)
+    ids = np.array([0], np.int32)
+    ip = lambda a: np.asarray(a, np.int32).ctypes.data_as(C.POINTER(C.c_int32))  # noqa: E731
+    lib = enc.lib
+    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), ip([9]), C.c_void_p(16)) == CAC_ESTATE
+    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([-2]), ip([8]), C.c_void_p(16)) == CAC_ESTATE
+    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), ip([8]), None) == CAC_EINVAL
+    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), ip([8]), C.c_void_p(16)) == CAC_ENODEV
+    enc2 = dry(C1)
+    assert lib.cac_import_state(enc2.ctx, 1, ip(ids), ip([3]), None, C.c_void_p(16)) == CAC_ESTATE
