@@ -1,0 +1,186 @@
+"""Throughput of the cache-aware streaming Conformer chunk step on one MI355X.
+
+A step is one push of one chunk for every stream of the workload through the whole path
+(front end if any, 17 blocks, joint projection), inputs already resident in HBM. The default
+workload is the 17-layer d=512 float32 encoder with one stream and 2 frames per chunk
+(1000 chunks). Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload C2|C3|C4|C5]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encoder frames/sec (streams×frames) per chunk step; % HBM or MFMA peak"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # dense bf16 MFMA
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="C2")
+    ap.add_argument("--profile-steps", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "cache_aware_conformer_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, launches_bytes: float):
+    """HBM bytes per launch from the committed counter summary of this kernel, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILES, "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(cfg, W, seconds: float):
+    """The float64 oracle's cached chunk step, timed on the host cores on a bounded prefix of the
+    same stream (streams are independent, so the rate scales to the workload)."""
+    from oracle import Oracle
+    from synth import make_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    orc = Oracle(cfg, W)
+    n_s = 1 if cfg.streams == 1 else min(cfg.streams, 8)
+    sts = [orc.new_state() for _ in range(n_s)]
+    xs = np.stack([make_inputs(cfg, s, cfg.chunks) for s in range(n_s)])
+    t0 = time.perf_counter()
+    chunks = 0
+    while chunks < cfg.chunks and (time.perf_counter() - t0 < seconds or chunks < 3):
+        orc.push(sts, xs[:, chunks].astype(np.float64))
+        chunks += 1
+    dt = time.perf_counter() - t0
+    frames = n_s * cfg.n_emit * chunks
+    return {"value": frames / dt, "unit": "frames/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{cfg.name}: {n_s} fresh stream(s) x first {chunks} chunks, float64 cached step, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the chunk step shards by stream with no "
+                                   "collectives, so N GPUs run N independent copies; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    from cache_aware_conformer_amd import StreamingEncoder
+    from synth import CONFIGS, make_inputs, make_state, make_weights
+
+    cfg = CONFIGS[args.workload]
+    steps = args.steps if args.steps is not None else min(cfg.chunks, 1000)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    W = make_weights(cfg)
+    S = cfg.streams
+    enc = StreamingEncoder(cfg, W, max_streams=S)
+    if cfg.staggered:
+        for g0 in range(0, S, 64):
+            grp = list(range(g0, min(S, g0 + 64)))
+            enc.import_state_dicts(grp, [make_state(cfg, s) for s in grp])
+    per_stream = cfg.chunks
+    # chunk-major [chunks, S, frames, width]: each step's input is one contiguous slab in HBM
+    xs = np.ascontiguousarray(np.stack([make_inputs(cfg, s, per_stream) for s in range(S)]).swapaxes(0, 1))
+    x_dev = torch.from_numpy(xs).to(dev).to(tdt)
+    del xs
+    out = torch.empty((S, cfg.n_emit, cfg.joint_dim or cfg.d_model), dtype=torch.float32, device=dev)
+    ids = list(range(S))
+    k = 0
+
+    def step():
+        nonlocal k
+        enc.push_chunk(ids, x_dev[k % per_stream], out)
+        k += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    frames = S * cfg.n_emit * steps
+    value = frames / (ms / 1e3)
+
+    # per-kernel timing over a second window of the same workload
+    enc.profile(True)
+    for _ in range(args.profile_steps):
+        step()
+    torch.cuda.synchronize()
+    prof = enc.profile_read()
+    enc.profile(False)
+    dom = max(prof, key=lambda n: prof[n][1])
+    launches, kms, kbytes, kflops = prof[dom]
+    mfma_bound = "mfma" in dom and kbytes and kflops / kbytes > 312.0
+    if mfma_bound:
+        achieved = kflops / launches / (kms / launches / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        achieved = kbytes / launches / (kms / launches / 1e3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(dom, kbytes / launches)
+    roof["kernel"] = dom
+    roof["avg_launch_us"] = kms / launches * 1e3
+    roof["algorithmic_bytes_per_launch"] = kbytes / launches
+    step_bytes = sum(v[2] for v in prof.values()) / args.profile_steps
+    step_flops = sum(v[3] for v in prof.values()) / args.profile_steps
+    ms_step = ms / steps
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "frames/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32" if cfg.dtype == "f32" else "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": cfg.n_layers, "d_model": cfg.d_model, "heads": cfg.n_heads,
+                   "d_ff": cfg.d_ff, "att_left": cfg.att_left, "streams": S, "frames_per_chunk": cfg.n_emit,
+                   "frames_computed_per_chunk": cfg.n_compute, "joint_dim": cfg.joint_dim,
+                   "frontend": cfg.frontend, "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "step": {"algorithmic_bytes": step_bytes, "algorithmic_flops": step_flops,
+                 "hbm_frac_of_peak": step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+                 "kernels": {n: {"launches_per_step": v[0] / args.profile_steps,
+                                 "us_per_step": v[1] / args.profile_steps * 1e3} for n, v in
+                             sorted(prof.items(), key=lambda kv: -kv[1][1])}},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, W, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

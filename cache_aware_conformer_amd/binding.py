@@ -48,6 +48,9 @@ SIGNATURES = {
     "cac_destroy": (_i32, [_vp]),
     "cac_last_error": (C.c_char_p, [_vp]),
     "cac_test_gemm": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "cac_profile": (_i32, [_vp, _i32]),
+    "cac_profile_read": (_i32, [_vp, _i32, C.c_char_p, _i32, C.POINTER(C.c_int64), C.POINTER(C.c_double),
+                                C.POINTER(C.c_double), C.POINTER(C.c_double)]),
 }
 
 _lib = None
@@ -194,6 +197,11 @@ class StreamingEncoder:
         Returns (out [n, n_frames_out, P] float32, emitted per stream as np.int32)."""
         ids, idp = _ids(stream_ids)
         n = ids.size
+        if hasattr(x, "is_contiguous"):
+            want = self.torch.bfloat16 if self.c.dtype == CAC_BF16 else self.torch.float32
+            if not x.is_contiguous() or x.dtype != want or x.shape[0] != n:
+                raise ValueError(f"input must be a contiguous {want} tensor with {n} rows, got "
+                                 f"{x.dtype} {tuple(x.shape)} contiguous={x.is_contiguous()}")
         if n_frames is None:
             if self.cfg.n_lookahead:
                 n_frames = self.cfg.n_emit
@@ -241,6 +249,27 @@ class StreamingEncoder:
         return self._check(self.lib.cac_import_state(self.ctx, ids.size, idp, pos.ctypes.data_as(_ip),
                                                      pend.ctypes.data_as(_ip), bp))
 
+    def state_blob(self, st: dict) -> np.ndarray:
+        """Canonical float32 state blob (header layout) of one stream from a dict with keys
+        k, v [L][Lc][D], conv [L][K-1][D], mel_tail (front end), x0_tail (lookahead)."""
+        parts = [np.asarray(st["k"], np.float32).reshape(-1), np.asarray(st["v"], np.float32).reshape(-1),
+                 np.asarray(st["conv"], np.float32).reshape(-1)]
+        if self.cfg.frontend:
+            parts.append(np.asarray(st["mel_tail"], np.float32).reshape(-1))
+        if self.cfg.n_lookahead:
+            parts.append(np.asarray(st["x0_tail"], np.float32).reshape(-1))
+        blob = np.concatenate(parts)
+        assert blob.size == self.sfloats, (blob.size, self.sfloats)
+        return blob
+
+    def import_state_dicts(self, stream_ids, states, pending=None):
+        """Import per-stream state dicts (see state_blob; positions from st['pos'])."""
+        blob = self.torch.from_numpy(np.stack([self.state_blob(st) for st in states])).to(self.device)
+        pos = [int(st["pos"]) for st in states]
+        if pending is None and self.cfg.n_lookahead:
+            pending = [len(st["x0_tail"]) for st in states]
+        return self.import_state(stream_ids, pos, pending, blob)
+
     def stream_info(self, stream_id) -> StreamInfo:
         p, q, f = C.c_int32(), C.c_int32(), C.c_int32()
         self._check(self.lib.cac_stream_info(self.ctx, int(stream_id), C.byref(p), C.byref(q), C.byref(f)))
@@ -251,6 +280,22 @@ class StreamingEncoder:
 
     def synchronize(self):
         return self._check(self.lib.cac_synchronize(self.ctx))
+
+    def profile(self, enable: bool):
+        return self._check(self.lib.cac_profile(self.ctx, int(bool(enable))))
+
+    def profile_read(self) -> dict:
+        """{kernel name: (launches, total_ms, bytes, flops)} of the launches since profile(True)."""
+        n = self._check(self.lib.cac_profile_read(self.ctx, 0, None, 64, None, None, None, None))
+        names = C.create_string_buffer(64 * max(n, 1))
+        launches = (C.c_int64 * max(n, 1))()
+        ms, by, fl = (C.c_double * max(n, 1))(), (C.c_double * max(n, 1))(), (C.c_double * max(n, 1))()
+        n = self._check(self.lib.cac_profile_read(self.ctx, n, names, 64, launches, ms, by, fl))
+        out = {}
+        for i in range(n):
+            nm = names.raw[64 * i:64 * (i + 1)].split(b"\0", 1)[0].decode()
+            out[nm] = (int(launches[i]), float(ms[i]), float(by[i]), float(fl[i]))
+        return out
 
     def close(self):
         if getattr(self, "ctx", None):

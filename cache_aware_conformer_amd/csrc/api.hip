@@ -2,6 +2,7 @@
 // repacking, host-side stream bookkeeping and the per-push launch sequence.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdio>
@@ -205,6 +206,8 @@ struct cac_ctx {
   std::vector<int32_t> stamp;
   int32_t stamp_gen = 0;
   std::string err;
+  bool profiling = false;
+  Profiler prof;
 
   template <class T> T* P(size_t off) const { return (T*)(ws + off); }
   int fail(int code, const std::string& m) { err = m; return code; }
@@ -240,6 +243,7 @@ struct Pass {
   Launcher& L;
   CallView cv;
   int M;
+  double kv_rows;  // sum over the call's streams of the K/V rows attention reads (fill + new)
 
   EpiArgs epi0() const {
     EpiArgs e{};
@@ -296,6 +300,12 @@ struct Pass {
       at.D = d.D; at.H = d.H; at.R = d.R; at.Lc = d.Lc; at.chunk = d.c; at.right = d.right;
       at.lookahead = d.lookahead; at.rel_lo = d.rel_lo; at.nrel = d.nrel;
       at.scale = 1.0f / sqrtf((float)d.hd);
+      {
+        const double nrows = (double)cv.n_streams * cv.nf;
+        const double bytes = kv_rows * 2.0 * d.D * d.esz + (double)d.H * d.nrel * d.hd * 4.0;
+        const double flops = 6.0 * nrows * (kv_rows / cv.n_streams) * d.D + 2.0 * nrows * d.nrel * d.D;
+        L.tag("attention", bytes, flops);
+      }
       launch_attention(L, at, d.dt, d.hd);
       EpiArgs wo = epi0();
       wo.kind = EPI_RESID; wo.bias = (const float*)(lb + lo.b_o); wo.out = c->P<void>(c->lay.x); wo.ldo = d.D; wo.alpha = 1.0f;
@@ -305,6 +315,7 @@ struct Pass {
       glu.kind = EPI_GLU; glu.bias = (const float*)(lb + lo.b_pw1); glu.cring = cr;
       gemm_ln((const float*)(lb + lo.ln[4]), (const float*)(lb + lo.ln[5]), lb + lo.w_pw1, 2 * d.D, d.D, glu);
       DwArgs dw{cv, cr, (const float*)(lb + lo.dw_w), (const float*)(lb + lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
+      L.tag("dwconv", (double)cv.n_streams * (d.Kc + cv.nf) * d.D * d.esz, 2.0 * d.K * d.D * M);
       launch_dwconv(L, dw, d.dt);
       EpiArgs pw2 = epi0();
       pw2.kind = EPI_RESID; pw2.bias = (const float*)(lb + lo.b_pw2); pw2.out = c->P<void>(c->lay.x); pw2.ldo = d.D; pw2.alpha = 1.0f;
@@ -548,6 +559,7 @@ int32_t cac_push_chunk(cac_ctx* c, int32_t n, const int32_t* ids, int32_t n_fram
 
   Launcher L;
   L.stream = c->stream;
+  if (c->profiling) L.prof = &c->prof;
   L.err = upload(c, c->dev_ids, c->lay.ids, ids, n);
   const int32_t* dids = c->P<int32_t>(c->lay.ids);
   int32_t* dpos = c->P<int32_t>(c->lay.pos);
@@ -577,7 +589,9 @@ int32_t cac_push_chunk(cac_ctx* c, int32_t n, const int32_t* ids, int32_t n_fram
       InputArgs ia{d_input, c->P<float>(c->lay.x), M, d.D};
       launch_input(L, ia, d.dt);
     }
-    Pass ps{c, L, cv, M};
+    double kvr = 0;
+    for (int i = 0; i < n; ++i) kvr += std::min(c->hpos[ids[i]], d.Lc) + n_frames;
+    Pass ps{c, L, cv, M, kvr};
     ps.layers();
     ps.joint(d_out, M, RowMap{INT_MAX, 0, d.D}, nullptr, 1, 0);
     AdvanceArgs ad{dids, dpos, dpend, n, n_frames, 0};
@@ -596,7 +610,9 @@ int32_t cac_push_chunk(cac_ctx* c, int32_t n, const int32_t* ids, int32_t n_fram
       CallView cv{dcids, dpos, d.nc, nC};
       LaGatherArgs lg{cv, c->ws + c->lay.x0, c->P<float>(c->lay.x), d.D, d.Rx};
       launch_la_gather(L, lg, d.dt);
-      Pass ps{c, L, cv, nC * d.nc};
+      double kvr = 0;
+      for (int id : cids) kvr += std::min(c->hpos[id], d.Lc) + d.nc;
+      Pass ps{c, L, cv, nC * d.nc, kvr};
       ps.layers();
       ps.joint(d_out, nC * d.ne, RowMap{d.ne, d.nc * d.D, d.D}, c->P<int32_t>(c->lay.cidx), d.ne, d.ne);
       AdvanceArgs a2{dcids, dpos, dpend, nC, d.ne, -d.ne};
@@ -648,6 +664,7 @@ int32_t cac_flush(cac_ctx* c, int32_t n, const int32_t* ids, float* d_out, int32
   }
   Launcher L;
   L.stream = c->stream;
+  if (c->profiling) L.prof = &c->prof;
   // one final pass per distinct pending count; pending frames see keys up to their own end
   for (int m = 1; m <= d.nla && L.err == hipSuccess; ++m) {
     std::vector<int32_t> cids, cidx;
@@ -662,7 +679,9 @@ int32_t cac_flush(cac_ctx* c, int32_t n, const int32_t* ids, float* d_out, int32
     CallView cv{dcids, dpos, m, nC};
     LaGatherArgs lg{cv, c->ws + c->lay.x0, c->P<float>(c->lay.x), d.D, d.Rx};
     launch_la_gather(L, lg, d.dt);
-    Pass ps{c, L, cv, nC * m};
+    double kvr = 0;
+    for (int id : cids) kvr += std::min(c->hpos[id], d.Lc) + m;
+    Pass ps{c, L, cv, nC * m, kvr};
     ps.layers();
     ps.joint(d_out, nC * m, RowMap{INT_MAX, 0, d.D}, c->P<int32_t>(c->lay.cidx), m, d.nla);
     AdvanceArgs ad{dcids, dpos, c->P<int32_t>(c->lay.pend), nC, m, -m};
@@ -751,6 +770,37 @@ int32_t cac_synchronize(cac_ctx* c) {
   hipError_t e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("device error: ") + hipGetErrorString(e));
   return CAC_OK;
+}
+
+int32_t cac_profile(cac_ctx* c, int32_t enable) {
+  if (!c) return CAC_EINVAL;
+  if (enable) {
+    c->prof.clear();
+    c->profiling = true;
+  } else {
+    c->prof.drain();
+    c->profiling = false;
+  }
+  return c->prof.err == hipSuccess ? CAC_OK : c->fail(CAC_EHIP, std::string("profiling: ") + hipGetErrorString(c->prof.err));
+}
+
+int32_t cac_profile_read(cac_ctx* c, int32_t max_entries, char* names, int32_t name_len, int64_t* launches,
+                         double* total_ms, double* bytes, double* flops) {
+  if (!c || max_entries < 0 || name_len < 1) return CAC_EINVAL;
+  c->prof.drain();
+  if (c->prof.err != hipSuccess) return c->fail(CAC_EHIP, std::string("profiling: ") + hipGetErrorString(c->prof.err));
+  const int n = (int)c->prof.names.size();
+  for (int i = 0; i < n && i < max_entries; ++i) {
+    if (names) {
+      strncpy(names + (size_t)i * name_len, c->prof.names[i].c_str(), name_len - 1);
+      names[(size_t)i * name_len + name_len - 1] = 0;
+    }
+    if (launches) launches[i] = c->prof.launches[i];
+    if (total_ms) total_ms[i] = c->prof.ms[i];
+    if (bytes) bytes[i] = c->prof.bytes[i];
+    if (flops) flops[i] = c->prof.flops[i];
+  }
+  return n;
 }
 
 int32_t cac_destroy(cac_ctx* c) {

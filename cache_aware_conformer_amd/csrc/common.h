@@ -5,6 +5,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+#include <vector>
+
 typedef uint16_t bf16_t;  // bfloat16 storage
 
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
@@ -210,12 +213,33 @@ struct LaGatherArgs {   // lookahead: x rows of a pass from the pending ring
 // Kernels are launched through a Launcher: either straight onto a stream, or appended to a
 // HIP graph as a chain of kernel nodes (node handles are kept so pointer arguments can be
 // re-pointed before each replay).
+// Optional per-kernel timing: every launch bracketed by two HIP events on the launch stream,
+// aggregated by kernel name together with the launch's algorithmic bytes and flops.
+struct Profiler {
+  struct Rec { int name; double bytes, flops; hipEvent_t a, b; };
+  std::vector<hipEvent_t> free_ev;
+  std::vector<Rec> pending;
+  std::vector<std::string> names;
+  std::vector<long> launches;
+  std::vector<double> ms, bytes, flops;
+  hipError_t err = hipSuccess;
+  int name_id(const char* n);
+  hipEvent_t get();
+  void drain();   // synchronise pending events, accumulate, recycle
+  void clear();
+  ~Profiler();
+};
+
 struct Launcher {
   hipStream_t stream = nullptr;
   hipGraph_t graph = nullptr;        // non-null: record instead of launch
   hipGraphNode_t last = nullptr;
   hipGraphNode_t last_node = nullptr;  // node of the most recent launch (record mode)
   hipError_t err = hipSuccess;
+  Profiler* prof = nullptr;          // direct launches only
+  const char* tag_name = "kernel";   // set by the wrappers before each launch
+  double tag_bytes = 0.0, tag_flops = 0.0;
+  void tag(const char* n, double bytes, double flops) { tag_name = n; tag_bytes = bytes; tag_flops = flops; }
   void launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* args);
 };
 

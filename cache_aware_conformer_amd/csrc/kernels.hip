@@ -17,12 +17,65 @@
 #include <climits>
 
 // =============================================================================== launcher
+int Profiler::name_id(const char* n) {
+  for (size_t i = 0; i < names.size(); ++i)
+    if (names[i] == n) return (int)i;
+  names.emplace_back(n);
+  launches.push_back(0);
+  ms.push_back(0.0);
+  bytes.push_back(0.0);
+  flops.push_back(0.0);
+  return (int)names.size() - 1;
+}
+hipEvent_t Profiler::get() {
+  if (free_ev.empty() && pending.size() >= 2048) drain();
+  if (!free_ev.empty()) { hipEvent_t e = free_ev.back(); free_ev.pop_back(); return e; }
+  hipEvent_t e = nullptr;
+  hipError_t r = hipEventCreate(&e);
+  if (r != hipSuccess && err == hipSuccess) err = r;
+  return e;
+}
+void Profiler::drain() {
+  for (Rec& r : pending) {
+    float t = 0.0f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    launches[r.name] += 1;
+    ms[r.name] += t;
+    bytes[r.name] += r.bytes;
+    flops[r.name] += r.flops;
+    free_ev.push_back(r.a);
+    free_ev.push_back(r.b);
+  }
+  pending.clear();
+}
+void Profiler::clear() {
+  drain();
+  names.clear(); launches.clear(); ms.clear(); bytes.clear(); flops.clear();
+  err = hipSuccess;
+}
+Profiler::~Profiler() {
+  drain();
+  for (hipEvent_t e : free_ev) (void)hipEventDestroy(e);
+}
+
 void Launcher::launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* args) {
   if (err != hipSuccess) return;
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return;
   void* kp[1] = {args};
   if (!graph) {
+    if (prof) {
+      hipEvent_t a = prof->get(), b = prof->get();
+      if (a && b) err = hipEventRecord(a, stream);
+      if (err == hipSuccess) err = hipLaunchKernel(fn, grid, block, kp, shmem, stream);
+      if (err == hipSuccess && a && b) err = hipEventRecord(b, stream);
+      if (err == hipSuccess && a && b) prof->pending.push_back({prof->name_id(tag_name), tag_bytes, tag_flops, a, b});
+      tag_bytes = tag_flops = 0.0;
+      return;
+    }
     err = hipLaunchKernel(fn, grid, block, kp, shmem, stream);
+    tag_bytes = tag_flops = 0.0;
     return;
   }
   hipKernelNodeParams p = {};
@@ -337,6 +390,21 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
 }
 
 // =============================================================================== dense dispatch
+// Algorithmic HBM bytes of one dense product: the weights once, plus what its epilogue writes
+// to per-stream state (K/V rows, depthwise input rows) or to the caller's output. Activations
+// that stay on chip or in the last-level cache are not counted.
+static double gemm_bytes(const GemmArgs& a, size_t wsz) {
+  double b = (double)a.N * a.K * wsz;
+  const double esz = (double)wsz;
+  switch (a.epi.kind) {
+    case EPI_QKV: b += (double)a.M * 2.0 * a.epi.D * esz; break;
+    case EPI_GLU: b += (double)a.M * (a.N / 2) * esz; break;
+    case EPI_F32: if (a.epi.ldo != a.epi.D || a.epi.omap) b += (double)a.M * a.N * 4.0; break;
+    default: break;
+  }
+  return b;
+}
+
 template <typename TW, typename TA>
 static void gemv_dispatch(Launcher& L, const GemmArgs& a) {
   const int units = a.epi.kind == EPI_GLU ? a.N / 2 : a.N;
@@ -354,6 +422,7 @@ static void gemv_dispatch(Launcher& L, const GemmArgs& a) {
   fn = vec ? (const void*)&gemv_kernel<TW, TA, mr, VW> : (const void*)&gemv_kernel<TW, TA, mr, 1>;
   if (MR == 2) { GEMV_PICK(2) } else if (MR == 4) { GEMV_PICK(4) } else { GEMV_PICK(8) }
 #undef GEMV_PICK
+  L.tag(sizeof(TW) == 4 ? "gemm_small_m_f32" : "gemm_small_m_bf16", gemm_bytes(a, sizeof(TW)), 2.0 * a.M * a.N * a.K);
   L.launch(fn, dim3((units + upb - 1) / upb, (a.M + MR - 1) / MR), dim3(256), shm, &args);
 }
 
@@ -363,6 +432,7 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a) {
   GemmArgs args = a;
   const void* fn;
   dim3 grid;
+  L.tag("gemm_mfma_bf16", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K);
   // largest tile that still yields >= 256 workgroups; GLU needs 64-column wave tiles
   if (tiles(128, 128) >= 256) {
     fn = (const void*)&gemm_mfma_kernel<128, 128, 2, 2>;
@@ -405,10 +475,12 @@ void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path) {
     // materialise the bf16 operand first: LayerNorm rows, or a rounded (gathered) copy
     if (a.ln_g) {
       LnArgs la{(const float*)a.A, a.a_scratch, a.ln_g, a.ln_b, a.M, a.K, 0};
+      L.tag("layernorm", 0.0, 0.0);
       L.launch((const void*)&ln_kernel<bf16_t>, dim3((a.M + 3) / 4), dim3(256), 0, &la);
     } else {
       CvtArgs cv{(const float*)a.A, a.amap, a.a_scratch, a.M, a.K};
       const long total = (long)a.M * a.K;
+      L.tag("convert_rows", 0.0, 0.0);
       L.launch((const void*)&cvt_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &cv);
     }
     g.A = a.a_scratch;
@@ -422,6 +494,7 @@ void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path) {
 void launch_ln(Launcher& L, const LnArgs& a, int dtype) {
   LnArgs args = a;
   const void* fn = (a.out_f32 || dtype == DT_F32) ? (const void*)&ln_kernel<float> : (const void*)&ln_kernel<bf16_t>;
+  L.tag("layernorm", 0.0, 0.0);
   L.launch(fn, dim3((a.M + 3) / 4), dim3(256), 0, &args);
 }
 
@@ -549,6 +622,7 @@ void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd) {
   fn = dtype == DT_F32 ? (const void*)&attn_kernel<float, HDV> : (const void*)&attn_kernel<bf16_t, HDV>;
   if (hd == 16) { ATT_PICK(16) } else if (hd == 32) { ATT_PICK(32) } else { ATT_PICK(64) }
 #undef ATT_PICK
+  L.tag_name = "attention";  // the caller tags bytes and flops (it knows each stream's fill)
   L.launch(fn, dim3((pairs + 3) / 4), dim3(256), shm, &args);
 }
 
@@ -575,6 +649,7 @@ void launch_dwconv(Launcher& L, const DwArgs& a, int dtype) {
   DwArgs args = a;
   const long total = (long)a.cv.n_streams * a.cv.nf * a.D;
   const void* fn = dtype == DT_F32 ? (const void*)&dw_kernel<float> : (const void*)&dw_kernel<bf16_t>;
+  L.tag_name = "dwconv";  // the caller tags bytes and flops
   L.launch(fn, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
 }
 
@@ -588,6 +663,7 @@ void launch_input(Launcher& L, const InputArgs& a, int dtype) {
   InputArgs args = a;
   const long total = (long)a.M * a.D;
   const void* fn = dtype == DT_F32 ? (const void*)&input_kernel<float> : (const void*)&input_kernel<bf16_t>;
+  L.tag("input", (double)total * (dtype == DT_F32 ? 4 : 2), 0.0);
   L.launch(fn, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
 }
 
@@ -601,6 +677,7 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(CopyRowsArgs a) {
 void launch_copy_rows(Launcher& L, const CopyRowsArgs& a) {
   CopyRowsArgs args = a;
   const long total = (long)a.M * a.D;
+  L.tag("copy_rows", (double)total * 4, 0.0);
   L.launch((const void*)&copy_rows_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
 }
 
@@ -625,6 +702,7 @@ void launch_fe_window(Launcher& L, const FeWindowArgs& a, int dtype) {
   FeWindowArgs args = a;
   const int total = a.cv.n_streams * a.bins;
   const void* fn = dtype == DT_F32 ? (const void*)&fe_window_kernel<float> : (const void*)&fe_window_kernel<bf16_t>;
+  L.tag("fe_window", (double)a.cv.n_streams * (a.mel_new + 2 * a.mel_tail) * a.bins * (dtype == DT_F32 ? 4 : 2), 0.0);
   L.launch(fn, dim3((total + 255) / 256), dim3(256), 0, &args);
 }
 
@@ -638,6 +716,7 @@ __global__ void advance_kernel(AdvanceArgs a) {
 }
 void launch_advance(Launcher& L, const AdvanceArgs& a) {
   AdvanceArgs args = a;
+  L.tag("advance", 0.0, 0.0);
   L.launch((const void*)&advance_kernel, dim3((a.n + 255) / 256), dim3(256), 0, &args);
 }
 
@@ -664,6 +743,7 @@ __global__ __launch_bounds__(512) void posproj_kernel(PosProjArgs a) {
 }
 void launch_posproj(Launcher& L, const PosProjArgs& a) {
   PosProjArgs args = a;
+  L.tag("posproj", 0.0, 0.0);
   L.launch((const void*)&posproj_kernel, dim3(a.nrel, a.L), dim3(512), (size_t)a.D * sizeof(double), &args);
 }
 
@@ -760,6 +840,7 @@ void launch_state(Launcher& L, const StateArgs& a, int op) {
   if (op == 0) fn = f32 ? (const void*)&state_reset_kernel<float> : (const void*)&state_reset_kernel<bf16_t>;
   else if (op == 1) fn = f32 ? (const void*)&state_xfer_kernel<float, true> : (const void*)&state_xfer_kernel<bf16_t, true>;
   else fn = f32 ? (const void*)&state_xfer_kernel<float, false> : (const void*)&state_xfer_kernel<bf16_t, false>;
+  L.tag("state", 0.0, 0.0);
   L.launch(fn, dim3(64, a.n), dim3(256), 0, &args);
 }
 
@@ -788,12 +869,14 @@ void launch_la_store(Launcher& L, const LaStoreArgs& a, int dtype) {
   LaStoreArgs args = a;
   const long total = (long)a.cv.n_streams * a.cv.nf * a.D;
   const void* fn = dtype == DT_F32 ? (const void*)&la_store_kernel<float> : (const void*)&la_store_kernel<bf16_t>;
+  L.tag("lookahead_store", (double)total * 2 * (dtype == DT_F32 ? 4 : 2), 0.0);
   L.launch(fn, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
 }
 void launch_la_gather(Launcher& L, const LaGatherArgs& a, int dtype) {
   LaGatherArgs args = a;
   const long total = (long)a.cv.n_streams * a.cv.nf * a.D;
   const void* fn = dtype == DT_F32 ? (const void*)&la_gather_kernel<float> : (const void*)&la_gather_kernel<bf16_t>;
+  L.tag("lookahead_gather", (double)total * (dtype == DT_F32 ? 4 : 2), 0.0);
   L.launch(fn, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
 }
 

@@ -111,8 +111,9 @@ size_t cac_state_floats(const cac_config* cfg);
 
 /* Validate cfg, repack the float32 host parameters (h_params, cac_param_count floats) into the
  * workspace in the compute layout (bf16 rounding to nearest even for CAC_BF16), compute each
- * layer's projected position table (streaming spec step 3: "posProj rows precomputed per
- * layer"), reset every stream to position 0, and return the context in *out. hip_stream is a
+ * layer's projected position table once (streaming spec, "Per-chunk flow" step 3: the
+ * projected position rows are a per-layer constant), reset every stream to position 0, and
+ * return the context in *out. hip_stream is a
  * hipStream_t (NULL = default stream). Synchronises hip_stream before returning. The caller may
  * free h_params afterwards; d_workspace must stay allocated until cac_destroy. */
 int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t n_params,
@@ -135,7 +136,8 @@ int32_t cac_push_chunk(cac_ctx* ctx, int32_t n_streams, const int32_t* h_stream_
  * caches, mel tail and position). Returns n. */
 int32_t cac_reset_stream(cac_ctx* ctx, int32_t n, const int32_t* h_stream_ids);
 
-/* End streams (streaming spec, "Status": padBottom at flush only). The lookahead variant runs a
+/* End streams (streaming spec, "Status": end-of-stream padding happens only at flush). The
+ * lookahead variant runs a
  * final pass over each stream's pending frames and writes all of them to d_out
  * ([n][n_lookahead][P], first h_frames_out[i] rows of stream i); the exact variant has nothing
  * left to emit. Flushed streams reject pushes until reset. Returns the largest frame count. */
@@ -160,6 +162,18 @@ int32_t cac_set_stream(cac_ctx* ctx, void* hip_stream);
 
 /* Synchronise the context's stream and report any asynchronous device error (CAC_EHIP). */
 int32_t cac_synchronize(cac_ctx* ctx);
+
+/* Per-kernel timing of later pushes and flushes (measurement aid; adds two HIP events per
+ * launch on the context's stream). cac_profile(ctx, 1) clears and starts, 0 stops.
+ * cac_profile_read synchronises the recorded events and fills, per kernel name (up to
+ * max_entries; names is max_entries * name_len chars): launches, total milliseconds between
+ * each launch's events, and the algorithmic bytes and flops the library attributes to those
+ * launches (weights read once per launch, K/V and depthwise ring rows read and written,
+ * inputs and outputs; activations that stay on chip are not counted). Returns the number of
+ * kernel names recorded. */
+int32_t cac_profile(cac_ctx* ctx, int32_t enable);
+int32_t cac_profile_read(cac_ctx* ctx, int32_t max_entries, char* names, int32_t name_len, int64_t* launches,
+                         double* total_ms, double* bytes, double* flops);
 
 /* Free the host context (the workspace stays the caller's). Accepts NULL. */
 int32_t cac_destroy(cac_ctx* ctx);

@@ -24,27 +24,14 @@ def to_dev(a: np.ndarray, cfg) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0").to(dev_dtype(cfg))
 
 
-def state_blob(cfg, st: dict) -> np.ndarray:
-    parts = [st["k"].reshape(-1), st["v"].reshape(-1), st["conv"].reshape(-1)]
-    if cfg.frontend:
-        parts.append(st["mel_tail"].reshape(-1))
-    if cfg.n_lookahead:
-        parts.append(st["x0_tail"].reshape(-1))
-    return np.concatenate(parts).astype(np.float32)
-
-
 def import_staggered(enc, cfg, n_streams: int, group: int = 64) -> list:
     """Inject the seeded mid-stream state of every stream; returns the positions."""
     positions = []
     for g0 in range(0, n_streams, group):
         ids = list(range(g0, min(n_streams, g0 + group)))
         sts = [make_state(cfg, s) for s in ids]
-        blob = torch.from_numpy(np.stack([state_blob(cfg, st) for st in sts])).to("cuda:0")
-        pos = [st["pos"] for st in sts]
-        pend = [cfg.n_lookahead for _ in sts] if cfg.n_lookahead else None
-        enc.import_state(ids, pos, pend, blob)
-        positions += pos
-        del blob
+        enc.import_state_dicts(ids, sts)
+        positions += [st["pos"] for st in sts]
     torch.cuda.synchronize()
     return positions
 

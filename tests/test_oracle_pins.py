@@ -139,8 +139,8 @@ def test_relshift_picks_relative_offset():
 
 
 def test_mask_window_is_chunk_start_minus_lc_to_chunk_start_plus_one():
-    """Streaming spec, "Why this is provably correct": frame i attends
-    [chunkStart-70 .. chunkStart+1] (chunk 2)."""
+    """Streaming spec, "Why this is provably correct": with chunks of 2 and a left context of
+    70, a frame sees the 70 frames before its chunk's first frame plus its own chunk."""
     orc = Oracle(C2, {})
     for p in (0, 1, 2, 3, 70, 71, 140, 141, 1001):
         cs = p - p % 2
