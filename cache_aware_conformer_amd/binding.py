@@ -44,6 +44,7 @@ SIGNATURES = {
     "cac_import_state": (_i32, [_vp, _i32, _ip, _ip, _ip, _vp]),
     "cac_stream_info": (_i32, [_vp, _i32, _ip, _ip, _ip]),
     "cac_set_stream": (_i32, [_vp, _vp]),
+    "cac_set_graph": (_i32, [_vp, _i32]),
     "cac_synchronize": (_i32, [_vp]),
     "cac_destroy": (_i32, [_vp]),
     "cac_last_error": (C.c_char_p, [_vp]),
@@ -274,6 +275,9 @@ class StreamingEncoder:
         p, q, f = C.c_int32(), C.c_int32(), C.c_int32()
         self._check(self.lib.cac_stream_info(self.ctx, int(stream_id), C.byref(p), C.byref(q), C.byref(f)))
         return StreamInfo(p.value, q.value, bool(f.value))
+
+    def set_graph(self, enable: bool):
+        return self._check(self.lib.cac_set_graph(self.ctx, int(bool(enable))))
 
     def set_stream(self, stream):
         return self._check(self.lib.cac_set_stream(self.ctx, stream))

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -38,12 +39,12 @@ bool make_dims(const cac_config* c, Dims& d, std::string& why) {
   d.npush = c->max_push_frames; d.flags = c->flags;
   auto bad = [&](const char* m) { why = m; return false; };
   if (d.L < 1 || d.L > 64) return bad("n_layers must be in [1, 64]");
-  if (d.D < 64 || d.D > 4096 || d.D % 64) return bad("d_model must be a multiple of 64 in [64, 4096]");
+  if (d.D < 64 || d.D > 1024 || d.D % 64) return bad("d_model must be a multiple of 64 in [64, 1024]");
   if (d.H < 1 || d.D % d.H) return bad("n_heads must divide d_model");
   d.hd = d.D / d.H;
   if (d.hd != 16 && d.hd != 32 && d.hd != 64) return bad("head_dim must be 16, 32 or 64");
   if (d.F < 64 || d.F > 4096 || d.F % 64) return bad("d_ff must be a multiple of 64 in [64, 4096]");
-  if (d.K < 1 || d.K > 17) return bad("dw_kernel must be in [1, 17]");
+  if (d.K < 1 || d.K > 16) return bad("dw_kernel must be in [1, 16]");
   d.Kc = d.K - 1;
   if (d.Lc < 0 || d.Lc > 512) return bad("att_left must be in [0, 512]");
   if (d.c < 1 || d.c > 16) return bad("att_chunk must be in [1, 16]");
@@ -97,8 +98,8 @@ struct Layout {
   LayerOff lo;
   size_t layers, wj, bj, fe_w[3], fe_b[3], weights_end;
   size_t posproj, kring, vring, cring, tail, x0, pos, pend;
-  size_t ids, cids, cidx, sids, spos, spend;
-  size_t x, y, q, h, o, e, win, fe1, fe2;
+  size_t ids, cids, cidx, sids, spos, spend, cpos, ccpos;
+  size_t x, x2, y, q, h, o, e, win, fe1, fe2;
   size_t total;
 };
 
@@ -136,7 +137,8 @@ Layout make_layout(const Dims& d) {
   t.pos = w.take(S * 4); t.pend = w.take(S * 4);
   t.ids = w.take(S * 4); t.cids = w.take(S * 4); t.cidx = w.take(S * 4);
   t.sids = w.take(S * 4); t.spos = w.take(S * 4); t.spend = w.take(S * 4);
-  t.x = w.take(M * D * f4); t.y = w.take(M * D * e); t.q = w.take(M * D * f4);
+  t.cpos = w.take(S * 4); t.ccpos = w.take(S * 4);
+  t.x = w.take(M * D * f4); t.x2 = w.take(M * D * f4); t.y = w.take(M * D * e); t.q = w.take(M * D * f4);
   t.h = w.take(M * F * e); t.o = w.take(M * D * e); t.e = w.take(M * D * e);
   if (d.fe) {
     t.win = w.take(S * (d.tail + d.mpc) * d.bins * e);
@@ -208,6 +210,23 @@ struct cac_ctx {
   std::string err;
   bool profiling = false;
   Profiler prof;
+  // recorded push graphs, one per call shape
+  struct Graph {
+    hipGraph_t g = nullptr;
+    hipGraphExec_t exec = nullptr;
+    std::vector<NodeRec> nodes;
+    std::vector<std::vector<size_t>> in_offs, out_offs;  // per node: offsets of the caller pointers
+    const void* in = nullptr;
+    void* out = nullptr;
+  };
+  bool use_graph = true;
+  std::map<uint64_t, Graph> graphs;
+  ~cac_ctx() {
+    for (auto& kv : graphs) {
+      if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
+      if (kv.second.g) (void)hipGraphDestroy(kv.second.g);
+    }
+  }
 
   template <class T> T* P(size_t off) const { return (T*)(ws + off); }
   int fail(int code, const std::string& m) { err = m; return code; }
@@ -251,51 +270,76 @@ struct Pass {
     e.D = c->d.D; e.H = c->d.H; e.hd = c->d.hd; e.R = c->d.R; e.Rc = c->d.Rc;
     return e;
   }
-  // dense product whose A operand is LayerNorm(x) (float32 residual rows)
-  void gemm_ln(const float* g_ln, const float* b_ln, const void* W, int N, int K, const EpiArgs& e) {
-    GemmArgs g{};
-    g.M = M; g.N = N; g.K = K; g.W = W; g.epi = e;
-    g.A = c->P<float>(c->lay.x); g.amap = RowMap{INT_MAX, 0, K};
-    g.a_f32 = 1; g.ln_g = g_ln; g.ln_b = b_ln; g.a_scratch = c->P<void>(c->lay.y);
-    launch_gemm(L, g, c->d.dt, 0);
-  }
   void gemm_plain(const void* A, int lda, const void* W, int N, int K, const EpiArgs& e) {
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K; g.A = A; g.W = W; g.epi = e;
     g.amap = RowMap{INT_MAX, 0, lda};
     launch_gemm(L, g, c->d.dt, 0);
   }
-  void ff(char* lb, int ln_idx, size_t b1, size_t b2, size_t w1, size_t w2) {
-    const Dims& d = c->d;
-    const LayerOff& lo = c->lay.lo;
-    EpiArgs up = epi0();
-    up.kind = EPI_SILU; up.bias = (const float*)(lb + b1); up.out = c->P<void>(c->lay.h); up.ldo = d.F;
-    gemm_ln((const float*)(lb + lo.ln[ln_idx]), (const float*)(lb + lo.ln[ln_idx + 1]), lb + w1, d.F, d.D, up);
-    EpiArgs dn = epi0();
-    dn.kind = EPI_RESID; dn.bias = (const float*)(lb + b2); dn.out = c->P<void>(c->lay.x); dn.ldo = d.D; dn.alpha = 0.5f;
-    gemm_plain(c->P<void>(c->lay.h), d.F, lb + w2, d.D, d.F, dn);
-  }
+
+  // few rows (float32 workloads, or <= 8 rows): every dense product runs in the small-M kernel
+  // with its prologue fusions: the previous block's ln_out is applied by its consumers (FF1 up
+  // as an extra LayerNorm, FF1 down as the LayerNorm'ed residual base written to the other x
+  // buffer), and the depthwise conv + SiLU is pw2's A operand.
+  bool fused() const { return c->d.dt == CAC_F32 || M <= 8; }
+  float* cur = nullptr;  // buffer holding the residual stream (fused path: before ln_out)
 
   void layers() {
     const Dims& d = c->d;
     const LayerOff& lo = c->lay.lo;
+    cur = c->P<float>(c->lay.x);
+    float* other = c->P<float>(c->lay.x2);
+    const bool fz = fused();
+    const float *pre_g = nullptr, *pre_b = nullptr;  // previous block's ln_out (fused path)
     for (int l = 0; l < d.L; ++l) {
       char* lb = c->ws + c->lay.layers + (size_t)l * lo.size;
       const size_t kvl = (size_t)d.S * d.H * d.R * d.hd * d.esz;
       char* kr = c->ws + c->lay.kring + l * kvl;
       char* vr = c->ws + c->lay.vring + l * kvl;
       char* cr = c->ws + c->lay.cring + (size_t)l * d.S * d.Rc * d.D * d.esz;
-      // FF1 (macaron half step)
-      ff(lb, 0, lo.b_ff1_1, lo.b_ff1_2, lo.w_ff1_1, lo.w_ff1_2);
-      // MHSA: q to a buffer, k and v straight into the ring slots of their positions
+      auto F32 = [&](size_t off) { return (const float*)(lb + off); };
+      auto gemm_x = [&](const float* lng, const float* lnb, const void* W, int N, const EpiArgs& e, bool with_pre) {
+        GemmArgs g{};
+        g.M = M; g.N = N; g.K = d.D; g.W = W; g.epi = e;
+        g.A = cur; g.amap = RowMap{INT_MAX, 0, d.D};
+        g.a_f32 = 1; g.ln_g = lng; g.ln_b = lnb; g.a_scratch = c->P<void>(c->lay.y);
+        if (with_pre) { g.pre_g = pre_g; g.pre_b = pre_b; }
+        launch_gemm(L, g, d.dt, 0);
+      };
+      auto resid = [&](float alpha, const float* bias) {
+        EpiArgs e = epi0();
+        e.kind = EPI_RESID; e.bias = bias; e.out = cur; e.ldo = d.D; e.alpha = alpha;
+        return e;
+      };
+      // ---- FF1 (macaron half step)
+      {
+        EpiArgs up = epi0();
+        up.kind = EPI_SILU; up.bias = F32(lo.b_ff1_1); up.out = c->P<void>(c->lay.h); up.ldo = d.F;
+        L.role = "ff1_up";
+        gemm_x(F32(lo.ln[0]), F32(lo.ln[1]), lb + lo.w_ff1_1, d.F, up, fz);
+        EpiArgs dn = resid(0.5f, F32(lo.b_ff1_2));
+        GemmArgs g{};
+        g.M = M; g.N = d.D; g.K = d.F; g.W = lb + lo.w_ff1_2;
+        g.A = c->P<void>(c->lay.h); g.amap = RowMap{INT_MAX, 0, d.F};
+        if (fz) {  // out = ln_out_prev(cur) + 1/2 FF(...) into the other buffer
+          dn.out = other;
+          g.res_src = cur; g.res_g = pre_g; g.res_b = pre_b;
+        }
+        g.epi = dn;
+        L.role = "ff1_down";
+        launch_gemm(L, g, d.dt, 0);
+        if (fz) std::swap(cur, other);
+      }
+      // ---- MHSA: q to a buffer, k and v straight into the ring slots of their positions
       EpiArgs qkv = epi0();
-      qkv.kind = EPI_QKV; qkv.bias = (const float*)(lb + lo.b_qkv); qkv.qbuf = c->P<float>(c->lay.q);
+      qkv.kind = EPI_QKV; qkv.bias = F32(lo.b_qkv); qkv.qbuf = c->P<float>(c->lay.q);
       qkv.kring = kr; qkv.vring = vr;
-      gemm_ln((const float*)(lb + lo.ln[2]), (const float*)(lb + lo.ln[3]), lb + lo.w_qkv, 3 * d.D, d.D, qkv);
+      L.role = "qkv";
+      gemm_x(F32(lo.ln[2]), F32(lo.ln[3]), lb + lo.w_qkv, 3 * d.D, qkv, false);
       AttnArgs at{};
       at.cv = cv; at.q = c->P<float>(c->lay.q); at.kring = kr; at.vring = vr;
       at.posproj = c->P<float>(c->lay.posproj) + (size_t)l * d.H * d.nrel * d.hd;
-      at.pos_u = (const float*)(lb + lo.pos_u); at.pos_v = (const float*)(lb + lo.pos_v);
+      at.pos_u = F32(lo.pos_u); at.pos_v = F32(lo.pos_v);
       at.o = c->P<void>(c->lay.o);
       at.D = d.D; at.H = d.H; at.R = d.R; at.Lc = d.Lc; at.chunk = d.c; at.right = d.right;
       at.lookahead = d.lookahead; at.rel_lo = d.rel_lo; at.nrel = d.nrel;
@@ -303,36 +347,61 @@ struct Pass {
       {
         const double nrows = (double)cv.n_streams * cv.nf;
         const double bytes = kv_rows * 2.0 * d.D * d.esz + (double)d.H * d.nrel * d.hd * 4.0;
-        const double flops = 6.0 * nrows * (kv_rows / cv.n_streams) * d.D + 2.0 * nrows * d.nrel * d.D;
+        const double flops = 6.0 * nrows * (kv_rows / cv.n_streams) * d.D;
         L.tag("attention", bytes, flops);
       }
       launch_attention(L, at, d.dt, d.hd);
-      EpiArgs wo = epi0();
-      wo.kind = EPI_RESID; wo.bias = (const float*)(lb + lo.b_o); wo.out = c->P<void>(c->lay.x); wo.ldo = d.D; wo.alpha = 1.0f;
-      gemm_plain(c->P<void>(c->lay.o), d.D, lb + lo.w_o, d.D, d.D, wo);
-      // conv module: LN -> pw1 -> GLU into the ring; depthwise + SiLU; pw2 + residual
+      L.role = "wo";
+      gemm_plain(c->P<void>(c->lay.o), d.D, lb + lo.w_o, d.D, d.D, resid(1.0f, F32(lo.b_o)));
+      // ---- conv module: LN -> pw1 -> GLU into the ring; depthwise + SiLU; pw2 + residual
       EpiArgs glu = epi0();
-      glu.kind = EPI_GLU; glu.bias = (const float*)(lb + lo.b_pw1); glu.cring = cr;
-      gemm_ln((const float*)(lb + lo.ln[4]), (const float*)(lb + lo.ln[5]), lb + lo.w_pw1, 2 * d.D, d.D, glu);
-      DwArgs dw{cv, cr, (const float*)(lb + lo.dw_w), (const float*)(lb + lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
-      L.tag("dwconv", (double)cv.n_streams * (d.Kc + cv.nf) * d.D * d.esz, 2.0 * d.K * d.D * M);
-      launch_dwconv(L, dw, d.dt);
-      EpiArgs pw2 = epi0();
-      pw2.kind = EPI_RESID; pw2.bias = (const float*)(lb + lo.b_pw2); pw2.out = c->P<void>(c->lay.x); pw2.ldo = d.D; pw2.alpha = 1.0f;
-      gemm_plain(c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, d.D, pw2);
-      // FF2 (macaron half step), then the block's own LayerNorm in place
-      ff(lb, 6, lo.b_ff2_1, lo.b_ff2_2, lo.w_ff2_1, lo.w_ff2_2);
-      LnArgs lo_out{c->P<float>(c->lay.x), c->P<void>(c->lay.x), (const float*)(lb + lo.ln[8]),
-                    (const float*)(lb + lo.ln[9]), M, d.D, 1};
-      launch_ln(L, lo_out, d.dt);
+      glu.kind = EPI_GLU; glu.bias = F32(lo.b_pw1); glu.cring = cr;
+      L.role = "pw1";
+      gemm_x(F32(lo.ln[4]), F32(lo.ln[5]), lb + lo.w_pw1, 2 * d.D, glu, false);
+      if (fz) {
+        GemmArgs g{};
+        g.M = M; g.N = d.D; g.K = d.D; g.W = lb + lo.w_pw2; g.epi = resid(1.0f, F32(lo.b_pw2));
+        g.a_dw = 1; g.dw_ring = cr; g.dw_w = F32(lo.dw_w); g.dw_b = F32(lo.b_dw); g.dw_taps = d.K; g.dw_Rc = d.Rc;
+        g.amap = RowMap{INT_MAX, 0, d.D};
+        L.role = "pw2";
+        launch_gemm(L, g, d.dt, 0);
+      } else {
+        DwArgs dw{cv, cr, F32(lo.dw_w), F32(lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
+        L.tag("dwconv", (double)cv.n_streams * (d.Kc + cv.nf) * d.D * d.esz, 2.0 * d.K * d.D * M);
+        launch_dwconv(L, dw, d.dt);
+        L.role = "pw2";
+        gemm_plain(c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, d.D, resid(1.0f, F32(lo.b_pw2)));
+      }
+      // ---- FF2 (macaron half step)
+      {
+        EpiArgs up = epi0();
+        up.kind = EPI_SILU; up.bias = F32(lo.b_ff2_1); up.out = c->P<void>(c->lay.h); up.ldo = d.F;
+        L.role = "ff2_up";
+        gemm_x(F32(lo.ln[6]), F32(lo.ln[7]), lb + lo.w_ff2_1, d.F, up, false);
+        L.role = "ff2_down";
+        gemm_plain(c->P<void>(c->lay.h), d.F, lb + lo.w_ff2_2, d.D, d.F, resid(0.5f, F32(lo.b_ff2_2)));
+      }
+      // ---- the block's own LayerNorm: in place, or left to the consumers (fused path)
+      if (fz) {
+        pre_g = F32(lo.ln[8]); pre_b = F32(lo.ln[9]);
+      } else {
+        LnArgs lo_out{cur, cur, F32(lo.ln[8]), F32(lo.ln[9]), M, d.D, 1};
+        launch_ln(L, lo_out, d.dt);
+      }
     }
+    last_g = pre_g; last_b = pre_b;
   }
+  const float *last_g = nullptr, *last_b = nullptr;  // ln_out still to apply (fused path)
 
   // encoder-side joint projection of the rows picked by amap into d_out (rows remapped by omap)
   void joint(float* d_out, int rows, RowMap amap, const int32_t* omap, int ogroup, int ostride) {
     const Dims& d = c->d;
     if (d.P == 0) {
-      CopyRowsArgs cp{c->P<float>(c->lay.x), amap, d_out, omap, ogroup, ostride, rows, d.D};
+      if (last_g) {  // apply the last ln_out before handing out the hidden rows
+        LnArgs ln{cur, cur, last_g, last_b, M, d.D, 1};
+        launch_ln(L, ln, d.dt);
+      }
+      CopyRowsArgs cp{cur, amap, d_out, omap, ogroup, ostride, rows, d.D};
       launch_copy_rows(L, cp);
       return;
     }
@@ -340,8 +409,10 @@ struct Pass {
     e.kind = EPI_F32; e.out = d_out; e.ldo = d.P; e.bias = c->P<float>(c->lay.bj);
     e.omap = omap; e.ogroup = ogroup; e.ostride = ostride;
     GemmArgs g{};
-    g.M = rows; g.N = d.P; g.K = d.D; g.A = c->P<float>(c->lay.x); g.amap = amap;
+    g.M = rows; g.N = d.P; g.K = d.D; g.A = cur; g.amap = amap;
     g.W = c->P<void>(c->lay.wj); g.epi = e; g.a_f32 = 1; g.a_scratch = c->P<void>(c->lay.y);
+    g.ln_g = last_g; g.ln_b = last_b;
+    L.role = "joint";
     launch_gemm(L, g, d.dt, 0);
   }
 };
@@ -515,6 +586,134 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
 }
 
 
+}  // extern "C"
+
+namespace {
+
+// Everything one push enqueues after the id lists are on the device.
+void enqueue_push(cac_ctx* c, Launcher& L, int n, const int32_t* ids, int n_frames, const void* d_input, float* d_out,
+                  const std::vector<int32_t>& cids) {
+  const Dims& d = c->d;
+  const int32_t* dids = c->P<int32_t>(c->lay.ids);
+  int32_t* dpos = c->P<int32_t>(c->lay.pos);
+  int32_t* dpend = c->P<int32_t>(c->lay.pend);
+  if (!d.lookahead) {
+    CallView cv{dids, dpos, n_frames, n, c->P<int32_t>(c->lay.cpos)};
+    const int M = n * n_frames;
+    if (d.fe) {
+      FeWindowArgs fw{cv, d_input, c->ws + c->lay.tail, c->ws + c->lay.win, d.bins, d.tail, d.mpc};
+      launch_fe_window(L, fw, d.dt);
+      const int wrows = d.tail + d.mpc;
+      struct { int rows, neg; size_t in, out; int K; RowMap m; } st3[3] = {
+          {11, 6, c->lay.win, c->lay.fe1, 3 * d.bins, RowMap{11, wrows * d.bins, 2 * d.bins}},
+          {5, 2, c->lay.fe1, c->lay.fe2, 3 * d.D, RowMap{5, 11 * d.D, 2 * d.D}},
+          {2, 0, c->lay.fe2, c->lay.x, 3 * d.D, RowMap{2, 5 * d.D, 2 * d.D}}};
+      for (int i = 0; i < 3; ++i) {
+        EpiArgs e{};
+        e.cv = cv; e.bias = c->P<float>(c->lay.fe_b[i]);
+        if (i < 2) { e.kind = EPI_RELU_FE; e.out = c->ws + st3[i].out; e.ldo = d.D; e.fe_rows_per_stream = st3[i].rows; e.fe_neg_rows = st3[i].neg; }
+        else { e.kind = EPI_F32; e.out = c->ws + c->lay.x; e.ldo = d.D; }
+        GemmArgs g{};
+        g.M = n * st3[i].rows; g.N = d.D; g.K = st3[i].K; g.A = c->ws + st3[i].in; g.amap = st3[i].m;
+        g.W = c->ws + c->lay.fe_w[i]; g.epi = e;
+        L.role = i == 0 ? "fe_conv1" : (i == 1 ? "fe_conv2" : "fe_conv3");
+        launch_gemm(L, g, d.dt, 0);
+      }
+    } else {
+      InputArgs ia{cv, d_input, c->P<float>(c->lay.x), M, d.D};
+      launch_input(L, ia, d.dt);
+    }
+    double kvr = 0;
+    for (int i = 0; i < n; ++i) kvr += std::min(c->hpos[ids[i]], d.Lc) + n_frames;
+    Pass ps{c, L, cv, M, kvr};
+    ps.layers();
+    ps.joint(d_out, M, RowMap{INT_MAX, 0, d.D}, nullptr, 1, 0);
+    AdvanceArgs ad{dids, dpos, dpend, n, n_frames, 0};
+    launch_advance(L, ad);
+  } else {
+    CallView pv{dids, dpos, d.ne, n, c->P<int32_t>(c->lay.cpos)};
+    LaStoreArgs ls{pv, dpend, d_input, c->ws + c->lay.x0, d.D, d.Rx};
+    launch_la_store(L, ls, d.dt);
+    AdvanceArgs a1{dids, dpos, dpend, n, 0, d.ne};
+    launch_advance(L, a1);
+    const int nC = (int)cids.size();
+    if (nC > 0) {
+      const int32_t* dcids = c->P<int32_t>(c->lay.cids);
+      CallView cv{dcids, dpos, d.nc, nC, c->P<int32_t>(c->lay.ccpos)};
+      LaGatherArgs lg{cv, c->ws + c->lay.x0, c->P<float>(c->lay.x), d.D, d.Rx};
+      launch_la_gather(L, lg, d.dt);
+      double kvr = 0;
+      for (int id : cids) kvr += std::min(c->hpos[id], d.Lc) + d.nc;
+      Pass ps{c, L, cv, nC * d.nc, kvr};
+      ps.layers();
+      ps.joint(d_out, nC * d.ne, RowMap{d.ne, d.nc * d.D, d.D}, c->P<int32_t>(c->lay.cidx), d.ne, d.ne);
+      AdvanceArgs a2{dcids, dpos, dpend, nC, d.ne, -d.ne};
+      launch_advance(L, a2);
+    }
+  }
+}
+
+// Offsets of 8-byte fields holding exactly the value p.
+std::vector<size_t> find_ptr(const std::vector<char>& args, const void* p) {
+  std::vector<size_t> offs;
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  for (size_t o = 0; o + 8 <= args.size(); o += 8) {
+    uint64_t w;
+    memcpy(&w, args.data() + o, 8);
+    if (w == v) offs.push_back(o);
+  }
+  return offs;
+}
+
+// Replay the recorded graph of this call shape (recording it on first use), re-pointing the
+// nodes that hold the caller's input and output pointers.
+hipError_t push_graph(cac_ctx* c, int n, const int32_t* ids, int n_frames, const void* d_input, float* d_out,
+                      const std::vector<int32_t>& cids) {
+  const uint64_t key = ((uint64_t)n << 32) | ((uint64_t)n_frames << 16) | (uint64_t)cids.size();
+  auto it = c->graphs.find(key);
+  if (it == c->graphs.end()) {
+    cac_ctx::Graph gr;
+    hipError_t e = hipGraphCreate(&gr.g, 0);
+    if (e != hipSuccess) return e;
+    Launcher L;
+    L.stream = c->stream;
+    L.graph = gr.g;
+    L.rec = &gr.nodes;
+    enqueue_push(c, L, n, ids, n_frames, d_input, d_out, cids);
+    if (L.err != hipSuccess) { (void)hipGraphDestroy(gr.g); return L.err; }
+    e = hipGraphInstantiate(&gr.exec, gr.g, nullptr, nullptr, 0);
+    if (e != hipSuccess) { (void)hipGraphDestroy(gr.g); return e; }
+    for (const NodeRec& r : gr.nodes) {
+      gr.in_offs.push_back(find_ptr(r.args, d_input));
+      gr.out_offs.push_back(find_ptr(r.args, d_out));
+    }
+    gr.in = d_input;
+    gr.out = d_out;
+    it = c->graphs.emplace(key, std::move(gr)).first;
+  }
+  cac_ctx::Graph& gr = it->second;
+  if (gr.in != d_input || gr.out != d_out) {
+    for (size_t i = 0; i < gr.nodes.size(); ++i) {
+      if (gr.in_offs[i].empty() && gr.out_offs[i].empty()) continue;
+      NodeRec& r = gr.nodes[i];
+      for (size_t o : gr.in_offs[i]) memcpy(r.args.data() + o, &d_input, 8);
+      for (size_t o : gr.out_offs[i]) memcpy(r.args.data() + o, &d_out, 8);
+      hipKernelNodeParams p = r.p;
+      void* kp[1] = {r.args.data()};
+      p.kernelParams = kp;
+      hipError_t e = hipGraphExecKernelNodeSetParams(gr.exec, r.node, &p);
+      if (e != hipSuccess) return e;
+    }
+    gr.in = d_input;
+    gr.out = d_out;
+  }
+  return hipGraphLaunch(gr.exec, c->stream);
+}
+
+}  // namespace
+
+extern "C" {
+
 int32_t cac_push_chunk(cac_ctx* c, int32_t n, const int32_t* ids, int32_t n_frames, const void* d_input,
                        float* d_out, int32_t* h_emitted) {
   if (!c) return CAC_EINVAL;
@@ -529,6 +728,7 @@ int32_t cac_push_chunk(cac_ctx* c, int32_t n, const int32_t* ids, int32_t n_fram
     return c->fail(CAC_EINVAL, "n_frames must be a multiple of att_chunk in [att_chunk, max_push_frames]");
   }
   if (!d_input || !d_out) return c->fail(CAC_EINVAL, "input or output pointer is NULL");
+  if ((const void*)d_out == d_input) return c->fail(CAC_EINVAL, "input and output must be different buffers");
 
   // host bookkeeping decides who runs a pass (lookahead: streams whose pending frames reach
   // n_emit + n_lookahead after this push)
@@ -557,71 +757,29 @@ int32_t cac_push_chunk(cac_ctx* c, int32_t n, const int32_t* ids, int32_t n_fram
   };
   if (c->dry) { commit(); return c->fail(CAC_ENODEV, "dry-run context: no device work"); }
 
-  Launcher L;
-  L.stream = c->stream;
-  if (c->profiling) L.prof = &c->prof;
-  L.err = upload(c, c->dev_ids, c->lay.ids, ids, n);
-  const int32_t* dids = c->P<int32_t>(c->lay.ids);
-  int32_t* dpos = c->P<int32_t>(c->lay.pos);
-  int32_t* dpend = c->P<int32_t>(c->lay.pend);
-  if (!d.lookahead) {
-    CallView cv{dids, dpos, n_frames, n};
-    const int M = n * n_frames;
-    if (d.fe) {
-      FeWindowArgs fw{cv, d_input, c->ws + c->lay.tail, c->ws + c->lay.win, d.bins, d.tail, d.mpc};
-      launch_fe_window(L, fw, d.dt);
-      const int wrows = d.tail + d.mpc;
-      struct { int rows, neg; size_t in, out; int K; RowMap m; } st3[3] = {
-          {11, 6, c->lay.win, c->lay.fe1, 3 * d.bins, RowMap{11, wrows * d.bins, 2 * d.bins}},
-          {5, 2, c->lay.fe1, c->lay.fe2, 3 * d.D, RowMap{5, 11 * d.D, 2 * d.D}},
-          {2, 0, c->lay.fe2, c->lay.x, 3 * d.D, RowMap{2, 5 * d.D, 2 * d.D}}};
-      for (int i = 0; i < 3; ++i) {
-        EpiArgs e{};
-        e.cv = cv; e.bias = c->P<float>(c->lay.fe_b[i]);
-        if (i < 2) { e.kind = EPI_RELU_FE; e.out = c->ws + st3[i].out; e.ldo = d.D; e.fe_rows_per_stream = st3[i].rows; e.fe_neg_rows = st3[i].neg; }
-        else { e.kind = EPI_F32; e.out = c->ws + c->lay.x; e.ldo = d.D; }
-        GemmArgs g{};
-        g.M = n * st3[i].rows; g.N = d.D; g.K = st3[i].K; g.A = c->ws + st3[i].in; g.amap = st3[i].m;
-        g.W = c->ws + c->lay.fe_w[i]; g.epi = e;
-        launch_gemm(L, g, d.dt, 0);
-      }
-    } else {
-      InputArgs ia{d_input, c->P<float>(c->lay.x), M, d.D};
-      launch_input(L, ia, d.dt);
-    }
-    double kvr = 0;
-    for (int i = 0; i < n; ++i) kvr += std::min(c->hpos[ids[i]], d.Lc) + n_frames;
-    Pass ps{c, L, cv, M, kvr};
-    ps.layers();
-    ps.joint(d_out, M, RowMap{INT_MAX, 0, d.D}, nullptr, 1, 0);
-    AdvanceArgs ad{dids, dpos, dpend, n, n_frames, 0};
-    launch_advance(L, ad);
+  hipError_t e = upload(c, c->dev_ids, c->lay.ids, ids, n);
+  if (e == hipSuccess && !cids.empty()) e = upload(c, c->dev_cids, c->lay.cids, cids.data(), (int)cids.size());
+  if (e == hipSuccess && !cids.empty()) e = upload(c, c->dev_cidx, c->lay.cidx, cidx.data(), (int)cidx.size());
+  if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("id upload failed: ") + hipGetErrorString(e));
+  if (c->use_graph && !c->profiling) {
+    e = push_graph(c, n, ids, n_frames, d_input, d_out, cids);
+    if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("graph replay failed: ") + hipGetErrorString(e));
+    rc = emitted;
   } else {
-    CallView pv{dids, dpos, d.ne, n};
-    LaStoreArgs ls{pv, dpend, d_input, c->ws + c->lay.x0, d.D, d.Rx};
-    launch_la_store(L, ls, d.dt);
-    AdvanceArgs a1{dids, dpos, dpend, n, 0, d.ne};
-    launch_advance(L, a1);
-    const int nC = (int)cids.size();
-    if (nC > 0) {
-      if (L.err == hipSuccess) L.err = upload(c, c->dev_cids, c->lay.cids, cids.data(), nC);
-      if (L.err == hipSuccess) L.err = upload(c, c->dev_cidx, c->lay.cidx, cidx.data(), nC);
-      const int32_t* dcids = c->P<int32_t>(c->lay.cids);
-      CallView cv{dcids, dpos, d.nc, nC};
-      LaGatherArgs lg{cv, c->ws + c->lay.x0, c->P<float>(c->lay.x), d.D, d.Rx};
-      launch_la_gather(L, lg, d.dt);
-      double kvr = 0;
-      for (int id : cids) kvr += std::min(c->hpos[id], d.Lc) + d.nc;
-      Pass ps{c, L, cv, nC * d.nc, kvr};
-      ps.layers();
-      ps.joint(d_out, nC * d.ne, RowMap{d.ne, d.nc * d.D, d.D}, c->P<int32_t>(c->lay.cidx), d.ne, d.ne);
-      AdvanceArgs a2{dcids, dpos, dpend, nC, d.ne, -d.ne};
-      launch_advance(L, a2);
-    }
+    Launcher L;
+    L.stream = c->stream;
+    if (c->profiling) L.prof = &c->prof;
+    enqueue_push(c, L, n, ids, n_frames, d_input, d_out, cids);
+    rc = finish(c, L, emitted);
   }
-  rc = finish(c, L, emitted);
   if (rc >= 0) commit();
   return rc;
+}
+
+int32_t cac_set_graph(cac_ctx* c, int32_t enable) {
+  if (!c) return CAC_EINVAL;
+  c->use_graph = enable != 0;
+  return CAC_OK;
 }
 
 int32_t cac_reset_stream(cac_ctx* c, int32_t n, const int32_t* ids) {
@@ -676,7 +834,7 @@ int32_t cac_flush(cac_ctx* c, int32_t n, const int32_t* ids, float* d_out, int32
     if (L.err == hipSuccess) L.err = upload(c, c->dev_cidx, c->lay.cidx, cidx.data(), nC);
     const int32_t* dcids = c->P<int32_t>(c->lay.cids);
     int32_t* dpos = c->P<int32_t>(c->lay.pos);
-    CallView cv{dcids, dpos, m, nC};
+    CallView cv{dcids, dpos, m, nC, c->P<int32_t>(c->lay.ccpos)};
     LaGatherArgs lg{cv, c->ws + c->lay.x0, c->P<float>(c->lay.x), d.D, d.Rx};
     launch_la_gather(L, lg, d.dt);
     double kvr = 0;
@@ -813,7 +971,7 @@ int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t
   if (dtype != CAC_F32 && dtype != CAC_BF16) return CAC_EINVAL;
   if (M < 1 || N < 1 || K < 1 || !d_A || !d_W || !d_C) return CAC_EINVAL;
   if (path < 0 || path > 2 || (path == 2 && dtype != CAC_BF16)) return CAC_EINVAL;
-  if (dtype == CAC_BF16 && path != 1 && K % 32) return CAC_EINVAL;  // MFMA tiles step K by 32
+  if (path == 2 && K % 64) return CAC_EINVAL;  // MFMA tiles step K by 64
   if ((size_t)8 * K * 4 > 160 * 1024 && path != 2) return CAC_EINVAL;
   kernels_init();
   Launcher L;

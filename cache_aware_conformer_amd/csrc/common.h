@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstdio>
 #include <string>
 #include <vector>
 
@@ -61,6 +62,7 @@ struct CallView {
   const int32_t* pos;  // [max_streams] stream positions (device)
   int nf;              // frames per stream in this call
   int n_streams;
+  int32_t* cpos;       // [n_streams] pos[ids[s]] of this call, written by the call's first kernel
 };
 
 // ------------------------------------------------------------------------ epilogues
@@ -105,6 +107,17 @@ struct GemmArgs {
   const float* ln_g;     // compute dtype before the product; the MFMA path first writes that
   const float* ln_b;     // operand to a_scratch ([M][K], compute dtype)
   void* a_scratch;
+  // small-M kernel only:
+  const float* pre_g;    // LayerNorm the A rows with (pre_g, pre_b) before (ln_g, ln_b)
+  const float* pre_b;
+  int a_dw;              // A rows are SiLU(depthwise conv over the ring) (see DwArgs fields)
+  const void* dw_ring;   // layer base [S][Rc][K]
+  const float* dw_w;     // [taps][K]
+  const float* dw_b;     // [K]
+  int dw_taps, dw_Rc;
+  const float* res_src;  // EPI_RESID: out = LN(res_src rows; res_g, res_b) + alpha (acc + b)
+  const float* res_g;    // (res_g null: out = res_src + alpha (acc + b)); out != res_src
+  const float* res_b;
   int upb;               // small-M kernel: output units (columns, or GLU channels) per block
   EpiArgs epi;
 };
@@ -141,6 +154,7 @@ struct DwArgs {
 };
 
 struct InputArgs {      // x[m][c] = in[m][c] (float32 residual from compute dtype input)
+  CallView cv;          // also fills cv.cpos
   const void* in;
   float* x;
   int M, D;
@@ -230,17 +244,40 @@ struct Profiler {
   ~Profiler();
 };
 
+// A kernel node recorded into a graph, with a copy of its argument bytes so pointer arguments
+// can be re-pointed before a replay.
+struct NodeRec {
+  hipGraphNode_t node;
+  hipKernelNodeParams p;
+  std::vector<char> args;
+};
+
 struct Launcher {
   hipStream_t stream = nullptr;
+  std::vector<NodeRec>* rec = nullptr;  // record mode: nodes appended here
   hipGraph_t graph = nullptr;        // non-null: record instead of launch
   hipGraphNode_t last = nullptr;
   hipGraphNode_t last_node = nullptr;  // node of the most recent launch (record mode)
   hipError_t err = hipSuccess;
   Profiler* prof = nullptr;          // direct launches only
   const char* tag_name = "kernel";   // set by the wrappers before each launch
+  const char* role = nullptr;        // optional role of the next dense product ("qkv", ...)
+  char name_buf[64];
   double tag_bytes = 0.0, tag_flops = 0.0;
-  void tag(const char* n, double bytes, double flops) { tag_name = n; tag_bytes = bytes; tag_flops = flops; }
-  void launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* args);
+  void tag(const char* n, double bytes, double flops) {
+    tag_name = n;
+    if (role) {
+      snprintf(name_buf, sizeof(name_buf), "%s/%s", n, role);
+      tag_name = name_buf;
+      role = nullptr;
+    }
+    tag_bytes = bytes;
+    tag_flops = flops;
+  }
+  void launch_raw(const void* fn, dim3 grid, dim3 block, size_t shmem, void* args, size_t args_size);
+  template <class A> void launch(const void* fn, dim3 grid, dim3 block, size_t shmem, A* args) {
+    launch_raw(fn, grid, block, shmem, (void*)args, sizeof(A));
+  }
 };
 
 // ------------------------------------------------------------------------ wrappers

@@ -60,7 +60,7 @@ Profiler::~Profiler() {
   for (hipEvent_t e : free_ev) (void)hipEventDestroy(e);
 }
 
-void Launcher::launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void* args) {
+void Launcher::launch_raw(const void* fn, dim3 grid, dim3 block, size_t shmem, void* args, size_t args_size) {
   if (err != hipSuccess) return;
   if (grid.x == 0 || grid.y == 0 || grid.z == 0) return;
   void* kp[1] = {args};
@@ -87,7 +87,18 @@ void Launcher::launch(const void* fn, dim3 grid, dim3 block, size_t shmem, void*
   p.extra = nullptr;
   hipGraphNode_t node;
   err = hipGraphAddKernelNode(&node, graph, last ? &last : nullptr, last ? 1 : 0, &p);
-  if (err == hipSuccess) last = last_node = node;
+  if (err == hipSuccess) {
+    last = last_node = node;
+    if (rec) {
+      NodeRec r;
+      r.node = node;
+      r.p = p;
+      r.p.kernelParams = nullptr;
+      r.args.assign((const char*)args, (const char*)args + args_size);
+      rec->push_back(std::move(r));
+    }
+  }
+  tag_bytes = tag_flops = 0.0;
 }
 
 // =============================================================================== epilogue
@@ -106,7 +117,7 @@ __device__ __forceinline__ void epi_one(const EpiArgs& e, int m, int n, float v)
     case EPI_RELU_FE: {
       if (e.bias) v += e.bias[n];
       int s = m / e.fe_rows_per_stream, j = m % e.fe_rows_per_stream;
-      bool before_start = e.cv.pos[e.cv.ids[s]] == 0 && j < e.fe_neg_rows;
+      bool before_start = e.cv.cpos[s] == 0 && j < e.fe_neg_rows;
       st<T>((T*)e.out + (long)m * e.ldo + n, before_start ? 0.0f : fmaxf(v, 0.0f));
     } break;
     case EPI_RESID: {
@@ -127,7 +138,7 @@ __device__ __forceinline__ void epi_one(const EpiArgs& e, int m, int n, float v)
       } else {
         int s = m / e.cv.nf, i = m % e.cv.nf;
         int id = e.cv.ids[s];
-        int slot = (e.cv.pos[id] + i) % e.R;
+        int slot = (e.cv.cpos[s] + i) % e.R;
         int h = c / e.hd, d = c % e.hd;
         T* ring = (T*)(which == 1 ? e.kring : e.vring);
         st<T>(ring + (((long)id * e.H + h) * e.R + slot) * e.hd + d, v);
@@ -145,7 +156,7 @@ __device__ __forceinline__ void epi_glu(const EpiArgs& e, int m, int c, float va
   float g = va * sigmoid_f(vb);
   int s = m / e.cv.nf, i = m % e.cv.nf;
   int id = e.cv.ids[s];
-  int slot = (e.cv.pos[id] + i) % e.Rc;
+  int slot = (e.cv.cpos[s] + i) % e.Rc;
   st<T>((T*)e.cring + ((long)id * e.Rc + slot) * e.D + c, g);
 }
 
@@ -153,106 +164,314 @@ __device__ __forceinline__ void epi_glu(const EpiArgs& e, int m, int c, float va
 __device__ __forceinline__ int glu_a_col(int c) { return (c >> 5) * 64 + (c & 31); }
 
 // =============================================================================== small-M GEMM
-// C[M][N] = A[M][K] W[N][K]^T for M up to a few rows per block. The block's MR rows of A sit
-// in LDS as float (optionally LayerNorm'ed, and rounded to bf16 when the weights are bf16);
-// each wave owns whole output columns and streams their weight rows once with 16-byte loads.
-template <typename TW, int VEC> struct WLoad;
-template <> struct WLoad<float, 4> {
-  static __device__ __forceinline__ void get(const float* p, float* w) {
-    float4 v = *(const float4*)p; w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-  }
-};
-template <> struct WLoad<float, 1> {
-  static __device__ __forceinline__ void get(const float* p, float* w) { w[0] = *p; }
-};
-template <> struct WLoad<bf16_t, 8> {
-  static __device__ __forceinline__ void get(const bf16_t* p, float* w) {
-    uint4 v = *(const uint4*)p;
-    uint32_t u[4] = {v.x, v.y, v.z, v.w};
+// C[M][N] = A[M][K] W[N][K]^T for few rows (MR per block). Each wave owns whole output units
+// (a column, or a GLU value/gate column pair) and issues the 16-byte loads of all their weight
+// rows before anything else, so HBM latency overlaps the A prologue: the block's rows of A are
+// staged in LDS as float, optionally formed from the depthwise ring (A = SiLU(dwconv)), then
+// LayerNorm'ed (an optional earlier LayerNorm first) and rounded to bf16 for bf16 weights.
+// KCH > 0: K == KCH * 64 * (16 / sizeof(TW)) and weights sit in registers; KCH == 0: generic K.
+template <typename TW> __device__ __forceinline__ void wunpack(const uint4& r, float* f);
+template <> __device__ __forceinline__ void wunpack<float>(const uint4& r, float* f) {
+  f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y); f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+}
+template <> __device__ __forceinline__ void wunpack<bf16_t>(const uint4& r, float* f) {
+  const uint32_t u[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { w[2 * i] = __uint_as_float(u[i] << 16); w[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u); }
-  }
-};
-template <> struct WLoad<bf16_t, 1> {
-  static __device__ __forceinline__ void get(const bf16_t* p, float* w) { w[0] = bf2f(*p); }
+  for (int i = 0; i < 4; ++i) { f[2 * i] = __uint_as_float(u[i] << 16); f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u); }
+}
+
+template <int KCH, bool GLU> struct GemvShape {
+  static constexpr int COLS = GLU ? 2 : 1;
+  static constexpr int UMAX = KCH > 0 ? (8 / (COLS * KCH) > 0 ? 8 / (COLS * KCH) : 1) : 1;
+  static constexpr int NR = KCH > 0 ? UMAX * COLS * KCH : 1;
 };
 
-template <typename TW, typename TA, int MR, int VEC>
+constexpr int GEMV_LPL = 16;  // LayerNorm parameters held per lane: K <= 1024
+
+// LayerNorm of one LDS row with this lane's gains/shifts in registers (k = lane + 64 j).
+__device__ __forceinline__ void row_ln_regs(float* row, int K, const float* g, const float* b, int lane) {
+  const int per = K / 64;
+  float v[GEMV_LPL];
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < GEMV_LPL; ++j) { v[j] = j < per ? row[lane + 64 * j] : 0.0f; s += v[j]; }
+  const float mean = wave_sum(s) / (float)K;
+  float q = 0.0f;
+#pragma unroll
+  for (int j = 0; j < GEMV_LPL; ++j) if (j < per) { const float d = v[j] - mean; q += d * d; }
+  const float rstd = rsqrtf(wave_sum(q) / (float)K + 1e-5f);
+#pragma unroll
+  for (int j = 0; j < GEMV_LPL; ++j) if (j < per) row[lane + 64 * j] = (v[j] - mean) * rstd * g[j] + b[j];
+}
+
+// Small-M dense product. Every global read the block will need is issued in one phase at the
+// start (weights, A rows, LayerNorm parameters, epilogue biases and residual bases, the rows'
+// stream slots), so one memory latency is paid per launch instead of one per dependent step.
+template <typename TW, typename TA, int MR, int KCH, bool GLU>
 __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
-  const int units_per_block = a.upb;
-  extern __shared__ float sA[];  // [MR][K]
+  extern __shared__ float sm[];
+  using Sh = GemvShape<KCH, GLU>;
+  constexpr int VEC = 16 / sizeof(TW);
+  constexpr int COLS = Sh::COLS, UMAX = Sh::UMAX, NR = Sh::NR;
+  constexpr int UE = KCH > 0 ? UMAX : 1;  // units whose epilogue operands are prefetched
   const int K = a.K;
+  float* sA = sm;              // [MR][K]
+  float* stats = sm + MR * K;  // [MR][2] mean, rstd of the residual base rows
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m0 = blockIdx.y * MR;
   const int mr = min(MR, a.M - m0);
-  for (int idx = tid; idx < MR * K; idx += 256) {
-    int r = idx / K, k = idx - r * K;
-    float v = 0.0f;
-    if (r < mr) v = ld<TA>((const TA*)a.A + a.amap.off(m0 + r) + k);
-    sA[idx] = v;
+  const int units = GLU ? a.N / 2 : a.N;
+  const int upw = a.upb;
+  const int u0 = (blockIdx.x * 4 + wave) * upw;
+  const TW* W = (const TW*)a.W;
+  const EpiArgs& e = a.epi;
+  const int D = e.ldo;  // residual row length for EPI_RESID
+
+  // ================= phase 0: issue every global load
+  // (a) weight rows of this wave's units
+  uint4 wr[NR];
+  if constexpr (KCH > 0) {
+#pragma unroll
+    for (int u = 0; u < UMAX; ++u)
+#pragma unroll
+      for (int c = 0; c < COLS; ++c)
+#pragma unroll
+        for (int k = 0; k < KCH; ++k) {
+          const int unit = u0 + u;
+          const bool ok = u < upw && unit < units;
+          const int col = GLU ? glu_a_col(unit) + 32 * c : unit;
+          wr[(u * COLS + c) * KCH + k] = ok ? *(const uint4*)(W + (long)col * K + (k * 64 + lane) * VEC) : make_uint4(0u, 0u, 0u, 0u);
+        }
   }
-  __syncthreads();
-  // bf16 weights with a float32 A: the operand is rounded to bf16 (after LayerNorm, if any)
-  constexpr bool round_bf16 = sizeof(TW) == 2 && sizeof(TA) == 4;
-  if (round_bf16 && !a.ln_g) {
-    for (int idx = tid; idx < MR * K; idx += 256) sA[idx] = bf2f(f2bf(sA[idx]));
-    __syncthreads();
+  // (b) LayerNorm parameters of this lane's columns
+  float lg[GEMV_LPL], lb[GEMV_LPL], pg[GEMV_LPL], pb[GEMV_LPL];
+  const int per = K / 64;
+#pragma unroll
+  for (int j = 0; j < GEMV_LPL; ++j) {
+    const bool ok = j < per;
+    lg[j] = (ok && a.ln_g) ? a.ln_g[lane + 64 * j] : 0.0f;
+    lb[j] = (ok && a.ln_g) ? a.ln_b[lane + 64 * j] : 0.0f;
+    pg[j] = (ok && a.pre_g) ? a.pre_g[lane + 64 * j] : 0.0f;
+    pb[j] = (ok && a.pre_g) ? a.pre_b[lane + 64 * j] : 0.0f;
   }
-  if (a.ln_g) {
-    for (int r = wave; r < mr; r += 4) {
-      float* row = sA + r * K;
-      float s = 0.0f;
-      for (int k = lane; k < K; k += 64) s += row[k];
-      const float mean = wave_sum(s) / (float)K;
-      float q = 0.0f;
-      for (int k = lane; k < K; k += 64) { float d = row[k] - mean; q += d * d; }
-      const float rstd = rsqrtf(wave_sum(q) / (float)K + 1e-5f);
-      for (int k = lane; k < K; k += 64) {
-        float y = (row[k] - mean) * rstd * a.ln_g[k] + a.ln_b[k];
-        row[k] = round_bf16 ? bf2f(f2bf(y)) : y;
+  // (c) epilogue operands of this lane's row (lane < mr) for each prefetched unit
+  const int m_lane = m0 + (lane < mr ? lane : 0);
+  int row_slot_pos = 0, row_id = 0;  // stream id and position of this lane's row
+  if (lane < mr && (e.kind == EPI_QKV || GLU || e.kind == EPI_RELU_FE)) {
+    const int sidx = (e.kind == EPI_RELU_FE ? m_lane / e.fe_rows_per_stream : m_lane / e.cv.nf);
+    row_id = e.cv.ids[sidx];
+    row_slot_pos = e.cv.cpos[sidx];
+  }
+  float eb[UE][COLS], er[UE];
+  int omap_row = m_lane;
+#pragma unroll
+  for (int u = 0; u < UE; ++u) {
+    const int unit = u0 + u;
+    const bool ok = lane < mr && u < upw && unit < units && KCH > 0;
+#pragma unroll
+    for (int c = 0; c < COLS; ++c)
+      eb[u][c] = (ok && e.bias) ? e.bias[GLU ? unit + c * e.D : unit] : 0.0f;
+    er[u] = 0.0f;
+    if (ok && e.kind == EPI_RESID) er[u] = a.res_src ? a.res_src[(long)m_lane * D + unit] : ((const float*)e.out)[(long)m_lane * D + unit];
+  }
+  if (e.kind == EPI_F32 && e.omap && lane < mr) omap_row = e.omap[m_lane / e.ogroup] * e.ostride + m_lane % e.ogroup;
+  // (d) residual-base rows for the LayerNorm statistics (rows wave and wave + 4)
+  constexpr int RPW = MR > 4 ? 2 : 1;
+  float xv[RPW][GEMV_LPL];
+  const bool res_stats = a.res_src && a.res_g;
+#pragma unroll
+  for (int t = 0; t < RPW; ++t) {
+    const int r = wave + 4 * t;
+    const float* x = a.res_src + (long)(m0 + (r < mr ? r : 0)) * D;
+#pragma unroll
+    for (int j = 0; j < GEMV_LPL; ++j) xv[t][j] = (res_stats && r < mr && j < D / 64) ? x[lane + 64 * j] : 0.0f;
+  }
+  // (e) A rows into LDS
+  if (a.a_dw) {
+    const int items = MR * (K / 4);
+    for (int it = tid; it < items; it += 256) {
+      const int r = it / (K / 4), ch = (it - r * (K / 4)) * 4;
+      float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (r < mr) {
+        const int m = m0 + r, sidx = m / e.cv.nf, i = m % e.cv.nf;
+        const int id = e.cv.ids[sidx];
+        const int p = e.cv.cpos[sidx] + i;
+        const TA* ring = (const TA*)a.dw_ring + (long)id * a.dw_Rc * K + ch;
+        float g[16][4];
+        float4 w[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int q = p - (a.dw_taps - 1) + t;
+          const bool ok = t < a.dw_taps && q >= 0;
+          w[t] = t < a.dw_taps ? *(const float4*)(a.dw_w + t * K + ch) : make_float4(0.f, 0.f, 0.f, 0.f);
+          if constexpr (sizeof(TA) == 4) {
+            const float4 v = ok ? *(const float4*)(ring + (long)(q % a.dw_Rc) * K) : make_float4(0.f, 0.f, 0.f, 0.f);
+            g[t][0] = v.x; g[t][1] = v.y; g[t][2] = v.z; g[t][3] = v.w;
+          } else {
+            const uint2 v = ok ? *(const uint2*)(ring + (long)(q % a.dw_Rc) * K) : make_uint2(0u, 0u);
+            g[t][0] = __uint_as_float(v.x << 16); g[t][1] = __uint_as_float(v.x & 0xffff0000u);
+            g[t][2] = __uint_as_float(v.y << 16); g[t][3] = __uint_as_float(v.y & 0xffff0000u);
+          }
+        }
+        const float4 b4 = *(const float4*)(a.dw_b + ch);
+        acc[0] = b4.x; acc[1] = b4.y; acc[2] = b4.z; acc[3] = b4.w;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          acc[0] += w[t].x * g[t][0]; acc[1] += w[t].y * g[t][1]; acc[2] += w[t].z * g[t][2]; acc[3] += w[t].w * g[t][3];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = silu_f(acc[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sA[r * K + ch + q] = acc[q];
+    }
+  } else if (K % (16 / sizeof(TA)) == 0) {
+    constexpr int VA = 16 / sizeof(TA);
+    const int cpr = K / VA, chunks = MR * cpr;
+    for (int c0 = 0; c0 < chunks; c0 += 256 * 8) {
+      uint4 rr[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u * 256 + tid, r = c / cpr, kc = c - r * cpr;
+        rr[u] = (c < chunks && r < mr) ? *(const uint4*)((const TA*)a.A + a.amap.off(m0 + r) + kc * VA) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int c = c0 + u * 256 + tid;
+        if (c >= chunks) continue;
+        float f[VA];
+        wunpack<TA>(rr[u], f);
+        float* dst = sA + c * VA;  // rows are contiguous: c * VA == r * K + kc * VA
+#pragma unroll
+        for (int q = 0; q < VA; ++q) dst[q] = f[q];
       }
     }
-    __syncthreads();
+  } else {
+    for (int idx = tid; idx < MR * K; idx += 256) {
+      const int r = idx / K, k = idx - r * K;
+      sA[idx] = r < mr ? ld<TA>((const TA*)a.A + a.amap.off(m0 + r) + k) : 0.0f;
+    }
   }
-  const bool glu = a.epi.kind == EPI_GLU;
-  const int units = glu ? a.N / 2 : a.N;
-  const int u_end = min(units, (int)(blockIdx.x + 1) * units_per_block);
-  const TW* W = (const TW*)a.W;
-  for (int u = blockIdx.x * units_per_block + wave; u < u_end; u += 4) {
-    const int ncol = glu ? 2 : 1;
-    const int col0 = glu ? glu_a_col(u) : u;
-    float acc[2][MR];
+  __syncthreads();
+
+  // ================= phase 1: row transforms (a wave per row), residual statistics
+  constexpr bool round_bf16 = sizeof(TW) == 2;
+  for (int r = wave; r < mr; r += 4) {
+    float* row = sA + r * K;
+    if (a.pre_g) row_ln_regs(row, K, pg, pb, lane);
+    if (a.ln_g) row_ln_regs(row, K, lg, lb, lane);
+    if (round_bf16 && (sizeof(TA) == 4 || a.a_dw))
+      for (int k = lane; k < K; k += 64) row[k] = bf2f(f2bf(row[k]));
+  }
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+  for (int t = 0; t < RPW; ++t) {
+    const int r = wave + 4 * t;
+    if (!res_stats || r >= mr) continue;
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < GEMV_LPL; ++j) s += xv[t][j];
+    const float mean = wave_sum(s) / (float)D;
+    float q = 0.0f;
+#pragma unroll
+    for (int j = 0; j < GEMV_LPL; ++j) if (j < D / 64) { const float d = xv[t][j] - mean; q += d * d; }
+    const float rstd = rsqrtf(wave_sum(q) / (float)D + 1e-5f);
+    if (lane == 0) { stats[2 * r] = mean; stats[2 * r + 1] = rstd; }
+  }
+  __syncthreads();
+
+  // ================= phase 2: products, reductions, epilogue
+  for (int u = 0; u < UMAX || (KCH == 0 && u < upw); ++u) {
+    if (u >= upw) break;
+    const int unit = u0 + u;
+    if (unit >= units) break;
+    float acc[COLS][MR];
+#pragma unroll
+    for (int c = 0; c < COLS; ++c)
 #pragma unroll
       for (int r = 0; r < MR; ++r) acc[c][r] = 0.0f;
-    for (int c = 0; c < ncol; ++c) {
-      const TW* wrow = W + (long)(col0 + 32 * c) * K;
-#pragma unroll 4
-      for (int k0 = lane * VEC; k0 < K; k0 += 64 * VEC) {
-        float w[VEC];
-        WLoad<TW, VEC>::get(wrow + k0, w);
+    if constexpr (KCH > 0) {
 #pragma unroll
-        for (int r = 0; r < MR; ++r) {
-          const float* ar = sA + r * K + k0;
-          float s = 0.0f;
+      for (int c = 0; c < COLS; ++c)
 #pragma unroll
-          for (int v = 0; v < VEC; ++v) s += w[v] * ar[v];
-          acc[c][r] += s;
+        for (int k = 0; k < KCH; ++k) {
+          float w[VEC];
+          wunpack<TW>(wr[((u < UMAX ? u : 0) * COLS + c) * KCH + k], w);
+          const float* ap = sA + (k * 64 + lane) * VEC;
+#pragma unroll
+          for (int r = 0; r < MR; ++r) {
+            float sacc = 0.0f;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) sacc += w[v] * ap[r * K + v];
+            acc[c][r] += sacc;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int c = 0; c < COLS; ++c) {
+        const int col = GLU ? glu_a_col(unit) + 32 * c : unit;
+        const TW* wrow = W + (long)col * K;
+        for (int k = lane; k < K; k += 64) {
+          const float w = ld<TW>(wrow + k);
+#pragma unroll
+          for (int r = 0; r < MR; ++r) acc[c][r] += w * sA[r * K + k];
         }
       }
     }
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < COLS; ++c)
 #pragma unroll
       for (int r = 0; r < MR; ++r) acc[c][r] = wave_sum(acc[c][r]);
-    if (lane < mr) {
-      float va = 0.0f, vb = 0.0f;
+    if (lane >= mr) continue;
+    float va = 0.0f, vb = 0.0f;
 #pragma unroll
-      for (int r = 0; r < MR; ++r)
-        if (r == lane) { va = acc[0][r]; vb = acc[1][r]; }
-      if (glu) epi_glu<TW>(a.epi, m0 + lane, u, va, vb);
-      else epi_one<TW>(a.epi, m0 + lane, u, va);
+    for (int r = 0; r < MR; ++r)
+      if (r == lane) { va = acc[0][r]; vb = acc[COLS - 1][r]; }
+    const int m = m_lane;
+    if (KCH == 0) {  // generic shape: operands read here
+      if constexpr (GLU) {
+        epi_glu<TW>(e, m, unit, va, vb);
+      } else if (e.kind == EPI_RESID && a.res_src) {
+        float base = a.res_src[(long)m * D + unit];
+        if (a.res_g) base = (base - stats[2 * lane]) * stats[2 * lane + 1] * a.res_g[unit] + a.res_b[unit];
+        if (e.bias) va += e.bias[unit];
+        ((float*)e.out)[(long)m * D + unit] = base + e.alpha * va;
+      } else {
+        epi_one<TW>(e, m, unit, va);
+      }
+      continue;
+    }
+    const int uu = u < UE ? u : 0;
+    if constexpr (GLU) {
+      const float g = (va + eb[uu][0]) * sigmoid_f(vb + eb[uu][COLS - 1]);
+      const int slot = (row_slot_pos + m % e.cv.nf) % e.Rc;
+      st<TW>((TW*)e.cring + ((long)row_id * e.Rc + slot) * e.D + unit, g);
+    } else {
+      const float v = va + eb[uu][0];
+      switch (e.kind) {
+        case EPI_STORE: st<TW>((TW*)e.out + (long)m * e.ldo + unit, v); break;
+        case EPI_SILU: st<TW>((TW*)e.out + (long)m * e.ldo + unit, silu_f(v)); break;
+        case EPI_RELU_FE: {
+          const bool before_start = row_slot_pos == 0 && m % e.fe_rows_per_stream < e.fe_neg_rows;
+          st<TW>((TW*)e.out + (long)m * e.ldo + unit, before_start ? 0.0f : fmaxf(v, 0.0f));
+        } break;
+        case EPI_RESID: {
+          float base = er[uu];
+          if (res_stats) base = (base - stats[2 * lane]) * stats[2 * lane + 1] * a.res_g[unit] + a.res_b[unit];
+          ((float*)e.out)[(long)m * D + unit] = base + e.alpha * v;
+        } break;
+        case EPI_F32: ((float*)e.out)[(long)omap_row * e.ldo + unit] = v; break;
+        case EPI_QKV: {
+          const int which = unit / e.D, c = unit % e.D;
+          if (which == 0) {
+            e.qbuf[(long)m * e.D + c] = v;
+          } else {
+            const int slot = (row_slot_pos + m % e.cv.nf) % e.R;
+            TW* ring = (TW*)(which == 1 ? e.kring : e.vring);
+            st<TW>(ring + (((long)row_id * e.H + c / e.hd) * e.R + slot) * e.hd + c % e.hd, v);
+          }
+        } break;
+        default: break;
+      }
     }
   }
 }
@@ -261,17 +480,19 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
 typedef __attribute__((ext_vector_type(16))) float f32x16_v;
 
-// Block tile BM x BN, k-step 32, 4 waves as WM x WN, each wave (BM/WM) x (BN/WN) made of
-// 32x32 MFMA fragments. A and W tiles are staged through LDS (row stride padded to 40 bf16);
-// the next k-tile is fetched into registers while the current one is multiplied.
+// Block tile BM x BN, k-step 64, 4 waves as WM x WN, each wave (BM/WM) x (BN/WN) made of
+// 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, 4 per k-step). A and W k-tiles live in two
+// LDS buffers (row stride 72 bf16: 16-byte aligned, conflict-free fragment reads); the next
+// k-tile is fetched into registers while the current one is multiplied and stored into the
+// other buffer afterwards, so each k-step has one barrier and its loads overlap a k-step of MFMA.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
-  constexpr int BK = 32, LDK = BK + 8;
+  constexpr int BK = 64, LDK = BK + 8;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr int A_PER_T = BM * 4 / 256, B_PER_T = BN * 4 / 256;
+  constexpr int A_PER_T = BM * (BK / 8) / 256, B_PER_T = BN * (BK / 8) / 256;
   static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small");
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BN * LDK];
+  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+  // buffer b: A tile at lds + b * (BM + BN) * LDK, W tile right after it
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int bm0 = blockIdx.y * BM, bn0 = blockIdx.x * BN;
@@ -281,20 +502,18 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
 
   const bf16_t* aptr[A_PER_T];
   const bf16_t* bptr[B_PER_T];
-  int aoff_s[A_PER_T], boff_s[B_PER_T];
+  int aoff[A_PER_T], boff[B_PER_T];
 #pragma unroll
   for (int i = 0; i < A_PER_T; ++i) {
-    int c = tid + i * 256, row = c >> 2, kc = (c & 3) * 8;
-    int m = min(bm0 + row, M - 1);
-    aptr[i] = A + a.amap.off(m) + kc;
-    aoff_s[i] = row * LDK + kc;
+    const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+    aptr[i] = A + a.amap.off(min(bm0 + row, M - 1)) + kc;
+    aoff[i] = row * LDK + kc;
   }
 #pragma unroll
   for (int i = 0; i < B_PER_T; ++i) {
-    int c = tid + i * 256, row = c >> 2, kc = (c & 3) * 8;
-    int n = min(bn0 + row, N - 1);
-    bptr[i] = W + (long)n * K + kc;
-    boff_s[i] = row * LDK + kc;
+    const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
+    bptr[i] = W + (long)min(bn0 + row, N - 1) * K + kc;
+    boff[i] = row * LDK + kc;
   }
   uint4 ra[A_PER_T], rb[B_PER_T];
   auto gload = [&](int kt) {
@@ -303,11 +522,13 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < B_PER_T; ++i) rb[i] = *(const uint4*)(bptr[i] + kt * BK);
   };
-  auto sstore = [&]() {
+  auto sstore = [&](int buf) {
+    bf16_t* Ab = lds + buf * (BM + BN) * LDK;
+    bf16_t* Bb = Ab + BM * LDK;
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) *(uint4*)(As + aoff_s[i]) = ra[i];
+    for (int i = 0; i < A_PER_T; ++i) *(uint4*)(Ab + aoff[i]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) *(uint4*)(Bs + boff_s[i]) = rb[i];
+    for (int i = 0; i < B_PER_T; ++i) *(uint4*)(Bb + boff[i]) = rb[i];
   };
 
   f32x16_v acc[FM][FN];
@@ -320,30 +541,30 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
 
   const int KT = K / BK;
   gload(0);
-  sstore();
+  sstore(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
     if (kt + 1 < KT) gload(kt + 1);
+    const bf16_t* Ab = lds + buf * (BM + BN) * LDK;
+    const bf16_t* Bb = Ab + BM * LDK;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
       bf16x8_v af[FM], bfv[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = *(const bf16x8_v*)(As + (wm * TM + i * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
+        af[i] = *(const bf16x8_v*)(Ab + (wm * TM + i * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfv[j] = *(const bf16x8_v*)(Bs + (wn * TN + j * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
+        bfv[j] = *(const bf16x8_v*)(Bb + (wn * TN + j * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
     }
+    if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
-    if (kt + 1 < KT) {
-      sstore();
-      __syncthreads();
-    }
   }
 
   // fragment element r of lane: row 8*(r/4) + 4*(lane/32) + r%4, column lane%32
@@ -373,29 +594,69 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
   }
 }
 
+template <int BM, int BN>
+constexpr size_t mfma_lds() { return (size_t)2 * (BM + BN) * (64 + 8) * sizeof(bf16_t); }
+
 // =============================================================================== LayerNorm
+// One wave per row; the row, gains and shifts are loaded together as 16-byte chunks (D a
+// multiple of 256, up to 4 chunks per lane), falling back to scalar loads otherwise.
 template <typename TO>
 __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= a.M) return;
   const float* x = a.x + (long)row * a.D;
+  TO* y = (TO*)a.y + (long)row * a.D;
+  if (a.D % 256 == 0 && a.D <= 1024) {
+    const int nv = a.D / 256;
+    float4 xv[4], gv[4], bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = j < nv;
+      const int k = (j * 64 + lane) * 4;
+      xv[j] = ok ? *(const float4*)(x + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+      gv[j] = ok ? *(const float4*)(a.g + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+      bv[j] = ok ? *(const float4*)(a.b + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += xv[j].x + xv[j].y + xv[j].z + xv[j].w;
+    const float mean = wave_sum(s) / (float)a.D;
+    float q = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < nv) {
+        const float d0 = xv[j].x - mean, d1 = xv[j].y - mean, d2 = xv[j].z - mean, d3 = xv[j].w - mean;
+        q += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
+      }
+    const float rstd = rsqrtf(wave_sum(q) / (float)a.D + 1e-5f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < nv) {
+        const int k = (j * 64 + lane) * 4;
+        st<TO>(y + k, (xv[j].x - mean) * rstd * gv[j].x + bv[j].x);
+        st<TO>(y + k + 1, (xv[j].y - mean) * rstd * gv[j].y + bv[j].y);
+        st<TO>(y + k + 2, (xv[j].z - mean) * rstd * gv[j].z + bv[j].z);
+        st<TO>(y + k + 3, (xv[j].w - mean) * rstd * gv[j].w + bv[j].w);
+      }
+    return;
+  }
   float s = 0.0f;
   for (int k = lane; k < a.D; k += 64) s += x[k];
   const float mean = wave_sum(s) / (float)a.D;
   float q = 0.0f;
   for (int k = lane; k < a.D; k += 64) { float d = x[k] - mean; q += d * d; }
   const float rstd = rsqrtf(wave_sum(q) / (float)a.D + 1e-5f);
-  TO* y = (TO*)a.y + (long)row * a.D;
   for (int k = lane; k < a.D; k += 64) st<TO>(y + k, (x[k] - mean) * rstd * a.g[k] + a.b[k]);
 }
 
 // =============================================================================== dense dispatch
-// Algorithmic HBM bytes of one dense product: the weights once, plus what its epilogue writes
-// to per-stream state (K/V rows, depthwise input rows) or to the caller's output. Activations
-// that stay on chip or in the last-level cache are not counted.
+// Algorithmic HBM bytes of one dense product: the weights once, plus the depthwise ring rows
+// it reads and what its epilogue writes to per-stream state (K/V rows, depthwise input rows)
+// or to the caller's output. Activations that stay on chip or in cache are not counted.
 static double gemm_bytes(const GemmArgs& a, size_t wsz) {
   double b = (double)a.N * a.K * wsz;
   const double esz = (double)wsz;
+  if (a.a_dw) b += (double)a.epi.cv.n_streams * (a.dw_taps - 1 + a.epi.cv.nf) * a.K * esz;
   switch (a.epi.kind) {
     case EPI_QKV: b += (double)a.M * 2.0 * a.epi.D * esz; break;
     case EPI_GLU: b += (double)a.M * (a.N / 2) * esz; break;
@@ -405,25 +666,46 @@ static double gemm_bytes(const GemmArgs& a, size_t wsz) {
   return b;
 }
 
+template <typename TW, typename TA, int MR, int KCH>
+static const void* gemv_pick_glu(bool glu) {
+  return glu ? (const void*)&gemv_kernel<TW, TA, MR, KCH, true> : (const void*)&gemv_kernel<TW, TA, MR, KCH, false>;
+}
+template <typename TW, typename TA, int MR>
+static const void* gemv_pick_kch(int kch, bool glu) {
+  constexpr bool f32w = sizeof(TW) == 4;
+  switch (kch) {
+    case 1: return gemv_pick_glu<TW, TA, MR, 1>(glu);
+    case 2: return f32w ? gemv_pick_glu<TW, TA, MR, 2>(glu) : nullptr;
+    case 3: return f32w ? nullptr : gemv_pick_glu<TW, TA, MR, 3>(glu);
+    case 4: return f32w ? nullptr : gemv_pick_glu<TW, TA, MR, 4>(glu);
+    case 6: return f32w ? gemv_pick_glu<TW, TA, MR, 6>(glu) : nullptr;
+    case 8: return f32w ? gemv_pick_glu<TW, TA, MR, 8>(glu) : nullptr;
+    default: return gemv_pick_glu<TW, TA, MR, 0>(glu);
+  }
+}
+static int gemv_umax(int kch, bool glu) {
+  const int cols = glu ? 2 : 1;
+  return kch > 0 ? std::max(1, 8 / (cols * kch)) : 1 << 30;
+}
+
 template <typename TW, typename TA>
 static void gemv_dispatch(Launcher& L, const GemmArgs& a) {
-  const int units = a.epi.kind == EPI_GLU ? a.N / 2 : a.N;
-  int upb = std::max(4, (units + 255) / 256);
-  upb = (upb + 3) / 4 * 4;
+  const bool glu = a.epi.kind == EPI_GLU;
+  const int units = glu ? a.N / 2 : a.N;
+  constexpr int VEC = 16 / sizeof(TW);
+  int kch = a.K % (64 * VEC) == 0 ? a.K / (64 * VEC) : 0;
+  if (kch && !gemv_pick_kch<TW, TA, 2>(kch, glu)) kch = 0;
+  if (kch != 1 && kch != 2 && kch != 3 && kch != 4 && kch != 6 && kch != 8) kch = 0;
+  // units per wave: enough waves for the chip, within the register budget
+  int upw = std::max(1, (units + 4 * 256 - 1) / (4 * 256));
+  upw = std::min(upw, gemv_umax(kch, glu));
   GemmArgs args = a;
-  args.upb = upb;
-  // MR rows per block; weights are re-streamed once per block row
-  const int MR = a.M <= 2 ? 2 : (a.M <= 4 ? 4 : 8);
-  const size_t shm = (size_t)MR * a.K * sizeof(float);
-  constexpr int VW = sizeof(TW) == 4 ? 4 : 8;
-  const bool vec = a.K % (64 * VW) == 0;
-  const void* fn = nullptr;
-#define GEMV_PICK(mr) \
-  fn = vec ? (const void*)&gemv_kernel<TW, TA, mr, VW> : (const void*)&gemv_kernel<TW, TA, mr, 1>;
-  if (MR == 2) { GEMV_PICK(2) } else if (MR == 4) { GEMV_PICK(4) } else { GEMV_PICK(8) }
-#undef GEMV_PICK
+  args.upb = upw;
+  const int MR = a.M <= 2 ? 2 : 8;
+  const void* fn = MR == 2 ? gemv_pick_kch<TW, TA, 2>(kch, glu) : gemv_pick_kch<TW, TA, 8>(kch, glu);
+  const size_t shm = ((size_t)MR * a.K + 2 * MR) * sizeof(float);
   L.tag(sizeof(TW) == 4 ? "gemm_small_m_f32" : "gemm_small_m_bf16", gemm_bytes(a, sizeof(TW)), 2.0 * a.M * a.N * a.K);
-  L.launch(fn, dim3((units + upb - 1) / upb, (a.M + MR - 1) / MR), dim3(256), shm, &args);
+  L.launch(fn, dim3((units + 4 * upw - 1) / (4 * upw), (a.M + MR - 1) / MR), dim3(256), shm, &args);
 }
 
 static void mfma_dispatch(Launcher& L, const GemmArgs& a) {
@@ -432,24 +714,29 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a) {
   GemmArgs args = a;
   const void* fn;
   dim3 grid;
+  size_t shm;
   L.tag("gemm_mfma_bf16", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K);
   // largest tile that still yields >= 256 workgroups; GLU needs 64-column wave tiles
   if (tiles(128, 128) >= 256) {
     fn = (const void*)&gemm_mfma_kernel<128, 128, 2, 2>;
     grid = dim3((a.N + 127) / 128, (a.M + 127) / 128);
+    shm = mfma_lds<128, 128>();
   } else if (glu || tiles(64, 64) < 128) {
     if (tiles(128, 64) >= tiles(64, 128) * 3 / 4 && a.M >= 128) {
       fn = (const void*)&gemm_mfma_kernel<128, 64, 4, 1>;
       grid = dim3((a.N + 63) / 64, (a.M + 127) / 128);
+      shm = mfma_lds<128, 64>();
     } else {
       fn = (const void*)&gemm_mfma_kernel<64, 128, 2, 2>;
       grid = dim3((a.N + 127) / 128, (a.M + 63) / 64);
+      shm = mfma_lds<64, 128>();
     }
   } else {
     fn = (const void*)&gemm_mfma_kernel<64, 64, 2, 2>;
     grid = dim3((a.N + 63) / 64, (a.M + 63) / 64);
+    shm = mfma_lds<64, 64>();
   }
-  L.launch(fn, grid, dim3(256), 0, &args);
+  L.launch(fn, grid, dim3(256), shm, &args);
 }
 
 __global__ __launch_bounds__(256) void cvt_kernel(CvtArgs a) {
@@ -464,15 +751,17 @@ void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path) {
     gemv_dispatch<float, float>(L, a);
     return;
   }
-  const bool small = path == 1 || (path == 0 && a.M <= 8);
+  const bool small = path == 1 || (path == 0 && a.M <= 8) || a.K % 64 != 0;
   if (small) {
-    if (a.a_f32) gemv_dispatch<bf16_t, float>(L, a);
+    if (a.a_f32 && !a.a_dw) gemv_dispatch<bf16_t, float>(L, a);
     else gemv_dispatch<bf16_t, bf16_t>(L, a);
     return;
   }
   GemmArgs g = a;
   if (a.a_f32) {
     // materialise the bf16 operand first: LayerNorm rows, or a rounded (gathered) copy
+    const char* role = L.role;
+    L.role = nullptr;
     if (a.ln_g) {
       LnArgs la{(const float*)a.A, a.a_scratch, a.ln_g, a.ln_b, a.M, a.K, 0};
       L.tag("layernorm", 0.0, 0.0);
@@ -483,6 +772,7 @@ void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path) {
       L.tag("convert_rows", 0.0, 0.0);
       L.launch((const void*)&cvt_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &cv);
     }
+    L.role = role;
     g.A = a.a_scratch;
     g.amap = RowMap{INT_MAX, 0, a.K};
     g.a_f32 = 0;
@@ -499,12 +789,20 @@ void launch_ln(Launcher& L, const LnArgs& a, int dtype) {
 }
 
 // =============================================================================== attention
-// One wave per (call stream, head). Keys are the ring rows of positions
-// [max(0, pos0 - Lc), pos0 + nf - 1]; the rows of this call were written by the QKV epilogue.
-// score(i, j) = ((q_i + u) . k_j + (q_i + v) . P[p_i - q_j]) * scale on visible keys,
-// with the position term taken from a per-wave table bd[i][rel] = (q_i + v) . P[rel].
+// One 256-thread block per (call stream, head). Everything the block reads is staged in LDS
+// first, all global loads issued together: the ring rows of positions
+// [max(0, pos0 - Lc), pos0 + nf - 1] (K and V; the rows of this call were written by the QKV
+// epilogue), the head's projected position rows, the call's q rows and u, v. Then one thread
+// per (query i, key j):
+//   s[i][j] = ((q_i + u) . k_j + (q_i + v) . P[p_i - q_j]) * scale on visible keys, else -inf,
+// a wave per query row for the softmax, and one thread per (query, dim) for o_i = sum_j p_ij v_j.
+constexpr int ATT_PAD = 4;  // row stride HD + 4 keeps 16-byte alignment and spreads LDS banks
+
 size_t attention_shmem(int nf, int nk_max, int nrel, int hd) {
-  return (size_t)4 * sizeof(float) * (2 * nf * hd + nf * nrel + nf * nk_max);
+  const size_t rs = (size_t)hd + ATT_PAD;
+  const size_t f = (size_t)nk_max * rs + (size_t)nk_max * hd + (size_t)nrel * rs + (size_t)nf * hd + 2 * (size_t)hd +
+                   (size_t)nf * nk_max;
+  return f * sizeof(float);
 }
 
 __device__ __forceinline__ bool att_visible(const AttnArgs& a, int p, int q) {
@@ -514,140 +812,196 @@ __device__ __forceinline__ bool att_visible(const AttnArgs& a, int p, int q) {
   return q >= cs - a.Lc && q <= cs + a.chunk - 1;
 }
 
+template <typename T> __device__ __forceinline__ void unpack16(const uint4& r, float* f);
+template <> __device__ __forceinline__ void unpack16<float>(const uint4& r, float* f) {
+  f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y); f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
+}
+template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4& r, float* f) {
+  const uint32_t u[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f[2 * i] = __uint_as_float(u[i] << 16); f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u); }
+}
+
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   extern __shared__ float sm[];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int RS = HD + ATT_PAD;
+  constexpr int EPC = 16 / sizeof(T);  // K/V elements per 16-byte chunk
+  constexpr int KCPR = HD / EPC;       // chunks per K/V row
+  constexpr int FCPR = HD / 4;         // chunks per float row (P, q, u, v)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nf = a.cv.nf, nrel = a.nrel, nkmax = a.Lc + nf;
-  const int per_wave = 2 * nf * HD + nf * nrel + nf * nkmax;
-  float* qu = sm + wave * per_wave;
-  float* qv = qu + nf * HD;
-  float* bd = qv + nf * HD;
-  float* sc = bd + nf * nrel;
-  const int pair = blockIdx.x * 4 + wave;
-  const bool active = pair < a.cv.n_streams * a.H;
-  const int s = active ? pair / a.H : 0, h = active ? pair % a.H : 0;
+  float* Ks = sm;
+  float* Vs = Ks + nkmax * RS;
+  float* Ps = Vs + nkmax * HD;
+  float* Qs = Ps + nrel * RS;
+  float* Us = Qs + nf * HD;
+  float* Wv = Us + HD;
+  float* sc = Wv + HD;
+  const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int id = a.cv.ids[s];
-  const int pos0 = a.cv.pos[id];
-  const int q_lo = max(0, pos0 - a.Lc), q_hi = pos0 + nf - 1, nk = q_hi - q_lo + 1;
+  const int pos0 = a.cv.cpos[s];
+  const int q_lo = max(0, pos0 - a.Lc), nk = pos0 + nf - q_lo;
+  const T* kbase = (const T*)a.kring + ((long)id * a.H + h) * a.R * HD;
+  const T* vbase = (const T*)a.vring + ((long)id * a.H + h) * a.R * HD;
+  const float* pbase = a.posproj + (long)h * nrel * HD;
 
-  if (active) {
-    for (int idx = lane; idx < nf * HD; idx += 64) {
-      const int i = idx / HD, d = idx - i * HD;
-      const float q = a.q[(long)(s * nf + i) * a.D + h * HD + d];
-      qu[idx] = q + a.pos_u[h * HD + d];
-      qv[idx] = q + a.pos_v[h * HD + d];
+  // ---- stage K, V, P, q, u, v (16-byte chunks, up to 16 in flight per thread)
+  const int nK = nk * KCPR, nP = nrel * FCPR, nQ = nf * FCPR;
+  const int total = 2 * nK + nP + nQ + 2 * FCPR;
+  constexpr int U = 16;
+  for (int base = 0; base < total; base += 256 * U) {
+    uint4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = base + u * 256 + tid;
+      const uint4* src = nullptr;
+      if (c < nK) {
+        src = (const uint4*)(kbase + (long)((q_lo + c / KCPR) % a.R) * HD) + c % KCPR;
+      } else if (c < 2 * nK) {
+        const int cc = c - nK;
+        src = (const uint4*)(vbase + (long)((q_lo + cc / KCPR) % a.R) * HD) + cc % KCPR;
+      } else if (c < 2 * nK + nP) {
+        const int cc = c - 2 * nK;
+        src = (const uint4*)(pbase + (long)(cc / FCPR) * HD) + cc % FCPR;
+      } else if (c < 2 * nK + nP + nQ) {
+        const int cc = c - 2 * nK - nP;
+        src = (const uint4*)(a.q + (long)(s * nf + cc / FCPR) * a.D + h * HD) + cc % FCPR;
+      } else if (c < total) {
+        const int cc = c - 2 * nK - nP - nQ;
+        src = (const uint4*)((cc < FCPR ? a.pos_u : a.pos_v) + h * HD) + cc % FCPR;
+      }
+      r[u] = src ? *src : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = base + u * 256 + tid;
+      if (c >= total) continue;
+      if (c < 2 * nK) {
+        float f[EPC];
+        unpack16<T>(r[u], f);
+        const int cc = c < nK ? c : c - nK;
+        float* dst = (c < nK ? Ks + (cc / KCPR) * RS : Vs + (cc / KCPR) * HD) + (cc % KCPR) * EPC;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) dst[e] = f[e];
+      } else {
+        float f[4];
+        unpack16<float>(r[u], f);
+        float* dst;
+        if (c < 2 * nK + nP) { const int cc = c - 2 * nK; dst = Ps + (cc / FCPR) * RS + (cc % FCPR) * 4; }
+        else if (c < 2 * nK + nP + nQ) { const int cc = c - 2 * nK - nP; dst = Qs + (cc / FCPR) * HD + (cc % FCPR) * 4; }
+        else { const int cc = c - 2 * nK - nP - nQ; dst = (cc < FCPR ? Us : Wv) + (cc % FCPR) * 4; }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = f[e];
+      }
     }
   }
   __syncthreads();
-  if (active) {
-    // position term table
-    for (int r = lane; r < nrel; r += 64) {
-      const float* prow = a.posproj + ((long)h * nrel + r) * HD;
-      float pr[HD];
+
+  // ---- scores: one (query, key) pair per thread
+  for (int pr = tid; pr < nf * nk; pr += 256) {
+    const int i = pr / nk, j = pr - i * nk;
+    const int p = pos0 + i, qk = q_lo + j;
+    float sv = -INFINITY;
+    if (att_visible(a, p, qk)) {
+      const float* qi = Qs + i * HD;
+      const float* kj = Ks + j * RS;
+      const float* pj = Ps + (p - qk - a.rel_lo) * RS;
+      float ac = 0.0f, bdv = 0.0f;
 #pragma unroll
       for (int d = 0; d < HD; d += 4) {
-        float4 v = *(const float4*)(prow + d);
-        pr[d] = v.x; pr[d + 1] = v.y; pr[d + 2] = v.z; pr[d + 3] = v.w;
+        const float4 q4 = *(const float4*)(qi + d), k4 = *(const float4*)(kj + d), p4 = *(const float4*)(pj + d);
+        const float4 u4 = *(const float4*)(Us + d), v4 = *(const float4*)(Wv + d);
+        ac += (q4.x + u4.x) * k4.x + (q4.y + u4.y) * k4.y + (q4.z + u4.z) * k4.z + (q4.w + u4.w) * k4.w;
+        bdv += (q4.x + v4.x) * p4.x + (q4.y + v4.y) * p4.y + (q4.z + v4.z) * p4.z + (q4.w + v4.w) * p4.w;
       }
-      for (int i = 0; i < nf; ++i) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int d = 0; d < HD; ++d) acc += qv[i * HD + d] * pr[d];
-        bd[i * nrel + r] = acc;
-      }
+      sv = (ac + bdv) * a.scale;
     }
+    sc[i * nkmax + j] = sv;
   }
   __syncthreads();
-  if (active) {
-    const T* kbase = (const T*)a.kring + ((long)id * a.H + h) * a.R * HD;
+  // ---- softmax: a wave per query row
+  for (int i = wave; i < nf; i += 4) {
+    float* row = sc + i * nkmax;
+    float mx = -INFINITY;
+    for (int j = lane; j < nk; j += 64) mx = fmaxf(mx, row[j]);
+    mx = wave_max(mx);
+    float sum = 0.0f;
     for (int j = lane; j < nk; j += 64) {
-      const int qk = q_lo + j;
-      const T* krow = kbase + (long)(qk % a.R) * HD;
-      float kr[HD];
-#pragma unroll
-      for (int d = 0; d < HD; ++d) kr[d] = ld<T>(krow + d);
-      for (int i = 0; i < nf; ++i) {
-        const int p = pos0 + i;
-        float sv = -INFINITY;
-        if (att_visible(a, p, qk)) {
-          float acc = 0.0f;
-#pragma unroll
-          for (int d = 0; d < HD; ++d) acc += qu[i * HD + d] * kr[d];
-          sv = (acc + bd[i * nrel + (p - qk - a.rel_lo)]) * a.scale;
-        }
-        sc[i * nkmax + j] = sv;
-      }
+      const float e = __expf(row[j] - mx);
+      row[j] = e;
+      sum += e;
     }
+    const float inv = 1.0f / wave_sum(sum);
+    for (int j = lane; j < nk; j += 64) row[j] *= inv;
   }
   __syncthreads();
-  if (active) {
-    for (int i = 0; i < nf; ++i) {
-      float mx = -INFINITY;
-      for (int j = lane; j < nk; j += 64) mx = fmaxf(mx, sc[i * nkmax + j]);
-      mx = wave_max(mx);
-      float sum = 0.0f;
-      for (int j = lane; j < nk; j += 64) {
-        const float e = __expf(sc[i * nkmax + j] - mx);
-        sc[i * nkmax + j] = e;
-        sum += e;
-      }
-      sum = wave_sum(sum);
-      const float inv = 1.0f / sum;
-      for (int j = lane; j < nk; j += 64) sc[i * nkmax + j] *= inv;
-    }
-  }
-  __syncthreads();
-  if (active && lane < HD) {
-    const T* vbase = (const T*)a.vring + ((long)id * a.H + h) * a.R * HD;
-    float acc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < nk; ++j) {
-      const float vv = ld<T>(vbase + (long)((q_lo + j) % a.R) * HD + lane);
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (i < nf) acc[i] += sc[i * nkmax + j] * vv;
-    }
-    for (int i = 0; i < nf; ++i) st<T>((T*)a.o + (long)(s * nf + i) * a.D + h * HD + lane, acc[i]);
+  // ---- o = P V: one (query, dim) pair per thread
+  for (int pr = tid; pr < nf * HD; pr += 256) {
+    const int i = pr / HD, d = pr - i * HD;
+    const float* row = sc + i * nkmax;
+    float acc = 0.0f;
+    for (int j = 0; j < nk; ++j) acc += row[j] * Vs[j * HD + d];
+    st<T>((T*)a.o + (long)(s * nf + i) * a.D + h * HD + d, acc);
   }
 }
 
 void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd) {
   AttnArgs args = a;
-  const int pairs = a.cv.n_streams * a.H;
   const size_t shm = attention_shmem(a.cv.nf, a.Lc + a.cv.nf, a.nrel, hd);
   const void* fn = nullptr;
-#define ATT_PICK(HDV)                                                                   \
+#define ATT_PICK(HDV) \
   fn = dtype == DT_F32 ? (const void*)&attn_kernel<float, HDV> : (const void*)&attn_kernel<bf16_t, HDV>;
   if (hd == 16) { ATT_PICK(16) } else if (hd == 32) { ATT_PICK(32) } else { ATT_PICK(64) }
 #undef ATT_PICK
   L.tag_name = "attention";  // the caller tags bytes and flops (it knows each stream's fill)
-  L.launch(fn, dim3((pairs + 3) / 4), dim3(256), shm, &args);
+  L.launch(fn, dim3(a.cv.n_streams * a.H), dim3(256), shm, &args);
 }
 
 // =============================================================================== depthwise conv
+// One thread per (row, 4 channels): the taps and ring rows are loaded together, positions
+// before the stream start read as zero.
 template <typename T>
 __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  const long total = (long)a.cv.n_streams * a.cv.nf * a.D;
+  const int cg = a.D / 4;
+  const long total = (long)a.cv.n_streams * a.cv.nf * cg;
   if (idx >= total) return;
-  const int m = (int)(idx / a.D), c = (int)(idx % a.D);
+  const int m = (int)(idx / cg), c = (int)(idx % cg) * 4;
   const int s = m / a.cv.nf, i = m % a.cv.nf;
   const int id = a.cv.ids[s];
-  const int p = a.cv.pos[id] + i;
-  const T* ring = (const T*)a.cring + (long)id * a.Rc * a.D;
-  float acc = a.b[c];
-  for (int k = 0; k < a.K; ++k) {
-    const int q = p - (a.K - 1) + k;
-    if (q >= 0) acc += a.w[k * a.D + c] * ld<T>(ring + (long)(q % a.Rc) * a.D + c);
+  const int p = a.cv.cpos[s] + i;
+  const T* ring = (const T*)a.cring + (long)id * a.Rc * a.D + c;
+  float g[16][4];
+  float4 w[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int q = p - (a.K - 1) + t;
+    const bool ok = t < a.K && q >= 0;
+    w[t] = t < a.K ? *(const float4*)(a.w + t * a.D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if constexpr (sizeof(T) == 4) {
+      const float4 v = ok ? *(const float4*)(ring + (long)(q % a.Rc) * a.D) : make_float4(0.f, 0.f, 0.f, 0.f);
+      g[t][0] = v.x; g[t][1] = v.y; g[t][2] = v.z; g[t][3] = v.w;
+    } else {
+      const uint2 v = ok ? *(const uint2*)(ring + (long)(q % a.Rc) * a.D) : make_uint2(0u, 0u);
+      g[t][0] = __uint_as_float(v.x << 16); g[t][1] = __uint_as_float(v.x & 0xffff0000u);
+      g[t][2] = __uint_as_float(v.y << 16); g[t][3] = __uint_as_float(v.y & 0xffff0000u);
+    }
   }
-  st<T>((T*)a.e + (long)m * a.D + c, silu_f(acc));
+  const float4 b4 = *(const float4*)(a.b + c);
+  float acc[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    acc[0] += w[t].x * g[t][0]; acc[1] += w[t].y * g[t][1]; acc[2] += w[t].z * g[t][2]; acc[3] += w[t].w * g[t][3];
+  }
+  T* e = (T*)a.e + (long)m * a.D + c;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) st<T>(e + q, silu_f(acc[q]));
 }
 
 void launch_dwconv(Launcher& L, const DwArgs& a, int dtype) {
   DwArgs args = a;
-  const long total = (long)a.cv.n_streams * a.cv.nf * a.D;
+  const long total = (long)a.cv.n_streams * a.cv.nf * (a.D / 4);
   const void* fn = dtype == DT_F32 ? (const void*)&dw_kernel<float> : (const void*)&dw_kernel<bf16_t>;
   L.tag_name = "dwconv";  // the caller tags bytes and flops
   L.launch(fn, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
@@ -658,6 +1012,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void input_kernel(InputArgs a) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx < (long)a.M * a.D) a.x[idx] = ld<T>((const T*)a.in + idx);
+  if (idx < a.cv.n_streams) a.cv.cpos[idx] = a.cv.pos[a.cv.ids[idx]];
 }
 void launch_input(Launcher& L, const InputArgs& a, int dtype) {
   InputArgs args = a;
@@ -689,7 +1044,9 @@ __global__ __launch_bounds__(256) void fe_window_kernel(FeWindowArgs a) {
   if (idx >= a.cv.n_streams * a.bins) return;
   const int s = idx / a.bins, b = idx % a.bins;
   const int id = a.cv.ids[s];
-  const bool fresh = a.cv.pos[id] == 0;
+  const int pos = a.cv.pos[id];
+  const bool fresh = pos == 0;
+  if (b == 0) a.cv.cpos[s] = pos;
   const int nt = a.mel_tail, nn = a.mel_new, rows = nt + nn;
   T* tail = (T*)a.tail + (long)id * nt * a.bins + b;
   const T* mel = (const T*)a.mel + (long)s * nn * a.bins + b;
@@ -862,8 +1219,10 @@ __global__ __launch_bounds__(256) void la_gather_kernel(LaGatherArgs a) {
   const int m = (int)(idx / a.D), c = (int)(idx % a.D);
   const int s = m / a.cv.nf, i = m % a.cv.nf;
   const int id = a.cv.ids[s];
-  const int slot = (a.cv.pos[id] + i) % a.Rx;
+  const int pos = a.cv.pos[id];
+  const int slot = (pos + i) % a.Rx;
   a.x[idx] = ld<T>((const T*)a.x0 + ((long)id * a.Rx + slot) * a.D + c);
+  if (i == 0 && c == 0) a.cv.cpos[s] = pos;
 }
 void launch_la_store(Launcher& L, const LaStoreArgs& a, int dtype) {
   LaStoreArgs args = a;
@@ -887,18 +1246,21 @@ void kernels_init() {
   if (done) return;
   done = true;
   const int lds = 160 * 1024;
-  const void* fns[] = {
-      (const void*)&gemv_kernel<float, float, 2, 4>, (const void*)&gemv_kernel<float, float, 4, 4>,
-      (const void*)&gemv_kernel<float, float, 8, 4>, (const void*)&gemv_kernel<float, float, 2, 1>,
-      (const void*)&gemv_kernel<float, float, 4, 1>, (const void*)&gemv_kernel<float, float, 8, 1>,
-      (const void*)&gemv_kernel<bf16_t, float, 2, 8>, (const void*)&gemv_kernel<bf16_t, float, 4, 8>,
-      (const void*)&gemv_kernel<bf16_t, float, 8, 8>, (const void*)&gemv_kernel<bf16_t, float, 2, 1>,
-      (const void*)&gemv_kernel<bf16_t, float, 4, 1>, (const void*)&gemv_kernel<bf16_t, float, 8, 1>,
-      (const void*)&gemv_kernel<bf16_t, bf16_t, 2, 8>, (const void*)&gemv_kernel<bf16_t, bf16_t, 4, 8>,
-      (const void*)&gemv_kernel<bf16_t, bf16_t, 8, 8>, (const void*)&gemv_kernel<bf16_t, bf16_t, 2, 1>,
-      (const void*)&gemv_kernel<bf16_t, bf16_t, 4, 1>, (const void*)&gemv_kernel<bf16_t, bf16_t, 8, 1>,
+  std::vector<const void*> fns = {
+      (const void*)&gemm_mfma_kernel<128, 128, 2, 2>, (const void*)&gemm_mfma_kernel<128, 64, 4, 1>,
+      (const void*)&gemm_mfma_kernel<64, 128, 2, 2>, (const void*)&gemm_mfma_kernel<64, 64, 2, 2>,
       (const void*)&attn_kernel<float, 16>, (const void*)&attn_kernel<float, 32>, (const void*)&attn_kernel<float, 64>,
       (const void*)&attn_kernel<bf16_t, 16>, (const void*)&attn_kernel<bf16_t, 32>, (const void*)&attn_kernel<bf16_t, 64>,
   };
-  for (const void* f : fns) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  for (int kch : {0, 1, 2, 3, 4, 6, 8})
+    for (bool glu : {false, true}) {
+      fns.push_back(gemv_pick_kch<float, float, 2>(kch, glu));
+      fns.push_back(gemv_pick_kch<float, float, 8>(kch, glu));
+      fns.push_back(gemv_pick_kch<bf16_t, float, 2>(kch, glu));
+      fns.push_back(gemv_pick_kch<bf16_t, float, 8>(kch, glu));
+      fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 2>(kch, glu));
+      fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 8>(kch, glu));
+    }
+  for (const void* f : fns)
+    if (f) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }

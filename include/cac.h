@@ -63,10 +63,10 @@ typedef struct cac_ctx cac_ctx;
 
 typedef struct {
   int32_t n_layers;      /* Conformer blocks (17; the model card's "Config" table) */
-  int32_t d_model;       /* D (512), a multiple of 64 */
+  int32_t d_model;       /* D (512), a multiple of 64, <= 1024 */
   int32_t n_heads;       /* H (8); head_dim = D/H must be 16, 32 or 64 */
   int32_t d_ff;          /* F (2048), a multiple of 64 */
-  int32_t dw_kernel;     /* depthwise kernel width (9); cache of dw_kernel-1 columns, <= 16 */
+  int32_t dw_kernel;     /* depthwise kernel width (9), <= 16; cache of dw_kernel-1 columns */
   int32_t att_left;      /* Lc: left attention context = K/V cache rows (70) */
   int32_t att_chunk;     /* c: attention chunk in frames (2); pushes are multiples of c */
   int32_t att_right;     /* right context of the lookahead variant (3), else 0 */
@@ -127,6 +127,7 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
  *   lookahead variant: n_frames must equal n_emit; the frames join each stream's pending
  *     inputs; streams with n_emit + n_lookahead pending run one pass and emit n_emit frames
  *     into d_out rows [i][0 .. n_emit) ; streams still warming up emit nothing.
+ * d_input and d_out must be different buffers.
  * h_emitted (optional, n_streams int32) receives each stream's emitted frame count.
  * Returns the largest per-stream emitted count. Asynchronous (see Conventions). */
 int32_t cac_push_chunk(cac_ctx* ctx, int32_t n_streams, const int32_t* h_stream_ids,
@@ -156,6 +157,12 @@ int32_t cac_import_state(cac_ctx* ctx, int32_t n, const int32_t* h_stream_ids,
 /* Host view of a stream: position, pending frames, flushed flag (no device access). */
 int32_t cac_stream_info(const cac_ctx* ctx, int32_t stream_id, int32_t* pos, int32_t* pending,
                         int32_t* flushed);
+
+/* Pushes are recorded once per call shape (stream count, frames, lookahead passes) into a HIP
+ * graph of kernel nodes and replayed; only the nodes holding the caller's input and output
+ * pointers are re-pointed between replays. enable = 0 launches every kernel directly (as
+ * profiling always does). Default on. */
+int32_t cac_set_graph(cac_ctx* ctx, int32_t enable);
 
 /* Change the HIP stream later calls enqueue on. */
 int32_t cac_set_stream(cac_ctx* ctx, void* hip_stream);

@@ -88,7 +88,7 @@ def push(enc, ids, n_frames):
     ids_a = np.asarray(ids, dtype=np.int32)
     em = np.zeros(len(ids_a), dtype=np.int32)
     rc = enc.lib.cac_push_chunk(enc.ctx, len(ids_a), ids_a.ctypes.data_as(C.POINTER(C.c_int32)), n_frames,
-                                C.c_void_p(16), C.c_void_p(16), em.ctypes.data_as(C.POINTER(C.c_int32)))
+                                C.c_void_p(16), C.c_void_p(32), em.ctypes.data_as(C.POINTER(C.c_int32)))
     return rc, em
 
 
@@ -107,6 +107,9 @@ def test_push_validation_and_positions():
     assert enc.stream_info(0).pos == 6 and enc.stream_info(3).pos == 4
     rc = enc.lib.cac_push_chunk(enc.ctx, 1, np.zeros(1, np.int32).ctypes.data_as(C.POINTER(C.c_int32)), 2, None, None, None)
     assert rc == CAC_EINVAL
+    rc = enc.lib.cac_push_chunk(enc.ctx, 1, np.zeros(1, np.int32).ctypes.data_as(C.POINTER(C.c_int32)), 2,
+                                C.c_void_p(16), C.c_void_p(16), None)
+    assert rc == CAC_EINVAL and b"different" in enc.lib.cac_last_error(enc.ctx)
 
 
 def test_flush_then_push_needs_reset():
