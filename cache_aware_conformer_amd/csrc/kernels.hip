@@ -380,32 +380,86 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
   __syncthreads();
 
   // ================= phase 2: products, reductions, epilogue
-  for (int u = 0; u < UMAX || (KCH == 0 && u < upw); ++u) {
-    if (u >= upw) break;
-    const int unit = u0 + u;
-    if (unit >= units) break;
-    float acc[COLS][MR];
+  if constexpr (KCH > 0) {
 #pragma unroll
-    for (int c = 0; c < COLS; ++c)
+    for (int u = 0; u < UMAX; ++u) {
+      const int unit = u0 + u;
+      if (u < upw && unit < units) {
+        float acc[COLS][MR];
 #pragma unroll
-      for (int r = 0; r < MR; ++r) acc[c][r] = 0.0f;
-    if constexpr (KCH > 0) {
+        for (int c = 0; c < COLS; ++c)
+#pragma unroll
+          for (int r = 0; r < MR; ++r) acc[c][r] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < COLS; ++c)
+#pragma unroll
+          for (int k = 0; k < KCH; ++k) {
+            float w[VEC];
+            wunpack<TW>(wr[(u * COLS + c) * KCH + k], w);
+            const float* ap = sA + (k * 64 + lane) * VEC;
+#pragma unroll
+            for (int r = 0; r < MR; ++r) {
+              float sacc = 0.0f;
+#pragma unroll
+              for (int v = 0; v < VEC; ++v) sacc += w[v] * ap[r * K + v];
+              acc[c][r] += sacc;
+            }
+          }
+#pragma unroll
+        for (int c = 0; c < COLS; ++c)
+#pragma unroll
+          for (int r = 0; r < MR; ++r) acc[c][r] = wave_sum(acc[c][r]);
+        float va = 0.0f, vb = 0.0f;
+#pragma unroll
+        for (int r = 0; r < MR; ++r)
+          if (r == lane) { va = acc[0][r]; vb = acc[COLS - 1][r]; }
+        if (lane < mr) {
+          const int m = m_lane;
+          if constexpr (GLU) {
+            const float g = (va + eb[u][0]) * sigmoid_f(vb + eb[u][COLS - 1]);
+            const int slot = (row_slot_pos + m % e.cv.nf) % e.Rc;
+            st<TW>((TW*)e.cring + ((long)row_id * e.Rc + slot) * e.D + unit, g);
+          } else {
+            const float v = va + eb[u][0];
+            switch (e.kind) {
+              case EPI_STORE: st<TW>((TW*)e.out + (long)m * e.ldo + unit, v); break;
+              case EPI_SILU: st<TW>((TW*)e.out + (long)m * e.ldo + unit, silu_f(v)); break;
+              case EPI_RELU_FE: {
+                const bool before_start = row_slot_pos == 0 && m % e.fe_rows_per_stream < e.fe_neg_rows;
+                st<TW>((TW*)e.out + (long)m * e.ldo + unit, before_start ? 0.0f : fmaxf(v, 0.0f));
+              } break;
+              case EPI_RESID: {
+                float base = er[u];
+                if (res_stats) base = (base - stats[2 * lane]) * stats[2 * lane + 1] * a.res_g[unit] + a.res_b[unit];
+                ((float*)e.out)[(long)m * D + unit] = base + e.alpha * v;
+              } break;
+              case EPI_F32: ((float*)e.out)[(long)omap_row * e.ldo + unit] = v; break;
+              case EPI_QKV: {
+                const int which = unit / e.D, c = unit % e.D;
+                if (which == 0) {
+                  e.qbuf[(long)m * e.D + c] = v;
+                } else {
+                  const int slot = (row_slot_pos + m % e.cv.nf) % e.R;
+                  TW* ring = (TW*)(which == 1 ? e.kring : e.vring);
+                  st<TW>(ring + (((long)row_id * e.H + c / e.hd) * e.R + slot) * e.hd + c % e.hd, v);
+                }
+              } break;
+              default: break;
+            }
+          }
+        }
+      }
+    }
+  } else {
+    // generic K: weights read here, epilogue operands read at the end
+    for (int u = 0; u < upw; ++u) {
+      const int unit = u0 + u;
+      if (unit >= units) break;
+      float acc[COLS][MR];
 #pragma unroll
       for (int c = 0; c < COLS; ++c)
 #pragma unroll
-        for (int k = 0; k < KCH; ++k) {
-          float w[VEC];
-          wunpack<TW>(wr[((u < UMAX ? u : 0) * COLS + c) * KCH + k], w);
-          const float* ap = sA + (k * 64 + lane) * VEC;
-#pragma unroll
-          for (int r = 0; r < MR; ++r) {
-            float sacc = 0.0f;
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) sacc += w[v] * ap[r * K + v];
-            acc[c][r] += sacc;
-          }
-        }
-    } else {
+        for (int r = 0; r < MR; ++r) acc[c][r] = 0.0f;
 #pragma unroll
       for (int c = 0; c < COLS; ++c) {
         const int col = GLU ? glu_a_col(unit) + 32 * c : unit;
@@ -416,61 +470,26 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
           for (int r = 0; r < MR; ++r) acc[c][r] += w * sA[r * K + k];
         }
       }
-    }
 #pragma unroll
-    for (int c = 0; c < COLS; ++c)
+      for (int c = 0; c < COLS; ++c)
 #pragma unroll
-      for (int r = 0; r < MR; ++r) acc[c][r] = wave_sum(acc[c][r]);
-    if (lane >= mr) continue;
-    float va = 0.0f, vb = 0.0f;
+        for (int r = 0; r < MR; ++r) acc[c][r] = wave_sum(acc[c][r]);
+      float va = 0.0f, vb = 0.0f;
 #pragma unroll
-    for (int r = 0; r < MR; ++r)
-      if (r == lane) { va = acc[0][r]; vb = acc[COLS - 1][r]; }
-    const int m = m_lane;
-    if (KCH == 0) {  // generic shape: operands read here
-      if constexpr (GLU) {
-        epi_glu<TW>(e, m, unit, va, vb);
-      } else if (e.kind == EPI_RESID && a.res_src) {
-        float base = a.res_src[(long)m * D + unit];
-        if (a.res_g) base = (base - stats[2 * lane]) * stats[2 * lane + 1] * a.res_g[unit] + a.res_b[unit];
-        if (e.bias) va += e.bias[unit];
-        ((float*)e.out)[(long)m * D + unit] = base + e.alpha * va;
-      } else {
-        epi_one<TW>(e, m, unit, va);
-      }
-      continue;
-    }
-    const int uu = u < UE ? u : 0;
-    if constexpr (GLU) {
-      const float g = (va + eb[uu][0]) * sigmoid_f(vb + eb[uu][COLS - 1]);
-      const int slot = (row_slot_pos + m % e.cv.nf) % e.Rc;
-      st<TW>((TW*)e.cring + ((long)row_id * e.Rc + slot) * e.D + unit, g);
-    } else {
-      const float v = va + eb[uu][0];
-      switch (e.kind) {
-        case EPI_STORE: st<TW>((TW*)e.out + (long)m * e.ldo + unit, v); break;
-        case EPI_SILU: st<TW>((TW*)e.out + (long)m * e.ldo + unit, silu_f(v)); break;
-        case EPI_RELU_FE: {
-          const bool before_start = row_slot_pos == 0 && m % e.fe_rows_per_stream < e.fe_neg_rows;
-          st<TW>((TW*)e.out + (long)m * e.ldo + unit, before_start ? 0.0f : fmaxf(v, 0.0f));
-        } break;
-        case EPI_RESID: {
-          float base = er[uu];
-          if (res_stats) base = (base - stats[2 * lane]) * stats[2 * lane + 1] * a.res_g[unit] + a.res_b[unit];
-          ((float*)e.out)[(long)m * D + unit] = base + e.alpha * v;
-        } break;
-        case EPI_F32: ((float*)e.out)[(long)omap_row * e.ldo + unit] = v; break;
-        case EPI_QKV: {
-          const int which = unit / e.D, c = unit % e.D;
-          if (which == 0) {
-            e.qbuf[(long)m * e.D + c] = v;
-          } else {
-            const int slot = (row_slot_pos + m % e.cv.nf) % e.R;
-            TW* ring = (TW*)(which == 1 ? e.kring : e.vring);
-            st<TW>(ring + (((long)row_id * e.H + c / e.hd) * e.R + slot) * e.hd + c % e.hd, v);
-          }
-        } break;
-        default: break;
+      for (int r = 0; r < MR; ++r)
+        if (r == lane) { va = acc[0][r]; vb = acc[COLS - 1][r]; }
+      if (lane < mr) {
+        const int m = m_lane;
+        if constexpr (GLU) {
+          epi_glu<TW>(e, m, unit, va, vb);
+        } else if (e.kind == EPI_RESID && a.res_src) {
+          float base = a.res_src[(long)m * D + unit];
+          if (a.res_g) base = (base - stats[2 * lane]) * stats[2 * lane + 1] * a.res_g[unit] + a.res_b[unit];
+          if (e.bias) va += e.bias[unit];
+          ((float*)e.out)[(long)m * D + unit] = base + e.alpha * va;
+        } else {
+          epi_one<TW>(e, m, unit, va);
+        }
       }
     }
   }
@@ -479,6 +498,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
 // =============================================================================== MFMA GEMM (bf16)
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
 typedef __attribute__((ext_vector_type(16))) float f32x16_v;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_v;  // 16-byte staging register
 
 // Block tile BM x BN, k-step 64, 4 waves as WM x WN, each wave (BM/WM) x (BN/WN) made of
 // 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, 4 per k-step). A and W k-tiles live in two
@@ -486,7 +506,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_v;
 // k-tile is fetched into registers while the current one is multiplied and stored into the
 // other buffer afterwards, so each k-step has one barrier and its loads overlap a k-step of MFMA.
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_mfma_kernel(GemmArgs a) {
   constexpr int BK = 64, LDK = BK + 8;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int A_PER_T = BM * (BK / 8) / 256, B_PER_T = BN * (BK / 8) / 256;
@@ -515,21 +535,19 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
     bptr[i] = W + (long)min(bn0 + row, N - 1) * K + kc;
     boff[i] = row * LDK + kc;
   }
-  uint4 ra[A_PER_T], rb[B_PER_T];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) ra[i] = *(const uint4*)(aptr[i] + kt * BK);
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) rb[i] = *(const uint4*)(bptr[i] + kt * BK);
-  };
-  auto sstore = [&](int buf) {
-    bf16_t* Ab = lds + buf * (BM + BN) * LDK;
-    bf16_t* Bb = Ab + BM * LDK;
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) *(uint4*)(Ab + aoff[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) *(uint4*)(Bb + boff[i]) = rb[i];
-  };
+  u32x4_v ra[A_PER_T], rb[B_PER_T];
+#define MFMA_GLOAD(kt)                                                                     \
+  {                                                                                        \
+    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) ra[i] = *(const u32x4_v*)(aptr[i] + (kt) * BK); \
+    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) rb[i] = *(const u32x4_v*)(bptr[i] + (kt) * BK); \
+  }
+#define MFMA_SSTORE(buf)                                                                   \
+  {                                                                                        \
+    bf16_t* Ab_ = lds + (buf) * (BM + BN) * LDK;                                           \
+    bf16_t* Bb_ = Ab_ + BM * LDK;                                                          \
+    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) *(u32x4_v*)(Ab_ + aoff[i]) = ra[i];  \
+    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) *(u32x4_v*)(Bb_ + boff[i]) = rb[i];  \
+  }
 
   f32x16_v acc[FM][FN];
 #pragma unroll
@@ -540,12 +558,15 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int KT = K / BK;
-  gload(0);
-  sstore(0);
+  MFMA_GLOAD(0);
+  MFMA_SSTORE(0);
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < KT) gload(kt + 1);
+    // unconditional prefetch (the last k-step reloads its own tile into the idle buffer) keeps
+    // ra/rb in registers
+    const int nxt = kt + 1 < KT ? kt + 1 : kt;
+    MFMA_GLOAD(nxt);
     const bf16_t* Ab = lds + buf * (BM + BN) * LDK;
     const bf16_t* Bb = Ab + BM * LDK;
 #pragma unroll
@@ -563,39 +584,51 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs a) {
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) sstore(buf ^ 1);
+    // schedule: the next k-tile's global loads first, then this k-step's MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x020, A_PER_T + B_PER_T, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * FM * FN, 0);
+    MFMA_SSTORE(buf ^ 1);
     __syncthreads();
   }
+#undef MFMA_GLOAD
+#undef MFMA_SSTORE
 
-  // fragment element r of lane: row 8*(r/4) + 4*(lane/32) + r%4, column lane%32
-  const bool glu = a.epi.kind == EPI_GLU;
+  // The accumulator tile goes to LDS (fragment element r of a lane is row 8*(r/4) +
+  // 4*(lane/32) + r%4, column lane%32; all indices compile-time, so acc stays in registers),
+  // then the epilogue walks the tile row-major: coalesced stores, no register indexing.
+  constexpr int CS = BN + 4;
+  float* ct = (float*)lds;  // the last k-step ended with a barrier: the staging buffers are free
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = bm0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= M) continue;
-      if (glu) {
-        // wave tile holds 32-column pairs: fragment 2j = values, 2j+1 = gates
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j + 1 < FN; j += 2) {
-          const int pcol = bn0 + wn * TN + j * 32;  // multiple of 64
-          const int c = (pcol >> 6) * 32 + (lane & 31);
-          if (pcol < N) epi_glu<bf16_t>(a.epi, row, c, acc[i][j][r], acc[i][j + 1][r]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = bn0 + wn * TN + j * 32 + (lane & 31);
-          if (col < N) epi_one<bf16_t>(a.epi, row, col, acc[i][j][r]);
-        }
-      }
+      for (int r = 0; r < 16; ++r)
+        ct[(wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * CS + wn * TN + j * 32 + (lane & 31)] = acc[i][j][r];
+  __syncthreads();
+  if (a.epi.kind == EPI_GLU) {
+    // packed columns: each 64-column block holds 32 value columns then their 32 gates
+    for (int idx = tid; idx < BM * (BN / 2); idx += 256) {
+      const int rr = idx / (BN / 2), ch = idx % (BN / 2);
+      const int pc = (ch >> 5) * 64 + (ch & 31);
+      const int row = bm0 + rr;
+      if (row < M && bn0 + pc < N)
+        epi_glu<bf16_t>(a.epi, row, (bn0 >> 6) * 32 + ch, ct[rr * CS + pc], ct[rr * CS + pc + 32]);
+    }
+  } else {
+    for (int idx = tid; idx < BM * BN; idx += 256) {
+      const int rr = idx / BN, cc = idx % BN;
+      const int row = bm0 + rr, col = bn0 + cc;
+      if (row < M && col < N) epi_one<bf16_t>(a.epi, row, col, ct[rr * CS + cc]);
     }
   }
 }
 
 template <int BM, int BN>
-constexpr size_t mfma_lds() { return (size_t)2 * (BM + BN) * (64 + 8) * sizeof(bf16_t); }
+constexpr size_t mfma_lds() {
+  // two k-tile buffers, reused afterwards for the float accumulator tile
+  return std::max((size_t)2 * (BM + BN) * (64 + 8) * sizeof(bf16_t), (size_t)BM * (BN + 4) * sizeof(float));
+}
 
 // =============================================================================== LayerNorm
 // One wave per row; the row, gains and shifts are loaded together as 16-byte chunks (D a
