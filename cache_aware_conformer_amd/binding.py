@@ -212,6 +212,10 @@ class StreamingEncoder:
                 n_frames = x.shape[1]
         if out is None and not self.dry:
             out = self.torch.empty((n, n_frames, self.P), dtype=self.torch.float32, device=self.device)
+        elif hasattr(out, "is_contiguous"):
+            if not out.is_contiguous() or out.dtype != self.torch.float32 or out.numel() < n * n_frames * self.P:
+                raise ValueError(f"out must be a contiguous float32 tensor of at least {n}x{n_frames}x{self.P} "
+                                 f"elements, got {out.dtype} {tuple(out.shape)} contiguous={out.is_contiguous()}")
         emitted = np.zeros(n, dtype=np.int32)
         xp = None if x is None else (x.data_ptr() if hasattr(x, "data_ptr") else int(x))
         op = None if out is None else (out.data_ptr() if hasattr(out, "data_ptr") else int(out))
@@ -227,6 +231,10 @@ class StreamingEncoder:
         n = ids.size
         if out is None and not self.dry and self.cfg.n_lookahead:
             out = self.torch.empty((n, self.cfg.n_lookahead, self.P), dtype=self.torch.float32, device=self.device)
+        elif out is not None and (not out.is_contiguous() or out.dtype != self.torch.float32
+                                  or out.numel() < n * self.cfg.n_lookahead * self.P):
+            raise ValueError(f"out must be a contiguous float32 tensor of at least {n}x{self.cfg.n_lookahead}x{self.P} "
+                             f"elements, got {out.dtype} {tuple(out.shape)}")
         frames = np.zeros(n, dtype=np.int32)
         op = None if out is None else out.data_ptr()
         self._check(self.lib.cac_flush(self.ctx, n, idp, op, frames.ctypes.data_as(_ip)))

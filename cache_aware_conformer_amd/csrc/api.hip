@@ -191,7 +191,6 @@ struct Packer {
   }
 };
 
-int glu_a_col_host(int c) { return (c >> 5) * 64 + (c & 31); }
 
 }  // namespace
 
@@ -356,9 +355,22 @@ struct Pass {
       // ---- conv module: LN -> pw1 -> GLU into the ring; depthwise + SiLU; pw2 + residual
       EpiArgs glu = epi0();
       glu.kind = EPI_GLU; glu.bias = F32(lo.b_pw1); glu.cring = cr;
+      // two rows: the depthwise conv + SiLU runs in pw1's epilogue (the rows of the call sit on
+      // neighbouring lanes there), pw2 reads its output as a plain operand
+      GemmArgs pw1{};
+      pw1.M = M; pw1.N = 2 * d.D; pw1.K = d.D; pw1.W = lb + lo.w_pw1;
+      pw1.A = cur; pw1.amap = RowMap{INT_MAX, 0, d.D};
+      pw1.a_f32 = 1; pw1.ln_g = F32(lo.ln[4]); pw1.ln_b = F32(lo.ln[5]); pw1.a_scratch = c->P<void>(c->lay.y);
+      pw1.epi = glu;
+      pw1.epi.kind = EPI_GLU_DW; pw1.epi.out = c->P<void>(c->lay.e); pw1.epi.ldo = d.D;
+      pw1.dw_w = F32(lo.dw_w); pw1.dw_b = F32(lo.b_dw); pw1.dw_taps = d.K; pw1.dw_Rc = d.Rc;
       L.role = "pw1";
-      gemm_x(F32(lo.ln[4]), F32(lo.ln[5]), lb + lo.w_pw1, 2 * d.D, glu, false);
-      if (fz) {
+      if (fz && rowdot_supported(pw1, d.dt)) {
+        launch_gemm(L, pw1, d.dt, 0);
+        L.role = "pw2";
+        gemm_plain(c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, d.D, resid(1.0f, F32(lo.b_pw2)));
+      } else if (fz) {
+        gemm_x(F32(lo.ln[4]), F32(lo.ln[5]), lb + lo.w_pw1, 2 * d.D, glu, false);
         GemmArgs g{};
         g.M = M; g.N = d.D; g.K = d.D; g.W = lb + lo.w_pw2; g.epi = resid(1.0f, F32(lo.b_pw2));
         g.a_dw = 1; g.dw_ring = cr; g.dw_w = F32(lo.dw_w); g.dw_b = F32(lo.b_dw); g.dw_taps = d.K; g.dw_Rc = d.Rc;
@@ -366,6 +378,7 @@ struct Pass {
         L.role = "pw2";
         launch_gemm(L, g, d.dt, 0);
       } else {
+        gemm_x(F32(lo.ln[4]), F32(lo.ln[5]), lb + lo.w_pw1, 2 * d.D, glu, false);
         DwArgs dw{cv, cr, F32(lo.dw_w), F32(lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
         L.tag("dwconv", (double)cv.n_streams * (d.Kc + cv.nf) * d.D * d.esz, 2.0 * d.K * d.D * M);
         launch_dwconv(L, dw, d.dt);
@@ -520,7 +533,7 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
     {  // pw1 [D][2D] -> GLU-packed rows: value channel c at glu_a_col(c), its gate 32 rows later
       const float* w = take(D * 2 * D);
       for (size_t ch = 0; ch < D; ++ch) {
-        const size_t ra = glu_a_col_host((int)ch), rb = ra + 32;
+        const size_t ra = glu_a_col((int)ch), rb = ra + 32;
         for (size_t k = 0; k < D; ++k) {
           pk.op(base + lo.w_pw1, ra * D + k, w[k * 2 * D + ch]);
           pk.op(base + lo.w_pw1, rb * D + k, w[k * 2 * D + D + ch]);

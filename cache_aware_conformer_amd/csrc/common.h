@@ -74,7 +74,13 @@ enum EpiKind {
   EPI_F32 = 4,     // out_f[row_out(m)][n] = acc + b              (float32)
   EPI_QKV = 5,     // q -> qbuf (f32); k, v -> ring slots of the row's position
   EPI_GLU = 6,     // a*sigmoid(b) of GLU-packed column pairs -> conv ring slot
+  EPI_GLU_DW = 7,  // EPI_GLU, then the causal depthwise conv + SiLU of the call's rows over the
+                   // ring -> out_t[m][c] (compute dtype); two-row kernel only (GemmArgs dw_*)
 };
+
+// GLU packing of the pointwise-1 weight rows: packed row (c / 32) * 64 + c % 32 holds value
+// channel c, 32 rows further its gate (so a 32-wide tile holds matching value/gate halves).
+__host__ __device__ __forceinline__ int glu_a_col(int c) { return (c >> 5) * 64 + (c & 31); }
 
 struct EpiArgs {
   int kind;
@@ -227,8 +233,10 @@ struct LaGatherArgs {   // lookahead: x rows of a pass from the pending ring
 // Kernels are launched through a Launcher: either straight onto a stream, or appended to a
 // HIP graph as a chain of kernel nodes (node handles are kept so pointer arguments can be
 // re-pointed before each replay).
-// Optional per-kernel timing: every launch bracketed by two HIP events on the launch stream,
-// aggregated by kernel name together with the launch's algorithmic bytes and flops.
+// Optional per-kernel timing (direct launches): each kernel is launched with a start and a stop
+// HIP event bound to its own dispatch (hipExtLaunchKernel), so the elapsed time is the kernel's
+// execution on the launch stream, without the host's submission gaps; aggregated by kernel name
+// together with the launch's algorithmic bytes and flops.
 struct Profiler {
   struct Rec { int name; double bytes, flops; hipEvent_t a, b; };
   std::vector<hipEvent_t> free_ev;
@@ -282,6 +290,11 @@ struct Launcher {
 
 // ------------------------------------------------------------------------ wrappers
 void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path);
+// Two-row kernel: true when it takes this product (M <= 2 and a supported operand/epilogue mix);
+// rowdot_launch returns false, launching nothing, otherwise.
+bool rowdot_supported(const GemmArgs& a, int dtype);
+bool rowdot_launch(Launcher& L, const GemmArgs& a, int dtype);
+double gemm_bytes(const GemmArgs& a, int wsz);
 void launch_ln(Launcher& L, const LnArgs& a, int dtype);
 void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd);
 void launch_dwconv(Launcher& L, const DwArgs& a, int dtype);

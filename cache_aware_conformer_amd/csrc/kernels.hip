@@ -13,6 +13,8 @@
 // rows a call still reads are never the ones it overwrites.
 #include "common.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <climits>
 
@@ -67,10 +69,12 @@ void Launcher::launch_raw(const void* fn, dim3 grid, dim3 block, size_t shmem, v
   if (!graph) {
     if (prof) {
       hipEvent_t a = prof->get(), b = prof->get();
-      if (a && b) err = hipEventRecord(a, stream);
-      if (err == hipSuccess) err = hipLaunchKernel(fn, grid, block, kp, shmem, stream);
-      if (err == hipSuccess && a && b) err = hipEventRecord(b, stream);
-      if (err == hipSuccess && a && b) prof->pending.push_back({prof->name_id(tag_name), tag_bytes, tag_flops, a, b});
+      if (a && b) {
+        err = hipExtLaunchKernel(fn, grid, block, kp, shmem, stream, a, b, 0);
+        if (err == hipSuccess) prof->pending.push_back({prof->name_id(tag_name), tag_bytes, tag_flops, a, b});
+      } else {
+        err = hipLaunchKernel(fn, grid, block, kp, shmem, stream);
+      }
       tag_bytes = tag_flops = 0.0;
       return;
     }
@@ -160,8 +164,6 @@ __device__ __forceinline__ void epi_glu(const EpiArgs& e, int m, int c, float va
   st<T>((T*)e.cring + ((long)id * e.Rc + slot) * e.D + c, g);
 }
 
-// GLU packing: packed column (c / 32) * 64 + c % 32 holds value channel c, +32 its gate.
-__device__ __forceinline__ int glu_a_col(int c) { return (c >> 5) * 64 + (c & 31); }
 
 // =============================================================================== small-M GEMM
 // C[M][N] = A[M][K] W[N][K]^T for few rows (MR per block). Each wave owns whole output units
@@ -686,13 +688,16 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
 // Algorithmic HBM bytes of one dense product: the weights once, plus the depthwise ring rows
 // it reads and what its epilogue writes to per-stream state (K/V rows, depthwise input rows)
 // or to the caller's output. Activations that stay on chip or in cache are not counted.
-static double gemm_bytes(const GemmArgs& a, size_t wsz) {
+double gemm_bytes(const GemmArgs& a, int wsz) {
   double b = (double)a.N * a.K * wsz;
   const double esz = (double)wsz;
   if (a.a_dw) b += (double)a.epi.cv.n_streams * (a.dw_taps - 1 + a.epi.cv.nf) * a.K * esz;
   switch (a.epi.kind) {
     case EPI_QKV: b += (double)a.M * 2.0 * a.epi.D * esz; break;
     case EPI_GLU: b += (double)a.M * (a.N / 2) * esz; break;
+    case EPI_GLU_DW:  // ring rows written and the older ring rows the conv reads
+      b += (double)a.M * (a.N / 2) * esz + (double)a.epi.cv.n_streams * (a.dw_taps - 1) * (a.N / 2) * esz;
+      break;
     case EPI_F32: if (a.epi.ldo != a.epi.D || a.epi.omap) b += (double)a.M * a.N * 4.0; break;
     default: break;
   }
@@ -737,7 +742,7 @@ static void gemv_dispatch(Launcher& L, const GemmArgs& a) {
   const int MR = a.M <= 2 ? 2 : 8;
   const void* fn = MR == 2 ? gemv_pick_kch<TW, TA, 2>(kch, glu) : gemv_pick_kch<TW, TA, 8>(kch, glu);
   const size_t shm = ((size_t)MR * a.K + 2 * MR) * sizeof(float);
-  L.tag(sizeof(TW) == 4 ? "gemm_small_m_f32" : "gemm_small_m_bf16", gemm_bytes(a, sizeof(TW)), 2.0 * a.M * a.N * a.K);
+  L.tag(sizeof(TW) == 4 ? "gemm_small_m_f32" : "gemm_small_m_bf16", gemm_bytes(a, (int)sizeof(TW)), 2.0 * a.M * a.N * a.K);
   L.launch(fn, dim3((units + 4 * upw - 1) / (4 * upw), (a.M + MR - 1) / MR), dim3(256), shm, &args);
 }
 
@@ -780,6 +785,11 @@ __global__ __launch_bounds__(256) void cvt_kernel(CvtArgs a) {
 }
 
 void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path) {
+  if (path == 0 && rowdot_launch(L, a, dtype)) return;
+  if (a.epi.kind == EPI_GLU_DW) {  // only the two-row kernel has this epilogue
+    if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
+    return;
+  }
   if (dtype == DT_F32) {
     gemv_dispatch<float, float>(L, a);
     return;

@@ -13,7 +13,16 @@ from oracle.brute import attention_brute
 from synth import C1, C2, make_inputs, make_weights
 from synth.configs import EncConfig
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True)
+def _float64_default():
+    """torch reference ops of this module run in float64; the default is restored afterwards
+    so that tests collected later (the GPU parity tests) allocate float32 as they expect."""
+    prev = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(prev)
 
 
 def tiny(**kw):
