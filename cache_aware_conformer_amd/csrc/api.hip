@@ -77,7 +77,8 @@ bool make_dims(const cac_config* c, Dims& d, std::string& why) {
   if (d.lookahead) { d.rel_lo = -d.right; d.nrel = d.Lc + d.right + 1; }
   else { d.rel_lo = -(d.c - 1); d.nrel = d.Lc + 2 * d.c - 1; }
   d.esz = d.dt == CAC_BF16 ? 2 : 4;
-  if (attention_shmem(d.nfmax, d.Lc + d.nfmax, d.nrel, d.hd) > 160 * 1024) return bad("attention tile exceeds LDS: reduce att_left or frames per call");
+  if (d.R > 256) return bad("att_left + frames per call must be at most 256 (K/V ring slots)");
+  if (attention_shmem(d.nfmax, d.R, d.nrel, d.hd, d.esz) > 160 * 1024) return bad("attention tile exceeds LDS: reduce att_left or frames per call");
   return true;
 }
 

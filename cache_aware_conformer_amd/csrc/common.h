@@ -42,6 +42,58 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// ------------------------------------------------------------------------ register exchanges
+// Cross-lane exchanges that never go through LDS: v_readlane, the gfx950 lane-half swaps
+// (v_permlane32_swap / v_permlane16_swap) and DPP row patterns.
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+// pair_sum32(a, b): lanes 0..31 get a[L] + a[L + 32], lanes 32..63 get b[L - 32] + b[L]
+// (pair_sum16 likewise across the two 16-lane halves of each 32).
+__device__ __forceinline__ float pair_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// value of lane L ^ 32 / L ^ 16
+__device__ __forceinline__ float xor32(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((lane & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor16(float v, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((lane & 16) ? r[0] : r[1]);
+}
+// value of lane L ^ 15 (row mirror), L ^ 7 (half-row mirror), L ^ 2, L ^ 1
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_MIRROR16 = 0x140, DPP_MIRROR8 = 0x141, DPP_XOR2 = 0x4E, DPP_XOR1 = 0xB1;
+
+// sum / max over all 64 lanes, the result on every lane
+__device__ __forceinline__ float wave_total(float v) {
+  v += dpp<DPP_MIRROR16>(v);
+  v += dpp<DPP_MIRROR8>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_XOR1>(v);
+  v = pair_sum16(v, v);
+  return pair_sum32(v, v);
+}
+__device__ __forceinline__ float wave_top(float v) {
+  v = fmaxf(v, dpp<DPP_MIRROR16>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR8>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // ------------------------------------------------------------------------ row addressing
 // Row m of a logical [M][K] operand lives at base + (m / group) * group_stride +
 // (m % group) * row_stride elements. Plain row-major: group = M (or any value > M),
@@ -307,4 +359,4 @@ void launch_posproj(Launcher& L, const PosProjArgs& a);
 void launch_state(Launcher& L, const StateArgs& a, int op);  // 0 reset, 1 import, 2 export
 void launch_la_store(Launcher& L, const LaStoreArgs& a, int dtype);
 void launch_la_gather(Launcher& L, const LaGatherArgs& a, int dtype);
-size_t attention_shmem(int nf, int nk_max, int nrel, int hd);
+size_t attention_shmem(int nf, int R, int nrel, int hd, int esz);

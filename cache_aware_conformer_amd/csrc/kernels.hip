@@ -832,20 +832,20 @@ void launch_ln(Launcher& L, const LnArgs& a, int dtype) {
 }
 
 // =============================================================================== attention
-// One 256-thread block per (call stream, head). Everything the block reads is staged in LDS
-// first, all global loads issued together: the ring rows of positions
-// [max(0, pos0 - Lc), pos0 + nf - 1] (K and V; the rows of this call were written by the QKV
-// epilogue), the head's projected position rows, the call's q rows and u, v. Then one thread
-// per (query i, key j):
-//   s[i][j] = ((q_i + u) . k_j + (q_i + v) . P[p_i - q_j]) * scale on visible keys, else -inf,
-// a wave per query row for the softmax, and one thread per (query, dim) for o_i = sum_j p_ij v_j.
-constexpr int ATT_PAD = 4;  // row stride HD + 4 keeps 16-byte alignment and spreads LDS banks
+// One block of 4 waves per (call stream, head). Every global read is issued before the block's
+// single barrier: all R slots of the head's K and V rings (their addresses depend on the stream
+// id only, not on its position), the head's projected-position rows, the call's q rows and u, v.
+// K and V stay in their storage type in LDS. Then a wave per query row i, lanes over ring slots
+// j (slot j holds position q_j, the one position of the ring window congruent to j mod R):
+//   s[i][j] = ((q_i + u) . k_j + (q_i + v) . P[p_i - q_j]) * scale on visible keys, else -inf;
+// max and sum of the row by register exchanges, and o_i = sum_j softmax(s)_ij v_j with lanes
+// over head dims taking each p_ij from the lane that holds it.
+constexpr int ATT_UM = 8;  // 16-byte chunks per thread per staging pass and array
 
-size_t attention_shmem(int nf, int nk_max, int nrel, int hd) {
-  const size_t rs = (size_t)hd + ATT_PAD;
-  const size_t f = (size_t)nk_max * rs + (size_t)nk_max * hd + (size_t)nrel * rs + (size_t)nf * hd + 2 * (size_t)hd +
-                   (size_t)nf * nk_max;
-  return f * sizeof(float);
+size_t attention_shmem(int nf, int R, int nrel, int hd, int esz) {
+  const size_t kv_row = ((size_t)hd * esz / 16 + 1) * 16;  // rows padded by one chunk
+  const size_t f_row = ((size_t)hd / 4 + 1) * 16;
+  return 2 * (size_t)R * kv_row + (size_t)nrel * f_row + ((size_t)nf + 2) * hd * 4 + 4 * 256 * 4;
 }
 
 __device__ __forceinline__ bool att_visible(const AttnArgs& a, int p, int q) {
@@ -855,146 +855,190 @@ __device__ __forceinline__ bool att_visible(const AttnArgs& a, int p, int q) {
   return q >= cs - a.Lc && q <= cs + a.chunk - 1;
 }
 
-template <typename T> __device__ __forceinline__ void unpack16(const uint4& r, float* f);
-template <> __device__ __forceinline__ void unpack16<float>(const uint4& r, float* f) {
-  f[0] = __uint_as_float(r.x); f[1] = __uint_as_float(r.y); f[2] = __uint_as_float(r.z); f[3] = __uint_as_float(r.w);
-}
-template <> __device__ __forceinline__ void unpack16<bf16_t>(const uint4& r, float* f) {
-  const uint32_t u[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) { f[2 * i] = __uint_as_float(u[i] << 16); f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u); }
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
+
+// four consecutive elements (index 4c..4c+3) of an LDS row of T as float
+template <typename T>
+__device__ __forceinline__ f32x4_v lds4(const unsigned char* row, int c) {
+  if constexpr (sizeof(T) == 4) {
+    return ((const f32x4_v*)row)[c];
+  } else {
+    const uint2 u = ((const uint2*)row)[c];
+    return f32x4_v{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                   __uint_as_float(u.y & 0xffff0000u)};
+  }
 }
 
-template <typename T, int HD>
+template <typename T, int HD, int JT>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  extern __shared__ float sm[];
-  constexpr int RS = HD + ATT_PAD;
-  constexpr int EPC = 16 / sizeof(T);  // K/V elements per 16-byte chunk
-  constexpr int KCPR = HD / EPC;       // chunks per K/V row
-  constexpr int FCPR = HD / 4;         // chunks per float row (P, q, u, v)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smb[];
+  constexpr int KC = HD * (int)sizeof(T) / 16;  // 16-byte chunks per K/V row
+  constexpr int KS = (KC + 1) * 16;             // LDS bytes per K/V row
+  constexpr int FC = HD / 4;                    // chunks per float row
+  constexpr int FS = (FC + 1) * 16;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nf = a.cv.nf, nrel = a.nrel, nkmax = a.Lc + nf;
-  float* Ks = sm;
-  float* Vs = Ks + nkmax * RS;
-  float* Ps = Vs + nkmax * HD;
-  float* Qs = Ps + nrel * RS;
-  float* Us = Qs + nf * HD;
-  float* Wv = Us + HD;
-  float* sc = Wv + HD;
-  const int s = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int nf = a.cv.nf, R = a.R, nrel = a.nrel;
+  const int s = blockIdx.x / a.H, h = blockIdx.x - s * a.H;
   const int id = a.cv.ids[s];
   const int pos0 = a.cv.cpos[s];
-  const int q_lo = max(0, pos0 - a.Lc), nk = pos0 + nf - q_lo;
-  const T* kbase = (const T*)a.kring + ((long)id * a.H + h) * a.R * HD;
-  const T* vbase = (const T*)a.vring + ((long)id * a.H + h) * a.R * HD;
-  const float* pbase = a.posproj + (long)h * nrel * HD;
+  unsigned char* Ks = smb;
+  unsigned char* Vs = Ks + R * KS;
+  unsigned char* Ps = Vs + R * KS;
+  float* Qs = (float*)(Ps + nrel * FS);  // [nf][HD], then u [HD], v [HD]
+  float* Pw = Qs + (nf + 2) * HD + wave * 256;  // this wave's softmax weights, by ring slot
+  const u32x4_v* kg = (const u32x4_v*)((const T*)a.kring + ((long)id * a.H + h) * R * HD);
+  const u32x4_v* vg = (const u32x4_v*)((const T*)a.vring + ((long)id * a.H + h) * R * HD);
+  const u32x4_v* pg = (const u32x4_v*)(a.posproj + (long)h * nrel * HD);
+  const int nkv = R * KC, np = nrel * FC, nq = (nf + 2) * FC;
 
-  // ---- stage K, V, P, q, u, v (16-byte chunks, up to 16 in flight per thread)
-  const int nK = nk * KCPR, nP = nrel * FCPR, nQ = nf * FCPR;
-  const int total = 2 * nK + nP + nQ + 2 * FCPR;
-  constexpr int U = 16;
-  for (int base = 0; base < total; base += 256 * U) {
-    uint4 r[U];
+  // ---- staging: K, V, P in passes of ATT_UM chunks per thread (one pass unless R is large),
+  // indices clamped so that every load is unconditional; q, u, v with the first pass
+  for (int base = 0; base < nkv || base < np; base += 256 * ATT_UM) {
+    u32x4_v rk[ATT_UM], rv[ATT_UM], rp[ATT_UM], rq[2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < ATT_UM; ++u) {
       const int c = base + u * 256 + tid;
-      const uint4* src = nullptr;
-      if (c < nK) {
-        src = (const uint4*)(kbase + (long)((q_lo + c / KCPR) % a.R) * HD) + c % KCPR;
-      } else if (c < 2 * nK) {
-        const int cc = c - nK;
-        src = (const uint4*)(vbase + (long)((q_lo + cc / KCPR) % a.R) * HD) + cc % KCPR;
-      } else if (c < 2 * nK + nP) {
-        const int cc = c - 2 * nK;
-        src = (const uint4*)(pbase + (long)(cc / FCPR) * HD) + cc % FCPR;
-      } else if (c < 2 * nK + nP + nQ) {
-        const int cc = c - 2 * nK - nP;
-        src = (const uint4*)(a.q + (long)(s * nf + cc / FCPR) * a.D + h * HD) + cc % FCPR;
-      } else if (c < total) {
-        const int cc = c - 2 * nK - nP - nQ;
-        src = (const uint4*)((cc < FCPR ? a.pos_u : a.pos_v) + h * HD) + cc % FCPR;
+      const int ck = min(c, nkv - 1), cp = min(c, np - 1);
+      rk[u] = kg[ck];
+      rv[u] = vg[ck];
+      rp[u] = pg[cp];
+    }
+    if (base == 0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = min(u * 256 + tid, nq - 1), row = c / FC, col = c - row * FC;
+        const float* src = row < nf ? a.q + (long)(s * nf + row) * a.D + h * HD : (row == nf ? a.pos_u : a.pos_v) + h * HD;
+        rq[u] = *((const u32x4_v*)src + col);
       }
-      r[u] = src ? *src : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < ATT_UM; ++u) {
       const int c = base + u * 256 + tid;
-      if (c >= total) continue;
-      if (c < 2 * nK) {
-        float f[EPC];
-        unpack16<T>(r[u], f);
-        const int cc = c < nK ? c : c - nK;
-        float* dst = (c < nK ? Ks + (cc / KCPR) * RS : Vs + (cc / KCPR) * HD) + (cc % KCPR) * EPC;
+      if (c < nkv) {
+        const int row = c / KC, col = c - row * KC;
+        *(u32x4_v*)(Ks + row * KS + col * 16) = rk[u];
+        *(u32x4_v*)(Vs + row * KS + col * 16) = rv[u];
+      }
+      if (c < np) {
+        const int row = c / FC, col = c - row * FC;
+        *(u32x4_v*)(Ps + row * FS + col * 16) = rp[u];
+      }
+    }
+    if (base == 0) {
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) dst[e] = f[e];
-      } else {
-        float f[4];
-        unpack16<float>(r[u], f);
-        float* dst;
-        if (c < 2 * nK + nP) { const int cc = c - 2 * nK; dst = Ps + (cc / FCPR) * RS + (cc % FCPR) * 4; }
-        else if (c < 2 * nK + nP + nQ) { const int cc = c - 2 * nK - nP; dst = Qs + (cc / FCPR) * HD + (cc % FCPR) * 4; }
-        else { const int cc = c - 2 * nK - nP - nQ; dst = (cc < FCPR ? Us : Wv) + (cc % FCPR) * 4; }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = f[e];
+      for (int u = 0; u < 2; ++u) {
+        const int c = u * 256 + tid;
+        if (c < nq) ((u32x4_v*)Qs)[c] = rq[u];
       }
     }
   }
   __syncthreads();
 
-  // ---- scores: one (query, key) pair per thread
-  for (int pr = tid; pr < nf * nk; pr += 256) {
-    const int i = pr / nk, j = pr - i * nk;
-    const int p = pos0 + i, qk = q_lo + j;
-    float sv = -INFINITY;
-    if (att_visible(a, p, qk)) {
-      const float* qi = Qs + i * HD;
-      const float* kj = Ks + j * RS;
-      const float* pj = Ps + (p - qk - a.rel_lo) * RS;
-      float ac = 0.0f, bdv = 0.0f;
+  // ---- ring slots of this lane: slot j holds position pe - ((pe - j) mod R)
+  const int pe = pos0 + nf - 1, pm = pe % R, q_lo = max(0, pos0 - a.Lc);
+  int qj[JT];
 #pragma unroll
-      for (int d = 0; d < HD; d += 4) {
-        const float4 q4 = *(const float4*)(qi + d), k4 = *(const float4*)(kj + d), p4 = *(const float4*)(pj + d);
-        const float4 u4 = *(const float4*)(Us + d), v4 = *(const float4*)(Wv + d);
-        ac += (q4.x + u4.x) * k4.x + (q4.y + u4.y) * k4.y + (q4.z + u4.z) * k4.z + (q4.w + u4.w) * k4.w;
-        bdv += (q4.x + v4.x) * p4.x + (q4.y + v4.y) * p4.y + (q4.z + v4.z) * p4.z + (q4.w + v4.w) * p4.w;
-      }
-      sv = (ac + bdv) * a.scale;
-    }
-    sc[i * nkmax + j] = sv;
+  for (int t = 0; t < JT; ++t) {
+    const int j = lane + 64 * t;
+    int dd = pm - j;
+    dd += dd < 0 ? R : 0;
+    qj[t] = (j < R && pe - dd >= q_lo) ? pe - dd : -1;  // -1: no key in this slot
   }
-  __syncthreads();
-  // ---- softmax: a wave per query row
+  const float* Us = Qs + nf * HD;
+  const float* Ws = Us + HD;
   for (int i = wave; i < nf; i += 4) {
-    float* row = sc + i * nkmax;
-    float mx = -INFINITY;
-    for (int j = lane; j < nk; j += 64) mx = fmaxf(mx, row[j]);
-    mx = wave_max(mx);
-    float sum = 0.0f;
-    for (int j = lane; j < nk; j += 64) {
-      const float e = __expf(row[j] - mx);
-      row[j] = e;
-      sum += e;
+    const int p = pos0 + i;
+    bool vis[JT];
+    int rel[JT];
+    const unsigned char* krow[JT];
+#pragma unroll
+    for (int t = 0; t < JT; ++t) {
+      vis[t] = qj[t] >= 0 && att_visible(a, p, qj[t]);
+      rel[t] = vis[t] ? p - qj[t] - a.rel_lo : 0;
+      krow[t] = Ks + min(lane + 64 * t, R - 1) * KS;
     }
-    const float inv = 1.0f / wave_sum(sum);
-    for (int j = lane; j < nk; j += 64) row[j] *= inv;
-  }
-  __syncthreads();
-  // ---- o = P V: one (query, dim) pair per thread
-  for (int pr = tid; pr < nf * HD; pr += 256) {
-    const int i = pr / HD, d = pr - i * HD;
-    const float* row = sc + i * nkmax;
-    float acc = 0.0f;
-    for (int j = 0; j < nk; ++j) acc += row[j] * Vs[j * HD + d];
-    st<T>((T*)a.o + (long)(s * nf + i) * a.D + h * HD + d, acc);
+    float ac[JT], bd[JT];
+#pragma unroll
+    for (int t = 0; t < JT; ++t) { ac[t] = 0.0f; bd[t] = 0.0f; }
+    const f32x4_v* qi = (const f32x4_v*)(Qs + i * HD);
+#pragma unroll 4
+    for (int c = 0; c < FC; ++c) {
+      const f32x4_v q4 = qi[c];
+      const f32x4_v qu = q4 + ((const f32x4_v*)Us)[c], qv = q4 + ((const f32x4_v*)Ws)[c];
+#pragma unroll
+      for (int t = 0; t < JT; ++t) {
+        const f32x4_v k4 = lds4<T>(krow[t], c);
+        const f32x4_v p4 = ((const f32x4_v*)(Ps + rel[t] * FS))[c];
+        ac[t] += qu.x * k4.x + qu.y * k4.y + qu.z * k4.z + qu.w * k4.w;
+        bd[t] += qv.x * p4.x + qv.y * p4.y + qv.z * p4.z + qv.w * p4.w;
+      }
+    }
+    float sc[JT], mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < JT; ++t) {
+      sc[t] = vis[t] ? (ac[t] + bd[t]) * a.scale : -INFINITY;
+      mx = fmaxf(mx, sc[t]);
+    }
+    mx = wave_top(mx);  // finite: a query always sees its own position
+    float pr[JT], sum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < JT; ++t) {
+      pr[t] = vis[t] ? __expf(sc[t] - mx) : 0.0f;
+      sum += pr[t];
+    }
+    const float inv = 1.0f / wave_total(sum);
+    // o_i = sum_j p_ij v_j: the weights go to this wave's LDS strip; slots holding no key get a
+    // zero V row first (their weight is 0 but their contents are arbitrary, and 0 * NaN is NaN;
+    // every wave zeroes the same rows before reading them, so no wave depends on another)
+#pragma unroll
+    for (int t = 0; t < JT; ++t) {
+      const int j = lane + 64 * t;
+      Pw[j] = pr[t];
+      if (j < R && qj[t] < 0) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) *(u32x4_v*)(Vs + j * KS + c * 16) = u32x4_v{0u, 0u, 0u, 0u};
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    // lanes as (4-dim chunk c4, key phase ph): lane sums slots ph, ph + NPH, ... of its chunk
+    constexpr int NCH = HD / 4, NPH = 64 / NCH;
+    const int c4 = lane % NCH, ph = lane / NCH;
+    f32x4_v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < JT * 64 / NPH; ++m) {
+      const int j = ph + NPH * m;
+      const float pj = Pw[j];  // 0 for slots past R
+      acc += pj * lds4<T>(Vs + min(j, R - 1) * KS, c4);
+    }
+    // sum over the phases (lane bits log2(NCH) .. 5)
+#pragma unroll
+    for (int b = NCH; b < 64; b <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float v = acc[e];
+        if (b == 32) v = pair_sum32(v, v);
+        else if (b == 16) v = pair_sum16(v, v);
+        else v += __shfl_xor(v, b, 64);
+        acc[e] = v;
+      }
+    }
+    if (lane < NCH) {
+      T* dst = (T*)a.o + (long)(s * nf + i) * a.D + h * HD + 4 * lane;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st<T>(dst + e, acc[e] * inv);
+    }
+    __builtin_amdgcn_wave_barrier();  // the strip is rewritten by this wave's next query row
   }
 }
 
 void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd) {
   AttnArgs args = a;
-  const size_t shm = attention_shmem(a.cv.nf, a.Lc + a.cv.nf, a.nrel, hd);
+  const size_t shm = attention_shmem(a.cv.nf, a.R, a.nrel, hd, dtype == DT_F32 ? 4 : 2);
   const void* fn = nullptr;
-#define ATT_PICK(HDV) \
-  fn = dtype == DT_F32 ? (const void*)&attn_kernel<float, HDV> : (const void*)&attn_kernel<bf16_t, HDV>;
+  const bool wide = a.R > 128;  // ring slots per lane: 2 up to R = 128, else 4 (R <= 256)
+#define ATT_PICK(HDV)                                                                                     \
+  fn = dtype == DT_F32 ? (wide ? (const void*)&attn_kernel<float, HDV, 4> : (const void*)&attn_kernel<float, HDV, 2>) \
+                       : (wide ? (const void*)&attn_kernel<bf16_t, HDV, 4> : (const void*)&attn_kernel<bf16_t, HDV, 2>);
   if (hd == 16) { ATT_PICK(16) } else if (hd == 32) { ATT_PICK(32) } else { ATT_PICK(64) }
 #undef ATT_PICK
   L.tag_name = "attention";  // the caller tags bytes and flops (it knows each stream's fill)
@@ -1292,8 +1336,10 @@ void kernels_init() {
   std::vector<const void*> fns = {
       (const void*)&gemm_mfma_kernel<128, 128, 2, 2>, (const void*)&gemm_mfma_kernel<128, 64, 4, 1>,
       (const void*)&gemm_mfma_kernel<64, 128, 2, 2>, (const void*)&gemm_mfma_kernel<64, 64, 2, 2>,
-      (const void*)&attn_kernel<float, 16>, (const void*)&attn_kernel<float, 32>, (const void*)&attn_kernel<float, 64>,
-      (const void*)&attn_kernel<bf16_t, 16>, (const void*)&attn_kernel<bf16_t, 32>, (const void*)&attn_kernel<bf16_t, 64>,
+      (const void*)&attn_kernel<float, 16, 2>, (const void*)&attn_kernel<float, 32, 2>, (const void*)&attn_kernel<float, 64, 2>,
+      (const void*)&attn_kernel<bf16_t, 16, 2>, (const void*)&attn_kernel<bf16_t, 32, 2>, (const void*)&attn_kernel<bf16_t, 64, 2>,
+      (const void*)&attn_kernel<float, 16, 4>, (const void*)&attn_kernel<float, 32, 4>, (const void*)&attn_kernel<float, 64, 4>,
+      (const void*)&attn_kernel<bf16_t, 16, 4>, (const void*)&attn_kernel<bf16_t, 32, 4>, (const void*)&attn_kernel<bf16_t, 64, 4>,
   };
   for (int kch : {0, 1, 2, 3, 4, 6, 8})
     for (bool glu : {false, true}) {

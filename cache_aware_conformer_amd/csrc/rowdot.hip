@@ -69,37 +69,6 @@ __device__ __forceinline__ void unpack_w(const u32x4& r, float* f) {
   }
 }
 
-__device__ __forceinline__ float lane_value(float v, int src) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
-}
-
-// Cross-lane exchanges without LDS: the gfx950 lane-half swaps, and DPP within rows of 16.
-// pair_sum32(a, b): lanes 0..31 get a[L] + a[L + 32], lanes 32..63 get b[L - 32] + b[L]
-// (pair_sum16 likewise across the two 16-lane halves of each 32).
-__device__ __forceinline__ float pair_sum32(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float pair_sum16(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// value of lane L ^ 32 / L ^ 16
-__device__ __forceinline__ float xor32(float v, int lane) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((lane & 32) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float xor16(float v, int lane) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((lane & 16) ? r[0] : r[1]);
-}
-// value of lane L ^ 15 (row mirror), L ^ 7 (half-row mirror), L ^ 2, L ^ 1
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int DPP_MIRROR16 = 0x140, DPP_MIRROR8 = 0x141, DPP_XOR2 = 0x4E, DPP_XOR1 = 0xB1;
-
 // 64-lane totals of NV per-lane values; afterwards every lane holds the total of value
 // v(lane) = sum_j ((lane >> (5 - j)) & 1) << j. Halving steps pair lanes on bit 5, 4, 3 (a lane
 // keeps one of each pair of values and adds its partner's copy of it), then plain sums over the

@@ -269,7 +269,8 @@ def test_export_import_resume(cfg):
 
 def test_poisoned_cache_slots_never_reach_outputs():
     """With NaN in every unwritten cache slot, outputs are finite and identical to the zero
-    reset: no kernel reads a slot that does not hold a valid row."""
+    reset: nothing read from a slot that does not hold a valid row reaches an output (attention
+    stages whole rings and must discard such slots exactly, never as 0 * NaN)."""
     from cache_aware_conformer_amd import CAC_FLAG_POISON
     for cfg in (C1, C4.replace(n_layers=2, streams=3, staggered=False)):
         W = make_weights(cfg)
