@@ -895,14 +895,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   // indices clamped so that every load is unconditional; q, u, v with the first pass
   for (int base = 0; base < nkv || base < np; base += 256 * ATT_UM) {
     u32x4_v rk[ATT_UM], rv[ATT_UM], rp[ATT_UM], rq[2];
+    // position rows and q/u/v first: they do not wait for the stream id, K and V do
 #pragma unroll
-    for (int u = 0; u < ATT_UM; ++u) {
-      const int c = base + u * 256 + tid;
-      const int ck = min(c, nkv - 1), cp = min(c, np - 1);
-      rk[u] = kg[ck];
-      rv[u] = vg[ck];
-      rp[u] = pg[cp];
-    }
+    for (int u = 0; u < ATT_UM; ++u) rp[u] = pg[min(base + u * 256 + tid, np - 1)];
     if (base == 0) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -913,12 +908,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < ATT_UM; ++u) {
+      const int ck = min(base + u * 256 + tid, nkv - 1);
+      rk[u] = kg[ck];
+      rv[u] = vg[ck];
+    }
+    // stored in arrival order
+#pragma unroll
+    for (int u = 0; u < ATT_UM; ++u) {
       const int c = base + u * 256 + tid;
-      if (c < nkv) {
-        const int row = c / KC, col = c - row * KC;
-        *(u32x4_v*)(Ks + row * KS + col * 16) = rk[u];
-        *(u32x4_v*)(Vs + row * KS + col * 16) = rv[u];
-      }
       if (c < np) {
         const int row = c / FC, col = c - row * FC;
         *(u32x4_v*)(Ps + row * FS + col * 16) = rp[u];
@@ -929,6 +926,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       for (int u = 0; u < 2; ++u) {
         const int c = u * 256 + tid;
         if (c < nq) ((u32x4_v*)Qs)[c] = rq[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < ATT_UM; ++u) {
+      const int c = base + u * 256 + tid;
+      if (c < nkv) {
+        const int row = c / KC, col = c - row * KC;
+        *(u32x4_v*)(Ks + row * KS + col * 16) = rk[u];
+        *(u32x4_v*)(Vs + row * KS + col * 16) = rv[u];
       }
     }
   }

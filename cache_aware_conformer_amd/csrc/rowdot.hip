@@ -148,6 +148,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
   constexpr int NV = UPW * RD_ROWS * COLS;
   constexpr int LG = NV == 2 ? 1 : NV == 4 ? 2 : 3;
   static_assert(NV == (1 << LG), "two, four or eight sums per lane");
+  static_assert(!GLU || UPW == 1, "the depthwise epilogue puts one tap on each lane of a 16-lane row group");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)));
   const int units = GLU ? a.N / 2 : a.N;
@@ -157,14 +158,32 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
   const EpiArgs& e = a.epi;
   const TW* W = (const TW*)a.W;
 
+  // this lane's output after the fold: value v = ((u * RD_ROWS) + r) * COLS + c
+  int v = 0;
+#pragma unroll
+  for (int j = 0; j < LG; ++j) v |= ((lane >> (5 - j)) & 1) << j;
+  const int c_l = v % COLS, r_l = (v / COLS) % RD_ROWS, u_l = v / (COLS * RD_ROWS);
+  const int unit = u0 + u_l;
+  const bool writer = unit < units && r_l < M && c_l == 0 && (lane & ((64 >> LG) - 1)) == 0;
+  const int un = min(unit, units - 1), m = min(r_l, M - 1);
+
+  // stream, frame and absolute position of this lane's row: loaded first, so that the ring
+  // loads that depend on them wait for these two loads only, not for the weight stream
+  int sid = 0, frame = 0, pos = 0;
+  if constexpr (EK == EPI_QKV || GLU) {
+    const int s = m / e.cv.nf;
+    frame = m - s * e.cv.nf;
+    sid = e.cv.ids[s];
+    pos = e.cv.cpos[s] + frame;
+  }
   // ---------------------------------------------------------------- every global read
   u32x4 wr[UPW][COLS][KCH];
 #pragma unroll
   for (int u = 0; u < UPW; ++u)
 #pragma unroll
     for (int c = 0; c < COLS; ++c) {
-      const int un = min(u0 + u, units - 1);
-      const int col = GLU ? glu_a_col(un) + 32 * c : un;
+      const int uw = min(u0 + u, units - 1);
+      const int col = GLU ? glu_a_col(uw) + 32 * c : uw;
 #pragma unroll
       for (int k = 0; k < KCH; ++k) wr[u][c][k] = *(const u32x4*)(W + (long)col * K + (k * 64 + lane) * VEC);
     }
@@ -188,27 +207,10 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
     }
   }
 
-  // this lane's output after the fold: value v = ((u * RD_ROWS) + r) * COLS + c
-  int v = 0;
-#pragma unroll
-  for (int j = 0; j < LG; ++j) v |= ((lane >> (5 - j)) & 1) << j;
-  const int c_l = v % COLS, r_l = (v / COLS) % RD_ROWS, u_l = v / (COLS * RD_ROWS);
-  const int unit = u0 + u_l;
-  const bool writer = unit < units && r_l < M && c_l == 0 && (lane & ((64 >> LG) - 1)) == 0;
-  const int un = min(unit, units - 1), m = min(r_l, M - 1);
-
   float bias0 = 0.0f, bias1 = 0.0f;
   if (e.bias) {
     bias0 = e.bias[un];
     if constexpr (GLU) bias1 = e.bias[e.D + un];
-  }
-  // stream, frame and absolute position of this lane's row
-  int sid = 0, frame = 0, pos = 0;
-  if constexpr (EK == EPI_QKV || GLU) {
-    const int s = m / e.cv.nf;
-    frame = m - s * e.cv.nf;
-    sid = e.cv.ids[s];
-    pos = e.cv.cpos[s] + frame;
   }
   // residual base, and the residual rows for their LayerNorm statistics
   float base = 0.0f;
@@ -226,23 +228,21 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
           rx[r][j] = *(const f32x4*)(a.res_src + (long)min(r, M - 1) * e.ldo + (min(j, rch - 1) * 64 + lane) * 4);
     }
   }
-  // depthwise operands: taps, bias, and the older ring rows (offsets o >= 1 behind the row)
-  float dwt[RD_TAPS], dring[RD_TAPS], dwb = 0.0f;
+  // depthwise operands. After the fold a GLU wave (one unit) holds each (row, value/gate) total
+  // on a 16-lane group, so lane o of a row's group takes tap o: the tap weight and, for taps
+  // behind the rows of this call, the ring row o positions back (loaded after the stream info)
+  float dw_tap = 0.0f, dw_old = 0.0f, dwb = 0.0f;
+  const int tap = lane & 15;
   if constexpr (GLU) {
     const int T = a.dw_taps, Rc = e.Rc;
-    const int pr = pos % Rc;  // ring slot of this row; o rows behind it: pr - o, wrapped once
-    const TW* ring = (const TW*)e.cring + (long)sid * Rc * e.D + un;
+    const int oa = tap < T ? tap : T - 1;  // T - 1 < Rc: one wrap below
+    const float tw = a.dw_w[(long)(T - 1 - oa) * e.D + un];
+    dw_tap = tap < T ? tw : 0.0f;
+    int sl = pos % Rc - oa;
+    sl += sl < 0 ? Rc : 0;
+    const float rv = ld<TW>((const TW*)e.cring + ((long)sid * Rc + sl) * e.D + un);
+    dw_old = (tap >= 1 && tap < T && tap > frame && pos - tap >= 0) ? rv : 0.0f;
     dwb = a.dw_b[un];
-#pragma unroll
-    for (int o = 0; o < RD_TAPS; ++o) {
-      const float tw = a.dw_w[(long)(T - 1 - o > 0 ? T - 1 - o : 0) * e.D + un];
-      dwt[o] = o < T ? tw : 0.0f;
-      const int oa = o < T ? o : T - 1;  // taps beyond T are discarded; T - 1 < Rc keeps one wrap
-      int sl = pr - oa;
-      sl += sl < 0 ? Rc : 0;
-      const float rv = ld<TW>(ring + (long)sl * e.D);
-      dring[o] = (o >= 1 && o < T && o > frame && pos - o >= 0) ? rv : 0.0f;
-    }
   }
   int orow = m;
   if constexpr (EK == EPI_F32) {
@@ -306,13 +306,15 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
     const float gate = xor32(val, lane);
     const float g = round_to<TW>((val + bias0) * sigmoid_f(gate + bias1));
     const float prev = xor16(g, lane);
+    const float xin = tap == 0 ? g : (tap == 1 && frame >= 1 ? prev : dw_old);
+    float conv = dw_tap * xin;  // this lane's tap; summed over the 16 lanes of the row's group
+    conv += dpp<DPP_MIRROR16>(conv);
+    conv += dpp<DPP_MIRROR8>(conv);
+    conv += dpp<DPP_XOR2>(conv);
+    conv += dpp<DPP_XOR1>(conv);
     if (writer) {
-      st<TW>((TW*)e.cring + ((long)sid * e.Rc + pos % e.Rc) * e.D + unit, g);  // slot pr
-      float acc = dwb + dwt[0] * g;
-      acc += dwt[1] * (frame >= 1 ? prev : dring[1]);
-#pragma unroll
-      for (int o = 2; o < RD_TAPS; ++o) acc += dwt[o] * dring[o];
-      st<TW>((TW*)e.out + (long)m * e.ldo + unit, silu_f(acc));
+      st<TW>((TW*)e.cring + ((long)sid * e.Rc + pos % e.Rc) * e.D + unit, g);
+      st<TW>((TW*)e.out + (long)m * e.ldo + unit, silu_f(dwb + conv));
     }
   } else if (writer) {
     const float y = val + bias0;
@@ -352,7 +354,7 @@ const void* pick_kch(int kch) {
 
 template <typename TW, typename TA, int AM, int EK>
 const void* pick_upw(int upw, int kch) {
-  if constexpr (AM == AM_PLAIN) return upw == 1 ? pick_kch<TW, TA, AM, EK, 1>(kch) : nullptr;
+  if constexpr (AM == AM_PLAIN || EK == EPI_GLU_DW) return upw == 1 ? pick_kch<TW, TA, AM, EK, 1>(kch) : nullptr;
   else return upw == 2 ? pick_kch<TW, TA, AM, EK, 2>(kch) : pick_kch<TW, TA, AM, EK, 1>(kch);
 }
 
@@ -403,7 +405,8 @@ Plan plan(const GemmArgs& a, int dtype) {
   const int units = ek == EPI_GLU_DW ? a.N / 2 : a.N;
   // two units per wave only where that still leaves a wave per SIMD; 4-wave blocks only where
   // they still cover every CU
-  const int upw = (am != AM_PLAIN && units >= 2048) ? 2 : 1;
+  // (the GLU + depthwise epilogue needs one unit per wave: 16-lane groups, a lane per tap)
+  const int upw = (am != AM_PLAIN && units >= 2048 && ek != EPI_GLU_DW) ? 2 : 1;
   const int waves = (units + upw - 1) / upw;
   p.wpb = waves >= 1024 ? 4 : 1;
   if (dtype == DT_F32) p.fn = pick_mode<float, float>(am, ek, upw, kch);
