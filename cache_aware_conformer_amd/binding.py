@@ -52,6 +52,8 @@ SIGNATURES = {
     "cac_profile": (_i32, [_vp, _i32]),
     "cac_profile_read": (_i32, [_vp, _i32, C.c_char_p, _i32, C.POINTER(C.c_int64), C.POINTER(C.c_double),
                                 C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+    "cac_profile_replay": (_i32, [_vp, C.c_char_p, _i32, C.POINTER(C.c_double), C.POINTER(C.c_int32),
+                                  C.POINTER(C.c_double), C.POINTER(C.c_double)]),
 }
 
 _lib = None
@@ -308,6 +310,15 @@ class StreamingEncoder:
             nm = names.raw[64 * i:64 * (i + 1)].split(b"\0", 1)[0].decode()
             out[nm] = (int(launches[i]), float(ms[i]), float(by[i]), float(fl[i]))
         return out
+
+    def profile_replay(self, prefix: str, reps: int = 20) -> dict:
+        """Back-to-back duration of the kernel family `prefix` from the last replayed push graph
+        (leaves the streams of that push in an unspecified state)."""
+        us, nb, by, fl = C.c_double(), C.c_int32(), C.c_double(), C.c_double()
+        self._check(self.lib.cac_profile_replay(self.ctx, prefix.encode(), int(reps), C.byref(us), C.byref(nb),
+                                                C.byref(by), C.byref(fl)))
+        return {"us_per_launch": us.value, "launches": nb.value, "bytes_per_launch": by.value,
+                "flops_per_launch": fl.value}
 
     def close(self):
         if getattr(self, "ctx", None):

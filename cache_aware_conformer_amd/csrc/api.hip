@@ -221,6 +221,7 @@ struct cac_ctx {
   };
   bool use_graph = true;
   std::map<uint64_t, Graph> graphs;
+  Graph* last_graph = nullptr;  // graph of the most recent replayed push
   ~cac_ctx() {
     for (auto& kv : graphs) {
       if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
@@ -706,6 +707,7 @@ hipError_t push_graph(cac_ctx* c, int n, const int32_t* ids, int n_frames, const
     it = c->graphs.emplace(key, std::move(gr)).first;
   }
   cac_ctx::Graph& gr = it->second;
+  c->last_graph = &gr;
   if (gr.in != d_input || gr.out != d_out) {
     for (size_t i = 0; i < gr.nodes.size(); ++i) {
       if (gr.in_offs[i].empty() && gr.out_offs[i].empty()) continue;
@@ -973,6 +975,58 @@ int32_t cac_profile_read(cac_ctx* c, int32_t max_entries, char* names, int32_t n
     if (flops) flops[i] = c->prof.flops[i];
   }
   return n;
+}
+
+int32_t cac_profile_replay(cac_ctx* c, const char* prefix, int32_t reps, double* us_per_launch, int32_t* launches,
+                           double* bytes, double* flops) {
+  if (!c) return CAC_EINVAL;
+  if (!prefix || reps < 1) return c->fail(CAC_EINVAL, "profile_replay: prefix and reps >= 1 required");
+  if (!c->last_graph) return c->fail(CAC_EINVAL, "profile_replay: no push graph has been replayed yet");
+  if (c->dry) return c->fail(CAC_ENODEV, "dry-run context: no device work");
+  const size_t pl = strlen(prefix);
+  std::vector<const NodeRec*> sel;
+  for (const NodeRec& r : c->last_graph->nodes)
+    if (r.name.compare(0, pl, prefix) == 0) sel.push_back(&r);
+  if (sel.empty()) return c->fail(CAC_EINVAL, std::string("profile_replay: no launch named ") + prefix + "*");
+  hipGraph_t g = nullptr;
+  hipGraphExec_t ge = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipGraphCreate(&g, 0);
+  hipGraphNode_t last = nullptr;
+  double sb = 0.0, sf = 0.0;
+  for (const NodeRec* r : sel) {
+    if (e != hipSuccess) break;
+    hipKernelNodeParams p = r->p;
+    std::vector<char> args = r->args;
+    void* kp[1] = {args.data()};
+    p.kernelParams = kp;
+    hipGraphNode_t n;
+    e = hipGraphAddKernelNode(&n, g, last ? &last : nullptr, last ? 1 : 0, &p);
+    last = n;
+    sb += r->bytes;
+    sf += r->flops;
+  }
+  if (e == hipSuccess) e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+  if (e == hipSuccess) e = hipGraphLaunch(ge, c->stream);  // warm
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) e = hipEventRecord(e0, c->stream);
+  for (int i = 0; i < reps && e == hipSuccess; ++i) e = hipGraphLaunch(ge, c->stream);
+  if (e == hipSuccess) e = hipEventRecord(e1, c->stream);
+  if (e == hipSuccess) e = hipEventSynchronize(e1);
+  float ms = 0.0f;
+  if (e == hipSuccess) e = hipEventElapsedTime(&ms, e0, e1);
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (ge) (void)hipGraphExecDestroy(ge);
+  if (g) (void)hipGraphDestroy(g);
+  if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("profile_replay: ") + hipGetErrorString(e));
+  const double n = (double)sel.size();
+  if (us_per_launch) *us_per_launch = (double)ms * 1e3 / ((double)reps * n);
+  if (launches) *launches = (int32_t)sel.size();
+  if (bytes) *bytes = sb / n;
+  if (flops) *flops = sf / n;
+  return CAC_OK;
 }
 
 int32_t cac_destroy(cac_ctx* c) {

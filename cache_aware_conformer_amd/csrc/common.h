@@ -310,6 +310,8 @@ struct NodeRec {
   hipGraphNode_t node;
   hipKernelNodeParams p;
   std::vector<char> args;
+  std::string name;     // kernel tag ("family/role")
+  double bytes, flops;  // algorithmic bytes and flops of the launch
 };
 
 struct Launcher {

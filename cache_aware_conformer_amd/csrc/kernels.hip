@@ -99,6 +99,9 @@ void Launcher::launch_raw(const void* fn, dim3 grid, dim3 block, size_t shmem, v
       r.p = p;
       r.p.kernelParams = nullptr;
       r.args.assign((const char*)args, (const char*)args + args_size);
+      r.name = tag_name;
+      r.bytes = tag_bytes;
+      r.flops = tag_flops;
       rec->push_back(std::move(r));
     }
   }

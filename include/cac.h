@@ -170,8 +170,11 @@ int32_t cac_set_stream(cac_ctx* ctx, void* hip_stream);
 /* Synchronise the context's stream and report any asynchronous device error (CAC_EHIP). */
 int32_t cac_synchronize(cac_ctx* ctx);
 
-/* Per-kernel timing of later pushes and flushes (measurement aid; adds two HIP events per
- * launch on the context's stream). cac_profile(ctx, 1) clears and starts, 0 stops.
+/* Per-kernel timing of later pushes and flushes (measurement aid). While on, pushes launch
+ * directly (no graph replay) and every kernel is launched with a start and a stop HIP event
+ * bound to its own dispatch on the context's stream (hipExtLaunchKernel), so each time is
+ * that kernel's execution plus the event markers, without host submission gaps.
+ * cac_profile(ctx, 1) clears and starts, 0 stops.
  * cac_profile_read synchronises the recorded events and fills, per kernel name (up to
  * max_entries; names is max_entries * name_len chars): launches, total milliseconds between
  * each launch's events, and the algorithmic bytes and flops the library attributes to those
@@ -181,6 +184,19 @@ int32_t cac_synchronize(cac_ctx* ctx);
 int32_t cac_profile(cac_ctx* ctx, int32_t enable);
 int32_t cac_profile_read(cac_ctx* ctx, int32_t max_entries, char* names, int32_t name_len, int64_t* launches,
                          double* total_ms, double* bytes, double* flops);
+
+/* Back-to-back duration of one kernel family (measurement aid). Takes the kernel launches of
+ * the most recently replayed push graph whose kernel names start with `prefix` (for example
+ * "gemm_tworow_f32"), chains just those launches, in their order and with their arguments,
+ * into a graph, replays it `reps` times on the context's stream between two HIP events, and
+ * writes the mean time per launch in microseconds to *us_per_launch and the number of
+ * launches per replay to *launches, plus their mean algorithmic bytes and flops per launch to
+ * *bytes / *flops (any of the four pointers may be NULL). The kernels run on whatever the
+ * workspace holds, so the state of the streams of that push is unspecified afterwards: reset
+ * or re-import them before pushing them again. Returns CAC_OK, CAC_EINVAL (no recorded push
+ * graph, no launch with that prefix, reps < 1) or CAC_EHIP. */
+int32_t cac_profile_replay(cac_ctx* ctx, const char* prefix, int32_t reps, double* us_per_launch, int32_t* launches,
+                           double* bytes, double* flops);
 
 /* Free the host context (the workspace stays the caller's). Accepts NULL. */
 int32_t cac_destroy(cac_ctx* ctx);

@@ -169,3 +169,12 @@ def test_import_validation():
     assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), ip([8]), C.c_void_p(16)) == CAC_ENODEV
     enc2 = dry(C1)
     assert lib.cac_import_state(enc2.ctx, 1, ip(ids), ip([3]), None, C.c_void_p(16)) == CAC_ESTATE
+
+
+def test_profile_replay_needs_a_replayed_push_graph():
+    enc = dry(C1)
+    us, n = C.c_double(), C.c_int32()
+    assert enc.lib.cac_profile_replay(enc.ctx, b"gemm", 5, C.byref(us), C.byref(n), None, None) == CAC_EINVAL
+    assert b"no push graph" in enc.lib.cac_last_error(enc.ctx)
+    assert enc.lib.cac_profile_replay(enc.ctx, None, 5, None, None, None, None) == CAC_EINVAL
+    assert enc.lib.cac_profile_replay(enc.ctx, b"gemm", 0, None, None, None, None) == CAC_EINVAL

@@ -336,3 +336,21 @@ def test_profiled_launches_time_every_kernel_and_match_graph_replay():
     assert sum(v[0] for v in prof.values()) == 4 * (9 * cfg.n_layers + 3)
     for n, (launches, ms, _, _) in prof.items():
         assert launches % 4 == 0 and ms > 0.0, n
+
+
+def test_profile_replay_times_one_kernel_family():
+    """The family replay chains exactly the family's launches of the last replayed push."""
+    from cache_aware_conformer_amd.binding import CacError
+    cfg = C2.replace(n_layers=3)
+    enc = _enc(cfg, make_weights(cfg), max_streams=1)
+    xs = make_inputs(cfg, 0, 2)
+    for c in range(2):
+        enc.push_chunk([0], to_dev(xs[c][None], cfg))
+    torch.cuda.synchronize()
+    rep = enc.profile_replay("gemm_tworow_f32", reps=5)
+    assert rep["launches"] == 8 * cfg.n_layers + 1   # 8 dense products per layer + the joint
+    assert rep["us_per_launch"] > 0.0 and rep["bytes_per_launch"] > 0.0
+    att = enc.profile_replay("attention", reps=5)
+    assert att["launches"] == cfg.n_layers
+    with pytest.raises(CacError):
+        enc.profile_replay("no_such_kernel", reps=5)
