@@ -955,6 +955,74 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
   const float* Us = Qs + nf * HD;
   const float* Ws = Us + HD;
+  constexpr int NCH = HD / 4, NPH = 64 / NCH;  // PV lanes as (4-dim chunk, key phase)
+  const int c4 = lane % NCH, ph = lane / NCH;
+
+  if (JT == 2 && nf <= 2) {
+    // ---- two query rows or fewer: all 4 waves busy as (query row i, half kh of the ring
+    // slots); each half keeps its own max, sum and unnormalised PV, combined after a barrier
+    const int i = wave & 1, kh = wave >> 1;
+    const int ii = i < nf ? i : 0;  // a wave without a row computes row 0 and stores nothing
+    const int p = pos0 + ii, j = lane + 64 * kh, q = qj[kh];
+    const bool vis = q >= 0 && att_visible(a, p, q);
+    const int rel = vis ? p - q - a.rel_lo : 0;
+    const unsigned char* krow = Ks + min(j, R - 1) * KS;
+    const unsigned char* prow = Ps + rel * FS;
+    const f32x4_v* qi = (const f32x4_v*)(Qs + ii * HD);
+    float ac = 0.0f, bd = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < FC; ++c) {
+      const f32x4_v q4 = qi[c];
+      const f32x4_v qu = q4 + ((const f32x4_v*)Us)[c], qv = q4 + ((const f32x4_v*)Ws)[c];
+      const f32x4_v k4 = lds4<T>(krow, c), p4 = ((const f32x4_v*)prow)[c];
+      ac += qu.x * k4.x + qu.y * k4.y + qu.z * k4.z + qu.w * k4.w;
+      bd += qv.x * p4.x + qv.y * p4.y + qv.z * p4.z + qv.w * p4.w;
+    }
+    const float sc = vis ? (ac + bd) * a.scale : -INFINITY;
+    const float mw = wave_top(sc);  // -inf when this half holds no visible key
+    const float ew = vis ? __expf(sc - mw) : 0.0f;
+    const float lw = wave_total(ew);
+    f32x4_v acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (64 * kh < R) {
+      // weights to the strip; slots of this half holding no key get a zero V row first
+      Pw[lane] = ew;
+      if (j < R && q < 0) {
+#pragma unroll
+        for (int c = 0; c < KC; ++c) *(u32x4_v*)(Vs + j * KS + c * 16) = u32x4_v{0u, 0u, 0u, 0u};
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int m = 0; m < 64 / NPH; ++m) {
+        const int jj = ph + NPH * m;  // rows past R - 1 clamp to R - 1, inside this half
+        acc += Pw[jj] * lds4<T>(Vs + min(64 * kh + jj, R - 1) * KS, c4);
+      }
+#pragma unroll
+      for (int b = NCH; b < 64; b <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = acc[e];
+          if (b == 32) v = pair_sum32(v, v);
+          else if (b == 16) v = pair_sum16(v, v);
+          else v += __shfl_xor(v, b, 64);
+          acc[e] = v;
+        }
+      }
+    }
+    float* cmb = Pw + 64;  // [max, sum, o[HD]] of this wave's half
+    if (lane < NCH) *(f32x4_v*)(cmb + 4 + 4 * lane) = acc;
+    if (lane == 0) { cmb[0] = mw; cmb[1] = lw; }
+    __syncthreads();
+    if (kh == 0 && i < nf) {
+      const float* c1 = cmb + 2 * 256;  // the same row's other half (wave + 2)
+      const float m0 = cmb[0], m1 = c1[0], mx = fmaxf(m0, m1);  // finite: a row sees itself
+      const float f0 = m0 == -INFINITY ? 0.0f : __expf(m0 - mx), f1 = m1 == -INFINITY ? 0.0f : __expf(m1 - mx);
+      const float inv = 1.0f / (cmb[1] * f0 + c1[1] * f1);
+      if (lane < HD)
+        st<T>((T*)a.o + (long)(s * nf + i) * a.D + h * HD + lane, (cmb[4 + lane] * f0 + c1[4 + lane] * f1) * inv);
+    }
+    return;
+  }
+
   for (int i = wave; i < nf; i += 4) {
     const int p = pos0 + i;
     bool vis[JT];
@@ -1010,8 +1078,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     }
     __builtin_amdgcn_wave_barrier();
     // lanes as (4-dim chunk c4, key phase ph): lane sums slots ph, ph + NPH, ... of its chunk
-    constexpr int NCH = HD / 4, NPH = 64 / NCH;
-    const int c4 = lane % NCH, ph = lane / NCH;
     f32x4_v acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int m = 0; m < JT * 64 / NPH; ++m) {

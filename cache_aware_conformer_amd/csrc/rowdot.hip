@@ -166,12 +166,14 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
   const int unit = u0 + u_l;
   const bool writer = unit < units && r_l < M && c_l == 0 && (lane & ((64 >> LG) - 1)) == 0;
   const int un = min(unit, units - 1), m = min(r_l, M - 1);
+  // the two rows' operand offsets (row 0 is at offset 0): no runtime division
+  const long a_off1 = a.amap.group == 1 ? (long)a.amap.group_stride : (long)a.amap.row_stride;
 
   // stream, frame and absolute position of this lane's row: loaded first, so that the ring
   // loads that depend on them wait for these two loads only, not for the weight stream
   int sid = 0, frame = 0, pos = 0;
   if constexpr (EK == EPI_QKV || GLU) {
-    const int s = m / e.cv.nf;
+    const int s = e.cv.nf == 1 ? m : 0;  // m / nf for m < 2
     frame = m - s * e.cv.nf;
     sid = e.cv.ids[s];
     pos = e.cv.cpos[s] + frame;
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
   float x[RD_ROWS][PER];
 #pragma unroll
   for (int r = 0; r < RD_ROWS; ++r) {
-    const TA* ar = (const TA*)a.A + a.amap.off(min(r, M - 1));
+    const TA* ar = (const TA*)a.A + (min(r, M - 1) ? a_off1 : 0);
 #pragma unroll
     for (int k = 0; k < KCH; ++k) load_vals<TA, VEC>(ar + (k * 64 + lane) * VEC, &x[r][k * VEC]);
   }
@@ -246,7 +248,10 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
   }
   int orow = m;
   if constexpr (EK == EPI_F32) {
-    if (e.omap) orow = e.omap[m / e.ogroup] * e.ostride + m % e.ogroup;
+    if (e.omap) {  // m / ogroup and m % ogroup for m < 2
+      const int q = e.ogroup == 1 ? m : 0;
+      orow = e.omap[q] * e.ostride + (m - q * e.ogroup);
+    }
   }
 
   // ---------------------------------------------------------------- operand transforms
@@ -327,13 +332,14 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
     } else if constexpr (EK == EPI_F32) {
       ((float*)e.out)[(long)orow * e.ldo + unit] = y;
     } else if constexpr (EK == EPI_QKV) {
-      const int which = unit / e.D, c = unit - which * e.D;
+      const int which = (unit >= e.D) + (unit >= 2 * e.D), c = unit - which * e.D;
       if (which == 0) {
         e.qbuf[(long)m * e.D + c] = y;
       } else {
         const int slot = pos % e.R;
+        const int lg = 31 - __clz(e.hd);  // head sizes are powers of two
         TW* ring = (TW*)(which == 1 ? e.kring : e.vring);
-        st<TW>(ring + (((long)sid * e.H + c / e.hd) * e.R + slot) * e.hd + c % e.hd, y);
+        st<TW>(ring + (((long)sid * e.H + (c >> lg)) * e.R + slot) * e.hd + (c & (e.hd - 1)), y);
       }
     }
   }
