@@ -1038,9 +1038,9 @@ int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t
                       const float* d_bias, float* d_C, void* hip_stream) {
   if (dtype != CAC_F32 && dtype != CAC_BF16) return CAC_EINVAL;
   if (M < 1 || N < 1 || K < 1 || !d_A || !d_W || !d_C) return CAC_EINVAL;
-  if (path < 0 || path > 2 || (path == 2 && dtype != CAC_BF16)) return CAC_EINVAL;
-  if (path == 2 && K % 64) return CAC_EINVAL;  // MFMA tiles step K by 64
-  if ((size_t)8 * K * 4 > 160 * 1024 && path != 2) return CAC_EINVAL;
+  if (path < 0 || path > 6 || (path >= 2 && dtype != CAC_BF16)) return CAC_EINVAL;
+  if (path >= 2 && K % 64) return CAC_EINVAL;  // MFMA tiles step K by 64
+  if ((size_t)8 * K * 4 > 160 * 1024 && path < 2) return CAC_EINVAL;
   kernels_init();
   Launcher L;
   L.stream = (hipStream_t)hip_stream;

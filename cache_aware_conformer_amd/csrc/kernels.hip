@@ -504,18 +504,85 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
 typedef __attribute__((ext_vector_type(16))) float f32x16_v;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_v;  // 16-byte staging register
+typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 
 // Block tile BM x BN, k-step 64, 4 waves as WM x WN, each wave (BM/WM) x (BN/WN) made of
-// 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, 4 per k-step). A and W k-tiles live in two
-// LDS buffers (row stride 72 bf16: 16-byte aligned, conflict-free fragment reads); the next
-// k-tile is fetched into registers while the current one is multiplied and stored into the
-// other buffer afterwards, so each k-step has one barrier and its loads overlap a k-step of MFMA.
-template <int BM, int BN, int WM, int WN>
+// 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, 4 per k-step). Global loads run MFMA_ST
+// k-tiles ahead in rotating register sets (the k-loop is unrolled by MFMA_ST so each set is a
+// compile-time register block), so a k-step waits for loads issued MFMA_ST k-steps earlier
+// instead of one: at these tile sizes one k-step of MFMA is far shorter than a memory round
+// trip. Each k-step stores its register set into one of two LDS buffers (row stride 72 bf16:
+// 16-byte aligned, conflict-free fragment reads), passes the block's one barrier and
+// multiplies out of it. The epilogue kind is a template parameter; the accumulator tile goes
+// through LDS and every thread finishes 8 consecutive columns of a row with 16-byte accesses.
+constexpr int MFMA_ST = 4;
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16); }
+__device__ __forceinline__ void st_bf8(bf16_t* p, const float* y) {
+  *(u32x4_v*)p = u32x4_v{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]), pack_bf2(y[4], y[5]), pack_bf2(y[6], y[7])};
+}
+__device__ __forceinline__ void ld_f8(const float* p, float* v) {
+  const f32x4_v a = ((const f32x4_v*)p)[0], b = ((const f32x4_v*)p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void st_f8(float* p, const float* v) {
+  ((f32x4_v*)p)[0] = f32x4_v{v[0], v[1], v[2], v[3]};
+  ((f32x4_v*)p)[1] = f32x4_v{v[4], v[5], v[6], v[7]};
+}
+
+// Epilogue of 8 consecutive output columns col..col+7 of row `row` (v = accumulators).
+template <int EK>
+__device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, float* v) {
+  const EpiArgs& e = a.epi;
+  if (e.bias) {
+    float b[8];
+    ld_f8(e.bias + col, b);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] += b[q];
+  }
+  if constexpr (EK == EPI_STORE) {
+    st_bf8((bf16_t*)e.out + (long)row * e.ldo + col, v);
+  } else if constexpr (EK == EPI_SILU) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = silu_f(v[q]);
+    st_bf8((bf16_t*)e.out + (long)row * e.ldo + col, v);
+  } else if constexpr (EK == EPI_RELU_FE) {
+    const int s = row / e.fe_rows_per_stream, j = row - s * e.fe_rows_per_stream;
+    const bool before_start = e.cv.cpos[s] == 0 && j < e.fe_neg_rows;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = before_start ? 0.0f : fmaxf(v[q], 0.0f);
+    st_bf8((bf16_t*)e.out + (long)row * e.ldo + col, v);
+  } else if constexpr (EK == EPI_RESID) {
+    float* x = (float*)e.out + (long)row * e.ldo + col;
+    float r[8];
+    ld_f8(x, r);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) r[q] += e.alpha * v[q];
+    st_f8(x, r);
+  } else if constexpr (EK == EPI_F32) {
+    const long ro = e.omap ? (long)e.omap[row / e.ogroup] * e.ostride + row % e.ogroup : row;
+    st_f8((float*)e.out + ro * e.ldo + col, v);
+  } else if constexpr (EK == EPI_QKV) {
+    const int which = (col >= e.D) + (col >= 2 * e.D), c = col - which * e.D;
+    if (which == 0) {
+      st_f8(e.qbuf + (long)row * e.D + c, v);
+    } else {
+      const int s = row / e.cv.nf, i = row - s * e.cv.nf;
+      const int slot = (e.cv.cpos[s] + i) % e.R;
+      const int lg = 31 - __clz(e.hd);  // head sizes are powers of two; 8 columns stay in one head
+      bf16_t* ring = (bf16_t*)(which == 1 ? e.kring : e.vring);
+      st_bf8(ring + (((long)e.cv.ids[s] * e.H + (c >> lg)) * e.R + slot) * e.hd + (c & (e.hd - 1)), v);
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int EK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_mfma_kernel(GemmArgs a) {
-  constexpr int BK = 64, LDK = BK + 8;
+  constexpr int BK = 64, LDK = BK + 8, ST = MFMA_ST;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int A_PER_T = BM * (BK / 8) / 256, B_PER_T = BN * (BK / 8) / 256;
   static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small");
+  static_assert(ST % 2 == 0, "the LDS buffer of a k-step is its set index mod 2");
   extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
   // buffer b: A tile at lds + b * (BM + BN) * LDK, W tile right after it
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -540,18 +607,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     bptr[i] = W + (long)min(bn0 + row, N - 1) * K + kc;
     boff[i] = row * LDK + kc;
   }
-  u32x4_v ra[A_PER_T], rb[B_PER_T];
-#define MFMA_GLOAD(kt)                                                                     \
-  {                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) ra[i] = *(const u32x4_v*)(aptr[i] + (kt) * BK); \
-    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) rb[i] = *(const u32x4_v*)(bptr[i] + (kt) * BK); \
+  u32x4_v ra[ST][A_PER_T], rb[ST][B_PER_T];
+#define MFMA_GLOAD(s, kt)                                                                         \
+  {                                                                                               \
+    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) ra[s][i] = *(const u32x4_v*)(aptr[i] + (kt) * BK); \
+    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) rb[s][i] = *(const u32x4_v*)(bptr[i] + (kt) * BK); \
   }
-#define MFMA_SSTORE(buf)                                                                   \
-  {                                                                                        \
-    bf16_t* Ab_ = lds + (buf) * (BM + BN) * LDK;                                           \
-    bf16_t* Bb_ = Ab_ + BM * LDK;                                                          \
-    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) *(u32x4_v*)(Ab_ + aoff[i]) = ra[i];  \
-    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) *(u32x4_v*)(Bb_ + boff[i]) = rb[i];  \
+#define MFMA_SSTORE(buf, s)                                                                       \
+  {                                                                                               \
+    bf16_t* Ab_ = lds + (buf) * (BM + BN) * LDK;                                                  \
+    bf16_t* Bb_ = Ab_ + BM * LDK;                                                                 \
+    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) *(u32x4_v*)(Ab_ + aoff[i]) = ra[s][i];     \
+    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) *(u32x4_v*)(Bb_ + boff[i]) = rb[s][i];     \
   }
 
   f32x16_v acc[FM][FN];
@@ -563,46 +630,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   const int KT = K / BK;
-  MFMA_GLOAD(0);
-  MFMA_SSTORE(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    // unconditional prefetch (the last k-step reloads its own tile into the idle buffer) keeps
-    // ra/rb in registers
-    const int nxt = kt + 1 < KT ? kt + 1 : kt;
-    MFMA_GLOAD(nxt);
-    const bf16_t* Ab = lds + buf * (BM + BN) * LDK;
-    const bf16_t* Bb = Ab + BM * LDK;
+  // k-tiles 0..ST-1 in flight (indices past the end reload the last tile: every load stays
+  // unconditional, so the compiler counts them in order)
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8_v af[FM], bfv[FN];
+  for (int s = 0; s < ST; ++s) MFMA_GLOAD(s, min(s, KT - 1));
+  for (int kt0 = 0; kt0 < KT; kt0 += ST) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *(const bf16x8_v*)(Ab + (wm * TM + i * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
+    for (int s = 0; s < ST; ++s) {
+      const int kt = kt0 + s;
+      if (kt < KT) {
+        // the set holding k-tile kt goes to buffer s & 1 (read two k-steps ago, released by the
+        // barrier of the k-step in between), then reloads k-tile kt + ST
+        MFMA_SSTORE(s & 1, s);
+        __syncthreads();
+        MFMA_GLOAD(s, min(kt + ST, KT - 1));
+        const bf16_t* Ab = lds + (s & 1) * (BM + BN) * LDK;
+        const bf16_t* Bb = Ab + BM * LDK;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfv[j] = *(const bf16x8_v*)(Bb + (wn * TN + j * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
+        for (int kk = 0; kk < BK; kk += 16) {
+          bf16x8_v af[FM], bfv[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+          for (int i = 0; i < FM; ++i)
+            af[i] = *(const bf16x8_v*)(Ab + (wm * TM + i * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < FN; ++j)
+            bfv[j] = *(const bf16x8_v*)(Bb + (wn * TN + j * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+        }
+      }
     }
-    // schedule: the next k-tile's global loads first, then this k-step's MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x020, A_PER_T + B_PER_T, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * FM * FN, 0);
-    MFMA_SSTORE(buf ^ 1);
-    __syncthreads();
   }
 #undef MFMA_GLOAD
 #undef MFMA_SSTORE
+  __syncthreads();  // every wave is done reading the k-tile buffers
 
   // The accumulator tile goes to LDS (fragment element r of a lane is row 8*(r/4) +
   // 4*(lane/32) + r%4, column lane%32; all indices compile-time, so acc stays in registers),
-  // then the epilogue walks the tile row-major: coalesced stores, no register indexing.
+  // then each thread takes 8 consecutive columns of a row at a time.
   constexpr int CS = BN + 4;
-  float* ct = (float*)lds;  // the last k-step ended with a barrier: the staging buffers are free
+  float* ct = (float*)lds;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -611,20 +681,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       for (int r = 0; r < 16; ++r)
         ct[(wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * CS + wn * TN + j * 32 + (lane & 31)] = acc[i][j][r];
   __syncthreads();
-  if (a.epi.kind == EPI_GLU) {
-    // packed columns: each 64-column block holds 32 value columns then their 32 gates
-    for (int idx = tid; idx < BM * (BN / 2); idx += 256) {
-      const int rr = idx / (BN / 2), ch = idx % (BN / 2);
+  if constexpr (EK == EPI_GLU) {
+    // packed columns: each 64-column block holds 32 value columns then their 32 gates; a thread
+    // takes 8 channels (8 values, 8 gates) and writes them to the conv ring with one store
+    const EpiArgs& e = a.epi;
+    constexpr int G8 = BN / 16;  // 8-channel groups per tile row
+    for (int it = tid; it < BM * G8; it += 256) {
+      const int rr = it / G8, ch = (it - rr * G8) * 8;
       const int pc = (ch >> 5) * 64 + (ch & 31);
-      const int row = bm0 + rr;
-      if (row < M && bn0 + pc < N)
-        epi_glu<bf16_t>(a.epi, row, (bn0 >> 6) * 32 + ch, ct[rr * CS + pc], ct[rr * CS + pc + 32]);
+      const int row = bm0 + rr, c = bn0 / 2 + ch;
+      if (row >= M || bn0 + pc >= N) continue;
+      float va[8], vb[8], ba[8], bb[8];
+      ld_f8(ct + rr * CS + pc, va);
+      ld_f8(ct + rr * CS + pc + 32, vb);
+      ld_f8(e.bias + c, ba);
+      ld_f8(e.bias + e.D + c, bb);
+      float g[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) g[q] = (va[q] + ba[q]) * sigmoid_f(vb[q] + bb[q]);
+      const int s = row / e.cv.nf, i = row - s * e.cv.nf;
+      const int slot = (e.cv.cpos[s] + i) % e.Rc;
+      st_bf8((bf16_t*)e.cring + ((long)e.cv.ids[s] * e.Rc + slot) * e.D + c, g);
     }
   } else {
-    for (int idx = tid; idx < BM * BN; idx += 256) {
-      const int rr = idx / BN, cc = idx % BN;
+    constexpr int C8 = BN / 8;
+    for (int it = tid; it < BM * C8; it += 256) {
+      const int rr = it / C8, cc = (it - rr * C8) * 8;
       const int row = bm0 + rr, col = bn0 + cc;
-      if (row < M && col < N) epi_one<bf16_t>(a.epi, row, col, ct[rr * CS + cc]);
+      if (row >= M || col >= N) continue;
+      float v[8];
+      ld_f8(ct + rr * CS + cc, v);
+      mfma_epi8<EK>(a, row, col, v);
     }
   }
 }
@@ -749,33 +836,44 @@ static void gemv_dispatch(Launcher& L, const GemmArgs& a) {
   L.launch(fn, dim3((units + 4 * upw - 1) / (4 * upw), (a.M + MR - 1) / MR), dim3(256), shm, &args);
 }
 
-static void mfma_dispatch(Launcher& L, const GemmArgs& a) {
+template <int BM, int BN, int WM, int WN>
+static const void* mfma_pick_epi(int ek) {
+  switch (ek) {
+    case EPI_STORE: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_STORE>;
+    case EPI_SILU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_SILU>;
+    case EPI_RELU_FE: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RELU_FE>;
+    case EPI_RESID: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RESID>;
+    case EPI_F32: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_F32>;
+    case EPI_QKV: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_QKV>;
+    case EPI_GLU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_GLU>;
+    default: return nullptr;
+  }
+}
+
+// tile: 0 = chosen here; 1 = 128x128, 2 = 128x64, 3 = 64x128, 4 = 64x64 (test entry point)
+static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   const bool glu = a.epi.kind == EPI_GLU;
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   GemmArgs args = a;
+  L.tag("gemm_mfma_bf16", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K);
+  if (tile == 0) {
+    // largest tile that still yields >= 256 workgroups; GLU needs 64-column wave tiles
+    if (tiles(128, 128) >= 256) tile = 1;
+    else if (glu || tiles(64, 64) < 128) tile = (tiles(128, 64) >= tiles(64, 128) * 3 / 4 && a.M >= 128) ? 2 : 3;
+    else tile = 4;
+  }
   const void* fn;
   dim3 grid;
   size_t shm;
-  L.tag("gemm_mfma_bf16", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K);
-  // largest tile that still yields >= 256 workgroups; GLU needs 64-column wave tiles
-  if (tiles(128, 128) >= 256) {
-    fn = (const void*)&gemm_mfma_kernel<128, 128, 2, 2>;
-    grid = dim3((a.N + 127) / 128, (a.M + 127) / 128);
-    shm = mfma_lds<128, 128>();
-  } else if (glu || tiles(64, 64) < 128) {
-    if (tiles(128, 64) >= tiles(64, 128) * 3 / 4 && a.M >= 128) {
-      fn = (const void*)&gemm_mfma_kernel<128, 64, 4, 1>;
-      grid = dim3((a.N + 63) / 64, (a.M + 127) / 128);
-      shm = mfma_lds<128, 64>();
-    } else {
-      fn = (const void*)&gemm_mfma_kernel<64, 128, 2, 2>;
-      grid = dim3((a.N + 127) / 128, (a.M + 63) / 64);
-      shm = mfma_lds<64, 128>();
-    }
-  } else {
-    fn = (const void*)&gemm_mfma_kernel<64, 64, 2, 2>;
-    grid = dim3((a.N + 63) / 64, (a.M + 63) / 64);
-    shm = mfma_lds<64, 64>();
+  switch (tile) {
+    case 1: fn = mfma_pick_epi<128, 128, 2, 2>(a.epi.kind); grid = dim3((a.N + 127) / 128, (a.M + 127) / 128); shm = mfma_lds<128, 128>(); break;
+    case 2: fn = mfma_pick_epi<128, 64, 4, 1>(a.epi.kind); grid = dim3((a.N + 63) / 64, (a.M + 127) / 128); shm = mfma_lds<128, 64>(); break;
+    case 3: fn = mfma_pick_epi<64, 128, 2, 2>(a.epi.kind); grid = dim3((a.N + 127) / 128, (a.M + 63) / 64); shm = mfma_lds<64, 128>(); break;
+    default: fn = mfma_pick_epi<64, 64, 2, 2>(a.epi.kind); grid = dim3((a.N + 63) / 64, (a.M + 63) / 64); shm = mfma_lds<64, 64>(); break;
+  }
+  if (!fn) {
+    if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
+    return;
   }
   L.launch(fn, grid, dim3(256), shm, &args);
 }
@@ -824,7 +922,7 @@ void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path) {
     g.a_f32 = 0;
     g.ln_g = g.ln_b = nullptr;
   }
-  mfma_dispatch(L, g);
+  mfma_dispatch(L, g, path >= 3 ? path - 2 : 0);
 }
 
 void launch_ln(Launcher& L, const LnArgs& a, int dtype) {
@@ -858,7 +956,6 @@ __device__ __forceinline__ bool att_visible(const AttnArgs& a, int p, int q) {
   return q >= cs - a.Lc && q <= cs + a.chunk - 1;
 }
 
-typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 
 // four consecutive elements (index 4c..4c+3) of an LDS row of T as float
 template <typename T>
@@ -1409,8 +1506,7 @@ void kernels_init() {
   done = true;
   const int lds = 160 * 1024;
   std::vector<const void*> fns = {
-      (const void*)&gemm_mfma_kernel<128, 128, 2, 2>, (const void*)&gemm_mfma_kernel<128, 64, 4, 1>,
-      (const void*)&gemm_mfma_kernel<64, 128, 2, 2>, (const void*)&gemm_mfma_kernel<64, 64, 2, 2>,
+
       (const void*)&attn_kernel<float, 16, 2>, (const void*)&attn_kernel<float, 32, 2>, (const void*)&attn_kernel<float, 64, 2>,
       (const void*)&attn_kernel<bf16_t, 16, 2>, (const void*)&attn_kernel<bf16_t, 32, 2>, (const void*)&attn_kernel<bf16_t, 64, 2>,
       (const void*)&attn_kernel<float, 16, 4>, (const void*)&attn_kernel<float, 32, 4>, (const void*)&attn_kernel<float, 64, 4>,
@@ -1425,6 +1521,12 @@ void kernels_init() {
       fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 2>(kch, glu));
       fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 8>(kch, glu));
     }
+  for (int ek : {EPI_STORE, EPI_SILU, EPI_RELU_FE, EPI_RESID, EPI_F32, EPI_QKV, EPI_GLU}) {
+    fns.push_back(mfma_pick_epi<128, 128, 2, 2>(ek));
+    fns.push_back(mfma_pick_epi<128, 64, 4, 1>(ek));
+    fns.push_back(mfma_pick_epi<64, 128, 2, 2>(ek));
+    fns.push_back(mfma_pick_epi<64, 64, 2, 2>(ek));
+  }
   for (const void* f : fns)
     if (f) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }

@@ -207,8 +207,9 @@ const char* cac_last_error(const cac_ctx* ctx);
 
 /* Test-only: C[M][N] (float32) = A[M][K] W[N][K]^T + bias through the library's dense kernels
  * (dtype selects bf16 or float32 operands for A and W; bias may be NULL). path: 0 = the
- * library's own choice, 1 = the small-M kernel, 2 = the MFMA tile kernel (bf16 only).
- * Enqueued on hip_stream. */
+ * library's own choice, 1 = the small-M kernel, 2 = the MFMA tile kernel with its own tile
+ * choice, 3..6 = the MFMA tile kernel with 128x128, 128x64, 64x128 or 64x64 block tiles
+ * (MFMA paths: bf16 only, K a multiple of 64). Enqueued on hip_stream. */
 int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t K,
                       const void* d_A, const void* d_W, const float* d_bias, float* d_C,
                       void* hip_stream);

@@ -42,7 +42,8 @@ GEMM_SHAPES = [(2048, 512), (512, 2048), (1536, 512), (640, 512), (1024, 512), (
 
 @pytest.mark.parametrize("dtype,path,M", [("f32", 1, 1), ("f32", 1, 2), ("f32", 1, 5), ("f32", 1, 8), ("f32", 1, 19),
                                           ("bf16", 1, 2), ("bf16", 1, 7), ("bf16", 2, 64), ("bf16", 2, 100),
-                                          ("bf16", 2, 512), ("bf16", 2, 2048)])
+                                          ("bf16", 2, 512), ("bf16", 2, 2048), ("bf16", 3, 300), ("bf16", 4, 300),
+                                          ("bf16", 5, 300), ("bf16", 6, 300)])
 def test_gemm_kernels(dtype, path, M):
     from cache_aware_conformer_amd.binding import CAC_BF16, CAC_F32, test_gemm
     rng = np.random.default_rng(M * 7 + path)
