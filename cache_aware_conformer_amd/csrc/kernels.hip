@@ -723,8 +723,19 @@ constexpr size_t mfma_lds() {
 }
 
 // =============================================================================== LayerNorm
-// One wave per row; the row, gains and shifts are loaded together as 16-byte chunks (D a
-// multiple of 256, up to 4 chunks per lane), falling back to scalar loads otherwise.
+// One wave per row. D a multiple of 256 up to 1024: the row, gains and shifts are loaded
+// together as 16-byte chunks, the statistics come from one pass over the row shifted by its
+// first element (register-exchange reductions), and the output is written 4 elements at a
+// time. Other D: scalar two-pass fallback.
+template <typename TO>
+__device__ __forceinline__ void st4(TO* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(TO) == 4) {
+    *(f32x4_v*)p = f32x4_v{a, b, c, d};
+  } else {
+    *(uint2*)p = make_uint2(pack_bf2(a, b), pack_bf2(c, d));
+  }
+}
+
 template <typename TO>
 __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -733,44 +744,41 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
   TO* y = (TO*)a.y + (long)row * a.D;
   if (a.D % 256 == 0 && a.D <= 1024) {
     const int nv = a.D / 256;
-    float4 xv[4], gv[4], bv[4];
+    f32x4_v xv[4], gv[4], bv[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool ok = j < nv;
-      const int k = (j * 64 + lane) * 4;
-      xv[j] = ok ? *(const float4*)(x + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-      gv[j] = ok ? *(const float4*)(a.g + k) : make_float4(0.f, 0.f, 0.f, 0.f);
-      bv[j] = ok ? *(const float4*)(a.b + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int k = (min(j, nv - 1) * 64 + lane) * 4;  // clamped: every load unconditional
+      xv[j] = *(const f32x4_v*)(x + k);
+      gv[j] = *(const f32x4_v*)(a.g + k);
+      bv[j] = *(const f32x4_v*)(a.b + k);
     }
-    float s = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += xv[j].x + xv[j].y + xv[j].z + xv[j].w;
-    const float mean = wave_sum(s) / (float)a.D;
-    float q = 0.0f;
+    const float c0 = lane_value(xv[0].x, 0);
+    float s = 0.0f, q = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (j < nv) {
-        const float d0 = xv[j].x - mean, d1 = xv[j].y - mean, d2 = xv[j].z - mean, d3 = xv[j].w - mean;
-        q += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
+        const f32x4_v d = xv[j] - c0;
+        s += d.x + d.y + d.z + d.w;
+        q += d.x * d.x + d.y * d.y + d.z * d.z + d.w * d.w;
       }
-    const float rstd = rsqrtf(wave_sum(q) / (float)a.D + 1e-5f);
+    const float inv = 1.0f / (float)a.D;
+    s = wave_total(s) * inv;
+    q = wave_total(q) * inv;
+    const float mean = c0 + s, rstd = rsqrtf(fmaxf(q - s * s, 0.0f) + 1e-5f);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (j < nv) {
-        const int k = (j * 64 + lane) * 4;
-        st<TO>(y + k, (xv[j].x - mean) * rstd * gv[j].x + bv[j].x);
-        st<TO>(y + k + 1, (xv[j].y - mean) * rstd * gv[j].y + bv[j].y);
-        st<TO>(y + k + 2, (xv[j].z - mean) * rstd * gv[j].z + bv[j].z);
-        st<TO>(y + k + 3, (xv[j].w - mean) * rstd * gv[j].w + bv[j].w);
+        const f32x4_v o = (xv[j] - mean) * rstd * gv[j] + bv[j];
+        st4<TO>(y + (j * 64 + lane) * 4, o.x, o.y, o.z, o.w);
       }
     return;
   }
   float s = 0.0f;
   for (int k = lane; k < a.D; k += 64) s += x[k];
-  const float mean = wave_sum(s) / (float)a.D;
+  const float mean = wave_total(s) / (float)a.D;
   float q = 0.0f;
   for (int k = lane; k < a.D; k += 64) { float d = x[k] - mean; q += d * d; }
-  const float rstd = rsqrtf(wave_sum(q) / (float)a.D + 1e-5f);
+  const float rstd = rsqrtf(wave_total(q) / (float)a.D + 1e-5f);
   for (int k = lane; k < a.D; k += 64) st<TO>(y + k, (x[k] - mean) * rstd * a.g[k] + a.b[k]);
 }
 
@@ -852,14 +860,14 @@ static const void* mfma_pick_epi(int ek) {
 
 // tile: 0 = chosen here; 1 = 128x128, 2 = 128x64, 3 = 64x128, 4 = 64x64 (test entry point)
 static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
-  const bool glu = a.epi.kind == EPI_GLU;
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   GemmArgs args = a;
   L.tag("gemm_mfma_bf16", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K);
   if (tile == 0) {
-    // largest tile that still yields >= 256 workgroups; GLU needs 64-column wave tiles
-    if (tiles(128, 128) >= 256) tile = 1;
-    else if (glu || tiles(64, 64) < 128) tile = (tiles(128, 64) >= tiles(64, 128) * 3 / 4 && a.M >= 128) ? 2 : 3;
+    // measured at 2048 - 8192 rows: the largest tile only pays with >= 2 workgroups per CU,
+    // 128x64 from 1.5; below that 64x64
+    if (tiles(128, 128) >= 512) tile = 1;
+    else if (tiles(128, 64) >= 384) tile = 2;
     else tile = 4;
   }
   const void* fn;
