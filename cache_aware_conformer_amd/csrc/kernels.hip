@@ -587,7 +587,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   // buffer b: A tile at lds + b * (BM + BN) * LDK, W tile right after it
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int bm0 = blockIdx.y * BM, bn0 = blockIdx.x * BN;
+  // XCD-aware tile order: workgroup L runs on XCD L mod 8, each with its own L2. Give every
+  // XCD a contiguous run of tiles (column tiles fastest), so the blocks that share A rows, and
+  // most of those sharing W rows, meet in one L2 instead of fetching them once per XCD.
+  const int gx = gridDim.x, ntiles = gridDim.x * gridDim.y;
+  const int L = blockIdx.y * gx + blockIdx.x, xq = ntiles / 8, xr = ntiles % 8, xcd = L % 8;
+  const int t = xcd * xq + min(xcd, xr) + L / 8;
+  const int bm0 = (t / gx) * BM, bn0 = (t - (t / gx) * gx) * BN;
   const int M = a.M, N = a.N, K = a.K;
   const bf16_t* A = (const bf16_t*)a.A;
   const bf16_t* W = (const bf16_t*)a.W;
