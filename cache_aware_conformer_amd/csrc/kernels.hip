@@ -746,9 +746,10 @@ constexpr size_t mfma_lds() {
 template <typename TO>
 __device__ __forceinline__ void st4(TO* p, float a, float b, float c, float d) {
   if constexpr (sizeof(TO) == 4) {
-    *(f32x4_v*)p = f32x4_v{a, b, c, d};
+    __builtin_nontemporal_store(f32x4_v{a, b, c, d}, (f32x4_v*)p);
   } else {
-    *(uint2*)p = make_uint2(pack_bf2(a, b), pack_bf2(c, d));
+    typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_v;
+    __builtin_nontemporal_store(u32x2_v{pack_bf2(a, b), pack_bf2(c, d)}, (u32x2_v*)p);
   }
 }
 
