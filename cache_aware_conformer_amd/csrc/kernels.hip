@@ -507,15 +507,17 @@ typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_v;  // 16-byte st
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 
 // Block tile BM x BN, k-step 64, 4 waves as WM x WN, each wave (BM/WM) x (BN/WN) made of
-// 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, 4 per k-step). Global loads run MFMA_ST
-// k-tiles ahead in rotating register sets (the k-loop is unrolled by MFMA_ST so each set is a
-// compile-time register block), so a k-step waits for loads issued MFMA_ST k-steps earlier
+// 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, 4 per k-step). Global loads run ST = 4 or 8
+// k-tiles ahead in rotating register sets (the k-loop is unrolled by ST so each set is a
+// compile-time register block), so a k-step waits for loads issued ST k-steps earlier
 // instead of one: at these tile sizes one k-step of MFMA is far shorter than a memory round
 // trip. Each k-step stores its register set into one of two LDS buffers (row stride 72 bf16:
 // 16-byte aligned, conflict-free fragment reads), passes the block's one barrier and
 // multiplies out of it. The epilogue kind is a template parameter; the accumulator tile goes
 // through LDS and every thread finishes 8 consecutive columns of a row with 16-byte accesses.
-constexpr int MFMA_ST = 4;
+// k-tiles in flight: 8 for 64x64 blocks (16 registers per set), 4 for larger blocks, whose
+// register sets are 2-3x bigger (8 there leaves one wave per SIMD and was measured slower)
+template <int BM, int BN> constexpr int mfma_stages() { return BM * BN <= 64 * 64 ? 8 : 4; }
 
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16); }
 // Epilogue stores are non-temporal: the product's output is read by the next kernel, after the
@@ -582,7 +584,7 @@ __device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, f
 
 template <int BM, int BN, int WM, int WN, int EK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_mfma_kernel(GemmArgs a) {
-  constexpr int BK = 64, LDK = BK + 8, ST = MFMA_ST;
+  constexpr int BK = 64, LDK = BK + 8, ST = mfma_stages<BM, BN>();
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int A_PER_T = BM * (BK / 8) / 256, B_PER_T = BN * (BK / 8) / 256;
   static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small");
@@ -966,7 +968,12 @@ void launch_ln(Launcher& L, const LnArgs& a, int dtype) {
 //   s[i][j] = ((q_i + u) . k_j + (q_i + v) . P[p_i - q_j]) * scale on visible keys, else -inf;
 // max and sum of the row by register exchanges, and o_i = sum_j softmax(s)_ij v_j with lanes
 // over head dims taking each p_ij from the lane that holds it.
-constexpr int ATT_UM = 8;  // 16-byte chunks per thread per staging pass and array
+// 16-byte chunks per thread per staging pass: K/V rings (a 72-80 slot ring is 576-640 chunks in
+// bf16, 1152-1280 in float32) and position rows (73-74 rows of 16 chunks). Larger rings take
+// more passes. Slots past an array's end reload its last chunk: skipping them by a branch
+// serialises the loads (measured 5x slower).
+template <typename T> constexpr int att_um_kv() { return sizeof(T) == 2 ? 3 : 5; }
+constexpr int ATT_UM_P = 5;
 
 size_t attention_shmem(int nf, int R, int nrel, int hd, int esz) {
   const size_t kv_row = ((size_t)hd * esz / 16 + 1) * 16;  // rows padded by one chunk
@@ -1016,14 +1023,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const u32x4_v* pg = (const u32x4_v*)(a.posproj + (long)h * nrel * HD);
   const int nkv = R * KC, np = nrel * FC, nq = (nf + 2) * FC;
 
-  // ---- staging: K, V, P in passes of ATT_UM chunks per thread (one pass unless R is large),
+  // ---- staging: K, V, P in passes of UKV / UP chunks per thread (one pass at the usual sizes),
   // indices clamped so that every load is unconditional; q, u, v with the first pass
-  for (int base = 0; base < nkv || base < np; base += 256 * ATT_UM) {
-    u32x4_v rk[ATT_UM], rv[ATT_UM], rp[ATT_UM], rq[2];
+  constexpr int UKV = att_um_kv<T>(), UP = ATT_UM_P;
+  for (int pass = 0; pass * 256 * UKV < nkv || pass * 256 * UP < np; ++pass) {
+    const int bkv = pass * 256 * UKV, bp = pass * 256 * UP;
+    u32x4_v rk[UKV], rv[UKV], rp[UP], rq[2];
     // position rows and q/u/v first: they do not wait for the stream id, K and V do
 #pragma unroll
-    for (int u = 0; u < ATT_UM; ++u) rp[u] = pg[min(base + u * 256 + tid, np - 1)];
-    if (base == 0) {
+    for (int u = 0; u < UP; ++u) rp[u] = pg[min(bp + u * 256 + tid, np - 1)];
+    if (pass == 0) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c = min(u * 256 + tid, nq - 1), row = c / FC, col = c - row * FC;
@@ -1032,21 +1041,21 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < ATT_UM; ++u) {
-      const int ck = min(base + u * 256 + tid, nkv - 1);
+    for (int u = 0; u < UKV; ++u) {
+      const int ck = min(bkv + u * 256 + tid, nkv - 1);
       rk[u] = kg[ck];
       rv[u] = vg[ck];
     }
     // stored in arrival order
 #pragma unroll
-    for (int u = 0; u < ATT_UM; ++u) {
-      const int c = base + u * 256 + tid;
+    for (int u = 0; u < UP; ++u) {
+      const int c = bp + u * 256 + tid;
       if (c < np) {
         const int row = c / FC, col = c - row * FC;
         *(u32x4_v*)(Ps + row * FS + col * 16) = rp[u];
       }
     }
-    if (base == 0) {
+    if (pass == 0) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int c = u * 256 + tid;
@@ -1054,8 +1063,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < ATT_UM; ++u) {
-      const int c = base + u * 256 + tid;
+    for (int u = 0; u < UKV; ++u) {
+      const int c = bkv + u * 256 + tid;
       if (c < nkv) {
         const int row = c / KC, col = c - row * KC;
         *(u32x4_v*)(Ks + row * KS + col * 16) = rk[u];
