@@ -100,7 +100,7 @@ struct Layout {
   size_t layers, wj, bj, fe_w[3], fe_b[3], weights_end;
   size_t posproj, kring, vring, cring, tail, x0, pos, pend;
   size_t ids, cids, cidx, sids, spos, spend, cpos, ccpos;
-  size_t x, x2, y, q, h, o, e, win, fe1, fe2;
+  size_t x, x2, y, q, h, o, e, part, win, fe1, fe2;
   size_t total;
 };
 
@@ -141,6 +141,8 @@ Layout make_layout(const Dims& d) {
   t.cpos = w.take(S * 4); t.ccpos = w.take(S * 4);
   t.x = w.take(M * D * f4); t.x2 = w.take(M * D * f4); t.y = w.take(M * D * e); t.q = w.take(M * D * f4);
   t.h = w.take(M * F * e); t.o = w.take(M * D * e); t.e = w.take(M * D * e);
+  // split-K partials of the residual products (bf16 MFMA path): up to 4 k-ranges
+  if (d.dt == CAC_BF16) t.part = w.take(4 * M * D * f4);
   if (d.fe) {
     t.win = w.take(S * (d.tail + d.mpc) * d.bins * e);
     t.fe1 = w.take(S * 11 * D * e);
@@ -283,21 +285,74 @@ struct Pass {
   // as an extra LayerNorm, FF1 down as the LayerNorm'ed residual base written to the other x
   // buffer), and the depthwise conv + SiLU is pw2's A operand.
   bool fused() const { return c->d.dt == CAC_F32 || M <= 8; }
+  // many rows with D a multiple of 256 (<= 1024): each residual product is followed by one row
+  // kernel that adds it to the residual stream and writes the next product's LayerNorm'ed
+  // operand to y, so the products read y as plain compute-dtype rows
+  bool row_kernels() const { return !fused() && c->d.D % 256 == 0 && c->d.D <= 1024; }
   float* cur = nullptr;  // buffer holding the residual stream (fused path: before ln_out)
+
+  // k-ranges of a residual product (MFMA path): enough 64x64 tiles x ranges for a block per
+  // CU, each range at least 128 deep; 1: no split
+  int ksplit_for(int N, int K) const {
+    const int tiles = ((M + 63) / 64) * ((N + 63) / 64);
+    int s = 1;
+    while (s < 4 && tiles * s < 256 && K % (64 * 2 * s) == 0 && K / (2 * s) >= 128) s *= 2;
+    return s;
+  }
+  void row_kernel(const ResLnArgs& r) {
+    if (!launch_resid_ln(L, r, c->d.dt) && L.err == hipSuccess) L.err = hipErrorInvalidValue;
+  }
+  // cur += alpha (A W^T + bias), then cur = LN(cur; go, bo) when go, then y = LN(cur; gn, bn)
+  // (y = cur when gn is null): split-K partials summed by the row kernel, or the product's
+  // residual epilogue followed by the row kernel
+  void resid_rows(const char* role, const void* A, int lda, const void* W, int K, float alpha, const float* bias,
+                  const float* go, const float* bo, const float* gn, const float* bn) {
+    const Dims& d = c->d;
+    const int ks = ksplit_for(d.D, K);
+    GemmArgs g{};
+    g.M = M; g.N = d.D; g.K = K; g.A = A; g.W = W; g.amap = RowMap{INT_MAX, 0, lda};
+    EpiArgs e = epi0();
+    ResLnArgs r{};
+    if (ks > 1) {
+      e.kind = EPI_PART; e.out = c->P<void>(c->lay.part); e.ldo = d.D; e.pstride = (long)M * d.D;
+      g.ksplit = ks;
+      r.part = c->P<float>(c->lay.part); r.pstride = e.pstride; r.nparts = ks; r.bias = bias; r.alpha = alpha;
+    } else {
+      e.kind = EPI_RESID; e.bias = bias; e.out = cur; e.ldo = d.D; e.alpha = alpha;
+    }
+    g.epi = e;
+    L.role = role;
+    launch_gemm(L, g, d.dt, 0);
+    r.x = cur; r.go = go; r.bo = bo; r.gn = gn; r.bn = bn; r.y = c->P<void>(c->lay.y); r.M = M; r.D = d.D;
+    L.role = role;
+    row_kernel(r);
+  }
 
   void layers() {
     const Dims& d = c->d;
     const LayerOff& lo = c->lay.lo;
     cur = c->P<float>(c->lay.x);
     float* other = c->P<float>(c->lay.x2);
-    const bool fz = fused();
+    const bool fz = fused(), rk = row_kernels();
     const float *pre_g = nullptr, *pre_b = nullptr;  // previous block's ln_out (fused path)
+    if (rk) {  // y = LN(x) for the first block's FF1
+      const char* l0 = c->ws + c->lay.layers;
+      ResLnArgs r{};
+      r.x = cur; r.gn = (const float*)(l0 + lo.ln[0]); r.bn = (const float*)(l0 + lo.ln[1]);
+      r.y = c->P<void>(c->lay.y); r.M = M; r.D = d.D;
+      L.role = "ln_in";
+      row_kernel(r);
+    }
     for (int l = 0; l < d.L; ++l) {
       char* lb = c->ws + c->lay.layers + (size_t)l * lo.size;
       const size_t kvl = (size_t)d.S * d.H * d.R * d.hd * d.esz;
       char* kr = c->ws + c->lay.kring + l * kvl;
       char* vr = c->ws + c->lay.vring + l * kvl;
       char* cr = c->ws + c->lay.cring + (size_t)l * d.S * d.Rc * d.D * d.esz;
+      if (rk) {
+        rows_layer(l, lb, kr, vr, cr);
+        continue;
+      }
       auto F32 = [&](size_t off) { return (const float*)(lb + off); };
       auto gemm_x = [&](const float* lng, const float* lnb, const void* W, int N, const EpiArgs& e, bool with_pre) {
         GemmArgs g{};
@@ -337,21 +392,7 @@ struct Pass {
       qkv.kring = kr; qkv.vring = vr;
       L.role = "qkv";
       gemm_x(F32(lo.ln[2]), F32(lo.ln[3]), lb + lo.w_qkv, 3 * d.D, qkv, false);
-      AttnArgs at{};
-      at.cv = cv; at.q = c->P<float>(c->lay.q); at.kring = kr; at.vring = vr;
-      at.posproj = c->P<float>(c->lay.posproj) + (size_t)l * d.H * d.nrel * d.hd;
-      at.pos_u = F32(lo.pos_u); at.pos_v = F32(lo.pos_v);
-      at.o = c->P<void>(c->lay.o);
-      at.D = d.D; at.H = d.H; at.R = d.R; at.Lc = d.Lc; at.chunk = d.c; at.right = d.right;
-      at.lookahead = d.lookahead; at.rel_lo = d.rel_lo; at.nrel = d.nrel;
-      at.scale = 1.0f / sqrtf((float)d.hd);
-      {
-        const double nrows = (double)cv.n_streams * cv.nf;
-        const double bytes = kv_rows * 2.0 * d.D * d.esz + (double)d.H * d.nrel * d.hd * 4.0;
-        const double flops = 6.0 * nrows * (kv_rows / cv.n_streams) * d.D;
-        L.tag("attention", bytes, flops);
-      }
-      launch_attention(L, at, d.dt, d.hd);
+      attention(l, lb, kr, vr);
       L.role = "wo";
       gemm_plain(c->P<void>(c->lay.o), d.D, lb + lo.w_o, d.D, d.D, resid(1.0f, F32(lo.b_o)));
       // ---- conv module: LN -> pw1 -> GLU into the ring; depthwise + SiLU; pw2 + residual
@@ -405,8 +446,74 @@ struct Pass {
       }
     }
     last_g = pre_g; last_b = pre_b;
+    rows_y = rk;
   }
   const float *last_g = nullptr, *last_b = nullptr;  // ln_out still to apply (fused path)
+  bool rows_y = false;  // y holds the final rows in the compute dtype (row-kernel path)
+
+  // rel-pos attention of layer l over the rings (q rows in q, output rows to o)
+  void attention(int l, const char* lb, char* kr, char* vr) {
+    const Dims& d = c->d;
+    const LayerOff& lo = c->lay.lo;
+    AttnArgs at{};
+    at.cv = cv; at.q = c->P<float>(c->lay.q); at.kring = kr; at.vring = vr;
+    at.posproj = c->P<float>(c->lay.posproj) + (size_t)l * d.H * d.nrel * d.hd;
+    at.pos_u = (const float*)(lb + lo.pos_u); at.pos_v = (const float*)(lb + lo.pos_v);
+    at.o = c->P<void>(c->lay.o);
+    at.D = d.D; at.H = d.H; at.R = d.R; at.Lc = d.Lc; at.chunk = d.c; at.right = d.right;
+    at.lookahead = d.lookahead; at.rel_lo = d.rel_lo; at.nrel = d.nrel;
+    at.scale = 1.0f / sqrtf((float)d.hd);
+    const double nrows = (double)cv.n_streams * cv.nf;
+    const double bytes = kv_rows * 2.0 * d.D * d.esz + (double)d.H * d.nrel * d.hd * 4.0;
+    const double flops = 6.0 * nrows * (kv_rows / cv.n_streams) * d.D;
+    L.tag("attention", bytes, flops);
+    launch_attention(L, at, d.dt, d.hd);
+  }
+
+  // One Conformer block on the row-kernel path: on entry y holds LN_ff1(cur); every product
+  // reads y (or h, o, e) as plain rows and every residual product ends in the row kernel that
+  // writes the next LayerNorm'ed operand; the last one applies the block's ln_out to cur and
+  // writes the next block's FF1 operand (after the last block: y = cur rounded, for the joint).
+  void rows_layer(int l, const char* lb, char* kr, char* vr, char* cr) {
+    const Dims& d = c->d;
+    const LayerOff& lo = c->lay.lo;
+    auto F32 = [&](size_t off) { return (const float*)(lb + off); };
+    void* y = c->P<void>(c->lay.y);
+    // ---- FF1 (macaron half step)
+    EpiArgs up = epi0();
+    up.kind = EPI_SILU; up.bias = F32(lo.b_ff1_1); up.out = c->P<void>(c->lay.h); up.ldo = d.F;
+    L.role = "ff1_up";
+    gemm_plain(y, d.D, lb + lo.w_ff1_1, d.F, d.D, up);
+    resid_rows("ff1_down", c->P<void>(c->lay.h), d.F, lb + lo.w_ff1_2, d.F, 0.5f, F32(lo.b_ff1_2), nullptr, nullptr,
+               F32(lo.ln[2]), F32(lo.ln[3]));
+    // ---- MHSA
+    EpiArgs qkv = epi0();
+    qkv.kind = EPI_QKV; qkv.bias = F32(lo.b_qkv); qkv.qbuf = c->P<float>(c->lay.q);
+    qkv.kring = kr; qkv.vring = vr;
+    L.role = "qkv";
+    gemm_plain(y, d.D, lb + lo.w_qkv, 3 * d.D, d.D, qkv);
+    attention(l, lb, kr, vr);
+    resid_rows("wo", c->P<void>(c->lay.o), d.D, lb + lo.w_o, d.D, 1.0f, F32(lo.b_o), nullptr, nullptr, F32(lo.ln[4]),
+               F32(lo.ln[5]));
+    // ---- conv module: pw1 -> GLU into the ring; depthwise + SiLU; pw2
+    EpiArgs glu = epi0();
+    glu.kind = EPI_GLU; glu.bias = F32(lo.b_pw1); glu.cring = cr;
+    L.role = "pw1";
+    gemm_plain(y, d.D, lb + lo.w_pw1, 2 * d.D, d.D, glu);
+    DwArgs dw{cv, cr, F32(lo.dw_w), F32(lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
+    L.tag("dwconv", (double)cv.n_streams * (d.Kc + cv.nf) * d.D * d.esz, 2.0 * d.K * d.D * M);
+    launch_dwconv(L, dw, d.dt);
+    resid_rows("pw2", c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, 1.0f, F32(lo.b_pw2), nullptr, nullptr,
+               F32(lo.ln[6]), F32(lo.ln[7]));
+    // ---- FF2 (macaron half step), then ln_out
+    up.bias = F32(lo.b_ff2_1);
+    L.role = "ff2_up";
+    gemm_plain(y, d.D, lb + lo.w_ff2_1, d.F, d.D, up);
+    const bool last = l + 1 == d.L;
+    const char* nb = lb + lo.size;  // next block's parameters
+    resid_rows("ff2_down", c->P<void>(c->lay.h), d.F, lb + lo.w_ff2_2, d.F, 0.5f, F32(lo.b_ff2_2), F32(lo.ln[8]),
+               F32(lo.ln[9]), last ? nullptr : (const float*)(nb + lo.ln[0]), last ? nullptr : (const float*)(nb + lo.ln[1]));
+  }
 
   // encoder-side joint projection of the rows picked by amap into d_out (rows remapped by omap)
   void joint(float* d_out, int rows, RowMap amap, const int32_t* omap, int ogroup, int ostride) {
@@ -427,6 +534,11 @@ struct Pass {
     g.M = rows; g.N = d.P; g.K = d.D; g.A = cur; g.amap = amap;
     g.W = c->P<void>(c->lay.wj); g.epi = e; g.a_f32 = 1; g.a_scratch = c->P<void>(c->lay.y);
     g.ln_g = last_g; g.ln_b = last_b;
+    if (rows_y) {  // the last row kernel left y = cur in the compute dtype
+      g.A = c->P<void>(c->lay.y);
+      g.a_f32 = 0;
+      g.a_scratch = nullptr;
+    }
     L.role = "joint";
     launch_gemm(L, g, d.dt, 0);
   }
@@ -1038,9 +1150,11 @@ int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t
                       const float* d_bias, float* d_C, void* hip_stream) {
   if (dtype != CAC_F32 && dtype != CAC_BF16) return CAC_EINVAL;
   if (M < 1 || N < 1 || K < 1 || !d_A || !d_W || !d_C) return CAC_EINVAL;
-  if (path < 0 || path > 6 || (path >= 2 && dtype != CAC_BF16)) return CAC_EINVAL;
+  if (path < 0 || path > 8 || (path >= 2 && dtype != CAC_BF16)) return CAC_EINVAL;
   if (path >= 2 && K % 64) return CAC_EINVAL;  // MFMA tiles step K by 64
   if ((size_t)8 * K * 4 > 160 * 1024 && path < 2) return CAC_EINVAL;
+  const int ks = path == 7 ? 2 : path == 8 ? 4 : 1;
+  if (ks > 1 && (K % (64 * ks) || N % 256 || N > 1024)) return CAC_EINVAL;
   kernels_init();
   Launcher L;
   L.stream = (hipStream_t)hip_stream;
@@ -1048,8 +1162,26 @@ int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t
   e.kind = EPI_F32; e.bias = d_bias; e.out = d_C; e.ldo = N;
   GemmArgs g{};
   g.M = M; g.N = N; g.K = K; g.A = d_A; g.W = d_W; g.amap = RowMap{INT_MAX, 0, K}; g.epi = e;
-  launch_gemm(L, g, dtype, path);
-  return L.err == hipSuccess ? CAC_OK : CAC_EHIP;
+  if (ks == 1) {
+    launch_gemm(L, g, dtype, path);
+    return L.err == hipSuccess ? CAC_OK : CAC_EHIP;
+  }
+  // split-K: partials in a temporary buffer, summed with the bias into the zeroed output by
+  // the residual row kernel
+  float* part = nullptr;
+  if (hipMalloc((void**)&part, (size_t)ks * M * N * sizeof(float)) != hipSuccess) return CAC_EHIP;
+  hipError_t err = hipMemsetAsync(d_C, 0, (size_t)M * N * sizeof(float), L.stream);
+  g.epi.kind = EPI_PART; g.epi.bias = nullptr; g.epi.out = part; g.epi.pstride = (long)M * N; g.ksplit = ks;
+  if (err == hipSuccess) {
+    launch_gemm(L, g, dtype, 0);
+    ResLnArgs r{};
+    r.part = part; r.pstride = (long)M * N; r.nparts = ks; r.bias = d_bias; r.alpha = 1.0f; r.x = d_C; r.M = M; r.D = N;
+    if (L.err == hipSuccess && !launch_resid_ln(L, r, dtype)) L.err = hipErrorInvalidValue;
+    err = L.err;
+  }
+  const hipError_t se = hipStreamSynchronize(L.stream);
+  (void)hipFree(part);
+  return err == hipSuccess && se == hipSuccess ? CAC_OK : CAC_EHIP;
 }
 
 }  // extern "C"

@@ -128,6 +128,8 @@ enum EpiKind {
   EPI_GLU = 6,     // a*sigmoid(b) of GLU-packed column pairs -> conv ring slot
   EPI_GLU_DW = 7,  // EPI_GLU, then the causal depthwise conv + SiLU of the call's rows over the
                    // ring -> out_t[m][c] (compute dtype); two-row kernel only (GemmArgs dw_*)
+  EPI_PART = 8,    // part[z][m][n] = acc over k-range z (float32, no bias): split-K partial of
+                   // the MFMA kernel, summed by resid_ln (GemmArgs ksplit, EpiArgs pstride)
 };
 
 // GLU packing of the pointwise-1 weight rows: packed row (c / 32) * 64 + c % 32 holds value
@@ -140,6 +142,7 @@ struct EpiArgs {
   void* out;          // EPI_STORE/SILU/RELU_FE: compute dtype; EPI_RESID/F32: float
   int ldo;
   float alpha;
+  long pstride;       // EPI_PART: elements between the partials of consecutive k-ranges
   // EPI_F32 output row remap (lookahead emits a subset of rows): row_out = omap[m / ogroup] *
   // ostride + m % ogroup when omap != null
   const int32_t* omap;
@@ -177,6 +180,7 @@ struct GemmArgs {
   const float* res_g;    // (res_g null: out = res_src + alpha (acc + b)); out != res_src
   const float* res_b;
   int upb;               // small-M kernel: output units (columns, or GLU channels) per block
+  int ksplit;            // MFMA kernel with EPI_PART: K in ksplit equal ranges (0 or 1: one)
   EpiArgs epi;
 };
 
@@ -187,6 +191,24 @@ struct LnArgs {
   const float* b;
   int M, D;
   int out_f32;     // 1: y is float32
+};
+
+// Residual update and LayerNorm(s) of whole rows, one wave per row (D a multiple of 256, at
+// most 1024):  v = sum_z part[z][m] (z in order) + bias;  x[m] += alpha * v  (nparts > 0);
+// x[m] = LN(x[m]; go, bo) when go;  y[m] = LN(x[m]; gn, bn) (gn) or x[m] (gn null) when y.
+struct ResLnArgs {
+  const float* part;  // [nparts][M][D] split-K partials (nparts 0: no residual update)
+  long pstride;       // elements between consecutive partials
+  int nparts;
+  const float* bias;  // [D] or null
+  float alpha;
+  float* x;           // [M][D] float32 residual stream, updated in place
+  const float* go;    // LayerNorm applied to x in place (null: none)
+  const float* bo;
+  const float* gn;    // LayerNorm of the y rows (null: y = x)
+  const float* bn;
+  void* y;            // [M][D] compute dtype (null: not written)
+  int M, D;
 };
 
 struct AttnArgs {
@@ -350,6 +372,8 @@ bool rowdot_supported(const GemmArgs& a, int dtype);
 bool rowdot_launch(Launcher& L, const GemmArgs& a, int dtype);
 double gemm_bytes(const GemmArgs& a, int wsz);
 void launch_ln(Launcher& L, const LnArgs& a, int dtype);
+// false (nothing launched) when D is not a multiple of 256 up to 1024 or nparts is not 0, 2 or 4
+bool launch_resid_ln(Launcher& L, const ResLnArgs& a, int dtype);
 void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd);
 void launch_dwconv(Launcher& L, const DwArgs& a, int dtype);
 void launch_input(Launcher& L, const InputArgs& a, int dtype);

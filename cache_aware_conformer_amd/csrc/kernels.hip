@@ -594,15 +594,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   // XCD-aware tile order: workgroup L runs on XCD L mod 8, each with its own L2. Give every
-  // XCD a contiguous run of tiles (column tiles fastest), so the blocks that share A rows, and
-  // most of those sharing W rows, meet in one L2 instead of fetching them once per XCD.
-  const int gx = gridDim.x, ntiles = gridDim.x * gridDim.y;
-  const int L = blockIdx.y * gx + blockIdx.x, xq = ntiles / 8, xr = ntiles % 8, xcd = L % 8;
-  const int t = xcd * xq + min(xcd, xr) + L / 8;
+  // XCD a contiguous run of tiles (column tiles fastest, then row tiles, then k-ranges), so the
+  // blocks that share A rows, and most of those sharing W rows, meet in one L2 instead of
+  // fetching them once per XCD.
+  const int gx = gridDim.x, ntiles = gridDim.x * gridDim.y, nall = ntiles * gridDim.z;
+  const int L = (blockIdx.z * gridDim.y + blockIdx.y) * gx + blockIdx.x, xq = nall / 8, xr = nall % 8, xcd = L % 8;
+  const int f = xcd * xq + min(xcd, xr) + L / 8;
+  const int kz = f / ntiles, t = f - kz * ntiles;
   const int bm0 = (t / gx) * BM, bn0 = (t - (t / gx) * gx) * BN;
-  const int M = a.M, N = a.N, K = a.K;
-  const bf16_t* A = (const bf16_t*)a.A;
-  const bf16_t* W = (const bf16_t*)a.W;
+  // split-K (gridDim.z ranges, EPI_PART): this block's k-range starts at column k0
+  const int M = a.M, N = a.N, K = a.K, Ks = K / (int)gridDim.z, k0 = kz * Ks;
+  const bf16_t* A = (const bf16_t*)a.A + k0;
+  const bf16_t* W = (const bf16_t*)a.W + k0;
 
   const bf16_t* aptr[A_PER_T];
   const bf16_t* bptr[B_PER_T];
@@ -641,7 +644,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int KT = K / BK;
+  const int KT = Ks / BK;
   // k-tiles 0..ST-1 in flight (indices past the end reload the last tile: every load stays
   // unconditional, so the compiler counts them in order)
 #pragma unroll
@@ -729,7 +732,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       if (row >= M || col >= N) continue;
       float v[8];
       ld_f8(ct + rr * CS + cc, v);
-      mfma_epi8<EK>(a, row, col, v);
+      if constexpr (EK == EPI_PART) st_f8((float*)a.epi.out + kz * a.epi.pstride + (long)row * a.epi.ldo + col, v);
+      else mfma_epi8<EK>(a, row, col, v);
     }
   }
 }
@@ -799,6 +803,110 @@ __global__ __launch_bounds__(256) void ln_kernel(LnArgs a) {
   for (int k = lane; k < a.D; k += 64) { float d = x[k] - mean; q += d * d; }
   const float rstd = rsqrtf(wave_total(q) / (float)a.D + 1e-5f);
   for (int k = lane; k < a.D; k += 64) st<TO>(y + k, (x[k] - mean) * rstd * a.g[k] + a.b[k]);
+}
+
+// =============================================================================== residual + LayerNorm rows
+// One wave per row of D = 256 * NV: chunk j of the row is elements (j * 64 + lane) * 4 .. +3.
+// Every operand of the row (x, the NP split-K partials, bias, both LayerNorms' gains and
+// shifts) is loaded up front, null operands from a stand-in address and ignored, so the row
+// costs one memory round trip. The partials are added in k-range order, so the result does
+// not depend on which block of the product finished first.
+template <int NV>
+__device__ __forceinline__ void row_layernorm(f32x4_v* v, const f32x4_v* g, const f32x4_v* b, float inv_d) {
+  float s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) s += (v[j].x + v[j].y) + (v[j].z + v[j].w);
+  const float mean = wave_total(s) * inv_d;
+  float q = 0.0f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const f32x4_v d = v[j] - mean;
+    q += (d.x * d.x + d.y * d.y) + (d.z * d.z + d.w * d.w);
+  }
+  const float rstd = rsqrtf(wave_total(q) * inv_d + 1e-5f);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = (v[j] - mean) * rstd * g[j] + b[j];
+}
+
+template <typename TO, int NP, int NV>
+__global__ __launch_bounds__(256) void resid_ln_kernel(ResLnArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= a.M) return;
+  const long ro = (long)row * a.D;
+  float* x = a.x + ro;
+  const float* any = a.x;  // stand-in for null operands
+  const float* bias = a.bias ? a.bias : any;
+  const float* go = a.go ? a.go : any;
+  const float* bo = a.bo ? a.bo : any;
+  const float* gn = a.gn ? a.gn : any;
+  const float* bn = a.bn ? a.bn : any;
+  f32x4_v xv[NV], bv[NV], gov[NV], bov[NV], gnv[NV], bnv[NV];
+  f32x4_v pv[NP > 0 ? NP : 1][NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int k = (j * 64 + lane) * 4;
+    xv[j] = *(const f32x4_v*)(x + k);
+#pragma unroll
+    for (int z = 0; z < NP; ++z) pv[z][j] = *(const f32x4_v*)(a.part + z * a.pstride + ro + k);
+    bv[j] = *(const f32x4_v*)(bias + k);
+    gov[j] = *(const f32x4_v*)(go + k);
+    bov[j] = *(const f32x4_v*)(bo + k);
+    gnv[j] = *(const f32x4_v*)(gn + k);
+    bnv[j] = *(const f32x4_v*)(bn + k);
+  }
+  const float inv_d = 1.0f / (float)a.D;
+  if constexpr (NP > 0) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      f32x4_v v = pv[0][j];
+#pragma unroll
+      for (int z = 1; z < NP; ++z) v += pv[z][j];
+      if (a.bias) v += bv[j];
+      xv[j] += a.alpha * v;
+    }
+  }
+  if (a.go) row_layernorm<NV>(xv, gov, bov, inv_d);
+  if (NP > 0 || a.go) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) *(f32x4_v*)(x + (j * 64 + lane) * 4) = xv[j];
+  }
+  if (a.y) {
+    if (a.gn) row_layernorm<NV>(xv, gnv, bnv, inv_d);
+    TO* y = (TO*)a.y + ro;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) st4<TO>(y + (j * 64 + lane) * 4, xv[j].x, xv[j].y, xv[j].z, xv[j].w);
+  }
+}
+
+template <typename TO, int NP>
+static const void* resid_ln_pick_nv(int nv) {
+  switch (nv) {
+    case 1: return (const void*)&resid_ln_kernel<TO, NP, 1>;
+    case 2: return (const void*)&resid_ln_kernel<TO, NP, 2>;
+    case 3: return (const void*)&resid_ln_kernel<TO, NP, 3>;
+    case 4: return (const void*)&resid_ln_kernel<TO, NP, 4>;
+    default: return nullptr;
+  }
+}
+template <typename TO>
+static const void* resid_ln_pick(int np, int nv) {
+  switch (np) {
+    case 0: return resid_ln_pick_nv<TO, 0>(nv);
+    case 2: return resid_ln_pick_nv<TO, 2>(nv);
+    case 4: return resid_ln_pick_nv<TO, 4>(nv);
+    default: return nullptr;
+  }
+}
+
+bool launch_resid_ln(Launcher& L, const ResLnArgs& a, int dtype) {
+  if (a.D % 256 || a.D > 1024 || a.M < 1) return false;
+  const void* fn = dtype == DT_F32 ? resid_ln_pick<float>(a.nparts, a.D / 256) : resid_ln_pick<bf16_t>(a.nparts, a.D / 256);
+  if (!fn) return false;
+  ResLnArgs args = a;
+  // algorithmic bytes: none (activations and partials stay in the last-level cache)
+  L.tag("resid_ln", 0.0, 0.0);
+  L.launch(fn, dim3((a.M + 3) / 4), dim3(256), 0, &args);
+  return true;
 }
 
 // =============================================================================== dense dispatch
@@ -873,6 +981,7 @@ static const void* mfma_pick_epi(int ek) {
     case EPI_F32: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_F32>;
     case EPI_QKV: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_QKV>;
     case EPI_GLU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_GLU>;
+    case EPI_PART: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_PART>;
     default: return nullptr;
   }
 }
@@ -882,11 +991,16 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   GemmArgs args = a;
   L.tag("gemm_mfma_bf16", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K);
+  const int ks = std::max(a.ksplit, 1);
+  if (ks > 1 && (a.epi.kind != EPI_PART || a.K % (64 * ks))) {  // split-K writes partials only
+    if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
+    return;
+  }
   if (tile == 0) {
     // measured at 2048 - 8192 rows: the largest tile only pays with >= 2 workgroups per CU,
-    // 128x64 from 1.5; below that 64x64
-    if (tiles(128, 128) >= 512) tile = 1;
-    else if (tiles(128, 64) >= 384) tile = 2;
+    // 128x64 from 1.5; below that 64x64 (always with split-K, whose k-ranges add the blocks)
+    if (ks == 1 && tiles(128, 128) >= 512) tile = 1;
+    else if (ks == 1 && tiles(128, 64) >= 384) tile = 2;
     else tile = 4;
   }
   const void* fn;
@@ -902,6 +1016,7 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
     if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
     return;
   }
+  grid.z = ks;
   L.launch(fn, grid, dim3(256), shm, &args);
 }
 
@@ -1555,7 +1670,7 @@ void kernels_init() {
       fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 2>(kch, glu));
       fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 8>(kch, glu));
     }
-  for (int ek : {EPI_STORE, EPI_SILU, EPI_RELU_FE, EPI_RESID, EPI_F32, EPI_QKV, EPI_GLU}) {
+  for (int ek : {EPI_STORE, EPI_SILU, EPI_RELU_FE, EPI_RESID, EPI_F32, EPI_QKV, EPI_GLU, EPI_PART}) {
     fns.push_back(mfma_pick_epi<128, 128, 2, 2>(ek));
     fns.push_back(mfma_pick_epi<128, 64, 4, 1>(ek));
     fns.push_back(mfma_pick_epi<64, 128, 2, 2>(ek));
