@@ -187,7 +187,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
       const int uw = min(u0 + u, units - 1);
       const int col = GLU ? glu_a_col(uw) + 32 * c : uw;
 #pragma unroll
-      for (int k = 0; k < KCH; ++k) wr[u][c][k] = *(const u32x4*)(W + (long)col * K + (k * 64 + lane) * VEC);
+      for (int k = 0; k < KCH; ++k) wr[u][c][k] = __builtin_nontemporal_load((const u32x4*)(W + (long)col * K + (k * 64 + lane) * VEC));
     }
   float x[RD_ROWS][PER];
 #pragma unroll
