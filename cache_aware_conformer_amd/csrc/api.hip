@@ -98,7 +98,7 @@ struct LayerOff {
 struct Layout {
   LayerOff lo;
   size_t layers, wj, bj, fe_w[3], fe_b[3], weights_end;
-  size_t posproj, kring, vring, cring, tail, x0, pos, pend;
+  size_t posproj, posproj_bf, kring, vring, cring, tail, x0, pos, pend;
   size_t ids, cids, cidx, sids, spos, spend, cpos, ccpos;
   size_t x, x2, y, q, h, o, e, part, win, fe1, fe2;
   size_t total;
@@ -130,6 +130,8 @@ Layout make_layout(const Dims& d) {
   t.weights_end = w.take(0);
   const size_t S = d.S, L = d.L, M = S * d.nfmax;
   t.posproj = w.take(L * d.H * d.nrel * d.hd * f4);
+  // bf16 copy of the position table (operand of the bf16 MFMA attention kernel)
+  if (d.dt == CAC_BF16) t.posproj_bf = w.take(L * d.H * d.nrel * d.hd * 2);
   t.kring = w.take(L * S * d.H * d.R * d.hd * e);
   t.vring = w.take(L * S * d.H * d.R * d.hd * e);
   t.cring = w.take(L * S * d.Rc * D * e);
@@ -458,6 +460,7 @@ struct Pass {
     AttnArgs at{};
     at.cv = cv; at.q = c->P<float>(c->lay.q); at.kring = kr; at.vring = vr;
     at.posproj = c->P<float>(c->lay.posproj) + (size_t)l * d.H * d.nrel * d.hd;
+    if (d.dt == CAC_BF16) at.posproj_bf = c->P<bf16_t>(c->lay.posproj_bf) + (size_t)l * d.H * d.nrel * d.hd;
     at.pos_u = (const float*)(lb + lo.pos_u); at.pos_v = (const float*)(lb + lo.pos_v);
     at.o = c->P<void>(c->lay.o);
     at.D = d.D; at.H = d.H; at.R = d.R; at.Lc = d.Lc; at.chunk = d.c; at.right = d.right;
@@ -689,6 +692,10 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
       PosProjArgs pa{c->P<float>(lay.layers + (size_t)l * lay.lo.size + lay.lo.wpos),
                      c->P<float>(lay.posproj) + (size_t)l * d.H * d.nrel * d.hd, 1, d.D, d.H, d.hd, d.rel_lo, d.nrel};
       launch_posproj(L, pa);
+    }
+    if (d.dt == CAC_BF16) {
+      CvtArgs cv{c->P<float>(lay.posproj), RowMap{INT_MAX, 0, d.hd}, c->ws + lay.posproj_bf, d.L * d.H * d.nrel, d.hd};
+      launch_cvt(L, cv);
     }
     e = L.err;
   }

@@ -222,6 +222,7 @@ struct AttnArgs {
   void* o;              // [M][D] compute dtype
   int D, H, R, Lc, chunk, right, lookahead, rel_lo, nrel;
   float scale;
+  const void* posproj_bf;  // bf16 copy of posproj (MFMA attention kernel), or null
 };
 
 struct DwArgs {
@@ -372,6 +373,7 @@ bool rowdot_supported(const GemmArgs& a, int dtype);
 bool rowdot_launch(Launcher& L, const GemmArgs& a, int dtype);
 double gemm_bytes(const GemmArgs& a, int wsz);
 void launch_ln(Launcher& L, const LnArgs& a, int dtype);
+void launch_cvt(Launcher& L, const CvtArgs& a);  // y = bf16(x rows)
 // false (nothing launched) when D is not a multiple of 256 up to 1024 or nparts is not 0, 2 or 4
 bool launch_resid_ln(Launcher& L, const ResLnArgs& a, int dtype);
 void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd);

@@ -1067,6 +1067,13 @@ void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path) {
   mfma_dispatch(L, g, path >= 3 ? path - 2 : 0);
 }
 
+void launch_cvt(Launcher& L, const CvtArgs& a) {
+  CvtArgs args = a;
+  const long total = (long)a.M * a.K;
+  L.tag("convert_rows", 0.0, 0.0);
+  L.launch((const void*)&cvt_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
+}
+
 void launch_ln(Launcher& L, const LnArgs& a, int dtype) {
   LnArgs args = a;
   const void* fn = (a.out_f32 || dtype == DT_F32) ? (const void*)&ln_kernel<float> : (const void*)&ln_kernel<bf16_t>;
@@ -1354,8 +1361,230 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ bf16, head size 64, MFMA
+// One wave per (call stream, head); the score and position-term products on
+// v_mfma_f32_16x16x32_bf16 with the query rows as the 16-row A operand (rows past nf zero):
+//   S[i][j] = (q_i + u) . K_j over 16-slot tiles, B operand = the slot's K row read straight
+//     from the ring (non-temporal: read once per call);
+//   T[i][r] = (q_i + v) . P[r] over 16-distance tiles of the head's position table (bf16 copy);
+//   score[i][j] = (S[i][j] + T[i][p_i - q_j - rel_lo]) * scale on visible slots, else -inf
+//     (T goes through LDS for the lookup by distance);
+//   softmax per query row over the 16 lanes that hold it (MFMA output layout: lane l holds
+//     slot 16 t + l % 16 of rows 4 (l / 16) .. + 3);
+//   PV on VALU from the V rows staged in LDS by non-temporal direct copies, lanes as (4-dim
+//   chunk, slot phase mod 4), every query row at once.
+// q + u and q + v are rounded to bf16 for the products (K and V are bf16 already); everything
+// after the products is float32. Slots holding no key (and padding slots past R) get weight 0
+// and a zeroed V row.
+// LDS written by some lanes of a wave and read by others: order the accesses (a wave's LDS
+// operations execute in issue order, so a compiler fence suffices)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+constexpr int CPOL_NT = 2;  // cache-policy bits of a direct global-to-LDS load: non-temporal
+
+// LDS of the MFMA attention kernel: V rows of NT 16-slot tiles, then position terms and
+// weights of NR query rows
+static size_t attn_mfma_lds(int nt, int nr) { return (size_t)nt * 16 * 128 + 2 * (size_t)nr * nt * 16 * 4; }
+
+__device__ __forceinline__ float row16_max(float v) {  // over the 16 lanes of v's DPP row
+  v = fmaxf(v, dpp<DPP_MIRROR16>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR8>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  return fmaxf(v, dpp<DPP_XOR1>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp<DPP_MIRROR16>(v);
+  v += dpp<DPP_MIRROR8>(v);
+  v += dpp<DPP_XOR2>(v);
+  return v + dpp<DPP_XOR1>(v);
+}
+
+template <int NT, int NR>
+__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int HD = 64, NS = NT * 16;
+  extern __shared__ __attribute__((aligned(16))) unsigned char mf_lds[];
+  unsigned char* Vs = mf_lds;                // [NS][128 B] V rows
+  float* Ts = (float*)(mf_lds + NS * 128);   // [NR][NS] position terms by distance
+  float* Ws = Ts + NR * NS;                  // [NR][NS] weights
+  const int lane = threadIdx.x, l16 = lane & 15, lg = lane >> 4;
+  const int s = blockIdx.x / a.H, h = blockIdx.x - s * a.H;
+  const int id = a.cv.ids[s];
+  const int pos0 = a.cv.cpos[s];
+  const int nf = a.cv.nf, R = a.R, nrel = a.nrel;
+  const long head = ((long)id * a.H + h) * R * HD;
+  {  // V rows to LDS; chunks past the ring's end repeat its last one (those rows are zeroed)
+    const unsigned char* vg = (const unsigned char*)((const bf16_t*)a.vring + head);
+    const int nch = R * 8;
+#pragma unroll
+    for (int c0 = 0; c0 < NS * 8; c0 += 64)
+      __builtin_amdgcn_global_load_lds((glob_void_t*)(vg + min(c0 + lane, nch - 1) * 16), (lds_void_t*)(Vs + c0 * 16), 16, 0,
+                                       CPOL_NT);
+  }
+  // K and position rows as B operands: tile t, k-step ks -> row 16 t + l16, dims 32 ks + 8 lg ..
+  u32x4_v kb[NT][2], pb[NT][2];
+  {
+    const bf16_t* kg = (const bf16_t*)a.kring + head + 8 * lg;
+    const bf16_t* pg = (const bf16_t*)a.posproj_bf + (long)h * nrel * HD + 8 * lg;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const long j = min(16 * t + l16, R - 1), r = min(16 * t + l16, nrel - 1);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        kb[t][ks] = __builtin_nontemporal_load((const u32x4_v*)(kg + j * HD + 32 * ks));
+        pb[t][ks] = *(const u32x4_v*)(pg + r * HD + 32 * ks);
+      }
+    }
+  }
+  // query rows as A operands: row l16 (zero past nf), dims 32 ks + 8 lg .. + 7
+  u32x4_v qa[2], qb[2];
+  {
+    const bool live = l16 < nf;
+    const float* qp = a.q + ((long)s * nf + min(l16, nf - 1)) * a.D + h * HD + 8 * lg;
+    const float* up = a.pos_u + h * HD + 8 * lg;
+    const float* vp = a.pos_v + h * HD + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const f32x4_v q0 = *(const f32x4_v*)(qp + 32 * ks), q1 = *(const f32x4_v*)(qp + 32 * ks + 4);
+      const f32x4_v u0 = *(const f32x4_v*)(up + 32 * ks), u1 = *(const f32x4_v*)(up + 32 * ks + 4);
+      const f32x4_v v0 = *(const f32x4_v*)(vp + 32 * ks), v1 = *(const f32x4_v*)(vp + 32 * ks + 4);
+      const f32x4_v a0 = q0 + u0, a1 = q1 + u1, b0 = q0 + v0, b1 = q1 + v1;
+      qa[ks] = live ? u32x4_v{pack_bf2(a0.x, a0.y), pack_bf2(a0.z, a0.w), pack_bf2(a1.x, a1.y), pack_bf2(a1.z, a1.w)}
+                    : u32x4_v{0u, 0u, 0u, 0u};
+      qb[ks] = live ? u32x4_v{pack_bf2(b0.x, b0.y), pack_bf2(b0.z, b0.w), pack_bf2(b1.x, b1.y), pack_bf2(b1.z, b1.w)}
+                    : u32x4_v{0u, 0u, 0u, 0u};
+    }
+  }
+  // ---- the two products
+  f32x4_v S[NT], T[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    S[t] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+    T[t] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, qa[ks]), __builtin_bit_cast(bf16x8_v, kb[t][ks]),
+                                                     S[t], 0, 0, 0);
+      T[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, qb[ks]), __builtin_bit_cast(bf16x8_v, pb[t][ks]),
+                                                     T[t], 0, 0, 0);
+    }
+  }
+  // ---- ring slot positions; zero the V rows of slots without a key once the copies landed
+  const int pe = pos0 + nf - 1, pm = pe % R, q_lo = max(0, pos0 - a.Lc);
+  auto slot_pos = [&](int j) {  // -1: no key (also the padding slots j >= R)
+    int dd = pm - j;
+    dd += dd < 0 ? R : 0;
+    return (j < R && pe - dd >= q_lo) ? pe - dd : -1;
+  };
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  wave_sync();
+#pragma unroll
+  for (int j0 = 0; j0 < NS; j0 += 8) {
+    const int j = j0 + (lane >> 3);
+    if (slot_pos(j) < 0) *(u32x4_v*)(Vs + j * 128 + (lane & 7) * 16) = u32x4_v{0u, 0u, 0u, 0u};
+  }
+  // position terms to LDS (rows 4 lg + c of each tile)
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (4 * lg + c < NR) Ts[(4 * lg + c) * NS + 16 * t + l16] = T[t][c];
+  wave_sync();
+  // ---- scores and softmax of rows 4 lg + c
+  int qk[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) qk[t] = slot_pos(16 * t + l16);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int m = 4 * lg + c;
+    const int p = pos0 + m;
+    int lo, hi;
+    if (a.lookahead) { lo = p - a.Lc; hi = p + a.right; }
+    else { const int cs = p - p % a.chunk; lo = cs - a.Lc; hi = cs + a.chunk - 1; }
+    lo = max(lo, 0);
+    if (m >= nf) hi = -1;  // rows past the call's frames see nothing
+    const float* tr = Ts + min(m, NR - 1) * NS;
+    float x[NT], mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int q = qk[t];
+      const bool vis = q >= lo && q <= hi;  // q = -1 (no key) fails q >= lo
+      x[t] = vis ? (S[t][c] + tr[vis ? p - q - a.rel_lo : 0]) * a.scale : -INFINITY;
+      mx = fmaxf(mx, x[t]);
+    }
+    mx = row16_max(mx);
+    float sum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      x[t] = mx == -INFINITY ? 0.0f : __expf(x[t] - mx);
+      sum += x[t];
+    }
+    sum = row16_sum(sum);
+    const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+    if (m < NR) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) Ws[m * NS + 16 * t + l16] = x[t] * inv;
+    }
+  }
+  wave_sync();
+  // ---- PV: lane (4-dim chunk c4, phase ph) sums slots ph, ph + 4, ... for every row
+  const int c4 = lane & 15, ph = lane >> 4;
+  f32x4_v o[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) o[i] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+  for (int j0 = 0; j0 < NS; j0 += 4) {
+    const int j = j0 + ph;
+    const uint2 vw = *(const uint2*)(Vs + j * 128 + c4 * 8);
+    const f32x4_v v4 = {__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u), __uint_as_float(vw.y << 16),
+                        __uint_as_float(vw.y & 0xffff0000u)};
+#pragma unroll
+    for (int i = 0; i < NR; ++i) o[i] += Ws[i * NS + j] * v4;
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = o[i][e];
+      v = pair_sum16(v, v);
+      o[i][e] = pair_sum32(v, v);
+    }
+    if (lane < 16 && i < nf) {
+      bf16_t* dst = (bf16_t*)a.o + ((long)s * nf + i) * a.D + h * HD + 4 * lane;
+      *(uint2*)dst = uint2{pack_bf2(o[i].x, o[i].y), pack_bf2(o[i].z, o[i].w)};
+    }
+  }
+}
+
+template <int NT>
+static const void* attn_mfma_pick_nr(int nf) {
+  if (nf <= 2) return (const void*)&attn_mfma_kernel<NT, 2>;
+  if (nf <= 4) return (const void*)&attn_mfma_kernel<NT, 4>;
+  if (nf <= 8) return (const void*)&attn_mfma_kernel<NT, 8>;
+  if (nf <= 12) return (const void*)&attn_mfma_kernel<NT, 12>;
+  return (const void*)&attn_mfma_kernel<NT, 16>;
+}
+static int attn_mfma_nr(int nf) { return nf <= 2 ? 2 : nf <= 4 ? 4 : nf <= 8 ? 8 : nf <= 12 ? 12 : 16; }
+
 void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd) {
   AttnArgs args = a;
+  if (dtype == DT_BF16 && hd == 64 && a.posproj_bf && a.R <= 128 && a.nrel <= 128 && a.cv.nf <= 16) {
+    const int nt = (std::max(a.R, a.nrel) + 15) / 16;
+    const void* fn = nullptr;
+    switch (nt) {
+      case 1: case 2: case 3: case 4: fn = attn_mfma_pick_nr<4>(a.cv.nf); break;
+      case 5: fn = attn_mfma_pick_nr<5>(a.cv.nf); break;
+      case 6: fn = attn_mfma_pick_nr<6>(a.cv.nf); break;
+      case 7: fn = attn_mfma_pick_nr<7>(a.cv.nf); break;
+      default: fn = attn_mfma_pick_nr<8>(a.cv.nf); break;
+    }
+    L.tag_name = "attention";
+    L.launch(fn, dim3(a.cv.n_streams * a.H), dim3(64), attn_mfma_lds(std::max(nt, 4), attn_mfma_nr(a.cv.nf)), &args);
+    return;
+  }
   const size_t shm = attention_shmem(a.cv.nf, a.R, a.nrel, hd, dtype == DT_F32 ? 4 : 2);
   const void* fn = nullptr;
   const bool wide = a.R > 128;  // ring slots per lane: 2 up to R = 128, else 4 (R <= 256)
