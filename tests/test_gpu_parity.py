@@ -185,6 +185,18 @@ def test_c5_bf16_lookahead_512_streams_and_flush():
         assert r <= BF16_TOL
 
 
+@pytest.mark.parametrize("cfg", [
+    # head size 16: the general attention kernel in bf16, LayerNorm launches (D not a multiple of 256)
+    C1.replace(name="C1_bf16_staggered", dtype="bf16", streams=6, staggered=True, chunks=6),
+    # MFMA attention with 1, 4 and 5 query rows per stream (chunk 1, chunk 4, lookahead 2 + 3)
+    C3.replace(name="C3_chunk1", n_layers=2, streams=12, att_chunk=1, n_emit=1, chunks=6),
+    C3.replace(name="C3_chunk4", n_layers=2, streams=12, att_chunk=4, n_emit=4, chunks=6),
+    C5.replace(name="C5_la3", n_layers=2, streams=12, n_lookahead=3, chunks=6),
+], ids=["bf16-hd16", "mfma-att-1row", "mfma-att-4rows", "mfma-att-5rows-lookahead"])
+def test_bf16_attention_shapes(cfg):
+    _run_staggered(cfg, cfg.chunks, 4)
+
+
 def test_bf16_single_stream_small_m_path():
     """1 stream in bf16 runs every dense product through the small-M kernel."""
     cfg = C3.replace(streams=1, staggered=False, chunks=40)
