@@ -15,11 +15,13 @@ enum DType { DT_F32 = 0, DT_BF16 = 1 };
 
 // ------------------------------------------------------------------------ element helpers
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);  // keep NaN a NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                                         // nearest, ties to even
-  return (bf16_t)(u >> 16);
+// float -> bf16, round to nearest even, NaN kept a (quiet) NaN: the gfx950 conversion
+// instruction (v_cvt_pk_bf16_f32), checked bit for bit against the software rounding over
+// random bit patterns, ties, subnormals, infinities and NaNs
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_hw;
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, bf16x2_hw{(__bf16)lo, (__bf16)hi});
 }
 template <typename T> __device__ __forceinline__ float ld(const T* p);
 template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }

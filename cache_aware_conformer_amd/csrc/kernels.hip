@@ -519,7 +519,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 // register sets are 2-3x bigger (8 there leaves one wave per SIMD and was measured slower)
 template <int BM, int BN> constexpr int mfma_stages() { return BM * BN <= 64 * 64 ? 8 : 4; }
 
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16); }
 // Epilogue stores are non-temporal: the product's output is read by the next kernel, after the
 // kernel boundary has written the L2 back anyway, so streaming it past the L2 saves that
 // write-back at the end of the kernel (measured: ~3 us of a 13 us 2048x2048x512 product).
