@@ -996,10 +996,11 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
     return;
   }
   if (tile == 0) {
-    // measured at 2048 - 8192 rows: the largest tile only pays with >= 2 workgroups per CU,
-    // 128x64 from 1.5; below that 64x64 (always with split-K, whose k-ranges add the blocks)
-    if (ks == 1 && tiles(128, 128) >= 512) tile = 1;
-    else if (ks == 1 && tiles(128, 64) >= 384) tile = 2;
+    // measured at 512 - 5120 rows (K 512 / 2048, N 512 - 2048): a larger tile pays from about
+    // 1.25 workgroups per CU (320 tiles); below that 64x64 (always with split-K, whose
+    // k-ranges add the blocks)
+    if (ks == 1 && tiles(128, 128) >= 320) tile = 1;
+    else if (ks == 1 && tiles(128, 64) >= 320) tile = 2;
     else tile = 4;
   }
   const void* fn;
