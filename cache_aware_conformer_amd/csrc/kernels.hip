@@ -1386,9 +1386,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glob_void_t;
 constexpr int CPOL_NT = 2;  // cache-policy bits of a direct global-to-LDS load: non-temporal
 
-// LDS of the MFMA attention kernel: V rows of NT 16-slot tiles, then position terms and
-// weights of NR query rows
-static size_t attn_mfma_lds(int nt, int nr) { return (size_t)nt * 16 * 128 + 2 * (size_t)nr * nt * 16 * 4; }
+// LDS of the MFMA attention kernel: V rows of NT 16-slot tiles, then the position terms of NR
+// query rows, each row overwritten by its softmax weights once its scores are formed (the 16
+// lanes that read a row's terms are the ones that write its weights)
+static size_t attn_mfma_lds(int nt, int nr) { return (size_t)nt * 16 * 128 + (size_t)nr * nt * 16 * 4; }
 
 __device__ __forceinline__ float row16_max(float v) {  // over the 16 lanes of v's DPP row
   v = fmaxf(v, dpp<DPP_MIRROR16>(v));
@@ -1404,12 +1405,12 @@ __device__ __forceinline__ float row16_sum(float v) {
 }
 
 template <int NT, int NR>
-__global__ __launch_bounds__(64) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void attn_mfma_kernel(AttnArgs a) {
   constexpr int HD = 64, NS = NT * 16;
   extern __shared__ __attribute__((aligned(16))) unsigned char mf_lds[];
   unsigned char* Vs = mf_lds;                // [NS][128 B] V rows
-  float* Ts = (float*)(mf_lds + NS * 128);   // [NR][NS] position terms by distance
-  float* Ws = Ts + NR * NS;                  // [NR][NS] weights
+  float* Ts = (float*)(mf_lds + NS * 128);   // [NR][NS] position terms by distance, then weights
+  float* Ws = Ts;
   const int lane = threadIdx.x, l16 = lane & 15, lg = lane >> 4;
   const int s = blockIdx.x / a.H, h = blockIdx.x - s * a.H;
   const int id = a.cv.ids[s];
