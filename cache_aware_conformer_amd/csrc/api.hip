@@ -753,8 +753,8 @@ void enqueue_push(cac_ctx* c, Launcher& L, int n, const int32_t* ids, int n_fram
         L.role = i == 0 ? "fe_conv1" : (i == 1 ? "fe_conv2" : "fe_conv3");
         launch_gemm(L, g, d.dt, 0);
       }
-    } else {
-      InputArgs ia{cv, d_input, c->P<float>(c->lay.x), M, d.D};
+    } else {  // the input kernel also advances the positions (every later kernel reads cpos)
+      InputArgs ia{cv, d_input, c->P<float>(c->lay.x), M, d.D, dpos, n_frames};
       launch_input(L, ia, d.dt);
     }
     double kvr = 0;
@@ -762,8 +762,10 @@ void enqueue_push(cac_ctx* c, Launcher& L, int n, const int32_t* ids, int n_fram
     Pass ps{c, L, cv, M, kvr};
     ps.layers();
     ps.joint(d_out, M, RowMap{INT_MAX, 0, d.D}, nullptr, 1, 0);
-    AdvanceArgs ad{dids, dpos, dpend, n, n_frames, 0};
-    launch_advance(L, ad);
+    if (d.fe) {  // the front-end window kernel reads the positions from every thread of a stream
+      AdvanceArgs ad{dids, dpos, dpend, n, n_frames, 0};
+      launch_advance(L, ad);
+    }
   } else {
     CallView pv{dids, dpos, d.ne, n, c->P<int32_t>(c->lay.cpos)};
     LaStoreArgs ls{pv, dpend, d_input, c->ws + c->lay.x0, d.D, d.Rx};

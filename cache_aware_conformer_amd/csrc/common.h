@@ -237,10 +237,12 @@ struct DwArgs {
 };
 
 struct InputArgs {      // x[m][c] = in[m][c] (float32 residual from compute dtype input)
-  CallView cv;          // also fills cv.cpos
+  CallView cv;          // also fills cv.cpos, then advances the streams' positions by adv
   const void* in;
   float* x;
   int M, D;
+  int32_t* pos;         // [max_streams] positions, advanced by adv (the same array as cv.pos)
+  int adv;
 };
 
 struct FeWindowArgs {   // win[s] = [tail(14) || mel_new(16)]; tail = last 14 of win

@@ -1652,7 +1652,12 @@ template <typename T>
 __global__ __launch_bounds__(256) void input_kernel(InputArgs a) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx < (long)a.M * a.D) a.x[idx] = ld<T>((const T*)a.in + idx);
-  if (idx < a.cv.n_streams) a.cv.cpos[idx] = a.cv.pos[a.cv.ids[idx]];
+  // the call's positions for every later kernel (they read cpos only), then the streams advance
+  if (idx < a.cv.n_streams) {
+    const int id = a.cv.ids[idx], p = a.pos[id];
+    a.cv.cpos[idx] = p;
+    a.pos[id] = p + a.adv;
+  }
 }
 void launch_input(Launcher& L, const InputArgs& a, int dtype) {
   InputArgs args = a;
