@@ -1224,14 +1224,21 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const unsigned char* krow = Ks + min(j, R - 1) * KS;
     const unsigned char* prow = Ps + rel * FS;
     const f32x4_v* qi = (const f32x4_v*)(Qs + ii * HD);
-    float ac = 0.0f, bd = 0.0f;
-#pragma unroll 4
+    // (q + u) and (q + v) of this wave's row in registers: the loop then reads only the lane's
+    // own K and position rows from LDS
+    f32x4_v qu[FC], qv[FC];
+#pragma unroll
     for (int c = 0; c < FC; ++c) {
       const f32x4_v q4 = qi[c];
-      const f32x4_v qu = q4 + ((const f32x4_v*)Us)[c], qv = q4 + ((const f32x4_v*)Ws)[c];
+      qu[c] = q4 + ((const f32x4_v*)Us)[c];
+      qv[c] = q4 + ((const f32x4_v*)Ws)[c];
+    }
+    float ac = 0.0f, bd = 0.0f;
+#pragma unroll
+    for (int c = 0; c < FC; ++c) {
       const f32x4_v k4 = lds4<T>(krow, c), p4 = ((const f32x4_v*)prow)[c];
-      ac += qu.x * k4.x + qu.y * k4.y + qu.z * k4.z + qu.w * k4.w;
-      bd += qv.x * p4.x + qv.y * p4.y + qv.z * p4.z + qv.w * p4.w;
+      ac += qu[c].x * k4.x + qu[c].y * k4.y + qu[c].z * k4.z + qu[c].w * k4.w;
+      bd += qv[c].x * p4.x + qv[c].y * p4.y + qv[c].z * p4.z + qv[c].w * p4.w;
     }
     const float sc = vis ? (ac + bd) * a.scale : -INFINITY;
     const float mw = wave_top(sc);  // -inf when this half holds no visible key
