@@ -1390,8 +1390,12 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glob_void_t;
-constexpr int CPOL_NT = 2;  // cache-policy bits of a direct global-to-LDS load: non-temporal
+constexpr int CPOL_NT = 2;  // cache-policy bits of a vector memory load: non-temporal
+// Raw buffer resource over [p, p + bytes) (stride 0; word 3 = 32-bit data format): loads at byte
+// offsets at or past `bytes` return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
 
 // LDS of the MFMA attention kernel: V rows of NT 16-slot tiles, then the position terms of NR
 // query rows, each row overwritten by its softmax weights once its scores are formed (the 16
@@ -1424,28 +1428,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
   const int pos0 = a.cv.cpos[s];
   const int nf = a.cv.nf, R = a.R, nrel = a.nrel;
   const long head = ((long)id * a.H + h) * R * HD;
-  {  // V rows to LDS; chunks past the ring's end repeat its last one (those rows are zeroed)
-    const unsigned char* vg = (const unsigned char*)((const bf16_t*)a.vring + head);
-    const int nch = R * 8;
+  // The head's K and V rows and its position rows are read through buffer resources sized to
+  // them: the hardware range check turns reads past the last row into zeros, so the 16-row tiles
+  // need no clamped addresses (the slots past R are masked, and their V rows zeroed, below).
+  const __amdgpu_buffer_rsrc_t kr = raw_rsrc((const bf16_t*)a.kring + head, R * HD * 2);
+  const __amdgpu_buffer_rsrc_t vr = raw_rsrc((const bf16_t*)a.vring + head, R * HD * 2);
+  const __amdgpu_buffer_rsrc_t pr = raw_rsrc((const bf16_t*)a.posproj_bf + (long)h * nrel * HD, nrel * HD * 2);
 #pragma unroll
-    for (int c0 = 0; c0 < NS * 8; c0 += 64)
-      __builtin_amdgcn_global_load_lds((glob_void_t*)(vg + min(c0 + lane, nch - 1) * 16), (lds_void_t*)(Vs + c0 * 16), 16, 0,
-                                       CPOL_NT);
-  }
+  for (int c0 = 0; c0 < NS * 8; c0 += 64)  // V rows to LDS, 16 bytes per lane
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(Vs + c0 * 16), 16, (c0 + lane) * 16, 0, 0, CPOL_NT);
   // K and position rows as B operands: tile t, k-step ks -> row 16 t + l16, dims 32 ks + 8 lg ..
   u32x4_v kb[NT][2], pb[NT][2];
   {
-    const bf16_t* kg = (const bf16_t*)a.kring + head + 8 * lg;
-    const bf16_t* pg = (const bf16_t*)a.posproj_bf + (long)h * nrel * HD + 8 * lg;
+    const int bo = l16 * HD * 2 + lg * 16;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const long j = min(16 * t + l16, R - 1), r = min(16 * t + l16, nrel - 1);
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        kb[t][ks] = __builtin_nontemporal_load((const u32x4_v*)(kg + j * HD + 32 * ks));
-        pb[t][ks] = *(const u32x4_v*)(pg + r * HD + 32 * ks);
+        const int off = bo + t * 16 * HD * 2 + ks * 64;
+        kb[t][ks] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, CPOL_NT));
+        pb[t][ks] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
       }
-    }
   }
   // query rows as A operands: row l16 (zero past nf), dims 32 ks + 8 lg .. + 7
   u32x4_v qa[2], qb[2];
@@ -1494,11 +1497,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
     const int j = j0 + (lane >> 3);
     if (slot_pos(j) < 0) *(u32x4_v*)(Vs + j * 128 + (lane & 7) * 16) = u32x4_v{0u, 0u, 0u, 0u};
   }
-  // position terms to LDS (rows 4 lg + c of each tile)
+  // position terms to LDS (rows 4 lg + c of each tile; with NR < 4 only lanes lg = 0 hold kept
+  // rows, and only their first NR)
+  constexpr int CR = NR < 4 ? NR : 4;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < CR; ++c)
       if (4 * lg + c < NR) Ts[(4 * lg + c) * NS + 16 * t + l16] = T[t][c];
   wave_sync();
   // ---- scores and softmax of rows 4 lg + c
@@ -1506,7 +1511,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 8))) void
 #pragma unroll
   for (int t = 0; t < NT; ++t) qk[t] = slot_pos(16 * t + l16);
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int c = 0; c < CR; ++c) {
     const int m = 4 * lg + c;
     const int p = pos0 + m;
     int lo, hi;
