@@ -192,7 +192,11 @@ def test_c5_bf16_lookahead_512_streams_and_flush():
     C3.replace(name="C3_chunk1", n_layers=2, streams=12, att_chunk=1, n_emit=1, chunks=6),
     C3.replace(name="C3_chunk4", n_layers=2, streams=12, att_chunk=4, n_emit=4, chunks=6),
     C5.replace(name="C5_la3", n_layers=2, streams=12, n_lookahead=3, chunks=6),
-], ids=["bf16-hd16", "mfma-att-1row", "mfma-att-4rows", "mfma-att-5rows-lookahead"])
+    # wide rings: 8 slot tiles with 2 query rows, and with 10 (register budget above 128)
+    C3.replace(name="C3_left110", n_layers=2, streams=12, att_left=110, chunks=6),
+    C5.replace(name="C5_left100", n_layers=2, streams=8, att_left=100, chunks=5),
+], ids=["bf16-hd16", "mfma-att-1row", "mfma-att-4rows", "mfma-att-5rows-lookahead", "mfma-att-8tiles",
+        "mfma-att-8tiles-10rows"])
 def test_bf16_attention_shapes(cfg):
     _run_staggered(cfg, cfg.chunks, 4)
 
