@@ -119,7 +119,8 @@ size_t cac_state_floats(const cac_config* cfg);
 int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t n_params,
                            void* d_workspace, size_t ws_bytes, void* hip_stream, cac_ctx** out);
 
-/* Push one chunk for n_streams streams (ids in h_stream_ids, distinct, in [0, max_streams)).
+/* Push one chunk for n_streams streams (1 <= n_streams <= max_streams; ids in h_stream_ids,
+ * distinct, in [0, max_streams)); an empty call (n_streams 0) is CAC_EINVAL and changes nothing.
  *   exact variant: d_input is [n_streams][n_frames][D] (or [n_streams][mel_per_chunk][mel_bins]
  *     log-mel with the front end, n_frames = mel_per_chunk/8), in the compute dtype (float32 or
  *     bf16); n_frames a multiple of att_chunk, <= max_push_frames (front end: exactly 2).

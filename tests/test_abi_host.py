@@ -102,6 +102,9 @@ def test_push_validation_and_positions():
     assert push(enc, [-1], 2)[0] == CAC_EINVAL
     assert push(enc, [1, 1], 2)[0] == CAC_EINVAL          # duplicate id
     assert b"twice" in enc.lib.cac_last_error(enc.ctx)
+    assert push(enc, [], 2)[0] == CAC_EINVAL              # empty call
+    assert push(enc, [0, 1, 2, 3, 0], 2)[0] == CAC_EINVAL  # more ids than max_streams
+    assert b"count" in enc.lib.cac_last_error(enc.ctx)
     assert enc.stream_info(1).pos == 2                     # failed calls change nothing
     assert push(enc, [3, 0], 4)[0] == CAC_ENODEV
     assert enc.stream_info(0).pos == 6 and enc.stream_info(3).pos == 4
