@@ -93,7 +93,7 @@ def cpu_baseline(cfg, W, seconds: float):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the chunk step shards by stream with no "
+        print(json.dumps({"error": "the benchmark runs on one GPU: the chunk step shards by stream with no "
                                    "collectives, so N GPUs run N independent copies; --gpus must be 1"}))
         sys.exit(2)
     import torch
