@@ -186,6 +186,7 @@ struct GemmArgs {
   const float* res_b;
   int upb;               // small-M kernel: output units (columns, or GLU channels) per block
   int ksplit;            // MFMA kernel with EPI_PART: K in ksplit equal ranges (0 or 1: one)
+  int xrg;               // MFMA kernel, set by its dispatch: XCD tile rectangles (see there)
   EpiArgs epi;
 };
 
