@@ -135,6 +135,8 @@ enum EpiKind {
                    // ring -> out_t[m][c] (compute dtype); two-row kernel only (GemmArgs dw_*)
   EPI_PART = 8,    // part[z][m][n] = acc over k-range z (float32, no bias): split-K partial of
                    // the MFMA kernel, summed by resid_ln (GemmArgs ksplit, EpiArgs pstride)
+  EPI_SILU_KEEP = 9,  // EPI_SILU with write-back stores that leave the rows in L2 (MFMA kernel;
+                      // the other kernels take it as EPI_SILU)
 };
 
 // GLU packing of the pointwise-1 weight rows: packed row (c / 32) * 64 + c % 32 holds value

@@ -522,9 +522,14 @@ template <int BM, int BN> constexpr int mfma_stages() { return BM * BN <= 64 * 6
 // Epilogue stores are non-temporal: the product's output is read by the next kernel, after the
 // kernel boundary has written the L2 back anyway, so streaming it past the L2 saves that
 // write-back at the end of the kernel (measured: ~3 us of a 13 us 2048x2048x512 product).
+// The exception (EPI_SILU_KEEP) is an output whose consumer runs its rows on the same XCD and
+// is bound by reading them: there the write-back pays for itself.
 __device__ __forceinline__ void st_bf8(bf16_t* p, const float* y) {
   __builtin_nontemporal_store(u32x4_v{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]), pack_bf2(y[4], y[5]), pack_bf2(y[6], y[7])},
                               (u32x4_v*)p);
+}
+__device__ __forceinline__ void st_bf8_keep(bf16_t* p, const float* y) {
+  *(u32x4_v*)p = u32x4_v{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]), pack_bf2(y[4], y[5]), pack_bf2(y[6], y[7])};
 }
 __device__ __forceinline__ void ld_f8(const float* p, float* v) {
   const f32x4_v a = ((const f32x4_v*)p)[0], b = ((const f32x4_v*)p)[1];
@@ -547,10 +552,11 @@ __device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, f
   }
   if constexpr (EK == EPI_STORE) {
     st_bf8((bf16_t*)e.out + (long)row * e.ldo + col, v);
-  } else if constexpr (EK == EPI_SILU) {
+  } else if constexpr (EK == EPI_SILU || EK == EPI_SILU_KEEP) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = silu_f(v[q]);
-    st_bf8((bf16_t*)e.out + (long)row * e.ldo + col, v);
+    if constexpr (EK == EPI_SILU_KEEP) st_bf8_keep((bf16_t*)e.out + (long)row * e.ldo + col, v);
+    else st_bf8((bf16_t*)e.out + (long)row * e.ldo + col, v);
   } else if constexpr (EK == EPI_RELU_FE) {
     const int s = row / e.fe_rows_per_stream, j = row - s * e.fe_rows_per_stream;
     const bool before_start = e.cv.cpos[s] == 0 && j < e.fe_neg_rows;
@@ -989,6 +995,7 @@ static const void* mfma_pick_epi(int ek) {
   switch (ek) {
     case EPI_STORE: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_STORE>;
     case EPI_SILU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_SILU>;
+    case EPI_SILU_KEEP: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_SILU_KEEP>;
     case EPI_RELU_FE: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RELU_FE>;
     case EPI_RESID: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RESID>;
     case EPI_F32: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_F32>;
@@ -1058,7 +1065,11 @@ __global__ __launch_bounds__(256) void cvt_kernel(CvtArgs a) {
   ((bf16_t*)a.y)[idx] = f2bf(a.x[a.amap.off(m) + k]);
 }
 
-void launch_gemm(Launcher& L, const GemmArgs& a, int dtype, int path) {
+void launch_gemm(Launcher& L, const GemmArgs& a0, int dtype, int path) {
+  GemmArgs a = a0;
+  // only the MFMA kernel keeps its SiLU rows in L2; the others store EPI_SILU as usual
+  const bool mfma = dtype != DT_F32 && path != 1 && !(path == 0 && a.M <= 8) && a.K % 64 == 0;
+  if (a.epi.kind == EPI_SILU_KEEP && !mfma) a.epi.kind = EPI_SILU;
   if (path == 0 && rowdot_launch(L, a, dtype)) return;
   if (a.epi.kind == EPI_GLU_DW) {  // only the two-row kernel has this epilogue
     if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
