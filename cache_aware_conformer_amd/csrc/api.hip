@@ -301,7 +301,15 @@ struct Pass {
     while (s < 4 && tiles * s < 256 && K % (64 * 2 * s) == 0 && K / (2 * s) >= 128) s *= 2;
     return s;
   }
-  void row_kernel(const ResLnArgs& r) {
+  // From 2048 rows the residual rows stay in the L2 of the XCD that owns them: the residual
+  // product writes x back (EPI_RESID_KEEP), the row kernel works on the same XCD's eighth of the
+  // rows and writes y back, and the next product reads its A rows there (measured: 1024 streams
+  // 2.817 -> 2.700 ms per step, lookahead 4.353 -> 4.151 ms; at 512 rows, where the residual
+  // products write split-K partials, 0.35% slower, so it stays off there).
+  bool keep_rows() const { return M >= 2048; }
+  void row_kernel(const ResLnArgs& r0) {
+    ResLnArgs r = r0;
+    r.keep = keep_rows();
     if (!launch_resid_ln(L, r, c->d.dt) && L.err == hipSuccess) L.err = hipErrorInvalidValue;
   }
   // cur += alpha (A W^T + bias), then cur = LN(cur; go, bo) when go, then y = LN(cur; gn, bn)
@@ -320,7 +328,7 @@ struct Pass {
       g.ksplit = ks;
       r.part = c->P<float>(c->lay.part); r.pstride = e.pstride; r.nparts = ks; r.bias = bias; r.alpha = alpha;
     } else {
-      e.kind = EPI_RESID; e.bias = bias; e.out = cur; e.ldo = d.D; e.alpha = alpha;
+      e.kind = keep_rows() ? EPI_RESID_KEEP : EPI_RESID; e.bias = bias; e.out = cur; e.ldo = d.D; e.alpha = alpha;
     }
     g.epi = e;
     L.role = role;

@@ -137,6 +137,7 @@ enum EpiKind {
                    // the MFMA kernel, summed by resid_ln (GemmArgs ksplit, EpiArgs pstride)
   EPI_SILU_KEEP = 9,  // EPI_SILU with write-back stores that leave the rows in L2 (MFMA kernel;
                       // the other kernels take it as EPI_SILU)
+  EPI_RESID_KEEP = 10,  // EPI_RESID likewise
 };
 
 // GLU packing of the pointwise-1 weight rows: packed row (c / 32) * 64 + c % 32 holds value
@@ -217,6 +218,7 @@ struct ResLnArgs {
   const float* bn;
   void* y;            // [M][D] compute dtype (null: not written)
   int M, D;
+  int keep;           // rows in XCD-contiguous eighths and y by write-back stores (see the kernel)
 };
 
 struct AttnArgs {

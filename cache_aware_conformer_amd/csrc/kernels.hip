@@ -563,13 +563,18 @@ __device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, f
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = before_start ? 0.0f : fmaxf(v[q], 0.0f);
     st_bf8((bf16_t*)e.out + (long)row * e.ldo + col, v);
-  } else if constexpr (EK == EPI_RESID) {
+  } else if constexpr (EK == EPI_RESID || EK == EPI_RESID_KEEP) {
     float* x = (float*)e.out + (long)row * e.ldo + col;
     float r[8];
     ld_f8(x, r);
 #pragma unroll
     for (int q = 0; q < 8; ++q) r[q] += e.alpha * v[q];
-    st_f8(x, r);
+    if constexpr (EK == EPI_RESID_KEEP) {
+      ((f32x4_v*)x)[0] = f32x4_v{r[0], r[1], r[2], r[3]};
+      ((f32x4_v*)x)[1] = f32x4_v{r[4], r[5], r[6], r[7]};
+    } else {
+      st_f8(x, r);
+    }
   } else if constexpr (EK == EPI_F32) {
     const long ro = e.omap ? (long)e.omap[row / e.ogroup] * e.ostride + row % e.ogroup : row;
     st_f8((float*)e.out + ro * e.ldo + col, v);
@@ -847,9 +852,13 @@ __device__ __forceinline__ void row_layernorm(f32x4_v* v, const f32x4_v* g, cons
   for (int j = 0; j < NV; ++j) v[j] = (v[j] - mean) * rstd * g[j] + b[j];
 }
 
-template <typename TO, int NP, int NV>
+// KEEP: block L takes rows of the XCD-contiguous eighth L mod 8 (the dense products give each
+// XCD such an eighth of their rows), and y goes out by write-back stores, so the x rows the
+// residual product just wrote and the y rows the next product reads stay in one XCD's L2.
+template <typename TO, int NP, int NV, bool KEEP>
 __global__ __launch_bounds__(256) void resid_ln_kernel(ResLnArgs a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int blk = KEEP ? (int)(blockIdx.x % 8) * (int)(gridDim.x / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const int row = blk * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (row >= a.M) return;
   const long ro = (long)row * a.D;
   float* x = a.x + ro;
@@ -892,34 +901,44 @@ __global__ __launch_bounds__(256) void resid_ln_kernel(ResLnArgs a) {
   if (a.y) {
     if (a.gn) row_layernorm<NV>(xv, gnv, bnv, inv_d);
     TO* y = (TO*)a.y + ro;
+    if constexpr (KEEP && sizeof(TO) == 2) {
+      typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_v;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) st4<TO>(y + (j * 64 + lane) * 4, xv[j].x, xv[j].y, xv[j].z, xv[j].w);
+      for (int j = 0; j < NV; ++j)
+        *(u32x2_v*)(y + (j * 64 + lane) * 4) = u32x2_v{pack_bf2(xv[j].x, xv[j].y), pack_bf2(xv[j].z, xv[j].w)};
+    } else {
+#pragma unroll
+      for (int j = 0; j < NV; ++j) st4<TO>(y + (j * 64 + lane) * 4, xv[j].x, xv[j].y, xv[j].z, xv[j].w);
+    }
   }
 }
 
-template <typename TO, int NP>
+template <typename TO, int NP, bool KEEP>
 static const void* resid_ln_pick_nv(int nv) {
   switch (nv) {
-    case 1: return (const void*)&resid_ln_kernel<TO, NP, 1>;
-    case 2: return (const void*)&resid_ln_kernel<TO, NP, 2>;
-    case 3: return (const void*)&resid_ln_kernel<TO, NP, 3>;
-    case 4: return (const void*)&resid_ln_kernel<TO, NP, 4>;
+    case 1: return (const void*)&resid_ln_kernel<TO, NP, 1, KEEP>;
+    case 2: return (const void*)&resid_ln_kernel<TO, NP, 2, KEEP>;
+    case 3: return (const void*)&resid_ln_kernel<TO, NP, 3, KEEP>;
+    case 4: return (const void*)&resid_ln_kernel<TO, NP, 4, KEEP>;
     default: return nullptr;
   }
 }
-template <typename TO>
+template <typename TO, bool KEEP>
 static const void* resid_ln_pick(int np, int nv) {
   switch (np) {
-    case 0: return resid_ln_pick_nv<TO, 0>(nv);
-    case 2: return resid_ln_pick_nv<TO, 2>(nv);
-    case 4: return resid_ln_pick_nv<TO, 4>(nv);
+    case 0: return resid_ln_pick_nv<TO, 0, KEEP>(nv);
+    case 2: return resid_ln_pick_nv<TO, 2, KEEP>(nv);
+    case 4: return resid_ln_pick_nv<TO, 4, KEEP>(nv);
     default: return nullptr;
   }
 }
 
 bool launch_resid_ln(Launcher& L, const ResLnArgs& a, int dtype) {
   if (a.D % 256 || a.D > 1024 || a.M < 1) return false;
-  const void* fn = dtype == DT_F32 ? resid_ln_pick<float>(a.nparts, a.D / 256) : resid_ln_pick<bf16_t>(a.nparts, a.D / 256);
+  // the XCD eighths need a whole number of blocks per XCD
+  const bool keep = a.keep && ((a.M + 3) / 4) % 8 == 0;
+  const void* fn = dtype == DT_F32 ? (keep ? resid_ln_pick<float, true>(a.nparts, a.D / 256) : resid_ln_pick<float, false>(a.nparts, a.D / 256))
+                                   : (keep ? resid_ln_pick<bf16_t, true>(a.nparts, a.D / 256) : resid_ln_pick<bf16_t, false>(a.nparts, a.D / 256));
   if (!fn) return false;
   ResLnArgs args = a;
   // algorithmic bytes: none (activations and partials stay in the last-level cache)
@@ -998,6 +1017,7 @@ static const void* mfma_pick_epi(int ek) {
     case EPI_SILU_KEEP: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_SILU_KEEP>;
     case EPI_RELU_FE: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RELU_FE>;
     case EPI_RESID: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RESID>;
+    case EPI_RESID_KEEP: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RESID_KEEP>;
     case EPI_F32: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_F32>;
     case EPI_QKV: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_QKV>;
     case EPI_GLU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_GLU>;
@@ -1067,9 +1087,10 @@ __global__ __launch_bounds__(256) void cvt_kernel(CvtArgs a) {
 
 void launch_gemm(Launcher& L, const GemmArgs& a0, int dtype, int path) {
   GemmArgs a = a0;
-  // only the MFMA kernel keeps its SiLU rows in L2; the others store EPI_SILU as usual
+  // only the MFMA kernel keeps its SiLU / residual rows in L2; the others store as usual
   const bool mfma = dtype != DT_F32 && path != 1 && !(path == 0 && a.M <= 8) && a.K % 64 == 0;
   if (a.epi.kind == EPI_SILU_KEEP && !mfma) a.epi.kind = EPI_SILU;
+  if (a.epi.kind == EPI_RESID_KEEP && !mfma) a.epi.kind = EPI_RESID;
   if (path == 0 && rowdot_launch(L, a, dtype)) return;
   if (a.epi.kind == EPI_GLU_DW) {  // only the two-row kernel has this epilogue
     if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
