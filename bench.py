@@ -1,11 +1,13 @@
 """Throughput of the cache-aware streaming Conformer chunk step on one MI355X.
 
 A step is one push of one chunk for every stream of the workload through the whole path
-(front end if any, 17 blocks, joint projection), inputs already resident in HBM. The default
-workload is the 17-layer d=512 float32 encoder with one stream and 2 frames per chunk
-(1000 chunks). Prints one JSON line.
+(front end if any, 17 blocks, joint projection), inputs already resident in HBM. The headline
+workload is the largest one-GPU configuration: 1024 streams at staggered positions, each
+pushing 16 log-mel frames through the front end and the 17-layer d=512 encoder in bf16 (fp32
+accumulate). The one-stream float32 encoder (the weight-bandwidth-bound case) is measured in
+the same run and reported in the same JSON line under "secondary". Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload C2|C3|C4|C5]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload C4|C2|C3|C5] [--secondary C2|none]
 """
 from __future__ import annotations
 
@@ -13,6 +15,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -30,11 +33,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="C2")
-    ap.add_argument("--profile-steps", type=int, default=50)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 100 for C4/C3/C5, 1000 for C2)")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="C4")
+    ap.add_argument("--secondary", default="C2", help="second workload reported in the same line, or 'none'")
+    ap.add_argument("--profile-steps", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time per CPU-baseline mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first copy a 256 MiB device buffer 4 times (the reference dispatches for "
@@ -51,65 +55,106 @@ def source_hash(files) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel: str):
+def traffic_for(kernel: str, workload: str):
     """HBM bytes per launch (read + write) from the committed counter summary of this kernel
-    family, if it was taken on the current source of that kernel; else None."""
+    family on this workload, if it was taken on the current source of that kernel; else None."""
     path = os.path.join(PROFILES, "pmc_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    ent = rec.get("kernels", {}).get(kernel)
+    ent = rec.get("kernels", {}).get(f"{workload}:{kernel}")
     if not ent or ent.get("source_hash") != source_hash(ent.get("sources", [])):
         return None
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(cfg, W, seconds: float):
-    """The float64 oracle's cached chunk step, timed on the host cores on a bounded prefix of the
-    same stream (streams are independent, so the rate scales to the workload)."""
-    from oracle import Oracle
-    from synth import make_inputs
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def usable_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(cfg, W, seconds: float):
+    """The float64 oracle's cached chunk step as it stands, timed on the host cores, once with
+    one BLAS thread and once with every usable core, on a bounded sample of the workload: for
+    many-stream workloads 32 streams from their staggered states (streams are independent, so
+    the per-stream rate scales to the batch), for one stream that stream; as many chunks as
+    fit in ``seconds`` per mode (at least one)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import Oracle
+    from synth import make_inputs, make_state
     orc = Oracle(cfg, W)
-    n_s = 1 if cfg.streams == 1 else min(cfg.streams, 8)
-    sts = [orc.new_state() for _ in range(n_s)]
-    xs = np.stack([make_inputs(cfg, s, cfg.chunks) for s in range(n_s)])
-    t0 = time.perf_counter()
-    chunks = 0
-    while chunks < cfg.chunks and (time.perf_counter() - t0 < seconds or chunks < 3):
-        orc.push(sts, xs[:, chunks].astype(np.float64))
-        chunks += 1
-    dt = time.perf_counter() - t0
-    frames = n_s * cfg.n_emit * chunks
-    return {"value": frames / dt, "unit": "frames/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{cfg.name}: {n_s} fresh stream(s) x first {chunks} chunks, float64 cached step, {dt:.1f} s"}
+    n_s = min(cfg.streams, 32)
+    ids = list(np.linspace(0, cfg.streams - 1, n_s).astype(int))
+    xs = np.stack([make_inputs(cfg, s, min(cfg.chunks, 200)) for s in ids])
+    modes = {}
+    for name, threads in (("1_thread", 1), ("all_cores", usable_cores())):
+        sts = [orc.state_from(make_state(cfg, s)) if cfg.staggered else orc.new_state() for s in ids]
+        with threadpool_limits(threads):
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+            t0 = time.perf_counter()
+            chunks = 0
+            while chunks < xs.shape[1] and (chunks < 1 or time.perf_counter() - t0 < seconds):
+                orc.push(sts, xs[:, chunks].astype(np.float64))
+                chunks += 1
+            dt = time.perf_counter() - t0
+        frames = n_s * cfg.n_emit * chunks
+        modes[name] = {"value": frames / dt, "threads": int(used), "chunks": chunks, "seconds": dt}
+    best = modes["all_cores"]
+    return {"value": best["value"], "unit": "frames/s", "cores": best["threads"], "kind": "oracle",
+            "cpu_model": cpu_model(), "usable_cores": usable_cores(),
+            "single_thread": {"value": modes["1_thread"]["value"], "cores": 1},
+            "sample": (f"{cfg.name}: {n_s} stream(s){' from staggered states' if cfg.staggered else ''} x "
+                       f"{best['chunks']} chunk(s), float64 cached step; {best['seconds']:.1f} s all-core "
+                       f"({best['threads']} threads), {modes['1_thread']['seconds']:.1f} s on one thread "
+                       f"({modes['1_thread']['chunks']} chunk(s))")}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": "the benchmark runs on one GPU: the chunk step shards by stream with no "
-                                   "collectives, so N GPUs run N independent copies; --gpus must be 1"}))
-        sys.exit(2)
+def roofline_of(enc, fam: str, workload: str, reps: int = 20) -> dict:
+    """Back-to-back launch duration of one kernel family (its launches of the last recorded
+    step, replayed as a graph between HIP events on the library's stream) against its
+    algorithmic work: MFMA-bound when its flops per algorithmic byte exceed the bf16 ridge
+    (312 flop/B), otherwise HBM-bound."""
+    rep = enc.profile_replay(fam, reps=reps)
+    us, kbytes, kflops = rep["us_per_launch"], rep["bytes_per_launch"], rep["flops_per_launch"]
+    if "mfma" in fam and kbytes and kflops / kbytes > 312.0:
+        roof = {"bound": "mfma", "achieved": kflops / (us * 1e-6) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kbytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(fam, workload)
+    roof["kernel"] = fam
+    roof["avg_launch_us"] = us
+    roof["launches_per_step"] = rep["launches"]
+    roof["algorithmic_bytes_per_launch"] = kbytes
+    roof["algorithmic_flops_per_launch"] = kflops
+    return roof
+
+
+def run_workload(key: str, steps, warmup: int, profile_steps: int, want_cpu: bool, cpu_seconds: float,
+                 extra_families=()):
     import torch
 
     from cache_aware_conformer_amd import StreamingEncoder
     from synth import CONFIGS, make_inputs, make_state, make_weights
 
-    if args.calibrate_copy:
-        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(4):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-    cfg = CONFIGS[args.workload]
-    steps = args.steps if args.steps is not None else min(cfg.chunks, 1000)
+    cfg = CONFIGS[key]
+    if steps is None:
+        steps = min(cfg.chunks, 1000) if cfg.streams == 1 else 100
     dev = torch.device("cuda:0")
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     W = make_weights(cfg)
@@ -119,7 +164,8 @@ def main():
         for g0 in range(0, S, 64):
             grp = list(range(g0, min(S, g0 + 64)))
             enc.import_state_dicts(grp, [make_state(cfg, s) for s in grp])
-    per_stream = cfg.chunks
+    # distinct inputs for every pushed chunk up to the workload's length, then cycled
+    per_stream = min(cfg.chunks, warmup + steps + profile_steps + 1)
     # chunk-major [chunks, S, frames, width]: each step's input is one contiguous slab in HBM
     xs = np.ascontiguousarray(np.stack([make_inputs(cfg, s, per_stream) for s in range(S)]).swapaxes(0, 1))
     x_dev = torch.from_numpy(xs).to(dev).to(tdt)
@@ -133,9 +179,11 @@ def main():
         enc.push_chunk(ids, x_dev[k % per_stream], out)
         k += 1
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # the library enqueues on torch's current stream (given at create time), so events recorded
+    # there bracket exactly the pushes
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
@@ -146,61 +194,86 @@ def main():
     ms = e0.elapsed_time(e1)
     frames = S * cfg.n_emit * steps
     value = frames / (ms / 1e3)
+    ms_step = ms / steps
 
     # per-kernel timing over a second window of the same workload
     enc.profile(True)
-    for _ in range(args.profile_steps):
+    for _ in range(profile_steps):
         step()
     torch.cuda.synchronize()
     prof = enc.profile_read()
     enc.profile(False)
-    # kernel families ("gemm_tworow_f32/qkv" -> "gemm_tworow_f32"); the roofline covers the
-    # family that takes the most time. Its launch duration is measured by replaying just that
-    # family's launches of one recorded step back to back (graph, HIP events on the library's
-    # stream); the per-role table above comes from the profiled window, whose dispatch-bound
-    # events add the event markers to every launch.
+    # kernel families ("gemm_mfma_bf16/qkv" -> "gemm_mfma_bf16"); the roofline covers the family
+    # that takes the most time, the others named in extra_families get their own figure
     fam = {}
     for n, v in prof.items():
         f = fam.setdefault(n.split("/")[0], [0, 0.0, 0.0, 0.0])
         for i in range(4):
             f[i] += v[i]
     dom = max(fam, key=lambda n: fam[n][1])
-    rep = enc.profile_replay(dom, reps=20)  # last: leaves the streams' state unspecified
-    us, kbytes, kflops = rep["us_per_launch"], rep["bytes_per_launch"], rep["flops_per_launch"]
-    mfma_bound = "mfma" in dom and kbytes and kflops / kbytes > 312.0
-    if mfma_bound:
-        roof = {"bound": "mfma", "achieved": kflops / (us * 1e-6) / 1e12, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": kbytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_for(dom)
-    roof["kernel"] = dom
-    roof["avg_launch_us"] = us
-    roof["launches_per_step"] = rep["launches"]
-    roof["algorithmic_bytes_per_launch"] = kbytes
-    roof["algorithmic_flops_per_launch"] = kflops
-    step_bytes = sum(v[2] for v in prof.values()) / args.profile_steps
-    step_flops = sum(v[3] for v in prof.values()) / args.profile_steps
-    ms_step = ms / steps
-
+    step()                       # a graph replay: the family replays use its recorded launches
+    torch.cuda.synchronize()
+    others = {f: roofline_of(enc, f, cfg.name) for f in extra_families if f in fam and f != dom}
+    roof = roofline_of(enc, dom, cfg.name)   # leaves the streams' state unspecified
+    step_bytes = sum(v[2] for v in prof.values()) / profile_steps
+    step_flops = sum(v[3] for v in prof.values()) / profile_steps
     res = {
-        "metric": METRIC, "value": value, "unit": "frames/s", "n_gpus": 1, "steps": steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32" if cfg.dtype == "f32" else "bf16", "data": "synthetic",
+        "value": value, "ms_per_step": ms_step, "steps": steps, "warmup": warmup,
+        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
         "config": {"workload": cfg.name, "layers": cfg.n_layers, "d_model": cfg.d_model, "heads": cfg.n_heads,
                    "d_ff": cfg.d_ff, "att_left": cfg.att_left, "streams": S, "frames_per_chunk": cfg.n_emit,
                    "frames_computed_per_chunk": cfg.n_compute, "joint_dim": cfg.joint_dim,
-                   "frontend": cfg.frontend, "parallelism": "none (1 GPU)"},
+                   "frontend": cfg.frontend, "staggered_start": cfg.staggered, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "step": {"algorithmic_bytes": step_bytes, "algorithmic_flops": step_flops,
                  "hbm_frac_of_peak": step_bytes / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS,
+                 "mfma_frac_of_peak": step_flops / (ms_step / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
                  "kernels_note": "dispatch-bound HIP events per launch (include the event markers)",
-                 "kernels": {n: {"launches_per_step": v[0] / args.profile_steps,
-                                 "us_per_step": v[1] / args.profile_steps * 1e3} for n, v in
+                 "kernels": {n: {"launches_per_step": v[0] / profile_steps,
+                                 "us_per_step": v[1] / profile_steps * 1e3} for n, v in
                              sorted(prof.items(), key=lambda kv: -kv[1][1])}},
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, W, args.cpu_seconds)
+    if others:
+        res["rooflines_other"] = others
+    enc.close()
+    del x_dev, out, enc
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if want_cpu:
+        res["cpu_baseline"] = cpu_baseline(cfg, W, cpu_seconds)
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU: the chunk step shards by stream with no "
+                                   "collectives, so N GPUs would run N independent copies; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    head = run_workload(args.workload, args.steps, args.warmup, args.profile_steps, not args.no_cpu_baseline,
+                        args.cpu_seconds, extra_families=("attention",))
+    res = {"metric": METRIC, "value": head["value"], "unit": "frames/s", "n_gpus": 1, "steps": head["steps"],
+           "warmup": head["warmup"], "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
+           "config": head["config"], "roofline": head["roofline"]}
+    for key in ("rooflines_other", "cpu_baseline", "step"):
+        if key in head:
+            res[key] = head[key]
+    if args.secondary and args.secondary.lower() != "none" and args.secondary != args.workload:
+        sec = run_workload(args.secondary, args.steps, args.warmup, args.profile_steps, False, 0.0)
+        res["secondary"] = {sec["config"]["workload"]: {k: sec[k] for k in
+                                                         ("value", "ms_per_step", "steps", "dtype", "config",
+                                                          "roofline", "step")}}
+        res["secondary"][sec["config"]["workload"]]["unit"] = "frames/s"
     print(json.dumps(res))
 
 

@@ -52,6 +52,7 @@ SIGNATURES = {
     "cac_profile": (_i32, [_vp, _i32]),
     "cac_profile_read": (_i32, [_vp, _i32, C.c_char_p, _i32, C.POINTER(C.c_int64), C.POINTER(C.c_double),
                                 C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+    "cac_state_header": (_i32, [_CFGP, C.POINTER(C.c_uint32)]),
     "cac_profile_replay": (_i32, [_vp, C.c_char_p, _i32, C.POINTER(C.c_double), C.POINTER(C.c_int32),
                                   C.POINTER(C.c_double), C.POINTER(C.c_double)]),
 }
@@ -260,11 +261,17 @@ class StreamingEncoder:
         return self._check(self.lib.cac_import_state(self.ctx, ids.size, idp, pos.ctypes.data_as(_ip),
                                                      pend.ctypes.data_as(_ip), bp))
 
+    def state_header(self) -> np.ndarray:
+        """The 4-word state-blob header of this context's config, as 4 float32 slots."""
+        h = np.zeros(4, dtype=np.uint32)
+        self._check(self.lib.cac_state_header(C.byref(self.c), h.ctypes.data_as(C.POINTER(C.c_uint32))))
+        return h.view(np.float32)
+
     def state_blob(self, st: dict) -> np.ndarray:
         """Canonical float32 state blob (header layout) of one stream from a dict with keys
         k, v [L][Lc][D], conv [L][K-1][D], mel_tail (front end), x0_tail (lookahead)."""
-        parts = [np.asarray(st["k"], np.float32).reshape(-1), np.asarray(st["v"], np.float32).reshape(-1),
-                 np.asarray(st["conv"], np.float32).reshape(-1)]
+        parts = [self.state_header(), np.asarray(st["k"], np.float32).reshape(-1),
+                 np.asarray(st["v"], np.float32).reshape(-1), np.asarray(st["conv"], np.float32).reshape(-1)]
         if self.cfg.frontend:
             parts.append(np.asarray(st["mel_tail"], np.float32).reshape(-1))
         if self.cfg.n_lookahead:

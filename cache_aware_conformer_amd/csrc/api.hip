@@ -169,7 +169,25 @@ size_t param_count(const Dims& d) {
 }
 
 size_t state_floats(const Dims& d) {
-  return 2 * (size_t)d.L * d.Lc * d.D + (size_t)d.L * d.Kc * d.D + (size_t)d.tail * d.bins + (size_t)d.nla * d.D;
+  return STATE_HDR + 2 * (size_t)d.L * d.Lc * d.D + (size_t)d.L * d.Kc * d.D + (size_t)d.tail * d.bins +
+         (size_t)d.nla * d.D;
+}
+
+// Header of a stream's state blob: magic, layout version, and a 64-bit FNV-1a hash of every
+// config field that defines the model and the state's meaning (all but max_streams,
+// max_push_frames and flags), taken after make_dims' normalisation.
+void state_header(const Dims& d, uint32_t out[STATE_HDR]) {
+  const int32_t f[] = {d.L, d.D, d.H, d.F, d.K, d.Lc, d.c, d.right, d.ne, d.nla, d.P, d.fe, d.bins, d.mpc, d.tail, d.dt};
+  uint64_t h = 1469598103934665603ull;
+  for (int32_t v : f)
+    for (int b = 0; b < 4; ++b) {
+      h ^= (uint64_t)(((uint32_t)v >> (8 * b)) & 0xffu);
+      h *= 1099511628211ull;
+    }
+  out[0] = STATE_MAGIC;
+  out[1] = STATE_VERSION;
+  out[2] = (uint32_t)h;
+  out[3] = (uint32_t)(h >> 32);
 }
 
 // ------------------------------------------------------------------------------- host packing
@@ -571,7 +589,17 @@ StateArgs state_args(cac_ctx* c, int n) {
   sa.Lc = d.Lc; sa.Kc = d.Kc; sa.tail_rows = d.tail; sa.bins = d.bins; sa.nla = d.nla; sa.Rx = d.Rx;
   sa.state_floats = (long)state_floats(d);
   sa.dtype = d.dt; sa.poison = (d.flags & CAC_FLAG_POISON) ? 1 : 0;
+  state_header(d, sa.hdr);
   return sa;
+}
+
+// An asynchronous device error left on the context's stream by earlier work is reported at the
+// next call that enqueues work (the query does not wait for the stream).
+int pending_error(cac_ctx* c) {
+  if (c->dry) return CAC_OK;
+  const hipError_t e = hipStreamQuery(c->stream);
+  if (e == hipSuccess || e == hipErrorNotReady) return CAC_OK;
+  return c->fail(CAC_EHIP, std::string("asynchronous device error from earlier work: ") + hipGetErrorString(e));
 }
 
 int finish(cac_ctx* c, Launcher& L, int ok_value) {
@@ -600,6 +628,14 @@ size_t cac_state_floats(const cac_config* cfg) {
   Dims d;
   std::string why;
   return make_dims(cfg, d, why) ? state_floats(d) : 0;
+}
+
+int32_t cac_state_header(const cac_config* cfg, uint32_t* h_out) {
+  Dims d;
+  std::string why;
+  if (!h_out || !make_dims(cfg, d, why)) return CAC_EINVAL;
+  state_header(d, h_out);
+  return CAC_OK;
 }
 
 const char* cac_last_error(const cac_ctx* ctx) {
@@ -817,7 +853,8 @@ std::vector<size_t> find_ptr(const std::vector<char>& args, const void* p) {
 // nodes that hold the caller's input and output pointers.
 hipError_t push_graph(cac_ctx* c, int n, const int32_t* ids, int n_frames, const void* d_input, float* d_out,
                       const std::vector<int32_t>& cids) {
-  const uint64_t key = ((uint64_t)n << 32) | ((uint64_t)n_frames << 16) | (uint64_t)cids.size();
+  // 21 bits per field: stream counts up to 2^20 (make_dims' limit), frames up to 16
+  const uint64_t key = ((uint64_t)n << 42) | ((uint64_t)n_frames << 21) | (uint64_t)cids.size();
   auto it = c->graphs.find(key);
   if (it == c->graphs.end()) {
     cac_ctx::Graph gr;
@@ -878,6 +915,7 @@ int32_t cac_push_chunk(cac_ctx* c, int32_t n, const int32_t* ids, int32_t n_fram
   }
   if (!d_input || !d_out) return c->fail(CAC_EINVAL, "input or output pointer is NULL");
   if ((const void*)d_out == d_input) return c->fail(CAC_EINVAL, "input and output must be different buffers");
+  if ((rc = pending_error(c))) return rc;
 
   // host bookkeeping decides who runs a pass (lookahead: streams whose pending frames reach
   // n_emit + n_lookahead after this push)
@@ -957,6 +995,7 @@ int32_t cac_flush(cac_ctx* c, int32_t n, const int32_t* ids, float* d_out, int32
   if (d.lookahead)
     for (int i = 0; i < n; ++i) maxm = std::max(maxm, c->hpend[ids[i]]);
   if (maxm > 0 && !d_out) return c->fail(CAC_EINVAL, "output pointer is NULL");
+  if ((rc = pending_error(c))) return rc;
   auto commit = [&]() {
     for (int i = 0; i < n; ++i) {
       const int id = ids[i];
@@ -1039,6 +1078,27 @@ int32_t cac_import_state(cac_ctx* c, int32_t n, const int32_t* ids, const int32_
       if (h_pending[i] < 0 || h_pending[i] > d.nla) return c->fail(CAC_ESTATE, "pending count out of [0, n_lookahead]");
       pend[i] = h_pending[i];
     }
+  }
+  // every stream's blob must carry this config's header (dry-run contexts read it from host
+  // memory, since they make no device calls)
+  const size_t sf = state_floats(d);
+  std::vector<uint32_t> hdrs((size_t)n * STATE_HDR);
+  if (c->dry) {
+    for (int i = 0; i < n; ++i) memcpy(&hdrs[(size_t)i * STATE_HDR], d_state + (size_t)i * sf, STATE_HDR * 4);
+  } else {
+    hipError_t e = hipMemcpy2DAsync(hdrs.data(), STATE_HDR * 4, d_state, sf * 4, STATE_HDR * 4, n,
+                                    hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("reading the state headers failed: ") + hipGetErrorString(e));
+  }
+  uint32_t want[STATE_HDR];
+  state_header(d, want);
+  for (int i = 0; i < n; ++i) {
+    const uint32_t* h = &hdrs[(size_t)i * STATE_HDR];
+    if (h[0] != want[0] || h[1] != want[1])
+      return c->fail(CAC_ESTATE, "state blob " + std::to_string(i) + " has no state header of this layout version");
+    if (h[2] != want[2] || h[3] != want[3])
+      return c->fail(CAC_ESTATE, "state blob " + std::to_string(i) + " was made with a different config");
   }
   if (c->dry) return c->fail(CAC_ENODEV, "dry-run context: no device work");
   Launcher L;

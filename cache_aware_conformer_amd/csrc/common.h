@@ -289,6 +289,12 @@ struct PosProjArgs {    // table[l][h][r][d] = sum_e PE(rel_lo + r, e) Wpos_l[e]
   int L, D, H, hd, rel_lo, nrel;
 };
 
+// Every stream's state blob starts with STATE_HDR 32-bit words: STATE_MAGIC, STATE_VERSION and
+// a 64-bit hash of the config it was made with (written on export, checked on import).
+constexpr int STATE_HDR = 4;
+constexpr uint32_t STATE_MAGIC = 0x53434143u;  // "CACS"
+constexpr uint32_t STATE_VERSION = 1u;
+
 struct StateArgs {      // reset / import / export of whole streams
   const int32_t* ids;   // [n]
   const int32_t* hpos;  // [n] positions (import) ; out for export via pos array
@@ -298,8 +304,9 @@ struct StateArgs {      // reset / import / export of whole streams
   void* kring; void* vring; void* cring; void* tail; void* x0;  // whole state regions
   float* blob;          // [n][state_floats]
   int n, S, L, D, H, hd, R, Rc, Lc, Kc, tail_rows, bins, nla, Rx;
-  long state_floats;
+  long state_floats;     // per stream, header included
   int dtype, poison;
+  uint32_t hdr[STATE_HDR];  // header export writes
 };
 
 struct LaStoreArgs {    // lookahead: append new frames to each stream's pending ring

@@ -1865,18 +1865,21 @@ __global__ __launch_bounds__(256) void state_reset_kernel(StateArgs a) {
   if (blockIdx.x == 0 && threadIdx.x == 0) { a.pos[id] = 0; a.pend[id] = 0; }
 }
 
-// Canonical blob of one stream (floats): K [L][Lc][D], V [L][Lc][D], conv [L][Kc][D],
-// tail [tail_rows][bins], x0 [nla][D].
+// Canonical blob of one stream (floats): header [STATE_HDR] (32-bit words), K [L][Lc][D],
+// V [L][Lc][D], conv [L][Kc][D], tail [tail_rows][bins], x0 [nla][D]. Export writes the
+// header; import leaves it to the host, which has checked it.
 template <typename T, bool IMPORT>
 __global__ __launch_bounds__(256) void state_xfer_kernel(StateArgs a) {
   const int s = blockIdx.y;
   const int id = a.ids[s];
   const int pos = a.hpos[s];
   const int pend = a.hpend ? a.hpend[s] : 0;
-  float* blob = a.blob + (long)s * a.state_floats;
+  float* blob = a.blob + (long)s * a.state_floats + STATE_HDR;
+  if (!IMPORT && blockIdx.x == 0 && threadIdx.x < STATE_HDR) ((uint32_t*)blob)[(int)threadIdx.x - STATE_HDR] = a.hdr[threadIdx.x];
   const long kvn = (long)a.L * a.Lc * a.D, cvn = (long)a.L * a.Kc * a.D;
-  const long tln = (long)a.tail_rows * a.bins, x0n = (long)a.nla * a.D;
-  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < a.state_floats; e += (long)gridDim.x * 256) {
+  const long tln = (long)a.tail_rows * a.bins;
+  const long body = a.state_floats - STATE_HDR;
+  for (long e = (long)blockIdx.x * 256 + threadIdx.x; e < body; e += (long)gridDim.x * 256) {
     long r = e;
     T* dst = nullptr;
     bool valid = false;
@@ -1986,7 +1989,8 @@ void kernels_init() {
       fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 2>(kch, glu));
       fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 8>(kch, glu));
     }
-  for (int ek : {EPI_STORE, EPI_SILU, EPI_RELU_FE, EPI_RESID, EPI_F32, EPI_QKV, EPI_GLU, EPI_PART}) {
+  for (int ek : {EPI_STORE, EPI_SILU, EPI_SILU_KEEP, EPI_RELU_FE, EPI_RESID, EPI_RESID_KEEP, EPI_F32, EPI_QKV, EPI_GLU,
+                 EPI_PART}) {
     fns.push_back(mfma_pick_epi<128, 128, 2, 2>(ek));
     fns.push_back(mfma_pick_epi<128, 64, 4, 1>(ek));
     fns.push_back(mfma_pick_epi<64, 128, 2, 2>(ek));

@@ -1,6 +1,7 @@
 // Dense products of at most two rows: one stream's chunk of two frames (or two streams of one
 // frame each), the shape every dense layer of a single-stream chunk step has
-// (Conformer, Sec. 2: feed-forward, self-attention projections, convolution module).
+// ("True streaming encode — implementation spec", "Per-chunk flow", step 3: FF1, the
+// attention projections, the conv module and FF2 of every layer).
 //
 // At two rows a product is a pass over the weight matrix: each wave owns one or two output
 // units (a column, or a GLU value/gate column pair) and reads their weight rows once, 16 bytes

@@ -20,9 +20,12 @@
  *   - All device work is enqueued on the HIP stream given at create time (or by
  *     cac_set_stream); no call synchronises the host except where stated. Outputs are valid
  *     once that stream has been synchronised.
- *   - The library never allocates device memory: the caller provides one workspace of
+ *   - The context calls never allocate device memory: the caller provides one workspace of
  *     cac_workspace_bytes() bytes that holds the repacked weights, every stream's state and
- *     all activations. The library keeps a pointer to it until cac_destroy.
+ *     all activations. The library keeps a pointer to it until cac_destroy. (The test-only
+ *     cac_test_gemm is the one exception; it says so below.)
+ *   - A call that enqueues device work first checks the context's stream for an asynchronous
+ *     error left by earlier work (without waiting for it) and returns CAC_EHIP if there is one.
  *   - Arguments are validated on the host before any device work; on error nothing is
  *     enqueued and the context is unchanged. cac_last_error() then describes the failure.
  *   - One context is used by one host thread at a time; there is no internal locking.
@@ -42,9 +45,11 @@ extern "C" {
 #define CAC_EINVAL (-1)  /* bad config or argument: null pointer, id out of range, duplicate id
                             in one call, n not a multiple of att_chunk, too many frames */
 #define CAC_ESTATE (-2)  /* stream state forbids the call: push to a flushed stream (reset it
-                            first), state import that does not fit the config */
+                            first), state import that does not fit the config (a blob made
+                            with another config, a position or pending count out of range) */
 #define CAC_ENOMEM (-3)  /* workspace smaller than cac_workspace_bytes() */
-#define CAC_EHIP (-4)    /* a HIP runtime call or a kernel launch failed */
+#define CAC_EHIP (-4)    /* a HIP runtime call or a kernel launch failed, or an asynchronous
+                            device error from earlier work was found on the context's stream */
 #define CAC_ENODEV (-5)  /* the context was created with CAC_FLAG_DRY_RUN: no device work */
 
 /* compute dtype of GEMM operands and caches (residual stream, LayerNorm, softmax, GLU and the
@@ -102,12 +107,21 @@ size_t cac_param_count(const cac_config* cfg);
 size_t cac_workspace_bytes(const cac_config* cfg);
 
 /* Floats per stream in the canonical state blob of cac_export_state / cac_import_state:
+ *   header[4]  four 32-bit words (not floats): magic 0x53434143, layout version 1 and a 64-bit
+ *              hash of the config (cac_state_header); export writes it, import rejects a blob
+ *              whose header differs from the context's with CAC_ESTATE
  *   K[n_layers][att_left][D], V[n_layers][att_left][D]   row r = position pos-att_left+r
  *   conv[n_layers][dw_kernel-1][D]                       column j = position pos-(K-1)+j
  *   mel_tail[mel_tail][mel_bins]                         (frontend only)
  *   x0[n_lookahead][D]  pending layer-0 inputs, row j = position pos+j (lookahead only)
  * Rows of positions before 0 are ignored on import and written as 0 on export. */
 size_t cac_state_floats(const cac_config* cfg);
+
+/* The 4-word state-blob header of cfg (h_out: 4 uint32, host): magic, version and the 64-bit
+ * FNV-1a hash of every config field except max_streams, max_push_frames and flags. Callers
+ * that build a state blob themselves put it in front of each stream's floats. Returns CAC_OK,
+ * or CAC_EINVAL for an invalid config or a NULL h_out. */
+int32_t cac_state_header(const cac_config* cfg, uint32_t* h_out);
 
 /* Validate cfg, repack the float32 host parameters (h_params, cac_param_count floats) into the
  * workspace in the compute layout (bf16 rounding to nearest even for CAC_BF16), compute each
@@ -149,7 +163,10 @@ int32_t cac_flush(cac_ctx* ctx, int32_t n, const int32_t* h_stream_ids, float* d
 /* Copy the state of n streams into / from the canonical float32 layout (cac_state_floats per
  * stream, d_state is [n][cac_state_floats] device memory). h_pos: stream positions (frames
  * emitted); h_pending: pending layer-0 inputs of the lookahead variant (ignored otherwise,
- * may be NULL then). Import requires 0 <= pending <= n_lookahead. */
+ * may be NULL then). Import requires 0 <= pending <= n_lookahead and the context's header in
+ * front of every stream's blob; it reads those headers (one small device-to-host copy) and
+ * rejects the whole call with CAC_ESTATE, changing nothing, if any differs. A dry-run context
+ * reads d_state as host memory. Both calls synchronise the context's stream. */
 int32_t cac_export_state(cac_ctx* ctx, int32_t n, const int32_t* h_stream_ids, int32_t* h_pos,
                          int32_t* h_pending, float* d_state);
 int32_t cac_import_state(cac_ctx* ctx, int32_t n, const int32_t* h_stream_ids,
@@ -213,8 +230,8 @@ const char* cac_last_error(const cac_ctx* ctx);
  * (MFMA paths: bf16 only, K a multiple of 64), 7 / 8 = the 64x64 MFMA kernel with K split in
  * 2 / 4 ranges whose float32 partials the residual row kernel sums with the bias (K a multiple
  * of 128 / 256, N a multiple of 256 up to 1024; allocates and frees a temporary partial buffer
- * and returns after the stream has drained). Enqueued on hip_stream; CAC_EINVAL for shapes a
- * path does not take. */
+ * with hipMalloc / hipFree, the one allocation in the library, and returns after the stream has
+ * drained). Enqueued on hip_stream; CAC_EINVAL for shapes a path does not take. */
 int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t K,
                       const void* d_A, const void* d_W, const float* d_bias, float* d_C,
                       void* hip_stream);

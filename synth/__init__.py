@@ -12,5 +12,6 @@ from .gen import (  # noqa: F401
     make_inputs,
     make_state,
     make_token_head,
+    state_position,
     weight_names,
 )

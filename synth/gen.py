@@ -121,6 +121,14 @@ def make_inputs(cfg: EncConfig, stream: int, chunks: int | None = None) -> np.nd
     return x if chunks is None else x[:chunks]
 
 
+def state_position(cfg: EncConfig, stream: int) -> int:
+    """Position of the injected state of one stream (see ``make_state``), drawn alone."""
+    g = _rng(cfg, f"state.s{stream}.pos")
+    c, Lc = cfg.att_chunk, cfg.att_left
+    fill = c * int(g.integers(0, Lc // c + 1))
+    return fill if fill < Lc else Lc + c * int(g.integers(0, 5001))
+
+
 def make_state(cfg: EncConfig, stream: int) -> dict:
     """Injected mid-stream state of one stream (staggered workloads).
 
@@ -138,10 +146,7 @@ def make_state(cfg: EncConfig, stream: int) -> dict:
       pos .. pos+n_lookahead-1 (lookahead variant only).
     """
     L, Lc, D, Kc = cfg.n_layers, cfg.att_left, cfg.d_model, cfg.conv_cache
-    g = _rng(cfg, f"state.s{stream}.pos")
-    c = cfg.att_chunk
-    fill = c * int(g.integers(0, Lc // c + 1))
-    pos = fill if fill < Lc else Lc + c * int(g.integers(0, 5001))
+    pos = state_position(cfg, stream)
     fill = min(pos, Lc)
     k = _draw_unit(cfg, f"state.s{stream}.k", (L, Lc, D))
     v = _draw_unit(cfg, f"state.s{stream}.v", (L, Lc, D))

@@ -1,0 +1,88 @@
+"""Oracle runs of many independent streams in worker processes.
+
+The float64 oracle spends most of its time in per-stream Python work (attention and the
+depthwise conv run stream by stream), so whole-workload parity (every stream of a
+256- or 1024-stream batch) splits the streams into groups and runs the groups in parallel.
+The workers are started with the "spawn" method: fresh interpreters that import only numpy,
+``oracle`` and ``synth``, never a copy of a process that holds the GPU. Each worker keeps the
+oracle of the last configuration it saw.
+"""
+from __future__ import annotations
+
+import multiprocessing as mp
+import os
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+_POOL = None
+_WORKERS = max(1, min(8, os.cpu_count() or 1))
+_CACHE = {}
+
+
+def _init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(2)
+    except Exception:  # pragma: no cover
+        pass
+
+
+def pool() -> ProcessPoolExecutor:
+    global _POOL
+    if _POOL is None:
+        _POOL = ProcessPoolExecutor(max_workers=_WORKERS, mp_context=mp.get_context("spawn"), initializer=_init)
+    return _POOL
+
+
+def _oracle(cfg):
+    from oracle import Oracle
+    from synth import make_weights
+    if cfg not in _CACHE:
+        _CACHE.clear()
+        _CACHE[cfg] = Oracle(cfg, make_weights(cfg))
+    return _CACHE[cfg]
+
+
+def _run_group(cfg, ids, chunks, staggered, flush):
+    """Oracle outputs of streams ``ids`` (their seeded inputs) over ``chunks`` pushes, from
+    their injected states or fresh; optionally followed by a flush of each stream."""
+    from synth import make_inputs, make_state
+    orc = _oracle(cfg)
+    sts = [orc.state_from(make_state(cfg, s)) if staggered else orc.new_state() for s in ids]
+    xs = np.stack([make_inputs(cfg, s, chunks) for s in ids])
+    outs = [orc.push(sts, xs[:, c].astype(np.float64)) for c in range(chunks)]
+    fl = [orc.flush(st) for st in sts] if flush else None
+    return outs, fl
+
+
+def submit_streams(cfg, ids, chunks, staggered=True, flush=False, group=None):
+    """Start the oracle runs of ``ids``; returns a handle for ``collect``."""
+    ids = list(ids)
+    if group is None:
+        group = max(1, -(-len(ids) // (2 * _WORKERS)))
+    groups = [ids[i:i + group] for i in range(0, len(ids), group)]
+    futs = [pool().submit(_run_group, cfg, g, chunks, staggered, flush) for g in groups]
+    return groups, futs, chunks, flush
+
+
+def collect(handle):
+    """Per-chunk oracle outputs [len(ids), m, P] (m = frames emitted by that push) in the order
+    of the submitted ids, and the flush outputs (a list, or None)."""
+    groups, futs, chunks, flush = handle
+    per_chunk = [[] for _ in range(chunks)]
+    flushed = [] if flush else None
+    for fut in futs:
+        outs, fl = fut.result()
+        for c in range(chunks):
+            per_chunk[c].append(outs[c])
+        if flush:
+            flushed += fl
+    return [np.concatenate(p, axis=0) for p in per_chunk], flushed
+
+
+def shutdown():
+    global _POOL
+    if _POOL is not None:
+        _POOL.shutdown(wait=True, cancel_futures=True)
+        _POOL = None

@@ -47,7 +47,7 @@ def test_param_and_state_layouts(cfg):
     expect = 2 * L * Lc * D + L * (cfg.dw_kernel - 1) * D
     expect += cfg.mel_tail * cfg.mel_bins if cfg.frontend else 0
     expect += cfg.n_lookahead * D
-    assert lib.cac_state_floats(C.byref(c)) == expect
+    assert lib.cac_state_floats(C.byref(c)) == 4 + expect  # 4-word header in front
     assert lib.cac_workspace_bytes(C.byref(c)) > 0
 
 
@@ -161,17 +161,67 @@ def test_frontend_push_is_one_mel_chunk():
     assert push(enc, [0], 2)[0] == CAC_ENODEV
 
 
+def _blob(enc, n, header=None):
+    """Zero state blobs of n streams with a header (the context's own by default)."""
+    b = np.zeros((n, enc.sfloats), np.float32)
+    b[:, :4] = enc.state_header() if header is None else header
+    return b
+
+
 def test_import_validation():
     enc = dry(C5.replace(n_layers=1, streams=2), streams=2)
     ids = np.array([0], np.int32)
     ip = lambda a: np.asarray(a, np.int32).ctypes.data_as(C.POINTER(C.c_int32))  # noqa: E731
     lib = enc.lib
-    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), ip([9]), C.c_void_p(16)) == CAC_ESTATE
-    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([-2]), ip([8]), C.c_void_p(16)) == CAC_ESTATE
+    blob = _blob(enc, 1)
+    bp = blob.ctypes.data_as(C.c_void_p)
+    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), ip([9]), bp) == CAC_ESTATE
+    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([-2]), ip([8]), bp) == CAC_ESTATE
     assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), ip([8]), None) == CAC_EINVAL
-    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), ip([8]), C.c_void_p(16)) == CAC_ENODEV
+    assert lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), ip([8]), bp) == CAC_ENODEV
     enc2 = dry(C1)
-    assert lib.cac_import_state(enc2.ctx, 1, ip(ids), ip([3]), None, C.c_void_p(16)) == CAC_ESTATE
+    b2 = _blob(enc2, 1)
+    assert lib.cac_import_state(enc2.ctx, 1, ip(ids), ip([3]), None, b2.ctypes.data_as(C.c_void_p)) == CAC_ESTATE
+
+
+@pytest.mark.parametrize("field,value", [("d_ff", 128), ("att_left", 69), ("n_heads", 2), ("dtype", 1),
+                                         ("joint_dim", 640), ("n_layers", 3)])
+def test_import_rejects_a_blob_of_another_config(field, value):
+    """The state blob carries the config it was made with: a blob whose header names any other
+    model config is rejected with CAC_ESTATE, and the stream keeps its state."""
+    enc = dry(C1, streams=2)
+    other = cac.make_config(C1, max_streams=2, flags=cac.binding.CAC_FLAG_DRY_RUN)
+    setattr(other, field, value)
+    h = np.zeros(4, np.uint32)
+    assert enc.lib.cac_state_header(C.byref(other), h.ctypes.data_as(C.POINTER(C.c_uint32))) == 0
+    assert not np.array_equal(h.view(np.float32), enc.state_header())
+    ids = np.array([1], np.int32)
+    ip = lambda a: np.asarray(a, np.int32).ctypes.data_as(C.POINTER(C.c_int32))  # noqa: E731
+    bad = _blob(enc, 1, h.view(np.float32))
+    assert enc.lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), None, bad.ctypes.data_as(C.c_void_p)) == CAC_ESTATE
+    assert b"different config" in enc.lib.cac_last_error(enc.ctx)
+    assert enc.stream_info(1).pos == 0
+    # a blob without any header (old layout, or not a state blob) is rejected too
+    raw = _blob(enc, 1, np.zeros(4, np.float32))
+    assert enc.lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), None, raw.ctypes.data_as(C.c_void_p)) == CAC_ESTATE
+    # the context's own header passes validation (a dry-run context then stops before device work)
+    good = _blob(enc, 1)
+    assert enc.lib.cac_import_state(enc.ctx, 1, ip(ids), ip([4]), None, good.ctypes.data_as(C.c_void_p)) == CAC_ENODEV
+
+
+def test_state_header_ignores_capacity_and_flags():
+    """Contexts that differ only in capacity (max_streams, max_push_frames) or flags share a
+    header: a stream's state moves between them."""
+    lib = cac.load()
+    a = cac.make_config(C3, max_streams=4)
+    b = cac.make_config(C3, max_streams=1024, max_push_frames=16, flags=cac.binding.CAC_FLAG_POISON)
+    ha, hb = np.zeros(4, np.uint32), np.zeros(4, np.uint32)
+    assert lib.cac_state_header(C.byref(a), ha.ctypes.data_as(C.POINTER(C.c_uint32))) == 0
+    assert lib.cac_state_header(C.byref(b), hb.ctypes.data_as(C.POINTER(C.c_uint32))) == 0
+    assert np.array_equal(ha, hb) and ha[0] == 0x53434143 and ha[1] == 1
+    bad = cac.make_config(C3)
+    bad.d_model = 100
+    assert lib.cac_state_header(C.byref(bad), ha.ctypes.data_as(C.POINTER(C.c_uint32))) == CAC_EINVAL
 
 
 def test_profile_replay_needs_a_replayed_push_graph():

@@ -1,15 +1,18 @@
 """GPU parity of the HIP chunk step (through the C ABI) against the float64 oracle.
 
-Bars: float32 workloads max-abs <= 1e-4 on every output and identical greedy tokens except
-frames the token head's own bound marks ambiguous; bf16 workloads
-||z_gpu - z_ref||_inf / ||z_ref||_inf <= 2e-2 on every step. Streams are independent, so the
-full-batch runs are checked on sampled streams the oracle computes one batch at a time."""
+Bars: float32 workloads max-abs <= 1e-4 on every output and identical greedy tokens on every
+frame (frames the token head's bound would call ambiguous are only counted and logged); bf16
+workloads ||z_gpu - z_ref||_inf / ||z_ref||_inf <= 2e-2 on every step over every checked
+stream. The GPU always runs the whole batch of a workload; the oracle checks every stream of
+the 256- and 1024-stream workloads and a fixed 64-stream subset of the lookahead workload,
+computed in worker processes while the GPU runs (streams are independent)."""
 import numpy as np
 import pytest
 import torch
 
+import oracle_pool
 from gpu_util import dev_dtype, import_staggered, log, rel_inf, to_dev
-from synth import C1, C2, C3, C4, C5, make_inputs, make_state, make_token_head, make_weights
+from synth import C1, C2, C3, C4, C5, make_inputs, make_state, make_token_head, make_weights, state_position
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +94,20 @@ def test_c1_tiny_f32_all_chunks():
     assert err[-20:].max() <= 10 * max(err[:20].max(), 1e-7)
 
 
+def _check_tokens(got, ref, tag):
+    """Greedy tokens of both paths identical on every frame; the frames whose oracle margin
+    the token head's perturbation bound would not cover are counted as a diagnostic."""
+    from oracle.tokens import ambiguous_frames, greedy_tokens
+    head = make_token_head(C2)
+    zg, zr = got.reshape(-1, C2.joint_dim), ref.reshape(-1, C2.joint_dim)
+    tg, _ = greedy_tokens(zg, head)
+    tr, margin = greedy_tokens(zr, head)
+    amb = ambiguous_frames(zr, zg, head)
+    log(f"{tag} tokens: {int((tg != tr).sum())} differ of {len(tr)}; {int(amb.sum())} frames inside the "
+        f"ambiguity bound; smallest oracle margin {float(margin.min()):.3e}")
+    assert np.array_equal(tg, tr), np.nonzero(tg != tr)[0][:20]
+
+
 def test_c2_eou_f32_one_stream_tokens():
     chunks = 80  # the 70-row cache fills at chunk 35 and wraps after
     log(f"C2 f32 17 layers, 1 stream x {chunks} chunks")
@@ -98,91 +115,122 @@ def test_c2_eou_f32_one_stream_tokens():
     err = np.abs(got - ref).max()
     log(f"C2 max-abs {err:.3e}")
     assert err <= F32_TOL
-    from oracle.tokens import ambiguous_frames, greedy_tokens
-    head = make_token_head(C2)
-    zg, zr = got.reshape(-1, C2.joint_dim), ref.reshape(-1, C2.joint_dim)
-    tg, _ = greedy_tokens(zg, head)
-    tr, _ = greedy_tokens(zr, head)
-    amb = ambiguous_frames(zr, zg, head)
-    log(f"C2 tokens: {int((tg != tr).sum())} differ, {int(amb.sum())} ambiguous of {len(tr)}")
-    assert np.all((tg == tr) | amb)
+    _check_tokens(got, ref, "C2/80")
 
 
 @pytest.mark.slow
 def test_c2_eou_f32_all_1000_chunks():
+    """The whole workload: max-abs on every output and identical tokens on all 2000 frames.
+    The oracle runs in a worker process while the GPU pushes."""
     log("C2 f32 all 1000 chunks")
-    got, ref = _run_single_stream(C2, C2.chunks)
+    h = oracle_pool.submit_streams(C2, [0], C2.chunks, staggered=False)
+    W = make_weights(C2)
+    enc = _enc(C2, W, max_streams=1)
+    xs = make_inputs(C2, 0, C2.chunks)
+    got = []
+    for c in range(C2.chunks):
+        out, _ = enc.push_chunk([0], to_dev(xs[c][None], C2))
+        got.append(out.cpu().numpy()[0])
+    got = np.stack(got)
+    refs, _ = oracle_pool.collect(h)
+    ref = np.stack([r[0] for r in refs])
     err = np.abs(got - ref).max(axis=(1, 2))
-    log(f"C2/1000 max-abs {err.max():.3e}")
+    log(f"C2/1000 max-abs {err.max():.3e} (chunk {int(err.argmax())})")
     assert err.max() <= F32_TOL
+    _check_tokens(got, ref, "C2/1000")
 
 
 # ----------------------------------------------------------------------------- bf16 workloads
 
-def _sampled(cfg, positions, k):
-    """Deterministic sample of streams: first, last, a fresh one and a full-cache one if any,
-    plus evenly spaced ones."""
-    S = len(positions)
-    pick = {0, S - 1}
-    fresh = [s for s, p in enumerate(positions) if p == 0]
-    full = [s for s, p in enumerate(positions) if p > cfg.att_left]
-    if fresh:
-        pick.add(fresh[0])
-    if full:
-        pick.add(full[len(full) // 2])
-    for s in np.linspace(0, S - 1, k).astype(int):
-        if len(pick) >= k:
-            break
-        pick.add(int(s))
-    return sorted(pick)
-
-
-def _run_staggered(cfg, chunks, n_sample):
+def _check_workload(cfg, chunks, check, flush=False, extra=None):
+    """The GPU pushes ``chunks`` chunks for every stream of the workload (from their injected
+    states); the oracle runs the streams ``check`` over those chunks, and optionally the
+    streams of ``extra = (ids, more_chunks)`` over a longer run, in worker processes started
+    before the GPU work. Every step must meet the bf16 bar over all checked streams."""
     W = make_weights(cfg)
     S = cfg.streams
+    check = sorted(check)
+    run = chunks
+    handles = [(check, chunks, oracle_pool.submit_streams(cfg, check, chunks, staggered=cfg.staggered, flush=flush))]
+    if extra:
+        ex_ids, ex_chunks = sorted(extra[0]), extra[1]
+        handles.append((ex_ids, ex_chunks, oracle_pool.submit_streams(cfg, ex_ids, ex_chunks, staggered=cfg.staggered)))
+        run = max(run, ex_chunks)
     enc = _enc(cfg, W, max_streams=S)
     log(f"{cfg.name}: importing {S} staggered states")
-    positions = import_staggered(enc, cfg, S)
-    sample = _sampled(cfg, positions, n_sample)
-    log(f"{cfg.name}: sampled streams {sample} at positions {[positions[s] for s in sample]}")
-    orc = _oracle(cfg, W)
-    sts = [orc.state_from(make_state(cfg, s)) for s in sample]
-    inputs = np.stack([make_inputs(cfg, s, chunks) for s in range(S)])  # [S, chunks, ...]
+    positions = import_staggered(enc, cfg, S) if cfg.staggered else [0] * S
+    inputs = np.stack([make_inputs(cfg, s, run) for s in range(S)])  # [S, chunks, ...]
     ids = list(range(S))
+    got, em = [], []
+    for c in range(run):
+        out, e = enc.push_chunk(ids, to_dev(inputs[:, c], cfg))
+        got.append(out.cpu().numpy())
+        em.append(e)
+    fl_got = enc.flush(check) if flush else None
     worst = 0.0
-    for c in range(chunks):
-        out, em = enc.push_chunk(ids, to_dev(inputs[:, c], cfg))
-        got = out.cpu().numpy()[sample]
-        ref = orc.push(sts, inputs[sample, c].astype(np.float64))
-        if ref.shape[1] == 0:
-            assert em.max() == 0
-            continue
-        assert np.all(em[sample] == ref.shape[1])
-        r = rel_inf(got[:, : ref.shape[1]], ref)
-        worst = max(worst, r)
-        log(f"{cfg.name} chunk {c}: rel {r:.3e}")
-        assert r <= BF16_TOL, (c, r)
-    return enc, orc, sts, sample, worst
+    for sel, nch, h in handles:
+        refs, fl_ref = oracle_pool.collect(h)
+        sel = np.asarray(sel)
+        per_stream = np.zeros(len(sel))
+        for c in range(nch):
+            ref = refs[c]
+            m = ref.shape[1]
+            assert np.all(em[c][sel] == m), c
+            if m == 0:
+                continue
+            g = got[c][sel, :m]
+            r = rel_inf(g, ref)
+            rms = float(np.sqrt(np.mean((g - ref) ** 2)) / np.sqrt(np.mean(ref ** 2)))
+            per_stream = np.maximum(per_stream, np.abs(g - ref).max(axis=(1, 2)) / np.abs(ref).max())
+            worst = max(worst, r)
+            log(f"{cfg.name} chunk {c}, {len(sel)} streams: rel {r:.3e}, rms-rel {rms:.3e}")
+            assert r <= BF16_TOL, (c, r)
+        log(f"{cfg.name}: {len(sel)} streams x {nch} chunks, worst stream {int(sel[per_stream.argmax()])} "
+            f"at {float(per_stream.max()):.3e}")
+        if fl_ref is not None:
+            out, frames = fl_got
+            out = out.cpu().numpy()
+            for j, ref in enumerate(fl_ref):
+                assert frames[j] == ref.shape[0], (sel[j], frames[j], ref.shape)
+                r = rel_inf(out[j, : ref.shape[0]], ref)
+                worst = max(worst, r)
+                assert r <= BF16_TOL, (sel[j], r)
+            log(f"{cfg.name}: flush of {len(fl_ref)} streams within the bar")
+    return enc, positions, worst
 
 
+def _wrapping(cfg, positions, frames, R, k):
+    """Up to k streams whose K/V ring slot (position mod R) passes the end of the ring within
+    ``frames`` frames, spread over the batch."""
+    wrap = [s for s, p in enumerate(positions) if p % R + frames >= R]
+    return [wrap[i] for i in np.linspace(0, len(wrap) - 1, min(k, len(wrap))).astype(int)] if wrap else []
+
+
+@pytest.mark.slow
 def test_c3_bf16_256_staggered_streams():
-    _run_staggered(C3, 8, 6)
+    """Every stream of the 256-stream workload over 8 chunks."""
+    _check_workload(C3, 8, range(C3.streams))
 
 
+@pytest.mark.slow
 def test_c4_bf16_1024_streams_frontend():
-    _run_staggered(C4, 4, 6)
+    """Every stream of the 1024-stream front-end workload over 4 chunks, plus 64 streams over
+    12 chunks, most of them chosen so that their K/V ring (att_left + 8 slots, the binding's
+    default push limit) wraps during the run."""
+    R = C4.att_left + 8
+    pos = [state_position(C4, s) for s in range(C4.streams)]
+    wrap = _wrapping(C4, pos, 24, R, 48)
+    rest = [s for s in np.linspace(0, C4.streams - 1, 64).astype(int) if s not in wrap][: 64 - len(wrap)]
+    fresh = [s for s, p in enumerate(pos) if p == 0][:2]
+    extra = sorted(set(wrap) | set(rest[: 64 - len(wrap) - len(fresh)]) | set(fresh))
+    log(f"C4: {len(wrap)} of the 12-chunk streams wrap their ring; fresh streams {fresh}")
+    _check_workload(C4, 4, range(C4.streams), extra=(extra, 12))
 
 
+@pytest.mark.slow
 def test_c5_bf16_lookahead_512_streams_and_flush():
-    enc, orc, sts, sample, _ = _run_staggered(C5, 4, 5)
-    log("C5 flush of the sampled streams")
-    out, frames = enc.flush(sample)
-    assert frames.tolist() == [C5.n_lookahead] * len(sample)
-    for j, st in enumerate(sts):
-        ref = orc.flush(st)
-        r = rel_inf(out.cpu().numpy()[j, : ref.shape[0]], ref)
-        log(f"C5 flush stream {sample[j]}: rel {r:.3e}")
-        assert r <= BF16_TOL
+    """A fixed 64-stream subset (every 8th stream) over 8 passes, then the flush of all 64."""
+    _check_workload(C5, 8, range(0, C5.streams, 8), flush=True)
 
 
 @pytest.mark.parametrize("cfg", [
@@ -198,7 +246,7 @@ def test_c5_bf16_lookahead_512_streams_and_flush():
 ], ids=["bf16-hd16", "mfma-att-1row", "mfma-att-4rows", "mfma-att-5rows-lookahead", "mfma-att-8tiles",
         "mfma-att-8tiles-10rows"])
 def test_bf16_attention_shapes(cfg):
-    _run_staggered(cfg, cfg.chunks, 4)
+    _check_workload(cfg, cfg.chunks, range(cfg.streams))
 
 
 def test_bf16_single_stream_small_m_path():
@@ -287,6 +335,29 @@ def test_export_import_resume(cfg):
     for c in range(15, n):
         o, em = enc2.push_chunk([1], to_dev(xs[c][None], cfg))
         assert np.array_equal(o.cpu().numpy()[0, : em[0]], outs[c]), c
+
+
+def test_import_rejects_state_of_another_config():
+    """A state exported from one context imports into a context of the same config (whatever
+    its capacity) and is rejected with CAC_ESTATE, changing nothing, by a context of another
+    config: the header is read back from device memory."""
+    from cache_aware_conformer_amd.binding import CAC_ESTATE, CacError
+    cfg = C1
+    W = make_weights(cfg)
+    enc = _enc(cfg, W, max_streams=2)
+    xs = make_inputs(cfg, 0, 3)
+    for c in range(3):
+        enc.push_chunk([0], to_dev(xs[c][None], cfg))
+    pos, pend, blob = enc.export_state([0])
+    other = cfg.replace(d_ff=128)
+    enc2 = _enc(other, make_weights(other), max_streams=2)
+    with pytest.raises(CacError) as ei:
+        enc2.import_state([1], pos, pend, blob)
+    assert ei.value.code == CAC_ESTATE
+    assert enc2.stream_info(1).pos == 0
+    enc3 = _enc(cfg, W, max_streams=3, max_push_frames=4)
+    enc3.import_state([2], pos, pend, blob)
+    assert enc3.stream_info(2).pos == pos[0] == 6
 
 
 def test_poisoned_cache_slots_never_reach_outputs():
