@@ -11,7 +11,9 @@ from __future__ import annotations
 
 import multiprocessing as mp
 import os
-from concurrent.futures import ProcessPoolExecutor
+import sys
+import time
+from concurrent.futures import FIRST_COMPLETED, ProcessPoolExecutor, wait
 
 import numpy as np
 
@@ -70,6 +72,12 @@ def collect(handle):
     """Per-chunk oracle outputs [len(ids), m, P] (m = frames emitted by that push) in the order
     of the submitted ids, and the flush outputs (a list, or None)."""
     groups, futs, chunks, flush = handle
+    t0, pending = time.time(), set(futs)
+    while pending:
+        _, pending = wait(pending, timeout=30, return_when=FIRST_COMPLETED)
+        print(f"oracle: {len(futs) - len(pending)}/{len(futs)} stream groups done after {time.time() - t0:.0f} s",
+              flush=True)
+        sys.stdout.flush()
     per_chunk = [[] for _ in range(chunks)]
     flushed = [] if flush else None
     for fut in futs:
