@@ -53,6 +53,7 @@ SIGNATURES = {
     "cac_profile_read": (_i32, [_vp, _i32, C.c_char_p, _i32, C.POINTER(C.c_int64), C.POINTER(C.c_double),
                                 C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     "cac_state_header": (_i32, [_CFGP, C.POINTER(C.c_uint32)]),
+    "cac_test_gemm_noalloc": (_i32, [_i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "cac_profile_replay": (_i32, [_vp, C.c_char_p, _i32, C.POINTER(C.c_double), C.POINTER(C.c_int32),
                                   C.POINTER(C.c_double), C.POINTER(C.c_double)]),
 }
@@ -339,8 +340,9 @@ class StreamingEncoder:
             pass
 
 
-def test_gemm(dtype: int, path: int, A, W, bias=None, out=None, stream=None):
-    """C = A W^T + bias through the library's dense kernels (test-only export)."""
+def test_gemm(dtype: int, path: int, A, W, bias=None, out=None, stream=None, noalloc=False):
+    """C = A W^T + bias through the library's dense kernels (test-only export; noalloc: the
+    variant that allocates nothing and keeps split-K partials in the library's scratch)."""
     import torch
     lib = load()
     M, K = A.shape
@@ -348,8 +350,9 @@ def test_gemm(dtype: int, path: int, A, W, bias=None, out=None, stream=None):
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     s = stream if stream is not None else torch.cuda.current_stream(A.device).cuda_stream
-    rc = lib.cac_test_gemm(dtype, path, M, N, K, A.data_ptr(), W.data_ptr(),
-                           None if bias is None else bias.data_ptr(), out.data_ptr(), s)
+    fn = lib.cac_test_gemm_noalloc if noalloc else lib.cac_test_gemm
+    rc = fn(dtype, path, M, N, K, A.data_ptr(), W.data_ptr(), None if bias is None else bias.data_ptr(),
+            out.data_ptr(), s)
     if rc != CAC_OK:
-        raise CacError(rc, "cac_test_gemm failed")
+        raise CacError(rc, lib.cac_last_error(None).decode() or "test GEMM failed")
     return out

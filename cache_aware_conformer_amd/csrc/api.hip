@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -16,9 +17,37 @@
 
 void kernels_init();
 
+// Device scratch of the no-allocation test GEMM: the float32 split-K partials live in this
+// file-scope array (one copy per GPU, held until the process ends) instead of a hipMalloc'd
+// buffer. Host code never passes the array's name to a kernel: it takes the per-device address
+// hipGetSymbolAddress returns.
+constexpr size_t kScratchFloats = (size_t)4 << 20;  // 16 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
 namespace {
 
 thread_local std::string g_create_error;
+
+std::mutex g_scratch_mu;
+std::vector<float*> g_scratch_ptr;  // device address of `scratch`, per device id
+
+// Address of the current device's scratch array, looked up once per device.
+hipError_t scratch_ptr(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_ptr.size() <= dev) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 // ------------------------------------------------------------------------------- dimensions
 struct Dims {
@@ -1227,15 +1256,50 @@ int32_t cac_destroy(cac_ctx* c) {
   return CAC_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shape checks shared by the test GEMM entry points; returns the k-range count (>= 1) or an
+// error code.
+int test_gemm_ranges(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t K, const void* d_A,
+                     const void* d_W, float* d_C) {
+  g_create_error.clear();
+  auto bad = [](const char* m) { g_create_error = m; return CAC_EINVAL; };
+  if (dtype != CAC_F32 && dtype != CAC_BF16) return bad("dtype must be CAC_F32 or CAC_BF16");
+  if (M < 1 || N < 1 || K < 1 || !d_A || !d_W || !d_C) return bad("empty shape or NULL pointer");
+  if (path < 0 || path > 8 || (path >= 2 && dtype != CAC_BF16)) return bad("path out of range for this dtype");
+  if (path >= 2 && K % 64) return bad("MFMA paths need K a multiple of 64");  // MFMA tiles step K by 64
+  if ((size_t)8 * K * 4 > 160 * 1024 && path < 2) return bad("K too large for the small-M kernel");
+  const int ks = path == 7 ? 2 : path == 8 ? 4 : 1;
+  if (ks > 1 && (K % (64 * ks) || N % 256 || N > 1024)) return bad("split-K paths need K a multiple of 64 * ranges and N a multiple of 256 up to 1024");
+  return ks;
+}
+
+// C = A W^T + bias as the ks > 1 paths compute it: zero C, the split-K partials into part,
+// then the residual row kernel adds them (in k-range order) and the bias to C.
+void enqueue_split_gemm(Launcher& L, int32_t dtype, int ks, int32_t M, int32_t N, int32_t K, const void* d_A,
+                        const void* d_W, const float* d_bias, float* d_C, float* part) {
+  EpiArgs e{};
+  e.kind = EPI_PART; e.out = part; e.ldo = N; e.pstride = (long)M * N;
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K; g.A = d_A; g.W = d_W; g.amap = RowMap{INT_MAX, 0, K}; g.epi = e; g.ksplit = ks;
+  FillArgs z{d_C, (long)M * N, 0.0f};
+  launch_fill(L, z);
+  launch_gemm(L, g, dtype, 0);
+  ResLnArgs r{};
+  r.part = part; r.pstride = (long)M * N; r.nparts = ks; r.bias = d_bias; r.alpha = 1.0f; r.x = d_C; r.M = M; r.D = N;
+  if (L.err == hipSuccess && !launch_resid_ln(L, r, dtype)) L.err = hipErrorInvalidValue;
+}
+
+}  // namespace
+
+extern "C" {
+
 int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t K, const void* d_A, const void* d_W,
                       const float* d_bias, float* d_C, void* hip_stream) {
-  if (dtype != CAC_F32 && dtype != CAC_BF16) return CAC_EINVAL;
-  if (M < 1 || N < 1 || K < 1 || !d_A || !d_W || !d_C) return CAC_EINVAL;
-  if (path < 0 || path > 8 || (path >= 2 && dtype != CAC_BF16)) return CAC_EINVAL;
-  if (path >= 2 && K % 64) return CAC_EINVAL;  // MFMA tiles step K by 64
-  if ((size_t)8 * K * 4 > 160 * 1024 && path < 2) return CAC_EINVAL;
-  const int ks = path == 7 ? 2 : path == 8 ? 4 : 1;
-  if (ks > 1 && (K % (64 * ks) || N % 256 || N > 1024)) return CAC_EINVAL;
+  const int ks = test_gemm_ranges(dtype, path, M, N, K, d_A, d_W, d_C);
+  if (ks < 0) return ks;
   kernels_init();
   Launcher L;
   L.stream = (hipStream_t)hip_stream;
@@ -1263,6 +1327,36 @@ int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t
   const hipError_t se = hipStreamSynchronize(L.stream);
   (void)hipFree(part);
   return err == hipSuccess && se == hipSuccess ? CAC_OK : CAC_EHIP;
+}
+
+int32_t cac_test_gemm_noalloc(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t K, const void* d_A,
+                              const void* d_W, const float* d_bias, float* d_C, void* hip_stream) {
+  const int ks = test_gemm_ranges(dtype, path, M, N, K, d_A, d_W, d_C);
+  if (ks < 0) return ks;
+  if (ks > 1 && (size_t)ks * M * N > kScratchFloats) {
+    g_create_error = "split-K partials of " + std::to_string((size_t)ks * M * N) + " floats exceed the " +
+                     std::to_string(kScratchFloats) + "-float device scratch";
+    return CAC_ENOMEM;
+  }
+  kernels_init();
+  Launcher L;
+  L.stream = (hipStream_t)hip_stream;
+  if (ks == 1) {
+    EpiArgs e{};
+    e.kind = EPI_F32; e.bias = d_bias; e.out = d_C; e.ldo = N;
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K; g.A = d_A; g.W = d_W; g.amap = RowMap{INT_MAX, 0, K}; g.epi = e;
+    launch_gemm(L, g, dtype, path);
+  } else {
+    float* part = nullptr;
+    L.err = scratch_ptr(&part);
+    if (L.err == hipSuccess) enqueue_split_gemm(L, dtype, ks, M, N, K, d_A, d_W, d_bias, d_C, part);
+  }
+  if (L.err != hipSuccess) {
+    g_create_error = std::string("HIP error: ") + hipGetErrorString(L.err);
+    return CAC_EHIP;
+  }
+  return CAC_OK;
 }
 
 }  // extern "C"

@@ -276,6 +276,12 @@ struct CvtArgs {         // y[m][k] = bf16(x[amap(m) + k])
   int M, K;
 };
 
+struct FillArgs {       // p[0 .. n) = v
+  float* p;
+  long n;
+  float v;
+};
+
 struct AdvanceArgs {    // pos[ids[s]] += adv, pend[ids[s]] += dpend
   const int32_t* ids;
   int32_t* pos;
@@ -402,6 +408,7 @@ void launch_copy_rows(Launcher& L, const CopyRowsArgs& a);
 void kernels_init();
 void launch_fe_window(Launcher& L, const FeWindowArgs& a, int dtype);
 void launch_advance(Launcher& L, const AdvanceArgs& a);
+void launch_fill(Launcher& L, const FillArgs& a);
 void launch_posproj(Launcher& L, const PosProjArgs& a);
 void launch_state(Launcher& L, const StateArgs& a, int op);  // 0 reset, 1 import, 2 export
 void launch_la_store(Launcher& L, const LaStoreArgs& a, int dtype);

@@ -1801,6 +1801,16 @@ void launch_advance(Launcher& L, const AdvanceArgs& a) {
   L.launch((const void*)&advance_kernel, dim3((a.n + 255) / 256), dim3(256), 0, &args);
 }
 
+__global__ __launch_bounds__(256) void fill_kernel(FillArgs a) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < a.n; i += (long)gridDim.x * 256) a.p[i] = a.v;
+}
+
+void launch_fill(Launcher& L, const FillArgs& a) {
+  FillArgs args = a;
+  L.tag("fill", 0.0, 0.0);
+  L.launch((const void*)&fill_kernel, dim3((unsigned)std::min<long>((a.n + 255) / 256, 4096)), dim3(256), 0, &args);
+}
+
 // =============================================================================== position table
 // Block per (layer, relative offset): the sinusoid row PE(rel) is formed once in LDS (double
 // precision), then each thread owns one output column of PE(rel) @ Wpos_l.

@@ -220,7 +220,7 @@ int32_t cac_profile_replay(cac_ctx* ctx, const char* prefix, int32_t reps, doubl
 int32_t cac_destroy(cac_ctx* ctx);
 
 /* Description of the last error on ctx; with ctx == NULL, of the last failed
- * cac_create_streams on this thread. Never NULL. */
+ * cac_create_streams (or test GEMM call) on this thread. Never NULL. */
 const char* cac_last_error(const cac_ctx* ctx);
 
 /* Test-only: C[M][N] (float32) = A[M][K] W[N][K]^T + bias through the library's dense kernels
@@ -235,6 +235,20 @@ const char* cac_last_error(const cac_ctx* ctx);
 int32_t cac_test_gemm(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t K,
                       const void* d_A, const void* d_W, const float* d_bias, float* d_C,
                       void* hip_stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): cac_test_gemm with the same arguments, shapes and
+ * results, that calls no hipMalloc, hipFree or other allocating routine and does not
+ * synchronise. The split-K paths (7, 8) keep their float32 partials in a device scratch array
+ * of the library (4 Mi floats = 16 MiB, one per GPU, held until the process ends): a call whose
+ * partials (ranges * M * N floats) do not fit returns CAC_ENOMEM before any device work. The
+ * output is cleared by a kernel (no memset node). Every call on one GPU shares that GPU's
+ * scratch and each call rewrites what it reads, so calls run one after another on one stream
+ * are independent, but calls that overlap in time on one GPU (different streams or threads)
+ * race on it. Errors are described by cac_last_error(NULL). */
+int32_t cac_test_gemm_noalloc(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t K,
+                              const void* d_A, const void* d_W, const float* d_bias, float* d_C,
+                              void* hip_stream);
 
 #ifdef __cplusplus
 }
