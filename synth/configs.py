@@ -66,5 +66,35 @@ C5 = EncConfig(name="C5_lookahead_bf16_512streams", seed=4, dtype="bf16", stream
 CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
 
 
+@dataclass(frozen=True)
+class DecConfig:
+    """Greedy RNNT + EOU decoding after the encoder: predictor (embedding + LSTM stack, its
+    output projected to the joint width) and the joint after projection over vocab + blank +
+    EOU classes, fed the encoder's projected frames."""
+    name: str
+    seed: int
+    joint_dim: int = 640        # P: width of the projected encoder and predictor outputs
+    pred_hidden: int = 640      # H: embedding and LSTM width
+    pred_layers: int = 2
+    vocab: int = 1024           # V; blank = V, EOU = V + 1
+    max_symbols: int = 4        # emissions per frame before the decoder moves on
+    blank_bias: float = 2.5     # added to the blank class's joint bias (synthetic weights)
+    streams: int = 1
+    frames: int = 2             # frames per decode call (one encoder chunk)
+    calls: int = 1000
+
+    @property
+    def classes(self) -> int:
+        return self.vocab + 2
+
+    def replace(self, **kw) -> "DecConfig":
+        return dataclasses.replace(self, **kw)
+
+
+D1 = DecConfig(name="D1_greedy_1stream", seed=11, streams=1, calls=1000)
+D2 = DecConfig(name="D2_greedy_1024streams", seed=12, streams=1024, calls=100)
+DEC_CONFIGS = {"D1": D1, "D2": D2}
+
+
 def get_config(key: str) -> EncConfig:
     return CONFIGS[key]

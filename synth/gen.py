@@ -20,7 +20,7 @@ import zlib
 
 import numpy as np
 
-from .configs import EncConfig
+from .configs import DecConfig, EncConfig
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -164,3 +164,33 @@ def make_state(cfg: EncConfig, stream: int) -> dict:
     if cfg.n_lookahead:
         st["x0_tail"] = _draw_unit(cfg, f"state.s{stream}.x0", (cfg.n_lookahead, D))
     return st
+
+
+def dec_weight_names(cfg: DecConfig):
+    """Ordered (name, shape, fan_in) of the decoder's parameters (matrices are [in][out])."""
+    H, P, C = cfg.pred_hidden, cfg.joint_dim, cfg.classes
+    specs = [("pred.embed", (C, H), 1)]
+    for l in range(cfg.pred_layers):
+        specs += [(f"pred.l{l}.w_ih", (H, 4 * H), H), (f"pred.l{l}.w_hh", (H, 4 * H), H),
+                  (f"pred.l{l}.b_ih", (4 * H,), H), (f"pred.l{l}.b_hh", (4 * H,), H)]
+    specs += [("pred.proj_w", (H, P), H), ("pred.proj_b", (P,), H),
+              ("joint.out_w", (P, C), P), ("joint.out_b", (C,), P)]
+    return specs
+
+
+def make_dec_weights(cfg: DecConfig) -> dict:
+    """Decoder weights, float32: every tensor ~ N(0, 1/fan_in) (the embedding N(0, 1)); the
+    blank class's joint bias is raised by ``blank_bias`` so that most frames decode to blank,
+    as a trained model's do."""
+    out = {}
+    for name, shape, fan in dec_weight_names(cfg):
+        out[name] = (_rng(cfg, name).standard_normal(shape) / np.sqrt(fan)).astype(np.float32)
+    out["joint.out_b"][cfg.vocab] += np.float32(cfg.blank_bias)
+    return out
+
+
+def make_dec_inputs(cfg: DecConfig, stream: int, calls: int | None = None) -> np.ndarray:
+    """Projected encoder frames of one stream, [calls, frames, joint_dim] ~ N(0, 1) float32
+    (the encoder's projected outputs have about unit scale)."""
+    x = _rng(cfg, f"dec.input.s{stream}").standard_normal((cfg.calls, cfg.frames, cfg.joint_dim), dtype=np.float32)
+    return x if calls is None else x[:calls]
