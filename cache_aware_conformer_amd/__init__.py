@@ -1,7 +1,8 @@
 """Cache-aware streaming Conformer chunk step for MI355X (gfx950).
 
-The work runs in ``libcac.so`` (HIP kernels behind the C ABI of ``include/cac.h``);
-``binding`` is its thin ctypes wrapper.
+The work runs in ``libcac.so`` (HIP kernels behind the C ABI of ``include/cac.h`` for the
+encoder chunk step and ``include/cac_decode.h`` for greedy decoding of its output); ``binding``
+is its thin ctypes wrapper.
 """
 from .binding import (  # noqa: F401
     CAC_BF16,
@@ -9,6 +10,7 @@ from .binding import (  # noqa: F401
     CAC_FLAG_DRY_RUN,
     CAC_FLAG_POISON,
     CacError,
+    StreamingDecoder,
     StreamingEncoder,
     load,
     make_config,

@@ -31,8 +31,23 @@ class cac_config(C.Structure):
         "dtype", "max_streams", "max_push_frames", "flags")]
 
 
+class cac_dec_config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "joint_dim", "pred_hidden", "pred_layers", "vocab", "max_symbols", "max_streams", "max_frames", "flags")]
+
+
 _CFGP = C.POINTER(cac_config)
+_DCFGP = C.POINTER(cac_dec_config)
 SIGNATURES = {
+    # include/cac_decode.h
+    "cac_dec_param_count": (_sz, [_DCFGP]),
+    "cac_dec_workspace_bytes": (_sz, [_DCFGP]),
+    "cac_dec_create": (_i32, [_DCFGP, _fp, _sz, _vp, _sz, _vp, C.POINTER(_vp)]),
+    "cac_dec_greedy": (_i32, [_vp, _i32, _ip, _i32, _vp, _vp, _vp, _vp]),
+    "cac_dec_reset": (_i32, [_vp, _i32, _ip]),
+    "cac_dec_destroy": (_i32, [_vp]),
+    "cac_dec_last_error": (C.c_char_p, [_vp]),
+    # include/cac.h
     "cac_param_count": (_sz, [_CFGP]),
     "cac_workspace_bytes": (_sz, [_CFGP]),
     "cac_state_floats": (_sz, [_CFGP]),
@@ -356,3 +371,101 @@ def test_gemm(dtype: int, path: int, A, W, bias=None, out=None, stream=None, noa
     if rc != CAC_OK:
         raise CacError(rc, lib.cac_last_error(None).decode() or "test GEMM failed")
     return out
+
+
+# ----------------------------------------------------------------------------- greedy decoding
+
+def dec_param_order(cfg):
+    """(name, shape) of the decoder parameters in the order cac_dec_create takes them."""
+    H, P, C_ = cfg.pred_hidden, cfg.joint_dim, cfg.vocab + 2
+    out = [("pred.embed", (C_, H))]
+    for l in range(cfg.pred_layers):
+        out += [(f"pred.l{l}.w_ih", (H, 4 * H)), (f"pred.l{l}.w_hh", (H, 4 * H)),
+                (f"pred.l{l}.b_ih", (4 * H,)), (f"pred.l{l}.b_hh", (4 * H,))]
+    out += [("pred.proj_w", (H, P)), ("pred.proj_b", (P,)), ("joint.out_w", (P, C_)), ("joint.out_b", (C_,))]
+    return out
+
+
+def make_dec_config(cfg, max_streams=None, max_frames=None, flags=0) -> cac_dec_config:
+    c = cac_dec_config()
+    for name in ("joint_dim", "pred_hidden", "pred_layers", "vocab", "max_symbols"):
+        setattr(c, name, int(getattr(cfg, name)))
+    c.max_streams = int(max_streams if max_streams is not None else cfg.streams)
+    c.max_frames = int(max_frames if max_frames is not None else cfg.frames)
+    c.flags = int(flags)
+    return c
+
+
+class StreamingDecoder:
+    """One greedy-decoding context (include/cac_decode.h): repacked float32 decoder weights and
+    the predictor state of ``max_streams`` streams in one device workspace, work enqueued on the
+    current torch stream."""
+
+    def __init__(self, cfg, params: dict, max_streams=None, max_frames=None, flags=0, device="cuda:0"):
+        self.lib = load()
+        self.cfg = cfg
+        self.c = make_dec_config(cfg, max_streams, max_frames, flags)
+        self.dry = bool(flags & CAC_FLAG_DRY_RUN)
+        self.m = cfg.max_symbols
+        n = self.lib.cac_dec_param_count(C.byref(self.c))
+        if n == 0:
+            self.lib.cac_dec_create(C.byref(self.c), None, 0, None, 0, None, C.byref(C.c_void_p()))
+            raise CacError(CAC_EINVAL, self.lib.cac_dec_last_error(None).decode())
+        flat = np.ascontiguousarray(np.concatenate([np.asarray(params[nm], np.float32).reshape(-1)
+                                                    for nm, shape in dec_param_order(cfg)]))
+        self.ws_bytes = self.lib.cac_dec_workspace_bytes(C.byref(self.c))
+        ctx = C.c_void_p()
+        if self.dry:
+            ws_ptr, stream, self.ws = None, None, None
+        else:
+            import torch
+            self.torch = torch
+            self.device = torch.device(device)
+            self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+            ws_ptr = (self.ws.data_ptr() + 255) // 256 * 256
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        rc = self.lib.cac_dec_create(C.byref(self.c), flat.ctypes.data_as(_fp), flat.size, ws_ptr, self.ws_bytes,
+                                     stream, C.byref(ctx))
+        if rc != CAC_OK:
+            raise CacError(rc, self.lib.cac_dec_last_error(None).decode())
+        self.ctx = ctx
+
+    def _check(self, rc):
+        if rc < 0:
+            raise CacError(rc, self.lib.cac_dec_last_error(self.ctx).decode())
+        return rc
+
+    def decode(self, stream_ids, z, tokens=None, frames=None, counts=None):
+        """z: device float32 [n, n_frames, P]. Returns device int32 (tokens [n, n_frames *
+        max_symbols], token frames (same shape), counts [n])."""
+        ids, idp = _ids(stream_ids)
+        n = ids.size
+        nf = int(z.shape[1]) if hasattr(z, "shape") else int(self.c.max_frames)
+        if hasattr(z, "is_contiguous") and (not z.is_contiguous() or z.dtype != self.torch.float32 or z.shape[0] != n):
+            raise ValueError(f"z must be a contiguous float32 tensor with {n} rows, got {z.dtype} {tuple(z.shape)}")
+        if not self.dry:
+            t = self.torch
+            if tokens is None:
+                tokens = t.empty((n, nf * self.m), dtype=t.int32, device=self.device)
+            if frames is None:
+                frames = t.empty((n, nf * self.m), dtype=t.int32, device=self.device)
+            if counts is None:
+                counts = t.empty(n, dtype=t.int32, device=self.device)
+        ptr = lambda x: None if x is None else (x.data_ptr() if hasattr(x, "data_ptr") else int(x))  # noqa: E731
+        self._check(self.lib.cac_dec_greedy(self.ctx, n, idp, nf, ptr(z), ptr(tokens), ptr(frames), ptr(counts)))
+        return tokens, frames, counts
+
+    def reset(self, stream_ids):
+        ids, idp = _ids(stream_ids)
+        return self._check(self.lib.cac_dec_reset(self.ctx, ids.size, idp))
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            self.lib.cac_dec_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

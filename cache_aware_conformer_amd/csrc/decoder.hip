@@ -1,0 +1,573 @@
+// Greedy RNNT + EOU decoding (include/cac_decode.h): the prediction network (embedding + LSTM
+// stack + projection), the joint after projection with an argmax epilogue, and the per-stream
+// greedy state machine, all in float32.
+//
+// One call runs a fixed sequence of rounds, so it can be launched without knowing on the host
+// how many symbols the streams will emit. Round j:
+//   1. predictor step for the call slots on list P_j (streams that emitted at round j-1, or
+//      whose stream carried a token into the call): LSTM layer 0 .. L-1, then the projection;
+//   2. joint for the call slots on list A_j (streams with frames left), every frame of the
+//      call at once (the predictor output does not change across blank frames);
+//   3. decision per slot on A_j: scan its frames from its cursor; the first frame whose
+//      argmax is not blank emits that class (the slot joins P_{j+1}, and A_{j+1} while it has
+//      frames left), earlier frames were blank; no emission ends the slot.
+// Each slot emits at most max_symbols per frame, so 1 + frames * max_symbols rounds finish
+// every slot. Kernels of a round whose list is empty return at once.
+//
+// The dense parts are one tile kernel on v_mfma_f32_32x32x2f32: 64 x 64 output tiles of four
+// waves (32 x 32 each), k-steps of 16 through two LDS buffers, the accumulator tile through LDS
+// to a mode-specific epilogue (LSTM cell update, projection store, joint argmax).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/cac.h"
+#include "../../include/cac_decode.h"
+#include "common.h"
+
+void kernels_init();
+
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_d;
+typedef __attribute__((ext_vector_type(4))) float f32x4_d;
+
+enum DecMode { DM_LSTM0 = 0, DM_LSTM = 1, DM_PROJ = 2, DM_JOINT = 3 };
+
+struct DecTileArgs {
+  int K, N;                 // contraction length, output columns (a multiple of 64)
+  const float* W;           // [K][N]
+  const float* bias;        // [N]
+  const int32_t* ids;       // [n] call slot -> stream id
+  const int32_t* list;      // rows: P list (predictor modes) or A list (joint: row = a * nf + f)
+  const int32_t* count;     // entries on the list
+  const int32_t* slot_tok;  // [n] token a slot's predictor step consumes
+  const float* embed;       // [C][H]
+  float* h;                 // [S][L][H] state
+  float* c;                 // [S][L][H] state
+  float* hn;                // [L][n][H] new h of the round's P-list rows
+  float* p;                 // [S][P] state: projected predictor output
+  int32_t* need;            // [n] slot still has to consume slot_tok
+  const float* z;           // [n][nf][P] caller's projected encoder frames
+  float2* part;             // [n * nf][ntiles] joint argmax per 64-column tile (value, index)
+  int layer, L, H, P, C, nf, ntiles, n;
+};
+
+__device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// Element k of the A row of list row r (r < rows).
+template <int MODE>
+__device__ __forceinline__ f32x4_d dec_a4(const DecTileArgs& a, int r, int k) {
+  if constexpr (MODE == DM_JOINT) {
+    const int slot = a.list[r / a.nf], f = r - (r / a.nf) * a.nf;
+    const int id = a.ids[slot];
+    const f32x4_d zv = *(const f32x4_d*)(a.z + ((long)slot * a.nf + f) * a.P + k);
+    const f32x4_d pv = *(const f32x4_d*)(a.p + (long)id * a.P + k);
+    f32x4_d v = zv + pv;
+    v.x = fmaxf(v.x, 0.0f); v.y = fmaxf(v.y, 0.0f); v.z = fmaxf(v.z, 0.0f); v.w = fmaxf(v.w, 0.0f);
+    return v;
+  } else if constexpr (MODE == DM_PROJ) {
+    return *(const f32x4_d*)(a.hn + ((long)(a.L - 1) * a.n + r) * a.H + k);
+  } else {
+    const int slot = a.list[r];
+    if (k < a.H) {
+      if constexpr (MODE == DM_LSTM0) return *(const f32x4_d*)(a.embed + (long)a.slot_tok[slot] * a.H + k);
+      else return *(const f32x4_d*)(a.hn + ((long)(a.layer - 1) * a.n + r) * a.H + k);
+    }
+    const int id = a.ids[slot];
+    return *(const f32x4_d*)(a.h + ((long)id * a.L + a.layer) * a.H + (k - a.H));
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void dec_tile_kernel(DecTileArgs a) {
+  const int cnt = *a.count;
+  const int rows = MODE == DM_JOINT ? cnt * a.nf : cnt;
+  const int row0 = blockIdx.y * 64, col0 = blockIdx.x * 64;
+  if (row0 >= rows) return;  // the whole block: nothing on the list for these rows
+  __shared__ float As[2][16][68];   // k-major: As[buf][k][row]
+  __shared__ float Bs[2][16][68];   // Bs[buf][k][col]
+  __shared__ float Ct[64][65];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int lr = tid >> 2, lk = (tid & 3) * 4;          // A loader: row lr, k lk .. lk+3
+  const int ar = min(row0 + lr, rows - 1);              // rows past the end reload the last one
+  const int bk = tid >> 4, bn = (tid & 15) * 4;         // W loader: k bk, columns bn .. bn+3
+  const int KT = a.K / 16;
+  f32x4_d ra = dec_a4<MODE>(a, ar, lk);
+  f32x4_d rb = *(const f32x4_d*)(a.W + (long)bk * a.N + col0 + bn);
+  f32x16_d acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int b = kt & 1;
+    As[b][lk + 0][lr] = ra.x; As[b][lk + 1][lr] = ra.y; As[b][lk + 2][lr] = ra.z; As[b][lk + 3][lr] = ra.w;
+    *(f32x4_d*)&Bs[b][bk][bn] = rb;
+    __syncthreads();
+    if (kt + 1 < KT) {
+      ra = dec_a4<MODE>(a, ar, (kt + 1) * 16 + lk);
+      rb = *(const f32x4_d*)(a.W + (long)((kt + 1) * 16 + bk) * a.N + col0 + bn);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 16; kk += 2) {
+      const float av = As[b][kk + (lane >> 5)][wm * 32 + (lane & 31)];
+      const float bv = Bs[b][kk + (lane >> 5)][wn * 32 + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+  }
+  // accumulator element r of a lane: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+#pragma unroll
+  for (int r = 0; r < 16; ++r) Ct[wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][wn * 32 + (lane & 31)] = acc[r];
+  __syncthreads();
+
+  if constexpr (MODE == DM_LSTM0 || MODE == DM_LSTM) {
+    // packed gate columns: unit u's gates i, f, g, o are columns 4u .. 4u+3
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q, rr = idx >> 4, u = idx & 15;
+      const int r = row0 + rr;
+      if (r >= rows) continue;
+      const int col = col0 + 4 * u, U = col >> 2;
+      const float gi = Ct[rr][4 * u] + a.bias[col], gf = Ct[rr][4 * u + 1] + a.bias[col + 1];
+      const float gg = Ct[rr][4 * u + 2] + a.bias[col + 2], go = Ct[rr][4 * u + 3] + a.bias[col + 3];
+      const int id = a.ids[a.list[r]];
+      float* cp = a.c + ((long)id * a.L + a.layer) * a.H + U;
+      const float cn = sigm(gf) * *cp + sigm(gi) * tanhf(gg);
+      *cp = cn;
+      a.hn[((long)a.layer * a.n + r) * a.H + U] = sigm(go) * tanhf(cn);
+    }
+  } else if constexpr (MODE == DM_PROJ) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q, rr = idx >> 6, j = idx & 63;
+      const int r = row0 + rr;
+      if (r >= rows) continue;
+      const int id = a.ids[a.list[r]];
+      a.p[(long)id * a.P + col0 + j] = Ct[rr][j] + a.bias[col0 + j];
+    }
+    // the new h of every layer goes back to the stream state (nothing reads it any more in
+    // this round), and the slot's token has been consumed
+    for (int idx = tid; idx < 64 * a.L * 64; idx += 256) {
+      const int rr = idx / (a.L * 64), rem = idx - rr * a.L * 64, l = rem >> 6, j = rem & 63;
+      const int r = row0 + rr;
+      if (r >= rows) continue;
+      const int id = a.ids[a.list[r]];
+      for (int u = blockIdx.x * 64 + j; u < a.H; u += gridDim.x * 64)
+        a.h[((long)id * a.L + l) * a.H + u] = a.hn[((long)l * a.n + r) * a.H + u];
+    }
+    if (blockIdx.x == 0)
+      for (int rr = tid; rr < 64; rr += 256)
+        if (row0 + rr < rows) a.need[a.list[row0 + rr]] = 0;
+  } else {
+    // joint: argmax of the row over this tile's columns (bias added, columns past C ignored),
+    // ties to the lowest column; four threads per row
+    const int rr = tid >> 2, part4 = tid & 3;
+    float best = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int cc = part4 * 16 + j, col = col0 + cc;
+      if (col >= a.C) break;
+      const float v = Ct[rr][cc] + a.bias[col];
+      if (v > best || bi == INT_MAX) { best = v; bi = col; }
+    }
+#pragma unroll
+    for (int o = 1; o < 4; o <<= 1) {
+      const float ov = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (oi != INT_MAX && (bi == INT_MAX || ov > best || (ov == best && oi < bi))) { best = ov; bi = oi; }
+    }
+    const int r = row0 + rr;
+    if (part4 == 0 && r < rows) a.part[(long)r * a.ntiles + blockIdx.x] = make_float2(best, __int_as_float(bi));
+  }
+}
+
+struct DecRoundArgs {
+  const int32_t* ids;
+  int32_t* slot_t;      // [n] frame cursor
+  int32_t* slot_sym;    // [n] emissions at the cursor frame
+  int32_t* slot_tok;    // [n]
+  int32_t* slot_ntok;   // [n]
+  int32_t* need;        // [n]
+  int32_t* plist;       // [rounds + 1][n]
+  int32_t* pcnt;        // [rounds + 1]
+  int32_t* alist;       // [rounds + 1][n]
+  int32_t* acnt;        // [rounds + 1]
+  const float2* part;   // [n * nf][ntiles]
+  int32_t* tokens;      // [n][nf * m]
+  int32_t* tframes;     // [n][nf * m] or null
+  int32_t* counts;      // [n]
+  int32_t* pend;        // [S] token carried to the next call, -1 none
+  int n, nf, m, ntiles, blank, round, rounds;
+};
+
+// One block: per-call slot state, round lists and output padding.
+__global__ __launch_bounds__(256) void dec_begin_kernel(DecRoundArgs a) {
+  __shared__ int pc;
+  const int tid = threadIdx.x;
+  if (tid == 0) pc = 0;
+  for (int j = tid; j <= a.rounds; j += 256) { a.pcnt[j] = 0; a.acnt[j] = 0; }
+  __syncthreads();
+  for (int s = tid; s < a.n; s += 256) {
+    const int tok = a.pend[a.ids[s]];
+    a.slot_t[s] = 0; a.slot_sym[s] = 0; a.slot_ntok[s] = 0;
+    a.slot_tok[s] = tok; a.need[s] = tok >= 0;
+    if (tok >= 0) a.plist[atomicAdd(&pc, 1)] = s;
+    a.alist[s] = s;
+  }
+  const int tot = a.n * a.nf * a.m;
+  for (int i = tid; i < tot; i += 256) {
+    a.tokens[i] = -1;
+    if (a.tframes) a.tframes[i] = -1;
+  }
+  __syncthreads();
+  if (tid == 0) { a.pcnt[0] = pc; a.acnt[0] = a.n; }
+}
+
+// Greedy decision of round `round` for every slot on its A list (see the file comment).
+__global__ __launch_bounds__(256) void dec_decide_kernel(DecRoundArgs a) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int j = a.round;
+  if (e >= a.acnt[j]) return;
+  const int s = a.alist[(long)j * a.n + e];
+  int t = a.slot_t[s], sym = a.slot_sym[s];
+  for (int f = t; f < a.nf; ++f) {
+    const float2* pr = a.part + ((long)e * a.nf + f) * a.ntiles;
+    float best = pr[0].x;
+    int bi = __float_as_int(pr[0].y);
+    for (int q = 1; q < a.ntiles; ++q) {     // tiles in column order: strict > keeps the lower index
+      const float v = pr[q].x;
+      if (v > best) { best = v; bi = __float_as_int(pr[q].y); }
+    }
+    if (bi == a.blank) { sym = 0; continue; }
+    if (f != t) sym = 0;
+    const int k = a.slot_ntok[s];
+    a.tokens[(long)s * a.nf * a.m + k] = bi;
+    if (a.tframes) a.tframes[(long)s * a.nf * a.m + k] = f;
+    a.slot_ntok[s] = k + 1;
+    ++sym;
+    t = f;
+    if (sym == a.m) { t = f + 1; sym = 0; }
+    a.slot_t[s] = t; a.slot_sym[s] = sym;
+    a.slot_tok[s] = bi; a.need[s] = 1;
+    a.plist[(long)(j + 1) * a.n + atomicAdd(&a.pcnt[j + 1], 1)] = s;
+    if (t < a.nf) a.alist[(long)(j + 1) * a.n + atomicAdd(&a.acnt[j + 1], 1)] = s;
+    return;
+  }
+  a.slot_t[s] = a.nf; a.slot_sym[s] = 0;
+}
+
+// Carry the unconsumed token of each slot to its stream; emitted counts out.
+__global__ __launch_bounds__(256) void dec_end_kernel(DecRoundArgs a) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s >= a.n) return;
+  a.pend[a.ids[s]] = a.need[s] ? a.slot_tok[s] : -1;
+  a.counts[s] = a.slot_ntok[s];
+}
+
+struct DecResetArgs {
+  const int32_t* ids;
+  float* h; float* c; float* p; int32_t* pend;
+  int n, L, H, P, blank;
+};
+
+// One block per stream.
+__global__ __launch_bounds__(256) void dec_reset_kernel(DecResetArgs a) {
+  const int id = a.ids[blockIdx.x];
+  const long hs = (long)a.L * a.H;
+  for (long i = threadIdx.x; i < hs; i += 256) {
+    a.h[id * hs + i] = 0.0f;
+    a.c[id * hs + i] = 0.0f;
+  }
+  for (long i = threadIdx.x; i < a.P; i += 256) a.p[(long)id * a.P + i] = 0.0f;
+  if (threadIdx.x == 0) a.pend[id] = a.blank;
+}
+
+// ------------------------------------------------------------------------------- host side
+struct DecDims {
+  int P, H, L, V, C, Cpad, m, S, nfmax, flags, rounds_max;
+};
+
+bool dec_dims(const cac_dec_config* c, DecDims& d, std::string& why) {
+  if (!c) { why = "config is NULL"; return false; }
+  d.P = c->joint_dim; d.H = c->pred_hidden; d.L = c->pred_layers; d.V = c->vocab; d.m = c->max_symbols;
+  d.S = c->max_streams; d.nfmax = c->max_frames; d.flags = c->flags;
+  auto bad = [&](const char* msg) { why = msg; return false; };
+  if (d.P < 64 || d.P > 4096 || d.P % 64) return bad("joint_dim must be a multiple of 64 in [64, 4096]");
+  if (d.H < 16 || d.H > 4096 || d.H % 16) return bad("pred_hidden must be a multiple of 16 in [16, 4096]");
+  if (d.L < 1 || d.L > 8) return bad("pred_layers must be in [1, 8]");
+  if (d.V < 1 || d.V > (1 << 20)) return bad("vocab must be in [1, 2^20]");
+  if (d.m < 1 || d.m > 16) return bad("max_symbols must be in [1, 16]");
+  if (d.S < 1 || d.S > (1 << 16)) return bad("max_streams must be in [1, 65536]");
+  if (d.nfmax < 1 || d.nfmax > 16) return bad("max_frames must be in [1, 16]");
+  d.C = d.V + 2;
+  d.Cpad = (d.C + 63) / 64 * 64;
+  d.rounds_max = 1 + d.nfmax * d.m;
+  return true;
+}
+
+size_t dec_params(const DecDims& d) {
+  const size_t H = d.H, P = d.P, C = d.C;
+  return C * H + (size_t)d.L * (2 * H * 4 * H + 2 * 4 * H) + H * P + P + P * C + C;
+}
+
+struct DecLayout {
+  size_t embed, lstm_w, lstm_b, proj_w, proj_b, out_w, out_b, weights_end;
+  size_t h, c, p, pend;
+  size_t ids, slot_t, slot_sym, slot_tok, slot_ntok, need, plist, pcnt, alist, acnt, hn, part;
+  size_t total;
+};
+
+DecLayout dec_layout(const DecDims& d) {
+  DecLayout t{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { off = (off + 255) & ~(size_t)255; size_t o = off; off += bytes; return o; };
+  const size_t H = d.H, P = d.P, S = d.S, n = d.S, R = (size_t)d.rounds_max + 1;
+  t.embed = take((size_t)d.C * H * 4);
+  t.lstm_w = take((size_t)d.L * 2 * H * 4 * H * 4);
+  t.lstm_b = take((size_t)d.L * 4 * H * 4);
+  t.proj_w = take(H * P * 4);
+  t.proj_b = take(P * 4);
+  t.out_w = take(P * d.Cpad * 4);
+  t.out_b = take((size_t)d.Cpad * 4);
+  t.weights_end = take(0);
+  t.h = take(S * d.L * H * 4);
+  t.c = take(S * d.L * H * 4);
+  t.p = take(S * P * 4);
+  t.pend = take(S * 4);
+  t.ids = take(n * 4);
+  t.slot_t = take(n * 4); t.slot_sym = take(n * 4); t.slot_tok = take(n * 4); t.slot_ntok = take(n * 4);
+  t.need = take(n * 4);
+  t.plist = take(R * n * 4); t.pcnt = take(R * 4);
+  t.alist = take(R * n * 4); t.acnt = take(R * 4);
+  t.hn = take((size_t)d.L * n * H * 4);
+  t.part = take(n * d.nfmax * (size_t)(d.Cpad / 64) * 8);
+  t.total = take(0);
+  return t;
+}
+
+thread_local std::string g_dec_error;
+
+}  // namespace
+
+struct cac_dec {
+  DecDims d;
+  DecLayout lay;
+  char* ws = nullptr;
+  hipStream_t stream = nullptr;
+  bool dry = false;
+  std::vector<int32_t> stamp;
+  int32_t stamp_gen = 0;
+  std::string err;
+  template <class T> T* P(size_t off) const { return (T*)(ws + off); }
+  int fail(int code, const std::string& m) { err = m; return code; }
+};
+
+namespace {
+
+int dec_check_ids(cac_dec* c, int32_t n, const int32_t* ids) {
+  if (n < 1 || n > c->d.S) return c->fail(CAC_EINVAL, "stream count out of range");
+  if (!ids) return c->fail(CAC_EINVAL, "stream id list is NULL");
+  if (++c->stamp_gen == INT32_MAX) { std::fill(c->stamp.begin(), c->stamp.end(), 0); c->stamp_gen = 1; }
+  for (int i = 0; i < n; ++i) {
+    const int id = ids[i];
+    if (id < 0 || id >= c->d.S) return c->fail(CAC_EINVAL, "stream id " + std::to_string(id) + " out of range");
+    if (c->stamp[id] == c->stamp_gen) return c->fail(CAC_EINVAL, "stream id " + std::to_string(id) + " appears twice");
+    c->stamp[id] = c->stamp_gen;
+  }
+  return CAC_OK;
+}
+
+void dec_reset_launch(cac_dec* c, Launcher& L, int n) {
+  DecResetArgs r{c->P<int32_t>(c->lay.ids), c->P<float>(c->lay.h), c->P<float>(c->lay.c), c->P<float>(c->lay.p),
+                 c->P<int32_t>(c->lay.pend), n, c->d.L, c->d.H, c->d.P, c->d.V};
+  L.tag("dec_reset", 0.0, 0.0);
+  L.launch((const void*)&dec_reset_kernel, dim3(n), dim3(256), 0, &r);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t cac_dec_param_count(const cac_dec_config* cfg) {
+  DecDims d;
+  std::string why;
+  return dec_dims(cfg, d, why) ? dec_params(d) : 0;
+}
+
+size_t cac_dec_workspace_bytes(const cac_dec_config* cfg) {
+  DecDims d;
+  std::string why;
+  return dec_dims(cfg, d, why) ? dec_layout(d).total : 0;
+}
+
+const char* cac_dec_last_error(const cac_dec* ctx) { return ctx ? ctx->err.c_str() : g_dec_error.c_str(); }
+
+int32_t cac_dec_create(const cac_dec_config* cfg, const float* h_params, size_t n_params, void* d_workspace,
+                       size_t ws_bytes, void* hip_stream, cac_dec** out) {
+  g_dec_error.clear();
+  if (!out) { g_dec_error = "out is NULL"; return CAC_EINVAL; }
+  *out = nullptr;
+  DecDims d;
+  if (!dec_dims(cfg, d, g_dec_error)) return CAC_EINVAL;
+  if (!h_params) { g_dec_error = "parameter array is NULL"; return CAC_EINVAL; }
+  if (n_params != dec_params(d)) {
+    g_dec_error = "expected " + std::to_string(dec_params(d)) + " parameters, got " + std::to_string(n_params);
+    return CAC_EINVAL;
+  }
+  const bool dry = (d.flags & CAC_FLAG_DRY_RUN) != 0;
+  const DecLayout lay = dec_layout(d);
+  if (!dry) {
+    if (!d_workspace) { g_dec_error = "workspace is NULL"; return CAC_EINVAL; }
+    if (((uintptr_t)d_workspace) & 255) { g_dec_error = "workspace must be 256-byte aligned"; return CAC_EINVAL; }
+    if (ws_bytes < lay.total) { g_dec_error = "workspace too small: need " + std::to_string(lay.total) + " bytes"; return CAC_ENOMEM; }
+  }
+  cac_dec* c = new cac_dec();
+  c->d = d; c->lay = lay; c->ws = (char*)d_workspace; c->stream = (hipStream_t)hip_stream; c->dry = dry;
+  c->stamp.assign(d.S, 0);
+  if (dry) { *out = c; return CAC_OK; }
+  kernels_init();
+  // repack: LSTM gate columns per unit (unit u's i, f, g, o at 4u .. 4u+3), w_ih rows then w_hh
+  // rows as one [2H][4H] matrix, the two biases summed; joint columns padded to 64
+  const size_t H = d.H, P = d.P, C = d.C;
+  std::vector<uint8_t> buf(lay.weights_end, 0);
+  const float* q = h_params;
+  auto take = [&](size_t k) { const float* r = q; q += k; return r; };
+  memcpy(buf.data() + lay.embed, take(C * H), C * H * 4);
+  for (int l = 0; l < d.L; ++l) {
+    const float* wih = take(H * 4 * H);
+    const float* whh = take(H * 4 * H);
+    const float* bih = take(4 * H);
+    const float* bhh = take(4 * H);
+    float* w = (float*)(buf.data() + lay.lstm_w) + (size_t)l * 2 * H * 4 * H;
+    float* b = (float*)(buf.data() + lay.lstm_b) + (size_t)l * 4 * H;
+    for (size_t g = 0; g < 4; ++g)
+      for (size_t u = 0; u < H; ++u) {
+        const size_t src = g * H + u, dst = 4 * u + g;
+        b[dst] = bih[src] + bhh[src];
+        for (size_t k = 0; k < H; ++k) {
+          w[k * 4 * H + dst] = wih[k * 4 * H + src];
+          w[(H + k) * 4 * H + dst] = whh[k * 4 * H + src];
+        }
+      }
+  }
+  memcpy(buf.data() + lay.proj_w, take(H * P), H * P * 4);
+  memcpy(buf.data() + lay.proj_b, take(P), P * 4);
+  {
+    const float* w = take(P * C);
+    float* dst = (float*)(buf.data() + lay.out_w);
+    for (size_t k = 0; k < P; ++k) memcpy(dst + k * d.Cpad, w + k * C, C * 4);
+    memcpy(buf.data() + lay.out_b, take(C), C * 4);
+  }
+  hipError_t e = hipMemcpyAsync(c->ws, buf.data(), buf.size(), hipMemcpyHostToDevice, c->stream);
+  std::vector<int32_t> all(d.S);
+  for (int i = 0; i < d.S; ++i) all[i] = i;
+  if (e == hipSuccess) e = hipMemcpyAsync(c->ws + lay.ids, all.data(), (size_t)d.S * 4, hipMemcpyHostToDevice, c->stream);
+  if (e == hipSuccess) {
+    Launcher L;
+    L.stream = c->stream;
+    dec_reset_launch(c, L, d.S);
+    e = L.err;
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) {
+    g_dec_error = std::string("HIP error during create: ") + hipGetErrorString(e);
+    delete c;
+    return CAC_EHIP;
+  }
+  *out = c;
+  return CAC_OK;
+}
+
+int32_t cac_dec_greedy(cac_dec* c, int32_t n, const int32_t* ids, int32_t nf, const float* d_z, int32_t* d_tokens,
+                       int32_t* d_token_frames, int32_t* d_counts) {
+  if (!c) return CAC_EINVAL;
+  const DecDims& d = c->d;
+  int rc = dec_check_ids(c, n, ids);
+  if (rc) return rc;
+  if (nf < 1 || nf > d.nfmax) return c->fail(CAC_EINVAL, "n_frames must be in [1, max_frames]");
+  if (!d_z || !d_tokens || !d_counts) return c->fail(CAC_EINVAL, "z, tokens or counts pointer is NULL");
+  if (c->dry) return c->fail(CAC_ENODEV, "dry-run context: no device work");
+  const hipError_t pe = hipStreamQuery(c->stream);
+  if (pe != hipSuccess && pe != hipErrorNotReady)
+    return c->fail(CAC_EHIP, std::string("asynchronous device error from earlier work: ") + hipGetErrorString(pe));
+  const DecLayout& y = c->lay;
+  Launcher L;
+  L.stream = c->stream;
+  L.err = hipMemcpyAsync(c->ws + y.ids, ids, (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  const int rounds = 1 + nf * d.m, ntiles = d.Cpad / 64;
+  DecRoundArgs ra{};
+  ra.ids = c->P<int32_t>(y.ids);
+  ra.slot_t = c->P<int32_t>(y.slot_t); ra.slot_sym = c->P<int32_t>(y.slot_sym); ra.slot_tok = c->P<int32_t>(y.slot_tok);
+  ra.slot_ntok = c->P<int32_t>(y.slot_ntok); ra.need = c->P<int32_t>(y.need);
+  ra.plist = c->P<int32_t>(y.plist); ra.pcnt = c->P<int32_t>(y.pcnt);
+  ra.alist = c->P<int32_t>(y.alist); ra.acnt = c->P<int32_t>(y.acnt);
+  ra.part = c->P<float2>(y.part); ra.tokens = d_tokens; ra.tframes = d_token_frames; ra.counts = d_counts;
+  ra.pend = c->P<int32_t>(y.pend);
+  ra.n = n; ra.nf = nf; ra.m = d.m; ra.ntiles = ntiles; ra.blank = d.V; ra.rounds = rounds;
+  L.tag("dec_begin", 0.0, 0.0);
+  L.launch((const void*)&dec_begin_kernel, dim3(1), dim3(256), 0, &ra);
+  DecTileArgs ta{};
+  ta.ids = ra.ids; ta.slot_tok = ra.slot_tok; ta.embed = c->P<float>(y.embed);
+  ta.h = c->P<float>(y.h); ta.c = c->P<float>(y.c); ta.hn = c->P<float>(y.hn); ta.p = c->P<float>(y.p);
+  ta.need = ra.need; ta.z = d_z; ta.part = c->P<float2>(y.part);
+  ta.L = d.L; ta.H = d.H; ta.P = d.P; ta.C = d.C; ta.nf = nf; ta.ntiles = ntiles; ta.n = n;
+  const dim3 blk(256);
+  const unsigned prow = (unsigned)((n + 63) / 64), jrow = (unsigned)((n * nf + 63) / 64);
+  for (int j = 0; j < rounds && L.err == hipSuccess; ++j) {
+    // predictor step of the slots on P_j
+    DecTileArgs t = ta;
+    t.list = ra.plist + (size_t)j * n;
+    t.count = ra.pcnt + j;
+    for (int l = 0; l < d.L; ++l) {
+      t.layer = l; t.K = 2 * d.H; t.N = 4 * d.H;
+      t.W = c->P<float>(y.lstm_w) + (size_t)l * 2 * d.H * 4 * d.H;
+      t.bias = c->P<float>(y.lstm_b) + (size_t)l * 4 * d.H;
+      L.tag("dec_lstm", 0.0, 0.0);
+      L.launch(l == 0 ? (const void*)&dec_tile_kernel<DM_LSTM0> : (const void*)&dec_tile_kernel<DM_LSTM>,
+               dim3(4 * d.H / 64, prow), blk, 0, &t);
+    }
+    t.K = d.H; t.N = d.P; t.W = c->P<float>(y.proj_w); t.bias = c->P<float>(y.proj_b);
+    L.tag("dec_proj", 0.0, 0.0);
+    L.launch((const void*)&dec_tile_kernel<DM_PROJ>, dim3(d.P / 64, prow), blk, 0, &t);
+    // joint of the slots on A_j, all frames
+    DecTileArgs jt = ta;
+    jt.list = ra.alist + (size_t)j * n;
+    jt.count = ra.acnt + j;
+    jt.K = d.P; jt.N = d.Cpad; jt.W = c->P<float>(y.out_w); jt.bias = c->P<float>(y.out_b);
+    L.tag("dec_joint", 0.0, 0.0);
+    L.launch((const void*)&dec_tile_kernel<DM_JOINT>, dim3(ntiles, jrow), blk, 0, &jt);
+    DecRoundArgs r = ra;
+    r.round = j;
+    L.tag("dec_decide", 0.0, 0.0);
+    L.launch((const void*)&dec_decide_kernel, dim3((n + 255) / 256), blk, 0, &r);
+  }
+  L.tag("dec_end", 0.0, 0.0);
+  L.launch((const void*)&dec_end_kernel, dim3((n + 255) / 256), blk, 0, &ra);
+  if (L.err != hipSuccess) return c->fail(CAC_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(L.err));
+  return CAC_OK;
+}
+
+int32_t cac_dec_reset(cac_dec* c, int32_t n, const int32_t* ids) {
+  if (!c) return CAC_EINVAL;
+  int rc = dec_check_ids(c, n, ids);
+  if (rc) return rc;
+  if (c->dry) return c->fail(CAC_ENODEV, "dry-run context: no device work");
+  Launcher L;
+  L.stream = c->stream;
+  L.err = hipMemcpyAsync(c->ws + c->lay.ids, ids, (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  dec_reset_launch(c, L, n);
+  if (L.err != hipSuccess) return c->fail(CAC_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(L.err));
+  return n;
+}
+
+int32_t cac_dec_destroy(cac_dec* c) {
+  delete c;
+  return CAC_OK;
+}
+
+}  // extern "C"

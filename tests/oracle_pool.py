@@ -39,10 +39,11 @@ def pool() -> ProcessPoolExecutor:
 
 def _oracle(cfg):
     from oracle import Oracle
-    from synth import make_weights
+    from oracle.decoder import GreedyDecoder
+    from synth import DecConfig, make_dec_weights, make_weights
     if cfg not in _CACHE:
         _CACHE.clear()
-        _CACHE[cfg] = Oracle(cfg, make_weights(cfg))
+        _CACHE[cfg] = GreedyDecoder(cfg, make_dec_weights(cfg)) if isinstance(cfg, DecConfig) else Oracle(cfg, make_weights(cfg))
     return _CACHE[cfg]
 
 
@@ -94,3 +95,39 @@ def shutdown():
     if _POOL is not None:
         _POOL.shutdown(wait=True, cancel_futures=True)
         _POOL = None
+
+
+def _dec_group(cfg, ids, calls):
+    """Greedy decoding of streams ``ids`` over their seeded projected frames, ``calls`` calls of
+    cfg.frames frames each from fresh states; per call, per stream, the (frame, class) list."""
+    from synth import make_dec_inputs
+    dec = _oracle(cfg)
+    out = []
+    for s in ids:
+        st = dec.new_state()
+        xs = make_dec_inputs(cfg, s, calls)
+        out.append([dec.decode(st, xs[c]) for c in range(calls)])
+    return out
+
+
+def submit_decode(cfg, ids, calls, group=None):
+    ids = list(ids)
+    if group is None:
+        group = max(1, -(-len(ids) // (2 * _WORKERS)))
+    groups = [ids[i:i + group] for i in range(0, len(ids), group)]
+    return groups, [pool().submit(_dec_group, cfg, g, calls) for g in groups]
+
+
+def collect_decode(handle):
+    """{stream id: [per call: [(frame, class), ...]]}."""
+    groups, futs = handle
+    t0, pending = time.time(), set(futs)
+    while pending:
+        _, pending = wait(pending, timeout=30, return_when=FIRST_COMPLETED)
+        print(f"oracle decode: {len(futs) - len(pending)}/{len(futs)} stream groups done after {time.time() - t0:.0f} s",
+              flush=True)
+    res = {}
+    for g, fut in zip(groups, futs):
+        for s, calls in zip(g, fut.result()):
+            res[s] = calls
+    return res

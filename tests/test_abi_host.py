@@ -14,13 +14,15 @@ from cache_aware_conformer_amd.binding import CAC_EINVAL, CAC_ENODEV, CAC_ENOMEM
 from synth import C1, C2, C3, C4, C5, make_weights, weight_names
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "cac.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include"))) if h.endswith(".h")]
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(cac_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(cac_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_function():
@@ -231,3 +233,37 @@ def test_profile_replay_needs_a_replayed_push_graph():
     assert b"no push graph" in enc.lib.cac_last_error(enc.ctx)
     assert enc.lib.cac_profile_replay(enc.ctx, None, 5, None, None, None, None) == CAC_EINVAL
     assert enc.lib.cac_profile_replay(enc.ctx, b"gemm", 0, None, None, None, None) == CAC_EINVAL
+
+
+# ----------------------------------------------------------------------- greedy decoding ABI
+
+def test_decoder_param_layout_and_validation():
+    from synth import D1, dec_weight_names, make_dec_weights
+    lib = cac.load()
+    c = cac.binding.make_dec_config(D1, max_streams=4)
+    n = lib.cac_dec_param_count(C.byref(c))
+    assert n == sum(int(np.prod(s)) for _, s in cac.binding.dec_param_order(D1))
+    assert [nm for nm, _ in cac.binding.dec_param_order(D1)] == [nm for nm, *_ in dec_weight_names(D1)]
+    assert lib.cac_dec_workspace_bytes(C.byref(c)) > 0
+    for field, value in [("joint_dim", 100), ("pred_hidden", 20), ("pred_layers", 0), ("vocab", 0),
+                         ("max_symbols", 0), ("max_streams", 0), ("max_frames", 17)]:
+        bad = cac.binding.make_dec_config(D1, max_streams=4)
+        setattr(bad, field, value)
+        assert lib.cac_dec_param_count(C.byref(bad)) == 0, field
+        assert lib.cac_dec_workspace_bytes(C.byref(bad)) == 0, field
+    dec = cac.StreamingDecoder(D1, make_dec_weights(D1), max_streams=4, flags=cac.CAC_FLAG_DRY_RUN)
+    ip = lambda a: np.asarray(a, np.int32).ctypes.data_as(C.POINTER(C.c_int32))  # noqa: E731
+    z = C.c_void_p(256)
+    assert lib.cac_dec_greedy(dec.ctx, 1, ip([0]), 2, z, z, None, z) == CAC_ENODEV
+    assert lib.cac_dec_greedy(dec.ctx, 2, ip([1, 1]), 2, z, z, None, z) == CAC_EINVAL
+    assert b"twice" in lib.cac_dec_last_error(dec.ctx)
+    assert lib.cac_dec_greedy(dec.ctx, 1, ip([4]), 2, z, z, None, z) == CAC_EINVAL
+    assert lib.cac_dec_greedy(dec.ctx, 1, ip([0]), 3, z, z, None, z) == CAC_EINVAL   # max_frames is 2
+    assert lib.cac_dec_greedy(dec.ctx, 1, ip([0]), 0, z, z, None, z) == CAC_EINVAL
+    assert lib.cac_dec_greedy(dec.ctx, 1, ip([0]), 2, None, z, None, z) == CAC_EINVAL
+    assert lib.cac_dec_greedy(dec.ctx, 0, ip([0]), 2, z, z, None, z) == CAC_EINVAL
+    assert lib.cac_dec_reset(dec.ctx, 1, ip([3])) == CAC_ENODEV
+    assert lib.cac_dec_reset(dec.ctx, 1, ip([-1])) == CAC_EINVAL
+    with pytest.raises(CacError):
+        cac.StreamingDecoder(D1, {k: v[:1] for k, v in make_dec_weights(D1).items()}, max_streams=4,
+                             flags=cac.CAC_FLAG_DRY_RUN)
