@@ -4,8 +4,9 @@ A step is one push of one chunk for every stream of the workload through the who
 (front end if any, 17 blocks, joint projection), inputs already resident in HBM. The headline
 workload is the largest one-GPU configuration: 1024 streams at staggered positions, each
 pushing 16 log-mel frames through the front end and the 17-layer d=512 encoder in bf16 (fp32
-accumulate). The one-stream float32 encoder (the weight-bandwidth-bound case) is measured in
-the same run and reported in the same JSON line under "secondary". Prints one JSON line.
+accumulate). The one-stream float32 encoder (the weight-bandwidth-bound case) and greedy
+RNNT + EOU decoding of 1024 streams are measured in the same run and reported in the same JSON
+line under "secondary". Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload C4|C2|C3|C5] [--secondary C2|none]
 """
@@ -37,6 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--secondary", default="C2", help="second workload reported in the same line, or 'none'")
+    ap.add_argument("--decode", default="D2", help="greedy-decoding workload reported in the same line, or 'none'")
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time per CPU-baseline mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -244,6 +246,80 @@ def run_workload(key: str, steps, warmup: int, profile_steps: int, want_cpu: boo
     return res
 
 
+FP32_MFMA_PEAK_TFLOPS = 157.3  # dense fp32 matrix
+
+
+def run_decode(key: str, steps, warmup: int, profile_steps: int):
+    """Greedy decoding throughput of one decode workload: every stream decodes its next
+    ``frames`` projected frames per call (inputs resident in HBM), state carried across calls."""
+    import torch
+
+    from cache_aware_conformer_amd import StreamingDecoder
+    from synth import DEC_CONFIGS, make_dec_inputs, make_dec_weights
+
+    cfg = DEC_CONFIGS[key]
+    steps = steps if steps is not None else 100
+    S = cfg.streams
+    dev = torch.device("cuda:0")
+    dec = StreamingDecoder(cfg, make_dec_weights(cfg), max_streams=S)
+    per = min(cfg.calls, warmup + steps + profile_steps + 1)
+    xs = np.ascontiguousarray(np.stack([make_dec_inputs(cfg, s, per) for s in range(S)]).swapaxes(0, 1))
+    z = torch.from_numpy(xs).to(dev)
+    del xs
+    ids = list(range(S))
+    tok = torch.empty((S, cfg.frames * cfg.max_symbols), dtype=torch.int32, device=dev)
+    frm = torch.empty_like(tok)
+    cnt = torch.empty(S, dtype=torch.int32, device=dev)
+    k = 0
+
+    def call():
+        nonlocal k
+        dec.decode(ids, z[k % per], tok, frm, cnt)
+        k += 1
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    dec.profile(True)
+    emitted = 0
+    for _ in range(profile_steps):
+        call()
+        emitted += int(cnt.sum().item())
+    torch.cuda.synchronize()
+    prof = dec.profile_read()
+    dec.profile(False)
+    busy = {n: v for n, v in prof.items() if not n.endswith("/idle")}
+    dom = max(busy, key=lambda n: busy[n][1])
+    launches, tms, by, fl = busy[dom]
+    us = tms / launches * 1e3
+    roof = {"bound": "mfma", "achieved": fl / launches / (us * 1e-6) / 1e12, "peak": FP32_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "traffic": None, "kernel": dom, "avg_launch_us": us,
+            "launches_per_step": launches / profile_steps, "algorithmic_flops_per_launch": fl / launches,
+            "algorithmic_bytes_per_launch": by / launches,
+            "timing": "per-launch HIP events bound to each dispatch (include the event markers)"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    res = {"value": S * cfg.frames * steps / (ms / 1e3), "unit": "frames/s", "ms_per_step": ms / steps,
+           "steps": steps, "dtype": "f32",
+           "emitted_classes_per_step": emitted / profile_steps,
+           "config": {"workload": cfg.name, "streams": S, "frames_per_call": cfg.frames,
+                      "pred_layers": cfg.pred_layers, "pred_hidden": cfg.pred_hidden, "joint_dim": cfg.joint_dim,
+                      "classes": cfg.classes, "max_symbols": cfg.max_symbols,
+                      "rounds_per_call": 1 + cfg.frames * cfg.max_symbols},
+           "roofline": roof,
+           "kernels": {n: {"launches_per_step": v[0] / profile_steps, "us_per_step": v[1] / profile_steps * 1e3}
+                       for n, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}}
+    dec.close()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -274,6 +350,9 @@ def main():
                                                          ("value", "ms_per_step", "steps", "dtype", "config",
                                                           "roofline", "step")}}
         res["secondary"][sec["config"]["workload"]]["unit"] = "frames/s"
+    if args.decode and args.decode.lower() != "none":
+        dres = run_decode(args.decode, args.steps, args.warmup, args.profile_steps)
+        res.setdefault("secondary", {})[dres["config"]["workload"]] = dres
     print(json.dumps(res))
 
 

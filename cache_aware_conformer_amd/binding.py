@@ -47,6 +47,10 @@ SIGNATURES = {
     "cac_dec_reset": (_i32, [_vp, _i32, _ip]),
     "cac_dec_destroy": (_i32, [_vp]),
     "cac_dec_last_error": (C.c_char_p, [_vp]),
+    "cac_dec_set_graph": (_i32, [_vp, _i32]),
+    "cac_dec_profile": (_i32, [_vp, _i32]),
+    "cac_dec_profile_read": (_i32, [_vp, _i32, C.c_char_p, _i32, C.POINTER(C.c_int64), C.POINTER(C.c_double),
+                                    C.POINTER(C.c_double), C.POINTER(C.c_double)]),
     # include/cac.h
     "cac_param_count": (_sz, [_CFGP]),
     "cac_workspace_bytes": (_sz, [_CFGP]),
@@ -458,6 +462,25 @@ class StreamingDecoder:
     def reset(self, stream_ids):
         ids, idp = _ids(stream_ids)
         return self._check(self.lib.cac_dec_reset(self.ctx, ids.size, idp))
+
+    def set_graph(self, enable: bool):
+        return self._check(self.lib.cac_dec_set_graph(self.ctx, int(bool(enable))))
+
+    def profile(self, enable: bool):
+        return self._check(self.lib.cac_dec_profile(self.ctx, int(bool(enable))))
+
+    def profile_read(self) -> dict:
+        """{kernel name: (launches, total_ms, bytes, flops)} of the launches since profile(True)."""
+        n = self._check(self.lib.cac_dec_profile_read(self.ctx, 0, None, 64, None, None, None, None))
+        names = C.create_string_buffer(64 * max(n, 1))
+        launches = (C.c_int64 * max(n, 1))()
+        ms, by, fl = (C.c_double * max(n, 1))(), (C.c_double * max(n, 1))(), (C.c_double * max(n, 1))()
+        n = self._check(self.lib.cac_dec_profile_read(self.ctx, n, names, 64, launches, ms, by, fl))
+        out = {}
+        for i in range(n):
+            nm = names.raw[64 * i:64 * (i + 1)].split(b"\0", 1)[0].decode()
+            out[nm] = (int(launches[i]), float(ms[i]), float(by[i]), float(fl[i]))
+        return out
 
     def close(self):
         if getattr(self, "ctx", None):

@@ -23,6 +23,7 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -37,7 +38,9 @@ namespace {
 typedef __attribute__((ext_vector_type(16))) float f32x16_d;
 typedef __attribute__((ext_vector_type(4))) float f32x4_d;
 
-enum DecMode { DM_LSTM0 = 0, DM_LSTM = 1, DM_PROJ = 2, DM_JOINT = 3 };
+// DM_LSTM0: the first LSTM layer, whose input half embed[token] W_ih + biases is a per-token
+// table (DM_TABLE, computed once at create), so its product covers only h W_hh.
+enum DecMode { DM_LSTM0 = 0, DM_LSTM = 1, DM_PROJ = 2, DM_JOINT = 3, DM_TABLE = 4 };
 
 struct DecTileArgs {
   int K, N;                 // contraction length, output columns (a multiple of 64)
@@ -55,34 +58,54 @@ struct DecTileArgs {
   int32_t* need;            // [n] slot still has to consume slot_tok
   const float* z;           // [n][nf][P] caller's projected encoder frames
   float2* part;             // [n * nf][ntiles] joint argmax per 64-column tile (value, index)
+  float* table;             // [C][4H] embed[token] W_ih + b_ih + b_hh (first layer's input half)
   int layer, L, H, P, C, nf, ntiles, n;
 };
 
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-// Element k of the A row of list row r (r < rows).
+// Where the A row of list row r (r < rows) comes from, resolved once per block: element k is
+// ReLU(s0[k] + s1[k]) for the joint, s0[k] for k < split and s1[k - split] after it for the
+// LSTM layers above the first, s0[k] otherwise.
+struct ARow {
+  const float* s0;
+  const float* s1;
+  int split;
+};
+
 template <int MODE>
-__device__ __forceinline__ f32x4_d dec_a4(const DecTileArgs& a, int r, int k) {
+__device__ __forceinline__ ARow dec_arow(const DecTileArgs& a, int r) {
   if constexpr (MODE == DM_JOINT) {
     const int slot = a.list[r / a.nf], f = r - (r / a.nf) * a.nf;
-    const int id = a.ids[slot];
-    const f32x4_d zv = *(const f32x4_d*)(a.z + ((long)slot * a.nf + f) * a.P + k);
-    const f32x4_d pv = *(const f32x4_d*)(a.p + (long)id * a.P + k);
-    f32x4_d v = zv + pv;
-    v.x = fmaxf(v.x, 0.0f); v.y = fmaxf(v.y, 0.0f); v.z = fmaxf(v.z, 0.0f); v.w = fmaxf(v.w, 0.0f);
-    return v;
+    return {a.z + ((long)slot * a.nf + f) * a.P, a.p + (long)a.ids[slot] * a.P, 0};
   } else if constexpr (MODE == DM_PROJ) {
-    return *(const f32x4_d*)(a.hn + ((long)(a.L - 1) * a.n + r) * a.H + k);
+    return {a.hn + ((long)(a.L - 1) * a.n + r) * a.H, nullptr, 0};
+  } else if constexpr (MODE == DM_TABLE) {
+    return {a.embed + (long)r * a.H, nullptr, 0};
+  } else if constexpr (MODE == DM_LSTM0) {
+    return {a.h + (long)a.ids[a.list[r]] * a.L * a.H, nullptr, 0};
   } else {
-    const int slot = a.list[r];
-    if (k < a.H) {
-      if constexpr (MODE == DM_LSTM0) return *(const f32x4_d*)(a.embed + (long)a.slot_tok[slot] * a.H + k);
-      else return *(const f32x4_d*)(a.hn + ((long)(a.layer - 1) * a.n + r) * a.H + k);
-    }
-    const int id = a.ids[slot];
-    return *(const f32x4_d*)(a.h + ((long)id * a.L + a.layer) * a.H + (k - a.H));
+    const int id = a.ids[a.list[r]];
+    return {a.hn + ((long)(a.layer - 1) * a.n + r) * a.H, a.h + ((long)id * a.L + a.layer) * a.H, a.H};
   }
 }
+
+template <int MODE>
+__device__ __forceinline__ f32x4_d dec_a4(const ARow& src, int k) {
+  if constexpr (MODE == DM_JOINT) {
+    f32x4_d v = *(const f32x4_d*)(src.s0 + k) + *(const f32x4_d*)(src.s1 + k);
+    v.x = fmaxf(v.x, 0.0f); v.y = fmaxf(v.y, 0.0f); v.z = fmaxf(v.z, 0.0f); v.w = fmaxf(v.w, 0.0f);
+    return v;
+  } else if constexpr (MODE == DM_LSTM) {
+    return k < src.split ? *(const f32x4_d*)(src.s0 + k) : *(const f32x4_d*)(src.s1 + (k - src.split));
+  } else {
+    return *(const f32x4_d*)(src.s0 + k);
+  }
+}
+
+constexpr int DEC_BK = 64;                    // k per step
+constexpr int DEC_AS = 65, DEC_BS = 68;        // LDS row strides (A k-major, W row-major)
+constexpr size_t DEC_LDS = (size_t)2 * DEC_BK * (DEC_AS + DEC_BS) * sizeof(float);  // 68 KB: two k-tile buffers
 
 template <int MODE>
 __global__ __launch_bounds__(256) void dec_tile_kernel(DecTileArgs a) {
@@ -90,33 +113,60 @@ __global__ __launch_bounds__(256) void dec_tile_kernel(DecTileArgs a) {
   const int rows = MODE == DM_JOINT ? cnt * a.nf : cnt;
   const int row0 = blockIdx.y * 64, col0 = blockIdx.x * 64;
   if (row0 >= rows) return;  // the whole block: nothing on the list for these rows
-  __shared__ float As[2][16][68];   // k-major: As[buf][k][row]
-  __shared__ float Bs[2][16][68];   // Bs[buf][k][col]
-  __shared__ float Ct[64][65];
+  // buffer b: A tile As[k][row] (stride DEC_AS), then W tile Bs[k][col] (stride DEC_BS); after the
+  // k-loop the accumulator tile Ct[64][65] reuses the space
+  extern __shared__ __attribute__((aligned(16))) float dlds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int lr = tid >> 2, lk = (tid & 3) * 4;          // A loader: row lr, k lk .. lk+3
-  const int ar = min(row0 + lr, rows - 1);              // rows past the end reload the last one
-  const int bk = tid >> 4, bn = (tid & 15) * 4;         // W loader: k bk, columns bn .. bn+3
-  const int KT = a.K / 16;
-  f32x4_d ra = dec_a4<MODE>(a, ar, lk);
-  f32x4_d rb = *(const f32x4_d*)(a.W + (long)bk * a.N + col0 + bn);
+  const int lr = tid >> 2, lk = (tid & 3) * 16;         // A loader: row lr, k lk .. lk+15
+  const ARow src = dec_arow<MODE>(a, min(row0 + lr, rows - 1));  // rows past the end reload the last one
+  const int bk = tid >> 2, bn = (tid & 3) * 16;         // W loader: k bk, columns bn .. bn+15
+  const int KT = a.K / DEC_BK;
+  f32x4_d ra[4], rb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    ra[q] = dec_a4<MODE>(src, lk + 4 * q);
+    rb[q] = *(const f32x4_d*)(a.W + (long)bk * a.N + col0 + bn + 4 * q);
+  }
   f32x16_d acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
   for (int kt = 0; kt < KT; ++kt) {
-    const int b = kt & 1;
-    As[b][lk + 0][lr] = ra.x; As[b][lk + 1][lr] = ra.y; As[b][lk + 2][lr] = ra.z; As[b][lk + 3][lr] = ra.w;
-    *(f32x4_d*)&Bs[b][bk][bn] = rb;
+    float* As = dlds + (kt & 1) * DEC_BK * (DEC_AS + DEC_BS);
+    float* Bs = As + DEC_BK * DEC_AS;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      As[(lk + 4 * q + 0) * DEC_AS + lr] = ra[q].x;
+      As[(lk + 4 * q + 1) * DEC_AS + lr] = ra[q].y;
+      As[(lk + 4 * q + 2) * DEC_AS + lr] = ra[q].z;
+      As[(lk + 4 * q + 3) * DEC_AS + lr] = ra[q].w;
+      *(f32x4_d*)&Bs[bk * DEC_BS + bn + 4 * q] = rb[q];
+    }
     __syncthreads();
     if (kt + 1 < KT) {
-      ra = dec_a4<MODE>(a, ar, (kt + 1) * 16 + lk);
-      rb = *(const f32x4_d*)(a.W + (long)((kt + 1) * 16 + bk) * a.N + col0 + bn);
+      const int k1 = (kt + 1) * DEC_BK;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        ra[q] = dec_a4<MODE>(src, k1 + lk + 4 * q);
+        rb[q] = *(const f32x4_d*)(a.W + (long)(k1 + bk) * a.N + col0 + bn + 4 * q);
+      }
     }
 #pragma unroll
-    for (int kk = 0; kk < 16; kk += 2) {
-      const float av = As[b][kk + (lane >> 5)][wm * 32 + (lane & 31)];
-      const float bv = Bs[b][kk + (lane >> 5)][wn * 32 + (lane & 31)];
+    for (int kk = 0; kk < DEC_BK; kk += 2) {
+      const float av = As[(kk + (lane >> 5)) * DEC_AS + wm * 32 + (lane & 31)];
+      const float bv = Bs[(kk + (lane >> 5)) * DEC_BS + wn * 32 + (lane & 31)];
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with the k-tile buffers
+  float (*Ct)[65] = (float (*)[65])dlds;
+  // slot, stream id and token of every row of the tile, looked up once
+  __shared__ int rslot[64], rid[64], rtok[64];
+  if constexpr (MODE == DM_LSTM0 || MODE == DM_LSTM || MODE == DM_PROJ) {
+    if (tid < 64) {
+      const int r = min(row0 + tid, rows - 1), slot = a.list[r];
+      rslot[tid] = slot;
+      rid[tid] = a.ids[slot];
+      rtok[tid] = MODE == DM_LSTM0 ? a.slot_tok[slot] : 0;
     }
   }
   // accumulator element r of a lane: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
@@ -132,36 +182,45 @@ __global__ __launch_bounds__(256) void dec_tile_kernel(DecTileArgs a) {
       const int r = row0 + rr;
       if (r >= rows) continue;
       const int col = col0 + 4 * u, U = col >> 2;
-      const float gi = Ct[rr][4 * u] + a.bias[col], gf = Ct[rr][4 * u + 1] + a.bias[col + 1];
-      const float gg = Ct[rr][4 * u + 2] + a.bias[col + 2], go = Ct[rr][4 * u + 3] + a.bias[col + 3];
-      const int id = a.ids[a.list[r]];
+      const int id = rid[rr];
+      // first layer: the token's row of the input table; other layers: the summed biases
+      const float* add = MODE == DM_LSTM0 ? a.table + (long)rtok[rr] * a.N + col : a.bias + col;
+      const float gi = Ct[rr][4 * u] + add[0], gf = Ct[rr][4 * u + 1] + add[1];
+      const float gg = Ct[rr][4 * u + 2] + add[2], go = Ct[rr][4 * u + 3] + add[3];
       float* cp = a.c + ((long)id * a.L + a.layer) * a.H + U;
       const float cn = sigm(gf) * *cp + sigm(gi) * tanhf(gg);
       *cp = cn;
       a.hn[((long)a.layer * a.n + r) * a.H + U] = sigm(go) * tanhf(cn);
     }
+  } else if constexpr (MODE == DM_TABLE) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 256 * q, rr = idx >> 6, j = idx & 63;
+      if (row0 + rr < rows) a.table[(long)(row0 + rr) * a.N + col0 + j] = Ct[rr][j] + a.bias[col0 + j];
+    }
   } else if constexpr (MODE == DM_PROJ) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int idx = tid + 256 * q, rr = idx >> 6, j = idx & 63;
-      const int r = row0 + rr;
-      if (r >= rows) continue;
-      const int id = a.ids[a.list[r]];
-      a.p[(long)id * a.P + col0 + j] = Ct[rr][j] + a.bias[col0 + j];
+      if (row0 + rr < rows) a.p[(long)rid[rr] * a.P + col0 + j] = Ct[rr][j] + a.bias[col0 + j];
     }
     // the new h of every layer goes back to the stream state (nothing reads it any more in
-    // this round), and the slot's token has been consumed
-    for (int idx = tid; idx < 64 * a.L * 64; idx += 256) {
-      const int rr = idx / (a.L * 64), rem = idx - rr * a.L * 64, l = rem >> 6, j = rem & 63;
-      const int r = row0 + rr;
-      if (r >= rows) continue;
-      const int id = a.ids[a.list[r]];
-      for (int u = blockIdx.x * 64 + j; u < a.H; u += gridDim.x * 64)
-        a.h[((long)id * a.L + l) * a.H + u] = a.hn[((long)l * a.n + r) * a.H + u];
+    // this round): block column c copies units [64c, 64c + 64) (and every further
+    // gridDim.x * 64), four threads per row, 16 units each
+    {
+      const int rr = tid >> 2, u0 = (tid & 3) * 16, r = row0 + rr;
+      if (r < rows) {
+        const long id = rid[rr];
+        for (int l = 0; l < a.L; ++l)
+          for (int ub = blockIdx.x * 64; ub < a.H; ub += gridDim.x * 64)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *(f32x4_d*)(a.h + (id * a.L + l) * a.H + ub + u0 + 4 * q) =
+                  *(const f32x4_d*)(a.hn + ((long)l * a.n + r) * a.H + ub + u0 + 4 * q);
+      }
     }
-    if (blockIdx.x == 0)
-      for (int rr = tid; rr < 64; rr += 256)
-        if (row0 + rr < rows) a.need[a.list[row0 + rr]] = 0;
+    // the slot's token has been consumed
+    if (blockIdx.x == 0 && tid < 64 && row0 + tid < rows) a.need[rslot[tid]] = 0;
   } else {
     // joint: argmax of the row over this tile's columns (bias added, columns past C ignored),
     // ties to the lowest column; four threads per row
@@ -198,9 +257,11 @@ struct DecRoundArgs {
   int32_t* alist;       // [rounds + 1][n]
   int32_t* acnt;        // [rounds + 1]
   const float2* part;   // [n * nf][ntiles]
-  int32_t* tokens;      // [n][nf * m]
-  int32_t* tframes;     // [n][nf * m] or null
-  int32_t* counts;      // [n]
+  int32_t* tokbuf;      // [n][nf * m] workspace: emitted classes
+  int32_t* frmbuf;      // [n][nf * m] workspace: their frames
+  int32_t* tokens;      // [n][nf * m] caller's (end kernel only)
+  int32_t* tframes;     // [n][nf * m] caller's or null (end kernel only)
+  int32_t* counts;      // [n] caller's (end kernel only)
   int32_t* pend;        // [S] token carried to the next call, -1 none
   int n, nf, m, ntiles, blank, round, rounds;
 };
@@ -221,8 +282,8 @@ __global__ __launch_bounds__(256) void dec_begin_kernel(DecRoundArgs a) {
   }
   const int tot = a.n * a.nf * a.m;
   for (int i = tid; i < tot; i += 256) {
-    a.tokens[i] = -1;
-    if (a.tframes) a.tframes[i] = -1;
+    a.tokbuf[i] = -1;
+    a.frmbuf[i] = -1;
   }
   __syncthreads();
   if (tid == 0) { a.pcnt[0] = pc; a.acnt[0] = a.n; }
@@ -246,8 +307,8 @@ __global__ __launch_bounds__(256) void dec_decide_kernel(DecRoundArgs a) {
     if (bi == a.blank) { sym = 0; continue; }
     if (f != t) sym = 0;
     const int k = a.slot_ntok[s];
-    a.tokens[(long)s * a.nf * a.m + k] = bi;
-    if (a.tframes) a.tframes[(long)s * a.nf * a.m + k] = f;
+    a.tokbuf[(long)s * a.nf * a.m + k] = bi;
+    a.frmbuf[(long)s * a.nf * a.m + k] = f;
     a.slot_ntok[s] = k + 1;
     ++sym;
     t = f;
@@ -261,12 +322,30 @@ __global__ __launch_bounds__(256) void dec_decide_kernel(DecRoundArgs a) {
   a.slot_t[s] = a.nf; a.slot_sym[s] = 0;
 }
 
-// Carry the unconsumed token of each slot to its stream; emitted counts out.
+// Carry the unconsumed token of each slot to its stream; emitted classes, their frames and the
+// counts out to the caller.
 __global__ __launch_bounds__(256) void dec_end_kernel(DecRoundArgs a) {
   const int s = blockIdx.x * 256 + threadIdx.x;
   if (s >= a.n) return;
   a.pend[a.ids[s]] = a.need[s] ? a.slot_tok[s] : -1;
   a.counts[s] = a.slot_ntok[s];
+  const long w = (long)a.nf * a.m, o = (long)s * w;
+  for (long i = 0; i < w; ++i) {
+    a.tokens[o + i] = a.tokbuf[o + i];
+    if (a.tframes) a.tframes[o + i] = a.frmbuf[o + i];
+  }
+}
+
+// The caller's projected frames into the workspace (so the joint nodes never hold a caller
+// pointer and a replayed call re-points only this node and the end kernel's).
+struct DecStageArgs {
+  const f32x4_d* z;
+  f32x4_d* zbuf;
+  long n4;
+};
+
+__global__ __launch_bounds__(256) void dec_stage_kernel(DecStageArgs a) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < a.n4; i += (long)gridDim.x * 256) a.zbuf[i] = a.z[i];
 }
 
 struct DecResetArgs {
@@ -298,7 +377,7 @@ bool dec_dims(const cac_dec_config* c, DecDims& d, std::string& why) {
   d.S = c->max_streams; d.nfmax = c->max_frames; d.flags = c->flags;
   auto bad = [&](const char* msg) { why = msg; return false; };
   if (d.P < 64 || d.P > 4096 || d.P % 64) return bad("joint_dim must be a multiple of 64 in [64, 4096]");
-  if (d.H < 16 || d.H > 4096 || d.H % 16) return bad("pred_hidden must be a multiple of 16 in [16, 4096]");
+  if (d.H < 64 || d.H > 4096 || d.H % 64) return bad("pred_hidden must be a multiple of 64 in [64, 4096]");
   if (d.L < 1 || d.L > 8) return bad("pred_layers must be in [1, 8]");
   if (d.V < 1 || d.V > (1 << 20)) return bad("vocab must be in [1, 2^20]");
   if (d.m < 1 || d.m > 16) return bad("max_symbols must be in [1, 16]");
@@ -316,9 +395,9 @@ size_t dec_params(const DecDims& d) {
 }
 
 struct DecLayout {
-  size_t embed, lstm_w, lstm_b, proj_w, proj_b, out_w, out_b, weights_end;
+  size_t embed, lstm_w, lstm_b, proj_w, proj_b, out_w, out_b, weights_end, table, ccount;
   size_t h, c, p, pend;
-  size_t ids, slot_t, slot_sym, slot_tok, slot_ntok, need, plist, pcnt, alist, acnt, hn, part;
+  size_t ids, slot_t, slot_sym, slot_tok, slot_ntok, need, plist, pcnt, alist, acnt, hn, part, zbuf, tokbuf, frmbuf;
   size_t total;
 };
 
@@ -335,6 +414,8 @@ DecLayout dec_layout(const DecDims& d) {
   t.out_w = take(P * d.Cpad * 4);
   t.out_b = take((size_t)d.Cpad * 4);
   t.weights_end = take(0);
+  t.table = take((size_t)d.C * 4 * H * 4);
+  t.ccount = take(4);
   t.h = take(S * d.L * H * 4);
   t.c = take(S * d.L * H * 4);
   t.p = take(S * P * 4);
@@ -346,6 +427,9 @@ DecLayout dec_layout(const DecDims& d) {
   t.alist = take(R * n * 4); t.acnt = take(R * 4);
   t.hn = take((size_t)d.L * n * H * 4);
   t.part = take(n * d.nfmax * (size_t)(d.Cpad / 64) * 8);
+  t.zbuf = take(n * d.nfmax * P * 4);
+  t.tokbuf = take(n * d.nfmax * d.m * 4);
+  t.frmbuf = take(n * d.nfmax * d.m * 4);
   t.total = take(0);
   return t;
 }
@@ -363,6 +447,25 @@ struct cac_dec {
   std::vector<int32_t> stamp;
   int32_t stamp_gen = 0;
   std::string err;
+  bool profiling = false;
+  Profiler prof;
+  std::vector<int32_t> dev_ids;  // contents last uploaded to the ids region
+  // recorded decode graphs, one per call shape (streams, frames, token frames wanted)
+  struct Graph {
+    hipGraph_t g = nullptr;
+    hipGraphExec_t exec = nullptr;
+    std::vector<NodeRec> nodes;
+    std::vector<std::vector<std::pair<size_t, int>>> offs;  // per node: (offset, caller pointer index)
+    const void* ptr[4] = {nullptr, nullptr, nullptr, nullptr};
+  };
+  bool use_graph = true;
+  std::map<uint64_t, Graph> graphs;
+  ~cac_dec() {
+    for (auto& kv : graphs) {
+      if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
+      if (kv.second.g) (void)hipGraphDestroy(kv.second.g);
+    }
+  }
   template <class T> T* P(size_t off) const { return (T*)(ws + off); }
   int fail(int code, const std::string& m) { err = m; return code; }
 };
@@ -387,6 +490,158 @@ void dec_reset_launch(cac_dec* c, Launcher& L, int n) {
                  c->P<int32_t>(c->lay.pend), n, c->d.L, c->d.H, c->d.P, c->d.V};
   L.tag("dec_reset", 0.0, 0.0);
   L.launch((const void*)&dec_reset_kernel, dim3(n), dim3(256), 0, &r);
+}
+
+// Every kernel of one decode call (see the file comment), in launch order: begin; per round the
+// LSTM layers, the projection, the joint and the decision; end.
+void dec_enqueue(cac_dec* c, Launcher& L, int n, int nf, const float* d_z, int32_t* d_tokens, int32_t* d_token_frames,
+                 int32_t* d_counts) {
+  const DecDims& d = c->d;
+  const DecLayout& y = c->lay;
+  const int rounds = 1 + nf * d.m, ntiles = d.Cpad / 64;
+  DecRoundArgs ra{};
+  ra.ids = c->P<int32_t>(y.ids);
+  ra.slot_t = c->P<int32_t>(y.slot_t); ra.slot_sym = c->P<int32_t>(y.slot_sym); ra.slot_tok = c->P<int32_t>(y.slot_tok);
+  ra.slot_ntok = c->P<int32_t>(y.slot_ntok); ra.need = c->P<int32_t>(y.need);
+  ra.plist = c->P<int32_t>(y.plist); ra.pcnt = c->P<int32_t>(y.pcnt);
+  ra.alist = c->P<int32_t>(y.alist); ra.acnt = c->P<int32_t>(y.acnt);
+  ra.part = c->P<float2>(y.part); ra.tokbuf = c->P<int32_t>(y.tokbuf); ra.frmbuf = c->P<int32_t>(y.frmbuf);
+  ra.pend = c->P<int32_t>(y.pend);
+  ra.n = n; ra.nf = nf; ra.m = d.m; ra.ntiles = ntiles; ra.blank = d.V; ra.rounds = rounds;
+  L.tag("dec_begin", 0.0, 0.0);
+  L.launch((const void*)&dec_begin_kernel, dim3(1), dim3(256), 0, &ra);
+  DecStageArgs sa{(const f32x4_d*)d_z, c->P<f32x4_d>(y.zbuf), (long)n * nf * d.P / 4};
+  L.tag("dec_stage", 0.0, 0.0);
+  L.launch((const void*)&dec_stage_kernel, dim3((unsigned)std::min<long>((sa.n4 + 255) / 256, 2048)), dim3(256), 0, &sa);
+  DecTileArgs ta{};
+  ta.ids = ra.ids; ta.slot_tok = ra.slot_tok; ta.embed = c->P<float>(y.embed);
+  ta.h = c->P<float>(y.h); ta.c = c->P<float>(y.c); ta.hn = c->P<float>(y.hn); ta.p = c->P<float>(y.p);
+  ta.need = ra.need; ta.z = c->P<float>(y.zbuf); ta.part = c->P<float2>(y.part); ta.table = c->P<float>(y.table);
+  ta.L = d.L; ta.H = d.H; ta.P = d.P; ta.C = d.C; ta.nf = nf; ta.ntiles = ntiles; ta.n = n;
+  const dim3 blk(256);
+  const unsigned prow = (unsigned)((n + 63) / 64), jrow = (unsigned)((n * nf + 63) / 64);
+  for (int j = 0; j < rounds && L.err == hipSuccess; ++j) {
+    // predictor step of the slots on P_j
+    DecTileArgs t = ta;
+    t.list = ra.plist + (size_t)j * n;
+    t.count = ra.pcnt + j;
+    for (int l = 0; l < d.L; ++l) {
+      t.layer = l; t.K = l == 0 ? d.H : 2 * d.H; t.N = 4 * d.H;
+      // layer 0 contracts h with the W_hh rows only (its input half is the token table)
+      t.W = c->P<float>(y.lstm_w) + (size_t)l * 2 * d.H * 4 * d.H + (l == 0 ? (size_t)d.H * 4 * d.H : 0);
+      t.bias = c->P<float>(y.lstm_b) + (size_t)l * 4 * d.H;
+      L.tag("dec_lstm", 0.0, 0.0);
+      L.launch(l == 0 ? (const void*)&dec_tile_kernel<DM_LSTM0> : (const void*)&dec_tile_kernel<DM_LSTM>,
+               dim3(4 * d.H / 64, prow), blk, DEC_LDS, &t);
+    }
+    t.K = d.H; t.N = d.P; t.W = c->P<float>(y.proj_w); t.bias = c->P<float>(y.proj_b);
+    L.tag("dec_proj", 0.0, 0.0);
+    L.launch((const void*)&dec_tile_kernel<DM_PROJ>, dim3(d.P / 64, prow), blk, DEC_LDS, &t);
+    // joint of the slots on A_j, all frames
+    DecTileArgs jt = ta;
+    jt.list = ra.alist + (size_t)j * n;
+    jt.count = ra.acnt + j;
+    jt.K = d.P; jt.N = d.Cpad; jt.W = c->P<float>(y.out_w); jt.bias = c->P<float>(y.out_b);
+    L.tag("dec_joint", 0.0, 0.0);
+    L.launch((const void*)&dec_tile_kernel<DM_JOINT>, dim3(ntiles, jrow), blk, DEC_LDS, &jt);
+    DecRoundArgs r = ra;
+    r.round = j;
+    L.tag("dec_decide", 0.0, 0.0);
+    L.launch((const void*)&dec_decide_kernel, dim3((n + 255) / 256), blk, 0, &r);
+  }
+  DecRoundArgs ea = ra;
+  ea.tokens = d_tokens; ea.tframes = d_token_frames; ea.counts = d_counts;
+  L.tag("dec_end", 0.0, 0.0);
+  L.launch((const void*)&dec_end_kernel, dim3((n + 255) / 256), blk, 0, &ea);
+}
+
+// Profiled call: once it has run, read back its round counts and give every recorded launch its
+// algorithmic flops and weight bytes; launches whose list was empty are named "<kernel>/idle".
+hipError_t dec_profile_fix(cac_dec* c, size_t first, int n, int nf) {
+  const DecDims& d = c->d;
+  const int rounds = 1 + nf * d.m;
+  std::vector<int32_t> pc(rounds + 1), ac(rounds + 1);
+  hipError_t e = hipMemcpyAsync(pc.data(), c->ws + c->lay.pcnt, pc.size() * 4, hipMemcpyDeviceToHost, c->stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(ac.data(), c->ws + c->lay.acnt, ac.size() * 4, hipMemcpyDeviceToHost, c->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+  if (e != hipSuccess) return e;
+  std::vector<Profiler::Rec>& rec = c->prof.pending;
+  if (rec.size() != first + 3 + (size_t)rounds * (d.L + 3)) return hipSuccess;  // events not taken: nothing to name
+  const double H = d.H, P = d.P, C = d.C;
+  size_t i = first + 2;  // past begin and stage
+  auto set = [&](const char* name, double rows, double flops_per_row, double wbytes) {
+    Profiler::Rec& r = rec[i++];
+    const std::string nm = std::string(name) + (rows > 0 ? "" : "/idle");
+    r.name = c->prof.name_id(nm.c_str());
+    r.flops = rows * flops_per_row;
+    r.bytes = rows > 0 ? wbytes : 0.0;
+  };
+  for (int j = 0; j < rounds; ++j) {
+    for (int l = 0; l < d.L; ++l) set("dec_lstm", pc[j], 2.0 * (l ? 2 : 1) * H * 4 * H, (l ? 2 : 1) * H * 4 * H * 4);
+    set("dec_proj", pc[j], 2.0 * H * P, H * P * 4);
+    set("dec_joint", (double)ac[j] * nf, 2.0 * P * C, P * d.Cpad * 4);
+    set("dec_decide", ac[j], 0.0, 0.0);
+  }
+  (void)n;
+  return hipSuccess;
+}
+
+// Offsets of 8-byte fields of a recorded argument block that hold exactly p.
+std::vector<size_t> dec_find_ptr(const std::vector<char>& args, const void* p) {
+  std::vector<size_t> offs;
+  if (!p) return offs;
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  for (size_t o = 0; o + 8 <= args.size(); o += 8) {
+    uint64_t w;
+    memcpy(&w, args.data() + o, 8);
+    if (w == v) offs.push_back(o);
+  }
+  return offs;
+}
+
+// Replay the recorded graph of this call shape (recording it on first use), re-pointing the
+// nodes that hold the caller's pointers (z, tokens, token frames, counts).
+hipError_t dec_graph(cac_dec* c, int n, int nf, const void* const ptrs[4]) {
+  const uint64_t key = ((uint64_t)n << 8) | ((uint64_t)nf << 1) | (ptrs[2] ? 1u : 0u);
+  auto it = c->graphs.find(key);
+  if (it == c->graphs.end()) {
+    cac_dec::Graph gr;
+    hipError_t e = hipGraphCreate(&gr.g, 0);
+    if (e != hipSuccess) return e;
+    Launcher L;
+    L.stream = c->stream;
+    L.graph = gr.g;
+    L.rec = &gr.nodes;
+    dec_enqueue(c, L, n, nf, (const float*)ptrs[0], (int32_t*)ptrs[1], (int32_t*)ptrs[2], (int32_t*)ptrs[3]);
+    if (L.err != hipSuccess) { (void)hipGraphDestroy(gr.g); return L.err; }
+    e = hipGraphInstantiate(&gr.exec, gr.g, nullptr, nullptr, 0);
+    if (e != hipSuccess) { (void)hipGraphDestroy(gr.g); return e; }
+    for (const NodeRec& r : gr.nodes) {
+      std::vector<std::pair<size_t, int>> o;
+      for (int q = 0; q < 4; ++q)
+        for (size_t off : dec_find_ptr(r.args, ptrs[q])) o.push_back({off, q});
+      gr.offs.push_back(o);
+    }
+    for (int q = 0; q < 4; ++q) gr.ptr[q] = ptrs[q];
+    it = c->graphs.emplace(key, std::move(gr)).first;
+  }
+  cac_dec::Graph& gr = it->second;
+  bool same = true;
+  for (int q = 0; q < 4; ++q) same = same && gr.ptr[q] == ptrs[q];
+  if (!same) {
+    for (size_t i = 0; i < gr.nodes.size(); ++i) {
+      if (gr.offs[i].empty()) continue;
+      NodeRec& r = gr.nodes[i];
+      for (const auto& oq : gr.offs[i]) memcpy(r.args.data() + oq.first, &ptrs[oq.second], 8);
+      hipKernelNodeParams p = r.p;
+      void* kp[1] = {r.args.data()};
+      p.kernelParams = kp;
+      hipError_t e = hipGraphExecKernelNodeSetParams(gr.exec, r.node, &p);
+      if (e != hipSuccess) return e;
+    }
+    for (int q = 0; q < 4; ++q) gr.ptr[q] = ptrs[q];
+  }
+  return hipGraphLaunch(gr.exec, c->stream);
 }
 
 }  // namespace
@@ -431,6 +686,10 @@ int32_t cac_dec_create(const cac_dec_config* cfg, const float* h_params, size_t 
   c->stamp.assign(d.S, 0);
   if (dry) { *out = c; return CAC_OK; }
   kernels_init();
+  for (const void* f : {(const void*)&dec_tile_kernel<DM_LSTM0>, (const void*)&dec_tile_kernel<DM_LSTM>,
+                        (const void*)&dec_tile_kernel<DM_PROJ>, (const void*)&dec_tile_kernel<DM_JOINT>,
+                        (const void*)&dec_tile_kernel<DM_TABLE>})
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS);
   // repack: LSTM gate columns per unit (unit u's i, f, g, o at 4u .. 4u+3), w_ih rows then w_hh
   // rows as one [2H][4H] matrix, the two biases summed; joint columns padded to 64
   const size_t H = d.H, P = d.P, C = d.C;
@@ -467,9 +726,19 @@ int32_t cac_dec_create(const cac_dec_config* cfg, const float* h_params, size_t 
   std::vector<int32_t> all(d.S);
   for (int i = 0; i < d.S; ++i) all[i] = i;
   if (e == hipSuccess) e = hipMemcpyAsync(c->ws + lay.ids, all.data(), (size_t)d.S * 4, hipMemcpyHostToDevice, c->stream);
+  c->dev_ids = all;
+  const int32_t cc = (int32_t)d.C;
+  if (e == hipSuccess) e = hipMemcpyAsync(c->ws + lay.ccount, &cc, 4, hipMemcpyHostToDevice, c->stream);
   if (e == hipSuccess) {
     Launcher L;
     L.stream = c->stream;
+    // first layer's input table: embed[token] W_ih + b_ih + b_hh for every class
+    DecTileArgs t{};
+    t.K = d.H; t.N = 4 * d.H; t.W = c->P<float>(lay.lstm_w); t.bias = c->P<float>(lay.lstm_b);
+    t.count = c->P<int32_t>(lay.ccount); t.embed = c->P<float>(lay.embed); t.table = c->P<float>(lay.table);
+    t.H = d.H; t.C = d.C;
+    L.tag("dec_table", 0.0, 0.0);
+    L.launch((const void*)&dec_tile_kernel<DM_TABLE>, dim3(4 * d.H / 64, (d.C + 63) / 64), dim3(256), DEC_LDS, &t);
     dec_reset_launch(c, L, d.S);
     e = L.err;
   }
@@ -495,61 +764,70 @@ int32_t cac_dec_greedy(cac_dec* c, int32_t n, const int32_t* ids, int32_t nf, co
   const hipError_t pe = hipStreamQuery(c->stream);
   if (pe != hipSuccess && pe != hipErrorNotReady)
     return c->fail(CAC_EHIP, std::string("asynchronous device error from earlier work: ") + hipGetErrorString(pe));
-  const DecLayout& y = c->lay;
+  hipError_t e = hipSuccess;
+  if ((int)c->dev_ids.size() != n || memcmp(c->dev_ids.data(), ids, (size_t)n * 4) != 0) {
+    c->dev_ids.assign(ids, ids + n);
+    e = hipMemcpyAsync(c->ws + c->lay.ids, c->dev_ids.data(), (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  }
+  if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("id upload failed: ") + hipGetErrorString(e));
+  const void* ptrs[4] = {d_z, d_tokens, d_token_frames, d_counts};
+  if (c->use_graph && !c->profiling) {
+    e = dec_graph(c, n, nf, ptrs);
+    if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("graph replay failed: ") + hipGetErrorString(e));
+    return CAC_OK;
+  }
   Launcher L;
   L.stream = c->stream;
-  L.err = hipMemcpyAsync(c->ws + y.ids, ids, (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
-  const int rounds = 1 + nf * d.m, ntiles = d.Cpad / 64;
-  DecRoundArgs ra{};
-  ra.ids = c->P<int32_t>(y.ids);
-  ra.slot_t = c->P<int32_t>(y.slot_t); ra.slot_sym = c->P<int32_t>(y.slot_sym); ra.slot_tok = c->P<int32_t>(y.slot_tok);
-  ra.slot_ntok = c->P<int32_t>(y.slot_ntok); ra.need = c->P<int32_t>(y.need);
-  ra.plist = c->P<int32_t>(y.plist); ra.pcnt = c->P<int32_t>(y.pcnt);
-  ra.alist = c->P<int32_t>(y.alist); ra.acnt = c->P<int32_t>(y.acnt);
-  ra.part = c->P<float2>(y.part); ra.tokens = d_tokens; ra.tframes = d_token_frames; ra.counts = d_counts;
-  ra.pend = c->P<int32_t>(y.pend);
-  ra.n = n; ra.nf = nf; ra.m = d.m; ra.ntiles = ntiles; ra.blank = d.V; ra.rounds = rounds;
-  L.tag("dec_begin", 0.0, 0.0);
-  L.launch((const void*)&dec_begin_kernel, dim3(1), dim3(256), 0, &ra);
-  DecTileArgs ta{};
-  ta.ids = ra.ids; ta.slot_tok = ra.slot_tok; ta.embed = c->P<float>(y.embed);
-  ta.h = c->P<float>(y.h); ta.c = c->P<float>(y.c); ta.hn = c->P<float>(y.hn); ta.p = c->P<float>(y.p);
-  ta.need = ra.need; ta.z = d_z; ta.part = c->P<float2>(y.part);
-  ta.L = d.L; ta.H = d.H; ta.P = d.P; ta.C = d.C; ta.nf = nf; ta.ntiles = ntiles; ta.n = n;
-  const dim3 blk(256);
-  const unsigned prow = (unsigned)((n + 63) / 64), jrow = (unsigned)((n * nf + 63) / 64);
-  for (int j = 0; j < rounds && L.err == hipSuccess; ++j) {
-    // predictor step of the slots on P_j
-    DecTileArgs t = ta;
-    t.list = ra.plist + (size_t)j * n;
-    t.count = ra.pcnt + j;
-    for (int l = 0; l < d.L; ++l) {
-      t.layer = l; t.K = 2 * d.H; t.N = 4 * d.H;
-      t.W = c->P<float>(y.lstm_w) + (size_t)l * 2 * d.H * 4 * d.H;
-      t.bias = c->P<float>(y.lstm_b) + (size_t)l * 4 * d.H;
-      L.tag("dec_lstm", 0.0, 0.0);
-      L.launch(l == 0 ? (const void*)&dec_tile_kernel<DM_LSTM0> : (const void*)&dec_tile_kernel<DM_LSTM>,
-               dim3(4 * d.H / 64, prow), blk, 0, &t);
-    }
-    t.K = d.H; t.N = d.P; t.W = c->P<float>(y.proj_w); t.bias = c->P<float>(y.proj_b);
-    L.tag("dec_proj", 0.0, 0.0);
-    L.launch((const void*)&dec_tile_kernel<DM_PROJ>, dim3(d.P / 64, prow), blk, 0, &t);
-    // joint of the slots on A_j, all frames
-    DecTileArgs jt = ta;
-    jt.list = ra.alist + (size_t)j * n;
-    jt.count = ra.acnt + j;
-    jt.K = d.P; jt.N = d.Cpad; jt.W = c->P<float>(y.out_w); jt.bias = c->P<float>(y.out_b);
-    L.tag("dec_joint", 0.0, 0.0);
-    L.launch((const void*)&dec_tile_kernel<DM_JOINT>, dim3(ntiles, jrow), blk, 0, &jt);
-    DecRoundArgs r = ra;
-    r.round = j;
-    L.tag("dec_decide", 0.0, 0.0);
-    L.launch((const void*)&dec_decide_kernel, dim3((n + 255) / 256), blk, 0, &r);
+  size_t first = 0;
+  if (c->profiling) {
+    c->prof.drain();
+    L.prof = &c->prof;
+    first = c->prof.pending.size();
   }
-  L.tag("dec_end", 0.0, 0.0);
-  L.launch((const void*)&dec_end_kernel, dim3((n + 255) / 256), blk, 0, &ra);
+  dec_enqueue(c, L, n, nf, d_z, d_tokens, d_token_frames, d_counts);
   if (L.err != hipSuccess) return c->fail(CAC_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(L.err));
+  if (c->profiling) {
+    e = dec_profile_fix(c, first, n, nf);
+    if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("profiling: ") + hipGetErrorString(e));
+  }
   return CAC_OK;
+}
+
+int32_t cac_dec_set_graph(cac_dec* c, int32_t enable) {
+  if (!c) return CAC_EINVAL;
+  c->use_graph = enable != 0;
+  return CAC_OK;
+}
+
+int32_t cac_dec_profile(cac_dec* c, int32_t enable) {
+  if (!c) return CAC_EINVAL;
+  if (enable) {
+    c->prof.clear();
+    c->profiling = true;
+  } else {
+    c->prof.drain();
+    c->profiling = false;
+  }
+  return c->prof.err == hipSuccess ? CAC_OK : c->fail(CAC_EHIP, std::string("profiling: ") + hipGetErrorString(c->prof.err));
+}
+
+int32_t cac_dec_profile_read(cac_dec* c, int32_t max_entries, char* names, int32_t name_len, int64_t* launches,
+                             double* total_ms, double* bytes, double* flops) {
+  if (!c || max_entries < 0 || name_len < 1) return CAC_EINVAL;
+  c->prof.drain();
+  if (c->prof.err != hipSuccess) return c->fail(CAC_EHIP, std::string("profiling: ") + hipGetErrorString(c->prof.err));
+  const int nn = (int)c->prof.names.size();
+  for (int i = 0; i < nn && i < max_entries; ++i) {
+    if (names) {
+      strncpy(names + (size_t)i * name_len, c->prof.names[i].c_str(), name_len - 1);
+      names[(size_t)i * name_len + name_len - 1] = 0;
+    }
+    if (launches) launches[i] = c->prof.launches[i];
+    if (total_ms) total_ms[i] = c->prof.ms[i];
+    if (bytes) bytes[i] = c->prof.bytes[i];
+    if (flops) flops[i] = c->prof.flops[i];
+  }
+  return nn;
 }
 
 int32_t cac_dec_reset(cac_dec* c, int32_t n, const int32_t* ids) {
@@ -559,7 +837,8 @@ int32_t cac_dec_reset(cac_dec* c, int32_t n, const int32_t* ids) {
   if (c->dry) return c->fail(CAC_ENODEV, "dry-run context: no device work");
   Launcher L;
   L.stream = c->stream;
-  L.err = hipMemcpyAsync(c->ws + c->lay.ids, ids, (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
+  c->dev_ids.assign(ids, ids + n);
+  L.err = hipMemcpyAsync(c->ws + c->lay.ids, c->dev_ids.data(), (size_t)n * 4, hipMemcpyHostToDevice, c->stream);
   dec_reset_launch(c, L, n);
   if (L.err != hipSuccess) return c->fail(CAC_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(L.err));
   return n;

@@ -37,7 +37,7 @@ typedef struct cac_dec cac_dec;
 typedef struct {
   int32_t joint_dim;    /* P (640): width of the projected encoder frames and predictor output;
                            a multiple of 64, <= 4096 */
-  int32_t pred_hidden;  /* H (640): embedding and LSTM width, a multiple of 16, <= 4096 */
+  int32_t pred_hidden;  /* H (640): embedding and LSTM width, a multiple of 64, <= 4096 */
   int32_t pred_layers;  /* LSTM layers (2), 1 .. 8 */
   int32_t vocab;        /* V (1024): classes are V + 2 (blank = V, EOU = V + 1) */
   int32_t max_symbols;  /* emissions per frame before moving on (4), 1 .. 16 */
@@ -78,6 +78,24 @@ int32_t cac_dec_create(const cac_dec_config* cfg, const float* h_params, size_t 
  * is synchronised. Returns 0. */
 int32_t cac_dec_greedy(cac_dec* ctx, int32_t n_streams, const int32_t* h_stream_ids, int32_t n_frames,
                        const float* d_z, int32_t* d_tokens, int32_t* d_token_frames, int32_t* d_counts);
+
+/* Decode calls are recorded once per call shape (streams, frames, whether token frames are
+ * wanted) into a HIP graph of kernel nodes and replayed, the nodes holding the caller's
+ * pointers re-pointed between replays; enable = 0 launches every kernel directly (as
+ * profiling always does). Default on. */
+int32_t cac_dec_set_graph(cac_dec* ctx, int32_t enable);
+
+/* Per-kernel timing of later decode calls (measurement aid), as cac_profile in cac.h: each
+ * kernel launched with start and stop HIP events bound to its dispatch. After each profiled
+ * call the library reads back how many streams each round's lists held (a synchronisation)
+ * and gives every launch its algorithmic flops (2 x rows x K x N of its tile product) and
+ * weight bytes; launches whose list was empty are recorded as "<kernel>/idle".
+ * cac_dec_profile(ctx, 1) clears and starts, 0 stops; cac_dec_profile_read synchronises and
+ * fills, per kernel name (up to max_entries; names is max_entries * name_len chars): launches,
+ * total milliseconds, bytes and flops. Returns the number of kernel names. */
+int32_t cac_dec_profile(cac_dec* ctx, int32_t enable);
+int32_t cac_dec_profile_read(cac_dec* ctx, int32_t max_entries, char* names, int32_t name_len, int64_t* launches,
+                             double* total_ms, double* bytes, double* flops);
 
 /* Return streams to the fresh state (zero LSTM state, next prediction from blank). Returns n. */
 int32_t cac_dec_reset(cac_dec* ctx, int32_t n, const int32_t* h_stream_ids);

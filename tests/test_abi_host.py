@@ -245,7 +245,7 @@ def test_decoder_param_layout_and_validation():
     assert n == sum(int(np.prod(s)) for _, s in cac.binding.dec_param_order(D1))
     assert [nm for nm, _ in cac.binding.dec_param_order(D1)] == [nm for nm, *_ in dec_weight_names(D1)]
     assert lib.cac_dec_workspace_bytes(C.byref(c)) > 0
-    for field, value in [("joint_dim", 100), ("pred_hidden", 20), ("pred_layers", 0), ("vocab", 0),
+    for field, value in [("joint_dim", 100), ("pred_hidden", 96), ("pred_layers", 0), ("vocab", 0),
                          ("max_symbols", 0), ("max_streams", 0), ("max_frames", 17)]:
         bad = cac.binding.make_dec_config(D1, max_streams=4)
         setattr(bad, field, value)

@@ -75,7 +75,7 @@ def test_d2_1024_streams_4_calls():
 
 @pytest.mark.parametrize("cfg", [D1.replace(name="D_m1", max_symbols=1, streams=6),
                                  D1.replace(name="D_f5", frames=5, streams=5, max_symbols=3),
-                                 D1.replace(name="D_small", joint_dim=128, pred_hidden=96, pred_layers=3, vocab=70,
+                                 D1.replace(name="D_small", joint_dim=128, pred_hidden=64, pred_layers=3, vocab=70,
                                             streams=70, blank_bias=1.0)],
                          ids=["max-symbols-1", "5-frames", "small-3-layers"])
 def test_decoder_shapes(cfg):
@@ -128,3 +128,34 @@ def test_encoder_then_decoder_tokens_match_the_oracle_pipeline():
         assert got == ref, (c, got, ref)
         emitted += len(ref)
     log(f"encoder + decoder, {chunks} chunks: {emitted} classes, identical")
+
+
+def test_decoder_graph_replay_and_profiling_match_direct_launches():
+    """Graph replays (re-pointed to other buffers every call, with eager work and host syncs in
+    between) and profiled direct launches give the classes of direct launches; the profile
+    times every kernel and gives the joint its flops."""
+    cfg = D1.replace(streams=40)
+    ids = list(range(40))
+    xs = np.stack([make_dec_inputs(cfg, s, 8) for s in ids])
+    z = torch.from_numpy(np.ascontiguousarray(xs.swapaxes(0, 1))).to("cuda:0")
+    g, d, p = _dec(cfg, max_streams=40), _dec(cfg, max_streams=40), _dec(cfg, max_streams=40)
+    d.set_graph(False)
+    p.profile(True)
+    bufs = [[torch.empty((40, cfg.frames * cfg.max_symbols), dtype=torch.int32, device="cuda:0") for _ in range(2)]
+            + [torch.empty(40, dtype=torch.int32, device="cuda:0")] for _ in range(3)]
+    scratch = torch.randn(1 << 16, device="cuda:0")
+    for c in range(8):
+        zc = z[c].clone()
+        tg, fg, cg = g.decode(ids, zc, *bufs[c % 3])
+        scratch.mul_(1.0001).add_(0.5)
+        td, fd, cd = d.decode(ids, zc)
+        tp, fp, cp = p.decode(ids, zc)
+        torch.cuda.synchronize()
+        for a, b in ((tg, td), (fg, fd), (cg, cd), (tp, td), (fp, fd), (cp, cd)):
+            assert torch.equal(a, b), c
+    prof = p.profile_read()
+    p.profile(False)
+    rounds = 1 + cfg.frames * cfg.max_symbols
+    launches = sum(v[0] for v in prof.values())
+    assert launches == 8 * (3 + rounds * (cfg.pred_layers + 3)), prof.keys()
+    assert prof["dec_joint"][3] > 0 and prof["dec_lstm"][3] > 0
