@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 100 for C4/C3/C5, 1000 for C2)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C4")
-    ap.add_argument("--secondary", default="C2", help="second workload reported in the same line, or 'none'")
+    ap.add_argument("--secondary", default="C2,C2Q",
+                    help="comma-separated workloads reported in the same line, or 'none'")
     ap.add_argument("--decode", default="D2", help="greedy-decoding workload reported in the same line, or 'none'")
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time per CPU-baseline mode")
@@ -221,7 +222,7 @@ def run_workload(key: str, steps, warmup: int, profile_steps: int, want_cpu: boo
     step_flops = sum(v[3] for v in prof.values()) / profile_steps
     res = {
         "value": value, "ms_per_step": ms_step, "steps": steps, "warmup": warmup,
-        "dtype": "f32" if cfg.dtype == "f32" else "bf16",
+        "dtype": {"f32": "f32", "bf16": "bf16", "i8w": "f32 (int8 weights)"}[cfg.dtype],
         "config": {"workload": cfg.name, "layers": cfg.n_layers, "d_model": cfg.d_model, "heads": cfg.n_heads,
                    "d_ff": cfg.d_ff, "att_left": cfg.att_left, "streams": S, "frames_per_chunk": cfg.n_emit,
                    "frames_computed_per_chunk": cfg.n_compute, "joint_dim": cfg.joint_dim,
@@ -344,12 +345,13 @@ def main():
     for key in ("rooflines_other", "cpu_baseline", "step"):
         if key in head:
             res[key] = head[key]
-    if args.secondary and args.secondary.lower() != "none" and args.secondary != args.workload:
-        sec = run_workload(args.secondary, args.steps, args.warmup, args.profile_steps, False, 0.0)
-        res["secondary"] = {sec["config"]["workload"]: {k: sec[k] for k in
-                                                         ("value", "ms_per_step", "steps", "dtype", "config",
-                                                          "roofline", "step")}}
-        res["secondary"][sec["config"]["workload"]]["unit"] = "frames/s"
+    for key in (args.secondary or "none").split(","):
+        if key.lower() == "none" or key == args.workload:
+            continue
+        sec = run_workload(key, args.steps, args.warmup, args.profile_steps, False, 0.0)
+        rec = {k: sec[k] for k in ("value", "ms_per_step", "steps", "dtype", "config", "roofline", "step")}
+        rec["unit"] = "frames/s"
+        res.setdefault("secondary", {})[sec["config"]["workload"]] = rec
     if args.decode and args.decode.lower() != "none":
         dres = run_decode(args.decode, args.steps, args.warmup, args.profile_steps)
         res.setdefault("secondary", {})[dres["config"]["workload"]] = dres

@@ -15,7 +15,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcac.so")
 
 CAC_OK, CAC_EINVAL, CAC_ESTATE, CAC_ENOMEM, CAC_EHIP, CAC_ENODEV = 0, -1, -2, -3, -4, -5
-CAC_F32, CAC_BF16 = 0, 1
+CAC_F32, CAC_BF16, CAC_F32_I8 = 0, 1, 2
 CAC_FLAG_DRY_RUN, CAC_FLAG_POISON = 1, 2
 ERROR_NAMES = {CAC_EINVAL: "CAC_EINVAL", CAC_ESTATE: "CAC_ESTATE", CAC_ENOMEM: "CAC_ENOMEM",
                CAC_EHIP: "CAC_EHIP", CAC_ENODEV: "CAC_ENODEV"}
@@ -137,7 +137,8 @@ def make_config(cfg, max_streams=None, max_push_frames=8, flags=0) -> cac_config
                  "att_right", "n_emit", "n_lookahead", "joint_dim", "mel_bins", "mel_per_chunk", "mel_tail"):
         setattr(c, name, int(getattr(cfg, name)))
     c.frontend = int(bool(cfg.frontend))
-    c.dtype = CAC_BF16 if str(cfg.dtype) in ("bf16", "bfloat16", str(CAC_BF16)) else CAC_F32
+    dt = str(cfg.dtype)
+    c.dtype = CAC_BF16 if dt in ("bf16", "bfloat16", str(CAC_BF16)) else CAC_F32_I8 if dt in ("i8w", str(CAC_F32_I8)) else CAC_F32
     c.max_streams = int(max_streams if max_streams is not None else cfg.streams)
     c.max_push_frames = int(max_push_frames)
     c.flags = int(flags)

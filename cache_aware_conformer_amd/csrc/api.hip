@@ -57,6 +57,11 @@ struct Dims {
   int R, Rc, Rx;      // ring depths: K/V, depthwise input, pending inputs
   int rel_lo, nrel;   // relative offsets covered by the position table
   size_t esz;         // bytes per compute-dtype element
+  int wq;             // dense weights are int8 codes + float32 row scales (CAC_F32_I8)
+  int dtype_cfg;      // the config's dtype field (dt is the activation/cache dtype)
+  size_t wsz(size_t rows, size_t cols) const {  // bytes of one dense matrix [rows][cols]
+    return wq ? rows * cols + rows * 4 : rows * cols * esz;
+  }
 };
 
 bool make_dims(const cac_config* c, Dims& d, std::string& why) {
@@ -84,7 +89,14 @@ bool make_dims(const cac_config* c, Dims& d, std::string& why) {
   d.nc = d.ne + d.nla;
   if (d.nc > 16) return bad("n_emit + n_lookahead must be <= 16");
   if (d.P < 0 || d.P > 8192) return bad("joint_dim must be in [0, 8192]");
-  if (d.dt != CAC_F32 && d.dt != CAC_BF16) return bad("dtype must be CAC_F32 or CAC_BF16");
+  if (d.dt != CAC_F32 && d.dt != CAC_BF16 && d.dt != CAC_F32_I8) return bad("dtype must be CAC_F32, CAC_BF16 or CAC_F32_I8");
+  d.dtype_cfg = d.dt;
+  d.wq = d.dt == CAC_F32_I8;
+  if (d.wq) {
+    d.dt = CAC_F32;  // activations and caches
+    if (c->frontend || c->n_lookahead > 0) return bad("CAC_F32_I8 is the one-stream path: no front end, no lookahead");
+    if (c->d_model % 256 || c->d_ff % 256) return bad("CAC_F32_I8 needs d_model and d_ff multiples of 256");
+  }
   if (d.S < 1 || d.S > (1 << 20)) return bad("max_streams must be in [1, 2^20]");
   if (d.fe) {
     if (d.lookahead) return bad("the front end is supported with the exact variant only");
@@ -144,14 +156,15 @@ Layout make_layout(const Dims& d) {
   lo.b_pw2 = b.take(D * f4); lo.b_ff2_1 = b.take(F * f4); lo.b_ff2_2 = b.take(D * f4);
   lo.pos_u = b.take(D * f4); lo.pos_v = b.take(D * f4); lo.dw_w = b.take((size_t)d.K * D * f4);
   lo.wpos = b.take(D * D * f4);
-  lo.w_ff1_1 = b.take(F * D * e); lo.w_ff1_2 = b.take(D * F * e); lo.w_qkv = b.take(3 * D * D * e);
-  lo.w_o = b.take(D * D * e); lo.w_pw1 = b.take(2 * D * D * e); lo.w_pw2 = b.take(D * D * e);
-  lo.w_ff2_1 = b.take(F * D * e); lo.w_ff2_2 = b.take(D * F * e);
+  // dense matrices [N][K] (int8 weights: the codes, then the N row scales)
+  lo.w_ff1_1 = b.take(d.wsz(F, D)); lo.w_ff1_2 = b.take(d.wsz(D, F)); lo.w_qkv = b.take(d.wsz(3 * D, D));
+  lo.w_o = b.take(d.wsz(D, D)); lo.w_pw1 = b.take(d.wsz(2 * D, D)); lo.w_pw2 = b.take(d.wsz(D, D));
+  lo.w_ff2_1 = b.take(d.wsz(F, D)); lo.w_ff2_2 = b.take(d.wsz(D, F));
   lo.size = (b.take(0) + 255) & ~(size_t)255;
 
   Bump w;
   t.layers = w.take(lo.size * d.L);
-  if (d.P) { t.wj = w.take((size_t)d.P * D * e); t.bj = w.take((size_t)d.P * f4); }
+  if (d.P) { t.wj = w.take(d.wsz(d.P, D)); t.bj = w.take((size_t)d.P * f4); }
   if (d.fe) {
     const size_t kin[3] = {(size_t)3 * d.bins, 3 * D, 3 * D};
     for (int i = 0; i < 3; ++i) { t.fe_w[i] = w.take(D * kin[i] * e); t.fe_b[i] = w.take(D * f4); }
@@ -206,7 +219,7 @@ size_t state_floats(const Dims& d) {
 // config field that defines the model and the state's meaning (all but max_streams,
 // max_push_frames and flags), taken after make_dims' normalisation.
 void state_header(const Dims& d, uint32_t out[STATE_HDR]) {
-  const int32_t f[] = {d.L, d.D, d.H, d.F, d.K, d.Lc, d.c, d.right, d.ne, d.nla, d.P, d.fe, d.bins, d.mpc, d.tail, d.dt};
+  const int32_t f[] = {d.L, d.D, d.H, d.F, d.K, d.Lc, d.c, d.right, d.ne, d.nla, d.P, d.fe, d.bins, d.mpc, d.tail, d.dtype_cfg};
   uint64_t h = 1469598103934665603ull;
   for (int32_t v : f)
     for (int b = 0; b < 4; ++b) {
@@ -231,15 +244,35 @@ uint16_t to_bf16(float f) {
 struct Packer {
   std::vector<uint8_t>& buf;
   int dt;
+  int wq = 0;          // dense matrices as int8 codes + row scales
+  size_t rows = 0;     // rows of the dense matrix being packed (its scales follow the codes)
   void f32(size_t off, const float* src, size_t n) { memcpy(buf.data() + off, src, n * 4); }
   void op(size_t off, size_t idx, float v) {
     if (dt == CAC_BF16) ((uint16_t*)(buf.data() + off))[idx] = to_bf16(v);
     else ((float*)(buf.data() + off))[idx] = v;
   }
-  // in [K][N] row-major -> out [N][K]
+  // column n of in [K][N] as row `row` of a dense matrix [rows][K] at off. int8: the column's
+  // scale s = max |w| / 127 and codes rint(w / s) clamped to [-127, 127] (0 for a zero
+  // column), in float32 arithmetic, round half to even
+  void column(size_t off, const float* in, size_t K, size_t N, size_t n, size_t row) {
+    if (!wq) {
+      for (size_t k = 0; k < K; ++k) op(off, row * K + k, in[k * N + n]);
+      return;
+    }
+    float m = 0.0f;
+    for (size_t k = 0; k < K; ++k) m = std::max(m, std::fabs(in[k * N + n]));
+    const float sc = m / 127.0f;
+    int8_t* q = (int8_t*)(buf.data() + off) + row * K;
+    for (size_t k = 0; k < K; ++k) {
+      float v = sc > 0.0f ? std::nearbyint(in[k * N + n] / sc) : 0.0f;
+      v = std::min(127.0f, std::max(-127.0f, v));
+      q[k] = (int8_t)v;
+    }
+    ((float*)(buf.data() + off + rows * K))[row] = sc;
+  }
+  // in [K][N] row-major -> rows row0 .. row0+N-1 of the [rows][K] matrix at off
   void transpose(size_t off, const float* in, size_t K, size_t N, size_t row0 = 0) {
-    for (size_t k = 0; k < K; ++k)
-      for (size_t n = 0; n < N; ++n) op(off, (row0 + n) * K + k, in[k * N + n]);
+    for (size_t n = 0; n < N; ++n) column(off, in, K, N, n, row0 + n);
   }
 };
 
@@ -322,11 +355,13 @@ struct Pass {
     e.D = c->d.D; e.H = c->d.H; e.hd = c->d.hd; e.R = c->d.R; e.Rc = c->d.Rc;
     return e;
   }
+  // weight dtype of the dense products (int8 codes + row scales, or the compute dtype)
+  int wdt() const { return c->d.wq ? DT_I8W : c->d.dt; }
   void gemm_plain(const void* A, int lda, const void* W, int N, int K, const EpiArgs& e) {
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K; g.A = A; g.W = W; g.epi = e;
     g.amap = RowMap{INT_MAX, 0, lda};
-    launch_gemm(L, g, c->d.dt, 0);
+    launch_gemm(L, g, wdt(), 0);
   }
 
   // few rows (float32 workloads, or <= 8 rows): every dense product runs in the small-M kernel
@@ -417,7 +452,7 @@ struct Pass {
         g.A = cur; g.amap = RowMap{INT_MAX, 0, d.D};
         g.a_f32 = 1; g.ln_g = lng; g.ln_b = lnb; g.a_scratch = c->P<void>(c->lay.y);
         if (with_pre) { g.pre_g = pre_g; g.pre_b = pre_b; }
-        launch_gemm(L, g, d.dt, 0);
+        launch_gemm(L, g, wdt(), 0);
       };
       auto resid = [&](float alpha, const float* bias) {
         EpiArgs e = epi0();
@@ -440,7 +475,7 @@ struct Pass {
         }
         g.epi = dn;
         L.role = "ff1_down";
-        launch_gemm(L, g, d.dt, 0);
+        launch_gemm(L, g, wdt(), 0);
         if (fz) std::swap(cur, other);
       }
       // ---- MHSA: q to a buffer, k and v straight into the ring slots of their positions
@@ -465,8 +500,8 @@ struct Pass {
       pw1.epi.kind = EPI_GLU_DW; pw1.epi.out = c->P<void>(c->lay.e); pw1.epi.ldo = d.D;
       pw1.dw_w = F32(lo.dw_w); pw1.dw_b = F32(lo.b_dw); pw1.dw_taps = d.K; pw1.dw_Rc = d.Rc;
       L.role = "pw1";
-      if (fz && rowdot_supported(pw1, d.dt)) {
-        launch_gemm(L, pw1, d.dt, 0);
+      if (fz && rowdot_supported(pw1, wdt())) {
+        launch_gemm(L, pw1, wdt(), 0);
         L.role = "pw2";
         gemm_plain(c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, d.D, resid(1.0f, F32(lo.b_pw2)));
       } else if (fz) {
@@ -476,7 +511,7 @@ struct Pass {
         g.a_dw = 1; g.dw_ring = cr; g.dw_w = F32(lo.dw_w); g.dw_b = F32(lo.b_dw); g.dw_taps = d.K; g.dw_Rc = d.Rc;
         g.amap = RowMap{INT_MAX, 0, d.D};
         L.role = "pw2";
-        launch_gemm(L, g, d.dt, 0);
+        launch_gemm(L, g, wdt(), 0);
       } else {
         gemm_x(F32(lo.ln[4]), F32(lo.ln[5]), lb + lo.w_pw1, 2 * d.D, glu, false);
         DwArgs dw{cv, cr, F32(lo.dw_w), F32(lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
@@ -602,7 +637,7 @@ struct Pass {
       g.a_scratch = nullptr;
     }
     L.role = "joint";
-    launch_gemm(L, g, d.dt, 0);
+    launch_gemm(L, g, wdt(), 0);
   }
 };
 
@@ -702,7 +737,7 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
   kernels_init();
   // repack the parameters on the host, then one copy into the workspace
   std::vector<uint8_t> wbuf(lay.weights_end, 0);
-  Packer pk{wbuf, d.dt};
+  Packer pk{wbuf, d.dt, d.wq};
   const float* p = h_params;
   const size_t D = d.D, F = d.F;
   auto take = [&](size_t n) { const float* r = p; p += n; return r; };
@@ -711,27 +746,27 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
     const LayerOff& lo = lay.lo;
     auto ffp = [&](int lnidx, size_t b1, size_t b2, size_t w1, size_t w2) {
       pk.f32(base + lo.ln[lnidx], take(D), D); pk.f32(base + lo.ln[lnidx + 1], take(D), D);
-      pk.transpose(base + w1, take(D * F), D, F); pk.f32(base + b1, take(F), F);
-      pk.transpose(base + w2, take(F * D), F, D); pk.f32(base + b2, take(D), D);
+      pk.rows = F; pk.transpose(base + w1, take(D * F), D, F); pk.f32(base + b1, take(F), F);
+      pk.rows = D; pk.transpose(base + w2, take(F * D), F, D); pk.f32(base + b2, take(D), D);
     };
     ffp(0, lo.b_ff1_1, lo.b_ff1_2, lo.w_ff1_1, lo.w_ff1_2);
     pk.f32(base + lo.ln[2], take(D), D); pk.f32(base + lo.ln[3], take(D), D);
+    pk.rows = 3 * D;
     for (int m = 0; m < 3; ++m) {  // wq, wk, wv stacked as rows of [3D][D]
       pk.transpose(base + lo.w_qkv, take(D * D), D, D, (size_t)m * D);
       pk.f32(base + lo.b_qkv + (size_t)m * D * 4, take(D), D);
     }
-    pk.transpose(base + lo.w_o, take(D * D), D, D); pk.f32(base + lo.b_o, take(D), D);
+    pk.rows = D; pk.transpose(base + lo.w_o, take(D * D), D, D); pk.f32(base + lo.b_o, take(D), D);
     pk.f32(base + lo.pos_u, take(D), D); pk.f32(base + lo.pos_v, take(D), D);
     pk.f32(base + lo.wpos, take(D * D), D * D);
     pk.f32(base + lo.ln[4], take(D), D); pk.f32(base + lo.ln[5], take(D), D);
     {  // pw1 [D][2D] -> GLU-packed rows: value channel c at glu_a_col(c), its gate 32 rows later
       const float* w = take(D * 2 * D);
+      pk.rows = 2 * D;
       for (size_t ch = 0; ch < D; ++ch) {
         const size_t ra = glu_a_col((int)ch), rb = ra + 32;
-        for (size_t k = 0; k < D; ++k) {
-          pk.op(base + lo.w_pw1, ra * D + k, w[k * 2 * D + ch]);
-          pk.op(base + lo.w_pw1, rb * D + k, w[k * 2 * D + D + ch]);
-        }
+        pk.column(base + lo.w_pw1, w, D, 2 * D, ch, ra);
+        pk.column(base + lo.w_pw1, w, D, 2 * D, D + ch, rb);
       }
       pk.f32(base + lo.b_pw1, take(2 * D), 2 * D);
     }
@@ -742,14 +777,16 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
         for (int k = 0; k < d.K; ++k) dst[(size_t)k * D + ch] = w[ch * d.K + k];
       pk.f32(base + lo.b_dw, take(D), D);
     }
-    pk.transpose(base + lo.w_pw2, take(D * D), D, D); pk.f32(base + lo.b_pw2, take(D), D);
+    pk.rows = D; pk.transpose(base + lo.w_pw2, take(D * D), D, D); pk.f32(base + lo.b_pw2, take(D), D);
     ffp(6, lo.b_ff2_1, lo.b_ff2_2, lo.w_ff2_1, lo.w_ff2_2);
     pk.f32(base + lo.ln[8], take(D), D); pk.f32(base + lo.ln[9], take(D), D);
   }
   if (d.P) {
+    pk.rows = d.P;
     pk.transpose(lay.wj, take(D * d.P), D, d.P);
     pk.f32(lay.bj, take(d.P), d.P);
   }
+  pk.wq = 0;  // the front end keeps the compute dtype
   if (d.fe) {  // conv [out][in][tap] -> [out][tap * in + c_in] (matches a window of 3 rows)
     const size_t cin[3] = {(size_t)d.bins, D, D};
     for (int i = 0; i < 3; ++i) {
@@ -944,6 +981,7 @@ int32_t cac_push_chunk(cac_ctx* c, int32_t n, const int32_t* ids, int32_t n_fram
   }
   if (!d_input || !d_out) return c->fail(CAC_EINVAL, "input or output pointer is NULL");
   if ((const void*)d_out == d_input) return c->fail(CAC_EINVAL, "input and output must be different buffers");
+  if (d.wq && (long)n * n_frames > 2) return c->fail(CAC_EINVAL, "with int8 weights a push carries at most 2 rows (streams x frames)");
   if ((rc = pending_error(c))) return rc;
 
   // host bookkeeping decides who runs a pass (lookahead: streams whose pending frames reach

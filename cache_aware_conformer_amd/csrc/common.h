@@ -11,7 +11,8 @@
 
 typedef uint16_t bf16_t;  // bfloat16 storage
 
-enum DType { DT_F32 = 0, DT_BF16 = 1 };
+// DT_I8W: float32 activations and caches, int8 weights with a float32 scale per output row
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_I8W = 2 };
 
 // ------------------------------------------------------------------------ element helpers
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }

@@ -952,8 +952,9 @@ bool launch_resid_ln(Launcher& L, const ResLnArgs& a, int dtype) {
 // it reads and what its epilogue writes to per-stream state (K/V rows, depthwise input rows)
 // or to the caller's output. Activations that stay on chip or in cache are not counted.
 double gemm_bytes(const GemmArgs& a, int wsz) {
-  double b = (double)a.N * a.K * wsz;
-  const double esz = (double)wsz;
+  // int8 weights (wsz 1): the codes, one float32 scale per row, float32 caches
+  double b = (double)a.N * a.K * wsz + (wsz == 1 ? 4.0 * a.N : 0.0);
+  const double esz = wsz == 1 ? 4.0 : (double)wsz;
   if (a.a_dw) b += (double)a.epi.cv.n_streams * (a.dw_taps - 1 + a.epi.cv.nf) * a.K * esz;
   switch (a.epi.kind) {
     case EPI_QKV: b += (double)a.M * 2.0 * a.epi.D * esz; break;
@@ -1092,7 +1093,7 @@ void launch_gemm(Launcher& L, const GemmArgs& a0, int dtype, int path) {
   if (a.epi.kind == EPI_SILU_KEEP && !mfma) a.epi.kind = EPI_SILU;
   if (a.epi.kind == EPI_RESID_KEEP && !mfma) a.epi.kind = EPI_RESID;
   if (path == 0 && rowdot_launch(L, a, dtype)) return;
-  if (a.epi.kind == EPI_GLU_DW) {  // only the two-row kernel has this epilogue
+  if (a.epi.kind == EPI_GLU_DW || dtype == DT_I8W) {  // only the two-row kernel has these
     if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
     return;
   }

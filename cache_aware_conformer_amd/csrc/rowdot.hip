@@ -137,10 +137,22 @@ __device__ __forceinline__ float round_to(float v) {
   return v;
 }
 
+// Four int8 weights (one 32-bit word, lowest byte first) as floats.
+__device__ __forceinline__ void unpack_i8(unsigned int r, float* f) {
+  f[0] = (float)((int)(r << 24) >> 24);
+  f[1] = (float)((int)(r << 16) >> 24);
+  f[2] = (float)((int)(r << 8) >> 24);
+  f[3] = (float)((int)r >> 24);
+}
+
 // y[m][n] = A[m] . W[n] for m < M <= 2, with the operand transform AM and the epilogue EK.
 // K = KCH * 64 * (16 / sizeof(TW)); UPW output units per wave; blocks of 4 waves.
-template <typename TW, typename TA, int KCH, int UPW, int AM, int EK>
+// WQ: the weights are int8 codes [N][K] followed by one float32 scale per row (N of them); TW
+// (float) stays the type of activations and caches, each lane reads its VEC codes of a chunk as
+// one 32-bit word, and the row's scale multiplies the lane's partial sums.
+template <typename TW, typename TA, int KCH, int UPW, int AM, int EK, int WQ = 0>
 __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
+  static_assert(!WQ || sizeof(TW) == 4, "int8 weights with float32 activations");
   constexpr int VEC = 16 / sizeof(TW);
   constexpr int K = KCH * 64 * VEC;
   constexpr int PER = KCH * VEC;  // elements of each row this lane holds
@@ -180,15 +192,26 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
     pos = e.cv.cpos[s] + frame;
   }
   // ---------------------------------------------------------------- every global read
-  u32x4 wr[UPW][COLS][KCH];
+  u32x4 wr[UPW][COLS][WQ ? 1 : KCH];
+  unsigned int wq[UPW][COLS][WQ ? KCH : 1];
+  float wsc[UPW][COLS];
+  const signed char* Wq = (const signed char*)a.W;
+  const float* wscale = (const float*)(Wq + (long)a.N * K);
 #pragma unroll
   for (int u = 0; u < UPW; ++u)
 #pragma unroll
     for (int c = 0; c < COLS; ++c) {
       const int uw = min(u0 + u, units - 1);
       const int col = GLU ? glu_a_col(uw) + 32 * c : uw;
+      if constexpr (WQ) {
 #pragma unroll
-      for (int k = 0; k < KCH; ++k) wr[u][c][k] = __builtin_nontemporal_load((const u32x4*)(W + (long)col * K + (k * 64 + lane) * VEC));
+        for (int k = 0; k < KCH; ++k)
+          wq[u][c][k] = __builtin_nontemporal_load((const unsigned int*)(Wq + (long)col * K + (k * 64 + lane) * VEC));
+        wsc[u][c] = wscale[col];
+      } else {
+#pragma unroll
+        for (int k = 0; k < KCH; ++k) wr[u][c][k] = __builtin_nontemporal_load((const u32x4*)(W + (long)col * K + (k * 64 + lane) * VEC));
+      }
     }
   float x[RD_ROWS][PER];
 #pragma unroll
@@ -294,14 +317,15 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
 #pragma unroll
       for (int k = 0; k < KCH; ++k) {
         float w[VEC];
-        unpack_w<TW>(wr[u][c][k], w);
+        if constexpr (WQ) unpack_i8(wq[u][c][k], w);
+        else unpack_w<TW>(wr[u][c][k], w);
 #pragma unroll
         for (int r = 0; r < RD_ROWS; ++r)
 #pragma unroll
           for (int j = 0; j < VEC; ++j) acc[r] += w[j] * x[r][k * VEC + j];
       }
 #pragma unroll
-      for (int r = 0; r < RD_ROWS; ++r) p[(u * RD_ROWS + r) * COLS + c] = acc[r];
+      for (int r = 0; r < RD_ROWS; ++r) p[(u * RD_ROWS + r) * COLS + c] = WQ ? acc[r] * wsc[u][c] : acc[r];
     }
   const float val = fold_sums<NV>(p, lane);
 
@@ -347,43 +371,43 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------------------ dispatch
-template <typename TW, typename TA, int AM, int EK, int UPW>
+template <typename TW, typename TA, int AM, int EK, int UPW, int WQ>
 const void* pick_kch(int kch) {
   constexpr int KMAX = AM == AM_PLAIN ? (sizeof(TW) == 4 ? 8 : 4) : (sizeof(TW) == 4 ? 4 : 2);
-  if (kch == 1) return (const void*)&rowdot_kernel<TW, TA, 1, UPW, AM, EK>;
-  if (kch == 2) return (const void*)&rowdot_kernel<TW, TA, 2, UPW, AM, EK>;
+  if (kch == 1) return (const void*)&rowdot_kernel<TW, TA, 1, UPW, AM, EK, WQ>;
+  if (kch == 2) return (const void*)&rowdot_kernel<TW, TA, 2, UPW, AM, EK, WQ>;
   if constexpr (KMAX >= 4)
-    if (kch == 4) return (const void*)&rowdot_kernel<TW, TA, 4, UPW, AM, EK>;
+    if (kch == 4) return (const void*)&rowdot_kernel<TW, TA, 4, UPW, AM, EK, WQ>;
   if constexpr (KMAX >= 8)
-    if (kch == 8) return (const void*)&rowdot_kernel<TW, TA, 8, UPW, AM, EK>;
+    if (kch == 8) return (const void*)&rowdot_kernel<TW, TA, 8, UPW, AM, EK, WQ>;
   return nullptr;
 }
 
-template <typename TW, typename TA, int AM, int EK>
+template <typename TW, typename TA, int AM, int EK, int WQ>
 const void* pick_upw(int upw, int kch) {
-  if constexpr (AM == AM_PLAIN || EK == EPI_GLU_DW) return upw == 1 ? pick_kch<TW, TA, AM, EK, 1>(kch) : nullptr;
-  else return upw == 2 ? pick_kch<TW, TA, AM, EK, 2>(kch) : pick_kch<TW, TA, AM, EK, 1>(kch);
+  if constexpr (AM == AM_PLAIN || EK == EPI_GLU_DW) return upw == 1 ? pick_kch<TW, TA, AM, EK, 1, WQ>(kch) : nullptr;
+  else return upw == 2 ? pick_kch<TW, TA, AM, EK, 2, WQ>(kch) : pick_kch<TW, TA, AM, EK, 1, WQ>(kch);
 }
 
 // The instantiated mixes: LayerNorm'ed float rows into SiLU (also after a second LayerNorm),
 // QKV, GLU + depthwise and float32 (joint) epilogues; plain compute-dtype rows into the
 // residual epilogue.
-template <typename TW, typename TA>
+template <typename TW, typename TA, int WQ = 0>
 const void* pick_mode(int am, int ek, int upw, int kch) {
   if constexpr (sizeof(TA) == 4) {
-    if (am == AM_LN2) return ek == EPI_SILU ? pick_upw<TW, TA, AM_LN2, EPI_SILU>(upw, kch) : nullptr;
+    if (am == AM_LN2) return ek == EPI_SILU ? pick_upw<TW, TA, AM_LN2, EPI_SILU, WQ>(upw, kch) : nullptr;
     if (am == AM_LN) {
       switch (ek) {
-        case EPI_SILU: return pick_upw<TW, TA, AM_LN, EPI_SILU>(upw, kch);
-        case EPI_QKV: return pick_upw<TW, TA, AM_LN, EPI_QKV>(upw, kch);
-        case EPI_GLU_DW: return pick_upw<TW, TA, AM_LN, EPI_GLU_DW>(upw, kch);
-        case EPI_F32: return pick_upw<TW, TA, AM_LN, EPI_F32>(upw, kch);
+        case EPI_SILU: return pick_upw<TW, TA, AM_LN, EPI_SILU, WQ>(upw, kch);
+        case EPI_QKV: return pick_upw<TW, TA, AM_LN, EPI_QKV, WQ>(upw, kch);
+        case EPI_GLU_DW: return pick_upw<TW, TA, AM_LN, EPI_GLU_DW, WQ>(upw, kch);
+        case EPI_F32: return pick_upw<TW, TA, AM_LN, EPI_F32, WQ>(upw, kch);
         default: return nullptr;
       }
     }
   }
   if constexpr (sizeof(TA) == sizeof(TW)) {
-    if (am == AM_PLAIN && ek == EPI_RESID) return pick_upw<TW, TA, AM_PLAIN, EPI_RESID>(upw, kch);
+    if (am == AM_PLAIN && ek == EPI_RESID) return pick_upw<TW, TA, AM_PLAIN, EPI_RESID, WQ>(upw, kch);
   }
   return nullptr;
 }
@@ -397,7 +421,7 @@ struct Plan {
 Plan plan(const GemmArgs& a, int dtype) {
   Plan p;
   if (a.M < 1 || a.M > RD_ROWS || a.a_dw) return p;
-  const int wsz = dtype == DT_F32 ? 4 : 2, vec = 16 / wsz;
+  const int wsz = dtype == DT_BF16 ? 2 : 4, vec = 16 / wsz;  // int8 weights keep the float32 lane layout
   if (a.K % (64 * vec)) return p;
   const int kch = a.K / (64 * vec);
   const int ek = a.epi.kind;
@@ -408,7 +432,7 @@ Plan plan(const GemmArgs& a, int dtype) {
   if (am == AM_LN2 && !a.pre_b) return p;
   if (ek == EPI_RESID && a.res_g && (a.epi.ldo % 256 || a.epi.ldo > 1024 || !a.res_src || !a.res_b)) return p;
   if (ek == EPI_GLU_DW && (a.dw_taps < 1 || a.dw_taps > RD_TAPS || !a.dw_w || !a.dw_b || a.N % 64)) return p;
-  const bool a_float = dtype == DT_F32 || a.a_f32;
+  const bool a_float = dtype != DT_BF16 || a.a_f32;
   const int units = ek == EPI_GLU_DW ? a.N / 2 : a.N;
   // two units per wave only where that still leaves a wave per SIMD; 4-wave blocks only where
   // they still cover every CU
@@ -417,6 +441,7 @@ Plan plan(const GemmArgs& a, int dtype) {
   const int waves = (units + upw - 1) / upw;
   p.wpb = waves >= 1024 ? 4 : 1;
   if (dtype == DT_F32) p.fn = pick_mode<float, float>(am, ek, upw, kch);
+  else if (dtype == DT_I8W) p.fn = pick_mode<float, float, 1>(am, ek, upw, kch);
   else if (a_float) p.fn = pick_mode<bf16_t, float>(am, ek, upw, kch);
   else p.fn = pick_mode<bf16_t, bf16_t>(am, ek, upw, kch);
   p.grid = dim3((waves + p.wpb - 1) / p.wpb);
@@ -430,8 +455,8 @@ bool rowdot_supported(const GemmArgs& a, int dtype) { return plan(a, dtype).fn !
 bool rowdot_launch(Launcher& L, const GemmArgs& a, int dtype) {
   const Plan p = plan(a, dtype);
   if (!p.fn) return false;
-  L.tag(dtype == DT_F32 ? "gemm_tworow_f32" : "gemm_tworow_bf16", gemm_bytes(a, dtype == DT_F32 ? 4 : 2),
-        2.0 * a.M * a.N * a.K);
+  L.tag(dtype == DT_F32 ? "gemm_tworow_f32" : dtype == DT_I8W ? "gemm_tworow_i8w" : "gemm_tworow_bf16",
+        gemm_bytes(a, dtype == DT_F32 ? 4 : dtype == DT_I8W ? 1 : 2), 2.0 * a.M * a.N * a.K);
   GemmArgs args = a;
   L.launch(p.fn, p.grid, dim3(64 * p.wpb), 0, &args);
   return true;

@@ -56,6 +56,15 @@ extern "C" {
    depthwise conv always run in fp32) */
 #define CAC_F32 0
 #define CAC_BF16 1
+/* float32 activations and caches with int8 dense weights: each matrix of the blocks (FF1/FF2
+   w1 and w2, wq/wk/wv/wo, pw1, pw2) and the joint is stored as codes q[n][k] with one float32
+   scale s[n] per output n, s = max_k |w[k][n]| / 127 and q = rint(w / s) clamped to +-127 (round
+   half to even, float32 arithmetic), and computes with q * s. The compression the pages name
+   for the weight-bandwidth-bound one-stream case ("Fast Accuracy-Preserving RNNT Beam Search on
+   Apple Silicon", §1.3; "True streaming encode — implementation spec", "Status"); an
+   approximation of the float32 encoder. No front end, no lookahead, d_model and d_ff multiples
+   of 256; a push carries at most 2 rows (streams x frames), else CAC_EINVAL. */
+#define CAC_F32_I8 2
 
 /* config flags */
 #define CAC_FLAG_DRY_RUN 1 /* host-only context: validation and stream bookkeeping, no device
@@ -82,7 +91,7 @@ typedef struct {
   int32_t mel_bins;      /* 128 */
   int32_t mel_per_chunk; /* 16 mel frames -> 2 subsampled frames */
   int32_t mel_tail;      /* 14 */
-  int32_t dtype;         /* CAC_F32 or CAC_BF16 */
+  int32_t dtype;         /* CAC_F32, CAC_BF16 or CAC_F32_I8 */
   int32_t max_streams;   /* stream ids are 0 .. max_streams-1 */
   int32_t max_push_frames; /* most frames one push may carry (exact variant), <= 16 */
   int32_t flags;         /* CAC_FLAG_* */

@@ -30,7 +30,7 @@ class EncConfig:
     mel_bins: int = 128
     mel_per_chunk: int = 16
     mel_tail: int = 14
-    dtype: str = "f32"      # "f32" or "bf16"
+    dtype: str = "f32"      # "f32", "bf16" or "i8w" (float32 with int8 dense weights)
     streams: int = 1
     chunks: int = 100       # pushes per stream in the workload
     staggered: bool = False  # streams start from injected random states
@@ -63,7 +63,10 @@ C4 = EncConfig(name="C4_eou_bf16_1024streams_frontend", seed=3, dtype="bf16", st
 C5 = EncConfig(name="C5_lookahead_bf16_512streams", seed=4, dtype="bf16", streams=512, chunks=300,
                staggered=True, att_right=3, n_emit=2, n_lookahead=8)
 
-CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
+# the one-stream encoder of C2 (same seed: same weights and inputs) with int8 dense weights
+C2Q = C2.replace(name="C2_eou_i8w_1stream", dtype="i8w")
+
+CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C2Q": C2Q}
 
 
 @dataclass(frozen=True)

@@ -41,9 +41,15 @@ def _oracle(cfg):
     from oracle import Oracle
     from oracle.decoder import GreedyDecoder
     from synth import DecConfig, make_dec_weights, make_weights
+    from oracle.quant import compress_weights
     if cfg not in _CACHE:
         _CACHE.clear()
-        _CACHE[cfg] = GreedyDecoder(cfg, make_dec_weights(cfg)) if isinstance(cfg, DecConfig) else Oracle(cfg, make_weights(cfg))
+        if isinstance(cfg, DecConfig):
+            _CACHE[cfg] = GreedyDecoder(cfg, make_dec_weights(cfg))
+        elif cfg.dtype == "i8w":   # int8 dense weights: the oracle runs on their reconstruction
+            _CACHE[cfg] = Oracle(cfg, compress_weights(make_weights(cfg)))
+        else:
+            _CACHE[cfg] = Oracle(cfg, make_weights(cfg))
     return _CACHE[cfg]
 
 

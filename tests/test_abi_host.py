@@ -37,6 +37,25 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(cac.binding.SIGNATURES)
 
 
+def test_int8_weights_config_and_push_limits():
+    """int8 dense weights: no front end or lookahead; a push carries at most two rows."""
+    from synth import C2Q
+    lib = cac.load()
+    for field, value in [("frontend", 1), ("n_lookahead", 8), ("d_ff", 2112)]:
+        c = cac.make_config(C2Q, max_streams=2)
+        setattr(c, field, value)
+        if field == "n_lookahead":
+            c.att_right = 3
+        assert lib.cac_workspace_bytes(C.byref(c)) == 0, field
+    c16 = cac.make_config(C2, max_streams=2)
+    c8 = cac.make_config(C2Q, max_streams=2)
+    assert 0 < lib.cac_workspace_bytes(C.byref(c8)) < lib.cac_workspace_bytes(C.byref(c16))
+    enc = dry(C2Q, streams=2)
+    assert push(enc, [0], 2)[0] == CAC_ENODEV
+    assert push(enc, [0, 1], 2)[0] == CAC_EINVAL
+    assert push(enc, [1], 4)[0] == CAC_EINVAL
+
+
 @pytest.mark.parametrize("cfg", [C1, C2, C3, C4, C5], ids=lambda c: c.name)
 def test_param_and_state_layouts(cfg):
     lib = cac.load()

@@ -140,6 +140,28 @@ def test_c2_eou_f32_all_1000_chunks():
     _check_tokens(got, ref, "C2/1000")
 
 
+def test_c2q_int8_weights_one_stream():
+    """The one-stream encoder with int8 dense weights over 300 chunks: max-abs <= 1e-4 and
+    identical tokens against the oracle on the reconstructed weights, and within the int8
+    approximation bar of the full-precision oracle."""
+    from synth import C2Q
+    from test_oracle_quant_pins import INT8_REL_BAR
+    chunks = 300
+    hq = oracle_pool.submit_streams(C2Q, [0], chunks, staggered=False)
+    hf = oracle_pool.submit_streams(C2, [0], chunks, staggered=False)
+    enc = _enc(C2Q, make_weights(C2Q), max_streams=1)
+    xs = make_inputs(C2Q, 0, chunks)
+    got = np.stack([enc.push_chunk([0], to_dev(xs[c][None], C2Q))[0].cpu().numpy()[0] for c in range(chunks)])
+    ref = np.stack([r[0] for r in oracle_pool.collect(hq)[0]])
+    full = np.stack([r[0] for r in oracle_pool.collect(hf)[0]])
+    err = np.abs(got - ref).max()
+    approx = float(np.abs(got - full).max() / np.abs(full).max())
+    log(f"C2 int8: max-abs {err:.3e} against the reconstructed-weight oracle; {approx:.3e} relative to full precision")
+    assert err <= F32_TOL
+    assert approx <= INT8_REL_BAR
+    _check_tokens(got, ref, "C2 int8/300")
+
+
 # ----------------------------------------------------------------------------- bf16 workloads
 
 def _check_workload(cfg, chunks, check, flush=False, extra=None):
