@@ -1,8 +1,8 @@
 """Cache-aware streaming Conformer chunk step for MI355X (gfx950).
 
 The work runs in ``libcac.so`` (HIP kernels behind the C ABI of ``include/cac.h`` for the
-encoder chunk step and ``include/cac_decode.h`` for greedy decoding of its output); ``binding``
-is its thin ctypes wrapper.
+encoder chunk step, ``include/cac_decode.h`` for greedy decoding of its output and
+``include/cac_mel.h`` for the streaming log-mel front); ``binding`` is its thin ctypes wrapper.
 """
 from .binding import (  # noqa: F401
     CAC_BF16,
@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     CacError,
     StreamingDecoder,
     StreamingEncoder,
+    StreamingMel,
     load,
     make_config,
     pack_params,

@@ -36,9 +36,23 @@ class cac_dec_config(C.Structure):
         "joint_dim", "pred_hidden", "pred_layers", "vocab", "max_symbols", "max_streams", "max_frames", "flags")]
 
 
+class cac_mel_config(C.Structure):
+    _fields_ = [("sample_rate", C.c_int32), ("n_fft", C.c_int32), ("win_length", C.c_int32), ("hop", C.c_int32),
+                ("n_mels", C.c_int32), ("fmin", C.c_float), ("fmax", C.c_float), ("preemph", C.c_float),
+                ("out_dtype", C.c_int32), ("max_streams", C.c_int32), ("max_hops", C.c_int32), ("flags", C.c_int32)]
+
+
 _CFGP = C.POINTER(cac_config)
 _DCFGP = C.POINTER(cac_dec_config)
+_MCFGP = C.POINTER(cac_mel_config)
 SIGNATURES = {
+    # include/cac_mel.h
+    "cac_mel_workspace_bytes": (_sz, [_MCFGP]),
+    "cac_mel_create": (_i32, [_MCFGP, _vp, _sz, _vp, C.POINTER(_vp)]),
+    "cac_mel_push": (_i32, [_vp, _i32, _ip, _i32, _vp, _vp]),
+    "cac_mel_reset": (_i32, [_vp, _i32, _ip]),
+    "cac_mel_destroy": (_i32, [_vp]),
+    "cac_mel_last_error": (C.c_char_p, [_vp]),
     # include/cac_decode.h
     "cac_dec_param_count": (_sz, [_DCFGP]),
     "cac_dec_workspace_bytes": (_sz, [_DCFGP]),
@@ -486,6 +500,81 @@ class StreamingDecoder:
     def close(self):
         if getattr(self, "ctx", None):
             self.lib.cac_dec_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ----------------------------------------------------------------------------- streaming log-mel
+
+def make_mel_config(cfg, max_streams=None, max_hops=None, flags=0) -> cac_mel_config:
+    c = cac_mel_config()
+    for name in ("sample_rate", "n_fft", "win_length", "hop", "n_mels"):
+        setattr(c, name, int(getattr(cfg, name)))
+    c.fmin, c.fmax, c.preemph = float(cfg.fmin), float(cfg.fmax), float(cfg.preemph)
+    c.out_dtype = CAC_BF16 if str(cfg.out_dtype) in ("bf16", str(CAC_BF16)) else CAC_F32
+    c.max_streams = int(max_streams if max_streams is not None else cfg.streams)
+    c.max_hops = int(max_hops if max_hops is not None else cfg.hops)
+    c.flags = int(flags)
+    return c
+
+
+class StreamingMel:
+    """One log-mel context (include/cac_mel.h): tables and every stream's sample tail in one
+    device workspace, work on the current torch stream."""
+
+    def __init__(self, cfg, max_streams=None, max_hops=None, flags=0, device="cuda:0"):
+        self.lib = load()
+        self.cfg = cfg
+        self.c = make_mel_config(cfg, max_streams, max_hops, flags)
+        self.dry = bool(flags & CAC_FLAG_DRY_RUN)
+        self.ws_bytes = self.lib.cac_mel_workspace_bytes(C.byref(self.c))
+        ctx = C.c_void_p()
+        if self.dry:
+            ws_ptr, stream, self.ws = None, None, None
+        else:
+            import torch
+            self.torch = torch
+            self.device = torch.device(device)
+            self.ws = torch.empty(max(self.ws_bytes, 1) + 256, dtype=torch.uint8, device=self.device)
+            ws_ptr = (self.ws.data_ptr() + 255) // 256 * 256
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        rc = self.lib.cac_mel_create(C.byref(self.c), ws_ptr, self.ws_bytes, stream, C.byref(ctx))
+        if rc != CAC_OK:
+            raise CacError(rc, self.lib.cac_mel_last_error(None).decode())
+        self.ctx = ctx
+
+    def _check(self, rc):
+        if rc < 0:
+            raise CacError(rc, self.lib.cac_mel_last_error(self.ctx).decode())
+        return rc
+
+    def push(self, stream_ids, audio, out=None):
+        """audio: device float32 [n, n_samples]. Returns device [n, n_samples // hop, n_mels]."""
+        ids, idp = _ids(stream_ids)
+        n, ns = ids.size, int(audio.shape[1])
+        if not self.dry:
+            t = self.torch
+            if audio.dtype != t.float32 or not audio.is_contiguous() or audio.shape[0] != n:
+                raise ValueError(f"audio must be a contiguous float32 tensor with {n} rows")
+            if out is None:
+                dt = t.bfloat16 if self.c.out_dtype == CAC_BF16 else t.float32
+                out = t.empty((n, ns // self.c.hop, self.c.n_mels), dtype=dt, device=self.device)
+        ptr = lambda x: None if x is None else (x.data_ptr() if hasattr(x, "data_ptr") else int(x))  # noqa: E731
+        self._check(self.lib.cac_mel_push(self.ctx, n, idp, ns, ptr(audio), ptr(out)))
+        return out
+
+    def reset(self, stream_ids):
+        ids, idp = _ids(stream_ids)
+        return self._check(self.lib.cac_mel_reset(self.ctx, ids.size, idp))
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            self.lib.cac_mel_destroy(self.ctx)
             self.ctx = None
 
     def __del__(self):

@@ -62,34 +62,37 @@ def hann(n=WIN):
     return 0.5 - 0.5 * np.cos(2.0 * np.pi * np.arange(n) / n)
 
 
-def power_spectrum(frames):
-    """|rfft(frame * hann, N_FFT)|^2 of frames [G, WIN] (M3)."""
-    return np.abs(np.fft.rfft(np.asarray(frames, np.float64) * hann(), n=N_FFT, axis=-1)) ** 2
+def power_spectrum(frames, n_fft=N_FFT):
+    """|rfft(frame * hann, n_fft)|^2 of frames [G, win] (M3)."""
+    frames = np.asarray(frames, np.float64)
+    return np.abs(np.fft.rfft(frames * hann(frames.shape[-1]), n=n_fft, axis=-1)) ** 2
 
 
-def logmel_offline(x):
-    """Log-mel frames [len(x) // HOP, N_MELS] of a whole signal (M1-M6)."""
+def logmel_offline(x, n_fft=N_FFT, win=WIN, hop=HOP):
+    """Log-mel frames [len(x) // hop, N_MELS] of a whole signal (M1-M6)."""
     x = np.asarray(x, dtype=np.float64)
     y = x - PREEMPH * np.concatenate([[0.0], x[:-1]])
-    G = x.size // HOP
-    ypad = np.concatenate([np.zeros(WIN - HOP), y])
-    frames = np.stack([ypad[g * HOP: g * HOP + WIN] for g in range(G)]) if G else np.zeros((0, WIN))
-    return np.log(power_spectrum(frames) @ mel_filters().T + LOG_GUARD)
+    G = x.size // hop
+    ypad = np.concatenate([np.zeros(win - hop), y])
+    frames = np.stack([ypad[g * hop: g * hop + win] for g in range(G)]) if G else np.zeros((0, win))
+    return np.log(power_spectrum(frames, n_fft) @ mel_filters(n_fft=n_fft).T + LOG_GUARD)
 
 
 class MelStream:
     """Streaming log-mel of one stream: each push of whole hops returns its own frames; the
-    stream carries the last WIN - HOP + 1 raw samples."""
+    stream carries the last win - hop + 1 raw samples."""
 
-    def __init__(self):
-        self.tail = np.zeros(WIN - HOP + 1)
+    def __init__(self, n_fft=N_FFT, win=WIN, hop=HOP):
+        self.n_fft, self.win, self.hop = n_fft, win, hop
+        self.tail = np.zeros(win - hop + 1)
 
     def push(self, chunk):
         chunk = np.asarray(chunk, dtype=np.float64)
-        assert chunk.size % HOP == 0
+        win, hop = self.win, self.hop
+        assert chunk.size % hop == 0
         xx = np.concatenate([self.tail, chunk])               # raw samples, one before the window
         y = xx[1:] - PREEMPH * xx[:-1]                        # preemphasis of tail[1:] || chunk
-        G = chunk.size // HOP
-        frames = np.stack([y[g * HOP: g * HOP + WIN] for g in range(G)]) if G else np.zeros((0, WIN))
-        self.tail = xx[-(WIN - HOP + 1):]
-        return np.log(power_spectrum(frames) @ mel_filters().T + LOG_GUARD)
+        G = chunk.size // hop
+        frames = np.stack([y[g * hop: g * hop + win] for g in range(G)]) if G else np.zeros((0, win))
+        self.tail = xx[-(win - hop + 1):]
+        return np.log(power_spectrum(frames, self.n_fft) @ mel_filters(n_fft=self.n_fft).T + LOG_GUARD)

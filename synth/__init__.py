@@ -5,12 +5,14 @@ inputs and injected stream states. It holds none of the encoder's arithmetic, so
 oracle under ``oracle/`` and the HIP path can both consume it without sharing any
 computation.
 """
-from .configs import C1, C2, C2Q, C3, C4, C5, CONFIGS, D1, D2, DEC_CONFIGS, DecConfig, EncConfig, get_config  # noqa: F401
+from .configs import (A4, C1, C2, C2Q, C3, C4, C5, CONFIGS, D1, D2, DEC_CONFIGS, MEL_CONFIGS, DecConfig,  # noqa: F401
+                      EncConfig, MelConfig, get_config)
 from .gen import (  # noqa: F401
     bf16_round,
     make_weights,
     make_dec_weights,
     make_dec_inputs,
+    make_audio,
     dec_weight_names,
     make_inputs,
     make_state,

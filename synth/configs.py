@@ -101,3 +101,29 @@ DEC_CONFIGS = {"D1": D1, "D2": D2}
 
 def get_config(key: str) -> EncConfig:
     return CONFIGS[key]
+
+
+@dataclass(frozen=True)
+class MelConfig:
+    """Streaming log-mel front: raw 16 kHz audio chunks of ``hops`` 10 ms hops per stream."""
+    name: str
+    seed: int
+    sample_rate: int = 16000
+    n_fft: int = 512
+    win_length: int = 400
+    hop: int = 160
+    n_mels: int = 128
+    fmin: float = 0.0
+    fmax: float = 8000.0
+    preemph: float = 0.97
+    out_dtype: str = "f32"
+    streams: int = 1
+    hops: int = 16          # one encoder chunk: 16 mel frames = 160 ms
+    chunks: int = 100
+
+    def replace(self, **kw) -> "MelConfig":
+        return dataclasses.replace(self, **kw)
+
+
+A4 = MelConfig(name="A4_logmel_1024streams", seed=5, streams=1024, chunks=100, out_dtype="bf16")
+MEL_CONFIGS = {"A4": A4}

@@ -20,7 +20,7 @@ import zlib
 
 import numpy as np
 
-from .configs import DecConfig, EncConfig
+from .configs import DecConfig, EncConfig, MelConfig
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
@@ -194,3 +194,18 @@ def make_dec_inputs(cfg: DecConfig, stream: int, calls: int | None = None) -> np
     (the encoder's projected outputs have about unit scale)."""
     x = _rng(cfg, f"dec.input.s{stream}").standard_normal((cfg.calls, cfg.frames, cfg.joint_dim), dtype=np.float32)
     return x if calls is None else x[:calls]
+
+
+def make_audio(cfg: MelConfig, stream: int, chunks: int | None = None) -> np.ndarray:
+    """Raw audio of one stream, [chunks, hops * hop] float32: white noise of amplitude 0.05 plus
+    two tones (frequency uniform in 80 Hz - 7.5 kHz, amplitude uniform in 0.05 - 0.5) that hold
+    for the whole stream (the pages' sample.wav is not available)."""
+    g = _rng(cfg, f"audio.s{stream}")
+    n = cfg.chunks * cfg.hops * cfg.hop
+    t = np.arange(n) / cfg.sample_rate
+    x = 0.05 * g.standard_normal(n)
+    for _ in range(2):
+        f, a, ph = g.uniform(80.0, 7500.0), g.uniform(0.05, 0.5), g.uniform(0.0, 2 * np.pi)
+        x += a * np.sin(2 * np.pi * f * t + ph)
+    x = x.astype(np.float32).reshape(cfg.chunks, cfg.hops * cfg.hop)
+    return x if chunks is None else x[:chunks]

@@ -286,3 +286,26 @@ def test_decoder_param_layout_and_validation():
     with pytest.raises(CacError):
         cac.StreamingDecoder(D1, {k: v[:1] for k, v in make_dec_weights(D1).items()}, max_streams=4,
                              flags=cac.CAC_FLAG_DRY_RUN)
+
+
+# ----------------------------------------------------------------------- streaming log-mel ABI
+
+def test_mel_config_and_push_validation():
+    from synth import A4
+    lib = cac.load()
+    c = cac.binding.make_mel_config(A4, max_streams=4)
+    assert lib.cac_mel_workspace_bytes(C.byref(c)) > 0
+    for field, value in [("n_fft", 500), ("win_length", 600), ("win_length", 160), ("win_length", 401), ("n_mels", 0),
+                         ("fmax", 9000.0), ("preemph", 1.5), ("max_hops", 0), ("max_streams", 0), ("out_dtype", 5)]:
+        bad = cac.binding.make_mel_config(A4, max_streams=4)
+        setattr(bad, field, value)
+        assert lib.cac_mel_workspace_bytes(C.byref(bad)) == 0, field
+    mel = cac.StreamingMel(A4, max_streams=4, flags=cac.CAC_FLAG_DRY_RUN)
+    ip = lambda a: np.asarray(a, np.int32).ctypes.data_as(C.POINTER(C.c_int32))  # noqa: E731
+    p = C.c_void_p(256)
+    assert lib.cac_mel_push(mel.ctx, 1, ip([0]), 2560, p, p) == CAC_ENODEV
+    assert lib.cac_mel_push(mel.ctx, 1, ip([0]), 2561, p, p) == CAC_EINVAL
+    assert lib.cac_mel_push(mel.ctx, 1, ip([0]), 160 * 17, p, p) == CAC_EINVAL
+    assert lib.cac_mel_push(mel.ctx, 2, ip([3, 3]), 160, p, p) == CAC_EINVAL
+    assert lib.cac_mel_push(mel.ctx, 1, ip([0]), 160, None, p) == CAC_EINVAL
+    assert lib.cac_mel_reset(mel.ctx, 1, ip([9])) == CAC_EINVAL

@@ -82,3 +82,13 @@ def test_streaming_chunks_equal_the_offline_frames(chunks):
         out.append(ms.push(x[s * HOP:(s + c) * HOP]))
         s += c
     assert np.abs(np.concatenate(out) - off).max() < 1e-12
+
+
+def test_streaming_equals_offline_for_other_frame_shapes():
+    rng = np.random.default_rng(4)
+    for n_fft, win, hop in ((256, 200, 80), (1024, 800, 320)):
+        x = rng.standard_normal(hop * 12)
+        off = logmel_offline(x, n_fft, win, hop)
+        ms = MelStream(n_fft, win, hop)
+        got = np.concatenate([ms.push(x[i * hop * 3:(i + 1) * hop * 3]) for i in range(4)])
+        assert np.abs(got - off).max() < 1e-12
