@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--secondary", default="C2,C2Q",
                     help="comma-separated workloads reported in the same line, or 'none'")
     ap.add_argument("--decode", default="D2", help="greedy-decoding workload reported in the same line, or 'none'")
+    ap.add_argument("--mel", default="A4", help="streaming log-mel workload reported in the same line, or 'none'")
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time per CPU-baseline mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -321,6 +322,65 @@ def run_decode(key: str, steps, warmup: int, profile_steps: int):
     return res
 
 
+FP64_VECTOR_PEAK_TFLOPS = 78.6
+
+
+def run_mel(key: str, steps, warmup: int):
+    """Streaming log-mel throughput: every stream pushes one chunk of raw audio (16 hops of 10 ms)
+    per step, inputs resident in HBM."""
+    import torch
+
+    from cache_aware_conformer_amd import StreamingMel
+    from synth import MEL_CONFIGS, make_audio
+
+    cfg = MEL_CONFIGS[key]
+    steps = steps if steps is not None else 100
+    S = cfg.streams
+    dev = torch.device("cuda:0")
+    mel = StreamingMel(cfg)
+    per = min(cfg.chunks, warmup + steps + 1)
+    xs = np.ascontiguousarray(np.stack([make_audio(cfg, s, per) for s in range(S)]).swapaxes(0, 1))
+    x = torch.from_numpy(xs).to(dev)
+    del xs
+    ids = list(range(S))
+    out = torch.empty((S, cfg.hops, cfg.n_mels), dtype=torch.bfloat16 if cfg.out_dtype == "bf16" else torch.float32,
+                      device=dev)
+    k = 0
+
+    def call():
+        nonlocal k
+        mel.push(ids, x[k % per], out)
+        k += 1
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    frames = S * cfg.hops
+    n2 = cfg.n_fft // 2
+    # float64 operations per frame: the complex FFT (5 N2 log2 N2), the real split (~10 per
+    # bin), the filter sums (2 per filter weight, about 2 bins per filter on average here)
+    flops = frames * (5.0 * n2 * np.log2(n2) + 10.0 * (n2 + 1) + 2.0 * 2 * cfg.n_mels)
+    res = {"value": frames / (ms / 1e3), "unit": "frames/s", "ms_per_step": ms, "steps": steps, "dtype": "f64 transform, "
+           + cfg.out_dtype + " out",
+           "config": {"workload": cfg.name, "streams": S, "hops_per_chunk": cfg.hops, "n_fft": cfg.n_fft,
+                      "win_length": cfg.win_length, "hop": cfg.hop, "n_mels": cfg.n_mels},
+           "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12, "peak": FP64_VECTOR_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "kernel": "logmel + mel_tail (one push)", "avg_launch_us": ms * 1e3,
+                        "traffic": None, "timing": "HIP events around each push (both kernels)",
+                        "hbm_bytes_per_push": S * cfg.hops * cfg.hop * 4.0 + frames * cfg.n_mels * 2.0}}
+    res["roofline"]["frac"] = res["roofline"]["achieved"] / res["roofline"]["peak"]
+    mel.close()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -352,6 +412,9 @@ def main():
         rec = {k: sec[k] for k in ("value", "ms_per_step", "steps", "dtype", "config", "roofline", "step")}
         rec["unit"] = "frames/s"
         res.setdefault("secondary", {})[sec["config"]["workload"]] = rec
+    if args.mel and args.mel.lower() != "none":
+        mres = run_mel(args.mel, args.steps, args.warmup)
+        res.setdefault("secondary", {})[mres["config"]["workload"]] = mres
     if args.decode and args.decode.lower() != "none":
         dres = run_decode(args.decode, args.steps, args.warmup, args.profile_steps)
         res.setdefault("secondary", {})[dres["config"]["workload"]] = dres

@@ -38,7 +38,7 @@ class cac_dec_config(C.Structure):
 
 class cac_mel_config(C.Structure):
     _fields_ = [("sample_rate", C.c_int32), ("n_fft", C.c_int32), ("win_length", C.c_int32), ("hop", C.c_int32),
-                ("n_mels", C.c_int32), ("fmin", C.c_float), ("fmax", C.c_float), ("preemph", C.c_float),
+                ("n_mels", C.c_int32), ("fmin", C.c_double), ("fmax", C.c_double), ("preemph", C.c_double),
                 ("out_dtype", C.c_int32), ("max_streams", C.c_int32), ("max_hops", C.c_int32), ("flags", C.c_int32)]
 
 

@@ -1,6 +1,9 @@
 // Streaming log-mel front (include/cac_mel.h): raw audio of many streams -> log-mel frames.
 //
-// One wave per (stream, frame), blocks on grid (stream, frame). The frame's win_length
+// One wave per (stream, frame), blocks on grid (stream, frame); the transform, power and filter
+// sums run in float64 (a bin's float32 error would scale with the frame's energy, not the bin's,
+// which the low bands after preemphasis hold a millionth of), the output is rounded once. The
+// frame's win_length
 // preemphasised, Hann-weighted samples are packed two to a complex value (even sample real,
 // odd sample imaginary) into LDS in
 // bit-reversed order, transformed by an n_fft/2-point radix-2 FFT, and split into the n_fft
@@ -30,35 +33,36 @@ struct MelArgs {
   const float* audio;    // [n][ns] caller's samples
   const float* tail;     // [S][T] raw samples before this push
   void* out;             // [n][G][n_mels] caller's frames
-  const float* win;      // [win_len] Hann window
-  const float2* tw;      // [N2 / 2] exp(-2 pi i j / N2)
-  const float2* tw2;     // [N2 + 1] exp(-2 pi i k / n_fft)
+  const double* win;     // [win_len] Hann window
+  const double2* tw;     // [N2 / 2] exp(-2 pi i j / N2)
+  const double2* tw2;    // [N2 + 1] exp(-2 pi i k / n_fft)
   const int32_t* fspan;  // [n_mels][2]: first bin, bin count
   const int32_t* foff;   // [n_mels] offset of the filter's weights in fw
-  const float* fw;
+  const double* fw;
   int n, ns, G, win_len, hop, T, N2, bits, n_mels, out_bf16;
-  float preemph;
+  double preemph;
 };
 
 __global__ __launch_bounds__(64) void mel_kernel(MelArgs a) {
   const int s = blockIdx.x, g = blockIdx.y, lane = threadIdx.x;
   const int id = a.ids[s];
-  extern __shared__ __attribute__((aligned(16))) float mlds[];
-  float2* buf = (float2*)mlds;                 // [N2]
-  float* pw = mlds + 2 * a.N2;                 // [N2 + 1]
+  extern __shared__ __attribute__((aligned(16))) double mlds[];
+  double2* buf = (double2*)mlds;               // [N2]
+  double* pw = mlds + 2 * a.N2;                // [N2 + 1]
   const float* tl = a.tail + (long)id * a.T;
   const float* au = a.audio + (long)s * a.ns;
   // raw sample q of tail || audio
-  auto raw = [&](int q) { return q < a.T ? tl[q] : au[q - a.T]; };
+  auto raw = [&](int q) { return (double)(q < a.T ? tl[q] : au[q - a.T]); };
+  const double pre = a.preemph;
   const int p0 = g * a.hop;  // window sample j is preemph(raw[p0 + j + 1], raw[p0 + j])
   for (int m = lane; m < a.N2; m += 64) {
-    float re = 0.0f, im = 0.0f;
+    double re = 0.0, im = 0.0;
     const int j = 2 * m;
     if (j + 1 < a.win_len) {
-      re = (raw(p0 + j + 1) - a.preemph * raw(p0 + j)) * a.win[j];
-      im = (raw(p0 + j + 2) - a.preemph * raw(p0 + j + 1)) * a.win[j + 1];
+      re = (raw(p0 + j + 1) - pre * raw(p0 + j)) * a.win[j];
+      im = (raw(p0 + j + 2) - pre * raw(p0 + j + 1)) * a.win[j + 1];
     }
-    buf[__brev((unsigned)m) >> (32 - a.bits)] = make_float2(re, im);
+    buf[__brev((unsigned)m) >> (32 - a.bits)] = make_double2(re, im);
   }
   __syncthreads();
   for (int len = 2; len <= a.N2; len <<= 1) {
@@ -66,30 +70,30 @@ __global__ __launch_bounds__(64) void mel_kernel(MelArgs a) {
     for (int b = lane; b < a.N2 / 2; b += 64) {
       const int grp = b / half, j = b - grp * half;
       const int i0 = grp * len + j, i1 = i0 + half;
-      const float2 w = a.tw[j * step];
-      const float2 u = buf[i0], v = buf[i1];
-      const float2 t = make_float2(w.x * v.x - w.y * v.y, w.x * v.y + w.y * v.x);
-      buf[i0] = make_float2(u.x + t.x, u.y + t.y);
-      buf[i1] = make_float2(u.x - t.x, u.y - t.y);
+      const double2 w = a.tw[j * step];
+      const double2 u = buf[i0], v = buf[i1];
+      const double2 t = make_double2(w.x * v.x - w.y * v.y, w.x * v.y + w.y * v.x);
+      buf[i0] = make_double2(u.x + t.x, u.y + t.y);
+      buf[i1] = make_double2(u.x - t.x, u.y - t.y);
     }
     __syncthreads();
   }
   // real split: Z[k] and conj(Z[N2 - k]) give the even-sample transform E and the odd one O
   for (int k = lane; k <= a.N2; k += 64) {
-    const float2 zk = buf[k & (a.N2 - 1)], zc = buf[(a.N2 - k) & (a.N2 - 1)];
-    const float er = 0.5f * (zk.x + zc.x), ei = 0.5f * (zk.y - zc.y);   // (Z[k] + conj Z[N2-k]) / 2
-    const float orr = 0.5f * (zk.y + zc.y), oi = -0.5f * (zk.x - zc.x); // (Z[k] - conj Z[N2-k]) / 2i
-    const float2 w = a.tw2[k];
-    const float xr = er + w.x * orr - w.y * oi, xi = ei + w.x * oi + w.y * orr;
+    const double2 zk = buf[k & (a.N2 - 1)], zc = buf[(a.N2 - k) & (a.N2 - 1)];
+    const double er = 0.5 * (zk.x + zc.x), ei = 0.5 * (zk.y - zc.y);   // (Z[k] + conj Z[N2-k]) / 2
+    const double orr = 0.5 * (zk.y + zc.y), oi = -0.5 * (zk.x - zc.x); // (Z[k] - conj Z[N2-k]) / 2i
+    const double2 w = a.tw2[k];
+    const double xr = er + w.x * orr - w.y * oi, xi = ei + w.x * oi + w.y * orr;
     pw[k] = xr * xr + xi * xi;
   }
   __syncthreads();
   for (int m = lane; m < a.n_mels; m += 64) {
     const int k0 = a.fspan[2 * m], nk = a.fspan[2 * m + 1];
-    const float* w = a.fw + a.foff[m];
-    float acc = 0.0f;
+    const double* w = a.fw + a.foff[m];
+    double acc = 0.0;
     for (int k = 0; k < nk; ++k) acc += pw[k0 + k] * w[k];
-    const float v = logf(acc + 5.9604644775390625e-8f);  // 2^-24
+    const float v = (float)log(acc + 5.9604644775390625e-8);  // 2^-24
     const long o = ((long)s * a.G + g) * a.n_mels + m;
     if (a.out_bf16) ((bf16_t*)a.out)[o] = f2bf(v);
     else ((float*)a.out)[o] = v;
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(256) void mel_reset_kernel(MelResetArgs a) {
 // ------------------------------------------------------------------------------- host side
 struct MelDims {
   int sr, nfft, win, hop, nm, out_bf16, S, max_hops, flags, N2, bits, T;
-  float fmin, fmax, pre;
+  double fmin, fmax, pre;
 };
 
 bool mel_dims(const cac_mel_config* c, MelDims& d, std::string& why) {
@@ -147,8 +151,8 @@ bool mel_dims(const cac_mel_config* c, MelDims& d, std::string& why) {
   if (d.nfft != 128 && d.nfft != 256 && d.nfft != 512 && d.nfft != 1024) return bad("n_fft must be 128, 256, 512 or 1024");
   if (d.hop < 1 || d.win <= d.hop || d.win > d.nfft || d.win % 2) return bad("need hop < win_length <= n_fft, win_length even");
   if (d.nm < 1 || d.nm > 256) return bad("n_mels must be in [1, 256]");
-  if (!(d.fmin >= 0.0f) || !(d.fmax > d.fmin) || d.fmax > 0.5f * d.sr) return bad("need 0 <= fmin < fmax <= sample_rate / 2");
-  if (!(d.pre >= 0.0f) || d.pre > 1.0f) return bad("preemph must be in [0, 1]");
+  if (!(d.fmin >= 0.0) || !(d.fmax > d.fmin) || d.fmax > 0.5 * d.sr) return bad("need 0 <= fmin < fmax <= sample_rate / 2");
+  if (!(d.pre >= 0.0) || d.pre > 1.0) return bad("preemph must be in [0, 1]");
   if (c->out_dtype != CAC_F32 && c->out_dtype != CAC_BF16) return bad("out_dtype must be CAC_F32 or CAC_BF16");
   if (d.S < 1 || d.S > (1 << 20)) return bad("max_streams must be in [1, 2^20]");
   if (d.max_hops < 1 || d.max_hops > 64) return bad("max_hops must be in [1, 64]");
@@ -165,7 +169,7 @@ double slaney_mel(double f) { return f < 1000.0 ? 3.0 * f / 200.0 : 15.0 + 27.0 
 double slaney_hz(double m) { return m < 15.0 ? 200.0 * m / 3.0 : 1000.0 * std::exp((m - 15.0) * std::log(6.4) / 27.0); }
 
 struct MelTables {
-  std::vector<float> win, tw, tw2, fw;
+  std::vector<double> win, tw, tw2, fw;
   std::vector<int32_t> fspan, foff;
 };
 
@@ -173,14 +177,14 @@ MelTables mel_tables(const MelDims& d) {
   MelTables t;
   const double pi = 3.14159265358979323846;
   t.win.resize(d.win);
-  for (int i = 0; i < d.win; ++i) t.win[i] = (float)(0.5 - 0.5 * std::cos(2.0 * pi * i / d.win));
+  for (int i = 0; i < d.win; ++i) t.win[i] = 0.5 - 0.5 * std::cos(2.0 * pi * i / d.win);
   for (int j = 0; j < d.N2 / 2; ++j) {
-    t.tw.push_back((float)std::cos(2.0 * pi * j / d.N2));
-    t.tw.push_back((float)-std::sin(2.0 * pi * j / d.N2));
+    t.tw.push_back(std::cos(2.0 * pi * j / d.N2));
+    t.tw.push_back(-std::sin(2.0 * pi * j / d.N2));
   }
   for (int k = 0; k <= d.N2; ++k) {
-    t.tw2.push_back((float)std::cos(2.0 * pi * k / d.nfft));
-    t.tw2.push_back((float)-std::sin(2.0 * pi * k / d.nfft));
+    t.tw2.push_back(std::cos(2.0 * pi * k / d.nfft));
+    t.tw2.push_back(-std::sin(2.0 * pi * k / d.nfft));
   }
   const double m0 = slaney_mel(d.fmin), m1 = slaney_mel(d.fmax);
   for (int m = 0; m < d.nm; ++m) {
@@ -195,8 +199,8 @@ MelTables mel_tables(const MelDims& d) {
       if (tri <= 0.0) continue;
       if (first < 0) first = k;
       // the bins between first and k are inside the triangle too (it is convex in f)
-      while (first + count < k) { t.fw.push_back(0.0f); ++count; }
-      t.fw.push_back((float)(tri * 2.0 / (hi - lo)));
+      while (first + count < k) { t.fw.push_back(0.0); ++count; }
+      t.fw.push_back(tri * 2.0 / (hi - lo));
       ++count;
     }
     t.fspan.push_back(first < 0 ? 0 : first);
@@ -213,12 +217,12 @@ MelLayout mel_layout(const MelDims& d, const MelTables& t) {
   MelLayout y{};
   size_t off = 0;
   auto take = [&](size_t b) { off = (off + 255) & ~(size_t)255; size_t o = off; off += b; return o; };
-  y.win = take(t.win.size() * 4);
-  y.tw = take(t.tw.size() * 4);
-  y.tw2 = take(t.tw2.size() * 4);
+  y.win = take(t.win.size() * 8);
+  y.tw = take(t.tw.size() * 8);
+  y.tw2 = take(t.tw2.size() * 8);
   y.fspan = take(t.fspan.size() * 4);
   y.foff = take(t.foff.size() * 4);
-  y.fw = take(std::max<size_t>(t.fw.size(), 1) * 4);
+  y.fw = take(std::max<size_t>(t.fw.size(), 1) * 8);
   y.tail = take((size_t)d.S * d.T * 4);
   y.ids = take((size_t)d.S * 4);
   y.total = take(0);
@@ -302,12 +306,12 @@ int32_t cac_mel_create(const cac_mel_config* cfg, void* d_workspace, size_t ws_b
   auto put = [&](size_t off, const void* src, size_t bytes) {
     if (e == hipSuccess && bytes) e = hipMemcpyAsync(c->ws + off, src, bytes, hipMemcpyHostToDevice, c->stream);
   };
-  put(lay.win, c->t.win.data(), c->t.win.size() * 4);
-  put(lay.tw, c->t.tw.data(), c->t.tw.size() * 4);
-  put(lay.tw2, c->t.tw2.data(), c->t.tw2.size() * 4);
+  put(lay.win, c->t.win.data(), c->t.win.size() * 8);
+  put(lay.tw, c->t.tw.data(), c->t.tw.size() * 8);
+  put(lay.tw2, c->t.tw2.data(), c->t.tw2.size() * 8);
   put(lay.fspan, c->t.fspan.data(), c->t.fspan.size() * 4);
   put(lay.foff, c->t.foff.data(), c->t.foff.size() * 4);
-  put(lay.fw, c->t.fw.data(), c->t.fw.size() * 4);
+  put(lay.fw, c->t.fw.data(), c->t.fw.size() * 8);
   c->dev_ids = all;
   put(lay.ids, c->dev_ids.data(), (size_t)d.S * 4);
   if (e == hipSuccess) {
@@ -347,11 +351,11 @@ int32_t cac_mel_push(cac_mel* c, int32_t n, const int32_t* ids, int32_t ns, cons
   const MelLayout& y = c->lay;
   MelArgs a{};
   a.ids = c->P<int32_t>(y.ids); a.audio = d_audio; a.tail = c->P<float>(y.tail); a.out = d_mel;
-  a.win = c->P<float>(y.win); a.tw = c->P<float2>(y.tw); a.tw2 = c->P<float2>(y.tw2);
-  a.fspan = c->P<int32_t>(y.fspan); a.foff = c->P<int32_t>(y.foff); a.fw = c->P<float>(y.fw);
+  a.win = c->P<double>(y.win); a.tw = c->P<double2>(y.tw); a.tw2 = c->P<double2>(y.tw2);
+  a.fspan = c->P<int32_t>(y.fspan); a.foff = c->P<int32_t>(y.foff); a.fw = c->P<double>(y.fw);
   a.n = n; a.ns = ns; a.G = G; a.win_len = d.win; a.hop = d.hop; a.T = d.T; a.N2 = d.N2; a.bits = d.bits;
   a.n_mels = d.nm; a.out_bf16 = d.out_bf16; a.preemph = d.pre;
-  const size_t shm = ((size_t)2 * d.N2 + d.N2 + 1) * sizeof(float);
+  const size_t shm = ((size_t)2 * d.N2 + d.N2 + 1) * sizeof(double);
   // algorithmic bytes: the new samples read, the frames written
   L.tag("logmel", (double)n * ns * 4.0 + (double)n * G * d.nm * (d.out_bf16 ? 2 : 4), 0.0);
   L.launch((const void*)&mel_kernel, dim3(n, G), dim3(64), shm, &a);

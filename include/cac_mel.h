@@ -10,7 +10,8 @@
  *   power |X[k]|^2, k = 0 .. n_fft/2; n_mels triangular filters on the Slaney mel scale
  *   between fmin and fmax, each of unit area; out = log(mel + 2^-24).
  * The stream carries its last win_length - hop + 1 raw samples between pushes, so chunked
- * pushes give exactly the frames of one push over the whole signal.
+ * pushes give exactly the frames of one push over the whole signal. The transform runs in
+ * float64 from the float32 samples; only the output is rounded (to out_dtype).
  *
  * Conventions as in cac.h (int32 returns, CAC_* error codes, "d_" device / "h_" host pointers,
  * work on the create-time stream, validation before any device work, no device allocation).
@@ -33,8 +34,8 @@ typedef struct {
   int32_t win_length;   /* 400: <= n_fft, > hop */
   int32_t hop;          /* 160 */
   int32_t n_mels;       /* 128, <= 256 */
-  float fmin, fmax;     /* 0, 8000 (0 <= fmin < fmax <= sample_rate / 2) */
-  float preemph;        /* 0.97 (0 = none) */
+  double fmin, fmax;    /* 0, 8000 (0 <= fmin < fmax <= sample_rate / 2) */
+  double preemph;       /* 0.97 (0 = none) */
   int32_t out_dtype;    /* CAC_F32 or CAC_BF16 (cac.h) */
   int32_t max_streams;  /* stream ids 0 .. max_streams-1, <= 2^20 */
   int32_t max_hops;     /* most hops one push carries (16 = one 160 ms chunk), <= 64 */
@@ -45,7 +46,7 @@ typedef struct {
  * 0 for an invalid config. */
 size_t cac_mel_workspace_bytes(const cac_mel_config* cfg);
 
-/* Validate cfg, build the tables (on the host, in double, then float32), zero every stream's
+/* Validate cfg, build the window, twiddle and filter tables (on the host, in double), zero every stream's
  * tail, synchronise and return the context. CAC_EINVAL / CAC_ENOMEM / CAC_EHIP. */
 int32_t cac_mel_create(const cac_mel_config* cfg, void* d_workspace, size_t ws_bytes, void* hip_stream,
                        cac_mel** out);
