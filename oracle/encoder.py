@@ -42,6 +42,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
+from . import subsample2d
+
 EPS = 1e-5
 
 
@@ -273,7 +275,10 @@ class Oracle:
         return out
 
     def frontend_offline(self, mel):
-        """Offline subsampling of a whole mel sequence [16C, B] -> [2C, D] (A21)."""
+        """Offline subsampling of a whole mel sequence [16C, B] -> [2C, D] (A21; the 2-D variant
+        in ``subsample2d`` when cfg.frontend == 2)."""
+        if self.cfg.frontend == 2:
+            return subsample2d.offline(self.W, mel)
         x = mel
         for w, b, relu in self._fe_layers():
             x = self.conv_s2(x, w, b, left_pad=2)
@@ -285,7 +290,9 @@ class Oracle:
         """Streaming subsampling (step 2; "State", melTail): the first chunk of a stream uses
         the causal pads; later chunks run valid convs over [melTail || new] (14+16 -> 14 -> 6
         -> 2 frames). melTail becomes the last 14 mel frames seen."""
-        if st.pos == 0:
+        if self.cfg.frontend == 2:
+            x = subsample2d.stream(self.W, st.mel_tail, mel_new, st.pos)
+        elif st.pos == 0:
             x = self.frontend_offline(mel_new)
         else:
             x = np.concatenate([st.mel_tail, mel_new], axis=0)

@@ -5,7 +5,7 @@ inputs and injected stream states. It holds none of the encoder's arithmetic, so
 oracle under ``oracle/`` and the HIP path can both consume it without sharing any
 computation.
 """
-from .configs import (A4, C1, C2, C2Q, C3, C4, C5, CONFIGS, D1, D2, DEC_CONFIGS, MEL_CONFIGS, DecConfig,  # noqa: F401
+from .configs import (A4, C1, C2, C2Q, C3, C4, C4S, C5, CONFIGS, D1, D2, DEC_CONFIGS, MEL_CONFIGS, DecConfig,  # noqa: F401
                       EncConfig, MelConfig, get_config)
 from .gen import (  # noqa: F401
     bf16_round,

@@ -26,7 +26,8 @@ class EncConfig:
     n_emit: int = 2         # frames emitted per stream per push
     n_lookahead: int = 0    # provisional frames recomputed every pass (lookahead variant)
     joint_dim: int = 640    # 0 = no joint projection
-    frontend: bool = False  # 3 causal stride-2 convs over log-mel
+    frontend: int = 0       # 1: 3 causal stride-2 convs over log-mel; 2: the 2-D time x frequency stack
+    fe_channels: int = 256  # channels of the 2-D stack
     mel_bins: int = 128
     mel_per_chunk: int = 16
     mel_tail: int = 14
@@ -63,10 +64,13 @@ C4 = EncConfig(name="C4_eou_bf16_1024streams_frontend", seed=3, dtype="bf16", st
 C5 = EncConfig(name="C5_lookahead_bf16_512streams", seed=4, dtype="bf16", streams=512, chunks=300,
                staggered=True, att_right=3, n_emit=2, n_lookahead=8)
 
+# the 1024-stream front-end workload with the 2-D time x frequency subsampling stack
+C4S = C4.replace(name="C4S_eou_bf16_1024streams_frontend2d", frontend=2)
+
 # the one-stream encoder of C2 (same seed: same weights and inputs) with int8 dense weights
 C2Q = C2.replace(name="C2_eou_i8w_1stream", dtype="i8w")
 
-CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C2Q": C2Q}
+CONFIGS = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5, "C2Q": C2Q, "C4S": C4S}
 
 
 @dataclass(frozen=True)

@@ -82,7 +82,15 @@ def weight_names(cfg: EncConfig):
     if cfg.joint_dim:
         P = cfg.joint_dim
         specs += [("joint.w", (D, P), "mat", D), ("joint.b", (P,), "mat", D)]
-    if cfg.frontend:
+    if cfg.frontend == 2:
+        C, F8 = cfg.fe_channels, cfg.mel_bins // 8
+        specs += [("fe2.c1.w", (C, 3, 3), "mat", 9), ("fe2.c1.b", (C,), "mat", 9),
+                  ("fe2.dw2.w", (C, 3, 3), "mat", 9), ("fe2.dw2.b", (C,), "mat", 9),
+                  ("fe2.pw2.w", (C, C), "mat", C), ("fe2.pw2.b", (C,), "mat", C),
+                  ("fe2.dw3.w", (C, 3, 3), "mat", 9), ("fe2.dw3.b", (C,), "mat", 9),
+                  ("fe2.pw3.w", (C, C), "mat", C), ("fe2.pw3.b", (C,), "mat", C),
+                  ("fe2.lin.w", (C * F8, D), "mat", C * F8), ("fe2.lin.b", (D,), "mat", C * F8)]
+    elif cfg.frontend:
         C, B = D, cfg.mel_bins
         specs += [("fe.c1.w", (C, B, 3), "mat", 3 * B), ("fe.c1.b", (C,), "mat", 3 * B),
                   ("fe.c2.w", (C, C, 3), "mat", 3 * C), ("fe.c2.b", (C,), "mat", 3 * C),
