@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: 100 for C4/C3/C5, 1000 for C2)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="C4")
-    ap.add_argument("--secondary", default="C2,C2Q",
+    ap.add_argument("--secondary", default="C2,C2Q,C4S",
                     help="comma-separated workloads reported in the same line, or 'none'")
     ap.add_argument("--decode", default="D2", help="greedy-decoding workload reported in the same line, or 'none'")
     ap.add_argument("--mel", default="A4", help="streaming log-mel workload reported in the same line, or 'none'")

@@ -28,7 +28,7 @@ class cac_config(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "n_layers", "d_model", "n_heads", "d_ff", "dw_kernel", "att_left", "att_chunk", "att_right",
         "n_emit", "n_lookahead", "joint_dim", "frontend", "mel_bins", "mel_per_chunk", "mel_tail",
-        "dtype", "max_streams", "max_push_frames", "flags")]
+        "dtype", "max_streams", "max_push_frames", "flags", "fe_channels")]
 
 
 class cac_dec_config(C.Structure):
@@ -137,7 +137,12 @@ def param_order(cfg):
         out += [(p + "out.ln_g", (D,)), (p + "out.ln_b", (D,))]
     if P:
         out += [("joint.w", (D, P)), ("joint.b", (P,))]
-    if cfg.frontend:
+    if cfg.frontend == 2:
+        Cc, F8 = cfg.fe_channels, cfg.mel_bins // 8
+        out += [("fe2.c1.w", (Cc, 3, 3)), ("fe2.c1.b", (Cc,)), ("fe2.dw2.w", (Cc, 3, 3)), ("fe2.dw2.b", (Cc,)),
+                ("fe2.pw2.w", (Cc, Cc)), ("fe2.pw2.b", (Cc,)), ("fe2.dw3.w", (Cc, 3, 3)), ("fe2.dw3.b", (Cc,)),
+                ("fe2.pw3.w", (Cc, Cc)), ("fe2.pw3.b", (Cc,)), ("fe2.lin.w", (Cc * F8, D)), ("fe2.lin.b", (D,))]
+    elif cfg.frontend:
         B = cfg.mel_bins
         out += [("fe.c1.w", (D, B, 3)), ("fe.c1.b", (D,)), ("fe.c2.w", (D, D, 3)), ("fe.c2.b", (D,)),
                 ("fe.c3.w", (D, D, 3)), ("fe.c3.b", (D,))]
@@ -150,7 +155,8 @@ def make_config(cfg, max_streams=None, max_push_frames=8, flags=0) -> cac_config
     for name in ("n_layers", "d_model", "n_heads", "d_ff", "dw_kernel", "att_left", "att_chunk",
                  "att_right", "n_emit", "n_lookahead", "joint_dim", "mel_bins", "mel_per_chunk", "mel_tail"):
         setattr(c, name, int(getattr(cfg, name)))
-    c.frontend = int(bool(cfg.frontend))
+    c.frontend = int(cfg.frontend)
+    c.fe_channels = int(getattr(cfg, "fe_channels", 0)) if c.frontend == 2 else 0
     dt = str(cfg.dtype)
     c.dtype = CAC_BF16 if dt in ("bf16", "bfloat16", str(CAC_BF16)) else CAC_F32_I8 if dt in ("i8w", str(CAC_F32_I8)) else CAC_F32
     c.max_streams = int(max_streams if max_streams is not None else cfg.streams)

@@ -52,6 +52,7 @@ hipError_t scratch_ptr(float** out) {
 // ------------------------------------------------------------------------------- dimensions
 struct Dims {
   int L, D, H, hd, F, K, Kc, Lc, c, right, ne, nla, nc, P, fe, bins, mpc, tail, dt, S, npush, flags;
+  int fc;             // channels of the 2-D front end (frontend 2), else 0
   bool lookahead;
   int nfmax;          // frames per stream a call runs through the layers
   int R, Rc, Rx;      // ring depths: K/V, depthwise input, pending inputs
@@ -98,6 +99,14 @@ bool make_dims(const cac_config* c, Dims& d, std::string& why) {
     if (c->d_model % 256 || c->d_ff % 256) return bad("CAC_F32_I8 needs d_model and d_ff multiples of 256");
   }
   if (d.S < 1 || d.S > (1 << 20)) return bad("max_streams must be in [1, 2^20]");
+  d.fc = 0;
+  if (d.fe != 0 && d.fe != 1 && d.fe != 2) return bad("frontend must be 0, 1 or 2");
+  if (d.fe == 2) {
+    d.fc = c->fe_channels;
+    if (d.fc < 64 || d.fc > 512 || d.fc % 64) return bad("fe_channels must be a multiple of 64 in [64, 512]");
+    if (d.dt != CAC_BF16) return bad("the 2-D front end runs in bf16 (CAC_BF16)");
+    if (c->mel_bins % 64) return bad("the 2-D front end needs mel_bins a multiple of 64");
+  }
   if (d.fe) {
     if (d.lookahead) return bad("the front end is supported with the exact variant only");
     if (d.mpc != 16 || d.tail != 14) return bad("the front end needs mel_per_chunk 16 and mel_tail 14");
@@ -139,6 +148,8 @@ struct LayerOff {
 struct Layout {
   LayerOff lo;
   size_t layers, wj, bj, fe_w[3], fe_b[3], weights_end;
+  size_t f2_c1w, f2_c1b, f2_dw2w, f2_dw2b, f2_pw2w, f2_pw2b, f2_dw3w, f2_dw3b, f2_pw3w, f2_pw3b, f2_linw, f2_linb;
+  size_t f2_a1, f2_d2, f2_a2, f2_d3, f2_a3;
   size_t posproj, posproj_bf, kring, vring, cring, tail, x0, pos, pend;
   size_t ids, cids, cidx, sids, spos, spend, cpos, ccpos;
   size_t x, x2, y, q, h, o, e, part, win, fe1, fe2;
@@ -165,9 +176,17 @@ Layout make_layout(const Dims& d) {
   Bump w;
   t.layers = w.take(lo.size * d.L);
   if (d.P) { t.wj = w.take(d.wsz(d.P, D)); t.bj = w.take((size_t)d.P * f4); }
-  if (d.fe) {
+  if (d.fe == 1) {
     const size_t kin[3] = {(size_t)3 * d.bins, 3 * D, 3 * D};
     for (int i = 0; i < 3; ++i) { t.fe_w[i] = w.take(D * kin[i] * e); t.fe_b[i] = w.take(D * f4); }
+  } else if (d.fe == 2) {
+    const size_t C = d.fc, K8 = (size_t)d.fc * (d.bins / 8);
+    t.f2_c1w = w.take(9 * C * f4); t.f2_c1b = w.take(C * f4);
+    t.f2_dw2w = w.take(9 * C * f4); t.f2_dw2b = w.take(C * f4);
+    t.f2_pw2w = w.take(C * C * e); t.f2_pw2b = w.take(C * f4);
+    t.f2_dw3w = w.take(9 * C * f4); t.f2_dw3b = w.take(C * f4);
+    t.f2_pw3w = w.take(C * C * e); t.f2_pw3b = w.take(C * f4);
+    t.f2_linw = w.take(D * K8 * e); t.f2_linb = w.take(D * f4);
   }
   t.weights_end = w.take(0);
   const size_t S = d.S, L = d.L, M = S * d.nfmax;
@@ -187,10 +206,17 @@ Layout make_layout(const Dims& d) {
   t.h = w.take(M * F * e); t.o = w.take(M * D * e); t.e = w.take(M * D * e);
   // split-K partials of the residual products (bf16 MFMA path): up to 4 k-ranges
   if (d.dt == CAC_BF16) t.part = w.take(4 * M * D * f4);
-  if (d.fe) {
-    t.win = w.take(S * (d.tail + d.mpc) * d.bins * e);
+  if (d.fe) t.win = w.take(S * (d.tail + d.mpc) * d.bins * e);
+  if (d.fe == 1) {
     t.fe1 = w.take(S * 11 * D * e);
     t.fe2 = w.take(S * 5 * D * e);
+  } else if (d.fe == 2) {  // channels-last stage maps: 11, 5 and 2 rows of F/2, F/4 and F/8 columns
+    const size_t C = d.fc, B = d.bins;
+    t.f2_a1 = w.take(S * 11 * (B / 2) * C * e);
+    t.f2_d2 = w.take(S * 5 * (B / 4) * C * e);
+    t.f2_a2 = w.take(S * 5 * (B / 4) * C * e);
+    t.f2_d3 = w.take(S * 2 * (B / 8) * C * e);
+    t.f2_a3 = w.take(S * 2 * (B / 8) * C * e);
   }
   t.total = w.take(0);
   return t;
@@ -206,7 +232,11 @@ size_t param_count(const Dims& d) {
   per += 2 * D;                                                // out
   size_t n = per * d.L;
   if (d.P) n += D * d.P + d.P;
-  if (d.fe) n += D * d.bins * 3 + D + 2 * (D * D * 3 + D);
+  if (d.fe == 1) n += D * d.bins * 3 + D + 2 * (D * D * 3 + D);
+  if (d.fe == 2) {
+    const size_t C = d.fc;
+    n += 3 * (9 * C + C) + 2 * (C * C + C) + C * (d.bins / 8) * D + D;
+  }
   return n;
 }
 
@@ -219,7 +249,7 @@ size_t state_floats(const Dims& d) {
 // config field that defines the model and the state's meaning (all but max_streams,
 // max_push_frames and flags), taken after make_dims' normalisation.
 void state_header(const Dims& d, uint32_t out[STATE_HDR]) {
-  const int32_t f[] = {d.L, d.D, d.H, d.F, d.K, d.Lc, d.c, d.right, d.ne, d.nla, d.P, d.fe, d.bins, d.mpc, d.tail, d.dtype_cfg};
+  const int32_t f[] = {d.L, d.D, d.H, d.F, d.K, d.Lc, d.c, d.right, d.ne, d.nla, d.P, d.fe, d.bins, d.mpc, d.tail, d.dtype_cfg, d.fc};
   uint64_t h = 1469598103934665603ull;
   for (int32_t v : f)
     for (int b = 0; b < 4; ++b) {
@@ -787,7 +817,36 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
     pk.f32(lay.bj, take(d.P), d.P);
   }
   pk.wq = 0;  // the front end keeps the compute dtype
-  if (d.fe) {  // conv [out][in][tap] -> [out][tap * in + c_in] (matches a window of 3 rows)
+  if (d.fe == 2) {
+    const size_t C = d.fc, F8 = d.bins / 8;
+    auto taps = [&](size_t off) {  // [C][3][3] -> [9][C] float32
+      const float* w = take(C * 9);
+      float* dst = (float*)(wbuf.data() + off);
+      for (size_t ch = 0; ch < C; ++ch)
+        for (int tp = 0; tp < 9; ++tp) dst[tp * C + ch] = w[ch * 9 + tp];
+    };
+    taps(lay.f2_c1w); pk.f32(lay.f2_c1b, take(C), C);
+    taps(lay.f2_dw2w); pk.f32(lay.f2_dw2b, take(C), C);
+    {  // pointwise [out][in] is already [N][K]
+      const float* w = take(C * C);
+      for (size_t i = 0; i < C * C; ++i) pk.op(lay.f2_pw2w, i, w[i]);
+      pk.f32(lay.f2_pw2b, take(C), C);
+    }
+    taps(lay.f2_dw3w); pk.f32(lay.f2_dw3b, take(C), C);
+    {
+      const float* w = take(C * C);
+      for (size_t i = 0; i < C * C; ++i) pk.op(lay.f2_pw3w, i, w[i]);
+      pk.f32(lay.f2_pw3b, take(C), C);
+    }
+    {  // lin [c * F8 + f][D] -> [D][f * C + c] (the maps are channels-last)
+      const float* w = take(C * F8 * D);
+      for (size_t ch = 0; ch < C; ++ch)
+        for (size_t f = 0; f < F8; ++f)
+          for (size_t o = 0; o < D; ++o) pk.op(lay.f2_linw, o * C * F8 + f * C + ch, w[(ch * F8 + f) * D + o]);
+      pk.f32(lay.f2_linb, take(D), D);
+    }
+  }
+  if (d.fe == 1) {  // conv [out][in][tap] -> [out][tap * in + c_in] (matches a window of 3 rows)
     const size_t cin[3] = {(size_t)d.bins, D, D};
     for (int i = 0; i < 3; ++i) {
       const float* w = take(D * cin[i] * 3);
@@ -848,7 +907,44 @@ void enqueue_push(cac_ctx* c, Launcher& L, int n, const int32_t* ids, int n_fram
   if (!d.lookahead) {
     CallView cv{dids, dpos, n_frames, n, c->P<int32_t>(c->lay.cpos)};
     const int M = n * n_frames;
-    if (d.fe) {
+    if (d.fe == 2) {
+      FeWindowArgs fw{cv, d_input, c->ws + c->lay.tail, c->ws + c->lay.win, d.bins, d.tail, d.mpc};
+      launch_fe_window(L, fw, d.dt);
+      // stage 1 (11 rows: positions 8c-6 .. 8c+4 of the chunk's subsampled-by-2 grid; the first
+      // 6 lie before a fresh stream's start), then depthwise + pointwise twice (5 rows, 2 of
+      // them before the start; 2 rows), then the projection of each frame's C x F/8 map
+      const int C = d.fc, B = d.bins, wrows = d.tail + d.mpc;
+      Fe2dArgs s1{cv, c->ws + c->lay.win, c->ws + c->lay.f2_a1, c->P<float>(c->lay.f2_c1w), c->P<float>(c->lay.f2_c1b),
+                  wrows, B, 11, B / 2, C, 1, 6};
+      launch_fe2d(L, s1);
+      struct { size_t in, dw, dwb, mid, pw, pwb, out; int Tin, Fin, Tout, Fout, neg; const char* role; } st2[2] = {
+          {c->lay.f2_a1, c->lay.f2_dw2w, c->lay.f2_dw2b, c->lay.f2_d2, c->lay.f2_pw2w, c->lay.f2_pw2b, c->lay.f2_a2, 11, B / 2, 5,
+           B / 4, 2, "fe2d_pw2"},
+          {c->lay.f2_a2, c->lay.f2_dw3w, c->lay.f2_dw3b, c->lay.f2_d3, c->lay.f2_pw3w, c->lay.f2_pw3b, c->lay.f2_a3, 5, B / 4, 2,
+           B / 8, 0, "fe2d_pw3"}};
+      for (int i = 0; i < 2; ++i) {
+        Fe2dArgs dw{cv, c->ws + st2[i].in, c->ws + st2[i].mid, c->P<float>(st2[i].dw), c->P<float>(st2[i].dwb),
+                    st2[i].Tin, st2[i].Fin, st2[i].Tout, st2[i].Fout, C, 0, 0};
+        launch_fe2d(L, dw);
+        EpiArgs e{};
+        e.cv = cv; e.bias = c->P<float>(st2[i].pwb);
+        e.kind = EPI_RELU_FE; e.out = c->ws + st2[i].out; e.ldo = C;
+        e.fe_rows_per_stream = st2[i].Tout * st2[i].Fout; e.fe_neg_rows = st2[i].neg * st2[i].Fout;
+        GemmArgs g{};
+        g.M = n * st2[i].Tout * st2[i].Fout; g.N = C; g.K = C; g.A = c->ws + st2[i].mid; g.amap = RowMap{INT_MAX, 0, C};
+        g.W = c->ws + st2[i].pw; g.epi = e;
+        L.role = st2[i].role;
+        launch_gemm(L, g, d.dt, 0);
+      }
+      EpiArgs e{};
+      e.cv = cv; e.bias = c->P<float>(c->lay.f2_linb); e.kind = EPI_F32; e.out = c->ws + c->lay.x; e.ldo = d.D;
+      GemmArgs g{};
+      const int K8 = C * (B / 8);
+      g.M = n * 2; g.N = d.D; g.K = K8; g.A = c->ws + c->lay.f2_a3; g.amap = RowMap{INT_MAX, 0, K8};
+      g.W = c->ws + c->lay.f2_linw; g.epi = e;
+      L.role = "fe2d_lin";
+      launch_gemm(L, g, d.dt, 0);
+    } else if (d.fe) {
       FeWindowArgs fw{cv, d_input, c->ws + c->lay.tail, c->ws + c->lay.win, d.bins, d.tail, d.mpc};
       launch_fe_window(L, fw, d.dt);
       const int wrows = d.tail + d.mpc;

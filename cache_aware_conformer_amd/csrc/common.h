@@ -262,6 +262,19 @@ struct FeWindowArgs {   // win[s] = [tail(14) || mel_new(16)]; tail = last 14 of
   int bins, mel_tail, mel_new;
 };
 
+// 2-D front end, one 3 x 3 stride-2 stage over channels-last maps [n][Tin][Fin][C] (bf16),
+// frequency padded by one column on each side, time valid (output row r reads input rows
+// 2r .. 2r+2): stage 1 (cin1: a single input channel, the mel window [n][Tin][Fin], + ReLU,
+// rows r < neg of streams at position 0 zeroed) or depthwise (C channels, no activation).
+struct Fe2dArgs {
+  CallView cv;
+  const void* in;
+  void* out;
+  const float* w;      // [9][C] taps
+  const float* b;      // [C]
+  int Tin, Fin, Tout, Fout, C, cin1, neg;
+};
+
 struct CopyRowsArgs {    // out[row_out(m)][c] = x[amap(m) + c], row_out as in EPI_F32
   const float* x;
   RowMap amap;
@@ -408,6 +421,7 @@ void launch_input(Launcher& L, const InputArgs& a, int dtype);
 void launch_copy_rows(Launcher& L, const CopyRowsArgs& a);
 void kernels_init();
 void launch_fe_window(Launcher& L, const FeWindowArgs& a, int dtype);
+void launch_fe2d(Launcher& L, const Fe2dArgs& a);
 void launch_advance(Launcher& L, const AdvanceArgs& a);
 void launch_fill(Launcher& L, const FillArgs& a);
 void launch_posproj(Launcher& L, const PosProjArgs& a);

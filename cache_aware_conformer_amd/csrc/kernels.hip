@@ -1788,6 +1788,61 @@ void launch_fe_window(Launcher& L, const FeWindowArgs& a, int dtype) {
   L.launch(fn, dim3((total + 255) / 256), dim3(256), 0, &args);
 }
 
+// One thread per (stream, output row, output column, 8 channels): 9 taps, 16-byte stores.
+__global__ __launch_bounds__(256) void fe2d_kernel(Fe2dArgs a) {
+  const int c8 = a.C / 8;
+  long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)a.cv.n_streams * a.Tout * a.Fout * c8;
+  if (idx >= total) return;
+  const int cg = (int)(idx % c8);
+  idx /= c8;
+  const int f = (int)(idx % a.Fout);
+  idx /= a.Fout;
+  const int r = (int)(idx % a.Tout);
+  const int s = (int)(idx / a.Tout);
+  const int c0 = cg * 8;
+  float acc[8];
+  ld_f8(a.b + c0, acc);
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const int row = 2 * r + i;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int col = 2 * f + j - 1;
+      if (col < 0 || col >= a.Fin) continue;
+      float w[8];
+      ld_f8(a.w + (long)(i * 3 + j) * a.C + c0, w);
+      if (a.cin1) {
+        const float v = bf2f(((const bf16_t*)a.in)[((long)s * a.Tin + row) * a.Fin + col]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += w[q] * v;
+      } else {
+        const u32x4_v raw = *(const u32x4_v*)((const bf16_t*)a.in + (((long)s * a.Tin + row) * a.Fin + col) * a.C + c0);
+        const unsigned int u[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += w[2 * q] * __uint_as_float(u[q] << 16);
+          acc[2 * q + 1] += w[2 * q + 1] * __uint_as_float(u[q] & 0xffff0000u);
+        }
+      }
+    }
+  }
+  if (a.cin1) {
+    const bool before_start = a.cv.cpos[s] == 0 && r < a.neg;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = before_start ? 0.0f : fmaxf(acc[q], 0.0f);
+  }
+  st_bf8((bf16_t*)a.out + (((long)s * a.Tout + r) * a.Fout + f) * a.C + c0, acc);
+}
+
+void launch_fe2d(Launcher& L, const Fe2dArgs& a) {
+  Fe2dArgs args = a;
+  const long total = (long)a.cv.n_streams * a.Tout * a.Fout * (a.C / 8);
+  const double outb = (double)a.cv.n_streams * a.Tout * a.Fout * a.C * 2.0;
+  L.tag(a.cin1 ? "fe2d_conv1" : "fe2d_depthwise", 0.0, 2.0 * 9.0 * outb / 2.0);
+  L.launch((const void*)&fe2d_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
+}
+
 // =============================================================================== positions
 __global__ void advance_kernel(AdvanceArgs a) {
   const int s = blockIdx.x * 256 + threadIdx.x;

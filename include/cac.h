@@ -87,7 +87,8 @@ typedef struct {
   int32_t n_emit;        /* frames emitted per pass (lookahead variant), else frames per push */
   int32_t n_lookahead;   /* provisional frames recomputed every pass (8), 0 = exact streaming */
   int32_t joint_dim;     /* P (640); 0 = no joint projection, outputs are the hidden rows */
-  int32_t frontend;      /* 1 = inputs are log-mel chunks run through the conv front end */
+  int32_t frontend;      /* 1 = inputs are log-mel chunks run through the conv front end;
+                            2 = the same inputs through the 2-D time x frequency stack */
   int32_t mel_bins;      /* 128 */
   int32_t mel_per_chunk; /* 16 mel frames -> 2 subsampled frames */
   int32_t mel_tail;      /* 14 */
@@ -95,6 +96,8 @@ typedef struct {
   int32_t max_streams;   /* stream ids are 0 .. max_streams-1 */
   int32_t max_push_frames; /* most frames one push may carry (exact variant), <= 16 */
   int32_t flags;         /* CAC_FLAG_* */
+  int32_t fe_channels;   /* channels of the 2-D front end (frontend 2: a multiple of 64, <= 512),
+                            else ignored */
 } cac_config;
 
 /* Number of float parameters cac_create_streams expects, in this order (all float32, host):
@@ -106,8 +109,16 @@ typedef struct {
  *     ff2: ln_g[D] ln_b[D] w1[D][F] b1[F] w2[F][D] b2[D]
  *     out: ln_g[D] ln_b[D]
  *   if joint_dim: joint w[D][P] b[P]
- *   if frontend: c1 w[D][mel_bins][3] b[D]; c2 w[D][D][3] b[D]; c3 w[D][D][3] b[D]
- * Matrices are [in][out] row-major (y = x W + b); conv weights are [out][in][tap].
+ *   if frontend 1: c1 w[D][mel_bins][3] b[D]; c2 w[D][D][3] b[D]; c3 w[D][D][3] b[D]
+ *   if frontend 2 (C = fe_channels, F8 = mel_bins / 8): c1 w[C][3][3] b[C]; dw2 w[C][3][3] b[C];
+ *     pw2 w[C][C] ([out][in]) b[C]; dw3 w[C][3][3] b[C]; pw3 w[C][C] b[C];
+ *     lin w[C * F8][D] (input index c * F8 + f) b[D]
+ * Matrices are [in][out] row-major (y = x W + b); conv weights are [out][in][tap] (2-D:
+ * [out][time tap][frequency tap]).
+ * The 2-D front end (frontend 2): stage 1 is a 3 x 3 convolution from the mel map to C
+ * channels, stages 2 and 3 a depthwise 3 x 3 then a pointwise C x C convolution, each stage
+ * stride 2 in time and frequency with ReLU, causal in time exactly like the 1-D front end and
+ * padded by one column in frequency; the C x F/8 map of each frame is projected to D by lin.
  * Returns 0 for an invalid config. */
 size_t cac_param_count(const cac_config* cfg);
 

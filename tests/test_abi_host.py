@@ -11,7 +11,7 @@ import pytest
 
 import cache_aware_conformer_amd as cac
 from cache_aware_conformer_amd.binding import CAC_EINVAL, CAC_ENODEV, CAC_ENOMEM, CAC_ESTATE, CacError, cac_config
-from synth import C1, C2, C3, C4, C5, make_weights, weight_names
+from synth import C1, C2, C3, C4, C4S, C5, make_weights, weight_names
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include"))) if h.endswith(".h")]
@@ -56,7 +56,7 @@ def test_int8_weights_config_and_push_limits():
     assert push(enc, [1], 4)[0] == CAC_EINVAL
 
 
-@pytest.mark.parametrize("cfg", [C1, C2, C3, C4, C5], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [C1, C2, C3, C4, C5, C4S], ids=lambda c: c.name)
 def test_param_and_state_layouts(cfg):
     lib = cac.load()
     c = cac.make_config(cfg)

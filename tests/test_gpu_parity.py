@@ -250,6 +250,22 @@ def test_c4_bf16_1024_streams_frontend():
 
 
 @pytest.mark.slow
+def test_c4s_bf16_1024_streams_2d_front_end():
+    """Every stream of the 1024-stream workload on the 2-D time x frequency front end over 4
+    chunks."""
+    from synth import C4S
+    _check_workload(C4S, 4, range(C4S.streams))
+
+
+def test_2d_front_end_fresh_streams():
+    """Fresh streams through the 2-D front end (the rows before the stream start are zero at
+    every stage) over 6 chunks, 2 layers, one stream and five."""
+    from synth import C4S
+    for S in (1, 5):
+        _check_workload(C4S.replace(n_layers=2, streams=S, staggered=False, chunks=6), 6, range(S))
+
+
+@pytest.mark.slow
 def test_c5_bf16_lookahead_512_streams_and_flush():
     """A fixed 64-stream subset (every 8th stream) over 8 passes, then the flush of all 64."""
     _check_workload(C5, 8, range(0, C5.streams, 8), flush=True)
@@ -387,7 +403,8 @@ def test_poisoned_cache_slots_never_reach_outputs():
     reset: nothing read from a slot that does not hold a valid row reaches an output (attention
     stages whole rings and must discard such slots exactly, never as 0 * NaN)."""
     from cache_aware_conformer_amd import CAC_FLAG_POISON
-    for cfg in (C1, C4.replace(n_layers=2, streams=3, staggered=False)):
+    from synth import C4S
+    for cfg in (C1, C4.replace(n_layers=2, streams=3, staggered=False), C4S.replace(n_layers=2, streams=3, staggered=False)):
         W = make_weights(cfg)
         a = _enc(cfg, W, max_streams=3)
         b = _enc(cfg, W, max_streams=3, flags=CAC_FLAG_POISON)
