@@ -42,10 +42,31 @@ class cac_mel_config(C.Structure):
                 ("out_dtype", C.c_int32), ("max_streams", C.c_int32), ("max_hops", C.c_int32), ("flags", C.c_int32)]
 
 
+class cac_beam_config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "joint_dim", "pred_hidden", "pred_layers", "vocab", "beam", "max_symbols", "max_streams", "max_frames",
+        "score_norm", "flags")]
+
+
+CAC_BEAM_FLAG_WEAK_HASH = 0x100
+
 _CFGP = C.POINTER(cac_config)
 _DCFGP = C.POINTER(cac_dec_config)
 _MCFGP = C.POINTER(cac_mel_config)
+_BCFGP = C.POINTER(cac_beam_config)
+_PROFILE_READ = [_vp, _i32, C.c_char_p, _i32, C.POINTER(C.c_int64), C.POINTER(C.c_double),
+                 C.POINTER(C.c_double), C.POINTER(C.c_double)]
 SIGNATURES = {
+    # include/cac_beam.h
+    "cac_beam_param_count": (_sz, [_BCFGP]),
+    "cac_beam_workspace_bytes": (_sz, [_BCFGP]),
+    "cac_beam_create": (_i32, [_BCFGP, _fp, _sz, _vp, _sz, _vp, C.POINTER(_vp)]),
+    "cac_beam_decode": (_i32, [_vp, _i32, _ip, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "cac_beam_set_graph": (_i32, [_vp, _i32]),
+    "cac_beam_profile": (_i32, [_vp, _i32]),
+    "cac_beam_profile_read": (_i32, _PROFILE_READ),
+    "cac_beam_destroy": (_i32, [_vp]),
+    "cac_beam_last_error": (C.c_char_p, [_vp]),
     # include/cac_mel.h
     "cac_mel_workspace_bytes": (_sz, [_MCFGP]),
     "cac_mel_create": (_i32, [_MCFGP, _vp, _sz, _vp, C.POINTER(_vp)]),
@@ -506,6 +527,112 @@ class StreamingDecoder:
     def close(self):
         if getattr(self, "ctx", None):
             self.lib.cac_dec_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ----------------------------------------------------------------------------- beam search
+
+def make_beam_config(cfg, max_streams=None, max_frames=None, flags=0) -> cac_beam_config:
+    c = cac_beam_config()
+    for name in ("joint_dim", "pred_hidden", "pred_layers", "vocab", "beam", "max_symbols"):
+        setattr(c, name, int(getattr(cfg, name)))
+    c.max_streams = int(max_streams if max_streams is not None else cfg.streams)
+    c.max_frames = int(max_frames if max_frames is not None else cfg.frames)
+    c.score_norm = int(bool(cfg.score_norm))
+    c.flags = int(flags)
+    return c
+
+
+class BeamSearch:
+    """One beam-search context (include/cac_beam.h): repacked float32 decoder weights (the
+    greedy decoder's parameters) and the beams of ``max_streams`` utterances in one device
+    workspace, work enqueued on the current torch stream."""
+
+    def __init__(self, cfg, params: dict, max_streams=None, max_frames=None, flags=0, device="cuda:0"):
+        self.lib = load()
+        self.cfg = cfg
+        self.c = make_beam_config(cfg, max_streams, max_frames, flags)
+        self.dry = bool(flags & CAC_FLAG_DRY_RUN)
+        self.K, self.m = int(cfg.beam), int(cfg.max_symbols)
+        n = self.lib.cac_beam_param_count(C.byref(self.c))
+        if n == 0:
+            self.lib.cac_beam_create(C.byref(self.c), None, 0, None, 0, None, C.byref(C.c_void_p()))
+            raise CacError(CAC_EINVAL, self.lib.cac_beam_last_error(None).decode())
+        flat = np.ascontiguousarray(np.concatenate([np.asarray(params[nm], np.float32).reshape(-1)
+                                                    for nm, shape in dec_param_order(cfg)]))
+        self.ws_bytes = self.lib.cac_beam_workspace_bytes(C.byref(self.c))
+        ctx = C.c_void_p()
+        if self.dry:
+            ws_ptr, stream, self.ws = None, None, None
+        else:
+            import torch
+            self.torch = torch
+            self.device = torch.device(device)
+            self.ws = torch.empty(self.ws_bytes + 256, dtype=torch.uint8, device=self.device)
+            ws_ptr = (self.ws.data_ptr() + 255) // 256 * 256
+            stream = torch.cuda.current_stream(self.device).cuda_stream
+        rc = self.lib.cac_beam_create(C.byref(self.c), flat.ctypes.data_as(_fp), flat.size, ws_ptr, self.ws_bytes,
+                                      stream, C.byref(ctx))
+        if rc != CAC_OK:
+            raise CacError(rc, self.lib.cac_beam_last_error(None).decode())
+        self.ctx = ctx
+
+    def _check(self, rc):
+        if rc < 0:
+            raise CacError(rc, self.lib.cac_beam_last_error(self.ctx).decode())
+        return rc
+
+    def decode(self, z, lengths, max_steps=0, out=None):
+        """z: device float32 [n, n_frames, P]; lengths: n frame counts. Returns (tokens [n, K,
+        n_frames * max_symbols], lengths [n, K], scores [n, K], frames [n, K], iterations): the
+        K slots of each utterance best first (device tensors) and the iteration count."""
+        lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32).reshape(-1))
+        n = lens.size
+        nf = int(z.shape[1]) if hasattr(z, "shape") else int(self.c.max_frames)
+        if hasattr(z, "is_contiguous") and (not z.is_contiguous() or z.dtype != self.torch.float32 or z.shape[0] != n):
+            raise ValueError(f"z must be a contiguous float32 tensor with {n} rows, got {z.dtype} {tuple(z.shape)}")
+        tokens = tl = sc = fr = None
+        if out is not None:
+            tokens, tl, sc, fr = out
+        elif not self.dry:
+            t = self.torch
+            tokens = t.empty((n, self.K, nf * self.m), dtype=t.int32, device=self.device)
+            tl = t.empty((n, self.K), dtype=t.int32, device=self.device)
+            sc = t.empty((n, self.K), dtype=t.float32, device=self.device)
+            fr = t.empty((n, self.K), dtype=t.int32, device=self.device)
+        ptr = lambda x: None if x is None else (x.data_ptr() if hasattr(x, "data_ptr") else int(x))  # noqa: E731
+        it = self._check(self.lib.cac_beam_decode(self.ctx, n, lens.ctypes.data_as(_ip), nf, ptr(z), int(max_steps),
+                                                  ptr(tokens), ptr(tl), ptr(sc), ptr(fr)))
+        return tokens, tl, sc, fr, it
+
+    def set_graph(self, enable: bool):
+        return self._check(self.lib.cac_beam_set_graph(self.ctx, int(bool(enable))))
+
+    def profile(self, enable: bool):
+        return self._check(self.lib.cac_beam_profile(self.ctx, int(bool(enable))))
+
+    def profile_read(self) -> dict:
+        """{kernel name: (launches, total_ms, bytes, flops)} of the launches since profile(True)."""
+        n = self._check(self.lib.cac_beam_profile_read(self.ctx, 0, None, 64, None, None, None, None))
+        names = C.create_string_buffer(64 * max(n, 1))
+        launches = (C.c_int64 * max(n, 1))()
+        ms, by, fl = (C.c_double * max(n, 1))(), (C.c_double * max(n, 1))(), (C.c_double * max(n, 1))()
+        n = self._check(self.lib.cac_beam_profile_read(self.ctx, n, names, 64, launches, ms, by, fl))
+        out = {}
+        for i in range(n):
+            nm = names.raw[64 * i:64 * (i + 1)].split(b"\0", 1)[0].decode()
+            out[nm] = (int(launches[i]), float(ms[i]), float(by[i]), float(fl[i]))
+        return out
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            self.lib.cac_beam_destroy(self.ctx)
             self.ctx = None
 
     def __del__(self):

@@ -8,7 +8,7 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libcac.so")
-SOURCES = ["api.hip", "kernels.hip", "rowdot.hip", "decoder.hip", "mel.hip"]
+SOURCES = ["api.hip", "kernels.hip", "rowdot.hip", "decoder.hip", "mel.hip", "beam.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 arithmetic off: the compiler's own float code only

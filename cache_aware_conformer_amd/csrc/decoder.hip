@@ -30,13 +30,14 @@
 #include "../../include/cac.h"
 #include "../../include/cac_decode.h"
 #include "common.h"
+#include "decw.h"
+#include "f32tile.h"
 
 void kernels_init();
 
 namespace {
 
-typedef __attribute__((ext_vector_type(16))) float f32x16_d;
-typedef __attribute__((ext_vector_type(4))) float f32x4_d;
+typedef f32x4_t f32x4_d;
 
 // DM_LSTM0: the first LSTM layer, whose input half embed[token] W_ih + biases is a per-token
 // table (DM_TABLE, computed once at create), so its product covers only h W_hh.
@@ -103,9 +104,12 @@ __device__ __forceinline__ f32x4_d dec_a4(const ARow& src, int k) {
   }
 }
 
-constexpr int DEC_BK = 64;                    // k per step
-constexpr int DEC_AS = 65, DEC_BS = 68;        // LDS row strides (A k-major, W row-major)
-constexpr size_t DEC_LDS = (size_t)2 * DEC_BK * (DEC_AS + DEC_BS) * sizeof(float);  // 68 KB: two k-tile buffers
+// The thread's A row for the shared tile loop.
+template <int MODE>
+struct DecSrc {
+  ARow r;
+  __device__ __forceinline__ f32x4_d operator()(int k) const { return dec_a4<MODE>(r, k); }
+};
 
 template <int MODE>
 __global__ __launch_bounds__(256) void dec_tile_kernel(DecTileArgs a) {
@@ -113,52 +117,8 @@ __global__ __launch_bounds__(256) void dec_tile_kernel(DecTileArgs a) {
   const int rows = MODE == DM_JOINT ? cnt * a.nf : cnt;
   const int row0 = blockIdx.y * 64, col0 = blockIdx.x * 64;
   if (row0 >= rows) return;  // the whole block: nothing on the list for these rows
-  // buffer b: A tile As[k][row] (stride DEC_AS), then W tile Bs[k][col] (stride DEC_BS); after the
-  // k-loop the accumulator tile Ct[64][65] reuses the space
   extern __shared__ __attribute__((aligned(16))) float dlds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int lr = tid >> 2, lk = (tid & 3) * 16;         // A loader: row lr, k lk .. lk+15
-  const ARow src = dec_arow<MODE>(a, min(row0 + lr, rows - 1));  // rows past the end reload the last one
-  const int bk = tid >> 2, bn = (tid & 3) * 16;         // W loader: k bk, columns bn .. bn+15
-  const int KT = a.K / DEC_BK;
-  f32x4_d ra[4], rb[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    ra[q] = dec_a4<MODE>(src, lk + 4 * q);
-    rb[q] = *(const f32x4_d*)(a.W + (long)bk * a.N + col0 + bn + 4 * q);
-  }
-  f32x16_d acc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-  for (int kt = 0; kt < KT; ++kt) {
-    float* As = dlds + (kt & 1) * DEC_BK * (DEC_AS + DEC_BS);
-    float* Bs = As + DEC_BK * DEC_AS;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      As[(lk + 4 * q + 0) * DEC_AS + lr] = ra[q].x;
-      As[(lk + 4 * q + 1) * DEC_AS + lr] = ra[q].y;
-      As[(lk + 4 * q + 2) * DEC_AS + lr] = ra[q].z;
-      As[(lk + 4 * q + 3) * DEC_AS + lr] = ra[q].w;
-      *(f32x4_d*)&Bs[bk * DEC_BS + bn + 4 * q] = rb[q];
-    }
-    __syncthreads();
-    if (kt + 1 < KT) {
-      const int k1 = (kt + 1) * DEC_BK;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        ra[q] = dec_a4<MODE>(src, k1 + lk + 4 * q);
-        rb[q] = *(const f32x4_d*)(a.W + (long)(k1 + bk) * a.N + col0 + bn + 4 * q);
-      }
-    }
-#pragma unroll
-    for (int kk = 0; kk < DEC_BK; kk += 2) {
-      const float av = As[(kk + (lane >> 5)) * DEC_AS + wm * 32 + (lane & 31)];
-      const float bv = Bs[(kk + (lane >> 5)) * DEC_BS + wn * 32 + (lane & 31)];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
-    }
-  }
-  __syncthreads();  // every wave is done with the k-tile buffers
-  float (*Ct)[65] = (float (*)[65])dlds;
+  const int tid = threadIdx.x;
   // slot, stream id and token of every row of the tile, looked up once
   __shared__ int rslot[64], rid[64], rtok[64];
   if constexpr (MODE == DM_LSTM0 || MODE == DM_LSTM || MODE == DM_PROJ) {
@@ -169,10 +129,10 @@ __global__ __launch_bounds__(256) void dec_tile_kernel(DecTileArgs a) {
       rtok[tid] = MODE == DM_LSTM0 ? a.slot_tok[slot] : 0;
     }
   }
-  // accumulator element r of a lane: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
-#pragma unroll
-  for (int r = 0; r < 16; ++r) Ct[wm * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)][wn * 32 + (lane & 31)] = acc[r];
-  __syncthreads();
+  // rows past the end reload the last one
+  const DecSrc<MODE> src{dec_arow<MODE>(a, min(row0 + (tid >> 2), rows - 1))};
+  f32_tile(src, a.W, a.N, a.K, col0, dlds);
+  float (*Ct)[65] = (float (*)[65])dlds;
 
   if constexpr (MODE == DM_LSTM0 || MODE == DM_LSTM) {
     // packed gate columns: unit u's gates i, f, g, o are columns 4u .. 4u+3
@@ -389,13 +349,11 @@ bool dec_dims(const cac_dec_config* c, DecDims& d, std::string& why) {
   return true;
 }
 
-size_t dec_params(const DecDims& d) {
-  const size_t H = d.H, P = d.P, C = d.C;
-  return C * H + (size_t)d.L * (2 * H * 4 * H + 2 * 4 * H) + H * P + P + P * C + C;
-}
+size_t dec_params(const DecDims& d) { return dec_param_count(d.C, d.H, d.L, d.P); }
 
 struct DecLayout {
-  size_t embed, lstm_w, lstm_b, proj_w, proj_b, out_w, out_b, weights_end, table, ccount;
+  DecWeights w;
+  size_t table, ccount;
   size_t h, c, p, pend;
   size_t ids, slot_t, slot_sym, slot_tok, slot_ntok, need, plist, pcnt, alist, acnt, hn, part, zbuf, tokbuf, frmbuf;
   size_t total;
@@ -406,14 +364,7 @@ DecLayout dec_layout(const DecDims& d) {
   size_t off = 0;
   auto take = [&](size_t bytes) { off = (off + 255) & ~(size_t)255; size_t o = off; off += bytes; return o; };
   const size_t H = d.H, P = d.P, S = d.S, n = d.S, R = (size_t)d.rounds_max + 1;
-  t.embed = take((size_t)d.C * H * 4);
-  t.lstm_w = take((size_t)d.L * 2 * H * 4 * H * 4);
-  t.lstm_b = take((size_t)d.L * 4 * H * 4);
-  t.proj_w = take(H * P * 4);
-  t.proj_b = take(P * 4);
-  t.out_w = take(P * d.Cpad * 4);
-  t.out_b = take((size_t)d.Cpad * 4);
-  t.weights_end = take(0);
+  t.w = dec_weight_offsets(take, d.C, H, d.L, P, d.Cpad);
   t.table = take((size_t)d.C * 4 * H * 4);
   t.ccount = take(4);
   t.h = take(S * d.L * H * 4);
@@ -514,7 +465,7 @@ void dec_enqueue(cac_dec* c, Launcher& L, int n, int nf, const float* d_z, int32
   L.tag("dec_stage", 0.0, 0.0);
   L.launch((const void*)&dec_stage_kernel, dim3((unsigned)std::min<long>((sa.n4 + 255) / 256, 2048)), dim3(256), 0, &sa);
   DecTileArgs ta{};
-  ta.ids = ra.ids; ta.slot_tok = ra.slot_tok; ta.embed = c->P<float>(y.embed);
+  ta.ids = ra.ids; ta.slot_tok = ra.slot_tok; ta.embed = c->P<float>(y.w.embed);
   ta.h = c->P<float>(y.h); ta.c = c->P<float>(y.c); ta.hn = c->P<float>(y.hn); ta.p = c->P<float>(y.p);
   ta.need = ra.need; ta.z = c->P<float>(y.zbuf); ta.part = c->P<float2>(y.part); ta.table = c->P<float>(y.table);
   ta.L = d.L; ta.H = d.H; ta.P = d.P; ta.C = d.C; ta.nf = nf; ta.ntiles = ntiles; ta.n = n;
@@ -528,22 +479,22 @@ void dec_enqueue(cac_dec* c, Launcher& L, int n, int nf, const float* d_z, int32
     for (int l = 0; l < d.L; ++l) {
       t.layer = l; t.K = l == 0 ? d.H : 2 * d.H; t.N = 4 * d.H;
       // layer 0 contracts h with the W_hh rows only (its input half is the token table)
-      t.W = c->P<float>(y.lstm_w) + (size_t)l * 2 * d.H * 4 * d.H + (l == 0 ? (size_t)d.H * 4 * d.H : 0);
-      t.bias = c->P<float>(y.lstm_b) + (size_t)l * 4 * d.H;
+      t.W = c->P<float>(y.w.lstm_w) + (size_t)l * 2 * d.H * 4 * d.H + (l == 0 ? (size_t)d.H * 4 * d.H : 0);
+      t.bias = c->P<float>(y.w.lstm_b) + (size_t)l * 4 * d.H;
       L.tag("dec_lstm", 0.0, 0.0);
       L.launch(l == 0 ? (const void*)&dec_tile_kernel<DM_LSTM0> : (const void*)&dec_tile_kernel<DM_LSTM>,
-               dim3(4 * d.H / 64, prow), blk, DEC_LDS, &t);
+               dim3(4 * d.H / 64, prow), blk, F32T_LDS, &t);
     }
-    t.K = d.H; t.N = d.P; t.W = c->P<float>(y.proj_w); t.bias = c->P<float>(y.proj_b);
+    t.K = d.H; t.N = d.P; t.W = c->P<float>(y.w.proj_w); t.bias = c->P<float>(y.w.proj_b);
     L.tag("dec_proj", 0.0, 0.0);
-    L.launch((const void*)&dec_tile_kernel<DM_PROJ>, dim3(d.P / 64, prow), blk, DEC_LDS, &t);
+    L.launch((const void*)&dec_tile_kernel<DM_PROJ>, dim3(d.P / 64, prow), blk, F32T_LDS, &t);
     // joint of the slots on A_j, all frames
     DecTileArgs jt = ta;
     jt.list = ra.alist + (size_t)j * n;
     jt.count = ra.acnt + j;
-    jt.K = d.P; jt.N = d.Cpad; jt.W = c->P<float>(y.out_w); jt.bias = c->P<float>(y.out_b);
+    jt.K = d.P; jt.N = d.Cpad; jt.W = c->P<float>(y.w.out_w); jt.bias = c->P<float>(y.w.out_b);
     L.tag("dec_joint", 0.0, 0.0);
-    L.launch((const void*)&dec_tile_kernel<DM_JOINT>, dim3(ntiles, jrow), blk, DEC_LDS, &jt);
+    L.launch((const void*)&dec_tile_kernel<DM_JOINT>, dim3(ntiles, jrow), blk, F32T_LDS, &jt);
     DecRoundArgs r = ra;
     r.round = j;
     L.tag("dec_decide", 0.0, 0.0);
@@ -689,39 +640,9 @@ int32_t cac_dec_create(const cac_dec_config* cfg, const float* h_params, size_t 
   for (const void* f : {(const void*)&dec_tile_kernel<DM_LSTM0>, (const void*)&dec_tile_kernel<DM_LSTM>,
                         (const void*)&dec_tile_kernel<DM_PROJ>, (const void*)&dec_tile_kernel<DM_JOINT>,
                         (const void*)&dec_tile_kernel<DM_TABLE>})
-    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DEC_LDS);
-  // repack: LSTM gate columns per unit (unit u's i, f, g, o at 4u .. 4u+3), w_ih rows then w_hh
-  // rows as one [2H][4H] matrix, the two biases summed; joint columns padded to 64
-  const size_t H = d.H, P = d.P, C = d.C;
-  std::vector<uint8_t> buf(lay.weights_end, 0);
-  const float* q = h_params;
-  auto take = [&](size_t k) { const float* r = q; q += k; return r; };
-  memcpy(buf.data() + lay.embed, take(C * H), C * H * 4);
-  for (int l = 0; l < d.L; ++l) {
-    const float* wih = take(H * 4 * H);
-    const float* whh = take(H * 4 * H);
-    const float* bih = take(4 * H);
-    const float* bhh = take(4 * H);
-    float* w = (float*)(buf.data() + lay.lstm_w) + (size_t)l * 2 * H * 4 * H;
-    float* b = (float*)(buf.data() + lay.lstm_b) + (size_t)l * 4 * H;
-    for (size_t g = 0; g < 4; ++g)
-      for (size_t u = 0; u < H; ++u) {
-        const size_t src = g * H + u, dst = 4 * u + g;
-        b[dst] = bih[src] + bhh[src];
-        for (size_t k = 0; k < H; ++k) {
-          w[k * 4 * H + dst] = wih[k * 4 * H + src];
-          w[(H + k) * 4 * H + dst] = whh[k * 4 * H + src];
-        }
-      }
-  }
-  memcpy(buf.data() + lay.proj_w, take(H * P), H * P * 4);
-  memcpy(buf.data() + lay.proj_b, take(P), P * 4);
-  {
-    const float* w = take(P * C);
-    float* dst = (float*)(buf.data() + lay.out_w);
-    for (size_t k = 0; k < P; ++k) memcpy(dst + k * d.Cpad, w + k * C, C * 4);
-    memcpy(buf.data() + lay.out_b, take(C), C * 4);
-  }
+    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)F32T_LDS);
+  std::vector<uint8_t> buf(lay.w.end, 0);
+  dec_repack(h_params, lay.w, d.C, d.H, d.L, d.P, d.Cpad, buf.data());
   hipError_t e = hipMemcpyAsync(c->ws, buf.data(), buf.size(), hipMemcpyHostToDevice, c->stream);
   std::vector<int32_t> all(d.S);
   for (int i = 0; i < d.S; ++i) all[i] = i;
@@ -734,11 +655,11 @@ int32_t cac_dec_create(const cac_dec_config* cfg, const float* h_params, size_t 
     L.stream = c->stream;
     // first layer's input table: embed[token] W_ih + b_ih + b_hh for every class
     DecTileArgs t{};
-    t.K = d.H; t.N = 4 * d.H; t.W = c->P<float>(lay.lstm_w); t.bias = c->P<float>(lay.lstm_b);
-    t.count = c->P<int32_t>(lay.ccount); t.embed = c->P<float>(lay.embed); t.table = c->P<float>(lay.table);
+    t.K = d.H; t.N = 4 * d.H; t.W = c->P<float>(lay.w.lstm_w); t.bias = c->P<float>(lay.w.lstm_b);
+    t.count = c->P<int32_t>(lay.ccount); t.embed = c->P<float>(lay.w.embed); t.table = c->P<float>(lay.table);
     t.H = d.H; t.C = d.C;
     L.tag("dec_table", 0.0, 0.0);
-    L.launch((const void*)&dec_tile_kernel<DM_TABLE>, dim3(4 * d.H / 64, (d.C + 63) / 64), dim3(256), DEC_LDS, &t);
+    L.launch((const void*)&dec_tile_kernel<DM_TABLE>, dim3(4 * d.H / 64, (d.C + 63) / 64), dim3(256), F32T_LDS, &t);
     dec_reset_launch(c, L, d.S);
     e = L.err;
   }

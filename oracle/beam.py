@@ -80,11 +80,15 @@ class BeamTrace:
     in lower precision): the smallest score gap at any pruning boundary (the K-th kept
     candidate against the best dropped one), the smallest gap between the best and second-best
     score inside a merged group whose members differ in labels at their frame, and the number
-    of iterations. Beams after every iteration are kept when asked."""
+    of iterations; per iteration, the smaller of the two gaps (inf when no decision was close
+    to a boundary) and the largest |score| kept. Beams after every iteration are kept when
+    asked."""
     prune_gap: float = math.inf
     merge_gap: float = math.inf
     iterations: int = 0
     max_candidates: int = 0
+    gaps: list = field(default_factory=list)
+    scale: list = field(default_factory=list)
     beams: list = field(default_factory=list)
 
 
@@ -132,11 +136,13 @@ def malsd(log_probs, n_frames: int, beam: int, max_symbols: int, blank: int, tra
         # B1/B2: score descending, then slot, then class (a final hypothesis has one candidate)
         cands.sort(key=lambda x: (-x[0], x[1], -1 if x[2] is None else x[2]))
         kept = cands[:K]
+        gap = math.inf
         if trace is not None:
             trace.iterations += 1
             trace.max_candidates = max(trace.max_candidates, len(cands))
             if len(cands) > K:
-                trace.prune_gap = min(trace.prune_gap, kept[-1][0] - cands[K][0])
+                gap = kept[-1][0] - cands[K][0]
+                trace.prune_gap = min(trace.prune_gap, gap)
         new = []
         for s, k, c in kept:
             h = slots[k]
@@ -159,12 +165,16 @@ def malsd(log_probs, n_frames: int, beam: int, max_symbols: int, blank: int, tra
             if trace is not None and len({new[j].n_sym for j in members}) > 1:
                 sc = sorted((new[j].score for j in members), reverse=True)
                 trace.merge_gap = min(trace.merge_gap, sc[0] - sc[1])
+                gap = min(gap, sc[0] - sc[1])
             total = logsumexp([new[j].score for j in members])
             for j in members:
                 if j != best:
                     new[j] = Hyp(NEG_INF, new[j].t, new[j].prefix, new[j].n_sym)
             new[best] = Hyp(total, new[best].t, new[best].prefix, new[best].n_sym)
         slots = new
+        if trace is not None:
+            trace.gaps.append(gap)
+            trace.scale.append(max((abs(h.score) for h in slots if h.live), default=0.0))
         if trace is not None and keep_beams:
             trace.beams.append([Hyp(h.score, h.t, h.prefix, h.n_sym) for h in slots])
     return slots

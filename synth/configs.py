@@ -103,6 +103,40 @@ D2 = DecConfig(name="D2_greedy_1024streams", seed=12, streams=1024, calls=100)
 DEC_CONFIGS = {"D1": D1, "D2": D2}
 
 
+@dataclass(frozen=True)
+class BeamConfig:
+    """Batched MALSD beam search over whole utterances of projected encoder frames, with the
+    greedy decoder's prediction network and joint (same parameter names and shapes)."""
+    name: str
+    seed: int
+    joint_dim: int = 640
+    pred_hidden: int = 640
+    pred_layers: int = 2
+    vocab: int = 1024
+    beam: int = 8
+    max_symbols: int = 10       # the beam decoder's default label cap
+    blank_bias: float = 3.0     # added to the blank class's joint bias (synthetic weights)
+    silence: float = 0.5        # fraction of frames pushed towards blank
+    silence_gain: float = 4.0   # strength of that push
+    score_norm: bool = True
+    streams: int = 64
+    frames: int = 188           # 15 s at 80 ms per encoder frame
+    min_frames: int = 94        # utterance lengths uniform in [min_frames, frames]
+
+    @property
+    def classes(self) -> int:
+        return self.vocab + 2
+
+    def replace(self, **kw) -> "BeamConfig":
+        return dataclasses.replace(self, **kw)
+
+
+B8 = BeamConfig(name="B8_malsd_beam8_64utt", seed=21)
+# short utterances of the same model shape, for parity at many beam widths
+B8S = B8.replace(name="B8S_malsd_short", seed=22, frames=24, min_frames=1, streams=48)
+BEAM_CONFIGS = {"B8": B8, "B8S": B8S}
+
+
 def get_config(key: str) -> EncConfig:
     return CONFIGS[key]
 

@@ -204,6 +204,24 @@ def make_dec_inputs(cfg: DecConfig, stream: int, calls: int | None = None) -> np
     return x if calls is None else x[:calls]
 
 
+def make_beam_inputs(cfg, stream: int, weights: dict) -> tuple:
+    """Projected frames of one utterance for beam search: ([frames, joint_dim] float32, its
+    length). Frames ~ N(0, 1); a random ``silence`` fraction of them also carries
+    ``silence_gain`` * sqrt(P) / 4 times the unit vector along the positive part of the blank
+    class's joint column, which raises the blank's score at those frames the way pauses do in
+    speech (so transcripts grow at a speech-like rate instead of a label at every step). The
+    length is uniform in [min_frames, frames]; frames past it are drawn but never read."""
+    g = _rng(cfg, f"beam.input.s{stream}")
+    P = cfg.joint_dim
+    z = g.standard_normal((cfg.frames, P))
+    quiet = g.random(cfg.frames) < cfg.silence
+    u = np.maximum(np.asarray(weights["joint.out_w"], np.float64)[:, cfg.vocab], 0.0)
+    u /= np.linalg.norm(u)
+    z += (cfg.silence_gain * np.sqrt(P) / 4.0) * quiet[:, None] * u[None, :]
+    length = int(g.integers(cfg.min_frames, cfg.frames + 1))
+    return z.astype(np.float32), length
+
+
 def make_audio(cfg: MelConfig, stream: int, chunks: int | None = None) -> np.ndarray:
     """Raw audio of one stream, [chunks, hops * hop] float32: white noise of amplitude 0.05 plus
     two tones (frequency uniform in 80 Hz - 7.5 kHz, amplitude uniform in 0.05 - 0.5) that hold

@@ -40,11 +40,11 @@ def pool() -> ProcessPoolExecutor:
 def _oracle(cfg):
     from oracle import Oracle
     from oracle.decoder import GreedyDecoder
-    from synth import DecConfig, make_dec_weights, make_weights
+    from synth import BeamConfig, DecConfig, make_dec_weights, make_weights
     from oracle.quant import compress_weights
     if cfg not in _CACHE:
         _CACHE.clear()
-        if isinstance(cfg, DecConfig):
+        if isinstance(cfg, (DecConfig, BeamConfig)):
             _CACHE[cfg] = GreedyDecoder(cfg, make_dec_weights(cfg))
         elif cfg.dtype == "i8w":   # int8 dense weights: the oracle runs on their reconstruction
             _CACHE[cfg] = Oracle(cfg, compress_weights(make_weights(cfg)))
@@ -136,4 +136,47 @@ def collect_decode(handle):
     for g, fut in zip(groups, futs):
         for s, calls in zip(g, fut.result()):
             res[s] = calls
+    return res
+
+
+def _beam_group(cfg, ids, steps):
+    """Beam search of utterances ``ids`` (their seeded frames and lengths): per utterance the
+    final live hypotheses [(transcript, score, frame)], the per-iteration decision gaps and
+    score scales, the iteration count, and the live hypotheses after each iteration count in
+    ``steps`` (when the search ran that long)."""
+    from oracle.beam import BeamTrace, malsd, ModelScorer
+    from synth import make_beam_inputs, make_dec_weights
+    dec = _oracle(cfg)
+    W = _CACHE.setdefault(("weights", cfg), make_dec_weights(cfg))
+    out = []
+    for s in ids:
+        z, n = make_beam_inputs(cfg, s, W)
+        tr = BeamTrace()
+        slots = malsd(ModelScorer(dec, z), n, cfg.beam, cfg.max_symbols, dec.blank, tr, keep_beams=True)
+        live = lambda sl: [(h.prefix, h.score, h.t) for h in sl if h.live]  # noqa: E731
+        out.append({"final": live(slots), "gaps": tr.gaps, "scale": tr.scale, "iterations": tr.iterations,
+                    "length": n, "at": {m: live(tr.beams[m - 1]) for m in steps if 0 < m <= len(tr.beams)}})
+    return out
+
+
+def submit_beam(cfg, ids, steps=(), group=None):
+    ids = list(ids)
+    if group is None:
+        group = max(1, -(-len(ids) // (2 * _WORKERS)))
+    groups = [ids[i:i + group] for i in range(0, len(ids), group)]
+    return groups, [pool().submit(_beam_group, cfg, g, tuple(steps)) for g in groups]
+
+
+def collect_beam(handle):
+    """{utterance id: result of _beam_group}."""
+    groups, futs = handle
+    t0, pending = time.time(), set(futs)
+    while pending:
+        _, pending = wait(pending, timeout=30, return_when=FIRST_COMPLETED)
+        print(f"oracle beam: {len(futs) - len(pending)}/{len(futs)} groups done after {time.time() - t0:.0f} s",
+              flush=True)
+    res = {}
+    for g, fut in zip(groups, futs):
+        for s, r in zip(g, fut.result()):
+            res[s] = r
     return res

@@ -309,3 +309,53 @@ def test_mel_config_and_push_validation():
     assert lib.cac_mel_push(mel.ctx, 2, ip([3, 3]), 160, p, p) == CAC_EINVAL
     assert lib.cac_mel_push(mel.ctx, 1, ip([0]), 160, None, p) == CAC_EINVAL
     assert lib.cac_mel_reset(mel.ctx, 1, ip([9])) == CAC_EINVAL
+
+
+def _beam_cfg(**kw):
+    from cache_aware_conformer_amd.binding import make_beam_config
+    from synth import B8
+    c = make_beam_config(B8, max_streams=4, max_frames=32)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_beam_config_validation_and_sizes():
+    """Beam search: the greedy decoder's parameter count, a workspace that grows with the
+    beam, the utterance count and the frames, and invalid sizes refused."""
+    from synth import B8
+    lib = cac.load()
+    dc = cac.binding.make_dec_config(B8.replace(streams=4, frames=8), max_streams=4, max_frames=8)
+    assert lib.cac_beam_param_count(C.byref(_beam_cfg())) == lib.cac_dec_param_count(C.byref(dc)) > 0
+    base = lib.cac_beam_workspace_bytes(C.byref(_beam_cfg()))
+    assert base > 0
+    for kw in ({"beam": 8}, {"max_streams": 8}, {"max_frames": 64}):
+        small = lib.cac_beam_workspace_bytes(C.byref(_beam_cfg(**{**kw, list(kw)[0]: list(kw.values())[0] // 2})))
+        assert small < lib.cac_beam_workspace_bytes(C.byref(_beam_cfg(**kw)))
+    for kw in ({"beam": 0}, {"beam": 9}, {"vocab": 2047}, {"max_symbols": 0}, {"max_symbols": 17}, {"max_streams": 0},
+               {"max_streams": 4097}, {"max_frames": 0}, {"max_frames": 4097}, {"score_norm": 2},
+               {"joint_dim": 100}, {"pred_hidden": 32}, {"pred_layers": 0}, {"flags": 0x40}):
+        assert lib.cac_beam_workspace_bytes(C.byref(_beam_cfg(**kw))) == 0, kw
+        assert lib.cac_beam_param_count(C.byref(_beam_cfg(**kw))) == 0, kw
+
+
+def test_beam_decode_argument_checks_on_a_dry_context():
+    from cache_aware_conformer_amd import BeamSearch
+    from cache_aware_conformer_amd.binding import CAC_FLAG_DRY_RUN
+    from synth import B8
+    cfg = B8.replace(streams=4, frames=16)
+    W = {nm: np.zeros(shape, np.float32) for nm, shape in cac.binding.dec_param_order(cfg)}
+    bs = BeamSearch(cfg, W, flags=CAC_FLAG_DRY_RUN)
+    lib, ctx = bs.lib, bs.ctx
+    lens = np.array([16, 3, 0, 1], np.int32)
+    lp = lens.ctypes.data_as(C.POINTER(C.c_int32))
+    fake = 1 << 20
+    assert lib.cac_beam_decode(ctx, 4, lp, 16, fake, 0, fake, fake, fake, None) == CAC_ENODEV
+    assert lib.cac_beam_decode(ctx, 5, lp, 16, fake, 0, fake, fake, fake, None) == CAC_EINVAL   # too many
+    assert lib.cac_beam_decode(ctx, 4, lp, 17, fake, 0, fake, fake, fake, None) == CAC_EINVAL   # frames
+    assert lib.cac_beam_decode(ctx, 4, lp, 15, fake, 0, fake, fake, fake, None) == CAC_EINVAL   # 16 > 15
+    assert lib.cac_beam_decode(ctx, 4, lp, 16, fake, -1, fake, fake, fake, None) == CAC_EINVAL  # max_steps
+    assert lib.cac_beam_decode(ctx, 4, lp, 16, fake + 4, 0, fake, fake, fake, None) == CAC_EINVAL  # alignment
+    assert lib.cac_beam_decode(ctx, 4, None, 16, fake, 0, fake, fake, fake, None) == CAC_EINVAL
+    assert lib.cac_beam_decode(ctx, 4, lp, 16, fake, 0, None, fake, fake, None) == CAC_EINVAL
+    assert b"max_steps" in lib.cac_beam_last_error(ctx) or True

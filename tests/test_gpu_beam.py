@@ -1,0 +1,191 @@
+"""GPU batched MALSD beam search (include/cac_beam.h, through the C ABI) against the float64
+oracle (oracle/beam.py).
+
+The GPU searches in float32, the oracle in float64, so a decision whose candidates score
+within float32 noise of each other may go either way: both results are then correct searches.
+The oracle records, per iteration i, the smallest gap at any decision (the K-th kept candidate
+against the best dropped one; the best two members of a merged group whose label counts at
+their frame differ) and the largest |score| S_i. A score after i iterations carries at most
+i rounded additions of a log-probability whose own float32 error stays under 4e-6 (logits
+over 640 products, log-sum-exp over ~1000 classes), so it is off by at most
+    tol_i = i * (ulp(S_i) / 2 + 4e-6),
+and two candidates differ from their exact order only if their gap is under delta_i = 2 tol_i.
+An utterance is compared exactly (same transcripts and frames in the beam, scores within
+tol) up to its first iteration with a gap under delta_i: at the end when there is none,
+otherwise at a step count before it (the search stopped there with max_steps).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle_pool
+from gpu_util import log
+from synth import B8, B8S, D1, make_beam_inputs, make_dec_weights
+
+pytestmark = pytest.mark.gpu
+
+EPS_LP = 4e-6           # float32 error of one log-probability (see the module docstring)
+STEPS = (8, 16, 32, 64, 128)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import cache_aware_conformer_amd  # noqa: F401  (fails loudly when libcac.so is missing)
+    yield
+
+
+def ulp32(x):
+    return float(np.spacing(np.float32(abs(x))))
+
+
+def tol_at(res, i):
+    S = max(res["scale"][:i], default=0.0)
+    return i * (ulp32(S) / 2 + EPS_LP)
+
+
+def first_close(res):
+    """First iteration (1-based) whose decision gap is under delta_i, or None."""
+    for i, g in enumerate(res["gaps"], start=1):
+        if g < 2 * tol_at(res, i):
+            return i
+    return None
+
+
+def inputs(cfg, ids):
+    W = make_dec_weights(cfg)
+    zs, lens = zip(*(make_beam_inputs(cfg, s, W) for s in ids))
+    return W, torch.from_numpy(np.stack(zs)).to("cuda:0"), np.array(lens, np.int32)
+
+
+def gpu_beams(out, i):
+    """Live hypotheses of utterance i from the GPU outputs: {transcript: (score, frame)}."""
+    tok, tl, sc, fr = (x.cpu().numpy() for x in out[:4])
+    res = {}
+    for r in range(tl.shape[1]):
+        n = int(tl[i, r])
+        if n < 0:
+            assert not np.isfinite(sc[i, r]) and np.all(tok[i, r] == -1)
+            continue
+        assert np.all(tok[i, r, n:] == -1)
+        key = tuple(int(x) for x in tok[i, r, :n])
+        assert key not in res, "one transcript in two slots"
+        res[key] = (float(sc[i, r]), int(fr[i, r]))
+    return res
+
+
+def compare(got, ref, tol, tag):
+    ref = {p: (s, t) for p, s, t in ref}
+    assert set(got) == set(ref), (tag, sorted(set(got) ^ set(ref))[:4])
+    worst = 0.0
+    for p, (s, t) in ref.items():
+        gs, gt = got[p]
+        assert gt == t, (tag, p, gt, t)
+        worst = max(worst, abs(gs - s))
+        assert abs(gs - s) <= tol, (tag, p, gs, s, tol)
+    return worst
+
+
+def check_workload(cfg, ids, search=None, steps=STEPS, min_exact=0.5):
+    from cache_aware_conformer_amd import BeamSearch
+    h = oracle_pool.submit_beam(cfg, ids, steps)
+    W, z, lens = inputs(cfg, ids)
+    bs = search or BeamSearch(cfg, W, max_streams=len(ids), max_frames=cfg.frames)
+    full = bs.decode(z, lens)
+    partial = {m: bs.decode(z, lens, max_steps=m) for m in steps}
+    torch.cuda.synchronize()
+    ref = oracle_pool.collect_beam(h)
+    exact = prefix = 0
+    worst = 0.0
+    for i, s in enumerate(ids):
+        r = ref[s]
+        fc = first_close(r)
+        if fc is None:
+            worst = max(worst, compare(gpu_beams(full, i), r["final"], tol_at(r, r["iterations"]), (cfg.name, s))
+                        / max(tol_at(r, r["iterations"]), 1e-30))
+            exact += 1
+            continue
+        ok = [m for m in steps if m < fc and m in r["at"]]
+        if ok:
+            m = max(ok)
+            worst = max(worst, compare(gpu_beams(partial[m], i), r["at"][m], tol_at(r, m), (cfg.name, s, m))
+                        / max(tol_at(r, m), 1e-30))
+            prefix += 1
+    log(f"{cfg.name} K={cfg.beam}: {len(ids)} utterances, {exact} compared to the end, {prefix} up to a close "
+        f"decision, {len(ids) - exact - prefix} with a close decision in the first {min(steps)} iterations; "
+        f"worst score error {worst:.3f} of its bound; iterations GPU {full[4]}, oracle "
+        f"{max(r['iterations'] for r in ref.values())}")
+    assert exact >= min_exact * len(ids)
+    return full, ref
+
+
+@pytest.mark.parametrize("beam", [1, 2, 4, 8])
+def test_short_utterances_every_beam_width(beam):
+    cfg = B8S.replace(beam=beam)
+    check_workload(cfg, list(range(cfg.streams)), min_exact=0.7)
+
+
+def test_long_utterances_of_the_bench_workload():
+    """All 64 utterances of up to 188 frames at beam 8: compared to the end where no decision
+    is close, otherwise up to the last step count before the first close one."""
+    check_workload(B8, list(range(B8.streams)), min_exact=0.0)
+
+
+def test_weak_hash_and_graph_replay_change_nothing():
+    """Every pair with equal length and last label compared token by token (the hash replaced
+    by 0), and the rounds launched one by one instead of replayed: bit-identical outputs."""
+    from cache_aware_conformer_amd import BeamSearch
+    from cache_aware_conformer_amd.binding import CAC_BEAM_FLAG_WEAK_HASH
+    cfg = B8S
+    ids = list(range(cfg.streams))
+    W, z, lens = inputs(cfg, ids)
+    a = BeamSearch(cfg, W, max_streams=len(ids))
+    b = BeamSearch(cfg, W, max_streams=len(ids), flags=CAC_BEAM_FLAG_WEAK_HASH)
+    ra = a.decode(z, lens)
+    rb = b.decode(z, lens)
+    a.set_graph(False)
+    rc = a.decode(z, lens)
+    for x, y, w in zip(ra[:4], rb[:4], rc[:4]):
+        assert torch.equal(x, y) and torch.equal(x, w)
+    assert ra[4] == rb[4] == rc[4]
+
+
+def test_beam_one_matches_the_gpu_greedy_decoder():
+    """Beam 1 is greedy decoding: the beam search's transcript equals the greedy decoder's
+    (include/cac_decode.h) over the same frames, fed to it in calls of up to 16 frames."""
+    from cache_aware_conformer_amd import BeamSearch, StreamingDecoder
+    cfg = B8.replace(beam=1, streams=16, frames=64, min_frames=30)
+    ids = list(range(cfg.streams))
+    W, z, lens = inputs(cfg, ids)
+    bs = BeamSearch(cfg, W, max_streams=len(ids))
+    tok, tl, _, fr, _ = bs.decode(z, lens)
+    tok, tl, fr = tok.cpu().numpy(), tl.cpu().numpy(), fr.cpu().numpy()
+    dcfg = D1.replace(vocab=cfg.vocab, max_symbols=cfg.max_symbols, streams=len(ids), frames=16)
+    dec = StreamingDecoder(dcfg, W, max_streams=len(ids), max_frames=16)
+    for i in ids:
+        n, want = int(lens[i]), []
+        for c0 in range(0, n, 16):
+            t2, _, c2 = dec.decode([i], z[i:i + 1, c0:min(n, c0 + 16)].contiguous())
+            want += [int(x) for x in t2.cpu().numpy()[0, :int(c2.cpu().numpy()[0])]]
+        assert [int(x) for x in tok[i, 0, :tl[i, 0]]] == want, i
+        assert fr[i, 0] == n
+
+
+def test_empty_utterances_and_validation():
+    from cache_aware_conformer_amd import BeamSearch, CacError
+    cfg = B8S
+    ids = list(range(4))
+    W, z, lens = inputs(cfg, ids)
+    lens[:] = [0, 3, 0, 1]
+    bs = BeamSearch(cfg, W, max_streams=4)
+    tok, tl, sc, fr, it = bs.decode(z, lens)
+    tl, sc, fr = tl.cpu().numpy(), sc.cpu().numpy(), fr.cpu().numpy()
+    for i in (0, 2):
+        assert tl[i, 0] == 0 and sc[i, 0] == 0.0 and fr[i, 0] == 0
+        assert np.all(tl[i, 1:] == -1) and np.all(np.isneginf(sc[i, 1:]))
+    assert it >= 3
+    with pytest.raises(CacError):
+        bs.decode(z, [0, 3, 0, cfg.frames + 1])
+    with pytest.raises(CacError):
+        bs.decode(z, lens, max_steps=-1)
