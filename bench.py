@@ -5,8 +5,9 @@ A step is one push of one chunk for every stream of the workload through the who
 workload is the largest one-GPU configuration: 1024 streams at staggered positions, each
 pushing 16 log-mel frames through the front end and the 17-layer d=512 encoder in bf16 (fp32
 accumulate). The one-stream float32 encoder (the weight-bandwidth-bound case) and greedy
-RNNT + EOU decoding of 1024 streams are measured in the same run and reported in the same JSON
-line under "secondary". Prints one JSON line.
+RNNT + EOU decoding of 1024 streams, the streaming log-mel front, and batched beam search over
+64 utterances are measured in the same run and reported in the same JSON line under
+"secondary". Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload C4|C2|C3|C5] [--secondary C2|none]
 """
@@ -41,6 +42,7 @@ def parse():
                     help="comma-separated workloads reported in the same line, or 'none'")
     ap.add_argument("--decode", default="D2", help="greedy-decoding workload reported in the same line, or 'none'")
     ap.add_argument("--mel", default="A4", help="streaming log-mel workload reported in the same line, or 'none'")
+    ap.add_argument("--beam", default="B8", help="beam-search workload reported in the same line, or 'none'")
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--cpu-seconds", type=float, default=8.0, help="oracle time per CPU-baseline mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -322,6 +324,67 @@ def run_decode(key: str, steps, warmup: int, profile_steps: int):
     return res
 
 
+def run_beam(key: str, steps, warmup: int):
+    """Batched MALSD beam search: one call decodes every utterance of the workload (frames
+    resident in HBM) to its K best transcripts; the call returns once the search has ended."""
+    import torch
+
+    from cache_aware_conformer_amd import BeamSearch
+    from synth import BEAM_CONFIGS, make_beam_inputs, make_dec_weights
+
+    cfg = BEAM_CONFIGS[key]
+    steps = steps if steps is not None else 10
+    steps = min(steps, 20)
+    n = cfg.streams
+    dev = torch.device("cuda:0")
+    W = make_dec_weights(cfg)
+    zs, lens = zip(*(make_beam_inputs(cfg, s, W) for s in range(n)))
+    z = torch.from_numpy(np.stack(zs)).to(dev)
+    lens = np.array(lens, np.int32)
+    bs = BeamSearch(cfg, W, max_streams=n, max_frames=cfg.frames)
+    out = bs.decode(z, lens)
+    iters = out[4]
+    for _ in range(warmup):
+        bs.decode(z, lens, out=out[:4])
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        bs.decode(z, lens, out=out[:4])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    bs.profile(True)
+    bs.decode(z, lens, out=out[:4])
+    torch.cuda.synchronize()
+    prof = bs.profile_read()
+    bs.profile(False)
+    busy = {k: v for k, v in prof.items() if not k.endswith("/idle") and v[3] > 0}
+    dom = max(busy, key=lambda k: busy[k][1])
+    launches, tms, by, fl = busy[dom]
+    us = tms / launches * 1e3
+    roof = {"bound": "mfma", "achieved": fl / launches / (us * 1e-6) / 1e12, "peak": FP32_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "traffic": None, "kernel": dom, "avg_launch_us": us,
+            "launches_per_step": launches, "algorithmic_flops_per_launch": fl / launches,
+            "algorithmic_bytes_per_launch": by / launches,
+            "timing": "per-launch HIP events bound to each dispatch (include the event markers)"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    tl = out[1].cpu().numpy()
+    res = {"value": float(lens.sum()) * steps / (ms / 1e3), "unit": "frames/s", "ms_per_step": ms / steps,
+           "utterances_per_s": n * steps / (ms / 1e3), "steps": steps, "dtype": "f32",
+           "iterations_per_call": iters, "best_transcript_tokens_mean": float(tl[:, 0].mean()),
+           "config": {"workload": cfg.name, "utterances": n, "frames_max": cfg.frames,
+                      "frames_total": int(lens.sum()), "beam": cfg.beam, "max_symbols": cfg.max_symbols,
+                      "pred_layers": cfg.pred_layers, "pred_hidden": cfg.pred_hidden, "joint_dim": cfg.joint_dim,
+                      "classes": cfg.classes},
+           "roofline": roof,
+           "kernels": {k: {"launches_per_step": v[0], "us_per_step": v[1] * 1e3}
+                       for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}}
+    bs.close()
+    return res
+
+
 FP64_VECTOR_PEAK_TFLOPS = 78.6
 
 
@@ -418,6 +481,9 @@ def main():
     if args.decode and args.decode.lower() != "none":
         dres = run_decode(args.decode, args.steps, args.warmup, args.profile_steps)
         res.setdefault("secondary", {})[dres["config"]["workload"]] = dres
+    if args.beam and args.beam.lower() != "none":
+        bres = run_beam(args.beam, None, min(args.warmup, 3))
+        res.setdefault("secondary", {})[bres["config"]["workload"]] = bres
     print(json.dumps(res))
 
 

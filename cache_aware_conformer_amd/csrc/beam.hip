@@ -1,8 +1,8 @@
 // Batched MALSD beam search (include/cac_beam.h): K hypotheses per utterance, float32.
 //
-// Device state per utterance b: two copies (by parity) of its K slots (score, frame, labels at
-// the frame, transcript length, last label, transcript hash, predictor state entry) and of
-// their transcripts; cur[b] names the live copy. Predictor states live in a pool: entry 0 is
+// Device state per utterance b: two copies of its K slots (score, frame, labels at the frame,
+// transcript length, last label, transcript hash, predictor state entry), the live one by the
+// parity of the round, and two copies of their transcripts, tcur[b] naming the live one. Predictor states live in a pool: entry 0 is
 // the zero state, entry 1 the state after the start symbol, and utterance b owns 2K entries
 // after those. A new label's state goes into an entry that no slot of the old beam refers to,
 // so the parents' entries are never overwritten while they are read; blank shares its
@@ -11,12 +11,16 @@
 // One iteration ("round") is five kernels:
 //   joint   - rows of the joint list (live hypotheses with frames left): ReLU(z[b][t] + p) Wout
 //             + bout into a logits row per slot (MFMA tiles, the predictor/joint tile loop);
-//   select  - one block per utterance with work: log_softmax and top-K per hypothesis, forced
-//             blank, final hypotheses, global top-K, new slots and transcripts, recombination,
-//             predictor entries for new labels, the next joint list; flips cur[b];
+//   select  - one block per utterance: log_softmax and top-K per hypothesis, forced blank,
+//             final hypotheses, global top-K, new slots and transcripts, recombination,
+//             predictor entries for new labels, the next joint list (each entry the frame row,
+//             predictor entry and logits row it needs, so the joint reads no beam state);
+//             an utterance without work copies its slots to the next parity;
 //   lstm x L, proj - the predictor for the new labels (MFMA tiles).
 // The host runs rounds in groups (a recorded graph per group) and reads the next joint list's
-// length between groups: zero means no hypothesis has frames left.
+// length between groups: zero means no hypothesis has frames left. Every kernel loads its list
+// length and its list entries together, so each launch waits for one round trip before it
+// reads its operands.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -57,15 +61,14 @@ enum BeamMode { BM_LSTM0 = 0, BM_LSTM = 1, BM_PROJ = 2, BM_JOINT = 3, BM_TABLE =
 
 struct BeamTileArgs {
   int K, N;                  // contraction length, output columns (multiple of 64)
-  const float* W;            // [K][N]
+  const float* W;            // [N][ldw]: output column n's K weights at W + n * ldw
+  int ldw;
   const float* bias;         // [N]
   const int32_t* count;      // rows on the list
   const int32_t* psrc;       // predictor list: parent's state entry
   const int32_t* pdst;       // predictor list: new entry
   const int32_t* ptok;       // predictor list: label
-  const int32_t* jlist;      // joint list: b * beam + k
-  const int32_t* cur;        // [n] live copy of each utterance's beam
-  const BeamSlot* slots;     // [2][n][beam]
+  const int4* jlist;         // joint list: (frame row b * T + t, predictor entry, logits row b * beam + k)
   const float* zbuf;         // [n][T][P]
   float* logits;             // [n * beam][Cpad]
   float* ph;                 // pool [E][L][H]
@@ -78,6 +81,7 @@ struct BeamTileArgs {
   int32_t* rnow;             // joint only: rounds started in this call (advanced by one)
   int32_t* log;              // [rounds][2] rows seen by the joint / the first LSTM layer (profiling)
   int layer, L, H, P, C, T, n, beam, round;
+  int gx;                    // column tiles (the grid holds 8 * ceil(gx / 8) per row tile)
 };
 
 __device__ __forceinline__ float bsigm(float x) { return 1.0f / (1.0f + expf(-x)); }
@@ -102,11 +106,19 @@ struct BeamSrc {
   }
 };
 
+// 32 x 32 output tiles (rows of the work list x output columns), each computed by a block's
+// BEAM_TW waves splitting the contraction (f32_tile32), then the mode's epilogue. The grid is
+// 1-D and bounded; blocks loop over the tiles of the rows the list holds, so a short list costs
+// no idle blocks. Tile t runs on XCD t mod 8 (its block's), and each XCD takes a contiguous
+// eighth of the column tiles for every row tile, so each weight row is fetched into one XCD's
+// L2 only.
+constexpr int BEAM_TW = 4;
+
 template <int MODE>
-__global__ __launch_bounds__(256) void beam_tile_kernel(BeamTileArgs a) {
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(64 * BEAM_TW) void beam_tile_kernel(BeamTileArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
   if constexpr (MODE == BM_JOINT) {
-    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+    if (blockIdx.x == 0 && tid == 0) {
       *a.clr0 = 0;
       *a.clr1 = 0;
       *a.rnow += 1;
@@ -114,109 +126,115 @@ __global__ __launch_bounds__(256) void beam_tile_kernel(BeamTileArgs a) {
     }
   }
   if constexpr (MODE == BM_LSTM0) {
-    if (a.log && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) a.log[2 * a.round + 1] = *a.count;
+    if (a.log && blockIdx.x == 0 && tid == 0) a.log[2 * a.round + 1] = *a.count;
   }
+  const int per = (a.gx + 7) >> 3;
   const int rows = *a.count;
-  const int row0 = blockIdx.y * 64, col0 = blockIdx.x * 64;
-  if (row0 >= rows) return;
-  extern __shared__ __attribute__((aligned(16))) float blds[];
-  __shared__ int rsrc[64], rdst[64], rtok[64];
+  __shared__ __attribute__((aligned(16))) float red[BEAM_TW * 32 * 33];
+  __shared__ int rsrc[32], rdst[32], rtok[32];
   const int L = a.L, H = a.H;
-  if (tid < 64) {
-    const int r = min(row0 + tid, rows - 1);
+  // tiles t = blockIdx.x, + gridDim.x, ... (gridDim.x a multiple of 8, so all of a block's
+  // tiles belong to its XCD's column eighth); the row tile grows with t
+  for (int t = blockIdx.x;; t += gridDim.x) {
+    const int xcd = t & 7, j = t >> 3;
+    const int cx = xcd * per + j % per, ry = j / per;
+    const int row0 = ry * 32, col0 = cx * 32;
+    if (row0 >= rows) break;
+    if (cx >= a.gx) continue;
+    // this lane's list entry (rows past the length take the list's first row)
+    const int r = row0 + (lane & 31);
+    const int rr0 = r < rows ? r : 0;
+    int4 je = make_int4(0, 0, 0, 0);
+    int ps = 0, pd = 0, pt = 0;
+    if constexpr (MODE == BM_JOINT) je = a.jlist[rr0];
+    else if constexpr (MODE != BM_TABLE) { ps = a.psrc[rr0]; pd = a.pdst[rr0]; pt = a.ptok[rr0]; }
+    __syncthreads();   // the previous tile's epilogue is done with the row info
+    if (tid < 32) {
+      if constexpr (MODE == BM_JOINT) rdst[tid] = je.z;
+      else { rsrc[tid] = ps; rdst[tid] = pd; rtok[tid] = pt; }
+    }
+    BeamSrc<MODE> src{nullptr, nullptr, 0};
     if constexpr (MODE == BM_JOINT) {
-      rdst[tid] = a.jlist[r];
-    } else if constexpr (MODE != BM_TABLE) {
-      rsrc[tid] = a.psrc[r];
-      rdst[tid] = a.pdst[r];
-      rtok[tid] = a.ptok[r];
+      src.s0 = a.zbuf + (long)je.x * a.P;
+      src.s1 = a.pp + (long)je.y * a.P;
+    } else if constexpr (MODE == BM_TABLE) {
+      src.s0 = a.embed + (long)rr0 * H;
+    } else if constexpr (MODE == BM_LSTM0) {
+      src.s0 = a.ph + (long)ps * L * H;
+    } else if constexpr (MODE == BM_LSTM) {
+      src.s0 = a.ph + ((long)pd * L + a.layer - 1) * H;
+      src.s1 = a.ph + ((long)ps * L + a.layer) * H;
+      src.split = H;
+    } else {
+      src.s0 = a.ph + ((long)pd * L + L - 1) * H;
     }
-  }
-  // this thread's A row (rows past the end reload the last one)
-  const int r = min(row0 + (tid >> 2), rows - 1);
-  BeamSrc<MODE> src{nullptr, nullptr, 0};
-  if constexpr (MODE == BM_JOINT) {
-    const int e = a.jlist[r], b = e / a.beam;
-    const BeamSlot s = a.slots[((long)a.cur[b] * a.n) * a.beam + e];
-    src.s0 = a.zbuf + ((long)b * a.T + s.t) * a.P;
-    src.s1 = a.pp + (long)s.ref * a.P;
-  } else if constexpr (MODE == BM_TABLE) {
-    src.s0 = a.embed + (long)r * H;
-  } else if constexpr (MODE == BM_LSTM0) {
-    src.s0 = a.ph + (long)a.psrc[r] * L * H;
-  } else if constexpr (MODE == BM_LSTM) {
-    src.s0 = a.ph + ((long)a.pdst[r] * L + a.layer - 1) * H;
-    src.s1 = a.ph + ((long)a.psrc[r] * L + a.layer) * H;
-    src.split = H;
-  } else {
-    src.s0 = a.ph + ((long)a.pdst[r] * L + L - 1) * H;
-  }
-  f32_tile(src, a.W, a.N, a.K, col0, blds);
-  float (*Ct)[65] = (float (*)[65])blds;
+    f32_tile32<BEAM_TW>(src, a.W + (long)(col0 + (lane & 31)) * a.ldw, a.K, red);
+    float (*Ct)[33] = (float (*)[33])red;
 
-  if constexpr (MODE == BM_LSTM0 || MODE == BM_LSTM) {
-    // unit u's gates i, f, g, o are columns 4u .. 4u+3
+    if constexpr (MODE == BM_LSTM0 || MODE == BM_LSTM) {
+      // unit u's gates i, f, g, o are columns 4u .. 4u+3: 32 rows x 8 units, one per thread
+      const int er = tid >> 3, u = tid & 7;
+      if (tid < 256 && row0 + er < rows) {
+        const int col = col0 + 4 * u, U = col >> 2;
+        const float* add = MODE == BM_LSTM0 ? a.table + (long)rtok[er] * a.N + col : a.bias + col;
+        const float gi = Ct[er][4 * u] + add[0], gf = Ct[er][4 * u + 1] + add[1];
+        const float gg = Ct[er][4 * u + 2] + add[2], go = Ct[er][4 * u + 3] + add[3];
+        const float cprev = a.pc[((long)rsrc[er] * L + a.layer) * H + U];
+        const float cn = bsigm(gf) * cprev + bsigm(gi) * tanhf(gg);
+        const long o = ((long)rdst[er] * L + a.layer) * H + U;
+        a.pc[o] = cn;
+        a.ph[o] = bsigm(go) * tanhf(cn);
+      }
+    } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = tid + 256 * q, rr = idx >> 4, u = idx & 15;
-      if (row0 + rr >= rows) continue;
-      const int col = col0 + 4 * u, U = col >> 2;
-      const float* add = MODE == BM_LSTM0 ? a.table + (long)rtok[rr] * a.N + col : a.bias + col;
-      const float gi = Ct[rr][4 * u] + add[0], gf = Ct[rr][4 * u + 1] + add[1];
-      const float gg = Ct[rr][4 * u + 2] + add[2], go = Ct[rr][4 * u + 3] + add[3];
-      const float cprev = a.pc[((long)rsrc[rr] * L + a.layer) * H + U];
-      const float cn = bsigm(gf) * cprev + bsigm(gi) * tanhf(gg);
-      const long o = ((long)rdst[rr] * L + a.layer) * H + U;
-      a.pc[o] = cn;
-      a.ph[o] = bsigm(go) * tanhf(cn);
+      for (int q = 0; q < 1024 / (64 * BEAM_TW); ++q) {
+        const int idx = tid + 64 * BEAM_TW * q, er = idx >> 5, jc = idx & 31;
+        if (row0 + er >= rows) continue;
+        const float v = Ct[er][jc] + a.bias[col0 + jc];
+        if constexpr (MODE == BM_PROJ) a.pp[(long)rdst[er] * a.P + col0 + jc] = v;
+        else if constexpr (MODE == BM_TABLE) a.table[(long)(row0 + er) * a.N + col0 + jc] = v;
+        else a.logits[(long)rdst[er] * a.N + col0 + jc] = v;
+      }
     }
-  } else {
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int idx = tid + 256 * q, rr = idx >> 6, j = idx & 63;
-      if (row0 + rr >= rows) continue;
-      const float v = Ct[rr][j] + a.bias[col0 + j];
-      if constexpr (MODE == BM_PROJ) a.pp[(long)rdst[rr] * a.P + col0 + j] = v;
-      else if constexpr (MODE == BM_TABLE) a.table[(long)(row0 + rr) * a.N + col0 + j] = v;
-      else a.logits[(long)rdst[rr] * a.N + col0 + j] = v;
-    }
+    __syncthreads();   // the output tile's LDS is free for the next tile
   }
 }
 
 struct BeamSelArgs {
   const float* logits;   // [n * beam][Cpad]
-  BeamSlot* slots;       // [2][n][beam]
-  int32_t* cur;          // [n]
+  BeamSlot* slots;       // [2][n][beam]: this round's at parity q, the next round's at q ^ 1
+  int32_t* tcur;         // [n] live transcript copy
   int32_t* tr;           // [2][n][beam][U] transcripts
   const int32_t* tlen;   // [n] frames per utterance
-  int32_t* jlist;        // next round's joint list
+  int4* jlist;           // next round's joint list
   int32_t* jcnt;
   int32_t* psrc; int32_t* pdst; int32_t* ptok; int32_t* pcnt;
   int32_t* rounds;       // iterations with work (max over utterances)
   const int32_t* rnow;   // rounds started in this call, this one included
-  int n, beam, C, Cpad, U, blank, m, weak_hash;
+  int n, beam, C, Cpad, U, blank, m, weak_hash, q, T;
 };
 
 // (value, index) pairs: higher value first, then lower index
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
+// The best (value, index) pair over the wave, on every lane: the largest value, then the
+// smallest index among the lanes holding it (indices below 2^24, exact in float). Register
+// exchanges only (DPP rows and the lane-half swaps).
 __device__ __forceinline__ void wave_best(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const float ov = __shfl_xor(v, o, 64);
-    const int oi = __shfl_xor(i, o, 64);
-    if (better(ov, oi, v, i)) { v = ov; i = oi; }
-  }
+  const float m = wave_top(v);
+  const float fi = (v == m && i != INT_MAX) ? (float)i : 3.0e9f;
+  const float mi = -wave_top(-fi);
+  v = m;
+  i = mi < 2.0e9f ? (int)mi : INT_MAX;
 }
 
-__global__ __launch_bounds__(256) void beam_select_kernel(BeamSelArgs a) {
+// One block of 64 K threads per utterance; wave k scores hypothesis k.
+__global__ __launch_bounds__(512) void beam_select_kernel(BeamSelArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.beam;
-  const int par = a.cur[b], T = a.tlen[b];
-  const BeamSlot* old = a.slots + ((long)par * a.n + b) * K;
-  BeamSlot* nw = a.slots + ((long)(par ^ 1) * a.n + b) * K;
-  const int32_t* otr = a.tr + ((long)par * a.n + b) * K * a.U;
-  int32_t* ntr = a.tr + ((long)(par ^ 1) * a.n + b) * K * a.U;
+  const int K = a.beam, nthr = 64 * K;
+  const int T = a.tlen[b];
+  const BeamSlot* old = a.slots + ((long)a.q * a.n + b) * K;
+  BeamSlot* nw = a.slots + ((long)(a.q ^ 1) * a.n + b) * K;
   __shared__ BeamSlot so[BEAM_MAX], sn[BEAM_MAX];
   __shared__ float cs[64];
   __shared__ int cc[64];
@@ -226,57 +244,64 @@ __global__ __launch_bounds__(256) void beam_select_kernel(BeamSelArgs a) {
   if (tid < K) so[tid] = old[tid];
   if (tid < 64) { cs[tid] = -INFINITY; cc[tid] = -2; }
   if (tid < BEAM_MAX * BEAM_MAX) eq[tid / BEAM_MAX][tid % BEAM_MAX] = 0;
+  // this wave's logits row, loaded before the slot state is known (the row is only used when
+  // hypothesis `wave` is live with frames left, when this round's joint wrote it)
+  const float* row = a.logits + ((long)b * K + wave) * a.Cpad;
+  float v[BEAM_NV];
+#pragma unroll
+  for (int i = 0; i < BEAM_NV; ++i) {
+    const int col = lane + 64 * i;
+    v[i] = col < a.C ? row[col] : -INFINITY;
+  }
   __syncthreads();
   bool work = false;
   for (int k = 0; k < K; ++k) work = work || (so[k].score > -INFINITY && so[k].t < T);
-  if (!work) return;  // every live hypothesis is final: the beam stands
+  if (!work) {  // every live hypothesis is final: the beam stands, carried to the next parity
+    if (tid < K) nw[tid] = so[tid];
+    return;
+  }
+  const int par = a.tcur[b];
+  const int32_t* __restrict__ otr = a.tr + ((long)par * a.n + b) * K * a.U;
+  int32_t* __restrict__ ntr = a.tr + ((long)(par ^ 1) * a.n + b) * K * a.U;
 
-  // candidates of each hypothesis: wave w takes slots w, w + 4
-  for (int k = wave; k < K; k += 4) {
+  // candidates of hypothesis `wave`
+  {
+    const int k = wave;
     const BeamSlot h = so[k];
-    if (!(h.score > -INFINITY)) continue;
-    if (h.t >= T) {
+    if (h.score > -INFINITY && h.t >= T) {
       if (lane == 0) { cs[k * K] = h.score; cc[k * K] = -1; }
-      continue;
-    }
-    const float* row = a.logits + ((long)b * K + k) * a.Cpad;
-    float v[BEAM_NV];
-    float mx = -INFINITY;
+    } else if (h.score > -INFINITY) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < BEAM_NV; ++i) {
-      const int col = lane + 64 * i;
-      v[i] = col < a.C ? row[col] : -INFINITY;
-      mx = fmaxf(mx, v[i]);
-    }
+      for (int i = 0; i < BEAM_NV; ++i) mx = fmaxf(mx, v[i]);
+      mx = wave_top(mx);
+      float sum = 0.0f;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    float sum = 0.0f;
+      for (int i = 0; i < BEAM_NV; ++i) sum += v[i] > -INFINITY ? __expf(v[i] - mx) : 0.0f;
+      sum = wave_total(sum);
+      const float lse = mx + __logf(sum);
+      if (h.nsym >= a.m) {  // label cap reached: blank only, with its full log-probability
+        if (lane == 0) { cs[k * K] = h.score + (row[a.blank] - lse); cc[k * K] = a.blank; }
+      } else {
+        // the K best classes: each pass takes the best (value, class) after the previous one
+        float pv = INFINITY;
+        int pi = -1;
+        for (int r = 0; r < K; ++r) {
+          float bv = -INFINITY;
+          int bi = INT_MAX;
 #pragma unroll
-    for (int i = 0; i < BEAM_NV; ++i) sum += v[i] > -INFINITY ? expf(v[i] - mx) : 0.0f;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-    const float lse = mx + logf(sum);
-    if (h.nsym >= a.m) {  // label cap reached: blank only, with its full log-probability
-      if (lane == 0) { cs[k * K] = h.score + (row[a.blank] - lse); cc[k * K] = a.blank; }
-      continue;
-    }
-    // the K best classes: each pass takes the best (value, class) after the previous pass's
-    float pv = INFINITY;
-    int pi = -1;
-    for (int r = 0; r < K; ++r) {
-      float bv = -INFINITY;
-      int bi = INT_MAX;
-#pragma unroll
-      for (int i = 0; i < BEAM_NV; ++i) {
-        const int col = lane + 64 * i;
-        const bool after = v[i] < pv || (v[i] == pv && col > pi);
-        if (after && v[i] > -INFINITY && better(v[i], col, bv, bi)) { bv = v[i]; bi = col; }
+          for (int i = 0; i < BEAM_NV; ++i) {
+            const int col = lane + 64 * i;
+            const bool after = v[i] < pv || (v[i] == pv && col > pi);
+            if (after && v[i] > -INFINITY && better(v[i], col, bv, bi)) { bv = v[i]; bi = col; }
+          }
+          wave_best(bv, bi);
+          if (!(bv > -INFINITY)) break;
+          if (lane == 0) { cs[k * K + r] = h.score + (bv - lse); cc[k * K + r] = bi; }
+          pv = bv;
+          pi = bi;
+        }
       }
-      wave_best(bv, bi);
-      if (!(bv > -INFINITY)) break;
-      if (lane == 0) { cs[k * K + r] = h.score + (bv - lse); cc[k * K + r] = bi; }
-      pv = bv;
-      pi = bi;
     }
   }
   __syncthreads();
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(256) void beam_select_kernel(BeamSelArgs a) {
     int cnt = 0;
     for (int r = 0; r < K; ++r) {
       float bv = taken ? -INFINITY : mine;
-      int bi = lane;
+      int bi = taken ? INT_MAX : lane;
       wave_best(bv, bi);
       if (!(bv > -INFINITY)) break;
       if (lane == bi) taken = true;
@@ -321,20 +346,29 @@ __global__ __launch_bounds__(256) void beam_select_kernel(BeamSelArgs a) {
     }
     sn[tid] = s;
   }
-  // transcripts: the parent's tokens, then the new label
-  for (int j = 0; j < K; ++j) {
-    if (j >= nsel) break;
-    const int p = sel_par[j], lp = so[p].len, c = sel_cls[j];
-    const int32_t* src = otr + (long)p * a.U;
-    int32_t* dst = ntr + (long)j * a.U;
-    for (int i = tid; i < lp; i += 256) dst[i] = src[i];
-    if (tid == 0 && c >= 0 && c != a.blank) dst[lp] = c;
+  // transcripts: the parent's tokens, then the new label; one pass over every (slot,
+  // position) pair, so the loads of all slots are in flight together
+  {
+    int start[BEAM_MAX + 1];
+    start[0] = 0;
+    for (int j = 0; j < K; ++j) start[j + 1] = start[j] + (j < nsel ? so[sel_par[j]].len : 0);
+    const int tot = start[K];
+    for (int e = tid; e < tot; e += nthr) {
+      int j = 0;
+      while (e >= start[j + 1]) ++j;
+      const int i = e - start[j];
+      ntr[(long)j * a.U + i] = otr[(long)sel_par[j] * a.U + i];
+    }
+    if (tid < nsel) {
+      const int c = sel_cls[tid];
+      if (c >= 0 && c != a.blank) ntr[(long)tid * a.U + so[sel_par[tid]].len] = c;
+    }
   }
   __syncthreads();
 
   // recombination: pairs with equal length, last label and hash compare their tokens (a wave
   // per pair)
-  for (int pr = wave; pr < K * K; pr += 4) {
+  for (int pr = wave; pr < K * K; pr += K) {
     const int i = pr / K, j = pr % K;
     if (i >= j || i >= nsel || j >= nsel) continue;
     const BeamSlot& x = sn[i];
@@ -371,51 +405,56 @@ __global__ __launch_bounds__(256) void beam_select_kernel(BeamSelArgs a) {
 
   if (tid == 0) {
     // predictor entries for the new labels: the utterance's 2K entries minus those the old
-    // beam refers to
+    // beam refers to; then one reservation on each work list
     const int base = POOL_BASE + b * 2 * K;
     uint32_t used = 0;
     for (int k = 0; k < K; ++k) {
       const int r = so[k].ref - base;
       if (r >= 0 && r < 2 * K) used |= 1u << r;
     }
-    int more = 0;
+    int npred = 0, nact = 0;
+    int tok[BEAM_MAX], act[BEAM_MAX];
+    for (int j = 0; j < K; ++j) {
+      const bool live = j < nsel && merged[j] > -INFINITY;
+      const int c = j < nsel ? sel_cls[j] : -1;
+      tok[j] = live && c >= 0 && c != a.blank;
+      act[j] = live && sn[j].t < T;
+      npred += tok[j];
+      nact += act[j];
+    }
+    const int p0 = npred ? atomicAdd(a.pcnt, npred) : 0;
+    const int a0 = nact ? atomicAdd(a.jcnt, nact) : 0;
+    int pi = p0, ai = a0;
     for (int j = 0; j < K; ++j) {
       BeamSlot s = sn[j];
       s.score = merged[j];
-      if (j < nsel && s.score > -INFINITY) {
-        const int c = sel_cls[j];
-        if (c >= 0 && c != a.blank) {
-          const int e = __builtin_ctz(~used);
-          used |= 1u << e;
-          const int idx = atomicAdd(a.pcnt, 1);
-          a.psrc[idx] = so[sel_par[j]].ref;
-          a.pdst[idx] = base + e;
-          a.ptok[idx] = c;
-          s.ref = base + e;
-        }
-        if (s.t < T) {
-          a.jlist[atomicAdd(a.jcnt, 1)] = b * K + j;
-          more = 1;
-        }
+      if (tok[j]) {
+        const int e = __builtin_ctz(~used);
+        used |= 1u << e;
+        a.psrc[pi] = so[sel_par[j]].ref;
+        a.pdst[pi] = base + e;
+        a.ptok[pi] = sel_cls[j];
+        ++pi;
+        s.ref = base + e;
       }
+      if (act[j]) a.jlist[ai++] = make_int4(b * a.T + s.t, s.ref, b * K + j, 0);
       nw[j] = s;
     }
-    a.cur[b] = par ^ 1;
+    a.tcur[b] = par ^ 1;
     atomicMax(a.rounds, *a.rnow);
-    (void)more;
   }
 }
 
 struct BeamEdgeArgs {
   BeamSlot* slots;
-  int32_t* cur;
+  int32_t* tcur;
   const int32_t* tlen;
-  int32_t* jlist; int32_t* jcnt;   // [2] counters
+  int4* jlist; int32_t* jcnt;      // [2] counters
   int32_t* pcnt; int32_t* rounds; int32_t* rnow;
   const int32_t* tr;
   int32_t* tokens; int32_t* lens; float* scores; int32_t* frames;   // end: caller's
   const float4* z; float4* zbuf; long n4;                           // stage
-  int n, beam, U, Ucall, score_norm;
+  int n, beam, U, Ucall, score_norm, T, q;   // q: parity of the final slots (end)
 };
 
 // One block: the start beam of every utterance and the first joint list.
@@ -424,14 +463,14 @@ __global__ __launch_bounds__(256) void beam_begin_kernel(BeamEdgeArgs a) {
   if (threadIdx.x == 0) cnt = 0;
   __syncthreads();
   for (int b = threadIdx.x; b < a.n; b += 256) {
-    a.cur[b] = 0;
+    a.tcur[b] = 0;
     for (int k = 0; k < a.beam; ++k) {
       BeamSlot s;
       s.score = k == 0 ? 0.0f : -INFINITY;
       s.t = 0; s.nsym = 0; s.len = 0; s.ref = POOL_START; s.last = -1; s.hash = 0;
       a.slots[(long)b * a.beam + k] = s;
     }
-    if (a.tlen[b] > 0) a.jlist[atomicAdd(&cnt, 1)] = b * a.beam;
+    if (a.tlen[b] > 0) a.jlist[atomicAdd(&cnt, 1)] = make_int4(b * a.T, POOL_START, b * a.beam, 0);
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -451,8 +490,8 @@ __global__ __launch_bounds__(256) void beam_stage_kernel(BeamEdgeArgs a) {
 // and written out.
 __global__ __launch_bounds__(256) void beam_end_kernel(BeamEdgeArgs a) {
   const int b = blockIdx.x, K = a.beam;
-  const int par = a.cur[b];
-  const BeamSlot* sl = a.slots + ((long)par * a.n + b) * K;
+  const int par = a.tcur[b];
+  const BeamSlot* sl = a.slots + ((long)a.q * a.n + b) * K;
   const int32_t* tr = a.tr + ((long)par * a.n + b) * K * a.U;
   __shared__ int order[BEAM_MAX];
   if (threadIdx.x == 0) {
@@ -520,9 +559,9 @@ bool beam_dims(const cac_beam_config* c, BeamDims& d, std::string& why) {
 
 struct BeamLayout {
   DecWeights w;
-  size_t table, zrow, slots, cur, tr, tlen, jlist, jcnt, psrc, pdst, ptok, pcnt, rounds, rnow, log, logits, zbuf;
+  size_t table, zrow, slots, tcur, tr, tlen, jlist, jcnt, psrc, pdst, ptok, pcnt, rounds, rnow, log, logits, zbuf;
   size_t ph, pc, pp, total;
-  size_t entries, rounds_max;
+  size_t entries, rounds_max, lrows;
 };
 
 BeamLayout beam_layout(const BeamDims& d) {
@@ -536,12 +575,15 @@ BeamLayout beam_layout(const BeamDims& d) {
   t.entries = POOL_BASE + S * 2 * K;
   t.rounds_max = (size_t)d.T * (d.m + 1);
   t.slots = take(2 * S * K * sizeof(BeamSlot));
-  t.cur = take(S * 4);
+  t.tcur = take(S * 4);
   t.tr = take(2 * S * K * (size_t)d.U * 4);
   t.tlen = take(S * 4);
-  t.jlist = take(2 * S * K * 4);
+  // work lists padded to a multiple of 32 rows (a tile block reads its 32 entries whatever
+  // the list's length)
+  t.lrows = (S * K + 31) / 32 * 32;
+  t.jlist = take(2 * t.lrows * 16);
   t.jcnt = take(2 * 4);
-  t.psrc = take(S * K * 4); t.pdst = take(S * K * 4); t.ptok = take(S * K * 4);
+  t.psrc = take(t.lrows * 4); t.pdst = take(t.lrows * 4); t.ptok = take(t.lrows * 4);
   t.pcnt = take(4);
   t.rounds = take(4);
   t.rnow = take(4);
@@ -592,12 +634,19 @@ BeamTileArgs beam_tile_base(cac_beam* c, int n, int T) {
   const BeamLayout& y = c->lay;
   BeamTileArgs t{};
   t.psrc = c->P<int32_t>(y.psrc); t.pdst = c->P<int32_t>(y.pdst); t.ptok = c->P<int32_t>(y.ptok);
-  t.cur = c->P<int32_t>(y.cur); t.slots = c->P<BeamSlot>(y.slots); t.zbuf = c->P<float>(y.zbuf);
+  t.zbuf = c->P<float>(y.zbuf);
   t.logits = c->P<float>(y.logits);
   t.ph = c->P<float>(y.ph); t.pc = c->P<float>(y.pc); t.pp = c->P<float>(y.pp);
   t.embed = c->P<float>(y.w.embed); t.table = c->P<float>(y.table);
   t.L = d.L; t.H = d.H; t.P = d.P; t.C = d.C; t.T = T; t.n = n; t.beam = d.K;
   return t;
+}
+
+// 1-D grid of a tile launch: one block per tile of the largest list (8 * ceil(gx / 8) per row
+// tile), at most BEAM_TILE_BLOCKS; blocks loop over the tiles of the rows the list holds.
+constexpr unsigned BEAM_TILE_BLOCKS = 512;
+dim3 beam_grid(int gx, unsigned row_tiles) {
+  return dim3(std::min<unsigned>((unsigned)((gx + 7) / 8 * 8) * row_tiles, BEAM_TILE_BLOCKS));
 }
 
 // The predictor kernels over the list (count) of (parent entry, new entry, label) rows.
@@ -607,21 +656,24 @@ void beam_predictor(cac_beam* c, Launcher& L, const BeamTileArgs& base, const in
   BeamTileArgs t = base;
   t.count = count;
   t.round = round;
-  const unsigned prow = (unsigned)((max_rows + 63) / 64);
+  const unsigned prow = (unsigned)((max_rows + 31) / 32);
   for (int l = 0; l < d.L; ++l) {
     t.layer = l;
     t.K = l == 0 ? d.H : 2 * d.H;
     t.N = 4 * d.H;
-    // the first layer contracts h with the W_hh rows only (its input half is the token table)
-    t.W = c->P<float>(y.w.lstm_w) + (size_t)l * 2 * d.H * 4 * d.H + (l == 0 ? (size_t)d.H * 4 * d.H : 0);
+    t.ldw = 2 * d.H;
+    // the first layer contracts h with the W_hh inputs only (its input half is the token table)
+    t.W = c->P<float>(y.w.lstm_w) + (size_t)l * 2 * d.H * 4 * d.H + (l == 0 ? (size_t)d.H : 0);
     t.bias = c->P<float>(y.w.lstm_b) + (size_t)l * 4 * d.H;
     L.tag("beam_lstm", 0.0, 0.0);
+    t.gx = 4 * d.H / 32;
     L.launch(l == 0 ? (const void*)&beam_tile_kernel<BM_LSTM0> : (const void*)&beam_tile_kernel<BM_LSTM>,
-             dim3(4 * d.H / 64, prow), dim3(256), F32T_LDS, &t);
+             beam_grid(t.gx, prow), dim3(64 * BEAM_TW), 0, &t);
   }
-  t.K = d.H; t.N = d.P; t.W = c->P<float>(y.w.proj_w); t.bias = c->P<float>(y.w.proj_b);
+  t.K = d.H; t.N = d.P; t.ldw = d.H; t.W = c->P<float>(y.w.proj_w); t.bias = c->P<float>(y.w.proj_b);
   L.tag("beam_proj", 0.0, 0.0);
-  L.launch((const void*)&beam_tile_kernel<BM_PROJ>, dim3(d.P / 64, prow), dim3(256), F32T_LDS, &t);
+  t.gx = d.P / 32;
+  L.launch((const void*)&beam_tile_kernel<BM_PROJ>, beam_grid(t.gx, prow), dim3(64 * BEAM_TW), 0, &t);
 }
 
 // Rounds r0 .. r0 + count - 1 (parity from the round index).
@@ -629,33 +681,34 @@ void beam_rounds(cac_beam* c, Launcher& L, int n, int T, int r0, int count) {
   const BeamDims& d = c->d;
   const BeamLayout& y = c->lay;
   const BeamTileArgs base = beam_tile_base(c, n, T);
-  int32_t* jlist = c->P<int32_t>(y.jlist);
+  int4* jlist = c->P<int4>(y.jlist);
   int32_t* jcnt = c->P<int32_t>(y.jcnt);
   const int nk = n * d.K;
   for (int i = 0; i < count && L.err == hipSuccess; ++i) {
     const int j = r0 + i, q = j & 1;
     BeamTileArgs jt = base;
     jt.count = jcnt + q;
-    jt.jlist = jlist + (size_t)q * d.S * d.K;
+    jt.jlist = jlist + (size_t)q * y.lrows;
     jt.clr0 = jcnt + (q ^ 1);
     jt.clr1 = c->P<int32_t>(y.pcnt);
     jt.rnow = c->P<int32_t>(y.rnow);
     jt.log = c->profiling ? c->P<int32_t>(y.log) : nullptr;
     jt.round = j;
-    jt.K = d.P; jt.N = d.Cpad; jt.W = c->P<float>(y.w.out_w); jt.bias = c->P<float>(y.w.out_b);
+    jt.K = d.P; jt.N = d.Cpad; jt.ldw = d.P; jt.W = c->P<float>(y.w.out_w); jt.bias = c->P<float>(y.w.out_b);
     L.tag("beam_joint", 0.0, 0.0);
-    L.launch((const void*)&beam_tile_kernel<BM_JOINT>, dim3(d.Cpad / 64, (unsigned)((nk + 63) / 64)), dim3(256),
-             F32T_LDS, &jt);
+    jt.gx = d.Cpad / 32;
+    L.launch((const void*)&beam_tile_kernel<BM_JOINT>, beam_grid(jt.gx, (unsigned)((nk + 31) / 32)), dim3(64 * BEAM_TW),
+             0, &jt);
     BeamSelArgs s{};
-    s.logits = c->P<float>(y.logits); s.slots = c->P<BeamSlot>(y.slots); s.cur = c->P<int32_t>(y.cur);
+    s.logits = c->P<float>(y.logits); s.slots = c->P<BeamSlot>(y.slots); s.tcur = c->P<int32_t>(y.tcur);
     s.tr = c->P<int32_t>(y.tr); s.tlen = c->P<int32_t>(y.tlen);
-    s.jlist = jlist + (size_t)(q ^ 1) * d.S * d.K; s.jcnt = jcnt + (q ^ 1);
+    s.jlist = jlist + (size_t)(q ^ 1) * y.lrows; s.jcnt = jcnt + (q ^ 1);
     s.psrc = c->P<int32_t>(y.psrc); s.pdst = c->P<int32_t>(y.pdst); s.ptok = c->P<int32_t>(y.ptok);
     s.pcnt = c->P<int32_t>(y.pcnt); s.rounds = c->P<int32_t>(y.rounds); s.rnow = c->P<int32_t>(y.rnow);
-    s.n = n; s.beam = d.K; s.C = d.C; s.Cpad = d.Cpad; s.U = d.U; s.blank = d.V; s.m = d.m;
+    s.n = n; s.beam = d.K; s.C = d.C; s.Cpad = d.Cpad; s.U = d.U; s.blank = d.V; s.m = d.m; s.q = q; s.T = T;
     s.weak_hash = (d.flags & CAC_BEAM_FLAG_WEAK_HASH) ? 1 : 0;
     L.tag("beam_select", 0.0, 0.0);
-    L.launch((const void*)&beam_select_kernel, dim3(n), dim3(256), 0, &s);
+    L.launch((const void*)&beam_select_kernel, dim3(n), dim3(64 * d.K), 0, &s);
     BeamTileArgs pt = base;
     pt.log = jt.log;
     beam_predictor(c, L, pt, c->P<int32_t>(y.pcnt), nk, j);
@@ -753,10 +806,6 @@ int32_t cac_beam_create(const cac_beam_config* cfg, const float* h_params, size_
   c->d = d; c->lay = lay; c->ws = (char*)d_workspace; c->stream = (hipStream_t)hip_stream; c->dry = dry;
   if (dry) { *out = c; return CAC_OK; }
   kernels_init();
-  for (const void* f : {(const void*)&beam_tile_kernel<BM_LSTM0>, (const void*)&beam_tile_kernel<BM_LSTM>,
-                        (const void*)&beam_tile_kernel<BM_PROJ>, (const void*)&beam_tile_kernel<BM_JOINT>,
-                        (const void*)&beam_tile_kernel<BM_TABLE>})
-    (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)F32T_LDS);
   std::vector<uint8_t> buf(lay.w.end, 0);
   dec_repack(h_params, lay.w, d.C, d.H, d.L, d.P, d.Cpad, buf.data());
   hipError_t e = hipMemcpyAsync(c->ws, buf.data(), buf.size(), hipMemcpyHostToDevice, c->stream);
@@ -776,10 +825,12 @@ int32_t cac_beam_create(const cac_beam_config* cfg, const float* h_params, size_
     L.stream = c->stream;
     BeamTileArgs t = beam_tile_base(c, 1, 1);
     // first layer's input table: embed[token] W_ih + b_ih + b_hh for every class
-    t.K = d.H; t.N = 4 * d.H; t.W = c->P<float>(lay.w.lstm_w); t.bias = c->P<float>(lay.w.lstm_b);
+    t.K = d.H; t.N = 4 * d.H; t.ldw = 2 * d.H; t.W = c->P<float>(lay.w.lstm_w); t.bias = c->P<float>(lay.w.lstm_b);
     t.count = c->P<int32_t>(lay.zrow);
     L.tag("beam_table", 0.0, 0.0);
-    L.launch((const void*)&beam_tile_kernel<BM_TABLE>, dim3(4 * d.H / 64, (d.C + 63) / 64), dim3(256), F32T_LDS, &t);
+    t.gx = 4 * d.H / 32;
+    L.launch((const void*)&beam_tile_kernel<BM_TABLE>, beam_grid(t.gx, (unsigned)((d.C + 31) / 32)), dim3(64 * BEAM_TW), 0,
+             &t);
     beam_predictor(c, L, beam_tile_base(c, 1, 1), c->P<int32_t>(lay.pcnt), 1, 0);
     e = L.err;
   }
@@ -823,12 +874,12 @@ int32_t cac_beam_decode(cac_beam* c, int32_t n, const int32_t* h_lengths, int32_
     first = c->prof.pending.size();
   }
   BeamEdgeArgs ea{};
-  ea.slots = c->P<BeamSlot>(y.slots); ea.cur = c->P<int32_t>(y.cur); ea.tlen = c->P<int32_t>(y.tlen);
-  ea.jlist = c->P<int32_t>(y.jlist); ea.jcnt = c->P<int32_t>(y.jcnt); ea.pcnt = c->P<int32_t>(y.pcnt);
+  ea.slots = c->P<BeamSlot>(y.slots); ea.tcur = c->P<int32_t>(y.tcur); ea.tlen = c->P<int32_t>(y.tlen);
+  ea.jlist = c->P<int4>(y.jlist); ea.jcnt = c->P<int32_t>(y.jcnt); ea.pcnt = c->P<int32_t>(y.pcnt);
   ea.rounds = c->P<int32_t>(y.rounds); ea.rnow = c->P<int32_t>(y.rnow); ea.tr = c->P<int32_t>(y.tr);
   ea.tokens = d_tokens; ea.lens = d_lengths; ea.scores = d_scores; ea.frames = d_frames;
   ea.z = (const float4*)d_z; ea.zbuf = c->P<float4>(y.zbuf); ea.n4 = (long)n * nf * d.P / 4;
-  ea.n = n; ea.beam = d.K; ea.U = d.U; ea.Ucall = nf * d.m; ea.score_norm = d.norm;
+  ea.n = n; ea.beam = d.K; ea.U = d.U; ea.Ucall = nf * d.m; ea.score_norm = d.norm; ea.T = nf;
   L.tag("beam_begin", 0.0, 0.0);
   L.launch((const void*)&beam_begin_kernel, dim3(1), dim3(256), 0, &ea);
   L.tag("beam_stage", 0.0, 0.0);
@@ -853,6 +904,7 @@ int32_t cac_beam_decode(cac_beam* c, int32_t n, const int32_t* h_lengths, int32_
     if (e != hipSuccess) return c->fail(CAC_EHIP, std::string("device error during the search: ") + hipGetErrorString(e));
     if (left == 0) break;
   }
+  ea.q = r & 1;   // every round moved every utterance's slots to the next parity
   L.tag("beam_end", 0.0, 0.0);
   L.launch((const void*)&beam_end_kernel, dim3(n), dim3(256), 0, &ea);
   if (L.err != hipSuccess) return c->fail(CAC_EHIP, std::string("HIP launch failed: ") + hipGetErrorString(L.err));

@@ -45,7 +45,8 @@ enum DecMode { DM_LSTM0 = 0, DM_LSTM = 1, DM_PROJ = 2, DM_JOINT = 3, DM_TABLE = 
 
 struct DecTileArgs {
   int K, N;                 // contraction length, output columns (a multiple of 64)
-  const float* W;           // [K][N]
+  const float* W;           // [N][ldw]: output column n's K weights at W + n * ldw
+  int ldw;
   const float* bias;        // [N]
   const int32_t* ids;       // [n] call slot -> stream id
   const int32_t* list;      // rows: P list (predictor modes) or A list (joint: row = a * nf + f)
@@ -131,7 +132,7 @@ __global__ __launch_bounds__(256) void dec_tile_kernel(DecTileArgs a) {
   }
   // rows past the end reload the last one
   const DecSrc<MODE> src{dec_arow<MODE>(a, min(row0 + (tid >> 2), rows - 1))};
-  f32_tile(src, a.W, a.N, a.K, col0, dlds);
+  f32_tile(src, a.W, a.ldw, a.K, col0, dlds);
   float (*Ct)[65] = (float (*)[65])dlds;
 
   if constexpr (MODE == DM_LSTM0 || MODE == DM_LSTM) {
@@ -477,22 +478,22 @@ void dec_enqueue(cac_dec* c, Launcher& L, int n, int nf, const float* d_z, int32
     t.list = ra.plist + (size_t)j * n;
     t.count = ra.pcnt + j;
     for (int l = 0; l < d.L; ++l) {
-      t.layer = l; t.K = l == 0 ? d.H : 2 * d.H; t.N = 4 * d.H;
-      // layer 0 contracts h with the W_hh rows only (its input half is the token table)
-      t.W = c->P<float>(y.w.lstm_w) + (size_t)l * 2 * d.H * 4 * d.H + (l == 0 ? (size_t)d.H * 4 * d.H : 0);
+      t.layer = l; t.K = l == 0 ? d.H : 2 * d.H; t.N = 4 * d.H; t.ldw = 2 * d.H;
+      // layer 0 contracts h with the W_hh inputs only (its input half is the token table)
+      t.W = c->P<float>(y.w.lstm_w) + (size_t)l * 2 * d.H * 4 * d.H + (l == 0 ? (size_t)d.H : 0);
       t.bias = c->P<float>(y.w.lstm_b) + (size_t)l * 4 * d.H;
       L.tag("dec_lstm", 0.0, 0.0);
       L.launch(l == 0 ? (const void*)&dec_tile_kernel<DM_LSTM0> : (const void*)&dec_tile_kernel<DM_LSTM>,
                dim3(4 * d.H / 64, prow), blk, F32T_LDS, &t);
     }
-    t.K = d.H; t.N = d.P; t.W = c->P<float>(y.w.proj_w); t.bias = c->P<float>(y.w.proj_b);
+    t.K = d.H; t.N = d.P; t.ldw = d.H; t.W = c->P<float>(y.w.proj_w); t.bias = c->P<float>(y.w.proj_b);
     L.tag("dec_proj", 0.0, 0.0);
     L.launch((const void*)&dec_tile_kernel<DM_PROJ>, dim3(d.P / 64, prow), blk, F32T_LDS, &t);
     // joint of the slots on A_j, all frames
     DecTileArgs jt = ta;
     jt.list = ra.alist + (size_t)j * n;
     jt.count = ra.acnt + j;
-    jt.K = d.P; jt.N = d.Cpad; jt.W = c->P<float>(y.w.out_w); jt.bias = c->P<float>(y.w.out_b);
+    jt.K = d.P; jt.N = d.Cpad; jt.ldw = d.P; jt.W = c->P<float>(y.w.out_w); jt.bias = c->P<float>(y.w.out_b);
     L.tag("dec_joint", 0.0, 0.0);
     L.launch((const void*)&dec_tile_kernel<DM_JOINT>, dim3(ntiles, jrow), blk, F32T_LDS, &jt);
     DecRoundArgs r = ra;
@@ -655,7 +656,7 @@ int32_t cac_dec_create(const cac_dec_config* cfg, const float* h_params, size_t 
     L.stream = c->stream;
     // first layer's input table: embed[token] W_ih + b_ih + b_hh for every class
     DecTileArgs t{};
-    t.K = d.H; t.N = 4 * d.H; t.W = c->P<float>(lay.w.lstm_w); t.bias = c->P<float>(lay.w.lstm_b);
+    t.K = d.H; t.N = 4 * d.H; t.ldw = 2 * d.H; t.W = c->P<float>(lay.w.lstm_w); t.bias = c->P<float>(lay.w.lstm_b);
     t.count = c->P<int32_t>(lay.ccount); t.embed = c->P<float>(lay.w.embed); t.table = c->P<float>(lay.table);
     t.H = d.H; t.C = d.C;
     L.tag("dec_table", 0.0, 0.0);

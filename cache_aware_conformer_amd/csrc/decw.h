@@ -3,10 +3,11 @@
 //
 // Caller order (cac_decode.h): embed [C][H]; per LSTM layer w_ih [H][4H], w_hh [H][4H], b_ih
 // [4H], b_hh [4H] (gate blocks i, f, g, o); proj_w [H][P], proj_b [P]; out_w [P][C], out_b [C].
-// Device order: the same embedding; per layer one [2H][4H] matrix (w_ih rows, then w_hh rows)
-// whose columns are packed per unit (unit u's gates i, f, g, o at columns 4u .. 4u+3), and the
-// two biases summed in the same column order; the projection as given; the joint matrix with
-// its columns (and bias) zero-padded to Cpad, a multiple of 64.
+// Device order: every matrix stored per output column, its K inputs contiguous ([N][K], the
+// layout the tile loop reads): the same embedding; per LSTM layer one [4H][2H] matrix whose row
+// n = 4u + g holds unit u's gate g (i, f, g, o) with the w_ih inputs first and the w_hh inputs
+// after them, and the two biases summed in the same row order; the projection as [P][H]; the
+// joint as [Cpad][P] with rows C .. Cpad-1 (and their bias) zero, Cpad a multiple of 64.
 #pragma once
 
 #include <cstddef>
@@ -53,16 +54,21 @@ inline void dec_repack(const float* params, const DecWeights& w, size_t C, size_
       for (size_t u = 0; u < H; ++u) {
         const size_t src = g * H + u, dst = 4 * u + g;
         b[dst] = bih[src] + bhh[src];
+        float* row = m + dst * 2 * H;
         for (size_t k = 0; k < H; ++k) {
-          m[k * 4 * H + dst] = wih[k * 4 * H + src];
-          m[(H + k) * 4 * H + dst] = whh[k * 4 * H + src];
+          row[k] = wih[k * 4 * H + src];
+          row[H + k] = whh[k * 4 * H + src];
         }
       }
   }
-  memcpy(buf + w.proj_w, take(H * P), H * P * 4);
+  const float* pw = take(H * P);
+  float* pd = (float*)(buf + w.proj_w);
+  for (size_t k = 0; k < H; ++k)
+    for (size_t n = 0; n < P; ++n) pd[n * H + k] = pw[k * P + n];
   memcpy(buf + w.proj_b, take(P), P * 4);
   const float* ow = take(P * C);
-  float* dst = (float*)(buf + w.out_w);
-  for (size_t k = 0; k < P; ++k) memcpy(dst + k * Cpad, ow + k * C, C * 4);
+  float* od = (float*)(buf + w.out_w);
+  for (size_t k = 0; k < P; ++k)
+    for (size_t n = 0; n < C; ++n) od[n * P + k] = ow[k * C + n];
   memcpy(buf + w.out_b, take(C), C * 4);
 }
