@@ -8,11 +8,12 @@
 // so the parents' entries are never overwritten while they are read; blank shares its
 // parent's entry.
 //
-// One iteration ("round") is five kernels:
+// One iteration ("round") is six kernels:
 //   joint   - rows of the joint list (live hypotheses with frames left): ReLU(z[b][t] + p) Wout
 //             + bout into a logits row per slot (MFMA tiles, the predictor/joint tile loop);
-//   select  - one block per utterance: log_softmax and top-K per hypothesis, forced blank,
-//             final hypotheses, global top-K, new slots and transcripts, recombination,
+//   cand    - one wave per hypothesis: log_softmax and its top-K (or forced blank, or a final
+//             hypothesis offering itself);
+//   select  - one block per utterance: global top-K, new slots and transcripts, recombination,
 //             predictor entries for new labels, the next joint list (each entry the frame row,
 //             predictor entry and logits row it needs, so the joint reads no beam state);
 //             an utterance without work copies its slots to the next parity;
@@ -202,6 +203,8 @@ __global__ __launch_bounds__(64 * BEAM_TW) void beam_tile_kernel(BeamTileArgs a)
 
 struct BeamSelArgs {
   const float* logits;   // [n * beam][Cpad]
+  float* cand_s;         // [n][64] candidate scores, slot-major (k * beam + rank); -inf: none
+  int32_t* cand_c;       // [n][64] candidate classes (-1: a final hypothesis offering itself)
   BeamSlot* slots;       // [2][n][beam]: this round's at parity q, the next round's at q ^ 1
   int32_t* tcur;         // [n] live transcript copy
   int32_t* tr;           // [2][n][beam][U] transcripts
@@ -228,31 +231,120 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
   i = mi < 2.0e9f ? (int)mi : INT_MAX;
 }
 
-// One block of 64 K threads per utterance; wave k scores hypothesis k.
-__global__ __launch_bounds__(512) void beam_select_kernel(BeamSelArgs a) {
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.beam, nthr = 64 * K;
+// One wave per hypothesis (block = one wave, grid n * beam): its candidates. A live hypothesis
+// with frames left takes log_softmax of its logits row; with labels left at its frame its
+// candidates are its K best classes (score + log-probability, ranked by logit then class),
+// else blank alone with the blank's log-probability; a final hypothesis offers itself; an empty
+// slot offers nothing.
+__global__ __launch_bounds__(64) void beam_cand_kernel(BeamSelArgs a) {
+  const int e = blockIdx.x, lane = threadIdx.x, K = a.beam;
+  const int b = e / K, k = e - b * K;
+  const BeamSlot h = a.slots[((long)a.q * a.n + b) * K + k];
   const int T = a.tlen[b];
-  const BeamSlot* old = a.slots + ((long)a.q * a.n + b) * K;
-  BeamSlot* nw = a.slots + ((long)(a.q ^ 1) * a.n + b) * K;
-  __shared__ BeamSlot so[BEAM_MAX], sn[BEAM_MAX];
-  __shared__ float cs[64];
-  __shared__ int cc[64];
-  __shared__ int sel_par[BEAM_MAX], sel_cls[BEAM_MAX], nsel;
-  __shared__ float sel_sc[BEAM_MAX], merged[BEAM_MAX];
-  __shared__ int eq[BEAM_MAX][BEAM_MAX];
-  if (tid < K) so[tid] = old[tid];
-  if (tid < 64) { cs[tid] = -INFINITY; cc[tid] = -2; }
-  if (tid < BEAM_MAX * BEAM_MAX) eq[tid / BEAM_MAX][tid % BEAM_MAX] = 0;
-  // this wave's logits row, loaded before the slot state is known (the row is only used when
-  // hypothesis `wave` is live with frames left, when this round's joint wrote it)
-  const float* row = a.logits + ((long)b * K + wave) * a.Cpad;
+  // the logits row, loaded with the slot (only used when this round's joint wrote it)
+  const float* row = a.logits + (long)e * a.Cpad;
   float v[BEAM_NV];
 #pragma unroll
   for (int i = 0; i < BEAM_NV; ++i) {
     const int col = lane + 64 * i;
     v[i] = col < a.C ? row[col] : -INFINITY;
   }
+  float* cs = a.cand_s + (long)b * 64 + k * K;
+  int32_t* cc = a.cand_c + (long)b * 64 + k * K;
+  float out_s = -INFINITY;
+  int out_c = -2;
+  if (h.score > -INFINITY && h.t >= T) {
+    if (lane == 0) { out_s = h.score; out_c = -1; }
+  } else if (h.score > -INFINITY) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < BEAM_NV; ++i) mx = fmaxf(mx, v[i]);
+    const float lmax = mx;   // this lane's largest logit
+    mx = wave_top(mx);
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BEAM_NV; ++i) sum += v[i] > -INFINITY ? __expf(v[i] - mx) : 0.0f;
+    sum = wave_total(sum);
+    const float lse = mx + __logf(sum);
+    if (h.nsym >= a.m) {  // label cap reached: blank only, with its full log-probability
+      if (lane == 0) { out_s = h.score + (row[a.blank] - lse); out_c = a.blank; }
+    } else {
+      // The K best classes. Every one of them is at least theta, the K-th largest of the lanes'
+      // maxima (those are K distinct classes), so only classes >= theta take part: when no lane
+      // holds more than two of them, each lane keeps its (at most two) in registers and the K
+      // passes pop lane heads; otherwise every pass scans all of a lane's classes.
+      float tv = lmax;
+      int ti = lane;
+      float theta = -INFINITY;
+      for (int r = 0; r < K; ++r) {
+        float bv = tv;
+        int bi = ti;
+        wave_best(bv, bi);
+        if (!(bv > -INFINITY)) break;
+        theta = bv;
+        if (lane == bi) tv = -INFINITY;
+      }
+      int nc = 0;
+      float c0v = -INFINITY, c1v = -INFINITY;
+      int c0i = INT_MAX, c1i = INT_MAX;
+#pragma unroll
+      for (int i = 0; i < BEAM_NV; ++i) {
+        const int col = lane + 64 * i;
+        if (v[i] >= theta && v[i] > -INFINITY) {
+          // classes arrive in increasing order: keep the pair sorted by (logit desc, class asc)
+          if (nc == 0) { c0v = v[i]; c0i = col; }
+          else if (v[i] > c0v) { c1v = c0v; c1i = c0i; c0v = v[i]; c0i = col; }
+          else if (nc == 1 || v[i] > c1v) { c1v = v[i]; c1i = col; }
+          ++nc;
+        }
+      }
+      const bool fast = !__any(nc > 2);
+      float pv = INFINITY;
+      int pi = -1;
+      for (int r = 0; r < K; ++r) {
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        if (fast) {
+          bv = c0v;
+          bi = c0i;
+        } else {
+#pragma unroll
+          for (int i = 0; i < BEAM_NV; ++i) {
+            const int col = lane + 64 * i;
+            const bool after = v[i] < pv || (v[i] == pv && col > pi);
+            if (after && v[i] > -INFINITY && better(v[i], col, bv, bi)) { bv = v[i]; bi = col; }
+          }
+        }
+        wave_best(bv, bi);
+        if (!(bv > -INFINITY)) break;
+        if (lane == r) { out_s = h.score + (bv - lse); out_c = bi; }
+        if (fast && c0i == bi) { c0v = c1v; c0i = c1i; c1v = -INFINITY; c1i = INT_MAX; }
+        pv = bv;
+        pi = bi;
+      }
+    }
+  }
+  if (lane < K) { cs[lane] = out_s; cc[lane] = out_c; }
+}
+
+// One block of 256 threads per utterance: the global top-K of the candidates, new slots and
+// transcripts, recombination, the next round's work lists.
+__global__ __launch_bounds__(256) void beam_select_kernel(BeamSelArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = a.beam, nthr = 256, NWV = 4;
+  const int T = a.tlen[b];
+  const BeamSlot* old = a.slots + ((long)a.q * a.n + b) * K;
+  BeamSlot* nw = a.slots + ((long)(a.q ^ 1) * a.n + b) * K;
+  __shared__ BeamSlot so[BEAM_MAX], sn[BEAM_MAX];
+  __shared__ int cc[64];
+  __shared__ int sel_par[BEAM_MAX], sel_cls[BEAM_MAX], nsel;
+  __shared__ float sel_sc[BEAM_MAX], merged[BEAM_MAX];
+  __shared__ int eq[BEAM_MAX][BEAM_MAX];
+  // candidates (one per lane of wave 0), loaded with the slots
+  const float mine = (wave == 0 && lane < K * K) ? a.cand_s[(long)b * 64 + lane] : -INFINITY;
+  if (wave == 0) cc[lane] = lane < K * K ? a.cand_c[(long)b * 64 + lane] : -2;
+  if (tid < K) so[tid] = old[tid];
+  if (tid < BEAM_MAX * BEAM_MAX) eq[tid / BEAM_MAX][tid % BEAM_MAX] = 0;
   __syncthreads();
   bool work = false;
   for (int k = 0; k < K; ++k) work = work || (so[k].score > -INFINITY && so[k].t < T);
@@ -264,51 +356,8 @@ __global__ __launch_bounds__(512) void beam_select_kernel(BeamSelArgs a) {
   const int32_t* __restrict__ otr = a.tr + ((long)par * a.n + b) * K * a.U;
   int32_t* __restrict__ ntr = a.tr + ((long)(par ^ 1) * a.n + b) * K * a.U;
 
-  // candidates of hypothesis `wave`
-  {
-    const int k = wave;
-    const BeamSlot h = so[k];
-    if (h.score > -INFINITY && h.t >= T) {
-      if (lane == 0) { cs[k * K] = h.score; cc[k * K] = -1; }
-    } else if (h.score > -INFINITY) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < BEAM_NV; ++i) mx = fmaxf(mx, v[i]);
-      mx = wave_top(mx);
-      float sum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < BEAM_NV; ++i) sum += v[i] > -INFINITY ? __expf(v[i] - mx) : 0.0f;
-      sum = wave_total(sum);
-      const float lse = mx + __logf(sum);
-      if (h.nsym >= a.m) {  // label cap reached: blank only, with its full log-probability
-        if (lane == 0) { cs[k * K] = h.score + (row[a.blank] - lse); cc[k * K] = a.blank; }
-      } else {
-        // the K best classes: each pass takes the best (value, class) after the previous one
-        float pv = INFINITY;
-        int pi = -1;
-        for (int r = 0; r < K; ++r) {
-          float bv = -INFINITY;
-          int bi = INT_MAX;
-#pragma unroll
-          for (int i = 0; i < BEAM_NV; ++i) {
-            const int col = lane + 64 * i;
-            const bool after = v[i] < pv || (v[i] == pv && col > pi);
-            if (after && v[i] > -INFINITY && better(v[i], col, bv, bi)) { bv = v[i]; bi = col; }
-          }
-          wave_best(bv, bi);
-          if (!(bv > -INFINITY)) break;
-          if (lane == 0) { cs[k * K + r] = h.score + (bv - lse); cc[k * K + r] = bi; }
-          pv = bv;
-          pi = bi;
-        }
-      }
-    }
-  }
-  __syncthreads();
-
   // the K best of all candidates (flat index k * K + rank: ties to the lower slot, then class)
   if (wave == 0) {
-    const float mine = cs[lane];
     bool taken = false;
     int cnt = 0;
     for (int r = 0; r < K; ++r) {
@@ -368,7 +417,7 @@ __global__ __launch_bounds__(512) void beam_select_kernel(BeamSelArgs a) {
 
   // recombination: pairs with equal length, last label and hash compare their tokens (a wave
   // per pair)
-  for (int pr = wave; pr < K * K; pr += K) {
+  for (int pr = wave; pr < K * K; pr += NWV) {
     const int i = pr / K, j = pr % K;
     if (i >= j || i >= nsel || j >= nsel) continue;
     const BeamSlot& x = sn[i];
@@ -560,6 +609,7 @@ bool beam_dims(const cac_beam_config* c, BeamDims& d, std::string& why) {
 struct BeamLayout {
   DecWeights w;
   size_t table, zrow, slots, tcur, tr, tlen, jlist, jcnt, psrc, pdst, ptok, pcnt, rounds, rnow, log, logits, zbuf;
+  size_t cand_s, cand_c;
   size_t ph, pc, pp, total;
   size_t entries, rounds_max, lrows;
 };
@@ -589,6 +639,8 @@ BeamLayout beam_layout(const BeamDims& d) {
   t.rnow = take(4);
   t.log = take((t.rounds_max + 1) * 2 * 4);
   t.logits = take(S * K * (size_t)d.Cpad * 4);
+  t.cand_s = take(S * 64 * 4);
+  t.cand_c = take(S * 64 * 4);
   t.zbuf = take(S * (size_t)d.T * P * 4);
   t.ph = take(t.entries * L * H * 4);
   t.pc = take(t.entries * L * H * 4);
@@ -707,8 +759,11 @@ void beam_rounds(cac_beam* c, Launcher& L, int n, int T, int r0, int count) {
     s.pcnt = c->P<int32_t>(y.pcnt); s.rounds = c->P<int32_t>(y.rounds); s.rnow = c->P<int32_t>(y.rnow);
     s.n = n; s.beam = d.K; s.C = d.C; s.Cpad = d.Cpad; s.U = d.U; s.blank = d.V; s.m = d.m; s.q = q; s.T = T;
     s.weak_hash = (d.flags & CAC_BEAM_FLAG_WEAK_HASH) ? 1 : 0;
+    s.cand_s = c->P<float>(y.cand_s); s.cand_c = c->P<int32_t>(y.cand_c);
+    L.tag("beam_cand", 0.0, 0.0);
+    L.launch((const void*)&beam_cand_kernel, dim3(n * d.K), dim3(64), 0, &s);
     L.tag("beam_select", 0.0, 0.0);
-    L.launch((const void*)&beam_select_kernel, dim3(n), dim3(64 * d.K), 0, &s);
+    L.launch((const void*)&beam_select_kernel, dim3(n), dim3(256), 0, &s);
     BeamTileArgs pt = base;
     pt.log = jt.log;
     beam_predictor(c, L, pt, c->P<int32_t>(y.pcnt), nk, j);
@@ -743,7 +798,7 @@ hipError_t beam_profile_fix(cac_beam* c, size_t first, int rounds) {
   if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
   if (e != hipSuccess) return e;
   std::vector<Profiler::Rec>& rec = c->prof.pending;
-  const size_t per = 2 + (size_t)d.L + 1;
+  const size_t per = 3 + (size_t)d.L + 1;
   if (rec.size() < first + 2 + (size_t)rounds * per) return hipSuccess;
   const double H = d.H, P = d.P, C = d.C;
   size_t i = first + 2;  // past begin and stage
@@ -757,6 +812,7 @@ hipError_t beam_profile_fix(cac_beam* c, size_t first, int rounds) {
   for (int j = 0; j < rounds; ++j) {
     const double jr = lg[2 * j], pr = lg[2 * j + 1];
     set("beam_joint", jr, 2.0 * P * C, P * d.Cpad * 4);
+    set("beam_cand", jr, 0.0, 0.0);
     set("beam_select", jr, 0.0, 0.0);
     for (int l = 0; l < d.L; ++l) set("beam_lstm", pr, 2.0 * (l ? 2 : 1) * H * 4 * H, (l ? 2 : 1) * H * 4 * H * 4);
     set("beam_proj", pr, 2.0 * H * P, H * P * 4);
