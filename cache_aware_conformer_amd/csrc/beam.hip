@@ -11,8 +11,8 @@
 // One iteration ("round") is six kernels:
 //   joint   - rows of the joint list (live hypotheses with frames left): ReLU(z[b][t] + p) Wout
 //             + bout into a logits row per slot (MFMA tiles, the predictor/joint tile loop);
-//   cand    - one wave per hypothesis: log_softmax and its top-K (or forced blank, or a final
-//             hypothesis offering itself);
+//   cand    - four waves per hypothesis: log_softmax and its top-K (or forced blank, or a
+//             final hypothesis offering itself);
 //   select  - one block per utterance: global top-K, new slots and transcripts, recombination,
 //             predictor entries for new labels, the next joint list (each entry the frame row,
 //             predictor entry and logits row it needs, so the joint reads no beam state);
@@ -231,100 +231,97 @@ __device__ __forceinline__ void wave_best(float& v, int& i) {
   i = mi < 2.0e9f ? (int)mi : INT_MAX;
 }
 
-// One wave per hypothesis (block = one wave, grid n * beam): its candidates. A live hypothesis
+// One block of four waves per hypothesis (grid n * beam): its candidates. A live hypothesis
 // with frames left takes log_softmax of its logits row; with labels left at its frame its
 // candidates are its K best classes (score + log-probability, ranked by logit then class),
 // else blank alone with the blank's log-probability; a final hypothesis offers itself; an empty
-// slot offers nothing.
-__global__ __launch_bounds__(64) void beam_cand_kernel(BeamSelArgs a) {
-  const int e = blockIdx.x, lane = threadIdx.x, K = a.beam;
+// slot offers nothing. The classes are dealt to the four waves (class lane + 64 (wave + 4 i)),
+// each wave finds its own K best, and the first wave merges the 4 K.
+constexpr int CAND_NV = BEAM_NV / 4;   // classes per lane and wave
+
+__global__ __launch_bounds__(256) void beam_cand_kernel(BeamSelArgs a) {
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, K = a.beam;
   const int b = e / K, k = e - b * K;
   const BeamSlot h = a.slots[((long)a.q * a.n + b) * K + k];
   const int T = a.tlen[b];
-  // the logits row, loaded with the slot (only used when this round's joint wrote it)
+  // this wave's share of the logits row, loaded with the slot (only used when this round's
+  // joint wrote the row)
   const float* row = a.logits + (long)e * a.Cpad;
-  float v[BEAM_NV];
+  float v[CAND_NV];
 #pragma unroll
-  for (int i = 0; i < BEAM_NV; ++i) {
-    const int col = lane + 64 * i;
+  for (int i = 0; i < CAND_NV; ++i) {
+    const int col = lane + 64 * (wave + 4 * i);
     v[i] = col < a.C ? row[col] : -INFINITY;
   }
+  __shared__ float red[4];
+  __shared__ float pv_s[4 * BEAM_MAX];
+  __shared__ int pc_s[4 * BEAM_MAX];
   float* cs = a.cand_s + (long)b * 64 + k * K;
   int32_t* cc = a.cand_c + (long)b * 64 + k * K;
-  float out_s = -INFINITY;
-  int out_c = -2;
-  if (h.score > -INFINITY && h.t >= T) {
-    if (lane == 0) { out_s = h.score; out_c = -1; }
-  } else if (h.score > -INFINITY) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < BEAM_NV; ++i) mx = fmaxf(mx, v[i]);
-    const float lmax = mx;   // this lane's largest logit
-    mx = wave_top(mx);
-    float sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < BEAM_NV; ++i) sum += v[i] > -INFINITY ? __expf(v[i] - mx) : 0.0f;
-    sum = wave_total(sum);
-    const float lse = mx + __logf(sum);
-    if (h.nsym >= a.m) {  // label cap reached: blank only, with its full log-probability
-      if (lane == 0) { out_s = h.score + (row[a.blank] - lse); out_c = a.blank; }
-    } else {
-      // The K best classes. Every one of them is at least theta, the K-th largest of the lanes'
-      // maxima (those are K distinct classes), so only classes >= theta take part: when no lane
-      // holds more than two of them, each lane keeps its (at most two) in registers and the K
-      // passes pop lane heads; otherwise every pass scans all of a lane's classes.
-      float tv = lmax;
-      int ti = lane;
-      float theta = -INFINITY;
-      for (int r = 0; r < K; ++r) {
-        float bv = tv;
-        int bi = ti;
-        wave_best(bv, bi);
-        if (!(bv > -INFINITY)) break;
-        theta = bv;
-        if (lane == bi) tv = -INFINITY;
-      }
-      int nc = 0;
-      float c0v = -INFINITY, c1v = -INFINITY;
-      int c0i = INT_MAX, c1i = INT_MAX;
-#pragma unroll
-      for (int i = 0; i < BEAM_NV; ++i) {
-        const int col = lane + 64 * i;
-        if (v[i] >= theta && v[i] > -INFINITY) {
-          // classes arrive in increasing order: keep the pair sorted by (logit desc, class asc)
-          if (nc == 0) { c0v = v[i]; c0i = col; }
-          else if (v[i] > c0v) { c1v = c0v; c1i = c0i; c0v = v[i]; c0i = col; }
-          else if (nc == 1 || v[i] > c1v) { c1v = v[i]; c1i = col; }
-          ++nc;
-        }
-      }
-      const bool fast = !__any(nc > 2);
-      float pv = INFINITY;
-      int pi = -1;
-      for (int r = 0; r < K; ++r) {
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-        if (fast) {
-          bv = c0v;
-          bi = c0i;
-        } else {
-#pragma unroll
-          for (int i = 0; i < BEAM_NV; ++i) {
-            const int col = lane + 64 * i;
-            const bool after = v[i] < pv || (v[i] == pv && col > pi);
-            if (after && v[i] > -INFINITY && better(v[i], col, bv, bi)) { bv = v[i]; bi = col; }
-          }
-        }
-        wave_best(bv, bi);
-        if (!(bv > -INFINITY)) break;
-        if (lane == r) { out_s = h.score + (bv - lse); out_c = bi; }
-        if (fast && c0i == bi) { c0v = c1v; c0i = c1i; c1v = -INFINITY; c1i = INT_MAX; }
-        pv = bv;
-        pi = bi;
-      }
+  const bool live = h.score > -INFINITY;
+  if (!live || h.t >= T) {   // block-uniform: an empty slot, or a final hypothesis offering itself
+    if (tid < K) {
+      cs[tid] = (live && tid == 0) ? h.score : -INFINITY;
+      cc[tid] = (live && tid == 0) ? -1 : -2;
     }
+    return;
   }
-  if (lane < K) { cs[lane] = out_s; cc[lane] = out_c; }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < CAND_NV; ++i) mx = fmaxf(mx, v[i]);
+  mx = wave_top(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  float sum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CAND_NV; ++i) sum += v[i] > -INFINITY ? __expf(v[i] - mx) : 0.0f;
+  sum = wave_total(sum);
+  __syncthreads();   // every wave has read the maxima
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  const float lse = mx + __logf((red[0] + red[1]) + (red[2] + red[3]));
+  if (h.nsym >= a.m) {  // label cap reached: blank only, with its full log-probability
+    if (tid < K) {
+      cs[tid] = tid == 0 ? h.score + (row[a.blank] - lse) : -INFINITY;
+      cc[tid] = tid == 0 ? a.blank : -2;
+    }
+    return;
+  }
+  // this wave's K best (logit desc, class asc): each pass takes the best after the previous one
+  float pv = INFINITY;
+  int pi = -1;
+  for (int r = 0; r < K; ++r) {
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < CAND_NV; ++i) {
+      const int col = lane + 64 * (wave + 4 * i);
+      const bool after = v[i] < pv || (v[i] == pv && col > pi);
+      if (after && v[i] > -INFINITY && better(v[i], col, bv, bi)) { bv = v[i]; bi = col; }
+    }
+    wave_best(bv, bi);
+    if (lane == 0) { pv_s[wave * K + r] = bv; pc_s[wave * K + r] = bi; }
+    pv = bv;
+    pi = bi;
+  }
+  __syncthreads();
+  // the first wave merges the four lists (one candidate per lane, its class as the tie index)
+  if (wave == 0) {
+    float mine = lane < 4 * K ? pv_s[lane] : -INFINITY;
+    const int cls = lane < 4 * K ? pc_s[lane] : INT_MAX;
+    float out_s = -INFINITY;
+    int out_c = -2;
+    for (int r = 0; r < K; ++r) {
+      float bv = mine > -INFINITY ? mine : -INFINITY;
+      int bi = mine > -INFINITY ? cls : INT_MAX;
+      wave_best(bv, bi);
+      if (!(bv > -INFINITY)) break;
+      if (lane == r) { out_s = h.score + (bv - lse); out_c = bi; }
+      if (cls == bi) mine = -INFINITY;
+    }
+    if (lane < K) { cs[lane] = out_s; cc[lane] = out_c; }
+  }
 }
 
 // One block of 256 threads per utterance: the global top-K of the candidates, new slots and
@@ -452,45 +449,55 @@ __global__ __launch_bounds__(256) void beam_select_kernel(BeamSelArgs a) {
   }
   __syncthreads();
 
-  if (tid == 0) {
-    // predictor entries for the new labels: the utterance's 2K entries minus those the old
-    // beam refers to; then one reservation on each work list
+  if (wave == 0) {
+    // Lane j < K finishes new slot j. Predictor entries for the new labels: the utterance's 2K
+    // entries minus those the old beam refers to, handed out in slot order; then one
+    // reservation on each work list, each slot's place in it from a prefix count of the lanes.
     const int base = POOL_BASE + b * 2 * K;
     uint32_t used = 0;
     for (int k = 0; k < K; ++k) {
       const int r = so[k].ref - base;
       if (r >= 0 && r < 2 * K) used |= 1u << r;
     }
-    int npred = 0, nact = 0;
-    int tok[BEAM_MAX], act[BEAM_MAX];
-    for (int j = 0; j < K; ++j) {
-      const bool live = j < nsel && merged[j] > -INFINITY;
-      const int c = j < nsel ? sel_cls[j] : -1;
-      tok[j] = live && c >= 0 && c != a.blank;
-      act[j] = live && sn[j].t < T;
-      npred += tok[j];
-      nact += act[j];
+    BeamSlot sj{};
+    bool tokj = false, actj = false;
+    int cj = -1;
+    if (lane < K) {
+      sj = sn[lane];
+      sj.score = merged[lane];
+      const bool live = lane < nsel && sj.score > -INFINITY;
+      cj = lane < nsel ? sel_cls[lane] : -1;
+      tokj = live && cj >= 0 && cj != a.blank;
+      actj = live && sj.t < T;
     }
-    const int p0 = npred ? atomicAdd(a.pcnt, npred) : 0;
-    const int a0 = nact ? atomicAdd(a.jcnt, nact) : 0;
-    int pi = p0, ai = a0;
-    for (int j = 0; j < K; ++j) {
-      BeamSlot s = sn[j];
-      s.score = merged[j];
-      if (tok[j]) {
-        const int e = __builtin_ctz(~used);
-        used |= 1u << e;
-        a.psrc[pi] = so[sel_par[j]].ref;
-        a.pdst[pi] = base + e;
-        a.ptok[pi] = sel_cls[j];
-        ++pi;
-        s.ref = base + e;
+    const uint64_t tm = __ballot(tokj), am = __ballot(actj);
+    const uint64_t below = (1ull << lane) - 1ull;
+    int p0 = 0, a0 = 0;
+    if (lane == 0) {
+      p0 = tm ? atomicAdd(a.pcnt, __popcll(tm)) : 0;
+      a0 = am ? atomicAdd(a.jcnt, __popcll(am)) : 0;
+    }
+    p0 = __shfl(p0, 0, 64);
+    a0 = __shfl(a0, 0, 64);
+    if (lane < K) {
+      if (tokj) {
+        // the rank-th entry (slot order) not used by the old beam
+        int rank = __popcll(tm & below), e = 0;
+        for (; e < 2 * BEAM_MAX - 1; ++e)   // found within the first 2K: the old beam uses at most K
+          if (!(used & (1u << e)) && rank-- == 0) break;
+        const int at = p0 + __popcll(tm & below);
+        a.psrc[at] = so[sel_par[lane]].ref;
+        a.pdst[at] = base + e;
+        a.ptok[at] = cj;
+        sj.ref = base + e;
       }
-      if (act[j]) a.jlist[ai++] = make_int4(b * a.T + s.t, s.ref, b * K + j, 0);
-      nw[j] = s;
+      if (actj) a.jlist[a0 + __popcll(am & below)] = make_int4(b * a.T + sj.t, sj.ref, b * K + lane, 0);
+      nw[lane] = sj;
     }
-    a.tcur[b] = par ^ 1;
-    atomicMax(a.rounds, *a.rnow);
+    if (lane == 0) {
+      a.tcur[b] = par ^ 1;
+      atomicMax(a.rounds, *a.rnow);
+    }
   }
 }
 
@@ -761,7 +768,7 @@ void beam_rounds(cac_beam* c, Launcher& L, int n, int T, int r0, int count) {
     s.weak_hash = (d.flags & CAC_BEAM_FLAG_WEAK_HASH) ? 1 : 0;
     s.cand_s = c->P<float>(y.cand_s); s.cand_c = c->P<int32_t>(y.cand_c);
     L.tag("beam_cand", 0.0, 0.0);
-    L.launch((const void*)&beam_cand_kernel, dim3(n * d.K), dim3(64), 0, &s);
+    L.launch((const void*)&beam_cand_kernel, dim3(n * d.K), dim3(256), 0, &s);
     L.tag("beam_select", 0.0, 0.0);
     L.launch((const void*)&beam_select_kernel, dim3(n), dim3(256), 0, &s);
     BeamTileArgs pt = base;
