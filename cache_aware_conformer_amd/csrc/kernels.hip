@@ -501,23 +501,32 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
 }
 
 // =============================================================================== MFMA GEMM (bf16)
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int CPOL_NT = 2;  // cache-policy bits of a vector memory load: non-temporal
+// Raw buffer resource over [p, p + bytes) (stride 0; word 3 = 32-bit data format): loads at byte
+// offsets at or past `bytes` return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_v;
 typedef __attribute__((ext_vector_type(16))) float f32x16_v;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_v;  // 16-byte staging register
 typedef __attribute__((ext_vector_type(4))) float f32x4_v;
 
-// Block tile BM x BN, k-step 64, 4 waves as WM x WN, each wave (BM/WM) x (BN/WN) made of
-// 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, 4 per k-step). Global loads run ST = 4 or 8
-// k-tiles ahead in rotating register sets (the k-loop is unrolled by ST so each set is a
-// compile-time register block), so a k-step waits for loads issued ST k-steps earlier
-// instead of one: at these tile sizes one k-step of MFMA is far shorter than a memory round
-// trip. Each k-step stores its register set into one of two LDS buffers (row stride 72 bf16:
-// 16-byte aligned, conflict-free fragment reads), passes the block's one barrier and
-// multiplies out of it. The epilogue kind is a template parameter; the accumulator tile goes
-// through LDS and every thread finishes 8 consecutive columns of a row with 16-byte accesses.
-// k-tiles in flight: 8 for 64x64 blocks (16 registers per set), 4 for larger blocks, whose
-// register sets are 2-3x bigger (8 there leaves one wave per SIMD and was measured slower)
-template <int BM, int BN> constexpr int mfma_stages() { return BM * BN <= 64 * 64 ? 8 : 4; }
+// Block tile BM x BN, k-step 64, KS groups of 4 waves; in a group the waves form WM x WN, each
+// (BM/WM) x (BN/WN) of 32x32 MFMA fragments (v_mfma_f32_32x32x16_bf16, 4 per k-step). Group g
+// takes k-steps [g KT/KS, (g+1) KT/KS) through its own ring of S stages in LDS. A stage holds
+// the A tile [BM][64] and then the W tile [BN][64], 128 bytes per row, with the 16-byte chunk c
+// of row r at chunk position c ^ ((r >> 1) & 7): the 16 rows that one quarter of an operand
+// read spans then fall on distinct banks. The stages are filled by direct buffer-to-LDS copies
+// (one wave instruction moves 8 rows, 1 KB), so operands never pass through registers: right
+// after the barrier of k-step kt the waves issue the copies of k-step kt + S - 1 into the stage
+// that k-step kt - 1 used, and S - 1 k-steps of operands are in flight while the MFMAs run. A
+// wave waits for its own copies of a stage (vmcnt), then the block barrier publishes them all.
+// More groups give a CU more waves when the tile grid alone has about one block per CU; their
+// partial tiles are summed in group order in the epilogue, so the result does not depend on
+// timing. The epilogue kind is a template parameter; the accumulator tiles go through LDS and
+// every thread finishes 8 consecutive columns of a row with 16-byte accesses.
 
 // Epilogue stores are non-temporal: the product's output is read by the next kernel, after the
 // kernel boundary has written the L2 back anyway, so streaming it past the L2 saves that
@@ -540,11 +549,16 @@ __device__ __forceinline__ void st_f8(float* p, const float* v) {
   __builtin_nontemporal_store(f32x4_v{v[4], v[5], v[6], v[7]}, (f32x4_v*)p + 1);
 }
 
-// Epilogue of 8 consecutive output columns col..col+7 of row `row` (v = accumulators).
+// Epilogue of 8 consecutive output columns col..col+7 of row `row` (v = accumulators). The
+// residual kinds take the row's x values and the biases loaded earlier (xp, bp).
 template <int EK>
-__device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, float* v) {
+__device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, float* v, const float* xp = nullptr,
+                                          const float* bp = nullptr) {
   const EpiArgs& e = a.epi;
-  if (e.bias) {
+  if (bp) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] += bp[q];
+  } else if (e.bias) {
     float b[8];
     ld_f8(e.bias + col, b);
 #pragma unroll
@@ -566,7 +580,12 @@ __device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, f
   } else if constexpr (EK == EPI_RESID || EK == EPI_RESID_KEEP) {
     float* x = (float*)e.out + (long)row * e.ldo + col;
     float r[8];
-    ld_f8(x, r);
+    if (xp) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) r[q] = xp[q];
+    } else {
+      ld_f8(x, r);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) r[q] += e.alpha * v[q];
     if constexpr (EK == EPI_RESID_KEEP) {
@@ -592,16 +611,39 @@ __device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, f
   }
 }
 
-template <int BM, int BN, int WM, int WN, int EK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_mfma_kernel(GemmArgs a) {
-  constexpr int BK = 64, LDK = BK + 8, ST = mfma_stages<BM, BN>();
+// s_waitcnt vmcnt(N): this wave's vector memory operations, direct LDS copies included, down
+// to the N most recent
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM, int BN, int KS>
+__device__ __forceinline__ void mfma_ct8(const float* ct, int idx, float* v) {
+  // 8 accumulator-tile values at idx of every group's tile, summed in group order
+  ld_f8(ct + idx, v);
+#pragma unroll
+  for (int g = 1; g < KS; ++g) {
+    float w[8];
+    ld_f8(ct + g * BM * (BN + 4) + idx, w);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] += w[q];
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int S, int KS, int EK>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 * KS))) void gemm_mfma_kernel(GemmArgs a) {
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr int A_PER_T = BM * (BK / 8) / 256, B_PER_T = BN * (BK / 8) / 256;
-  static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small");
-  static_assert(ST % 2 == 0, "the LDS buffer of a k-step is its set index mod 2");
-  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
-  // buffer b: A tile at lds + b * (BM + BN) * LDK, W tile right after it
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int SB = (BM + BN) * 128;        // bytes of one stage
+  constexpr int NA = BM / 32, NB = BN / 32;  // 1 KB copies of A and of W per wave and stage
+  static_assert(WM * WN == 4 && BM % 32 == 0 && BN % 32 == 0 && S >= 2, "tile shape");
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds8[];
+  // wave and group indices are wave-uniform: in scalar registers, so the copies' LDS bases and
+  // k offsets need no per-lane handling
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((tid >> 6) & 3), grp = __builtin_amdgcn_readfirstlane(tid >> 8);
   const int wm = wave / WN, wn = wave % WN;
   // XCD-aware tile order: workgroup L runs on XCD L mod 8, each with its own L2. With a.xrg
   // row groups (one k-range, tile grid divisible into 8 = a.xrg x (8 / a.xrg) rectangles) XCD x
@@ -626,40 +668,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     bm0 = (t / gx) * BM;
     bn0 = (t - (t / gx) * gx) * BN;
   }
-  // split-K (gridDim.z ranges, EPI_PART): this block's k-range starts at column k0
+  // split-K over blocks (gridDim.z ranges, EPI_PART): this block's k-range starts at column k0;
+  // within it, group grp takes k-steps kb .. kb + KT - 1
   const int M = a.M, N = a.N, K = a.K, Ks = K / (int)gridDim.z, k0 = kz * Ks;
-  const bf16_t* A = (const bf16_t*)a.A + k0;
-  const bf16_t* W = (const bf16_t*)a.W + k0;
-
-  const bf16_t* aptr[A_PER_T];
-  const bf16_t* bptr[B_PER_T];
-  int aoff[A_PER_T], boff[B_PER_T];
+  const int KT = Ks / 64 / KS, kb = grp * KT;
+  // byte offsets from A + k0 and W + k0 (the dispatch checks that they fit 31 bits); rows past
+  // the matrix read its last row, whose products land in rows or columns the epilogue skips
+  const __amdgpu_buffer_rsrc_t ar = raw_rsrc((const bf16_t*)a.A + k0, 0x7fffffff);
+  const __amdgpu_buffer_rsrc_t wr = raw_rsrc((const bf16_t*)a.W + k0, 0x7fffffff);
+  // copy i of wave w moves stage rows (4 i + w) * 8 .. + 7 of A (i < NA) or W (i < NB); its
+  // lane l takes row 8 (4 i + w) + l / 8 and the chunk stored at position l % 8
+  const int wv = wave;
+  unsigned char* ring = lds8 + grp * S * SB;
+  int voa[NA], vob[NB];
 #pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
-    aptr[i] = A + a.amap.off(min(bm0 + row, M - 1)) + kc;
-    aoff[i] = row * LDK + kc;
+  for (int i = 0; i < NA; ++i) {
+    const int rr = (4 * i + wave) * 8 + (lane >> 3), c = (lane & 7) ^ ((rr >> 1) & 7);
+    voa[i] = (int)(a.amap.off(min(bm0 + rr, M - 1)) * 2) + c * 16;
   }
 #pragma unroll
-  for (int i = 0; i < B_PER_T; ++i) {
-    const int c = tid + i * 256, row = c >> 3, kc = (c & 7) * 8;
-    bptr[i] = W + (long)min(bn0 + row, N - 1) * K + kc;
-    boff[i] = row * LDK + kc;
+  for (int i = 0; i < NB; ++i) {
+    const int rr = (4 * i + wave) * 8 + (lane >> 3), c = (lane & 7) ^ ((rr >> 1) & 7);
+    vob[i] = min(bn0 + rr, N - 1) * K * 2 + c * 16;
   }
-  u32x4_v ra[ST][A_PER_T], rb[ST][B_PER_T];
-#define MFMA_GLOAD(s, kt)                                                                         \
+  // (the offsets are copied to locals at the call: the builtin does not take an array element)
+#define MFMA_ISSUE(stage, kt)                                                                     \
   {                                                                                               \
-    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) ra[s][i] = *(const u32x4_v*)(aptr[i] + (kt) * BK); \
-    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) rb[s][i] = *(const u32x4_v*)(bptr[i] + (kt) * BK); \
+    const int so_ = (kt) * 128;                                                                   \
+    _Pragma("unroll") for (int i = 0; i < NA; ++i) {                                              \
+      const int vo_ = voa[i];                                                                     \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (lds_void_t*)(ring + (stage) * SB + (4 * i + wv) * 1024), 16, vo_, so_, 0, 0); \
+    }                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < NB; ++i) {                                              \
+      const int vo_ = vob[i];                                                                     \
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void_t*)(ring + (stage) * SB + BM * 128 + (4 * i + wv) * 1024), 16, vo_, so_, 0, 0); \
+    }                                                                                             \
   }
-#define MFMA_SSTORE(buf, s)                                                                       \
-  {                                                                                               \
-    bf16_t* Ab_ = lds + (buf) * (BM + BN) * LDK;                                                  \
-    bf16_t* Bb_ = Ab_ + BM * LDK;                                                                 \
-    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) *(u32x4_v*)(Ab_ + aoff[i]) = ra[s][i];     \
-    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) *(u32x4_v*)(Bb_ + boff[i]) = rb[s][i];     \
-  }
-
   f32x16_v acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -667,75 +711,112 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int KT = Ks / BK;
-  // k-tiles 0..ST-1 in flight (indices past the end reload the last tile: every load stays
-  // unconditional, so the compiler counts them in order)
+  // residual products: the x values (and biases) this thread's epilogue items update are loaded
+  // before the k-loop, so their memory latency hides behind it instead of following it
+  constexpr bool RES = EK == EPI_RESID || EK == EPI_RESID_KEEP;
+  constexpr int NT = 256 * KS, C8 = BN / 8, NIT8 = (BM * C8 + NT - 1) / NT;
+  float xpre[RES ? NIT8 : 1][8], bpre[RES ? NIT8 : 1][8];
+  if constexpr (RES) {
 #pragma unroll
-  for (int s = 0; s < ST; ++s) MFMA_GLOAD(s, min(s, KT - 1));
-  for (int kt0 = 0; kt0 < KT; kt0 += ST) {
+    for (int k = 0; k < NIT8; ++k) {
+      const int it = tid + NT * k, rr = it / C8, cc = (it - rr * C8) * 8;
+      const int row = min(bm0 + rr, M - 1), col = min(bn0 + cc, N - 8);
+      if (it < BM * C8) {
+        ld_f8((const float*)a.epi.out + (long)row * a.epi.ldo + col, xpre[k]);
+        if (a.epi.bias) ld_f8(a.epi.bias + col, bpre[k]);
+        else
 #pragma unroll
-    for (int s = 0; s < ST; ++s) {
-      const int kt = kt0 + s;
-      if (kt < KT) {
-        // the set holding k-tile kt goes to buffer s & 1 (read two k-steps ago, released by the
-        // barrier of the k-step in between), then reloads k-tile kt + ST
-        MFMA_SSTORE(s & 1, s);
-        __syncthreads();
-        MFMA_GLOAD(s, min(kt + ST, KT - 1));
-        const bf16_t* Ab = lds + (s & 1) * (BM + BN) * LDK;
-        const bf16_t* Bb = Ab + BM * LDK;
-#pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-          bf16x8_v af[FM], bfv[FN];
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-            af[i] = *(const bf16x8_v*)(Ab + (wm * TM + i * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            bfv[j] = *(const bf16x8_v*)(Bb + (wn * TN + j * 32 + (lane & 31)) * LDK + kk + (lane >> 5) * 8);
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
-        }
+          for (int q = 0; q < 8; ++q) bpre[k][q] = 0.0f;
       }
     }
   }
-#undef MFMA_GLOAD
-#undef MFMA_SSTORE
-  __syncthreads();  // every wave is done reading the k-tile buffers
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < KT) MFMA_ISSUE(s, kb + s);
+  // operand read offsets in a stage (bytes): lane l reads row l % 32 of a fragment, logical
+  // chunk 2 kk + l / 32 for the kk-th 16-k MFMA of the k-step
+  int aoffs[FM][4], boffs[FN][4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * TM + i * 32 + (lane & 31);
+      aoffs[i][kk] = r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * TN + j * 32 + (lane & 31);
+      boffs[j][kk] = BM * 128 + r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
+    }
+  }
+  int buf = 0;
+  for (int kt = 0; kt < KT; ++kt) {
+    // this wave's copies of k-step kt have landed (later stages may still be in flight) ...
+    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * (NA + NB)>();
+    else wait_vmcnt<0>();
+    // ... and every wave's, once all have passed the barrier; every wave has also finished
+    // reading the stage of k-step kt - 1, which the copies of k-step kt + S - 1 overwrite
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + S - 1 < KT) {
+      int nb = buf + S - 1;
+      nb -= nb >= S ? S : 0;
+      MFMA_ISSUE(nb, kb + kt + S - 1);
+    }
+    const unsigned char* st = ring + buf * SB;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8_v af[FM], bfv[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *(const bf16x8_v*)(st + aoffs[i][kk]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfv[j] = *(const bf16x8_v*)(st + boffs[j][kk]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+    }
+    asm volatile("" ::: "memory");
+    buf = buf + 1 == S ? 0 : buf + 1;
+  }
+#undef MFMA_ISSUE
+  __syncthreads();  // every copy has landed and every wave is done reading the stages
 
-  // The accumulator tile goes to LDS (fragment element r of a lane is row 8*(r/4) +
-  // 4*(lane/32) + r%4, column lane%32; all indices compile-time, so acc stays in registers),
-  // then each thread takes 8 consecutive columns of a row at a time.
+  // Each group's accumulator tile goes to its own LDS tile (fragment element r of a lane is row
+  // 8*(r/4) + 4*(lane/32) + r%4, column lane%32; all indices compile-time, so acc stays in
+  // registers), then each thread takes 8 consecutive columns of a row at a time.
   constexpr int CS = BN + 4;
-  float* ct = (float*)lds;
+  {
+    float* ctg = (float*)lds8 + grp * BM * CS;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ct[(wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * CS + wn * TN + j * 32 + (lane & 31)] = acc[i][j][r];
+        for (int r = 0; r < 16; ++r)
+          ctg[(wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * CS + wn * TN + j * 32 + (lane & 31)] = acc[i][j][r];
+  }
   __syncthreads();
+  const float* ct = (const float*)lds8;
   if constexpr (EK == EPI_GLU) {
     // packed columns: each 64-column block holds 32 value columns then their 32 gates; a thread
     // takes 8 channels (8 values, 8 gates) and writes them to the conv ring with one store
     const EpiArgs& e = a.epi;
     constexpr int G8 = BN / 16;  // 8-channel groups per tile row
-    static_assert(BM * G8 % 256 == 0, "whole items per thread");
+    constexpr int NIT = (BM * G8 + NT - 1) / NT;
 #pragma unroll
-    for (int k = 0; k < BM * G8 / 256; ++k) {
-      const int it = tid + 256 * k;
+    for (int k = 0; k < NIT; ++k) {
+      const int it = tid + NT * k;
+      if (it >= BM * G8) break;
       const int rr = it / G8, ch = (it - rr * G8) * 8;
       const int pc = (ch >> 5) * 64 + (ch & 31);
       const int row = bm0 + rr, c = bn0 / 2 + ch;
       if (row >= M || bn0 + pc >= N) continue;
       float va[8], vb[8], ba[8], bb[8];
-      ld_f8(ct + rr * CS + pc, va);
-      ld_f8(ct + rr * CS + pc + 32, vb);
+      mfma_ct8<BM, BN, KS>(ct, rr * CS + pc, va);
+      mfma_ct8<BM, BN, KS>(ct, rr * CS + pc + 32, vb);
       ld_f8(e.bias + c, ba);
       ld_f8(e.bias + e.D + c, bb);
       float g[8];
@@ -746,26 +827,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       st_bf8((bf16_t*)e.cring + ((long)e.cv.ids[s] * e.Rc + slot) * e.D + c, g);
     }
   } else {
-    constexpr int C8 = BN / 8;
-    static_assert(BM * C8 % 256 == 0, "whole items per thread");
 #pragma unroll
-    for (int k = 0; k < BM * C8 / 256; ++k) {
-      const int it = tid + 256 * k;
+    for (int k = 0; k < NIT8; ++k) {
+      const int it = tid + NT * k;
+      if (it >= BM * C8) break;
       const int rr = it / C8, cc = (it - rr * C8) * 8;
       const int row = bm0 + rr, col = bn0 + cc;
       if (row >= M || col >= N) continue;
       float v[8];
-      ld_f8(ct + rr * CS + cc, v);
+      mfma_ct8<BM, BN, KS>(ct, rr * CS + cc, v);
       if constexpr (EK == EPI_PART) st_f8((float*)a.epi.out + kz * a.epi.pstride + (long)row * a.epi.ldo + col, v);
+      else if constexpr (RES) mfma_epi8<EK>(a, row, col, v, xpre[k], bpre[k]);
       else mfma_epi8<EK>(a, row, col, v);
     }
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int S, int KS>
 constexpr size_t mfma_lds() {
-  // two k-tile buffers, reused afterwards for the float accumulator tile
-  return std::max((size_t)2 * (BM + BN) * (64 + 8) * sizeof(bf16_t), (size_t)BM * (BN + 4) * sizeof(float));
+  // KS rings of S stages, reused afterwards for KS float accumulator tiles
+  return std::max((size_t)KS * S * (BM + BN) * 128, (size_t)KS * BM * (BN + 4) * sizeof(float));
 }
 
 // =============================================================================== LayerNorm
@@ -1010,55 +1091,74 @@ static void gemv_dispatch(Launcher& L, const GemmArgs& a) {
   L.launch(fn, dim3((units + 4 * upw - 1) / (4 * upw), (a.M + MR - 1) / MR), dim3(256), shm, &args);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int S, int KS>
 static const void* mfma_pick_epi(int ek) {
   switch (ek) {
-    case EPI_STORE: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_STORE>;
-    case EPI_SILU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_SILU>;
-    case EPI_SILU_KEEP: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_SILU_KEEP>;
-    case EPI_RELU_FE: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RELU_FE>;
-    case EPI_RESID: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RESID>;
-    case EPI_RESID_KEEP: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_RESID_KEEP>;
-    case EPI_F32: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_F32>;
-    case EPI_QKV: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_QKV>;
-    case EPI_GLU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_GLU>;
-    case EPI_PART: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, EPI_PART>;
+    case EPI_STORE: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_STORE>;
+    case EPI_SILU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_SILU>;
+    case EPI_SILU_KEEP: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_SILU_KEEP>;
+    case EPI_RELU_FE: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_RELU_FE>;
+    case EPI_RESID: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_RESID>;
+    case EPI_RESID_KEEP: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_RESID_KEEP>;
+    case EPI_F32: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_F32>;
+    case EPI_QKV: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_QKV>;
+    case EPI_GLU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_GLU>;
+    case EPI_PART: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_PART>;
     default: return nullptr;
   }
 }
 
-// tile: 0 = chosen here; 1 = 128x128, 2 = 128x64, 3 = 64x128, 4 = 64x64 (test entry point)
+// The block tiles: shape, waves, stages and k-groups (stage counts measured at 2048 rows, K 512
+// and 2048, with operands that come from HBM rather than the caches)
+struct MfmaTile {
+  int bm, bn, groups;
+  const void* (*pick)(int);
+  size_t lds;
+};
+static const MfmaTile kMfmaTiles[7] = {
+    {0, 0, 0, nullptr, 0},
+    {128, 128, 1, &mfma_pick_epi<128, 128, 2, 2, 2, 1>, mfma_lds<128, 128, 2, 1>()},
+    {128, 64, 1, &mfma_pick_epi<128, 64, 4, 1, 3, 1>, mfma_lds<128, 64, 3, 1>()},
+    {64, 128, 1, &mfma_pick_epi<64, 128, 2, 2, 3, 1>, mfma_lds<64, 128, 3, 1>()},
+    {64, 64, 1, &mfma_pick_epi<64, 64, 2, 2, 3, 1>, mfma_lds<64, 64, 3, 1>()},
+    {64, 64, 2, &mfma_pick_epi<64, 64, 2, 2, 3, 2>, mfma_lds<64, 64, 3, 2>()},
+    {64, 64, 4, &mfma_pick_epi<64, 64, 2, 2, 2, 4>, mfma_lds<64, 64, 2, 4>()},
+};
+
+// tile: 0 = chosen here; 1 = 128x128, 2 = 128x64, 3 = 64x128, 4 = 64x64, 5 / 6 = 64x64 with its
+// k-steps split over 2 / 4 groups of waves (test entry point)
 static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   GemmArgs args = a;
   L.tag("gemm_mfma_bf16", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K);
   const int ks = std::max(a.ksplit, 1);
-  if (ks > 1 && (a.epi.kind != EPI_PART || a.K % (64 * ks))) {  // split-K writes partials only
+  auto fail = [&]() {
     if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
-    return;
-  }
+  };
+  if (ks > 1 && (a.epi.kind != EPI_PART || a.K % (64 * ks))) return fail();  // split-K writes partials only
+  // byte offsets of the operand copies are 32-bit: the A rows the row map reaches and all of W
+  const long amax = (long)((a.M - 1) / std::max(a.amap.group, 1)) * a.amap.group_stride +
+                    (long)(std::min(a.amap.group, a.M) - 1) * a.amap.row_stride + a.K;
+  if (a.M < 1 || a.N < 8 || a.N % 8 || a.K < 64 || amax * 2 >= (1L << 31) || (long)a.N * a.K * 2 >= (1L << 31)) return fail();
+  const int kt = a.K / 64 / ks;  // k-steps per block
   if (tile == 0) {
     // measured at 512 - 5120 rows (K 512 / 2048, N 512 - 2048): a larger tile pays from about
-    // 1.25 workgroups per CU (320 tiles); below that 64x64 (always with split-K, whose
-    // k-ranges add the blocks)
+    // 1.25 workgroups per CU (320 tiles), two stages of 128x128 then leaving room for two
+    // blocks per CU; below that 64x64 (always with split-K, whose k-ranges add the blocks),
+    // whose k-steps go to 2 groups of waves when there is about one tile per CU or fewer
+    // (2048 rows, operands from HBM, residual epilogue: 2048x512x512 8.7 -> 6.6 us,
+    // 2048x512x2048 16.7 -> 13.0 us against the register-staged kernel)
     if (ks == 1 && tiles(128, 128) >= 320) tile = 1;
     else if (ks == 1 && tiles(128, 64) >= 320) tile = 2;
+    else if (ks == 1 && tiles(64, 64) <= 256 && kt % 2 == 0) tile = 5;
     else tile = 4;
   }
-  const void* fn;
-  dim3 grid;
-  size_t shm;
-  switch (tile) {
-    case 1: fn = mfma_pick_epi<128, 128, 2, 2>(a.epi.kind); grid = dim3((a.N + 127) / 128, (a.M + 127) / 128); shm = mfma_lds<128, 128>(); break;
-    case 2: fn = mfma_pick_epi<128, 64, 4, 1>(a.epi.kind); grid = dim3((a.N + 63) / 64, (a.M + 127) / 128); shm = mfma_lds<128, 64>(); break;
-    case 3: fn = mfma_pick_epi<64, 128, 2, 2>(a.epi.kind); grid = dim3((a.N + 127) / 128, (a.M + 63) / 64); shm = mfma_lds<64, 128>(); break;
-    default: fn = mfma_pick_epi<64, 64, 2, 2>(a.epi.kind); grid = dim3((a.N + 63) / 64, (a.M + 63) / 64); shm = mfma_lds<64, 64>(); break;
-  }
-  if (!fn) {
-    if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
-    return;
-  }
-  grid.z = ks;
+  if (tile < 1 || tile > 6) return fail();
+  const MfmaTile& T = kMfmaTiles[tile];
+  if (kt % T.groups) return fail();  // every group takes the same number of k-steps
+  const void* fn = T.pick(a.epi.kind);
+  if (!fn) return fail();
+  dim3 grid((a.N + T.bn - 1) / T.bn, (a.M + T.bm - 1) / T.bm, ks);
   // XCD rectangles (one k-range, tile grid divisible): the row-group count whose rectangles
   // fetch the fewest A rows and W columns into the 8 L2s, taken when that is at most 60% of what
   // the contiguous runs fetch (each XCD: its rows of A, all of W). Measured: products whose
@@ -1066,17 +1166,16 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   // rows, savings of 20-33% made the 1024-stream step 0.5% slower. 0 keeps the contiguous runs.
   args.xrg = 0;
   if (ks == 1) {
-    const int bm = tile == 1 || tile == 2 ? 128 : 64, bn = tile == 1 || tile == 3 ? 128 : 64;
-    const long runs = (long)grid.y * bm + 8L * grid.x * bn;
+    const long runs = (long)grid.y * T.bm + 8L * grid.x * T.bn;
     long best = runs;
     for (int rg = 1; rg <= 8; rg *= 2) {
       const int cg = 8 / rg;
       if (grid.y % rg || grid.x % cg) continue;
-      const long cost = 8L * ((long)(grid.y / rg) * bm + (long)(grid.x / cg) * bn);
+      const long cost = 8L * ((long)(grid.y / rg) * T.bm + (long)(grid.x / cg) * T.bn);
       if (cost < best && 10 * cost <= 6 * runs) { best = cost; args.xrg = rg; }
     }
   }
-  L.launch(fn, grid, dim3(256), shm, &args);
+  L.launch(fn, grid, dim3(256 * T.groups), T.lds, &args);
 }
 
 __global__ __launch_bounds__(256) void cvt_kernel(CvtArgs a) {
@@ -1089,7 +1188,7 @@ __global__ __launch_bounds__(256) void cvt_kernel(CvtArgs a) {
 void launch_gemm(Launcher& L, const GemmArgs& a0, int dtype, int path) {
   GemmArgs a = a0;
   // only the MFMA kernel keeps its SiLU / residual rows in L2; the others store as usual
-  const bool mfma = dtype != DT_F32 && path != 1 && !(path == 0 && a.M <= 8) && a.K % 64 == 0;
+  const bool mfma = dtype != DT_F32 && path != 1 && !(path == 0 && (a.M <= 8 || a.N % 8 != 0)) && a.K % 64 == 0;
   if (a.epi.kind == EPI_SILU_KEEP && !mfma) a.epi.kind = EPI_SILU;
   if (a.epi.kind == EPI_RESID_KEEP && !mfma) a.epi.kind = EPI_RESID;
   if (path == 0 && rowdot_launch(L, a, dtype)) return;
@@ -1101,7 +1200,7 @@ void launch_gemm(Launcher& L, const GemmArgs& a0, int dtype, int path) {
     gemv_dispatch<float, float>(L, a);
     return;
   }
-  const bool small = path == 1 || (path == 0 && a.M <= 8) || a.K % 64 != 0;
+  const bool small = path == 1 || (path == 0 && (a.M <= 8 || a.N % 8 != 0)) || a.K % 64 != 0;
   if (small) {
     if (a.a_f32 && !a.a_dw) gemv_dispatch<bf16_t, float>(L, a);
     else gemv_dispatch<bf16_t, bf16_t>(L, a);
@@ -1128,7 +1227,8 @@ void launch_gemm(Launcher& L, const GemmArgs& a0, int dtype, int path) {
     g.a_f32 = 0;
     g.ln_g = g.ln_b = nullptr;
   }
-  mfma_dispatch(L, g, path >= 3 ? path - 2 : 0);
+  // paths 3..6: tiles 1..4; 9 / 10: tiles 5 / 6 (64x64 over 2 / 4 groups of waves)
+  mfma_dispatch(L, g, path >= 9 ? path - 4 : path >= 3 ? path - 2 : 0);
 }
 
 void launch_cvt(Launcher& L, const CvtArgs& a) {
@@ -1452,13 +1552,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   __builtin_amdgcn_wave_barrier();
-}
-typedef __attribute__((address_space(3))) void lds_void_t;
-constexpr int CPOL_NT = 2;  // cache-policy bits of a vector memory load: non-temporal
-// Raw buffer resource over [p, p + bytes) (stride 0; word 3 = 32-bit data format): loads at byte
-// offsets at or past `bytes` return zero instead of touching memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
 }
 
 // LDS of the MFMA attention kernel: V rows of NT 16-slot tiles, then the position terms of NR
@@ -2057,10 +2150,7 @@ void kernels_init() {
     }
   for (int ek : {EPI_STORE, EPI_SILU, EPI_SILU_KEEP, EPI_RELU_FE, EPI_RESID, EPI_RESID_KEEP, EPI_F32, EPI_QKV, EPI_GLU,
                  EPI_PART}) {
-    fns.push_back(mfma_pick_epi<128, 128, 2, 2>(ek));
-    fns.push_back(mfma_pick_epi<128, 64, 4, 1>(ek));
-    fns.push_back(mfma_pick_epi<64, 128, 2, 2>(ek));
-    fns.push_back(mfma_pick_epi<64, 64, 2, 2>(ek));
+    for (int t = 1; t <= 6; ++t) fns.push_back(kMfmaTiles[t].pick(ek));
   }
   for (const void* f : fns)
     if (f) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
