@@ -142,6 +142,11 @@ struct LayerOff {
   size_t ln[10];  // ff1 g,b  att g,b  conv g,b  ff2 g,b  out g,b
   size_t b_ff1_1, b_ff1_2, b_qkv, b_o, b_pw1, b_dw, b_pw2, b_ff2_1, b_ff2_2, pos_u, pos_v, dw_w, wpos;
   size_t w_ff1_1, w_ff1_2, w_qkv, w_o, w_pw1, w_pw2, w_ff2_1, w_ff2_2;
+  // bf16 weights: the products after the attention, conv and FF2 LayerNorms once more with the
+  // LayerNorm folded in (gain-scaled rows, and per output column c1 = sum of the row, c2 = sum
+  // of shift x weight + bias; pw1's c1, c2 in the bias order) for the rows that carry the
+  // LayerNorm through the products
+  size_t wg_qkv, c1_qkv, c2_qkv, wg_pw1, c1_pw1, c2_pw1, wg_ff2, c1_ff2, c2_ff2;
   size_t size;
 };
 
@@ -152,9 +157,13 @@ struct Layout {
   size_t f2_a1, f2_d2, f2_a2, f2_d3, f2_a3;
   size_t posproj, posproj_bf, kring, vring, cring, tail, x0, pos, pend;
   size_t ids, cids, cidx, sids, spos, spend, cpos, ccpos;
-  size_t x, x2, y, q, h, o, e, part, win, fe1, fe2;
+  size_t x, x2, y, q, h, o, e, part, lns_a, lns_b, lnm_a, lnm_b, win, fe1, fe2;
   size_t total;
 };
+
+// bf16 weights in the compute dtype with D in 64-column tiles (at most 16): the LayerNorms
+// before qkv, pw1 and FF2 up can ride on the products (see Pass::ln_carry)
+bool ln_fold(const Dims& d) { return d.dt == CAC_BF16 && !d.wq && d.D % 64 == 0 && d.D / 64 <= 16; }
 
 Layout make_layout(const Dims& d) {
   Layout t{};
@@ -171,6 +180,10 @@ Layout make_layout(const Dims& d) {
   lo.w_ff1_1 = b.take(d.wsz(F, D)); lo.w_ff1_2 = b.take(d.wsz(D, F)); lo.w_qkv = b.take(d.wsz(3 * D, D));
   lo.w_o = b.take(d.wsz(D, D)); lo.w_pw1 = b.take(d.wsz(2 * D, D)); lo.w_pw2 = b.take(d.wsz(D, D));
   lo.w_ff2_1 = b.take(d.wsz(F, D)); lo.w_ff2_2 = b.take(d.wsz(D, F));
+  const bool lnw = ln_fold(d);
+  lo.wg_qkv = b.take(lnw ? 3 * D * D * e : 0); lo.c1_qkv = b.take(lnw ? 3 * D * f4 : 0); lo.c2_qkv = b.take(lnw ? 3 * D * f4 : 0);
+  lo.wg_pw1 = b.take(lnw ? 2 * D * D * e : 0); lo.c1_pw1 = b.take(lnw ? 2 * D * f4 : 0); lo.c2_pw1 = b.take(lnw ? 2 * D * f4 : 0);
+  lo.wg_ff2 = b.take(lnw ? F * D * e : 0); lo.c1_ff2 = b.take(lnw ? F * f4 : 0); lo.c2_ff2 = b.take(lnw ? F * f4 : 0);
   lo.size = (b.take(0) + 255) & ~(size_t)255;
 
   Bump w;
@@ -206,6 +219,11 @@ Layout make_layout(const Dims& d) {
   t.h = w.take(M * F * e); t.o = w.take(M * D * e); t.e = w.take(M * D * e);
   // split-K partials of the residual products (bf16 MFMA path): up to 4 k-ranges
   if (d.dt == CAC_BF16) t.part = w.take(4 * M * D * f4);
+  // LayerNorm statistics carried through the products: two sets of [D / 64][M] (mean, M2)
+  if (ln_fold(d)) {
+    t.lns_a = w.take(D / 64 * M * 8); t.lns_b = w.take(D / 64 * M * 8);
+    t.lnm_a = w.take(M * f4); t.lnm_b = w.take(M * f4);
+  }
   if (d.fe) t.win = w.take(S * (d.tail + d.mpc) * d.bins * e);
   if (d.fe == 1) {
     t.fe1 = w.take(S * 11 * D * e);
@@ -270,6 +288,12 @@ uint16_t to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+float from_bf16(uint16_t h) {
+  const uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
 
 struct Packer {
   std::vector<uint8_t>& buf;
@@ -303,6 +327,21 @@ struct Packer {
   // in [K][N] row-major -> rows row0 .. row0+N-1 of the [rows][K] matrix at off
   void transpose(size_t off, const float* in, size_t K, size_t N, size_t row0 = 0) {
     for (size_t n = 0; n < N; ++n) column(off, in, K, N, n, row0 + n);
+  }
+  // LayerNorm (gains g, shifts b) folded into column n of in [K][N]: row `row` of the bf16
+  // matrix at off holds g[k] in[k][n] rounded; c1[ci] = the sum of that row as rounded,
+  // c2[ci] = sum_k b[k] in[k][n] + bias (float64 sums)
+  void ln_column(size_t off, size_t c1off, size_t c2off, const float* in, size_t K, size_t N, size_t n, size_t row,
+                 size_t ci, const float* g, const float* b, float bias) {
+    uint16_t* w = (uint16_t*)(buf.data() + off) + row * K;
+    double s1 = 0.0, s2 = bias;
+    for (size_t k = 0; k < K; ++k) {
+      w[k] = to_bf16(g[k] * in[k * N + n]);
+      s1 += (double)from_bf16(w[k]);
+      s2 += (double)b[k] * in[k * N + n];
+    }
+    ((float*)(buf.data() + c1off))[ci] = (float)s1;
+    ((float*)(buf.data() + c2off))[ci] = (float)s2;
   }
 };
 
@@ -428,7 +467,7 @@ struct Pass {
   // (y = cur when gn is null): split-K partials summed by the row kernel, or the product's
   // residual epilogue followed by the row kernel
   void resid_rows(const char* role, const void* A, int lda, const void* W, int K, float alpha, const float* bias,
-                  const float* go, const float* bo, const float* gn, const float* bn) {
+                  const float* go, const float* bo, const float* gn, const float* bn, float* mean = nullptr) {
     const Dims& d = c->d;
     const int ks = ksplit_for(d.D, K);
     GemmArgs g{};
@@ -446,8 +485,43 @@ struct Pass {
     L.role = role;
     launch_gemm(L, g, d.dt, 0);
     r.x = cur; r.go = go; r.bo = bo; r.gn = gn; r.bn = bn; r.y = c->P<void>(c->lay.y); r.M = M; r.D = d.D;
+    r.mean = mean;
     L.role = role;
     row_kernel(r);
+  }
+
+  // The LayerNorms before qkv, pw1 and FF2 up ride on the products (bf16 weights, from 2048
+  // rows, where the residual products run without split-K), which drops the three row kernels
+  // in front of them. The residual product before each (FF1 down, wo, pw2) updates x and also
+  // writes, per row, the (mean, M2) of each 64-column tile and the row centred on a shift s (the
+  // mean its previous statistics give) in bf16; the consumer multiplies those centred rows by
+  // the gain-scaled weights and finishes the LayerNorm in its epilogue:
+  //   LN(x) W^T + bias = rstd ((x - s) W'^T - (mean - s) c1) + c2.
+  // Rounding x - s rather than x keeps the operand's rounding error relative to the row's
+  // spread, as when the normalised row is rounded.
+  bool ln_carry() const {
+    const Dims& d = c->d;
+    return row_kernels() && keep_rows() && ln_fold(d) && ksplit_for(d.D, d.D) == 1 && ksplit_for(d.D, d.F) == 1;
+  }
+  // x += alpha (A W^T + bias), its tile statistics into st, the rows centred on the shifts to y
+  void resid_carry(const char* role, const void* A, int lda, const void* W, int K, float alpha, const float* bias,
+                   float2* st, const float* shift) {
+    const Dims& d = c->d;
+    GemmArgs g{};
+    g.M = M; g.N = d.D; g.K = K; g.A = A; g.W = W; g.amap = RowMap{INT_MAX, 0, lda};
+    EpiArgs e = epi0();
+    e.kind = EPI_RESID_LNS; e.bias = bias; e.out = cur; e.ldo = d.D; e.alpha = alpha;
+    e.lns = st; e.lns_shift = shift; e.lns_ld = M; e.lns_ntl = d.D / 64; e.xc = c->P<void>(c->lay.y);
+    g.epi = e;
+    L.role = role;
+    launch_gemm(L, g, d.dt, 0);
+  }
+  // a consumer of centred rows: LayerNorm finished from st (statistics) and shift; the rows'
+  // means go to mean (the next residual product's shifts)
+  EpiArgs carried(EpiArgs e, const float* c1, const float* c2, const float2* st, const float* shift, float* mean) const {
+    e.kind |= EPI_LNC; e.bias = nullptr; e.lnc_c1 = c1; e.lnc_c2 = c2;
+    e.lns = const_cast<float2*>(st); e.lns_shift = shift; e.lns_mean = mean; e.lns_ld = M; e.lns_ntl = c->d.D / 64;
+    return e;
   }
 
   void layers() {
@@ -462,6 +536,7 @@ struct Pass {
       ResLnArgs r{};
       r.x = cur; r.gn = (const float*)(l0 + lo.ln[0]); r.bn = (const float*)(l0 + lo.ln[1]);
       r.y = c->P<void>(c->lay.y); r.M = M; r.D = d.D;
+      if (ln_carry()) r.mean = c->P<float>(c->lay.lnm_a);
       L.role = "ln_in";
       row_kernel(r);
     }
@@ -602,6 +677,13 @@ struct Pass {
     const LayerOff& lo = c->lay.lo;
     auto F32 = [&](size_t off) { return (const float*)(lb + off); };
     void* y = c->P<void>(c->lay.y);
+    // with the LayerNorms carried: tile statistics sets sa / sb and row-mean sets ma / mb
+    // alternate (on entry ma holds the row means the last row kernel wrote)
+    const bool lc = ln_carry();
+    float2* sa = lc ? c->P<float2>(c->lay.lns_a) : nullptr;
+    float2* sb = lc ? c->P<float2>(c->lay.lns_b) : nullptr;
+    float* ma = lc ? c->P<float>(c->lay.lnm_a) : nullptr;
+    float* mb = lc ? c->P<float>(c->lay.lnm_b) : nullptr;
     // ---- FF1 (macaron half step)
     EpiArgs up = epi0();
     up.kind = EPI_SILU; up.bias = F32(lo.b_ff1_1); up.out = c->P<void>(c->lay.h); up.ldo = d.F;
@@ -611,35 +693,42 @@ struct Pass {
     if (M >= 4096) up.kind = EPI_SILU_KEEP;
     L.role = "ff1_up";
     gemm_plain(y, d.D, lb + lo.w_ff1_1, d.F, d.D, up);
-    resid_rows("ff1_down", c->P<void>(c->lay.h), d.F, lb + lo.w_ff1_2, d.F, 0.5f, F32(lo.b_ff1_2), nullptr, nullptr,
-               F32(lo.ln[2]), F32(lo.ln[3]));
+    if (lc) resid_carry("ff1_down", c->P<void>(c->lay.h), d.F, lb + lo.w_ff1_2, d.F, 0.5f, F32(lo.b_ff1_2), sb, ma);
+    else resid_rows("ff1_down", c->P<void>(c->lay.h), d.F, lb + lo.w_ff1_2, d.F, 0.5f, F32(lo.b_ff1_2), nullptr, nullptr,
+                    F32(lo.ln[2]), F32(lo.ln[3]));
     // ---- MHSA
     EpiArgs qkv = epi0();
     qkv.kind = EPI_QKV; qkv.bias = F32(lo.b_qkv); qkv.qbuf = c->P<float>(c->lay.q);
     qkv.kring = kr; qkv.vring = vr;
     L.role = "qkv";
-    gemm_plain(y, d.D, lb + lo.w_qkv, 3 * d.D, d.D, qkv);
+    if (lc) gemm_plain(y, d.D, lb + lo.wg_qkv, 3 * d.D, d.D, carried(qkv, F32(lo.c1_qkv), F32(lo.c2_qkv), sb, ma, mb));
+    else gemm_plain(y, d.D, lb + lo.w_qkv, 3 * d.D, d.D, qkv);
     attention(l, lb, kr, vr);
-    resid_rows("wo", c->P<void>(c->lay.o), d.D, lb + lo.w_o, d.D, 1.0f, F32(lo.b_o), nullptr, nullptr, F32(lo.ln[4]),
-               F32(lo.ln[5]));
+    if (lc) resid_carry("wo", c->P<void>(c->lay.o), d.D, lb + lo.w_o, d.D, 1.0f, F32(lo.b_o), sa, mb);
+    else resid_rows("wo", c->P<void>(c->lay.o), d.D, lb + lo.w_o, d.D, 1.0f, F32(lo.b_o), nullptr, nullptr, F32(lo.ln[4]),
+                    F32(lo.ln[5]));
     // ---- conv module: pw1 -> GLU into the ring; depthwise + SiLU; pw2
     EpiArgs glu = epi0();
     glu.kind = EPI_GLU; glu.bias = F32(lo.b_pw1); glu.cring = cr;
     L.role = "pw1";
-    gemm_plain(y, d.D, lb + lo.w_pw1, 2 * d.D, d.D, glu);
+    if (lc) gemm_plain(y, d.D, lb + lo.wg_pw1, 2 * d.D, d.D, carried(glu, F32(lo.c1_pw1), F32(lo.c2_pw1), sa, mb, ma));
+    else gemm_plain(y, d.D, lb + lo.w_pw1, 2 * d.D, d.D, glu);
     DwArgs dw{cv, cr, F32(lo.dw_w), F32(lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
     L.tag("dwconv", (double)cv.n_streams * (d.Kc + cv.nf) * d.D * d.esz, 2.0 * d.K * d.D * M);
     launch_dwconv(L, dw, d.dt);
-    resid_rows("pw2", c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, 1.0f, F32(lo.b_pw2), nullptr, nullptr,
-               F32(lo.ln[6]), F32(lo.ln[7]));
+    if (lc) resid_carry("pw2", c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, 1.0f, F32(lo.b_pw2), sb, ma);
+    else resid_rows("pw2", c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, 1.0f, F32(lo.b_pw2), nullptr, nullptr,
+                    F32(lo.ln[6]), F32(lo.ln[7]));
     // ---- FF2 (macaron half step), then ln_out
     up.bias = F32(lo.b_ff2_1);
     L.role = "ff2_up";
-    gemm_plain(y, d.D, lb + lo.w_ff2_1, d.F, d.D, up);
+    if (lc) gemm_plain(y, d.D, lb + lo.wg_ff2, d.F, d.D, carried(up, F32(lo.c1_ff2), F32(lo.c2_ff2), sb, ma, mb));
+    else gemm_plain(y, d.D, lb + lo.w_ff2_1, d.F, d.D, up);
     const bool last = l + 1 == d.L;
     const char* nb = lb + lo.size;  // next block's parameters
     resid_rows("ff2_down", c->P<void>(c->lay.h), d.F, lb + lo.w_ff2_2, d.F, 0.5f, F32(lo.b_ff2_2), F32(lo.ln[8]),
-               F32(lo.ln[9]), last ? nullptr : (const float*)(nb + lo.ln[0]), last ? nullptr : (const float*)(nb + lo.ln[1]));
+               F32(lo.ln[9]), last ? nullptr : (const float*)(nb + lo.ln[0]), last ? nullptr : (const float*)(nb + lo.ln[1]),
+               lc && !last ? ma : nullptr);
   }
 
   // encoder-side joint projection of the rows picked by amap into d_out (rows remapped by omap)
@@ -771,6 +860,7 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
   const float* p = h_params;
   const size_t D = d.D, F = d.F;
   auto take = [&](size_t n) { const float* r = p; p += n; return r; };
+  const bool lnw = ln_fold(d);
   for (int l = 0; l < d.L; ++l) {
     const size_t base = lay.layers + (size_t)l * lay.lo.size;
     const LayerOff& lo = lay.lo;
@@ -780,25 +870,42 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
       pk.rows = D; pk.transpose(base + w2, take(F * D), F, D); pk.f32(base + b2, take(D), D);
     };
     ffp(0, lo.b_ff1_1, lo.b_ff1_2, lo.w_ff1_1, lo.w_ff1_2);
-    pk.f32(base + lo.ln[2], take(D), D); pk.f32(base + lo.ln[3], take(D), D);
+    const float* g_att = take(D);
+    const float* b_att = take(D);
+    pk.f32(base + lo.ln[2], g_att, D); pk.f32(base + lo.ln[3], b_att, D);
     pk.rows = 3 * D;
     for (int m = 0; m < 3; ++m) {  // wq, wk, wv stacked as rows of [3D][D]
-      pk.transpose(base + lo.w_qkv, take(D * D), D, D, (size_t)m * D);
-      pk.f32(base + lo.b_qkv + (size_t)m * D * 4, take(D), D);
+      const float* w = take(D * D);
+      const float* bias = take(D);
+      pk.transpose(base + lo.w_qkv, w, D, D, (size_t)m * D);
+      pk.f32(base + lo.b_qkv + (size_t)m * D * 4, bias, D);
+      if (lnw)
+        for (size_t n = 0; n < D; ++n)
+          pk.ln_column(base + lo.wg_qkv, base + lo.c1_qkv, base + lo.c2_qkv, w, D, D, n, m * D + n, m * D + n, g_att,
+                       b_att, bias[n]);
     }
     pk.rows = D; pk.transpose(base + lo.w_o, take(D * D), D, D); pk.f32(base + lo.b_o, take(D), D);
     pk.f32(base + lo.pos_u, take(D), D); pk.f32(base + lo.pos_v, take(D), D);
     pk.f32(base + lo.wpos, take(D * D), D * D);
-    pk.f32(base + lo.ln[4], take(D), D); pk.f32(base + lo.ln[5], take(D), D);
+    const float* g_conv = take(D);
+    const float* b_conv = take(D);
+    pk.f32(base + lo.ln[4], g_conv, D); pk.f32(base + lo.ln[5], b_conv, D);
     {  // pw1 [D][2D] -> GLU-packed rows: value channel c at glu_a_col(c), its gate 32 rows later
       const float* w = take(D * 2 * D);
+      const float* bias = take(2 * D);
       pk.rows = 2 * D;
       for (size_t ch = 0; ch < D; ++ch) {
         const size_t ra = glu_a_col((int)ch), rb = ra + 32;
         pk.column(base + lo.w_pw1, w, D, 2 * D, ch, ra);
         pk.column(base + lo.w_pw1, w, D, 2 * D, D + ch, rb);
+        if (lnw) {
+          pk.ln_column(base + lo.wg_pw1, base + lo.c1_pw1, base + lo.c2_pw1, w, D, 2 * D, ch, ra, ch, g_conv, b_conv,
+                       bias[ch]);
+          pk.ln_column(base + lo.wg_pw1, base + lo.c1_pw1, base + lo.c2_pw1, w, D, 2 * D, D + ch, rb, D + ch, g_conv,
+                       b_conv, bias[D + ch]);
+        }
       }
-      pk.f32(base + lo.b_pw1, take(2 * D), 2 * D);
+      pk.f32(base + lo.b_pw1, bias, 2 * D);
     }
     {  // dw [D][K] -> taps [K][D]
       const float* w = take(D * d.K);
@@ -808,6 +915,14 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
       pk.f32(base + lo.b_dw, take(D), D);
     }
     pk.rows = D; pk.transpose(base + lo.w_pw2, take(D * D), D, D); pk.f32(base + lo.b_pw2, take(D), D);
+    if (lnw) {  // FF2 up with its LayerNorm folded in: its parameters come next in the array
+      const float* g_ff2 = p;
+      const float* b_ff2 = p + D;
+      const float* w = p + 2 * D;
+      const float* bias = w + D * F;
+      for (size_t n = 0; n < F; ++n)
+        pk.ln_column(base + lo.wg_ff2, base + lo.c1_ff2, base + lo.c2_ff2, w, D, F, n, n, n, g_ff2, b_ff2, bias[n]);
+    }
     ffp(6, lo.b_ff2_1, lo.b_ff2_2, lo.w_ff2_1, lo.w_ff2_2);
     pk.f32(base + lo.ln[8], take(D), D); pk.f32(base + lo.ln[9], take(D), D);
   }

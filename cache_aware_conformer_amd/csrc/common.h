@@ -139,6 +139,12 @@ enum EpiKind {
   EPI_SILU_KEEP = 9,  // EPI_SILU with write-back stores that leave the rows in L2 (MFMA kernel;
                       // the other kernels take it as EPI_SILU)
   EPI_RESID_KEEP = 10,  // EPI_RESID likewise
+  EPI_RESID_LNS = 11,   // EPI_RESID_KEEP that also writes what the next LayerNorm needs (MFMA
+                        // kernel, 64-column tiles): the rows centred on a per-row shift in the
+                        // compute dtype (xc) and each row's (mean, M2) over every 64-column tile
+  EPI_LNC = 0x100,      // flag on EPI_SILU(_KEEP) / EPI_QKV / EPI_GLU (MFMA kernel): A holds the
+                        // centred rows, W the gain-scaled weights, and the epilogue finishes the
+                        // LayerNorm from the tile statistics before the kind's own work
 };
 
 // GLU packing of the pointwise-1 weight rows: packed row (c / 32) * 64 + c % 32 holds value
@@ -165,6 +171,21 @@ struct EpiArgs {
   void* vring;
   void* cring;          // [S][Rc][D] of this layer (compute dtype)
   int D, H, hd, R, Rc;
+  // LayerNorm carried through the products (EPI_RESID_LNS writes, EPI_LNC reads):
+  //   lns[t * lns_ld + m] = (mean, sum of squared deviations) of row m's columns 64 t .. 64 t + 63
+  //   lns_shift[m] = the shift s_m the centred rows xc[m] = x[m] - s_m were taken around (the
+  //     row's mean before the residual update)
+  // and the consumer's output column n is rstd (acc - (mean - s) c1[n]) + c2[n] with
+  // c1[n] = sum_k w'[n][k] of its gain-scaled weights w'[n][k] = g[k] w[n][k] and
+  // c2[n] = sum_k b[k] w[n][k] + bias[n] (for GLU in the bias order: values, then gates); its
+  // blocks of the first column tile also write each row's mean to lns_mean (the next shift)
+  float2* lns;
+  const float* lns_shift;
+  float* lns_mean;
+  int lns_ld, lns_ntl;
+  void* xc;               // EPI_RESID_LNS: [M][ldo] centred rows (compute dtype)
+  const float* lnc_c1;
+  const float* lnc_c2;
 };
 
 // ------------------------------------------------------------------------ kernel args
@@ -220,6 +241,8 @@ struct ResLnArgs {
   void* y;            // [M][D] compute dtype (null: not written)
   int M, D;
   int keep;           // rows in XCD-contiguous eighths and y by write-back stores (see the kernel)
+  float* mean;        // mean[m] = mean of the final x row (null: not written): the shift the
+                      // next residual product centres its rows around
 };
 
 struct AttnArgs {

@@ -639,6 +639,9 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   constexpr int SB = (BM + BN) * 128;        // bytes of one stage
   constexpr int NA = BM / 32, NB = BN / 32;  // 1 KB copies of A and of W per wave and stage
   static_assert(WM * WN == 4 && BM % 32 == 0 && BN % 32 == 0 && S >= 2, "tile shape");
+  constexpr int EB = EK & 0xff;  // the kind without the EPI_LNC flag
+  constexpr bool LNC = (EK & EPI_LNC) != 0, LNS = EB == EPI_RESID_LNS;
+  static_assert(!LNS || BN == 64, "tile statistics cover one 64-column tile per block");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds8[];
   // wave and group indices are wave-uniform: in scalar registers, so the copies' LDS bases and
   // k offsets need no per-lane handling
@@ -711,11 +714,14 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  // residual products: the x values (and biases) this thread's epilogue items update are loaded
-  // before the k-loop, so their memory latency hides behind it instead of following it
-  constexpr bool RES = EK == EPI_RESID || EK == EPI_RESID_KEEP;
+  // Operands of the epilogue are loaded before the k-loop, so their memory latency hides behind
+  // it instead of following it: residual products load the x values (and biases, and with
+  // EPI_RESID_LNS the row shifts) their items update; EPI_LNC products load their rows' tile
+  // statistics and shifts (thread t < BM: row t) and their columns' c1, c2 (thread t < BN).
+  constexpr bool RES = EB == EPI_RESID || EB == EPI_RESID_KEEP || LNS;
   constexpr int NT = 256 * KS, C8 = BN / 8, NIT8 = (BM * C8 + NT - 1) / NT;
-  float xpre[RES ? NIT8 : 1][8], bpre[RES ? NIT8 : 1][8];
+  constexpr int RI = RES ? NIT8 : 1, LT = LNC ? 16 : 1;
+  float xpre[RI][8], bpre[RI][8], spre[RI];
   if constexpr (RES) {
 #pragma unroll
     for (int k = 0; k < NIT8; ++k) {
@@ -727,7 +733,28 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
         else
 #pragma unroll
           for (int q = 0; q < 8; ++q) bpre[k][q] = 0.0f;
+        if constexpr (LNS) spre[k] = a.epi.lns_shift[row];
       }
+    }
+  }
+  float2 lst[LT];
+  float lsh = 0.0f, lc1 = 0.0f, lc2 = 0.0f;
+  if constexpr (LNC) {
+    const EpiArgs& e = a.epi;
+    if (tid < BM) {
+      const int row = min(bm0 + tid, M - 1);
+#pragma unroll
+      for (int t = 0; t < LT; ++t) lst[t] = t < e.lns_ntl ? e.lns[t * e.lns_ld + row] : make_float2(0.0f, 0.0f);
+      lsh = e.lns_shift[row];
+    }
+    if (tid < BN) {
+      int idx = min(bn0 + tid, N - 1);
+      if constexpr (EB == EPI_GLU) {  // packed column -> value channel c, or its gate at D + c
+        const int ch = (idx >> 6) * 32 + (idx & 31);
+        idx = (idx & 63) >= 32 ? e.D + ch : ch;
+      }
+      lc1 = e.lnc_c1[idx];
+      lc2 = e.lnc_c2[idx];
     }
   }
 #pragma unroll
@@ -788,6 +815,29 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   // 8*(r/4) + 4*(lane/32) + r%4, column lane%32; all indices compile-time, so acc stays in
   // registers), then each thread takes 8 consecutive columns of a row at a time.
   constexpr int CS = BN + 4;
+  // EPI_LNC: per row (rstd, -rstd (mean - shift)) and per column (c1, c2) after the tiles
+  float2* lnrow = (float2*)((float*)lds8 + KS * BM * CS);
+  float2* lncol = lnrow + BM;
+  if constexpr (LNC) {
+    if (tid < BM) {  // combine the row's 64-column tiles (Chan et al.'s pairwise update)
+      const int ntl = a.epi.lns_ntl;
+      float mean = 0.0f;
+#pragma unroll
+      for (int t = 0; t < LT; ++t) mean += t < ntl ? lst[t].x : 0.0f;
+      mean /= (float)ntl;
+      float m2 = 0.0f;
+#pragma unroll
+      for (int t = 0; t < LT; ++t)
+        if (t < ntl) {
+          const float d = lst[t].x - mean;
+          m2 += lst[t].y + 64.0f * d * d;
+        }
+      const float rstd = rsqrtf(m2 / (float)(64 * ntl) + 1e-5f);
+      lnrow[tid] = make_float2(rstd, -rstd * (mean - lsh));
+      if (bn0 == 0 && bm0 + tid < M) a.epi.lns_mean[bm0 + tid] = mean;
+    }
+    if (tid < BN) lncol[tid] = make_float2(lc1, lc2);
+  }
   {
     float* ctg = (float*)lds8 + grp * BM * CS;
 #pragma unroll
@@ -800,7 +850,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   }
   __syncthreads();
   const float* ct = (const float*)lds8;
-  if constexpr (EK == EPI_GLU) {
+  if constexpr (EB == EPI_GLU) {
     // packed columns: each 64-column block holds 32 value columns then their 32 gates; a thread
     // takes 8 channels (8 values, 8 gates) and writes them to the conv ring with one store
     const EpiArgs& e = a.epi;
@@ -817,8 +867,20 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
       float va[8], vb[8], ba[8], bb[8];
       mfma_ct8<BM, BN, KS>(ct, rr * CS + pc, va);
       mfma_ct8<BM, BN, KS>(ct, rr * CS + pc + 32, vb);
-      ld_f8(e.bias + c, ba);
-      ld_f8(e.bias + e.D + c, bb);
+      if constexpr (LNC) {  // LayerNorm finished; c2 holds the biases
+        const float2 lr = lnrow[rr];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float2 ca = lncol[pc + q], cb = lncol[pc + 32 + q];
+          va[q] = lr.x * va[q] + lr.y * ca.x;
+          vb[q] = lr.x * vb[q] + lr.y * cb.x;
+          ba[q] = ca.y;
+          bb[q] = cb.y;
+        }
+      } else {
+        ld_f8(e.bias + c, ba);
+        ld_f8(e.bias + e.D + c, bb);
+      }
       float g[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) g[q] = (va[q] + ba[q]) * sigmoid_f(vb[q] + bb[q]);
@@ -836,17 +898,56 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
       if (row >= M || col >= N) continue;
       float v[8];
       mfma_ct8<BM, BN, KS>(ct, rr * CS + cc, v);
-      if constexpr (EK == EPI_PART) st_f8((float*)a.epi.out + kz * a.epi.pstride + (long)row * a.epi.ldo + col, v);
-      else if constexpr (RES) mfma_epi8<EK>(a, row, col, v, xpre[k], bpre[k]);
-      else mfma_epi8<EK>(a, row, col, v);
+      if constexpr (LNC) {  // LayerNorm finished (c2 holds the bias; the kind adds none)
+        const float2 lr = lnrow[rr];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float2 cl = lncol[cc + q];
+          v[q] = lr.x * v[q] + lr.y * cl.x + cl.y;
+        }
+      }
+      if constexpr (EB == EPI_PART) {
+        st_f8((float*)a.epi.out + kz * a.epi.pstride + (long)row * a.epi.ldo + col, v);
+      } else if constexpr (LNS) {
+        // x += alpha (acc + b), streamed (its next reader is the next residual product); this
+        // row's 64 columns of the tile sit on 8 neighbouring lanes (items it .. it + 7), which
+        // form the tile's (mean, M2) and write the row centred on its shift, kept in the L2 of
+        // the XCD whose blocks of the consumer read the same rows
+        const EpiArgs& e = a.epi;
+        float r[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) r[q] = xpre[k][q] + e.alpha * (v[q] + bpre[k][q]);
+        st_f8((float*)e.out + (long)row * e.ldo + col, r);
+        float sum = ((r[0] + r[1]) + (r[2] + r[3])) + ((r[4] + r[5]) + (r[6] + r[7]));
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        const float mt = sum * (1.0f / 64.0f);
+        float m2 = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) m2 += (r[q] - mt) * (r[q] - mt);
+        m2 += __shfl_xor(m2, 1);
+        m2 += __shfl_xor(m2, 2);
+        m2 += __shfl_xor(m2, 4);
+        if ((tid & 7) == 0) e.lns[(col >> 6) * e.lns_ld + row] = make_float2(mt, m2);
+        float c8[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) c8[q] = r[q] - spre[k];
+        st_bf8_keep((bf16_t*)e.xc + (long)row * e.ldo + col, c8);
+      } else if constexpr (RES) {
+        mfma_epi8<EB>(a, row, col, v, xpre[k], bpre[k]);
+      } else {
+        mfma_epi8<EB>(a, row, col, v);
+      }
     }
   }
 }
 
 template <int BM, int BN, int S, int KS>
 constexpr size_t mfma_lds() {
-  // KS rings of S stages, reused afterwards for KS float accumulator tiles
-  return std::max((size_t)KS * S * (BM + BN) * 128, (size_t)KS * BM * (BN + 4) * sizeof(float));
+  // KS rings of S stages, reused afterwards for KS float accumulator tiles and the LayerNorm
+  // row and column terms of EPI_LNC
+  return std::max((size_t)KS * S * (BM + BN) * 128, (size_t)KS * BM * (BN + 4) * sizeof(float) + (BM + BN) * 8);
 }
 
 // =============================================================================== LayerNorm
@@ -979,6 +1080,13 @@ __global__ __launch_bounds__(256) void resid_ln_kernel(ResLnArgs a) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) *(f32x4_v*)(x + (j * 64 + lane) * 4) = xv[j];
   }
+  if (a.mean) {  // the row's mean: the shift the next residual product centres around
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) sum += (xv[j].x + xv[j].y) + (xv[j].z + xv[j].w);
+    sum = wave_total(sum);
+    if (lane == 0) a.mean[row] = sum * inv_d;
+  }
   if (a.y) {
     if (a.gn) row_layernorm<NV>(xv, gnv, bnv, inv_d);
     TO* y = (TO*)a.y + ro;
@@ -1037,7 +1145,7 @@ double gemm_bytes(const GemmArgs& a, int wsz) {
   double b = (double)a.N * a.K * wsz + (wsz == 1 ? 4.0 * a.N : 0.0);
   const double esz = wsz == 1 ? 4.0 : (double)wsz;
   if (a.a_dw) b += (double)a.epi.cv.n_streams * (a.dw_taps - 1 + a.epi.cv.nf) * a.K * esz;
-  switch (a.epi.kind) {
+  switch (a.epi.kind & 0xff) {
     case EPI_QKV: b += (double)a.M * 2.0 * a.epi.D * esz; break;
     case EPI_GLU: b += (double)a.M * (a.N / 2) * esz; break;
     case EPI_GLU_DW:  // ring rows written and the older ring rows the conv reads
@@ -1104,6 +1212,13 @@ static const void* mfma_pick_epi(int ek) {
     case EPI_QKV: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_QKV>;
     case EPI_GLU: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_GLU>;
     case EPI_PART: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_PART>;
+    case EPI_SILU | EPI_LNC: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_SILU | EPI_LNC>;
+    case EPI_SILU_KEEP | EPI_LNC: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_SILU_KEEP | EPI_LNC>;
+    case EPI_QKV | EPI_LNC: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_QKV | EPI_LNC>;
+    case EPI_GLU | EPI_LNC: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_GLU | EPI_LNC>;
+    case EPI_RESID_LNS:
+      if constexpr (BN == 64) return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_RESID_LNS>;
+      return nullptr;
     default: return nullptr;
   }
 }
@@ -1140,6 +1255,10 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   const long amax = (long)((a.M - 1) / std::max(a.amap.group, 1)) * a.amap.group_stride +
                     (long)(std::min(a.amap.group, a.M) - 1) * a.amap.row_stride + a.K;
   if (a.M < 1 || a.N < 8 || a.N % 8 || a.K < 64 || amax * 2 >= (1L << 31) || (long)a.N * a.K * 2 >= (1L << 31)) return fail();
+  const bool lns = a.epi.kind == EPI_RESID_LNS, lnc = (a.epi.kind & EPI_LNC) != 0;
+  if ((lns || lnc) && (ks > 1 || !a.epi.lns || !a.epi.lns_shift || a.epi.lns_ntl < 1 || a.epi.lns_ntl > 16)) return fail();
+  if (lns && (a.N % 64 || a.N / 64 != a.epi.lns_ntl || !a.epi.xc)) return fail();
+  if (lnc && (!a.epi.lnc_c1 || !a.epi.lnc_c2 || !a.epi.lns_mean || a.K != 64 * a.epi.lns_ntl)) return fail();
   const int kt = a.K / 64 / ks;  // k-steps per block
   if (tile == 0) {
     // measured at 512 - 5120 rows (K 512 / 2048, N 512 - 2048): a larger tile pays from about
@@ -1154,6 +1273,7 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
     else tile = 4;
   }
   if (tile < 1 || tile > 6) return fail();
+  if (lns && kMfmaTiles[tile].bn != 64) tile = tiles(128, 64) >= 320 ? 2 : 4;  // one 64-column tile per block
   const MfmaTile& T = kMfmaTiles[tile];
   if (kt % T.groups) return fail();  // every group takes the same number of k-steps
   const void* fn = T.pick(a.epi.kind);
@@ -1191,6 +1311,10 @@ void launch_gemm(Launcher& L, const GemmArgs& a0, int dtype, int path) {
   const bool mfma = dtype != DT_F32 && path != 1 && !(path == 0 && (a.M <= 8 || a.N % 8 != 0)) && a.K % 64 == 0;
   if (a.epi.kind == EPI_SILU_KEEP && !mfma) a.epi.kind = EPI_SILU;
   if (a.epi.kind == EPI_RESID_KEEP && !mfma) a.epi.kind = EPI_RESID;
+  if ((a.epi.kind == EPI_RESID_LNS || (a.epi.kind & EPI_LNC)) && !mfma) {  // the MFMA kernel's kinds only
+    if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
+    return;
+  }
   if (path == 0 && rowdot_launch(L, a, dtype)) return;
   if (a.epi.kind == EPI_GLU_DW || dtype == DT_I8W) {  // only the two-row kernel has these
     if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
@@ -2148,8 +2272,9 @@ void kernels_init() {
       fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 2>(kch, glu));
       fns.push_back(gemv_pick_kch<bf16_t, bf16_t, 8>(kch, glu));
     }
-  for (int ek : {EPI_STORE, EPI_SILU, EPI_SILU_KEEP, EPI_RELU_FE, EPI_RESID, EPI_RESID_KEEP, EPI_F32, EPI_QKV, EPI_GLU,
-                 EPI_PART}) {
+  for (int ek : {(int)EPI_STORE, (int)EPI_SILU, (int)EPI_SILU_KEEP, (int)EPI_RELU_FE, (int)EPI_RESID, (int)EPI_RESID_KEEP,
+                 (int)EPI_F32, (int)EPI_QKV, (int)EPI_GLU, (int)EPI_PART, (int)EPI_RESID_LNS, EPI_SILU | EPI_LNC,
+                 EPI_SILU_KEEP | EPI_LNC, EPI_QKV | EPI_LNC, EPI_GLU | EPI_LNC}) {
     for (int t = 1; t <= 6; ++t) fns.push_back(kMfmaTiles[t].pick(ek));
   }
   for (const void* f : fns)
