@@ -1997,11 +1997,52 @@ __global__ __launch_bounds__(256) void fe_window_kernel(FeWindowArgs a) {
   for (int r = 0; r < nn; ++r) win[(long)(nt + r) * a.bins] = mel[(long)r * a.bins];
   for (int r = 0; r < nt; ++r) tail[(long)r * a.bins] = win[(long)(rows - nt + r) * a.bins];
 }
+// The same with one thread per (call stream, 16 bytes of bins) for windows of at most FW_MAXR
+// rows: every row is loaded into registers before any is stored, so the tail rows this thread
+// reads are read before it overwrites them, and all loads share one memory round trip (the
+// per-bin kernel pays one per row).
+constexpr int FW_MAXR = 32;
+template <typename T>
+__global__ __launch_bounds__(256) void fe_window_vec_kernel(FeWindowArgs a) {
+  constexpr int E = 16 / sizeof(T);
+  const int nch = a.bins / E;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.cv.n_streams * nch) return;
+  const int s = idx / nch, ch = idx - s * nch;
+  const int id = a.cv.ids[s];
+  const int pos = a.cv.pos[id];
+  const bool fresh = pos == 0;
+  if (ch == 0) a.cv.cpos[s] = pos;
+  const int nt = a.mel_tail, nn = a.mel_new, rows = nt + nn;
+  u32x4_v* tail = (u32x4_v*)((T*)a.tail + (long)id * nt * a.bins) + ch;
+  const u32x4_v* mel = (const u32x4_v*)((const T*)a.mel + (long)s * nn * a.bins) + ch;
+  u32x4_v* win = (u32x4_v*)((T*)a.win + (long)s * rows * a.bins) + ch;
+  u32x4_v v[FW_MAXR];
+#pragma unroll
+  for (int r = 0; r < FW_MAXR; ++r) {
+    if (r < nt) v[r] = fresh ? u32x4_v{0u, 0u, 0u, 0u} : tail[r * nch];
+    else if (r < rows) v[r] = mel[(r - nt) * nch];
+  }
+#pragma unroll
+  for (int r = 0; r < FW_MAXR; ++r)
+    if (r < rows) win[r * nch] = v[r];
+#pragma unroll
+  for (int r = 0; r < FW_MAXR; ++r)  // the last nt rows of the window become the tail
+    if (r < rows && r >= rows - nt) tail[(r - (rows - nt)) * nch] = v[r];
+}
+
 void launch_fe_window(Launcher& L, const FeWindowArgs& a, int dtype) {
   FeWindowArgs args = a;
+  const int esz = dtype == DT_F32 ? 4 : 2;
+  L.tag("fe_window", (double)a.cv.n_streams * (a.mel_new + 2 * a.mel_tail) * a.bins * esz, 0.0);
+  if ((a.bins * esz) % 16 == 0 && a.mel_tail + a.mel_new <= FW_MAXR) {
+    const int total = a.cv.n_streams * (a.bins * esz / 16);
+    const void* fn = dtype == DT_F32 ? (const void*)&fe_window_vec_kernel<float> : (const void*)&fe_window_vec_kernel<bf16_t>;
+    L.launch(fn, dim3((total + 255) / 256), dim3(256), 0, &args);
+    return;
+  }
   const int total = a.cv.n_streams * a.bins;
   const void* fn = dtype == DT_F32 ? (const void*)&fe_window_kernel<float> : (const void*)&fe_window_kernel<bf16_t>;
-  L.tag("fe_window", (double)a.cv.n_streams * (a.mel_new + 2 * a.mel_tail) * a.bins * (dtype == DT_F32 ? 4 : 2), 0.0);
   L.launch(fn, dim3((total + 255) / 256), dim3(256), 0, &args);
 }
 
