@@ -553,7 +553,8 @@ __device__ __forceinline__ void st_f8(float* p, const float* v) {
 // residual kinds take the row's x values and the biases loaded earlier (xp, bp).
 template <int EK>
 __device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, float* v, const float* xp = nullptr,
-                                          const float* bp = nullptr) {
+                                          const float* bp = nullptr, const int* meta = nullptr) {
+  // meta (loaded earlier): the row's stream position and id (EPI_QKV), or position (EPI_RELU_FE)
   const EpiArgs& e = a.epi;
   if (bp) {
 #pragma unroll
@@ -573,7 +574,7 @@ __device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, f
     else st_bf8((bf16_t*)e.out + (long)row * e.ldo + col, v);
   } else if constexpr (EK == EPI_RELU_FE) {
     const int s = row / e.fe_rows_per_stream, j = row - s * e.fe_rows_per_stream;
-    const bool before_start = e.cv.cpos[s] == 0 && j < e.fe_neg_rows;
+    const bool before_start = (meta ? meta[0] : e.cv.cpos[s]) == 0 && j < e.fe_neg_rows;
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = before_start ? 0.0f : fmaxf(v[q], 0.0f);
     st_bf8((bf16_t*)e.out + (long)row * e.ldo + col, v);
@@ -603,10 +604,11 @@ __device__ __forceinline__ void mfma_epi8(const GemmArgs& a, int row, int col, f
       st_f8(e.qbuf + (long)row * e.D + c, v);
     } else {
       const int s = row / e.cv.nf, i = row - s * e.cv.nf;
-      const int slot = (e.cv.cpos[s] + i) % e.R;
+      const int slot = ((meta ? meta[0] : e.cv.cpos[s]) + i) % e.R;
+      const int id = meta ? meta[1] : e.cv.ids[s];
       const int lg = 31 - __clz(e.hd);  // head sizes are powers of two; 8 columns stay in one head
       bf16_t* ring = (bf16_t*)(which == 1 ? e.kring : e.vring);
-      st_bf8(ring + (((long)e.cv.ids[s] * e.H + (c >> lg)) * e.R + slot) * e.hd + (c & (e.hd - 1)), v);
+      st_bf8(ring + (((long)id * e.H + (c >> lg)) * e.R + slot) * e.hd + (c & (e.hd - 1)), v);
     }
   }
 }
@@ -718,22 +720,53 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   // it instead of following it: residual products load the x values (and biases, and with
   // EPI_RESID_LNS the row shifts) their items update; EPI_LNC products load their rows' tile
   // statistics and shifts (thread t < BM: row t) and their columns' c1, c2 (thread t < BN).
+  // The other kinds load their items' biases, and the QKV and front-end kinds their rows'
+  // stream positions and ids, the same way (GLU: per 8-channel item, both halves' biases).
   constexpr bool RES = EB == EPI_RESID || EB == EPI_RESID_KEEP || LNS;
+  constexpr bool PB = !LNC && EB != EPI_PART && EB != EPI_GLU, PM = EB == EPI_QKV || EB == EPI_RELU_FE;
   constexpr int NT = 256 * KS, C8 = BN / 8, NIT8 = (BM * C8 + NT - 1) / NT;
-  constexpr int RI = RES ? NIT8 : 1, LT = LNC ? 16 : 1;
-  float xpre[RI][8], bpre[RI][8], spre[RI];
-  if constexpr (RES) {
+  constexpr int G8 = BN / 16, NITG = (BM * G8 + NT - 1) / NT;  // GLU: 8-channel items
+  constexpr int RI = RES ? NIT8 : 1, BI = PB ? NIT8 : 1, MI = PM ? NIT8 : EB == EPI_GLU ? NITG : 1;
+  constexpr int GI = EB == EPI_GLU && !LNC ? NITG : 1, LT = LNC ? 16 : 1;
+  float xpre[RI][8], bpre[BI][8], spre[RI], gpre[GI][16];
+  int mpre[MI][2];
+  if constexpr (RES || PB || PM) {
 #pragma unroll
     for (int k = 0; k < NIT8; ++k) {
       const int it = tid + NT * k, rr = it / C8, cc = (it - rr * C8) * 8;
       const int row = min(bm0 + rr, M - 1), col = min(bn0 + cc, N - 8);
       if (it < BM * C8) {
-        ld_f8((const float*)a.epi.out + (long)row * a.epi.ldo + col, xpre[k]);
-        if (a.epi.bias) ld_f8(a.epi.bias + col, bpre[k]);
-        else
-#pragma unroll
-          for (int q = 0; q < 8; ++q) bpre[k][q] = 0.0f;
+        if constexpr (RES) ld_f8((const float*)a.epi.out + (long)row * a.epi.ldo + col, xpre[k]);
         if constexpr (LNS) spre[k] = a.epi.lns_shift[row];
+        if constexpr (PB) {
+          if (a.epi.bias) ld_f8(a.epi.bias + col, bpre[k]);
+          else
+#pragma unroll
+            for (int q = 0; q < 8; ++q) bpre[k][q] = 0.0f;
+        }
+        if constexpr (EB == EPI_QKV) {
+          const int st = row / a.epi.cv.nf;
+          mpre[k][0] = a.epi.cv.cpos[st];
+          mpre[k][1] = a.epi.cv.ids[st];
+        } else if constexpr (EB == EPI_RELU_FE) {
+          mpre[k][0] = a.epi.cv.cpos[row / a.epi.fe_rows_per_stream];
+        }
+      }
+    }
+  }
+  if constexpr (EB == EPI_GLU) {
+#pragma unroll
+    for (int k = 0; k < NITG; ++k) {
+      const int it = tid + NT * k, rr = it / G8, ch = (it - rr * G8) * 8;
+      const int row = min(bm0 + rr, M - 1), c = min(bn0 / 2 + ch, a.epi.D - 8);
+      if (it < BM * G8) {
+        const int st = row / a.epi.cv.nf;
+        mpre[k][0] = a.epi.cv.cpos[st];
+        mpre[k][1] = a.epi.cv.ids[st];
+        if constexpr (!LNC) {
+          ld_f8(a.epi.bias + c, gpre[k]);
+          ld_f8(a.epi.bias + a.epi.D + c, gpre[k] + 8);
+        }
       }
     }
   }
@@ -854,10 +887,8 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
     // packed columns: each 64-column block holds 32 value columns then their 32 gates; a thread
     // takes 8 channels (8 values, 8 gates) and writes them to the conv ring with one store
     const EpiArgs& e = a.epi;
-    constexpr int G8 = BN / 16;  // 8-channel groups per tile row
-    constexpr int NIT = (BM * G8 + NT - 1) / NT;
 #pragma unroll
-    for (int k = 0; k < NIT; ++k) {
+    for (int k = 0; k < NITG; ++k) {
       const int it = tid + NT * k;
       if (it >= BM * G8) break;
       const int rr = it / G8, ch = (it - rr * G8) * 8;
@@ -878,15 +909,18 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
           bb[q] = cb.y;
         }
       } else {
-        ld_f8(e.bias + c, ba);
-        ld_f8(e.bias + e.D + c, bb);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          ba[q] = gpre[k][q];
+          bb[q] = gpre[k][8 + q];
+        }
       }
       float g[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) g[q] = (va[q] + ba[q]) * sigmoid_f(vb[q] + bb[q]);
       const int s = row / e.cv.nf, i = row - s * e.cv.nf;
-      const int slot = (e.cv.cpos[s] + i) % e.Rc;
-      st_bf8((bf16_t*)e.cring + ((long)e.cv.ids[s] * e.Rc + slot) * e.D + c, g);
+      const int slot = (mpre[k][0] + i) % e.Rc;
+      st_bf8((bf16_t*)e.cring + ((long)mpre[k][1] * e.Rc + slot) * e.D + c, g);
     }
   } else {
 #pragma unroll
@@ -936,6 +970,12 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
         st_bf8_keep((bf16_t*)e.xc + (long)row * e.ldo + col, c8);
       } else if constexpr (RES) {
         mfma_epi8<EB>(a, row, col, v, xpre[k], bpre[k]);
+      } else if constexpr (PB && PM) {
+        mfma_epi8<EB>(a, row, col, v, nullptr, bpre[k], mpre[k]);
+      } else if constexpr (PB) {
+        mfma_epi8<EB>(a, row, col, v, nullptr, bpre[k]);
+      } else if constexpr (PM) {
+        mfma_epi8<EB>(a, row, col, v, nullptr, nullptr, mpre[k]);
       } else {
         mfma_epi8<EB>(a, row, col, v);
       }
