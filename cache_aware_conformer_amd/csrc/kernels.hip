@@ -2133,11 +2133,95 @@ __global__ __launch_bounds__(256) void fe2d_kernel(Fe2dArgs a) {
   st_bf8((bf16_t*)a.out + (((long)s * a.Tout + r) * a.Fout + f) * a.C + c0, acc);
 }
 
+// The same stages with one thread per (stream, output row, FE2D_FG consecutive output columns,
+// 8 channels): the 9 taps' weights are loaded once for the thread's FE2D_FG outputs, and the
+// input pixels its outputs share (stride 2, width 3) once; threads of one pixel group differ
+// in their channels only. Needs Fout a multiple of FE2D_FG.
+constexpr int FE2D_FG = 4;
+template <bool CIN1>
+__global__ __launch_bounds__(256) void fe2d_group_kernel(Fe2dArgs a) {
+  constexpr int FG = FE2D_FG, NIC = 2 * FG + 1;  // input columns 2 f0 - 1 .. 2 f0 + 2 FG - 1
+  const int c8 = a.C / 8, fgs = a.Fout / FG;
+  long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const long total = (long)a.cv.n_streams * a.Tout * fgs * c8;
+  if (idx >= total) return;
+  const int cg = (int)(idx % c8);
+  idx /= c8;
+  const int f0 = (int)(idx % fgs) * FG;
+  idx /= fgs;
+  const int r = (int)(idx % a.Tout);
+  const int s = (int)(idx / a.Tout);
+  const int c0 = cg * 8;
+  float w[9][8], acc[FG][8];
+#pragma unroll
+  for (int t = 0; t < 9; ++t) ld_f8(a.w + (long)t * a.C + c0, w[t]);
+  {
+    float b[8];
+    ld_f8(a.b + c0, b);
+#pragma unroll
+    for (int o = 0; o < FG; ++o)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[o][q] = b[q];
+  }
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    const long rowbase = (long)s * a.Tin + 2 * r + i;
+    if constexpr (CIN1) {
+      float v[NIC];
+#pragma unroll
+      for (int j = 0; j < NIC; ++j) {
+        const int col = 2 * f0 - 1 + j;
+        v[j] = (col >= 0 && col < a.Fin) ? bf2f(((const bf16_t*)a.in)[rowbase * a.Fin + col]) : 0.0f;
+      }
+#pragma unroll
+      for (int o = 0; o < FG; ++o)
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[o][q] += w[i * 3 + j][q] * v[2 * o + j];
+    } else {
+      u32x4_v raw[NIC];
+#pragma unroll
+      for (int j = 0; j < NIC; ++j) {
+        const int col = 2 * f0 - 1 + j;
+        raw[j] = (col >= 0 && col < a.Fin) ? *(const u32x4_v*)((const bf16_t*)a.in + (rowbase * a.Fin + col) * a.C + c0)
+                                           : u32x4_v{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int o = 0; o < FG; ++o)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+          const u32x4_v u = raw[2 * o + j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[o][2 * q] += w[i * 3 + j][2 * q] * __uint_as_float(u[q] << 16);
+            acc[o][2 * q + 1] += w[i * 3 + j][2 * q + 1] * __uint_as_float(u[q] & 0xffff0000u);
+          }
+        }
+    }
+  }
+  const bool zero = CIN1 && a.cv.cpos[s] == 0 && r < a.neg;
+#pragma unroll
+  for (int o = 0; o < FG; ++o) {
+    if constexpr (CIN1) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[o][q] = zero ? 0.0f : fmaxf(acc[o][q], 0.0f);
+    }
+    st_bf8((bf16_t*)a.out + (((long)s * a.Tout + r) * a.Fout + f0 + o) * a.C + c0, acc[o]);
+  }
+}
+
 void launch_fe2d(Launcher& L, const Fe2dArgs& a) {
   Fe2dArgs args = a;
-  const long total = (long)a.cv.n_streams * a.Tout * a.Fout * (a.C / 8);
   const double outb = (double)a.cv.n_streams * a.Tout * a.Fout * a.C * 2.0;
   L.tag(a.cin1 ? "fe2d_conv1" : "fe2d_depthwise", 0.0, 2.0 * 9.0 * outb / 2.0);
+  if (a.Fout % FE2D_FG == 0 && a.C % 8 == 0) {
+    const long total = (long)a.cv.n_streams * a.Tout * (a.Fout / FE2D_FG) * (a.C / 8);
+    const void* fn = a.cin1 ? (const void*)&fe2d_group_kernel<true> : (const void*)&fe2d_group_kernel<false>;
+    L.launch(fn, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
+    return;
+  }
+  const long total = (long)a.cv.n_streams * a.Tout * a.Fout * (a.C / 8);
   L.launch((const void*)&fe2d_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
 }
 
