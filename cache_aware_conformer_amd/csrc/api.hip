@@ -1517,8 +1517,8 @@ int test_gemm_ranges(int32_t dtype, int32_t path, int32_t M, int32_t N, int32_t 
   auto bad = [](const char* m) { g_create_error = m; return CAC_EINVAL; };
   if (dtype != CAC_F32 && dtype != CAC_BF16) return bad("dtype must be CAC_F32 or CAC_BF16");
   if (M < 1 || N < 1 || K < 1 || !d_A || !d_W || !d_C) return bad("empty shape or NULL pointer");
-  if (path < 0 || path > 10 || (path >= 2 && dtype != CAC_BF16)) return bad("path out of range for this dtype");
-  if (path >= 9 && K % (path == 9 ? 128 : 256)) return bad("paths 9 / 10 need K a multiple of 128 / 256");
+  if (path < 0 || path > 12 || (path >= 2 && dtype != CAC_BF16)) return bad("path out of range for this dtype");
+  if (path >= 9 && K % (path == 10 ? 256 : 128)) return bad("paths 9, 11, 12 / 10 need K a multiple of 128 / 256");
   if (path >= 2 && K % 64) return bad("MFMA paths need K a multiple of 64");  // MFMA tiles step K by 64
   if (path >= 2 && N % 8) return bad("MFMA paths need N a multiple of 8");   // 8-column epilogue items
   if ((size_t)8 * K * 4 > 160 * 1024 && path < 2) return bad("K too large for the small-M kernel");

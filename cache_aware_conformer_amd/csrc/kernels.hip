@@ -1270,7 +1270,7 @@ struct MfmaTile {
   const void* (*pick)(int);
   size_t lds;
 };
-static const MfmaTile kMfmaTiles[7] = {
+static const MfmaTile kMfmaTiles[9] = {
     {0, 0, 0, nullptr, 0},
     {128, 128, 1, &mfma_pick_epi<128, 128, 2, 2, 2, 1>, mfma_lds<128, 128, 2, 1>()},
     {128, 64, 1, &mfma_pick_epi<128, 64, 4, 1, 3, 1>, mfma_lds<128, 64, 3, 1>()},
@@ -1278,10 +1278,13 @@ static const MfmaTile kMfmaTiles[7] = {
     {64, 64, 1, &mfma_pick_epi<64, 64, 2, 2, 3, 1>, mfma_lds<64, 64, 3, 1>()},
     {64, 64, 2, &mfma_pick_epi<64, 64, 2, 2, 3, 2>, mfma_lds<64, 64, 3, 2>()},
     {64, 64, 4, &mfma_pick_epi<64, 64, 2, 2, 2, 4>, mfma_lds<64, 64, 2, 4>()},
+    {128, 128, 2, &mfma_pick_epi<128, 128, 2, 2, 2, 2>, mfma_lds<128, 128, 2, 2>()},
+    {128, 96, 2, &mfma_pick_epi<128, 96, 4, 1, 2, 2>, mfma_lds<128, 96, 2, 2>()},
 };
 
 // tile: 0 = chosen here; 1 = 128x128, 2 = 128x64, 3 = 64x128, 4 = 64x64, 5 / 6 = 64x64 with its
-// k-steps split over 2 / 4 groups of waves (test entry point)
+// k-steps split over 2 / 4 groups of waves, 7 / 8 = 128x128 / 128x96 over 2 groups (test
+// entry point)
 static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   GemmArgs args = a;
@@ -1307,13 +1310,21 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
     // whose k-steps go to 2 groups of waves when there is about one tile per CU or fewer
     // (2048 rows, operands from HBM, residual epilogue: 2048x512x512 8.7 -> 6.6 us,
     // 2048x512x2048 16.7 -> 13.0 us against the register-staged kernel)
+    // A column count that 128x64 tiles cover in 1.5 rounds of the CUs and 128x96 tiles in one
+    // takes the latter over two groups of waves (2048x1536x512, qkv at 2048 rows: 11.6 -> 10.7 us
+    // in the step). 128x128 over two groups (tile 7) measured no better than 128x64 for
+    // 2048x2048x512 in the step, though 9.1 -> 8.6 us in a lab loop.
     if (ks == 1 && tiles(128, 128) >= 320) tile = 1;
+    else if (ks == 1 && (a.epi.kind & 0xff) != EPI_GLU && a.N % 96 == 0 && tiles(128, 96) >= 192 && tiles(128, 96) <= 256 &&
+             kt % 2 == 0)
+      tile = 8;
     else if (ks == 1 && tiles(128, 64) >= 320) tile = 2;
     else if (ks == 1 && tiles(64, 64) <= 256 && kt % 2 == 0) tile = 5;
     else tile = 4;
   }
-  if (tile < 1 || tile > 6) return fail();
+  if (tile < 1 || tile > 8) return fail();
   if (lns && kMfmaTiles[tile].bn != 64) tile = tiles(128, 64) >= 320 ? 2 : 4;  // one 64-column tile per block
+  if ((a.epi.kind & 0xff) == EPI_GLU && kMfmaTiles[tile].bn % 64) return fail();  // whole value/gate blocks
   const MfmaTile& T = kMfmaTiles[tile];
   if (kt % T.groups) return fail();  // every group takes the same number of k-steps
   const void* fn = T.pick(a.epi.kind);
@@ -1391,7 +1402,8 @@ void launch_gemm(Launcher& L, const GemmArgs& a0, int dtype, int path) {
     g.a_f32 = 0;
     g.ln_g = g.ln_b = nullptr;
   }
-  // paths 3..6: tiles 1..4; 9 / 10: tiles 5 / 6 (64x64 over 2 / 4 groups of waves)
+  // paths 3..6: tiles 1..4; 9..12: tiles 5..8 (64x64 over 2 / 4 groups of waves, 128x128 and
+  // 128x96 over 2)
   mfma_dispatch(L, g, path >= 9 ? path - 4 : path >= 3 ? path - 2 : 0);
 }
 
@@ -2440,7 +2452,7 @@ void kernels_init() {
   for (int ek : {(int)EPI_STORE, (int)EPI_SILU, (int)EPI_SILU_KEEP, (int)EPI_RELU_FE, (int)EPI_RESID, (int)EPI_RESID_KEEP,
                  (int)EPI_F32, (int)EPI_QKV, (int)EPI_GLU, (int)EPI_PART, (int)EPI_RESID_LNS, EPI_SILU | EPI_LNC,
                  EPI_SILU_KEEP | EPI_LNC, EPI_QKV | EPI_LNC, EPI_GLU | EPI_LNC}) {
-    for (int t = 1; t <= 6; ++t) fns.push_back(kMfmaTiles[t].pick(ek));
+    for (int t = 1; t <= 8; ++t) fns.push_back(kMfmaTiles[t].pick(ek));
   }
   for (const void* f : fns)
     if (f) (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);

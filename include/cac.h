@@ -248,8 +248,8 @@ const char* cac_last_error(const cac_ctx* ctx);
  * library's own choice, 1 = the small-M kernel, 2 = the MFMA tile kernel with its own tile
  * choice, 3..6 = the MFMA tile kernel with 128x128, 128x64, 64x128 or 64x64 block tiles
  * (MFMA paths: bf16 only, K a multiple of 64, N a multiple of 8), 9 / 10 = its 64x64 tile with the k-steps split
- * over 2 / 4 groups of waves in one block (K a multiple of 128 / 256), 7 / 8 = the 64x64 MFMA
- * kernel with K split in
+ * over 2 / 4 groups of waves in one block (K a multiple of 128 / 256), 11 / 12 = its 128x128 /
+ * 128x96 tile over 2 groups (K a multiple of 128), 7 / 8 = the 64x64 MFMA kernel with K split in
  * 2 / 4 ranges whose float32 partials the residual row kernel sums with the bias (K a multiple
  * of 128 / 256, N a multiple of 256 up to 1024; allocates and frees a temporary partial buffer
  * with hipMalloc / hipFree, the one allocation in the library, and returns after the stream has

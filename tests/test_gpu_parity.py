@@ -48,18 +48,18 @@ GEMM_SHAPES = [(2048, 512), (512, 2048), (1536, 512), (640, 512), (1024, 512), (
                                           ("bf16", 2, 512), ("bf16", 2, 2048), ("bf16", 3, 300), ("bf16", 4, 300),
                                           ("bf16", 5, 300), ("bf16", 6, 300), ("bf16", 7, 300), ("bf16", 8, 300),
                                           ("bf16", 8, 24), ("bf16", 9, 300), ("bf16", 10, 300), ("bf16", 10, 40),
-                                          ("bf16", 3, 7)])
+                                          ("bf16", 3, 7), ("bf16", 11, 300), ("bf16", 12, 300), ("bf16", 12, 2048)])
 def test_gemm_kernels(dtype, path, M):
     """Paths 7 and 8 (split-K partials summed by the residual row kernel) take N a multiple of
-    256 up to 1024 and K a multiple of 128 / 256; paths 9 and 10 (k-steps over 2 / 4 groups of
-    waves) K a multiple of 128 / 256; the other shapes are skipped for them."""
+    256 up to 1024 and K a multiple of 128 / 256; paths 9 to 12 (k-steps over 2 or 4 groups of
+    waves) K a multiple of 128 (256 for path 10); the other shapes are skipped for them."""
     from cache_aware_conformer_amd.binding import CAC_BF16, CAC_F32, test_gemm
     rng = np.random.default_rng(M * 7 + path)
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     for N, K in GEMM_SHAPES:
         if path in (7, 8) and (N % 256 or N > 1024 or K % (128 if path == 7 else 256)):
             continue
-        if path in (9, 10) and K % (128 if path == 9 else 256):
+        if path in (9, 10, 11, 12) and K % (256 if path == 10 else 128):
             continue
         log(f"gemm {dtype} path={path} M={M} N={N} K={K}")
         A = torch.from_numpy(rng.standard_normal((M, K), dtype=np.float32)).to("cuda:0").to(tdt)
