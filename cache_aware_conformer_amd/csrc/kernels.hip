@@ -1731,9 +1731,15 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // LDS of the MFMA attention kernel: V rows of NT 16-slot tiles, then the position terms of NR
-// query rows, each row overwritten by its softmax weights once its scores are formed (the 16
-// lanes that read a row's terms are the ones that write its weights)
-static size_t attn_mfma_lds(int nt, int nr) { return (size_t)nt * 16 * 128 + (size_t)nr * nt * 16 * 4; }
+// query rows, each
+// row overwritten by its softmax weights once its scores are formed (the 16 lanes that read a
+// row's terms are the ones that write its weights)
+__host__ __device__ constexpr int attn_mfma_vrows(int nt) { return nt * 16; }
+static size_t attn_mfma_lds(int nt, int nr) { return (size_t)attn_mfma_vrows(nt) * 128 + (size_t)nr * nt * 16 * 4; }
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_v;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_w;
+typedef __attribute__((address_space(3))) s16x4_v lds_s16x4_t;
 
 __device__ __forceinline__ float row16_max(float v) {  // over the 16 lanes of v's DPP row
   v = fmaxf(v, dpp<DPP_MIRROR16>(v));
@@ -1755,6 +1761,7 @@ __device__ __forceinline__ float row16_sum(float v) {
 template <int NT, int NR>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NR >= 8 || NT >= 6 ? 2 : 4, 8))) void attn_mfma_kernel(AttnArgs a) {
   constexpr int HD = 64, NS = NT * 16;
+  static_assert(attn_mfma_vrows(NT) == NS, "LDS layout");
   extern __shared__ __attribute__((aligned(16))) unsigned char mf_lds[];
   unsigned char* Vs = mf_lds;                // [NS][128 B] V rows
   float* Ts = (float*)(mf_lds + NS * 128);   // [NR][NS] position terms by distance, then weights
@@ -1880,31 +1887,57 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NR >= 8 || N
     }
   }
   wave_sync();
-  // ---- PV: lane (4-dim chunk c4, phase ph) sums slots ph, ph + 4, ... for every row
-  const int c4 = lane & 15, ph = lane >> 4;
-  f32x4_v o[NR];
+  // ---- PV on v_mfma_f32_16x16x32_bf16: O[i][d] = sum_j W[i][j] V[j][d] over 32-slot k-steps
+  // (and one 16-slot step on v_mfma_f32_16x16x16_bf16 when NT is odd), the weights rounded to
+  // bf16 as the 16-row A operand (rows past NR zero) and V as the B operand in 16-dim tiles.
+  // B needs consecutive slots of one dim per lane, V rows hold dims: ds_read_b64_tr_b16
+  // transposes within each 16-lane group, giving lane i of the group element i % 4 of the 4
+  // read by lane 4 j + i / 4 as its j-th value. So lane i reads dims d0 + 4 (i % 4) .. + 3 of
+  // slot (group slot base) + i / 4, and every lane ends with dim d0 + i of 4 consecutive slots;
+  // two such reads make the 8 of a 32-slot step.
+  f32x4_v O[4];
 #pragma unroll
-  for (int i = 0; i < NR; ++i) o[i] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll 4
-  for (int j0 = 0; j0 < NS; j0 += 4) {
-    const int j = j0 + ph;
-    const uint2 vw = *(const uint2*)(Vs + j * 128 + c4 * 8);
-    const f32x4_v v4 = {__uint_as_float(vw.x << 16), __uint_as_float(vw.x & 0xffff0000u), __uint_as_float(vw.y << 16),
-                        __uint_as_float(vw.y & 0xffff0000u)};
+  for (int dt = 0; dt < 4; ++dt) O[dt] = f32x4_v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < NR; ++i) o[i] += Ws[i * NS + j] * v4;
-  }
-#pragma unroll
-  for (int i = 0; i < NR; ++i) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float v = o[i][e];
-      v = pair_sum16(v, v);
-      o[i][e] = pair_sum32(v, v);
+  for (int ks = 0; ks < NS / 32; ++ks) {
+    const int j0 = 32 * ks + 8 * lg;  // this lane's 8 slots of the k-step (A and B alike)
+    u32x4_v wa = u32x4_v{0u, 0u, 0u, 0u};
+    if (l16 < NR) {
+      const f32x4_v w0 = *(const f32x4_v*)(Ws + l16 * NS + j0), w1 = *(const f32x4_v*)(Ws + l16 * NS + j0 + 4);
+      wa = u32x4_v{pack_bf2(w0.x, w0.y), pack_bf2(w0.z, w0.w), pack_bf2(w1.x, w1.y), pack_bf2(w1.z, w1.w)};
     }
-    if (lane < 16 && i < nf) {
-      bf16_t* dst = (bf16_t*)a.o + ((long)s * nf + i) * a.D + h * HD + 4 * lane;
-      *(uint2*)dst = uint2{pack_bf2(o[i].x, o[i].y), pack_bf2(o[i].z, o[i].w)};
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const unsigned char* vb = Vs + (j0 + (l16 >> 2)) * 128 + (16 * dt + 4 * (l16 & 3)) * 2;
+      const s16x4_v b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vb);
+      const s16x4_v b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + 4 * 128));
+      const u32x2_w p0 = __builtin_bit_cast(u32x2_w, b0), p1 = __builtin_bit_cast(u32x2_w, b1);
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, wa),
+                                                      __builtin_bit_cast(bf16x8_v, u32x4_v{p0.x, p0.y, p1.x, p1.y}), O[dt], 0, 0, 0);
+    }
+  }
+  if constexpr (NS % 32 != 0) {  // the last 16 slots: 4 per lane group
+    const int j0 = NS - 16 + 4 * lg;
+    u32x2_w wa = u32x2_w{0u, 0u};
+    if (l16 < NR) {
+      const f32x4_v w0 = *(const f32x4_v*)(Ws + l16 * NS + j0);
+      wa = u32x2_w{pack_bf2(w0.x, w0.y), pack_bf2(w0.z, w0.w)};
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const unsigned char* vb = Vs + (j0 + (l16 >> 2)) * 128 + (16 * dt + 4 * (l16 & 3)) * 2;
+      const s16x4_v b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)vb);
+      O[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_v, wa), b0, O[dt], 0, 0, 0);
+    }
+  }
+  // O[dt] element r of a lane: query row 4 (lane / 16) + r, dim 16 dt + lane % 16
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = 4 * lg + r;
+    if (i < nf && i < NR) {
+      bf16_t* dst = (bf16_t*)a.o + ((long)s * nf + i) * a.D + h * HD + l16;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) dst[16 * dt] = f2bf(O[dt][r]);
     }
   }
 }
