@@ -269,6 +269,16 @@ def test_2d_front_end_fresh_streams():
         _check_workload(C4S.replace(n_layers=2, streams=S, staggered=False, chunks=6), 6, range(S))
 
 
+@pytest.mark.parametrize("d_model,heads", [(256, 4), (1024, 16)], ids=["d256", "d1024"])
+def test_bf16_layernorm_carried_at_other_widths(d_model, heads):
+    """2048 rows (1024 streams x 2 frames), where the LayerNorms before qkv, pw1 and FF2 up ride
+    on the products, at 4 and 16 tiles of 64 columns per row; 64 staggered streams checked over
+    4 chunks."""
+    cfg = C3.replace(name=f"C3_d{d_model}_1024", n_layers=2, d_model=d_model, n_heads=heads, d_ff=4 * d_model,
+                     joint_dim=0, streams=1024, chunks=4)
+    _check_workload(cfg, 4, range(0, cfg.streams, 16))
+
+
 @pytest.mark.slow
 def test_c5_bf16_lookahead_512_streams_and_flush():
     """A fixed 64-stream subset (every 8th stream) over 8 passes, then the flush of all 64."""
