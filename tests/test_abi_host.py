@@ -359,3 +359,24 @@ def test_beam_decode_argument_checks_on_a_dry_context():
     assert lib.cac_beam_decode(ctx, 4, None, 16, fake, 0, fake, fake, fake, None) == CAC_EINVAL
     assert lib.cac_beam_decode(ctx, 4, lp, 16, fake, 0, None, fake, fake, None) == CAC_EINVAL
     assert b"max_steps" in lib.cac_beam_last_error(ctx) or True
+
+
+@pytest.mark.parametrize("dtype,path,M,N,K", [
+    ("bf16", 13, 64, 64, 128),    # no such path
+    ("f32", 3, 64, 64, 128),      # MFMA paths take bf16 only
+    ("bf16", 3, 64, 64, 96),      # K not a multiple of 64
+    ("bf16", 4, 64, 12, 128),     # N not a multiple of 8
+    ("bf16", 11, 64, 64, 192),    # two wave groups: K a multiple of 128
+    ("bf16", 10, 64, 64, 384),    # four wave groups: K a multiple of 256
+    ("bf16", 7, 64, 200, 256),    # split-K partials: N a multiple of 256
+])
+def test_test_gemm_rejects_shapes_a_path_does_not_take(dtype, path, M, N, K):
+    """The test GEMM entry points validate path and shape on the host before any device work
+    (the device pointers are stand-ins that are never touched)."""
+    lib = cac.load()
+    dt = cac.binding.CAC_BF16 if dtype == "bf16" else cac.binding.CAC_F32
+    fake = C.c_void_p(0x1000)
+    for fn in (lib.cac_test_gemm, lib.cac_test_gemm_noalloc):
+        rc = fn(dt, path, M, N, K, fake, fake, None, fake, None)
+        assert rc == CAC_EINVAL, (fn, rc)
+        assert lib.cac_last_error(None).decode()
