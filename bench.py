@@ -460,7 +460,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     head = run_workload(args.workload, args.steps, args.warmup, args.profile_steps, not args.no_cpu_baseline,
-                        args.cpu_seconds, extra_families=("attention",))
+                        args.cpu_seconds, extra_families=("attention", "gemm_mfma_bf16_dwconv"))
     res = {"metric": METRIC, "value": head["value"], "unit": "frames/s", "n_gpus": 1, "steps": head["steps"],
            "warmup": head["warmup"], "ms_per_step": head["ms_per_step"], "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",

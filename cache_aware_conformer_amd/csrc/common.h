@@ -151,6 +151,14 @@ enum EpiKind {
 // channel c, 32 rows further its gate (so a 32-wide tile holds matching value/gate halves).
 __host__ __device__ __forceinline__ int glu_a_col(int c) { return (c >> 5) * 64 + (c & 31); }
 
+// Depthwise conv input ring of one layer: [S][D / 32][Rc][32] in the compute dtype (D a multiple
+// of 32). A stream's rows of one 32-channel block lie together, so a reader of a few positions
+// of a block (the GLU tile's conv) takes whole cache lines. Element (slot, channel c) of ring
+// row group g (a stream of one layer, or layer l x S + stream across the layers):
+__host__ __device__ __forceinline__ long cring_idx(long g, int slot, int c, int D, int Rc) {
+  return g * Rc * D + ((long)(c >> 5) * Rc + slot) * 32 + (c & 31);
+}
+
 struct EpiArgs {
   int kind;
   const float* bias;  // [N] (may be null)
@@ -169,7 +177,7 @@ struct EpiArgs {
   float* qbuf;          // [M][D] float32
   void* kring;          // [S][H][R][hd] of this layer (compute dtype)
   void* vring;
-  void* cring;          // [S][Rc][D] of this layer (compute dtype)
+  void* cring;          // conv ring of this layer (cring_idx layout, compute dtype)
   int D, H, hd, R, Rc;
   // LayerNorm carried through the products (EPI_RESID_LNS writes, EPI_LNC reads):
   //   lns[t * lns_ld + m] = (mean, sum of squared deviations) of row m's columns 64 t .. 64 t + 63
@@ -202,7 +210,7 @@ struct GemmArgs {
   const float* pre_g;    // LayerNorm the A rows with (pre_g, pre_b) before (ln_g, ln_b)
   const float* pre_b;
   int a_dw;              // A rows are SiLU(depthwise conv over the ring) (see DwArgs fields)
-  const void* dw_ring;   // layer base [S][Rc][K]
+  const void* dw_ring;   // conv ring of the layer (cring_idx layout, width K)
   const float* dw_w;     // [taps][K]
   const float* dw_b;     // [K]
   int dw_taps, dw_Rc;
@@ -261,7 +269,7 @@ struct AttnArgs {
 
 struct DwArgs {
   CallView cv;
-  const void* cring;   // layer base [S][Rc][D]
+  const void* cring;   // conv ring of the layer (cring_idx layout)
   const float* w;      // [K][D] taps
   const float* b;      // [D]
   void* e;             // [M][D] compute dtype

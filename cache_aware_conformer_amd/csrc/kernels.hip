@@ -164,7 +164,7 @@ __device__ __forceinline__ void epi_glu(const EpiArgs& e, int m, int c, float va
   int s = m / e.cv.nf, i = m % e.cv.nf;
   int id = e.cv.ids[s];
   int slot = (e.cv.cpos[s] + i) % e.Rc;
-  st<T>((T*)e.cring + ((long)id * e.Rc + slot) * e.D + c, g);
+  st<T>((T*)e.cring + cring_idx(id, slot, c, e.D, e.Rc), g);
 }
 
 
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
         const int m = m0 + r, sidx = m / e.cv.nf, i = m % e.cv.nf;
         const int id = e.cv.ids[sidx];
         const int p = e.cv.cpos[sidx] + i;
-        const TA* ring = (const TA*)a.dw_ring + (long)id * a.dw_Rc * K + ch;
+        const TA* ring = (const TA*)a.dw_ring;  // 4 channels of one 32-channel block per read
         float g[16][4];
         float4 w[16];
 #pragma unroll
@@ -310,10 +310,10 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
           const bool ok = t < a.dw_taps && q >= 0;
           w[t] = t < a.dw_taps ? *(const float4*)(a.dw_w + t * K + ch) : make_float4(0.f, 0.f, 0.f, 0.f);
           if constexpr (sizeof(TA) == 4) {
-            const float4 v = ok ? *(const float4*)(ring + (long)(q % a.dw_Rc) * K) : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 v = ok ? *(const float4*)(ring + cring_idx(id, q % a.dw_Rc, ch, K, a.dw_Rc)) : make_float4(0.f, 0.f, 0.f, 0.f);
             g[t][0] = v.x; g[t][1] = v.y; g[t][2] = v.z; g[t][3] = v.w;
           } else {
-            const uint2 v = ok ? *(const uint2*)(ring + (long)(q % a.dw_Rc) * K) : make_uint2(0u, 0u);
+            const uint2 v = ok ? *(const uint2*)(ring + cring_idx(id, q % a.dw_Rc, ch, K, a.dw_Rc)) : make_uint2(0u, 0u);
             g[t][0] = __uint_as_float(v.x << 16); g[t][1] = __uint_as_float(v.x & 0xffff0000u);
             g[t][2] = __uint_as_float(v.y << 16); g[t][3] = __uint_as_float(v.y & 0xffff0000u);
           }
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(GemmArgs a) {
           if constexpr (GLU) {
             const float g = (va + eb[u][0]) * sigmoid_f(vb + eb[u][COLS - 1]);
             const int slot = (row_slot_pos + m % e.cv.nf) % e.Rc;
-            st<TW>((TW*)e.cring + ((long)row_id * e.Rc + slot) * e.D + unit, g);
+            st<TW>((TW*)e.cring + cring_idx(row_id, slot, unit, e.D, e.Rc), g);
           } else {
             const float v = va + eb[u][0];
             switch (e.kind) {
@@ -635,6 +635,20 @@ __device__ __forceinline__ void mfma_ct8(const float* ct, int idx, float* v) {
   }
 }
 
+template <int BM, int BN, int S, int KS>
+constexpr size_t mfma_lds() {
+  // KS rings of S stages, reused afterwards for KS float accumulator tiles and the LayerNorm
+  // row and column terms of EPI_LNC
+  return std::max((size_t)KS * S * (BM + BN) * 128, (size_t)KS * BM * (BN + 4) * sizeof(float) + (BM + BN) * 8);
+}
+// EPI_GLU_DW also keeps the tile's GLU outputs and 16 rows of conv taps there: only the tiles
+// whose rings cover that take it
+template <int BM, int BN, int S, int KS>
+constexpr bool mfma_dw_fits() {
+  return (size_t)KS * BM * (BN + 4) * sizeof(float) + (BM + BN) * 8 + (size_t)(BM + 16) * (BN / 2) * sizeof(float) <=
+         mfma_lds<BM, BN, S, KS>();
+}
+
 template <int BM, int BN, int WM, int WN, int S, int KS, int EK>
 __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 * KS))) void gemm_mfma_kernel(GemmArgs a) {
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
@@ -644,6 +658,10 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   constexpr int EB = EK & 0xff;  // the kind without the EPI_LNC flag
   constexpr bool LNC = (EK & EPI_LNC) != 0, LNS = EB == EPI_RESID_LNS;
   static_assert(!LNS || BN == 64, "tile statistics cover one 64-column tile per block");
+  // EPI_GLU_DW: the GLU epilogue, then the depthwise conv + SiLU of the tile's rows (each
+  // stream's rows of the call lie in one tile) over its channels
+  constexpr bool DW = EB == EPI_GLU_DW, GLU = EB == EPI_GLU || DW;
+  static_assert(!DW || mfma_dw_fits<BM, BN, S, KS>(), "conv taps and GLU rows past the tile's LDS");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds8[];
   // wave and group indices are wave-uniform: in scalar registers, so the copies' LDS bases and
   // k offsets need no per-lane handling
@@ -723,11 +741,11 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   // The other kinds load their items' biases, and the QKV and front-end kinds their rows'
   // stream positions and ids, the same way (GLU: per 8-channel item, both halves' biases).
   constexpr bool RES = EB == EPI_RESID || EB == EPI_RESID_KEEP || LNS;
-  constexpr bool PB = !LNC && EB != EPI_PART && EB != EPI_GLU, PM = EB == EPI_QKV || EB == EPI_RELU_FE;
+  constexpr bool PB = !LNC && EB != EPI_PART && !GLU, PM = EB == EPI_QKV || EB == EPI_RELU_FE;
   constexpr int NT = 256 * KS, C8 = BN / 8, NIT8 = (BM * C8 + NT - 1) / NT;
   constexpr int G8 = BN / 16, NITG = (BM * G8 + NT - 1) / NT;  // GLU: 8-channel items
-  constexpr int RI = RES ? NIT8 : 1, BI = PB ? NIT8 : 1, MI = PM ? NIT8 : EB == EPI_GLU ? NITG : 1;
-  constexpr int GI = EB == EPI_GLU && !LNC ? NITG : 1, LT = LNC ? 16 : 1;
+  constexpr int RI = RES ? NIT8 : 1, BI = PB ? NIT8 : 1, MI = PM ? NIT8 : GLU ? NITG : 1;
+  constexpr int GI = GLU && !LNC ? NITG : 1, LT = LNC ? 16 : 1;
   float xpre[RI][8], bpre[BI][8], spre[RI], gpre[GI][16];
   int mpre[MI][2];
   if constexpr (RES || PB || PM) {
@@ -754,11 +772,13 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
       }
     }
   }
-  if constexpr (EB == EPI_GLU) {
+  if constexpr (GLU) {
 #pragma unroll
     for (int k = 0; k < NITG; ++k) {
       const int it = tid + NT * k, rr = it / G8, ch = (it - rr * G8) * 8;
       const int row = min(bm0 + rr, M - 1), c = min(bn0 / 2 + ch, a.epi.D - 8);
+      mpre[k][0] = 0;
+      mpre[k][1] = 0;
       if (it < BM * G8) {
         const int st = row / a.epi.cv.nf;
         mpre[k][0] = a.epi.cv.cpos[st];
@@ -768,6 +788,23 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
           ld_f8(a.epi.bias + a.epi.D + c, gpre[k] + 8);
         }
       }
+    }
+  }
+  // EPI_GLU_DW: the block's channels of the conv taps (16 rows, zero past the kernel size),
+  // staged to LDS after the k-loop, and each item's channels of the conv bias
+  constexpr int CH = BN / 2, TPI = DW ? (16 * CH + NT - 1) / NT : 1, DI = DW ? NITG : 1;
+  float tpre[TPI], dbpre[DI][8];
+  if constexpr (DW) {
+    const int D = a.epi.D, ntap = a.dw_taps;
+#pragma unroll
+    for (int u = 0; u < TPI; ++u) {
+      const int e = tid + NT * u, t = e / CH, c = bn0 / 2 + (e - t * CH);
+      tpre[u] = (e < 16 * CH && t < ntap && c < D) ? a.dw_w[t * D + c] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < DI; ++k) {
+      const int it = tid + NT * k, rr = it / G8, ch = (it - rr * G8) * 8;
+      ld_f8(a.dw_b + min(bn0 / 2 + ch, D - 8), dbpre[k]);
     }
   }
   float2 lst[LT];
@@ -782,7 +819,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
     }
     if (tid < BN) {
       int idx = min(bn0 + tid, N - 1);
-      if constexpr (EB == EPI_GLU) {  // packed column -> value channel c, or its gate at D + c
+      if constexpr (GLU) {  // packed column -> value channel c, or its gate at D + c
         const int ch = (idx >> 6) * 32 + (idx & 31);
         idx = (idx & 63) >= 32 ? e.D + ch : ch;
       }
@@ -793,6 +830,29 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < KT) MFMA_ISSUE(s, kb + s);
+  // EPI_GLU_DW: each item's conv input rows at positions p0 - 8 .. p0 - 1 of its stream (p0:
+  // the call's first position), 8 channels each, issued after the prologue's copies since their
+  // addresses wait for the stream ids: NDW loads per wave, every wave issuing all of them
+  // (offsets past the resource read zero: rows before the stream start or outside the kernel's
+  // reach, and items past the tile), so the k-loop's first S - 1 waits can count them
+  constexpr int NDW = DW ? 8 * DI : 0;
+  u32x4_v dwo[DI][DW ? 8 : 1];
+  if constexpr (DW) {
+    asm volatile("" ::: "memory");
+    const EpiArgs& e = a.epi;
+    const __amdgpu_buffer_rsrc_t cr = raw_rsrc(e.cring, 0x7fffffff);
+#pragma unroll
+    for (int k = 0; k < DI; ++k) {
+      const int it = tid + NT * k, rr = it / G8, ch = (it - rr * G8) * 8;
+      const int c = min(bn0 / 2 + ch, e.D - 8), p0 = mpre[k][0], lo = max(0, p0 - (a.dw_taps - 1));
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int q = p0 - 8 + r;
+        const int off = (it < BM * G8 && q >= lo) ? (int)(cring_idx(mpre[k][1], q % e.Rc, c, e.D, e.Rc) * 2) : INT_MIN;
+        dwo[k][r] = __builtin_bit_cast(u32x4_v, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, 0));
+      }
+    }
+  }
   // operand read offsets in a stage (bytes): lane l reads row l % 32 of a fragment, logical
   // chunk 2 kk + l / 32 for the kk-th 16-k MFMA of the k-step
   int aoffs[FM][4], boffs[FN][4];
@@ -813,8 +873,12 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   int buf = 0;
   for (int kt = 0; kt < KT; ++kt) {
     // this wave's copies of k-step kt have landed (later stages may still be in flight) ...
-    if (kt + S - 2 < KT) wait_vmcnt<(S - 2) * (NA + NB)>();
-    else wait_vmcnt<0>();
+    if (kt + S - 2 < KT) {
+      if (DW && kt < S - 1) wait_vmcnt<(S - 2) * (NA + NB) + NDW>();  // the conv rows came after
+      else wait_vmcnt<(S - 2) * (NA + NB)>();
+    } else {
+      wait_vmcnt<0>();
+    }
     // ... and every wave's, once all have passed the barrier; every wave has also finished
     // reading the stage of k-step kt - 1, which the copies of k-step kt + S - 1 overwrite
     __builtin_amdgcn_s_barrier();
@@ -851,6 +915,16 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   // EPI_LNC: per row (rstd, -rstd (mean - shift)) and per column (c1, c2) after the tiles
   float2* lnrow = (float2*)((float*)lds8 + KS * BM * CS);
   float2* lncol = lnrow + BM;
+  // EPI_GLU_DW: the tile's GLU outputs [BM][CH] and the conv taps [16][CH] after those
+  float* fresh = (float*)(lncol + BN);
+  float* taps = fresh + BM * CH;
+  if constexpr (DW) {
+#pragma unroll
+    for (int u = 0; u < TPI; ++u) {
+      const int e = tid + NT * u;
+      if (e < 16 * CH) taps[e] = tpre[u];
+    }
+  }
   if constexpr (LNC) {
     if (tid < BM) {  // combine the row's 64-column tiles (Chan et al.'s pairwise update)
       const int ntl = a.epi.lns_ntl;
@@ -883,7 +957,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   }
   __syncthreads();
   const float* ct = (const float*)lds8;
-  if constexpr (EB == EPI_GLU) {
+  if constexpr (GLU) {
     // packed columns: each 64-column block holds 32 value columns then their 32 gates; a thread
     // takes 8 channels (8 values, 8 gates) and writes them to the conv ring with one store
     const EpiArgs& e = a.epi;
@@ -920,7 +994,51 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
       for (int q = 0; q < 8; ++q) g[q] = (va[q] + ba[q]) * sigmoid_f(vb[q] + bb[q]);
       const int s = row / e.cv.nf, i = row - s * e.cv.nf;
       const int slot = (mpre[k][0] + i) % e.Rc;
-      st_bf8((bf16_t*)e.cring + ((long)mpre[k][1] * e.Rc + slot) * e.D + c, g);
+      st_bf8((bf16_t*)e.cring + cring_idx(mpre[k][1], slot, c, e.D, e.Rc), g);
+      if constexpr (DW) {
+        *(f32x4_v*)(fresh + rr * CH + ch) = f32x4_v{g[0], g[1], g[2], g[3]};
+        *(f32x4_v*)(fresh + rr * CH + ch + 4) = f32x4_v{g[4], g[5], g[6], g[7]};
+      }
+    }
+    if constexpr (DW) {
+      // row (stream s, frame i) at position p = p0 + i: out = SiLU(b + sum_t w[t] u[p - (K - 1) + t])
+      // over the conv inputs u, the older ones from dwo (tap t = r + K - 9 - i for the row at
+      // p0 - 8 + r), the call's own from the tile (tap t = j - i + K - 1 for frame j <= i)
+      __syncthreads();
+      const int ntap = a.dw_taps;
+#pragma unroll
+      for (int k = 0; k < NITG; ++k) {
+        const int it = tid + NT * k;
+        if (it >= BM * G8) break;
+        const int rr = it / G8, ch = (it - rr * G8) * 8;
+        const int pc = (ch >> 5) * 64 + (ch & 31);
+        const int row = bm0 + rr, c = bn0 / 2 + ch;
+        if (row >= M || bn0 + pc >= N) continue;
+        const int i = row - (row / e.cv.nf) * e.cv.nf;
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = dbpre[k][q];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int t = r + ntap - 9 - i;
+          const float* w = taps + max(t, 0) * CH + ch;
+          const u32x4_v u = t >= 0 ? dwo[k][r] : u32x4_v{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            acc[2 * h] += w[2 * h] * __uint_as_float(u[h] << 16);
+            acc[2 * h + 1] += w[2 * h + 1] * __uint_as_float(u[h] & 0xffff0000u);
+          }
+        }
+        for (int j = max(0, i - ntap + 1); j <= i; ++j) {
+          const float* w = taps + (j - i + ntap - 1) * CH + ch;
+          const float* f = fresh + (rr - i + j) * CH + ch;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] += w[q] * f[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = silu_f(acc[q]);
+        st_bf8((bf16_t*)e.out + (long)row * e.ldo + c, acc);
+      }
     }
   } else {
 #pragma unroll
@@ -983,12 +1101,6 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   }
 }
 
-template <int BM, int BN, int S, int KS>
-constexpr size_t mfma_lds() {
-  // KS rings of S stages, reused afterwards for KS float accumulator tiles and the LayerNorm
-  // row and column terms of EPI_LNC
-  return std::max((size_t)KS * S * (BM + BN) * 128, (size_t)KS * BM * (BN + 4) * sizeof(float) + (BM + BN) * 8);
-}
 
 // =============================================================================== LayerNorm
 // One wave per row. D a multiple of 256 up to 1024: the row, gains and shifts are loaded
@@ -1256,6 +1368,13 @@ static const void* mfma_pick_epi(int ek) {
     case EPI_SILU_KEEP | EPI_LNC: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_SILU_KEEP | EPI_LNC>;
     case EPI_QKV | EPI_LNC: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_QKV | EPI_LNC>;
     case EPI_GLU | EPI_LNC: return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_GLU | EPI_LNC>;
+    case EPI_GLU_DW:
+      if constexpr (BN % 64 == 0 && mfma_dw_fits<BM, BN, S, KS>()) return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_GLU_DW>;
+      return nullptr;
+    case EPI_GLU_DW | EPI_LNC:
+      if constexpr (BN % 64 == 0 && mfma_dw_fits<BM, BN, S, KS>())
+        return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_GLU_DW | EPI_LNC>;
+      return nullptr;
     case EPI_RESID_LNS:
       if constexpr (BN == 64) return (const void*)&gemm_mfma_kernel<BM, BN, WM, WN, S, KS, EPI_RESID_LNS>;
       return nullptr;
@@ -1288,7 +1407,10 @@ static const MfmaTile kMfmaTiles[9] = {
 static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   GemmArgs args = a;
-  L.tag("gemm_mfma_bf16", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K);
+  // the product with the depthwise conv in its epilogue is a family of its own
+  const bool dw = (a.epi.kind & 0xff) == EPI_GLU_DW;
+  if (dw) L.tag("gemm_mfma_bf16_dwconv", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K + 2.0 * a.dw_taps * (a.N / 2) * a.M);
+  else L.tag("gemm_mfma_bf16", gemm_bytes(a, 2), 2.0 * a.M * a.N * a.K);
   const int ks = std::max(a.ksplit, 1);
   auto fail = [&]() {
     if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
@@ -1302,6 +1424,12 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   if ((lns || lnc) && (ks > 1 || !a.epi.lns || !a.epi.lns_shift || a.epi.lns_ntl < 1 || a.epi.lns_ntl > 16)) return fail();
   if (lns && (a.N % 64 || a.N / 64 != a.epi.lns_ntl || !a.epi.xc)) return fail();
   if (lnc && (!a.epi.lnc_c1 || !a.epi.lnc_c2 || !a.epi.lns_mean || a.K != 64 * a.epi.lns_ntl)) return fail();
+  // EPI_GLU_DW: the conv reads 8 older ring rows (kernel size at most 9), each stream's rows of
+  // the call must lie in one tile (tile rows a multiple of the frames per stream), and the ring
+  // offsets are 32-bit (the caller checks the layer's ring size)
+  if (dw && (a.dw_taps < 1 || a.dw_taps > 9 || !a.dw_w || !a.dw_b || !a.epi.out || !a.epi.cring || a.epi.D % 32 ||
+             a.epi.cv.nf < 1 || 64 % a.epi.cv.nf))
+    return fail();
   const int kt = a.K / 64 / ks;  // k-steps per block
   if (tile == 0) {
     // measured at 512 - 5120 rows (K 512 / 2048, N 512 - 2048): a larger tile pays from about
@@ -1315,7 +1443,7 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
     // in the step). 128x128 over two groups (tile 7) measured no better than 128x64 for
     // 2048x2048x512 in the step, though 9.1 -> 8.6 us in a lab loop.
     if (ks == 1 && tiles(128, 128) >= 320) tile = 1;
-    else if (ks == 1 && (a.epi.kind & 0xff) != EPI_GLU && a.N % 96 == 0 && tiles(128, 96) >= 192 && tiles(128, 96) <= 256 &&
+    else if (ks == 1 && (a.epi.kind & 0xff) != EPI_GLU && !dw && a.N % 96 == 0 && tiles(128, 96) >= 192 && tiles(128, 96) <= 256 &&
              kt % 2 == 0)
       tile = 8;
     else if (ks == 1 && tiles(128, 64) >= 320) tile = 2;
@@ -1324,7 +1452,8 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   }
   if (tile < 1 || tile > 8) return fail();
   if (lns && kMfmaTiles[tile].bn != 64) tile = tiles(128, 64) >= 320 ? 2 : 4;  // one 64-column tile per block
-  if ((a.epi.kind & 0xff) == EPI_GLU && kMfmaTiles[tile].bn % 64) return fail();  // whole value/gate blocks
+  if (dw && tile == 1) tile = 2;  // 128x128 has no LDS room for the conv's rows
+  if (((a.epi.kind & 0xff) == EPI_GLU || dw) && kMfmaTiles[tile].bn % 64) return fail();  // whole value/gate blocks
   const MfmaTile& T = kMfmaTiles[tile];
   if (kt % T.groups) return fail();  // every group takes the same number of k-steps
   const void* fn = T.pick(a.epi.kind);
@@ -1367,7 +1496,9 @@ void launch_gemm(Launcher& L, const GemmArgs& a0, int dtype, int path) {
     return;
   }
   if (path == 0 && rowdot_launch(L, a, dtype)) return;
-  if (a.epi.kind == EPI_GLU_DW || dtype == DT_I8W) {  // only the two-row kernel has these
+  // int8 weights: the two-row kernel only; the depthwise conv in the GLU epilogue: the two-row
+  // and MFMA kernels
+  if (dtype == DT_I8W || ((a.epi.kind & 0xff) == EPI_GLU_DW && !mfma)) {
     if (L.err == hipSuccess) L.err = hipErrorInvalidValue;
     return;
   }
@@ -1993,7 +2124,7 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
   const int s = m / a.cv.nf, i = m % a.cv.nf;
   const int id = a.cv.ids[s];
   const int p = a.cv.cpos[s] + i;
-  const T* ring = (const T*)a.cring + (long)id * a.Rc * a.D + c;
+  const T* ring = (const T*)a.cring;  // 4 channels of one 32-channel block per read
   float g[16][4];
   float4 w[16];
 #pragma unroll
@@ -2002,10 +2133,10 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
     const bool ok = t < a.K && q >= 0;
     w[t] = t < a.K ? *(const float4*)(a.w + t * a.D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     if constexpr (sizeof(T) == 4) {
-      const float4 v = ok ? *(const float4*)(ring + (long)(q % a.Rc) * a.D) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 v = ok ? *(const float4*)(ring + cring_idx(id, q % a.Rc, c, a.D, a.Rc)) : make_float4(0.f, 0.f, 0.f, 0.f);
       g[t][0] = v.x; g[t][1] = v.y; g[t][2] = v.z; g[t][3] = v.w;
     } else {
-      const uint2 v = ok ? *(const uint2*)(ring + (long)(q % a.Rc) * a.D) : make_uint2(0u, 0u);
+      const uint2 v = ok ? *(const uint2*)(ring + cring_idx(id, q % a.Rc, c, a.D, a.Rc)) : make_uint2(0u, 0u);
       g[t][0] = __uint_as_float(v.x << 16); g[t][1] = __uint_as_float(v.x & 0xffff0000u);
       g[t][2] = __uint_as_float(v.y << 16); g[t][3] = __uint_as_float(v.y & 0xffff0000u);
     }
@@ -2391,7 +2522,7 @@ __global__ __launch_bounds__(256) void state_xfer_kernel(StateArgs a) {
       const long l = r / ((long)a.Kc * a.D), j = (r / a.D) % a.Kc, c = r % a.D;
       const int q = pos - a.Kc + (int)j;
       valid = q >= 0;
-      if (valid) dst = (T*)a.cring + ((l * a.S + id) * a.Rc + q % a.Rc) * a.D + c;
+      if (valid) dst = (T*)a.cring + cring_idx(l * a.S + id, q % a.Rc, (int)c, a.D, a.Rc);
     } else if ((r -= cvn) < tln) {
       valid = true;
       dst = (T*)a.tail + id * tln + r;
@@ -2484,7 +2615,7 @@ void kernels_init() {
     }
   for (int ek : {(int)EPI_STORE, (int)EPI_SILU, (int)EPI_SILU_KEEP, (int)EPI_RELU_FE, (int)EPI_RESID, (int)EPI_RESID_KEEP,
                  (int)EPI_F32, (int)EPI_QKV, (int)EPI_GLU, (int)EPI_PART, (int)EPI_RESID_LNS, EPI_SILU | EPI_LNC,
-                 EPI_SILU_KEEP | EPI_LNC, EPI_QKV | EPI_LNC, EPI_GLU | EPI_LNC}) {
+                 EPI_SILU_KEEP | EPI_LNC, EPI_QKV | EPI_LNC, EPI_GLU | EPI_LNC, (int)EPI_GLU_DW, EPI_GLU_DW | EPI_LNC}) {
     for (int t = 1; t <= 8; ++t) fns.push_back(kMfmaTiles[t].pick(ek));
   }
   for (const void* f : fns)

@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
     dw_tap = tap < T ? tw : 0.0f;
     int sl = pos % Rc - oa;
     sl += sl < 0 ? Rc : 0;
-    const float rv = ld<TW>((const TW*)e.cring + ((long)sid * Rc + sl) * e.D + un);
+    const float rv = ld<TW>((const TW*)e.cring + cring_idx(sid, sl, un, e.D, Rc));
     dw_old = (tap >= 1 && tap < T && tap > frame && pos - tap >= 0) ? rv : 0.0f;
     dwb = a.dw_b[un];
   }
@@ -343,7 +343,7 @@ __global__ __launch_bounds__(256) void rowdot_kernel(GemmArgs a) {
     conv += dpp<DPP_XOR2>(conv);
     conv += dpp<DPP_XOR1>(conv);
     if (writer) {
-      st<TW>((TW*)e.cring + ((long)sid * e.Rc + pos % e.Rc) * e.D + unit, g);
+      st<TW>((TW*)e.cring + cring_idx(sid, pos % e.Rc, unit, e.D, e.Rc), g);
       st<TW>((TW*)e.out + (long)m * e.ldo + unit, silu_f(dwb + conv));
     }
   } else if (writer) {

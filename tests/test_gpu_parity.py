@@ -301,6 +301,20 @@ def test_bf16_attention_shapes(cfg):
     _check_workload(cfg, cfg.chunks, range(cfg.streams))
 
 
+@pytest.mark.parametrize("cfg", [
+    # the depthwise conv in pw1's epilogue: kernel sizes 5 and 3 (fewer taps than the 8 older rows
+    # it loads), 3 taps over 4 frames per stream (frames whose taps start inside the call), fresh
+    # streams (taps reaching before the stream start)
+    C3.replace(name="C3_dw5", n_layers=2, streams=40, dw_kernel=5, chunks=6),
+    C3.replace(name="C3_dw3_chunk4", n_layers=2, streams=40, dw_kernel=3, att_chunk=4, n_emit=4, chunks=6),
+    C3.replace(name="C3_dw9_fresh", n_layers=2, streams=40, staggered=False, chunks=6),
+    # kernel size 15 (14 older rows): the separate depthwise kernel
+    C3.replace(name="C3_dw15", n_layers=2, streams=40, dw_kernel=15, chunks=6),
+], ids=["dw5", "dw3-4rows", "dw9-fresh", "dw15-separate"])
+def test_bf16_depthwise_conv_shapes(cfg):
+    _check_workload(cfg, cfg.chunks, range(cfg.streams))
+
+
 def test_bf16_single_stream_small_m_path():
     """1 stream in bf16 runs every dense product through the small-M kernel."""
     cfg = C3.replace(streams=1, staggered=False, chunks=40)
