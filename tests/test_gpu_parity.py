@@ -315,6 +315,14 @@ def test_bf16_depthwise_conv_shapes(cfg):
     _check_workload(cfg, cfg.chunks, range(cfg.streams))
 
 
+def test_bf16_depthwise_conv_in_128_row_tiles():
+    """5120 rows (2560 streams x 2 frames): pw1 with the conv in its epilogue on 128x64 tiles
+    (the tile rule would pick 128x128, which has no LDS room for the conv's rows), LayerNorm
+    carried; 64 staggered streams checked over 2 chunks."""
+    cfg = C3.replace(name="C3_dw_2560", n_layers=2, streams=2560, chunks=2)
+    _check_workload(cfg, 2, range(0, cfg.streams, 40))
+
+
 def test_bf16_single_stream_small_m_path():
     """1 stream in bf16 runs every dense product through the small-M kernel."""
     cfg = C3.replace(streams=1, staggered=False, chunks=40)
