@@ -517,12 +517,13 @@ struct Pass {
     launch_gemm(L, g, d.dt, 0);
   }
   // The depthwise conv + SiLU runs in pw1's GLU epilogue (MFMA kernel) when the kernel size is
-  // at most 9 (it reads 8 older ring rows), each stream's rows of the call fit the 64- and
-  // 128-row tiles evenly, and the conv ring's byte offsets fit 31 bits. Measured at 1024
+  // at most 9 (it reads 8 older ring rows), the frames per call are at most 64, and the conv
+  // ring's byte offsets fit 31 bits; the streams whose rows cross a multiple of 64 rows (none
+  // when the frames per call divide 64) are left to a small kernel after pw1. Measured at 1024
   // streams: the separate kernel cost ~7 us per layer.
   bool dw_in_pw1() const {
     const Dims& d = c->d;
-    return !d.wq && d.K <= 9 && 64 % cv.nf == 0 && d.D % 32 == 0 &&
+    return !d.wq && d.K <= 9 && cv.nf <= 64 && d.D % 32 == 0 &&
            (double)d.S * d.Rc * d.D * d.esz < 2147483648.0 - 4096.0;
   }
   // a consumer of centred rows: LayerNorm finished from st (statistics) and shift; the rows'
@@ -729,10 +730,15 @@ struct Pass {
     g1.dw_w = F32(lo.dw_w); g1.dw_b = F32(lo.b_dw); g1.dw_taps = d.K; g1.dw_Rc = d.Rc;
     L.role = "pw1";
     launch_gemm(L, g1, wdt(), 0);
+    DwArgs dw{cv, cr, F32(lo.dw_w), F32(lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
     if (!dwf) {
-      DwArgs dw{cv, cr, F32(lo.dw_w), F32(lo.b_dw), c->P<void>(c->lay.e), d.D, d.K, d.Rc};
       L.tag("dwconv", (double)cv.n_streams * (d.Kc + cv.nf) * d.D * d.esz, 2.0 * d.K * d.D * M);
       launch_dwconv(L, dw, d.dt);
+    } else if (64 % cv.nf) {  // the streams across 64-row boundaries
+      const int nx = (M - 1) / 64;
+      L.role = "dw_straddle";
+      L.tag("dwconv", (double)nx * (d.Kc + cv.nf) * d.D * d.esz, 2.0 * d.K * d.D * nx * cv.nf);
+      launch_dwconv_straddle(L, dw);
     }
     if (lc) resid_carry("pw2", c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, 1.0f, F32(lo.b_pw2), sb, ma);
     else resid_rows("pw2", c->P<void>(c->lay.e), d.D, lb + lo.w_pw2, d.D, 1.0f, F32(lo.b_pw2), nullptr, nullptr,

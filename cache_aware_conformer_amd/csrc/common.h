@@ -448,6 +448,9 @@ void launch_cvt(Launcher& L, const CvtArgs& a);  // y = bf16(x rows)
 bool launch_resid_ln(Launcher& L, const ResLnArgs& a, int dtype);
 void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd);
 void launch_dwconv(Launcher& L, const DwArgs& a, int dtype);
+// the conv of the streams whose rows cross a multiple of 64 rows (bf16), after a product with
+// EPI_GLU_DW; false (nothing launched) when no stream crosses one
+bool launch_dwconv_straddle(Launcher& L, const DwArgs& a);
 void launch_input(Launcher& L, const InputArgs& a, int dtype);
 void launch_copy_rows(Launcher& L, const CopyRowsArgs& a);
 void kernels_init();

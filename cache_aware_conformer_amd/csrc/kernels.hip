@@ -658,8 +658,8 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
   constexpr int EB = EK & 0xff;  // the kind without the EPI_LNC flag
   constexpr bool LNC = (EK & EPI_LNC) != 0, LNS = EB == EPI_RESID_LNS;
   static_assert(!LNS || BN == 64, "tile statistics cover one 64-column tile per block");
-  // EPI_GLU_DW: the GLU epilogue, then the depthwise conv + SiLU of the tile's rows (each
-  // stream's rows of the call lie in one tile) over its channels
+  // EPI_GLU_DW: the GLU epilogue, then the depthwise conv + SiLU over the tile's channels of its
+  // rows, for the streams whose rows of the call lie in one 64-row block
   constexpr bool DW = EB == EPI_GLU_DW, GLU = EB == EPI_GLU || DW;
   static_assert(!DW || mfma_dw_fits<BM, BN, S, KS>(), "conv taps and GLU rows past the tile's LDS");
   extern __shared__ __attribute__((aligned(16))) unsigned char lds8[];
@@ -1017,6 +1017,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, 2 
         const int row = bm0 + rr, c = bn0 / 2 + ch;
         if (row >= M || bn0 + pc >= N) continue;
         const int i = row - (row / e.cv.nf) * e.cv.nf;
+        if (((row - i) >> 6) != ((row - i + e.cv.nf - 1) >> 6)) continue;  // across 64 rows: dw_straddle_kernel
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = dbpre[k][q];
@@ -1426,11 +1427,12 @@ static void mfma_dispatch(Launcher& L, const GemmArgs& a, int tile) {
   if ((lns || lnc) && (ks > 1 || !a.epi.lns || !a.epi.lns_shift || a.epi.lns_ntl < 1 || a.epi.lns_ntl > 16)) return fail();
   if (lns && (a.N % 64 || a.N / 64 != a.epi.lns_ntl || !a.epi.xc)) return fail();
   if (lnc && (!a.epi.lnc_c1 || !a.epi.lnc_c2 || !a.epi.lns_mean || a.K != 64 * a.epi.lns_ntl)) return fail();
-  // EPI_GLU_DW: the conv reads 8 older ring rows (kernel size at most 9), each stream's rows of
-  // the call must lie in one tile (tile rows a multiple of the frames per stream), and the ring
-  // offsets are 32-bit (the caller checks the layer's ring size)
+  // EPI_GLU_DW: the conv reads 8 older ring rows (kernel size at most 9); the epilogue convolves
+  // the streams whose rows of the call lie in one 64-row block (at most 64 frames per call: the
+  // others cross one boundary each and are left to dw_straddle_kernel), and the ring offsets are
+  // 32-bit (the caller checks the layer's ring size)
   if (dw && (a.dw_taps < 1 || a.dw_taps > 9 || !a.dw_w || !a.dw_b || !a.epi.out || !a.epi.cring || a.epi.D % 32 ||
-             a.epi.cv.nf < 1 || 64 % a.epi.cv.nf))
+             a.epi.cv.nf < 1 || a.epi.cv.nf > 64))
     return fail();
   const int kt = a.K / 64 / ks;  // k-steps per block
   if (tile == 0) {
@@ -2117,12 +2119,7 @@ void launch_attention(Launcher& L, const AttnArgs& a, int dtype, int hd) {
 // One thread per (row, 4 channels): the taps and ring rows are loaded together, positions
 // before the stream start read as zero.
 template <typename T>
-__global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  const int cg = a.D / 4;
-  const long total = (long)a.cv.n_streams * a.cv.nf * cg;
-  if (idx >= total) return;
-  const int m = (int)(idx / cg), c = (int)(idx % cg) * 4;
+__device__ __forceinline__ void dw_row4(const DwArgs& a, int m, int c) {
   const int s = m / a.cv.nf, i = m % a.cv.nf;
   const int id = a.cv.ids[s];
   const int p = a.cv.cpos[s] + i;
@@ -2154,12 +2151,41 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
   for (int q = 0; q < 4; ++q) st<T>(e + q, silu_f(acc[q]));
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int cg = a.D / 4;
+  const long total = (long)a.cv.n_streams * a.cv.nf * cg;
+  if (idx >= total) return;
+  dw_row4<T>(a, (int)(idx / cg), (int)(idx % cg) * 4);
+}
+
+// The streams whose rows cross a multiple of 64 rows (one per boundary at most, the frames per
+// call being at most 64): the MFMA GLU epilogue leaves their conv to this kernel, blockIdx.y
+// the boundary 64 (y + 1), x over the stream's (frame, 4 channels).
+__global__ __launch_bounds__(256) void dw_straddle_kernel(DwArgs a) {
+  const int b = 64 * ((int)blockIdx.y + 1), nf = a.cv.nf, s = b / nf;
+  if (b % nf == 0 || s >= a.cv.n_streams) return;
+  const int cg = a.D / 4, idx = (int)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= nf * cg) return;
+  dw_row4<bf16_t>(a, s * nf + idx / cg, (idx % cg) * 4);
+}
+
 void launch_dwconv(Launcher& L, const DwArgs& a, int dtype) {
   DwArgs args = a;
   const long total = (long)a.cv.n_streams * a.cv.nf * (a.D / 4);
   const void* fn = dtype == DT_F32 ? (const void*)&dw_kernel<float> : (const void*)&dw_kernel<bf16_t>;
   L.tag_name = "dwconv";  // the caller tags bytes and flops
   L.launch(fn, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
+}
+
+bool launch_dwconv_straddle(Launcher& L, const DwArgs& a) {
+  const int M = a.cv.n_streams * a.cv.nf;
+  if (a.cv.nf < 1 || a.cv.nf > 64 || 64 % a.cv.nf == 0 || M <= 64) return false;  // no stream crosses
+  DwArgs args = a;  // the caller tags the launch
+  L.launch((const void*)&dw_straddle_kernel, dim3((unsigned)((a.cv.nf * (a.D / 4) + 255) / 256), (unsigned)((M - 1) / 64)),
+           dim3(256), 0, &args);
+  return true;
 }
 
 // =============================================================================== input, FE window

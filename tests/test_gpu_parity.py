@@ -310,7 +310,11 @@ def test_bf16_attention_shapes(cfg):
     C3.replace(name="C3_dw9_fresh", n_layers=2, streams=40, staggered=False, chunks=6),
     # kernel size 15 (14 older rows): the separate depthwise kernel
     C3.replace(name="C3_dw15", n_layers=2, streams=40, dw_kernel=15, chunks=6),
-], ids=["dw5", "dw3-4rows", "dw9-fresh", "dw15-separate"])
+    # 5 and 10 frames per pass (lookahead): streams whose rows cross a multiple of 64 rows get
+    # their conv from the small kernel after pw1, the others in its epilogue
+    C5.replace(name="C5_la3_dw", n_layers=2, streams=40, n_lookahead=3, chunks=6),
+    C5.replace(name="C5_dw_40", n_layers=2, streams=40, chunks=6),
+], ids=["dw5", "dw3-4rows", "dw9-fresh", "dw15-separate", "dw-5rows-crossing", "dw-10rows-crossing"])
 def test_bf16_depthwise_conv_shapes(cfg):
     _check_workload(cfg, cfg.chunks, range(cfg.streams))
 
