@@ -133,7 +133,9 @@ enum EpiKind {
   EPI_QKV = 5,     // q -> qbuf (f32); k, v -> ring slots of the row's position
   EPI_GLU = 6,     // a*sigmoid(b) of GLU-packed column pairs -> conv ring slot
   EPI_GLU_DW = 7,  // EPI_GLU, then the causal depthwise conv + SiLU of the call's rows over the
-                   // ring -> out_t[m][c] (compute dtype); two-row kernel only (GemmArgs dw_*)
+                   // ring -> out_t[m][c] (compute dtype; GemmArgs dw_*): two-row kernel, and the
+                   // MFMA kernel (kernel size <= 9; the streams whose rows cross a multiple of
+                   // 64 rows are left to launch_dwconv_straddle)
   EPI_PART = 8,    // part[z][m][n] = acc over k-range z (float32, no bias): split-K partial of
                    // the MFMA kernel, summed by resid_ln (GemmArgs ksplit, EpiArgs pstride)
   EPI_SILU_KEEP = 9,  // EPI_SILU with write-back stores that leave the rows in L2 (MFMA kernel;
@@ -211,7 +213,7 @@ struct GemmArgs {
   const float* pre_b;
   int a_dw;              // A rows are SiLU(depthwise conv over the ring) (see DwArgs fields)
   const void* dw_ring;   // conv ring of the layer (cring_idx layout, width K)
-  const float* dw_w;     // [taps][K]
+  const float* dw_w;     // [taps][K] (also EPI_GLU_DW's taps, K = the GLU channels)
   const float* dw_b;     // [K]
   int dw_taps, dw_Rc;
   const float* res_src;  // EPI_RESID: out = LN(res_src rows; res_g, res_b) + alpha (acc + b)
