@@ -1053,9 +1053,15 @@ void enqueue_push(cac_ctx* c, Launcher& L, int n, const int32_t* ids, int n_fram
       // 6 lie before a fresh stream's start), then depthwise + pointwise twice (5 rows, 2 of
       // them before the start; 2 rows), then the projection of each frame's C x F/8 map
       const int C = d.fc, B = d.bins, wrows = d.tail + d.mpc;
-      Fe2dArgs s1{cv, c->ws + c->lay.win, c->ws + c->lay.f2_a1, c->P<float>(c->lay.f2_c1w), c->P<float>(c->lay.f2_c1b),
-                  wrows, B, 11, B / 2, C, 1, 6};
-      launch_fe2d(L, s1);
+      // stage 1 and the first depthwise stage in one launch where the stage-1 map fits on chip
+      Fe2dS1DwArgs sd{cv, c->ws + c->lay.win, c->ws + c->lay.f2_d2, c->P<float>(c->lay.f2_c1w), c->P<float>(c->lay.f2_c1b),
+                      c->P<float>(c->lay.f2_dw2w), c->P<float>(c->lay.f2_dw2b), wrows, B, 11, B / 2, 5, B / 4, C, 6};
+      const bool s1dw = launch_fe2d_s1dw(L, sd);
+      if (!s1dw) {
+        Fe2dArgs s1{cv, c->ws + c->lay.win, c->ws + c->lay.f2_a1, c->P<float>(c->lay.f2_c1w), c->P<float>(c->lay.f2_c1b),
+                    wrows, B, 11, B / 2, C, 1, 6};
+        launch_fe2d(L, s1);
+      }
       struct { size_t in, dw, dwb, mid, pw, pwb, out; int Tin, Fin, Tout, Fout, neg; const char* role; } st2[2] = {
           {c->lay.f2_a1, c->lay.f2_dw2w, c->lay.f2_dw2b, c->lay.f2_d2, c->lay.f2_pw2w, c->lay.f2_pw2b, c->lay.f2_a2, 11, B / 2, 5,
            B / 4, 2, "fe2d_pw2"},
@@ -1064,7 +1070,7 @@ void enqueue_push(cac_ctx* c, Launcher& L, int n, const int32_t* ids, int n_fram
       for (int i = 0; i < 2; ++i) {
         Fe2dArgs dw{cv, c->ws + st2[i].in, c->ws + st2[i].mid, c->P<float>(st2[i].dw), c->P<float>(st2[i].dwb),
                     st2[i].Tin, st2[i].Fin, st2[i].Tout, st2[i].Fout, C, 0, 0};
-        launch_fe2d(L, dw);
+        if (i > 0 || !s1dw) launch_fe2d(L, dw);
         EpiArgs e{};
         e.cv = cv; e.bias = c->P<float>(st2[i].pwb);
         e.kind = EPI_RELU_FE; e.out = c->ws + st2[i].out; e.ldo = C;

@@ -308,6 +308,21 @@ struct Fe2dArgs {
   int Tin, Fin, Tout, Fout, C, cin1, neg;
 };
 
+// 2-D front end stage 1 and the depthwise stage after it in one launch (fe2d_s1dw_kernel): the
+// stage-1 map [T1][F1][C] of each stream stays on chip; the depthwise output [n][T2][F2][C]
+// (bf16) is written. Stage 1 as Fe2dArgs with cin1 (ReLU, rows r < neg1 zero for streams at
+// position 0), the depthwise stage as Fe2dArgs without (no activation).
+struct Fe2dS1DwArgs {
+  CallView cv;
+  const void* in;      // [n][Tin][Fin] the mel window (bf16)
+  void* out;           // [n][T2][F2][C]
+  const float* w1;     // [9][C] stage-1 taps
+  const float* b1;     // [C]
+  const float* w2;     // [9][C] depthwise taps
+  const float* b2;     // [C]
+  int Tin, Fin, T1, F1, T2, F2, C, neg1;
+};
+
 struct CopyRowsArgs {    // out[row_out(m)][c] = x[amap(m) + c], row_out as in EPI_F32
   const float* x;
   RowMap amap;
@@ -458,6 +473,9 @@ void launch_copy_rows(Launcher& L, const CopyRowsArgs& a);
 void kernels_init();
 void launch_fe_window(Launcher& L, const FeWindowArgs& a, int dtype);
 void launch_fe2d(Launcher& L, const Fe2dArgs& a);
+// false (nothing launched) where the stage-1 map does not fit the kernel's LDS (F1 > 64) or C is
+// not a multiple of 32
+bool launch_fe2d_s1dw(Launcher& L, const Fe2dS1DwArgs& a);
 void launch_advance(Launcher& L, const AdvanceArgs& a);
 void launch_fill(Launcher& L, const FillArgs& a);
 void launch_posproj(Launcher& L, const PosProjArgs& a);

@@ -2429,6 +2429,92 @@ void launch_fe2d(Launcher& L, const Fe2dArgs& a) {
   L.launch((const void*)&fe2d_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, &args);
 }
 
+// Stage 1 and the depthwise stage after it for one stream and 32 channels per block: the mel
+// window and the stage-1 map (bf16, rounded as the separate launches store it) sit in LDS, so
+// the 11 x F1 x C stage-1 map never goes to memory (at 1024 streams, 128 bins, 256 channels it
+// is 369 MB per call, which the separate stage-1 launch spent ~190 us writing). Stage 1: thread
+// (column f, 8-channel group) over the rows; depthwise: thread (column, 8-channel group, row
+// parity) over every other row, 16-byte stores, the block's 4 groups of a position adjacent.
+constexpr int FE2D_CB = 32;
+__global__ __launch_bounds__(256) void fe2d_s1dw_kernel(Fe2dS1DwArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char fe_lds[];
+  bf16_t* win = (bf16_t*)fe_lds;                                     // [Tin][Fin]
+  bf16_t* m1 = (bf16_t*)(fe_lds + ((a.Tin * a.Fin * 2 + 15) & ~15));  // [T1][F1][32]
+  const int ncb = a.C / FE2D_CB, s = blockIdx.x / ncb, cb = blockIdx.x - s * ncb, tid = threadIdx.x;
+  const int cg = tid & 3, c0 = cb * FE2D_CB + cg * 8;
+  {  // the window, 16 bytes per thread
+    const u32x4_v* src = (const u32x4_v*)((const bf16_t*)a.in + (long)s * a.Tin * a.Fin);
+    const int n16 = a.Tin * a.Fin / 8;
+    for (int k = tid; k < n16; k += 256) ((u32x4_v*)win)[k] = src[k];
+  }
+  float w[9][8], b[8];
+#pragma unroll
+  for (int t = 0; t < 9; ++t) ld_f8(a.w1 + (long)t * a.C + c0, w[t]);
+  ld_f8(a.b1 + c0, b);
+  const bool fresh = a.cv.cpos[s] == 0;
+  __syncthreads();
+  const int f = tid >> 2;
+  if (f < a.F1) {
+    for (int r = 0; r < a.T1; ++r) {
+      float acc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = b[q];
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {  // unconditional reads (clamped column), padding selected out
+          const int col = 2 * f + j - 1;
+          const float raw = bf2f(win[(2 * r + i) * a.Fin + min(max(col, 0), a.Fin - 1)]);
+          const float v = (col >= 0 && col < a.Fin) ? raw : 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] += w[i * 3 + j][q] * v;
+        }
+      const bool zero = fresh && r < a.neg1;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = zero ? 0.0f : fmaxf(acc[q], 0.0f);
+      *(u32x4_v*)(m1 + ((r * a.F1 + f) * FE2D_CB + cg * 8)) =
+          u32x4_v{pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3]), pack_bf2(acc[4], acc[5]), pack_bf2(acc[6], acc[7])};
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < 9; ++t) ld_f8(a.w2 + (long)t * a.C + c0, w[t]);
+  ld_f8(a.b2 + c0, b);
+  __syncthreads();
+  const int f2 = (tid >> 2) & 31, rh = tid >> 7;
+  if (f2 >= a.F2) return;
+  for (int r2 = rh; r2 < a.T2; r2 += 2) {
+    float acc[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] = b[q];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int col = 2 * f2 + j - 1;
+        const u32x4_v raw = *(const u32x4_v*)(m1 + (((2 * r2 + i) * a.F1 + min(max(col, 0), a.F1 - 1)) * FE2D_CB + cg * 8));
+        const u32x4_v u = (col >= 0 && col < a.F1) ? raw : u32x4_v{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += w[i * 3 + j][2 * q] * __uint_as_float(u[q] << 16);
+          acc[2 * q + 1] += w[i * 3 + j][2 * q + 1] * __uint_as_float(u[q] & 0xffff0000u);
+        }
+      }
+    st_bf8((bf16_t*)a.out + (((long)s * a.T2 + r2) * a.F2 + f2) * a.C + c0, acc);
+  }
+}
+
+bool launch_fe2d_s1dw(Launcher& L, const Fe2dS1DwArgs& a) {
+  if (a.C % FE2D_CB || a.F1 > 64 || a.F2 > 32 || (a.Tin * a.Fin) % 8 || 2 * a.T2 + 1 > a.T1 || 2 * a.T1 + 1 > a.Tin)
+    return false;
+  Fe2dS1DwArgs args = a;
+  const size_t lds = (size_t)((a.Tin * a.Fin * 2 + 15) & ~15) + (size_t)a.T1 * a.F1 * FE2D_CB * 2;
+  if (lds > 64 * 1024) return false;
+  const double n = a.cv.n_streams;
+  L.tag("fe2d_conv1_depthwise", n * a.T2 * a.F2 * a.C * 2.0, 2.0 * 9.0 * n * (a.T1 * a.F1 + a.T2 * a.F2) * a.C);
+  L.launch((const void*)&fe2d_s1dw_kernel, dim3((unsigned)(a.cv.n_streams * (a.C / FE2D_CB))), dim3(256), lds, &args);
+  return true;
+}
+
 // =============================================================================== positions
 __global__ void advance_kernel(AdvanceArgs a) {
   const int s = blockIdx.x * 256 + threadIdx.x;
