@@ -269,6 +269,18 @@ def test_2d_front_end_fresh_streams():
         _check_workload(C4S.replace(n_layers=2, streams=S, staggered=False, chunks=6), 6, range(S))
 
 
+@pytest.mark.parametrize("bins,channels", [(64, 64), (256, 64)], ids=["bins64-fused", "bins256-separate"])
+def test_2d_front_end_other_widths(bins, channels):
+    """The 2-D front end with 64 mel bins and 64 channels (stage 1 and the first depthwise stage
+    in one launch, half its threads idle) and with 256 bins (a stage-1 map too wide for that
+    launch's LDS: the separate stage kernels), 2 layers, fresh and staggered streams."""
+    from synth import C4S
+    cfg = C4S.replace(name=f"C4S_b{bins}_c{channels}", n_layers=2, streams=6, mel_bins=bins, fe_channels=channels,
+                      chunks=4)
+    _check_workload(cfg, 4, range(cfg.streams))
+    _check_workload(cfg.replace(staggered=False), 4, range(cfg.streams))
+
+
 @pytest.mark.parametrize("d_model,heads", [(256, 4), (1024, 16)], ids=["d256", "d1024"])
 def test_bf16_layernorm_carried_at_other_widths(d_model, heads):
     """2048 rows (1024 streams x 2 frames), where the LayerNorms before qkv, pw1 and FF2 up ride
