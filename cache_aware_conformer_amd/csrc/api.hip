@@ -675,6 +675,7 @@ struct Pass {
     const double bytes = kv_rows * 2.0 * d.D * d.esz + (double)d.H * d.nrel * d.hd * 4.0;
     const double flops = 6.0 * nrows * (kv_rows / cv.n_streams) * d.D;
     L.tag("attention", bytes, flops);
+    L.tag_kv(kv_rows, 2.0 * d.D * d.esz, 6.0 * cv.nf * d.D);
     launch_attention(L, at, d.dt, d.hd);
   }
 
@@ -1036,6 +1037,19 @@ int32_t cac_create_streams(const cac_config* cfg, const float* h_params, size_t 
 
 namespace {
 
+// The K/V rows a push's attention reads, summed over the streams that run a pass: each one's
+// cache fill before the push plus the rows the pass computes (host positions, before the push
+// commits them).
+double call_kv_rows(const cac_ctx* c, int n, const int32_t* ids, int n_frames, const std::vector<int32_t>& cids) {
+  const Dims& d = c->d;
+  double kvr = 0;
+  if (!d.lookahead)
+    for (int i = 0; i < n; ++i) kvr += std::min(c->hpos[ids[i]], d.Lc) + n_frames;
+  else
+    for (int id : cids) kvr += std::min(c->hpos[id], d.Lc) + d.nc;
+  return kvr;
+}
+
 // Everything one push enqueues after the id lists are on the device.
 void enqueue_push(cac_ctx* c, Launcher& L, int n, const int32_t* ids, int n_frames, const void* d_input, float* d_out,
                   const std::vector<int32_t>& cids) {
@@ -1112,9 +1126,7 @@ void enqueue_push(cac_ctx* c, Launcher& L, int n, const int32_t* ids, int n_fram
       InputArgs ia{cv, d_input, c->P<float>(c->lay.x), M, d.D, dpos, n_frames};
       launch_input(L, ia, d.dt);
     }
-    double kvr = 0;
-    for (int i = 0; i < n; ++i) kvr += std::min(c->hpos[ids[i]], d.Lc) + n_frames;
-    Pass ps{c, L, cv, M, kvr};
+    Pass ps{c, L, cv, M, call_kv_rows(c, n, ids, n_frames, cids)};
     ps.layers();
     ps.joint(d_out, M, RowMap{INT_MAX, 0, d.D}, nullptr, 1, 0);
     if (d.fe) {  // the front-end window kernel reads the positions from every thread of a stream
@@ -1133,9 +1145,7 @@ void enqueue_push(cac_ctx* c, Launcher& L, int n, const int32_t* ids, int n_fram
       CallView cv{dcids, dpos, d.nc, nC, c->P<int32_t>(c->lay.ccpos)};
       LaGatherArgs lg{cv, c->ws + c->lay.x0, c->P<float>(c->lay.x), d.D, d.Rx};
       launch_la_gather(L, lg, d.dt);
-      double kvr = 0;
-      for (int id : cids) kvr += std::min(c->hpos[id], d.Lc) + d.nc;
-      Pass ps{c, L, cv, nC * d.nc, kvr};
+      Pass ps{c, L, cv, nC * d.nc, call_kv_rows(c, n, ids, n_frames, cids)};
       ps.layers();
       ps.joint(d_out, nC * d.ne, RowMap{d.ne, d.nc * d.D, d.D}, c->P<int32_t>(c->lay.cidx), d.ne, d.ne);
       AdvanceArgs a2{dcids, dpos, dpend, nC, d.ne, -d.ne};
@@ -1185,6 +1195,15 @@ hipError_t push_graph(cac_ctx* c, int n, const int32_t* ids, int n_frames, const
   }
   cac_ctx::Graph& gr = it->second;
   c->last_graph = &gr;
+  // the nodes' algorithmic work as of this push (attention's grows with the cache fill, which
+  // differs from the push that recorded the graph)
+  const double kvr = call_kv_rows(c, n, ids, n_frames, cids);
+  for (NodeRec& r : gr.nodes)
+    if (r.kv_bytes > 0.0 || r.kv_flops > 0.0) {
+      r.bytes += (kvr - r.kv_rows) * r.kv_bytes;
+      r.flops += (kvr - r.kv_rows) * r.kv_flops;
+      r.kv_rows = kvr;
+    }
   if (gr.in != d_input || gr.out != d_out) {
     for (size_t i = 0; i < gr.nodes.size(); ++i) {
       if (gr.in_offs[i].empty() && gr.out_offs[i].empty()) continue;

@@ -422,6 +422,10 @@ struct NodeRec {
   std::vector<char> args;
   std::string name;     // kernel tag ("family/role")
   double bytes, flops;  // algorithmic bytes and flops of the launch
+  // attention: the part of bytes and flops that grows with the K/V rows the call reads (per row),
+  // and those rows as of the push that last used the node, so that a replay at another cache
+  // fill can restate them
+  double kv_bytes = 0.0, kv_flops = 0.0, kv_rows = 0.0;
 };
 
 struct Launcher {
@@ -436,6 +440,13 @@ struct Launcher {
   const char* role = nullptr;        // optional role of the next dense product ("qkv", ...)
   char name_buf[64];
   double tag_bytes = 0.0, tag_flops = 0.0;
+  double tag_kv_rows = 0.0, tag_kv_bytes = 0.0, tag_kv_flops = 0.0;
+  // after tag(): how much of its bytes and flops is per K/V row read, and the call's rows
+  void tag_kv(double rows, double bytes_per_row, double flops_per_row) {
+    tag_kv_rows = rows;
+    tag_kv_bytes = bytes_per_row;
+    tag_kv_flops = flops_per_row;
+  }
   void tag(const char* n, double bytes, double flops) {
     tag_name = n;
     if (role) {

@@ -76,10 +76,12 @@ void Launcher::launch_raw(const void* fn, dim3 grid, dim3 block, size_t shmem, v
         err = hipLaunchKernel(fn, grid, block, kp, shmem, stream);
       }
       tag_bytes = tag_flops = 0.0;
+      tag_kv_rows = tag_kv_bytes = tag_kv_flops = 0.0;
       return;
     }
     err = hipLaunchKernel(fn, grid, block, kp, shmem, stream);
     tag_bytes = tag_flops = 0.0;
+    tag_kv_rows = tag_kv_bytes = tag_kv_flops = 0.0;
     return;
   }
   hipKernelNodeParams p = {};
@@ -102,10 +104,14 @@ void Launcher::launch_raw(const void* fn, dim3 grid, dim3 block, size_t shmem, v
       r.name = tag_name;
       r.bytes = tag_bytes;
       r.flops = tag_flops;
+      r.kv_rows = tag_kv_rows;
+      r.kv_bytes = tag_kv_bytes;
+      r.kv_flops = tag_kv_flops;
       rec->push_back(std::move(r));
     }
   }
   tag_bytes = tag_flops = 0.0;
+  tag_kv_rows = tag_kv_bytes = tag_kv_flops = 0.0;
 }
 
 // =============================================================================== epilogue

@@ -528,7 +528,7 @@ def test_profile_replay_times_one_kernel_family():
     from cache_aware_conformer_amd.binding import CacError
     cfg = C2.replace(n_layers=3)
     enc = _enc(cfg, make_weights(cfg), max_streams=1)
-    xs = make_inputs(cfg, 0, 2)
+    xs = make_inputs(cfg, 0, 3)
     for c in range(2):
         enc.push_chunk([0], to_dev(xs[c][None], cfg))
     torch.cuda.synchronize()
@@ -537,5 +537,13 @@ def test_profile_replay_times_one_kernel_family():
     assert rep["us_per_launch"] > 0.0 and rep["bytes_per_launch"] > 0.0
     att = enc.profile_replay("attention", reps=5)
     assert att["launches"] == cfg.n_layers
+    # the replayed attention work is that of the last push's cache fill, not of the push that
+    # recorded the graph: one more push of 2 frames reads 2 more K/V rows of D float32 values
+    # each (K and V), and 6 flops per query row, key row and dimension
+    enc.push_chunk([0], to_dev(xs[2][None], cfg))
+    torch.cuda.synchronize()
+    att3 = enc.profile_replay("attention", reps=5)
+    assert att3["bytes_per_launch"] - att["bytes_per_launch"] == pytest.approx(2 * 2 * cfg.d_model * 4)
+    assert att3["flops_per_launch"] - att["flops_per_launch"] == pytest.approx(6 * 2 * 2 * cfg.d_model)
     with pytest.raises(CacError):
         enc.profile_replay("no_such_kernel", reps=5)
